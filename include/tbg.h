@@ -1,0 +1,163 @@
+/*
+ * tbg.h — C ABI of the MI355X (gfx950) tiled bf16 GEMM library with descriptor-driven tile copies.
+ *
+ * The library computes C = A·B with bf16 inputs and fp32 accumulation, feeding its matrix cores
+ * from tiles that are copied global memory -> LDS as the descriptor pages describe them: a
+ * host-built tensor descriptor (rank <= 5, byte strides, a box, element strides, an XOR swizzle
+ * of the destination, out-of-bounds fill) plus coordinates per copy.
+ *
+ * Sources, cited by page title and section:
+ *   [TMA]  "2 · Le Tensor Memory Accelerator" (mkdocs.reaper.mx, cuda-moderne/02-tma)
+ *   [MAP]  "H100 · cuTensorMap（TMA 描述符）" (runguoli.com, h100-cuda-programming/l4)
+ *   [PIPE] "1 · Asynchronisme et mbarrier" (mkdocs.reaper.mx, cuda-moderne/01-asynchronisme...)
+ *   [GEMM] "GEMM: la moltiplicazione di matrici sull'hardware" (book.paithon.it)
+ *
+ * Conventions for every call:
+ *   - No HIP or framework types cross this boundary.  `stream` is a hipStream_t passed as
+ *     void* (NULL = the legacy default stream).  Device pointers are plain addresses of device
+ *     memory that the caller owns; the library never allocates, frees or retains memory.
+ *   - All argument checks run synchronously on the host and return a status; nothing is
+ *     enqueued when a check fails.  Device work is enqueued on `stream` and the call returns
+ *     without waiting; a fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - No exception crosses the ABI.  tbg_last_error() gives a readable detail of the last
+ *     failure on the calling thread.
+ *   - Every array of per-dimension values is ordered innermost dimension first ([MAP] §8.2).
+ */
+#ifndef TBG_H_
+#define TBG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TBG_OK = 0,
+    TBG_ERR_INVALID_VALUE = 1, /* a null pointer, a negative size, inconsistent arguments      */
+    TBG_ERR_MISALIGNED = 2,    /* base or stride not a multiple of 16 bytes ([TMA] §2.3)      */
+    TBG_ERR_UNSUPPORTED = 3,   /* rank outside 1..5, or a size this library does not take     */
+    TBG_ERR_OUT_OF_RANGE = 4,  /* a dimension, box, element stride or workspace out of range  */
+    TBG_ERR_NO_DEVICE = 5,     /* no usable gfx950 device                                     */
+    TBG_ERR_HIP = 6            /* the HIP runtime refused a launch                             */
+} tbg_status;
+
+/* Element type of a copy ([MAP] §7).  A copy moves bits: no conversion, no flush to zero. */
+typedef enum { TBG_U8 = 0, TBG_U16 = 1, TBG_U32 = 2, TBG_F16 = 3, TBG_BF16 = 4, TBG_F32 = 5 } tbg_dtype;
+
+/* Destination swizzle ([MAP] §11.3): for a byte offset a inside the box image,
+ *   a' = a ^ ((a & Y_mask) >> 3),  Y_mask = 0x080 (32B), 0x180 (64B), 0x380 (128B),
+ * i.e. 32B: a[4] ^= a[7]; 64B: a[5:4] ^= a[8:7]; 128B: a[6:4] ^= a[9:7].  16-byte units move
+ * whole ([MAP] §11.4).
+ * TBG_SWIZZLE_128B_2ROW is this library's extension of the same XOR form for gfx950's LDS,
+ * which serves 16 lanes of a 16-byte read per cycle from 64 four-byte banks (256 bytes):
+ *   a' = a ^ ((a & 0x700) >> 4),  i.e. a[6:4] ^= a[10:8],
+ * so sixteen consecutive 128-byte rows read at one logical 16-byte column hit 16 distinct
+ * 16-byte bank groups.  It permutes 16-byte units inside each aligned 128-byte block. */
+typedef enum {
+    TBG_SWIZZLE_NONE = 0,
+    TBG_SWIZZLE_32B = 1,
+    TBG_SWIZZLE_64B = 2,
+    TBG_SWIZZLE_128B = 3,
+    TBG_SWIZZLE_128B_2ROW = 4
+} tbg_swizzle;
+
+/* Out-of-bounds fill ([MAP] §14; [TMA] §2.5): box elements outside the tensor are written to
+ * the destination as zero bytes (TBG_OOB_ZERO, the pages' FILL_NONE) or as the element type's
+ * canonical quiet NaN (TBG_OOB_NAN: bf16 0x7FC0, f16 0x7E00, f32 0x7FC00000; floating types
+ * only).  The source is never touched outside the tensor. */
+typedef enum { TBG_OOB_ZERO = 0, TBG_OOB_NAN = 1 } tbg_oob_fill;
+
+/* L2 promotion hint ([MAP] §13).  Accepted and recorded; it does not change any result. */
+typedef enum { TBG_L2_NONE = 0, TBG_L2_64B = 1, TBG_L2_128B = 2, TBG_L2_256B = 3 } tbg_l2_hint;
+
+/* Layout of the GEMM's B operand: TBG_B_KN = row-major K×N (N contiguous);
+ * TBG_B_NK = N×K with K contiguous (B transposed, as weights are usually stored). */
+typedef enum { TBG_B_KN = 0, TBG_B_NK = 1 } tbg_b_layout;
+
+/* A host-built tensor descriptor: 128 bytes, plain data, copied by value ([TMA] §2.2; [MAP]
+ * §3, §5).  It records a raw device address and does not keep that memory alive. */
+typedef struct {
+    uint64_t opaque[16];
+} tbg_tensor_desc;
+
+/* Encode a tiled-copy descriptor ([TMA] §2.3; [MAP] §6, §8, §9).
+ *   out             caller storage for the descriptor.
+ *   dtype           element type (sets the element size).
+ *   rank            number of dimensions, 1..5 ([TMA] §2.2).
+ *   global_address  device address of element (0,...,0); must be a multiple of 16 bytes.
+ *   global_dim      [rank] elements per dimension, innermost first; each in 1..2^32 ([MAP] §8.2).
+ *   global_strides  [rank-1] byte distance between consecutive indices of dimensions 1..rank-1
+ *                   (dimension 0's stride is the element size, [MAP] §8.3); each a multiple of 16
+ *                   and below 2^40.  May be NULL when rank == 1.
+ *   box_dim         [rank] traversal box per copy, in elements, each 1..256 ([MAP] §9.2).
+ *   element_strides [rank] step between copied elements, each 1..8 ([MAP] §9.1); a box copies
+ *                   n[i] = ceil(box_dim[i] / element_strides[i]) elements per dimension.
+ *   swizzle, l2, oob as documented above.
+ * The image of one copy is dense, innermost first, elsize * prod(n[i]) bytes, at most 64 KiB.
+ * With a swizzle, box_dim[0] * elsize must not exceed 128 bytes for the 128-byte modes (32/64
+ * for the 32B/64B modes, [MAP] §9.2; [TMA] §2.3) and the image size must be a multiple of that
+ * span so the permutation stays inside the image.
+ * Returns TBG_OK, or UNSUPPORTED (rank), MISALIGNED (base/strides), OUT_OF_RANGE (dims, box,
+ * element strides, image size), INVALID_VALUE (null pointers, enum values, swizzle width, NaN
+ * fill of an integer type). */
+tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank, const void* global_address,
+                            const uint64_t* global_dim, const uint64_t* global_strides, const uint32_t* box_dim,
+                            const uint32_t* element_strides, tbg_swizzle swizzle, tbg_l2_hint l2,
+                            tbg_oob_fill oob);
+
+/* Bytes of one copy's image for an encoded descriptor; 0 if `d` is not a valid descriptor. */
+size_t tbg_box_bytes(const tbg_tensor_desc* d);
+
+/* Copy one box ([TMA] §2.2, §2.4): the element at box position j (innermost first) comes from
+ * tensor coordinates coords[i] + j[i] * element_strides[i] and lands at image byte offset
+ * swizzle(elsize * (j[0] + n[0]*(j[1] + n[1]*(...)))); positions outside the tensor get the
+ * fill.  The box passes through LDS on its way to `dst_image`.
+ *   coords     [rank] signed int32 coordinates in host memory (negative values allowed).
+ *   dst_image  device memory of tbg_box_bytes(d) bytes, 16-byte aligned.
+ * Returns INVALID_VALUE for null arguments or a bad descriptor, MISALIGNED for dst_image,
+ * NO_DEVICE / HIP for runtime failures. */
+tbg_status tbg_tiled_copy(const tbg_tensor_desc* d, const int32_t* coords, void* dst_image, void* stream);
+
+/* Copy n boxes of the same descriptor: box b uses coords_dev[b*rank .. b*rank+rank-1] (device
+ * memory, int32) and writes its image at dst_images + b * tbg_box_bytes(d).  n == 0 is a no-op.
+ * dst_images must be 16-byte aligned. */
+tbg_status tbg_tiled_copy_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n, void* dst_images,
+                               void* stream);
+
+/* Workspace bytes tbg_gemm needs for these sizes, assuming A and B start on 16-byte
+ * boundaries.  It is non-zero only when an operand has to be repacked first ([GEMM] section
+ * "I tensor core", packing of a block into a contiguous area; "In pratica", 16-byte alignment of
+ * the leading dimension): A when lda % 8 != 0 or K % 8 != 0; B (N×K) likewise with ldb; B (K×N)
+ * when ldb % 8 != 0. */
+size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, tbg_b_layout bl);
+
+/* C = A·B ([GEMM] "Il conto": C_ij = Σ_k A_ik B_kj, 2MNK flops), bf16 inputs, fp32 accumulation
+ * in the matrix cores ([GEMM] tensor-core section), fp32 or bf16 (round to nearest even) output.
+ *   A          bf16, row-major M×K, lda >= K (elements).
+ *   B          bf16, TBG_B_KN: row-major K×N, ldb >= N;  TBG_B_NK: N×K, ldb >= K.
+ *   C          TBG_F32 or TBG_BF16, row-major M×N, ldc >= N.  Only C[m][n] with m < M, n < N is
+ *              written; C must not overlap A, B or the workspace.
+ *   workspace  device memory of at least tbg_gemm_workspace_bytes(...) bytes (plus the pack
+ *              size of any operand whose base is not 16-byte aligned); may be NULL when 0.
+ * M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).  Leading dimensions are
+ * limited to 2^22 - 1 elements.
+ * Returns INVALID_VALUE (negative sizes, ld below its minimum, null pointers, bad enum),
+ * UNSUPPORTED (leading dimension too large), OUT_OF_RANGE (workspace too small; the detail
+ * names the size needed), NO_DEVICE / HIP for runtime failures. */
+tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                    tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* tbg_status_string(tbg_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* tbg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TBG_H_ */

@@ -1,0 +1,196 @@
+"""CPU oracle for the tiled copy and the bf16 GEMM — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark may import this
+package.  The GPU library never loads it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, built into ``liboracle.so`` by ``oracle/build.py``);
+this module only marshals numpy arrays into it.  Every routine cites the passage it follows:
+
+* ``swizzle`` — "H100 · cuTensorMap" §11.3 (XOR swizzle, per-mode bit lists).
+* ``tiled_copy`` — "H100 · cuTensorMap" §8.2, §8.3, §9.1, §9.2, §14; "2 · Le Tensor Memory
+  Accelerator" §2.2, §2.5 (box copy with element strides and out-of-bounds fill).
+* ``gemm`` / ``gemm_points`` — "GEMM: la moltiplicazione di matrici sull'hardware", section
+  "Il conto, e il problema della versione ingenua" (C = A·B, 2MNK) and the tensor-core section
+  (16-bit inputs, wide accumulation).
+
+Parity status: all routines pinned by ``tests/test_oracle_pins.py``; the GEMM is exact only up
+to the summation order, which the pages leave open (tolerance 1e-2 relative / 1e-3 absolute).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+SWIZZLE_MODES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
+# element type -> (element size, NaN kind understood by oracle.c; 0 = integer, no NaN)
+DTYPES = {
+    "u8": (1, 0), "u16": (2, 0), "u32": (4, 0),
+    "f16": (2, 2), "bf16": (2, 1), "f32": (4, 3),
+}
+
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+
+class Oracle:
+    """Handle on one build of ``liboracle.so`` (tests may load a deliberately broken build)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            from oracle import build as _b
+            _b.build(out=path)
+        lib = ctypes.CDLL(path)
+        lib.oracle_swizzle.restype = ctypes.c_uint64
+        lib.oracle_swizzle.argtypes = [ctypes.c_uint64, ctypes.c_int]
+        lib.oracle_swizzle_array.restype = None
+        lib.oracle_swizzle_array.argtypes = [_u64p, _u64p, ctypes.c_int64, ctypes.c_int]
+        lib.oracle_tiled_copy.restype = ctypes.c_uint64
+        lib.oracle_tiled_copy.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, _u64p, _u64p,
+                                          _u32p, _u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          _i32p, ctypes.c_void_p]
+        lib.oracle_gemm_rows.restype = None
+        lib.oracle_gemm_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _u16p,
+                                         ctypes.c_int64, _u16p, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.c_int64, _f64p, _f32p,
+                                         ctypes.c_int64, ctypes.c_int, _f64p]
+        lib.oracle_gemm_points.restype = None
+        lib.oracle_gemm_points.argtypes = [ctypes.c_int64, _u16p, ctypes.c_int64, _u16p,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int64, _i64p,
+                                           _i64p, _f64p, _f32p]
+        lib.oracle_f32_to_bf16_array.restype = None
+        lib.oracle_f32_to_bf16_array.argtypes = [_f32p, _u16p, ctypes.c_int64]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        self.lib = lib
+        self.path = path
+
+    # -- O1 ---------------------------------------------------------------------------------
+    def swizzle(self, offsets, mode: str | int):
+        m = SWIZZLE_MODES[mode] if isinstance(mode, str) else int(mode)
+        a = np.ascontiguousarray(np.asarray(offsets, dtype=np.uint64).reshape(-1))
+        out = np.empty_like(a)
+        self.lib.oracle_swizzle_array(a.ctypes.data_as(_u64p), out.ctypes.data_as(_u64p), a.size, m)
+        return out.reshape(np.shape(offsets))
+
+    # -- O2 ---------------------------------------------------------------------------------
+    def tiled_copy(self, src: np.ndarray, dtype: str, dims: Sequence[int], strides_bytes: Sequence[int],
+                   box: Sequence[int], estr: Sequence[int], swizzle: str | int, oob_nan: bool,
+                   coords: Sequence[int]) -> np.ndarray:
+        """Copy one box of ``src`` (raw bytes of the tensor; dims innermost first) to an image.
+
+        Returns the image as a uint8 array.  Raises ValueError where the plain reference
+        declines the arguments (rank, element stride 0, image not a whole number of swizzle
+        spans, NaN fill of an integer type)."""
+        elsize, nan_kind = DTYPES[dtype]
+        rank = len(dims)
+        m = SWIZZLE_MODES[swizzle] if isinstance(swizzle, str) else int(swizzle)
+        n = [(int(b) + int(e) - 1) // int(e) for b, e in zip(box, estr)]
+        image = elsize * int(np.prod(n))
+        dst = np.zeros(max(image, 1), dtype=np.uint8)
+        srcb = np.ascontiguousarray(src).view(np.uint8)
+        d = np.array(list(dims) + [1] * (5 - rank), dtype=np.uint64)
+        s = np.array(list(strides_bytes) + [0] * (5 - len(strides_bytes)), dtype=np.uint64)
+        b = np.array(list(box) + [1] * (5 - rank), dtype=np.uint32)
+        e = np.array(list(estr) + [1] * (5 - rank), dtype=np.uint32)
+        c = np.array(list(coords) + [0] * (5 - rank), dtype=np.int32)
+        got = self.lib.oracle_tiled_copy(elsize, rank, srcb.ctypes.data, d.ctypes.data_as(_u64p),
+                                         s.ctypes.data_as(_u64p), b.ctypes.data_as(_u32p),
+                                         e.ctypes.data_as(_u32p), m, int(bool(oob_nan)), nan_kind,
+                                         c.ctypes.data_as(_i32p), dst.ctypes.data)
+        if got == 0:
+            raise ValueError("oracle_tiled_copy declined these arguments")
+        assert got == image
+        return dst[:image]
+
+    # -- O3 ---------------------------------------------------------------------------------
+    def gemm(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, lda: int, ldb: int,
+             b_layout: str = "kn", rows: Optional[tuple] = None, want64: bool = False,
+             threads: int = 0):
+        """C rows [m0, m1) of A·B.  A, B: uint16 bf16 bit arrays (flat or 2-D, row-major with the
+        given leading dimensions).  Returns float32 (m1-m0, N), plus the float64 sums if asked."""
+        A = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1)
+        B = np.ascontiguousarray(B, dtype=np.uint16).reshape(-1)
+        m0, m1 = rows if rows is not None else (0, M)
+        bl = {"kn": 0, "nk": 1}[b_layout]
+        out32 = np.empty((m1 - m0, N), dtype=np.float32)
+        out64 = np.empty((m1 - m0, N), dtype=np.float64) if want64 else None
+        nthr = threads if threads > 0 else self.lib.oracle_max_threads()
+        scratch = np.empty(max(1, nthr) * max(N, 1) + 1, dtype=np.float64)
+        if m1 > m0 and N > 0:
+            self.lib.oracle_gemm_rows(M, N, K, A.ctypes.data_as(_u16p), lda, B.ctypes.data_as(_u16p), ldb,
+                                      bl, m0, m1,
+                                      out64.ctypes.data_as(_f64p) if want64 else None,
+                                      out32.ctypes.data_as(_f32p), N, nthr, scratch.ctypes.data_as(_f64p))
+        return (out32, out64) if want64 else out32
+
+    def gemm_points(self, A: np.ndarray, B: np.ndarray, K: int, lda: int, ldb: int, ms, ns,
+                    b_layout: str = "kn", want64: bool = False):
+        A = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1)
+        B = np.ascontiguousarray(B, dtype=np.uint16).reshape(-1)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        out32 = np.empty(ms.size, dtype=np.float32)
+        out64 = np.empty(ms.size, dtype=np.float64)
+        self.lib.oracle_gemm_points(K, A.ctypes.data_as(_u16p), lda, B.ctypes.data_as(_u16p), ldb,
+                                    {"kn": 0, "nk": 1}[b_layout], ms.size, ms.ctypes.data_as(_i64p),
+                                    ns.ctypes.data_as(_i64p), out64.ctypes.data_as(_f64p),
+                                    out32.ctypes.data_as(_f32p))
+        return (out32, out64) if want64 else out32
+
+    def f32_to_bf16(self, x: np.ndarray) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.oracle_f32_to_bf16_array(x.reshape(-1).ctypes.data_as(_f32p),
+                                          out.reshape(-1).ctypes.data_as(_u16p), x.size)
+        return out
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``oracle.c`` as committed (built on first use if absent)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float64 (exact: bf16 is the top half of a binary32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def gemm_check(got: np.ndarray, ref32: np.ndarray, rtol: float = 1e-2, atol: float = 1e-3) -> dict:
+    """O4: a GPU value g passes iff it is finite and |g − r| ≤ max(rtol·|r|, atol), where r is the
+    oracle's binary32 result (before any bf16 rounding).  Returns the statistics and the verdict."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref32, dtype=np.float64)
+    err = np.abs(g - r)
+    bound = np.maximum(rtol * np.abs(r), atol)
+    finite = np.isfinite(g)
+    ok = finite & (err <= bound)
+    rel = err / np.maximum(np.abs(r), 1e-30)
+    return {
+        "pass": bool(ok.all()),
+        "n": int(g.size),
+        "n_fail": int((~ok).sum()),
+        "max_abs_err": float(err.max()) if g.size else 0.0,
+        "max_rel_err": float(np.where(np.abs(r) >= atol / rtol, rel, 0.0).max()) if g.size else 0.0,
+        "n_abs_branch": int((np.abs(r) < atol / rtol).sum()),
+    }

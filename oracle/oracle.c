@@ -1,0 +1,235 @@
+/*
+ * oracle.c — plain, slow CPU reference for the tiled copy and the bf16 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load this file's
+ * library: only the test suite, the smoke check and the CPU-baseline leg of the benchmark do.
+ * It shares no code, header, table or constant with the GPU library; it takes raw parameters,
+ * never the packed descriptor.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [TMA]   "2 · Le Tensor Memory Accelerator" (mkdocs.reaper.mx, cuda-moderne/02-tma)
+ *   [MAP]   "H100 · cuTensorMap（TMA 描述符）" (runguoli.com, h100-cuda-programming/l4)
+ *   [GEMM]  "GEMM: la moltiplicazione di matrici sull'hardware" (book.paithon.it)
+ *
+ * Parity pins: every function here is pinned by CPU tests against facts the pages or plain
+ * mathematics fix (per-bit swizzle formulas, the worked descriptor example, brute-force index
+ * decoding, exact rational dot products, closed forms).  The one part left unpinned beyond
+ * the tolerance is the hardware's own accumulation order inside a matrix instruction.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------------
+ * Element conversions, written from the IEEE-754 binary16/bfloat16/binary32 definitions.
+ * bfloat16 is the top half of a binary32: widening is a 16-bit shift, which is exact.
+ * ---------------------------------------------------------------------------------------- */
+static double bf16_to_f64(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even.  A NaN stays a NaN (quiet bit set,
+ * sign and upper payload kept); everything else follows the rounding definition on the bit
+ * pattern: add half an ulp of the kept part, plus one if the kept part is odd, and truncate. */
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * O1 — swizzle.  [MAP] §11.3: a' = a ^ ((a & Y_mask) >> 3), low bits a[3:0] never change.
+ * The section's per-mode bit lists (32B: a[4]^=a[7]; 64B: a[5:4]^=a[8:7]; 128B: a[6:4]^=a[9:7])
+ * fix Y_mask as bits 7, 8:7 and 9:7 respectively (the single "1 << 7" printed there only
+ * reproduces the 32B row).  mode: 0 none, 1 32B, 2 64B, 3 128B.
+ * mode 4 is the library's extension of the same XOR form with the row bits taken one place
+ * higher, a ^ ((a & 0x700) >> 4), i.e. a[6:4] ^= a[10:8]; it is defined by that mask and shift.
+ * ---------------------------------------------------------------------------------------- */
+uint64_t oracle_swizzle_general(uint64_t a, uint64_t y_mask, unsigned shift) {
+    return a ^ ((a & y_mask) >> shift);
+}
+
+uint64_t oracle_swizzle(uint64_t a, int mode) {
+    switch (mode) {
+        case 0: return a;
+        case 1: return oracle_swizzle_general(a, 0x080u, 3);
+        case 2: return oracle_swizzle_general(a, 0x180u, 3);
+        case 3: return oracle_swizzle_general(a, 0x380u, 3);
+        case 4: return oracle_swizzle_general(a, 0x700u, 4);
+        default: return (uint64_t)-1;
+    }
+}
+
+void oracle_swizzle_array(const uint64_t* in, uint64_t* out, int64_t n, int mode) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_swizzle(in[i], mode);
+}
+
+/* Size in bytes of the aligned block inside which a mode permutes 16-byte units. */
+static uint64_t swizzle_span(int mode) {
+    return mode == 1 ? 32u : mode == 2 ? 64u : (mode == 3 || mode == 4) ? 128u : 1u;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * O2 — tiled copy of one box into a dense image.
+ *   [MAP] §8.2 globalDim: elements per dimension, innermost first.
+ *   [MAP] §8.3 globalStrides: rank-1 byte strides of dims 1..rank-1; dim 0's stride is the
+ *         element size.
+ *   [MAP] §9.1 elementStrides: per-dimension step in elements (nonzero, at most 8).
+ *   [MAP] §9.2 boxDim: the traversal box, in elements.
+ *   [MAP] §14 / [TMA] §2.5: elements outside the tensor are filled in the destination only
+ *         (zero, or NaN); the source is not touched.
+ *   [MAP] §11: the destination byte offset goes through the swizzle.
+ * Readings (pages silent): the box covers box[i] elements of traversal, of which every
+ * estr[i]-th is copied, so n[i] = ceil(box[i]/estr[i]) land densely, innermost first, with no
+ * padding; coordinates are signed; the swizzle acts on the byte offset inside the image.
+ * NaN fill writes the canonical quiet NaN of the element type.
+ *   elsize: 1, 2 or 4 bytes; nan_kind: 0 none (integer), 1 bf16, 2 f16, 3 f32.
+ * Returns the image size in bytes, or 0 on an argument this plain reference does not take.
+ * ---------------------------------------------------------------------------------------- */
+uint64_t oracle_tiled_copy(int elsize, int rank, const void* src, const uint64_t* dims,
+                           const uint64_t* strides_bytes, const uint32_t* box, const uint32_t* estr,
+                           int swizzle, int oob_nan, int nan_kind, const int32_t* coords, void* dst) {
+    if (rank < 1 || rank > 5 || (elsize != 1 && elsize != 2 && elsize != 4)) return 0;
+    uint64_t S[5], n[5], dim[5];
+    int64_t c[5];
+    for (int i = 0; i < 5; ++i) { S[i] = 0; n[i] = 1; dim[i] = 1; c[i] = 0; }
+    S[0] = (uint64_t)elsize;
+    for (int i = 1; i < rank; ++i) S[i] = strides_bytes[i - 1];
+    for (int i = 0; i < rank; ++i) {
+        if (estr[i] == 0) return 0;
+        n[i] = (box[i] + estr[i] - 1) / estr[i];
+        dim[i] = dims[i];
+        c[i] = coords[i];
+    }
+    uint64_t image = (uint64_t)elsize * n[0] * n[1] * n[2] * n[3] * n[4];
+    if (swizzle != 0 && image % swizzle_span(swizzle) != 0) return 0;
+
+    uint8_t fill[4] = {0, 0, 0, 0};
+    if (oob_nan) {
+        if (nan_kind == 1) { fill[0] = 0xC0; fill[1] = 0x7F; }                   /* bf16 0x7FC0 */
+        else if (nan_kind == 2) { fill[0] = 0x00; fill[1] = 0x7E; }              /* f16  0x7E00 */
+        else if (nan_kind == 3) { fill[2] = 0xC0; fill[3] = 0x7F; }              /* f32  0x7FC00000 */
+        else return 0;
+    }
+    const uint8_t* s = (const uint8_t*)src;
+    uint8_t* d = (uint8_t*)dst;
+
+    uint64_t j[5];
+    for (j[4] = 0; j[4] < n[4]; ++j[4])
+    for (j[3] = 0; j[3] < n[3]; ++j[3])
+    for (j[2] = 0; j[2] < n[2]; ++j[2])
+    for (j[1] = 0; j[1] < n[1]; ++j[1])
+    for (j[0] = 0; j[0] < n[0]; ++j[0]) {
+        int inside = 1;
+        uint64_t src_off = 0;
+        for (int i = 0; i < rank; ++i) {
+            int64_t x = c[i] + (int64_t)j[i] * (int64_t)estr[i];
+            if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;
+            else src_off += (uint64_t)x * S[i];
+        }
+        uint64_t lin = j[0] + n[0] * (j[1] + n[1] * (j[2] + n[2] * (j[3] + n[3] * j[4])));
+        uint64_t off = oracle_swizzle(lin * (uint64_t)elsize, swizzle);
+        if (off + (uint64_t)elsize > image) return 0; /* never writes past the image */
+        if (inside) memcpy(d + off, s + src_off, (size_t)elsize);
+        else memcpy(d + off, fill, (size_t)elsize);
+    }
+    return image;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * O3 — GEMM.  [GEMM] "Il conto": C = A·B, A (M,K), B (K,N), C (M,N), C_ij = Σ_k A_ik B_kj.
+ * [GEMM] tensor-core section: 16-bit inputs, the sum kept in a wide format.  Here every
+ * bf16·bf16 product is exact in binary64, the sum runs over k in ascending order in binary64,
+ * and the result is rounded once to binary32 (round to nearest even, the C cast).
+ *   A: bf16 bits, row-major M×K, leading dimension lda (elements).
+ *   B: bf16 bits; b_layout 0: row-major K×N (ldb >= N); 1: N×K with K contiguous (ldb >= K).
+ *   rows [m0, m1) of C are produced; out64 (if non-null) gets the binary64 sums and out32
+ *   (if non-null) the binary32 results, both row-major with leading dimension ldo, indexed
+ *   from row m0.  threads: worker count (0 = library default).
+ * ---------------------------------------------------------------------------------------- */
+void oracle_gemm_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                      const uint16_t* B, int64_t ldb, int b_layout, int64_t m0, int64_t m1,
+                      double* out64, float* out32, int64_t ldo, int threads, double* scratch) {
+    (void)M;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+    if (b_layout == 0) {
+        /* Each row's N sums are kept side by side; k runs outermost, so each sum still adds
+         * its terms in ascending k. scratch holds N doubles per worker. */
+#pragma omp parallel
+        {
+            int t = 0;
+#ifdef _OPENMP
+            t = omp_get_thread_num();
+#endif
+            double* acc = scratch + (size_t)t * (size_t)N;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t m = m0; m < m1; ++m) {
+                for (int64_t n = 0; n < N; ++n) acc[n] = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double a = bf16_to_f64(A[m * lda + k]);
+                    const uint16_t* brow = B + k * ldb;
+                    for (int64_t n = 0; n < N; ++n) acc[n] += a * bf16_to_f64(brow[n]);
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    if (out64) out64[(m - m0) * ldo + n] = acc[n];
+                    if (out32) out32[(m - m0) * ldo + n] = (float)acc[n];
+                }
+            }
+        }
+    } else {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t m = m0; m < m1; ++m) {
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(B[n * ldb + k]);
+                if (out64) out64[(m - m0) * ldo + n] = acc;
+                if (out32) out32[(m - m0) * ldo + n] = (float)acc;
+            }
+        }
+    }
+}
+
+/* The same sum at individual (m, n) points, for sampled checks of large products. */
+void oracle_gemm_points(int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                        int b_layout, int64_t npts, const int64_t* ms, const int64_t* ns,
+                        double* out64, float* out32) {
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npts; ++p) {
+        int64_t m = ms[p], n = ns[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[n * ldb + k];
+            acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(b);
+        }
+        if (out64) out64[p] = acc;
+        if (out32) out32[p] = (float)acc;
+    }
+}
+
+/* binary32 array -> bfloat16 bits (round to nearest even), for bf16 outputs. */
+void oracle_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle against what the pages and plain mathematics fix.
+
+Each pin takes an ``oracle.Oracle`` handle and raises AssertionError when the oracle disagrees,
+so ``test_oracle_pins.py`` can run them on the oracle as committed and on deliberately broken
+builds of it (every broken build must fail at least one pin).  None of these checks retypes the
+oracle's own formula: each goes through another route (per-bit statements, numpy slicing,
+index decoding, exact rationals, integer matmul, closed forms).
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pages_worked_examples.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------------------------
+# Swizzle ("H100 · cuTensorMap" §11.2–§11.4)
+# ---------------------------------------------------------------------------------------------
+# The library's gfx950 extension mode, stated bit by bit: a[6:4] ^= a[10:8].
+EXT_RULES = {"128B_2ROW": [[6, 10], [5, 9], [4, 8]]}
+
+
+def _per_bit(a: np.ndarray, rules) -> np.ndarray:
+    a = a.astype(np.uint64)
+    out = a.copy()
+    for dst, src in rules:
+        bit = ((a >> np.uint64(dst)) ^ (a >> np.uint64(src))) & np.uint64(1)
+        out = (out & ~np.uint64(1 << dst)) | (bit << np.uint64(dst))
+    return out
+
+
+def pin_swizzle_bit_rules(o):
+    g = golden()["swizzle_bit_rules"]
+    a = np.arange(1 << 14, dtype=np.uint64)
+    big = np.array([(1 << 40) + 12345, (1 << 33) - 1, 0xFFFF_FFF0], dtype=np.uint64)
+    a = np.concatenate([a, big])
+    assert np.array_equal(o.swizzle(a, "none"), a)
+    for mode in ("32B", "64B", "128B"):
+        assert np.array_equal(o.swizzle(a, mode), _per_bit(a, g[mode])), mode
+    for mode, rules in EXT_RULES.items():
+        assert np.array_equal(o.swizzle(a, mode), _per_bit(a, rules)), mode
+    # a[3:0] never changes (§11.3)
+    for mode in ("32B", "64B", "128B", "128B_2ROW"):
+        s = o.swizzle(a, mode)
+        assert np.array_equal(s & np.uint64(15), a & np.uint64(15))
+
+
+def pin_swizzle_hand_examples(o):
+    ex = golden()["swizzle_hand_examples"]
+    for mode in ("32B", "64B", "128B"):
+        for a, want in ex[mode]:
+            assert int(o.swizzle([a], mode)[0]) == want, (mode, a, want)
+
+
+def pin_swizzle_structure(o):
+    """Involution; bijection inside each atom (rows of 128 B × the rows the mode reads its
+    bits from); 16-byte units move whole; the permutation never leaves its span block."""
+    atoms = {"32B": 256, "64B": 512, "128B": 1024, "128B_2ROW": 2048}
+    spans = {"32B": 32, "64B": 64, "128B": 128, "128B_2ROW": 128}
+    a = np.arange(1 << 15, dtype=np.uint64)
+    for mode, atom in atoms.items():
+        s = o.swizzle(a, mode)
+        assert np.array_equal(o.swizzle(s, mode), a), mode
+        blocks = a.reshape(-1, atom)
+        sb = s.reshape(-1, atom)
+        for b, t in zip(blocks, sb):
+            assert np.array_equal(np.sort(t), b), mode
+        # whole 16-byte units: offsets of one unit stay together and in order
+        u = s.reshape(-1, 16)
+        assert np.all(u[:, 1:] - u[:, :-1] == 1), mode
+        span = spans[mode]
+        assert np.array_equal(s // np.uint64(span), a // np.uint64(span)), mode
+
+
+def pin_bank_spread(o):
+    """§11.2 bank = (a'/4) % 32: in 128B mode the same logical 16-byte column of 8 consecutive
+    128-byte rows lands in 8 distinct 16-byte bank groups, covering all 32 banks.  For the
+    library's 2-row mode, 16 consecutive rows fill a 64-bank (256-byte) window."""
+    g = golden()["bank_equation"]
+    for col in range(8):
+        offs = np.array([r * 128 + col * 16 for r in range(8)], dtype=np.uint64)
+        s = o.swizzle(offs, "128B")
+        banks = set()
+        for x in s:
+            for w in range(4):
+                banks.add(int((int(x) + 4 * w) // g["bank_bytes"]) % g["banks"])
+        assert banks == set(range(g["banks"])), col
+        # without a swizzle every row hits the same 4 banks
+        assert len({int(x // 4) % 32 for x in offs}) == 1
+    for col in range(8):
+        offs = np.array([r * 128 + col * 16 for r in range(16)], dtype=np.uint64)
+        s = o.swizzle(offs, "128B_2ROW")
+        assert len({int(x // 16) % 16 for x in s}) == 16, col
+
+
+# ---------------------------------------------------------------------------------------------
+# Tiled copy ("2 · Le Tensor Memory Accelerator" §2.2–§2.5; "H100 · cuTensorMap" §8–§9, §14)
+# ---------------------------------------------------------------------------------------------
+def _bf16_matrix(rows, cols, seed):
+    g = torch.Generator().manual_seed(seed)
+    t = (torch.rand((rows, cols), generator=g) * 2 - 1).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def pin_worked_descriptor(o):
+    """The page's creer_descripteur on a 256×256 bf16 matrix: the image is the 128×64 LDS
+    tile of §2.4 (16384 bytes, the byte count the barrier expects), swizzled in 16-byte units;
+    undoing the swizzle gives A[y:y+128, x:x+64] with zeros past the edges."""
+    g = golden()["tma_worked_descriptor"]
+    rows = cols = 256
+    A = _bf16_matrix(rows, cols, 11)
+    dims = [cols, rows]
+    strides = [cols * g["stride_bytes_per_col"]]
+    want_bytes = g["smem_tile_rows"] * g["smem_tile_cols"] * g["smem_tile_elsize"]
+    assert want_bytes == g["image_bytes"] == golden()["mbarrier_expect_tx_bytes"]["bytes"]
+    bits = golden()["swizzle_bit_rules"]["128B"]
+    for (x, y) in [(0, 0), (64, 0), (192, 128), (128, 64), (224, 192), (-32, -64), (250, 250), (-64, 0)]:
+        img = o.tiled_copy(A, "bf16", dims, strides, g["box"], g["element_strides"], g["swizzle"],
+                           g["oob"] == "nan", [x, y])
+        assert img.size == g["image_bytes"]
+        # undo the swizzle with the per-bit statement (an involution), element by element
+        offs = np.arange(img.size, dtype=np.uint64)
+        logical = np.empty_like(img)
+        logical[offs] = img[_per_bit(offs, bits)]
+        tile = logical.view(np.uint16).reshape(g["smem_tile_rows"], g["smem_tile_cols"])
+        want = np.zeros((128, 64), dtype=np.uint16)
+        ys, xs = max(y, 0), max(x, 0)
+        ye, xe = min(y + 128, rows), min(x + 64, cols)
+        if ye > ys and xe > xs:
+            want[ys - y:ye - y, xs - x:xe - x] = A[ys:ye, xs:xe]
+        assert np.array_equal(tile, want), (x, y)
+
+
+def _index_tensor(dims_inner_first, dtype):
+    total = int(np.prod(dims_inner_first))
+    npdt = {"u8": np.uint8, "u16": np.uint16, "u32": np.uint32, "f16": np.uint16, "bf16": np.uint16,
+            "f32": np.uint32}[dtype]
+    return np.arange(total, dtype=np.uint64).astype(npdt)
+
+
+def _decode_case(o, dims, box, estr, coords, dtype, oob, padded_rows=0, swz="none"):
+    """Fill a tensor with its own linear index, copy one box, and check every image element
+    against the coordinates it must come from (or the fill)."""
+    rank = len(dims)
+    elsize = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4}[dtype]
+    # row pitch of dim 1 padded by `padded_rows` elements, rounded so strides are 16-byte multiples
+    pitch = [elsize * (dims[0] + padded_rows)]
+    for i in range(2, rank):
+        pitch.append(pitch[-1] * dims[i - 1])
+    total_elems = (pitch[-1] * dims[rank - 1]) // elsize if rank > 1 else dims[0]
+    npdt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[elsize]
+    src = np.zeros(total_elems, dtype=npdt)
+    # linear index of coordinate x under these strides
+    idx = np.indices(dims[::-1]).reshape(rank, -1)[::-1]  # idx[i] = coordinate along dim i
+    lin = idx[0].astype(np.int64)
+    for i in range(1, rank):
+        lin = lin + idx[i].astype(np.int64) * (pitch[i - 1] // elsize)
+    tag = (np.arange(lin.size, dtype=np.int64) + 1)      # element tags 1..count
+    src[lin] = tag.astype(npdt)
+    before = src.copy()
+    img = o.tiled_copy(src, dtype, dims, pitch[:rank - 1], box, estr, swz, oob == "nan", coords)
+    assert np.array_equal(src, before), "source modified"
+    n = [(b + e - 1) // e for b, e in zip(box, estr)]
+    img_e = img.view(npdt)
+    if swz != "none":
+        # the swizzle permutes whole bytes; undo it and compare against the unswizzled copy
+        plain = o.tiled_copy(src, dtype, dims, pitch[:rank - 1], box, estr, "none", oob == "nan", coords)
+        offs = np.arange(img.size, dtype=np.uint64)
+        assert np.array_equal(img[o.swizzle(offs, swz)], plain)
+        return
+    jj = np.indices(n[::-1]).reshape(rank, -1)[::-1]
+    x = np.stack([coords[i] + jj[i] * estr[i] for i in range(rank)])
+    inside = np.all([(x[i] >= 0) & (x[i] < dims[i]) for i in range(rank)], axis=0)
+    # tag of an inside element: 1 + its rank among all elements in innermost-first order
+    t = x[0].astype(np.int64)
+    mul = 1
+    for i in range(1, rank):
+        mul *= dims[i - 1]
+        t = t + x[i].astype(np.int64) * mul
+    want_tag = (t + 1).astype(np.int64)
+    got = img_e.astype(np.int64)
+    if oob == "nan":
+        fill = {"f16": 0x7E00, "bf16": 0x7FC0, "f32": 0x7FC00000}[dtype]
+    else:
+        fill = 0
+    modv = 1 << (8 * elsize)
+    assert np.array_equal(got[inside], want_tag[inside] % modv)
+    assert np.all(got[~inside] == fill)
+
+
+def pin_copy_decode(o):
+    rng = np.random.default_rng(7)
+    # hand-picked cases: ragged edges, negative coordinates, element strides at each position
+    _decode_case(o, [40, 9, 3], [16, 4, 2], [1, 2, 1], [32, -2, 1], "u16", "zero")
+    _decode_case(o, [17, 5, 4, 3, 2], [8, 3, 2, 2, 2], [3, 1, 2, 1, 1], [-5, 3, 2, 2, 1], "f16", "nan")
+    _decode_case(o, [33], [20], [4], [20], "f32", "nan")
+    _decode_case(o, [64, 64], [64, 16], [1, 8], [0, 3], "u32", "zero")
+    _decode_case(o, [7, 6, 5, 4, 3], [8, 8, 8, 8, 8], [8, 7, 6, 5, 4], [-1, -2, 0, 1, -3], "u8", "zero")
+    _decode_case(o, [64, 10], [64, 8], [1, 1], [-8, -4], "bf16", "nan")
+    for _ in range(40):
+        rank = int(rng.integers(1, 6))
+        dims = [int(rng.integers(1, 12)) for _ in range(rank)]
+        box = [int(rng.integers(1, 10)) for _ in range(rank)]
+        estr = [int(rng.integers(1, 9)) for _ in range(rank)]
+        coords = [int(rng.integers(-6, d + 3)) for d in dims]
+        dtype = ["u8", "u16", "u32", "f16", "bf16", "f32"][int(rng.integers(0, 6))]
+        oob = "nan" if dtype in ("f16", "bf16", "f32") and rng.integers(0, 2) else "zero"
+        _decode_case(o, dims, box, estr, coords, dtype, oob, padded_rows=int(rng.integers(0, 3)) * 8)
+    # swizzled images are the same bytes permuted by the swizzle
+    _decode_case(o, [64, 20], [64, 16], [1, 1], [0, 8], "bf16", "zero", swz="128B")
+    _decode_case(o, [32, 20], [32, 8], [1, 2], [0, 3], "bf16", "nan", swz="64B")
+    _decode_case(o, [16, 20], [16, 8], [1, 1], [0, -3], "u16", "zero", swz="32B")
+    _decode_case(o, [64, 40], [64, 32], [1, 1], [0, 5], "bf16", "zero", swz="128B_2ROW")
+
+
+def pin_fill_and_source(o):
+    """§14: the fill is written to the destination only; zero fill gives zero bytes, NaN fill a
+    NaN of the element type; the source is not modified."""
+    for dtype, npdt in (("bf16", np.uint16), ("f16", np.uint16), ("f32", np.uint32)):
+        src = np.arange(64, dtype=npdt)
+        before = src.copy()
+        img = o.tiled_copy(src, dtype, [8, 8], [8 * src.itemsize], [4, 4], [1, 1], "none", True, [100, 100])
+        vals = img.view(npdt)
+        if dtype == "bf16":
+            f = (vals.astype(np.uint32) << 16).view(np.float32)
+        elif dtype == "f16":
+            f = vals.view(np.float16)
+        else:
+            f = vals.view(np.float32)
+        assert np.all(np.isnan(f)), dtype
+        img0 = o.tiled_copy(src, dtype, [8, 8], [8 * src.itemsize], [4, 4], [1, 1], "none", False, [100, 100])
+        assert np.all(img0 == 0)
+        assert np.array_equal(src, before)
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMM ("GEMM: la moltiplicazione di matrici sull'hardware")
+# ---------------------------------------------------------------------------------------------
+def _bits_of(values: np.ndarray) -> np.ndarray:
+    t = torch.tensor(values, dtype=torch.float32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_gemm_exact_rationals(o):
+    """Brute force on tiny shapes: each C_ij against Σ_k A_ik B_kj in exact rational arithmetic.
+    Every bf16 product is exact and these sums stay exact in binary64, so the binary64 result
+    must equal the rational exactly and the binary32 result is its correct rounding."""
+    rng = np.random.default_rng(3)
+    for (M, N, K, lda_pad, ldb_pad) in [(3, 4, 5, 0, 0), (7, 1, 9, 3, 0), (1, 1, 1, 0, 0), (5, 6, 17, 0, 5),
+                                        (2, 9, 33, 7, 1), (4, 3, 64, 0, 0)]:
+        lda, ldn = K + lda_pad, N + ldb_pad
+        A = _bits_of(rng.standard_normal((M, lda)).astype(np.float32))
+        Bkn = _bits_of(rng.standard_normal((K, ldn)).astype(np.float32))
+        Af, Bf = _f64(A), _f64(Bkn)
+        exact = [[sum((Fraction(Af[m, k]) * Fraction(Bf[k, n]) for k in range(K)), Fraction(0))
+                  for n in range(N)] for m in range(M)]
+        c32, c64 = o.gemm(A, Bkn, M, N, K, lda, ldn, "kn", want64=True)
+        for m in range(M):
+            for n in range(N):
+                assert Fraction(c64[m, n]) == exact[m][n], (M, N, K, m, n)
+                assert c32[m, n] == np.float32(float(exact[m][n]))
+        # the same product with B stored N×K (K contiguous)
+        ldk = K + ldb_pad
+        Bnk = np.zeros((N, ldk), dtype=np.uint16)
+        Bnk[:, :K] = Bkn[:K, :N].T
+        c32n = o.gemm(A, Bnk, M, N, K, lda, ldk, "nk")
+        assert np.array_equal(c32n, c32)
+        # sampled points agree with whole rows
+        ms = rng.integers(0, M, 5)
+        ns = rng.integers(0, N, 5)
+        p32 = o.gemm_points(A, Bkn, K, lda, ldn, ms, ns, "kn")
+        assert np.array_equal(p32, c32[ms, ns])
+        p32n = o.gemm_points(A, Bnk, K, lda, ldk, ms, ns, "nk")
+        assert np.array_equal(p32n, c32[ms, ns])
+
+
+def pin_gemm_closed_forms(o):
+    """A·I = A; all-ones gives C = K; integer-valued operands give exact integer products that
+    must equal numpy's integer matmul (exact for these magnitudes)."""
+    rng = np.random.default_rng(5)
+    M, K = 37, 29
+    A = _bits_of(rng.uniform(-1, 1, (M, K)).astype(np.float32))
+    I = _bits_of(np.eye(K, dtype=np.float32))
+    c = o.gemm(A, I, M, K, K, K, K, "kn")
+    assert np.array_equal(c, _f64(A).astype(np.float32))
+    c = o.gemm(A, I, M, K, K, K, K, "nk")
+    assert np.array_equal(c, _f64(A).astype(np.float32))
+    ones = _bits_of(np.ones((64, 64), dtype=np.float32))
+    for K1 in (1, 7, 64):
+        c = o.gemm(ones, ones, 5, 6, K1, 64, 64, "kn")
+        assert np.all(c == K1)
+    for (M, N, K, bl) in [(31, 45, 777, "kn"), (16, 9, 300, "nk"), (64, 64, 64, "kn")]:
+        Ai = rng.integers(-8, 9, (M, K))
+        Bi = rng.integers(-8, 9, (K, N))
+        want = (Ai.astype(np.int64) @ Bi.astype(np.int64)).astype(np.float64)
+        A = _bits_of(Ai.astype(np.float32))
+        if bl == "kn":
+            c = o.gemm(A, _bits_of(Bi.astype(np.float32)), M, N, K, K, N, "kn")
+        else:
+            c = o.gemm(A, _bits_of(np.ascontiguousarray(Bi.T).astype(np.float32)), M, N, K, K, K, "nk")
+        assert np.array_equal(c.astype(np.float64), want), (M, N, K, bl)
+
+
+def pin_gemm_tiled_equals_direct(o):
+    """The GEMM page's NumPy example: a T=32 tiled product of A (96,80) and B (80,64) equals the
+    direct product.  Tiles are cut with the oracle's own tiled copy (zero fill past the edges,
+    so the ragged K=80 edge contributes nothing), multiplied with numpy and summed over K."""
+    g = golden()["tiled_matmul_numpy_example"]
+    (M, K), (_, N), T = g["A_shape"], g["B_shape"], g["T"]
+    rng = np.random.default_rng(9)
+    A = _bits_of(rng.standard_normal((M, K)).astype(np.float32))
+    B = _bits_of(rng.standard_normal((K, N)).astype(np.float32))
+    _, c64 = o.gemm(A, B, M, N, K, K, N, "kn", want64=True)
+    C = np.zeros((M, N))
+    for i in range(0, M, T):
+        for j in range(0, N, T):
+            acc = np.zeros((T, T))
+            for k in range(0, K, T):
+                a = o.tiled_copy(A, "bf16", [K, M], [K * 2], [T, T], [1, 1], "none", False, [k, i])
+                b = o.tiled_copy(B, "bf16", [N, K], [N * 2], [T, T], [1, 1], "none", False, [j, k])
+                acc += _f64(a.view(np.uint16).reshape(T, T)) @ _f64(b.view(np.uint16).reshape(T, T))
+            C[i:i + T, j:j + T] = acc[:min(T, M - i), :min(T, N - j)]
+    assert np.allclose(C, c64, rtol=1e-12, atol=1e-12) == g["allclose"]
+    # and against numpy's direct product of the widened operands
+    assert np.allclose(_f64(A) @ _f64(B), c64, rtol=1e-12, atol=1e-12)
+
+
+def pin_f32_to_bf16(o):
+    """Round to nearest even against torch's conversion, on ties of every exponent, specials and
+    a dense random sample; NaN stays NaN."""
+    rng = np.random.default_rng(1)
+    u = rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    ties = (np.arange(1 << 16, dtype=np.uint32) << 16) | np.uint32(0x8000)
+    near = (np.arange(1 << 16, dtype=np.uint32) << 16) | np.uint32(0x7FFF)
+    specials = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7F7FFFFF, 0x00000001, 0x7FC00000,
+                         0x7F800001, 0x3F808000, 0x3F818000], dtype=np.uint32)
+    u = np.concatenate([u, ties, near, specials])
+    f = u.view(np.float32)
+    got = o.f32_to_bf16(f)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(f)
+    assert np.array_equal(got[~nan], want[~nan])
+    back = (got[nan].astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(back))
+
+
+ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_structure, pin_bank_spread,
+            pin_worked_descriptor, pin_copy_decode, pin_fill_and_source, pin_gemm_exact_rationals,
+            pin_gemm_closed_forms, pin_gemm_tiled_equals_direct, pin_f32_to_bf16]

@@ -1,0 +1,80 @@
+"""The CPU oracle against the pages' worked examples and plain mathematics (no GPU).
+
+Also checks the pins' strength: each deliberately broken copy of ``oracle/oracle.c`` (a dropped
+term, a wrong sign, index or bound, a transposed operand) must fail at least one pin.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# (description, text in oracle.c, replacement)
+MUTANTS = [
+    ("128B mask drops bit 9", "oracle_swizzle_general(a, 0x380u, 3)", "oracle_swizzle_general(a, 0x180u, 3)"),
+    ("64B shift off by one", "oracle_swizzle_general(a, 0x180u, 3)", "oracle_swizzle_general(a, 0x180u, 2)"),
+    ("2-row mode uses 128B bits", "oracle_swizzle_general(a, 0x700u, 4)", "oracle_swizzle_general(a, 0x380u, 3)"),
+    ("negative coordinate counted inside", "if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;",
+     "if ((uint64_t)x >= dim[i] && x >= 0) inside = 0;"),
+    ("upper bound off by one", "(uint64_t)x >= dim[i]", "(uint64_t)x > dim[i]"),
+    ("element stride dropped", "int64_t x = c[i] + (int64_t)j[i] * (int64_t)estr[i];", "int64_t x = c[i] + (int64_t)j[i];"),
+    ("floor instead of ceil", "n[i] = (box[i] + estr[i] - 1) / estr[i];", "n[i] = box[i] / estr[i] + (box[i] < estr[i]);"),
+    ("image index uses wrong extent", "j[0] + n[0] * (j[1] + n[1] *", "j[0] + n[1] * (j[1] + n[1] *"),
+    ("bf16 NaN bytes swapped", "fill[0] = 0xC0; fill[1] = 0x7F;", "fill[0] = 0x7F; fill[1] = 0xC0;"),
+    ("swizzle skipped on the image", "uint64_t off = oracle_swizzle(lin * (uint64_t)elsize, swizzle);",
+     "uint64_t off = lin * (uint64_t)elsize;"),
+    ("KN product reads B with lda", "const uint16_t* brow = B + k * ldb;", "const uint16_t* brow = B + k * lda;"),
+    ("wrong sign in accumulation", "acc[n] += a * bf16_to_f64(brow[n]);", "acc[n] -= a * bf16_to_f64(brow[n]);"),
+    ("NK operand transposed", "acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(B[n * ldb + k]);",
+     "acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(B[k * ldb + n]);"),
+    ("first term dropped", "for (int64_t k = 0; k < K; ++k) {\n                    double a", "for (int64_t k = 1; k < K; ++k) {\n                    double a"),
+    ("ties rounded up", "u += 0x7FFFu + lsb;", "u += 0x8000u;"),
+    ("points use the wrong layout", "uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[n * ldb + k];",
+     "uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[k * ldb + n];"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_broken_oracle_fails_a_pin(tmp_path, desc, old, new):
+    src = open(oracle_build.SRC).read()
+    assert old in src, f"mutation site not found: {desc}"
+    mutated = src.replace(old, new, 1)
+    csrc = tmp_path / "oracle.c"
+    csrc.write_text(mutated)
+    out = str(tmp_path / "liboracle_mut.so")
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off", str(csrc), "-o", out],
+                   check=True)
+    # The broken build runs in a child process: a wrong index can write past the image.
+    child = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import oracle\n"
+        "from tests import oracle_pins\n"
+        "o = oracle.Oracle(%r)\n"
+        "bad = []\n"
+        "for pin in oracle_pins.ALL_PINS:\n"
+        "    try:\n"
+        "        pin(o)\n"
+        "    except (AssertionError, ValueError, IndexError):\n"
+        "        bad.append(pin.__name__)\n"
+        "print('FAILED_PINS', ','.join(bad))\n"
+    ) % (ROOT, out)
+    r = subprocess.run([sys.executable, "-c", child], capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        # the broken build crashed inside a pin: it is caught, but only as a crash
+        assert "FAILED_PINS" not in r.stdout
+        return
+    line = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED_PINS")][0]
+    failures = [x for x in line.split(" ", 1)[1].split(",") if x]
+    assert failures, f"no pin catches: {desc}"
