@@ -1,0 +1,148 @@
+"""The C ABI on the host: exports, descriptor validation, argument errors (no GPU needed).
+
+The encoder's rules come from "2 · Le Tensor Memory Accelerator" §2.2–§2.3 (rank up to 5,
+16-byte base and stride alignment, swizzle width) and "H100 · cuTensorMap" §8–§9, §14
+(dimension ranges, element strides 1..8, box, NaN fill for floating types)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import tiled_bf16_gemm_amd as tbg
+
+BASE = 0x7F00_0000_0000  # any 16-byte-aligned address: encoding never touches memory
+
+
+def test_library_exports_every_declared_function():
+    names = tbg.declared_functions()
+    assert set(names) >= {"tbg_encode_tiled", "tbg_box_bytes", "tbg_tiled_copy", "tbg_tiled_copy_many",
+                          "tbg_gemm_workspace_bytes", "tbg_gemm", "tbg_status_string", "tbg_last_error"}
+    lib = ctypes.CDLL(tbg.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", tbg.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, f"{n} not exported with C linkage"
+
+
+def test_status_strings():
+    assert tbg.status_string(tbg.OK) == "TBG_OK"
+    assert tbg.status_string(tbg.ERR_MISALIGNED) == "TBG_ERR_MISALIGNED"
+    assert tbg.status_string(99) == "TBG_ERR_UNKNOWN"
+
+
+def _c1_args(**over):
+    a = dict(dtype="bf16", rank=2, global_address=BASE, global_dim=[256, 256], global_strides=[512],
+             box_dim=[64, 128], element_strides=[1, 1], swizzle="128B", l2="128B", oob="zero")
+    a.update(over)
+    return a
+
+
+def _c3_args(**over):
+    a = dict(dtype="bf16", rank=5, global_address=BASE, global_dim=[200, 129, 7, 5, 3],
+             global_strides=[400, 51600, 361200, 1806000], box_dim=[64, 16, 4, 2, 2],
+             element_strides=[1, 2, 1, 1, 1], swizzle="none", l2="none", oob="nan")
+    a.update(over)
+    return a
+
+
+def test_workload_descriptors_encode():
+    d = tbg.encode_tiled(**_c1_args())
+    assert tbg.box_bytes(d) == 64 * 128 * 2 == 16384
+    d = tbg.encode_tiled(**_c3_args())
+    assert tbg.box_bytes(d) == 2 * (64 * 8 * 4 * 2 * 2) == 16384
+    # GEMM operand boxes: A {64 k, 256 m} with the 2-row swizzle, B (K×N) {64 n, 64 k} 128B
+    d = tbg.encode_tiled("bf16", 2, BASE, [8192, 8192], [16384], [64, 256], [1, 1], "128B_2ROW")
+    assert tbg.box_bytes(d) == 32768
+    d = tbg.encode_tiled("bf16", 2, BASE, [8192, 8192], [16384], [64, 64], [1, 1], "128B")
+    assert tbg.box_bytes(d) == 8192
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(rank=0), tbg.ERR_UNSUPPORTED),
+    (dict(rank=6, global_dim=[1] * 6, box_dim=[1] * 6, element_strides=[1] * 6, global_strides=[16] * 5),
+     tbg.ERR_UNSUPPORTED),
+    (dict(global_address=BASE + 8), tbg.ERR_MISALIGNED),
+    (dict(global_address=0), tbg.ERR_INVALID_VALUE),
+    (dict(global_strides=[520]), tbg.ERR_MISALIGNED),
+    (dict(global_dim=[0, 256]), tbg.ERR_OUT_OF_RANGE),
+    (dict(global_dim=[(1 << 32) + 1, 256]), tbg.ERR_OUT_OF_RANGE),
+    (dict(box_dim=[0, 128]), tbg.ERR_OUT_OF_RANGE),
+    (dict(box_dim=[64, 257]), tbg.ERR_OUT_OF_RANGE),
+    (dict(element_strides=[0, 1]), tbg.ERR_OUT_OF_RANGE),
+    (dict(element_strides=[1, 9]), tbg.ERR_OUT_OF_RANGE),
+    (dict(box_dim=[128, 8]), tbg.ERR_INVALID_VALUE),             # 256-byte rows exceed the 128B span
+    (dict(swizzle="64B"), tbg.ERR_INVALID_VALUE),                # 128-byte rows exceed the 64B span
+    (dict(swizzle="32B", box_dim=[16, 8]), tbg.OK),
+    (dict(swizzle="128B", box_dim=[8, 3], element_strides=[1, 1]), tbg.ERR_INVALID_VALUE),
+    (dict(dtype="u16", oob="nan"), tbg.ERR_INVALID_VALUE),       # NaN fill needs a floating type
+    (dict(dtype="f32", box_dim=[32, 128], oob="nan"), tbg.OK),
+    (dict(swizzle=7), tbg.ERR_INVALID_VALUE),
+    (dict(oob=3), tbg.ERR_INVALID_VALUE),
+    (dict(l2=9), tbg.ERR_INVALID_VALUE),
+    (dict(dtype=42), tbg.ERR_INVALID_VALUE),
+    (dict(box_dim=[64, 256], element_strides=[1, 1], swizzle="none", global_strides=[512]), tbg.OK),
+])
+def test_encode_rejections(over, status):
+    assert tbg.encode_tiled_status(**_c1_args(**over)) == status, tbg.last_error()
+
+
+def test_encode_image_limit_and_estride_rounding():
+    # 5 dims of box 8 with element stride 3: n = 3 per dim -> 3^5 = 243 elements
+    d = tbg.encode_tiled("u8", 5, BASE, [9] * 5, [16, 160, 1600, 16000], [8] * 5, [3] * 5)
+    assert tbg.box_bytes(d) == 243
+    # 256 x 256 bf16 = 128 KiB image: over the 64 KiB limit
+    assert tbg.encode_tiled_status("bf16", 2, BASE, [256, 256], [512], [256, 256], [1, 1]) == tbg.ERR_OUT_OF_RANGE
+    assert "64 KiB" in tbg.last_error()
+
+
+def test_box_bytes_of_garbage_is_zero():
+    assert tbg.box_bytes(tbg.TensorDesc()) == 0
+
+
+def test_gemm_argument_errors():
+    g = dict(M=64, N=64, K=64, A=BASE, lda=64, B=BASE, ldb=64, b_layout="kn", C=BASE, ldc=64, c_dtype="f32")
+    assert tbg.gemm_status(**{**g, "M": -1}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "lda": 63}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "ldb": 32}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "b_layout": "nk", "ldb": 63}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "ldc": 10}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "c_dtype": "u8"}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "b_layout": 5}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "lda": 1 << 22}) == tbg.ERR_UNSUPPORTED
+    assert tbg.gemm_status(**{**g, "C": 0}) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_status(**{**g, "A": 0}) == tbg.ERR_INVALID_VALUE
+    # empty output: nothing to do, no device needed
+    assert tbg.gemm_status(**{**g, "M": 0, "A": 0, "B": 0, "C": 0}) == tbg.OK
+    assert tbg.gemm_status(**{**g, "N": 0}) == tbg.OK
+
+
+def test_workspace_bytes():
+    assert tbg.gemm_workspace_bytes(8192, 8192, 8192, 8192, 8192, "kn") == 0
+    assert tbg.gemm_workspace_bytes(16384, 14336, 4096, 4096, 4096, "nk") == 0
+    # the ragged workload: lda = 777 and ldb = 2049 are not 16-byte pitches
+    a = (3001 * 784 * 2 + 255) // 256 * 256
+    b = (777 * 2056 * 2 + 255) // 256 * 256
+    assert tbg.gemm_workspace_bytes(3001, 2049, 777, 777, 2049, "kn") == a + b
+    # padded pitches but K = 777 still needs A repacked (a partial 16-byte chunk along K)
+    assert tbg.gemm_workspace_bytes(3001, 2049, 777, 784, 2056, "kn") == a
+    assert tbg.gemm_workspace_bytes(64, 64, 64, 64, 72, "nk") == 0
+    assert tbg.gemm_workspace_bytes(64, 64, 60, 64, 64, "nk") == 2 * ((64 * 64 * 2 + 255) // 256 * 256)
+
+
+def test_calls_without_a_device_fail_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = tbg.gemm_status(64, 64, 64, BASE, 64, BASE, 64, "kn", BASE, 64, "f32")
+    assert st == tbg.ERR_NO_DEVICE, tbg.last_error()
+    d = tbg.encode_tiled(**_c1_args())
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_copy(d, [0, 0], BASE)
+    assert e.value.status == tbg.ERR_NO_DEVICE
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_copy(d, [0, 0], BASE + 8)
+    assert e.value.status == tbg.ERR_MISALIGNED
+    assert tbg.gemm_status(64, 64, 64, BASE, 64, BASE, 64, "kn", BASE, 64, "f32") == tbg.ERR_NO_DEVICE

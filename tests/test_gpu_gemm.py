@@ -1,0 +1,180 @@
+"""The GEMM on the GPU against the oracle ("GEMM: la moltiplicazione di matrici sull'hardware").
+
+Bar: every output finite and within max(1e-2·|r|, 1e-3) of the oracle's binary32 result r; bit
+for bit where the inputs are small integers (every partial sum is then exact in binary32, so any
+summation order gives the same bits).  The workload sizes that the oracle finishes in seconds
+are compared in full; the 8192³ and 16384×14336×4096 workloads — in the launch configuration the
+benchmark times — are compared on sampled whole rows and scattered points, and checked for
+finiteness and run-to-run determinism everywhere."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+gpu = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tiled_bf16_gemm_amd import torch_ops
+    return torch_ops
+
+
+def _run(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, ldc=None, a_offset=0, b_offset=0):
+    """A_cpu/B_cpu: row-major buffers (rows × ld).  Offsets shift the operands' start by whole
+    elements inside a larger device buffer (to test bases off a 16-byte boundary)."""
+    lda, ldb = A_cpu.shape[1], B_cpu.shape[1]
+    Ad = torch.empty(A_cpu.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    Bd = torch.empty(B_cpu.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    Ad[a_offset:a_offset + A_cpu.numel()] = A_cpu.reshape(-1).cuda()
+    Bd[b_offset:b_offset + B_cpu.numel()] = B_cpu.reshape(-1).cuda()
+    A = Ad[a_offset:a_offset + A_cpu.numel()].view(A_cpu.shape)[:, :K]
+    B = Bd[b_offset:b_offset + B_cpu.numel()].view(B_cpu.shape)
+    B = B[:, :N] if b_layout == "kn" else B[:, :K]
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    ldc = ldc or N
+    Cbuf = torch.full((M, ldc), float("nan"), dtype=tdt, device="cuda")
+    C = Cbuf[:, :N]
+    ops.gemm(A, B, b_layout, out_dtype, out=C)
+    torch.cuda.synchronize()
+    return Cbuf
+
+
+def _to_f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def _check(got: np.ndarray, ref: np.ndarray, what: str):
+    r = oracle.gemm_check(got, ref)
+    _say(f"  {what}: n={r['n']} max_abs={r['max_abs_err']:.3g} max_rel={r['max_rel_err']:.3g} fail={r['n_fail']}")
+    assert r["pass"], f"{what}: {r}"
+
+
+def _full_case(ops, orc, w: workloads.GemmWorkload):
+    A, B = workloads.gemm_inputs(w)
+    lda, ldb, ldc = w.lds()
+    _say(f"gemm {w.name}: M={w.M} N={w.N} K={w.K} {w.b_layout} {w.out_dtype} lda={lda} ldb={ldb} ldc={ldc}")
+    Cbuf = _run(ops, A, B, w.M, w.N, w.K, w.b_layout, w.out_dtype, ldc=ldc)
+    ref = orc.gemm(workloads.bits(A), workloads.bits(B), w.M, w.N, w.K, lda, ldb, w.b_layout)
+    got = _to_f32(Cbuf)
+    _check(got[:, :w.N], ref, w.name)
+    if ldc > w.N:
+        assert np.all(np.isnan(got[:, w.N:])), "columns past N were written"
+    return got[:, :w.N], ref
+
+
+@gpu
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c3_bf16", "c3_padded"])
+def test_workloads_full(ops, orc, name):
+    got, ref = _full_case(ops, orc, workloads.GEMMS[name])
+    if workloads.GEMMS[name].out_dtype == "bf16":
+        # informative: entries whose bf16 differs from the correctly rounded oracle value
+        want16 = orc.f32_to_bf16(ref)
+        got16 = torch.from_numpy(got).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        _say(f"  bf16 entries differing from RNE(oracle): {int((want16 != got16).sum())} of {got.size}")
+
+
+def _sampled(ops, orc, w: workloads.GemmWorkload, rows, npts=4096):
+    A, B = workloads.gemm_inputs(w)
+    lda, ldb, _ = w.lds()
+    _say(f"gemm {w.name} (sampled): M={w.M} N={w.N} K={w.K} {w.b_layout} {w.out_dtype}")
+    Cbuf = _run(ops, A, B, w.M, w.N, w.K, w.b_layout, w.out_dtype)
+    Cbuf2 = _run(ops, A, B, w.M, w.N, w.K, w.b_layout, w.out_dtype)
+    assert torch.equal(Cbuf.view(torch.int16) if Cbuf.dtype == torch.bfloat16 else Cbuf.view(torch.int32),
+                       Cbuf2.view(torch.int16) if Cbuf2.dtype == torch.bfloat16 else Cbuf2.view(torch.int32)), \
+        "two runs differ"
+    assert bool(torch.isfinite(Cbuf).all()), "non-finite output"
+    Ab, Bb = workloads.bits(A), workloads.bits(B)
+    got_rows = _to_f32(Cbuf[rows])
+    for i, m in enumerate(rows):
+        ref = orc.gemm(Ab, Bb, w.M, w.N, w.K, lda, ldb, w.b_layout, rows=(m, m + 1))
+        _check(got_rows[i:i + 1], ref, f"{w.name} row {m}")
+    rng = np.random.default_rng(99)
+    ms = rng.integers(0, w.M, npts)
+    ns = rng.integers(0, w.N, npts)
+    ref = orc.gemm_points(Ab, Bb, w.K, lda, ldb, ms, ns, w.b_layout)
+    got = _to_f32(Cbuf)[ms, ns]
+    _check(got, ref, f"{w.name} {npts} points")
+
+
+@gpu
+def test_c4_8192_sampled(ops, orc):
+    w = workloads.GEMMS["c4"]
+    _sampled(ops, orc, w, rows=[0, 1, 255, 256, 4097, 8190, 8191])
+
+
+@gpu
+def test_c5_mlp_sampled(ops, orc):
+    w = workloads.GEMMS["c5"]
+    _sampled(ops, orc, w, rows=[0, 300, 8191, 12345, 16383])
+
+
+@gpu
+@pytest.mark.parametrize("M,N,K,bl", [(300, 257, 136, "kn"), (300, 257, 136, "nk"), (3001, 2049, 777, "kn"),
+                                      (256, 512, 8192, "kn"), (17, 1000, 520, "nk")])
+def test_integer_inputs_bit_exact(ops, orc, M, N, K, bl):
+    """Small integer operands: every partial sum is an integer below 2^24, so the GPU result
+    must equal the oracle bit for bit, whatever order the matrix cores add in."""
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
+    shape_b = (K, N) if bl == "kn" else (N, K)
+    Bi = torch.from_numpy(rng.integers(-8, 9, shape_b).astype(np.float32)).to(torch.bfloat16)
+    _say(f"integer gemm M={M} N={N} K={K} {bl}")
+    Cbuf = _run(ops, Ai, Bi, M, N, K, bl, "f32")
+    ref = orc.gemm(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, shape_b[1], bl)
+    got = _to_f32(Cbuf)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"
+
+
+@gpu
+def test_random_shapes(ops, orc):
+    """Sizes 1..300 on every axis, both B layouts, both output types, padded leading dimensions
+    (padding holds NaN) and bases off a 16-byte boundary (the repacking path)."""
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        M, N, K, bl, out, pad = workloads.random_gemm_shape(rng)
+        lda = K + (8 * pad if pad else 0)
+        ldb = (N if bl == "kn" else K) + (8 * pad if pad else 0)
+        A = workloads.matrix(M, K, lda, ("normal", 1.0), 100 + case)
+        B = workloads.matrix(K, N, ldb, ("normal", 1.0), 200 + case) if bl == "kn" else \
+            workloads.matrix(N, K, ldb, ("normal", 1.0), 200 + case)
+        off = int(rng.integers(0, 3)) if case % 5 == 4 else 0
+        ldc = N + int(rng.integers(0, 5))
+        _say(f"random gemm {case}: M={M} N={N} K={K} {bl} {out} lda={lda} ldb={ldb} ldc={ldc} offset={off}")
+        Cbuf = _run(ops, A, B, M, N, K, bl, out, ldc=ldc, a_offset=off, b_offset=off)
+        ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, lda, ldb, bl)
+        got = _to_f32(Cbuf)
+        _check(got[:, :N], ref, f"case {case}")
+        assert np.all(np.isnan(got[:, N:])), "columns past N were written"
+
+
+@gpu
+def test_degenerate_sizes(ops):
+    A = torch.randn(64, 64, device="cuda").to(torch.bfloat16)
+    B = torch.randn(64, 64, device="cuda").to(torch.bfloat16)
+    _say("K = 0 writes zeros")
+    C = torch.full((64, 64), float("nan"), device="cuda")
+    ops.gemm(A[:, :0], B[:0, :], "kn", "f32", out=C)
+    torch.cuda.synchronize()
+    assert bool((C == 0).all())
+    _say("M = 0 and N = 0 are no-ops")
+    C = torch.full((1, 64), 7.0, device="cuda")
+    ops.gemm(A[:0], B, "kn", "f32", out=C[:0])
+    ops.gemm(A, B[:, :0], "kn", "f32", out=torch.empty(64, 0, device="cuda"))
+    torch.cuda.synchronize()
+    assert bool((C == 7.0).all())
+    _say("1 x 1 x 1")
+    C = ops.gemm(A[:1, :1], B[:1, :1], "kn", "f32")
+    torch.cuda.synchronize()
+    assert float(C[0, 0]) == float(A[0, 0].float() * B[0, 0].float())

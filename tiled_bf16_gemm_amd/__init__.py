@@ -1,0 +1,172 @@
+"""Python binding of the gfx950 tiled bf16 GEMM / tiled-copy library (``include/tbg.h``).
+
+Argument marshalling only: every function forwards to the C ABI of ``libtbg.so`` (built in-tree
+by ``tiled_bf16_gemm_amd/build.py``), whose kernels do all of the work.  Importing this package
+fails loudly when the library has not been built; there is no fallback path.
+
+Names follow the C ABI without the ``tbg_`` prefix.  Pointers are plain integers (device
+addresses, e.g. ``tensor.data_ptr()``); ``stream`` is a HIP stream handle as an integer
+(``torch.cuda.current_stream().cuda_stream``) or ``None`` for the default stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtbg.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tbg.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_bf16_gemm_amd.build` "
+                      "(or __graft_entry__.build()); there is no non-GPU fallback")
+
+# The library must bind to the same HIP runtime as the framework that owns the device memory and
+# streams it is handed.  PyTorch ships its own libamdhip64 (same soname); importing torch first
+# makes the dynamic linker resolve libtbg.so's dependency to that already-loaded runtime instead
+# of loading a second runtime instance, which could not see torch's streams or allocations.
+try:
+    import torch  # noqa: F401
+except ImportError:  # plain C-ABI use without PyTorch: the system ROCm runtime is used
+    pass
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- enums (values as in tbg.h) -------------------------------------------------------------
+OK, ERR_INVALID_VALUE, ERR_MISALIGNED, ERR_UNSUPPORTED, ERR_OUT_OF_RANGE, ERR_NO_DEVICE, ERR_HIP = range(7)
+DTYPES = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5}
+ELSIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4}
+SWIZZLES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
+OOB = {"zero": 0, "nan": 1}
+L2 = {"none": 0, "64B": 1, "128B": 2, "256B": 3}
+B_LAYOUTS = {"kn": 0, "nk": 1}
+
+
+class TensorDesc(ctypes.Structure):
+    """tbg_tensor_desc: 128 bytes, plain data."""
+    _fields_ = [("opaque", ctypes.c_uint64 * 16)]
+
+
+class Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+_lib.tbg_encode_tiled.restype = ctypes.c_int
+_lib.tbg_encode_tiled.argtypes = [ctypes.POINTER(TensorDesc), ctypes.c_int, ctypes.c_uint32, _vp, _u64p, _u64p,
+                                  _u32p, _u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+_lib.tbg_box_bytes.restype = ctypes.c_size_t
+_lib.tbg_box_bytes.argtypes = [ctypes.POINTER(TensorDesc)]
+_lib.tbg_tiled_copy.restype = ctypes.c_int
+_lib.tbg_tiled_copy.argtypes = [ctypes.POINTER(TensorDesc), _i32p, _vp, _vp]
+_lib.tbg_tiled_copy_many.restype = ctypes.c_int
+_lib.tbg_tiled_copy_many.argtypes = [ctypes.POINTER(TensorDesc), _vp, ctypes.c_uint32, _vp, _vp]
+_lib.tbg_gemm_workspace_bytes.restype = ctypes.c_size_t
+_lib.tbg_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+_lib.tbg_gemm.restype = ctypes.c_int
+_lib.tbg_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, ctypes.c_int, _vp,
+                          ctypes.c_size_t, _vp]
+_lib.tbg_status_string.restype = ctypes.c_char_p
+_lib.tbg_status_string.argtypes = [ctypes.c_int]
+_lib.tbg_last_error.restype = ctypes.c_char_p
+_lib.tbg_last_error.argtypes = []
+
+
+def status_string(status: int) -> str:
+    return _lib.tbg_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return _lib.tbg_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise Error(status, last_error())
+
+
+def _enum(table, v):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def _arr(ctype, values):
+    values = list(values)
+    return (ctype * max(1, len(values)))(*values)
+
+
+def encode_tiled(dtype, rank: int, global_address: int, global_dim: Sequence[int],
+                 global_strides: Optional[Sequence[int]], box_dim: Sequence[int], element_strides: Sequence[int],
+                 swizzle="none", l2="none", oob="zero") -> TensorDesc:
+    """tbg_encode_tiled.  Per-dimension arrays innermost first; strides in bytes (rank-1)."""
+    d = TensorDesc()
+    strides = None if global_strides is None else _arr(ctypes.c_uint64, global_strides)
+    st = _lib.tbg_encode_tiled(ctypes.byref(d), _enum(DTYPES, dtype), int(rank), _vp(int(global_address)),
+                               _arr(ctypes.c_uint64, global_dim), strides, _arr(ctypes.c_uint32, box_dim),
+                               _arr(ctypes.c_uint32, element_strides), _enum(SWIZZLES, swizzle), _enum(L2, l2),
+                               _enum(OOB, oob))
+    _check(st)
+    return d
+
+
+def encode_tiled_status(*args, **kwargs) -> int:
+    """Like encode_tiled but returns the status code instead of raising."""
+    try:
+        encode_tiled(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
+
+
+def box_bytes(desc: TensorDesc) -> int:
+    return int(_lib.tbg_box_bytes(ctypes.byref(desc)))
+
+
+def tiled_copy(desc: TensorDesc, coords: Sequence[int], dst_image: int, stream: Optional[int] = None) -> None:
+    _check(_lib.tbg_tiled_copy(ctypes.byref(desc), _arr(ctypes.c_int32, coords), _vp(int(dst_image)),
+                               _vp(stream or 0)))
+
+
+def tiled_copy_many(desc: TensorDesc, coords_dev: int, n: int, dst_images: int, stream: Optional[int] = None) -> None:
+    _check(_lib.tbg_tiled_copy_many(ctypes.byref(desc), _vp(int(coords_dev)), int(n), _vp(int(dst_images)),
+                                    _vp(stream or 0)))
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int, lda: int, ldb: int, b_layout="kn") -> int:
+    return int(_lib.tbg_gemm_workspace_bytes(M, N, K, lda, ldb, _enum(B_LAYOUTS, b_layout)))
+
+
+def gemm(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C: int, ldc: int, c_dtype,
+         workspace: int = 0, workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
+    """tbg_gemm: C = A·B (bf16 in, fp32 accumulate, fp32 or bf16 out) on `stream`."""
+    _check(_lib.tbg_gemm(M, N, K, _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout), _vp(int(C)), ldc,
+                         _enum(DTYPES, c_dtype), _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_status(*args, **kwargs) -> int:
+    """Like gemm but returns the status code instead of raising."""
+    try:
+        gemm(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
+
+
+def declared_functions() -> list:
+    """Names of the functions include/tbg.h declares (used to check the library's exports)."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tbg_[a-z_]+)\s*\(", text)))
+
+
+def library_path() -> str:
+    return LIB_PATH

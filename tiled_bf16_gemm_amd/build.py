@@ -1,0 +1,61 @@
+"""Build ``libtbg.so`` (the C-ABI library) from ``csrc/*.hip`` with hipcc, for gfx950 only.
+
+Run ``python -m tiled_bf16_gemm_amd.build`` (or ``__graft_entry__.build()``).  The library is
+built in-tree next to this file.  ``TBG_SAVE_ISA=<dir>`` also writes the device assembly there.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libtbg.so")
+
+
+def hipcc() -> str:
+    cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    return cand
+
+
+def flags():
+    return [
+        "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
+        # no packed fp32 arithmetic anywhere in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC,
+    ]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(out: str = LIB, verbose: bool = False) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *flags(), "-shared", *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    isa_dir = os.environ.get("TBG_SAVE_ISA")
+    if isa_dir:
+        save_isa(isa_dir)
+    return out
+
+
+def save_isa(out_dir: str) -> None:
+    os.makedirs(out_dir, exist_ok=True)
+    for src in sources():
+        name = os.path.splitext(os.path.basename(src))[0]
+        subprocess.run([hipcc(), *flags(), "--offload-device-only", "-S", src, "-o",
+                        os.path.join(out_dir, name + ".s")], check=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,345 @@
+// The C ABI (include/tbg.h): argument validation, descriptor encoding, operand packing and
+// kernel dispatch.  Everything here runs on the host; kernels are enqueued on the caller's
+// stream and never waited for.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <string>
+
+#include "launch.hpp"
+#include "tbg.h"
+#include "tbg_desc.hpp"
+
+
+using tbg::DescImpl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tbg_status fail(tbg_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tbg_status fail(tbg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+int elsize_of(int dtype) {
+  switch (dtype) {
+    case TBG_U8: return 1;
+    case TBG_U16: case TBG_F16: case TBG_BF16: return 2;
+    case TBG_U32: case TBG_F32: return 4;
+    default: return 0;
+  }
+}
+
+uint32_t swizzle_span(int mode) {
+  switch (mode) {
+    case TBG_SWIZZLE_32B: return 32;
+    case TBG_SWIZZLE_64B: return 64;
+    case TBG_SWIZZLE_128B: case TBG_SWIZZLE_128B_2ROW: return 128;
+    default: return 0;
+  }
+}
+
+// A usable device: the current HIP device must be gfx950.  Checked once per device id.
+tbg_status check_device() {
+  int dev = -1;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(TBG_ERR_NO_DEVICE, "no HIP device is visible");
+  }
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TBG_ERR_NO_DEVICE, "hipGetDevice failed");
+  }
+  static std::mutex mu;
+  static int checked[64] = {0};  // 0 unknown, 1 ok, 2 wrong architecture
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0 || dev >= 64) return fail(TBG_ERR_NO_DEVICE, "device id %d out of range", dev);
+  if (checked[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(TBG_ERR_NO_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    }
+    checked[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (checked[dev] == 2) g_last_error = std::string("device is ") + prop.gcnArchName + ", not gfx950";
+  }
+  if (checked[dev] != 1) return fail(TBG_ERR_NO_DEVICE, "current device %d is not a gfx950 GPU", dev);
+  return TBG_OK;
+}
+
+bool valid_desc(const tbg_tensor_desc* d, const DescImpl** out) {
+  if (!d) return false;
+  const DescImpl* di = reinterpret_cast<const DescImpl*>(d);
+  if (di->magic != tbg::kDescMagic || di->rank < 1 || di->rank > tbg::kMaxRank || di->image_bytes == 0) return false;
+  *out = di;
+  return true;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tbg_status_string(tbg_status s) {
+  switch (s) {
+    case TBG_OK: return "TBG_OK";
+    case TBG_ERR_INVALID_VALUE: return "TBG_ERR_INVALID_VALUE";
+    case TBG_ERR_MISALIGNED: return "TBG_ERR_MISALIGNED";
+    case TBG_ERR_UNSUPPORTED: return "TBG_ERR_UNSUPPORTED";
+    case TBG_ERR_OUT_OF_RANGE: return "TBG_ERR_OUT_OF_RANGE";
+    case TBG_ERR_NO_DEVICE: return "TBG_ERR_NO_DEVICE";
+    case TBG_ERR_HIP: return "TBG_ERR_HIP";
+    default: return "TBG_ERR_UNKNOWN";
+  }
+}
+
+const char* tbg_last_error(void) { return g_last_error.c_str(); }
+
+tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank, const void* global_address,
+                            const uint64_t* global_dim, const uint64_t* global_strides, const uint32_t* box_dim,
+                            const uint32_t* element_strides, tbg_swizzle swizzle, tbg_l2_hint l2, tbg_oob_fill oob) {
+  if (!out) return fail(TBG_ERR_INVALID_VALUE, "out is NULL");
+  const int es = elsize_of(dtype);
+  if (es == 0) return fail(TBG_ERR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
+  if (rank < 1 || rank > (uint32_t)tbg::kMaxRank) return fail(TBG_ERR_UNSUPPORTED, "rank %u not in 1..5", rank);
+  if (!global_address) return fail(TBG_ERR_INVALID_VALUE, "global_address is NULL");
+  if (((uintptr_t)global_address) % 16 != 0)
+    return fail(TBG_ERR_MISALIGNED, "global_address %p is not a multiple of 16 bytes", global_address);
+  if (!global_dim || !box_dim || !element_strides || (rank > 1 && !global_strides))
+    return fail(TBG_ERR_INVALID_VALUE, "a per-dimension array is NULL");
+  if ((int)swizzle < TBG_SWIZZLE_NONE || (int)swizzle > TBG_SWIZZLE_128B_2ROW)
+    return fail(TBG_ERR_INVALID_VALUE, "unknown swizzle %d", (int)swizzle);
+  if ((int)l2 < TBG_L2_NONE || (int)l2 > TBG_L2_256B) return fail(TBG_ERR_INVALID_VALUE, "unknown l2 hint %d", (int)l2);
+  if ((int)oob != TBG_OOB_ZERO && (int)oob != TBG_OOB_NAN)
+    return fail(TBG_ERR_INVALID_VALUE, "unknown oob fill %d", (int)oob);
+  if (oob == TBG_OOB_NAN && !(dtype == TBG_F16 || dtype == TBG_BF16 || dtype == TBG_F32))
+    return fail(TBG_ERR_INVALID_VALUE, "NaN fill needs a floating-point element type");
+
+  DescImpl d;
+  memset(&d, 0, sizeof(d));
+  d.magic = tbg::kDescMagic;
+  d.dtype = (uint8_t)dtype;
+  d.elsize = (uint8_t)es;
+  d.rank = (uint8_t)rank;
+  d.swizzle = (uint8_t)swizzle;
+  d.oob = (uint8_t)oob;
+  d.l2 = (uint8_t)l2;
+  d.base = (uint64_t)(uintptr_t)global_address;
+  uint64_t image = (uint64_t)es;
+  for (int i = 0; i < tbg::kMaxRank; ++i) {
+    d.dim[i] = 1;
+    d.box[i] = 1;
+    d.n[i] = 1;
+    d.estr[i] = 1;
+    d.stride[i] = 0;
+  }
+  d.stride[0] = (uint64_t)es;
+  for (uint32_t i = 0; i < rank; ++i) {
+    if (global_dim[i] < 1 || global_dim[i] > (1ull << 32))
+      return fail(TBG_ERR_OUT_OF_RANGE, "global_dim[%u] = %llu not in 1..2^32", i, (unsigned long long)global_dim[i]);
+    if (box_dim[i] < 1 || box_dim[i] > tbg::kMaxBox)
+      return fail(TBG_ERR_OUT_OF_RANGE, "box_dim[%u] = %u not in 1..256", i, box_dim[i]);
+    if (element_strides[i] < 1 || element_strides[i] > tbg::kMaxEstride)
+      return fail(TBG_ERR_OUT_OF_RANGE, "element_strides[%u] = %u not in 1..8", i, element_strides[i]);
+    d.dim[i] = global_dim[i];
+    d.box[i] = (uint16_t)box_dim[i];
+    d.estr[i] = (uint8_t)element_strides[i];
+    d.n[i] = (uint16_t)((box_dim[i] + element_strides[i] - 1) / element_strides[i]);
+    image *= d.n[i];
+  }
+  for (uint32_t i = 1; i < rank; ++i) {
+    const uint64_t s = global_strides[i - 1];
+    if (s % 16 != 0)
+      return fail(TBG_ERR_MISALIGNED, "global_strides[%u] = %llu is not a multiple of 16 bytes", i - 1,
+                  (unsigned long long)s);
+    if (s == 0 || s >= (1ull << 40))
+      return fail(TBG_ERR_OUT_OF_RANGE, "global_strides[%u] = %llu not in 16..2^40", i - 1, (unsigned long long)s);
+    d.stride[i] = s;
+  }
+  if (image > tbg::kMaxImageBytes)
+    return fail(TBG_ERR_OUT_OF_RANGE, "box image of %llu bytes exceeds 64 KiB", (unsigned long long)image);
+  if (swizzle != TBG_SWIZZLE_NONE) {
+    const uint32_t span = swizzle_span(swizzle);
+    if ((uint64_t)box_dim[0] * es > span)
+      return fail(TBG_ERR_INVALID_VALUE, "swizzled box inner extent %u bytes exceeds the %u-byte span",
+                  (unsigned)(box_dim[0] * es), span);
+    if (image % span != 0)
+      return fail(TBG_ERR_INVALID_VALUE, "swizzled image of %llu bytes is not a multiple of the %u-byte span",
+                  (unsigned long long)image, span);
+  }
+  d.image_bytes = (uint32_t)image;
+  memcpy(out, &d, sizeof(d));
+  return TBG_OK;
+}
+
+size_t tbg_box_bytes(const tbg_tensor_desc* d) {
+  const DescImpl* di = nullptr;
+  if (!valid_desc(d, &di)) return 0;
+  return di->image_bytes;
+}
+
+tbg_status tbg_tiled_copy(const tbg_tensor_desc* d, const int32_t* coords, void* dst_image, void* stream) {
+  const DescImpl* di = nullptr;
+  if (!valid_desc(d, &di)) return fail(TBG_ERR_INVALID_VALUE, "not an encoded descriptor");
+  if (!coords || !dst_image) return fail(TBG_ERR_INVALID_VALUE, "coords or dst_image is NULL");
+  if (((uintptr_t)dst_image) % 16 != 0) return fail(TBG_ERR_MISALIGNED, "dst_image is not 16-byte aligned");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  hipError_t e = tbg::launch_tiled_copy(*di, coords, nullptr, 1, dst_image, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "tiled copy launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
+tbg_status tbg_tiled_copy_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n, void* dst_images,
+                               void* stream) {
+  const DescImpl* di = nullptr;
+  if (!valid_desc(d, &di)) return fail(TBG_ERR_INVALID_VALUE, "not an encoded descriptor");
+  if (n == 0) return TBG_OK;
+  if (!coords_dev || !dst_images) return fail(TBG_ERR_INVALID_VALUE, "coords_dev or dst_images is NULL");
+  if (((uintptr_t)dst_images) % 16 != 0) return fail(TBG_ERR_MISALIGNED, "dst_images is not 16-byte aligned");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  hipError_t e = tbg::launch_tiled_copy(*di, nullptr, coords_dev, n, dst_images, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "tiled copy launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxLd = (1ll << 22) - 1;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct PackPlan {
+  bool pack_a = false, pack_b = false;
+  int64_t kext = 0;
+  int64_t lda_p = 0, ldb_p = 0;
+  size_t a_bytes = 0, b_bytes = 0;
+};
+
+PackPlan plan_packs(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bl, bool a_aligned,
+                    bool b_aligned) {
+  PackPlan pl;
+  pl.kext = round_up(K, 8);
+  if (K == 0) return pl;
+  pl.pack_a = (lda % 8) != 0 || (K % 8) != 0 || !a_aligned;
+  if (bl == TBG_B_NK) pl.pack_b = (ldb % 8) != 0 || (K % 8) != 0 || !b_aligned;
+  else pl.pack_b = (ldb % 8) != 0 || !b_aligned;
+  if (pl.pack_a) {
+    pl.lda_p = pl.kext;
+    pl.a_bytes = (size_t)round_up(M * pl.lda_p * 2, 256);
+  }
+  if (pl.pack_b) {
+    if (bl == TBG_B_NK) {
+      pl.ldb_p = pl.kext;
+      pl.b_bytes = (size_t)round_up(N * pl.ldb_p * 2, 256);
+    } else {
+      pl.ldb_p = round_up(N, 8);
+      pl.b_bytes = (size_t)round_up(K * pl.ldb_p * 2, 256);
+    }
+  }
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, tbg_b_layout bl) {
+  if (M <= 0 || N <= 0 || K <= 0 || lda <= 0 || ldb <= 0) return 0;
+  PackPlan pl = plan_packs(M, N, K, lda, ldb, (int)bl, true, true);
+  return pl.a_bytes + pl.b_bytes;
+}
+
+tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                    tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(TBG_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
+                                          (long long)M, (long long)N, (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(TBG_ERR_UNSUPPORTED, "sizes must stay below 2^31");
+  if ((int)bl != TBG_B_KN && (int)bl != TBG_B_NK) return fail(TBG_ERR_INVALID_VALUE, "unknown b_layout %d", (int)bl);
+  if (c_dtype != TBG_F32 && c_dtype != TBG_BF16) return fail(TBG_ERR_INVALID_VALUE, "C must be TBG_F32 or TBG_BF16");
+  if (lda < (K > 0 ? K : 1)) return fail(TBG_ERR_INVALID_VALUE, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+  const int64_t ldb_min = bl == TBG_B_KN ? N : K;
+  if (ldb < (ldb_min > 0 ? ldb_min : 1))
+    return fail(TBG_ERR_INVALID_VALUE, "ldb=%lld below its minimum %lld", (long long)ldb, (long long)ldb_min);
+  if (ldc < (N > 0 ? N : 1)) return fail(TBG_ERR_INVALID_VALUE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+  if (lda > kMaxLd || ldb > kMaxLd || ldc > (1ll << 40))
+    return fail(TBG_ERR_UNSUPPORTED, "leading dimensions are limited to 2^22-1 elements");
+  if (M == 0 || N == 0) return TBG_OK;
+  if (!C) return fail(TBG_ERR_INVALID_VALUE, "C is NULL");
+  if (K > 0 && (!A || !B)) return fail(TBG_ERR_INVALID_VALUE, "A or B is NULL");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+
+  const bool a_aligned = ((uintptr_t)A % 16) == 0, b_aligned = ((uintptr_t)B % 16) == 0;
+  PackPlan pl = plan_packs(M, N, K, lda, ldb, (int)bl, a_aligned, b_aligned);
+  const size_t need = pl.a_bytes + pl.b_bytes;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(TBG_ERR_OUT_OF_RANGE, "workspace of %zu bytes needed to repack unaligned operands (have %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256 != 0) return fail(TBG_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* Ae = (const uint16_t*)A;
+  const uint16_t* Be = (const uint16_t*)B;
+  int64_t lda_e = lda, ldb_e = ldb;
+  hipError_t e = hipSuccess;
+  if (pl.pack_a) {
+    uint16_t* dst = (uint16_t*)workspace;
+    e = tbg::launch_pack((const uint16_t*)A, lda, M, K, dst, pl.lda_p, s);
+    if (e != hipSuccess) return fail(TBG_ERR_HIP, "pack A: %s", hipGetErrorString(e));
+    Ae = dst;
+    lda_e = pl.lda_p;
+  }
+  if (pl.pack_b) {
+    uint16_t* dst = (uint16_t*)((uint8_t*)workspace + pl.a_bytes);
+    if (bl == TBG_B_NK) e = tbg::launch_pack((const uint16_t*)B, ldb, N, K, dst, pl.ldb_p, s);
+    else e = tbg::launch_pack((const uint16_t*)B, ldb, K, N, dst, pl.ldb_p, s);
+    if (e != hipSuccess) return fail(TBG_ERR_HIP, "pack B: %s", hipGetErrorString(e));
+    Be = dst;
+    ldb_e = pl.ldb_p;
+  }
+  tbg::GemmParams p;
+  p.A = Ae;
+  p.B = Be;
+  p.C = C;
+  p.lda = lda_e;
+  p.ldb = ldb_e;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.kchunks = (int)(pl.kext / 8);
+  p.tiles_m = (int)((M + tbg::gemm_tile_m() - 1) / tbg::gemm_tile_m());
+  p.tiles_n = (int)((N + tbg::gemm_tile_n() - 1) / tbg::gemm_tile_n());
+  p.group_m = env_int("TBG_GROUP_M", 8);
+  if (p.group_m < 1) p.group_m = 1;
+  p.vec_store = (((uintptr_t)C) % 16 == 0) && (ldc % 4 == 0);
+  e = tbg::launch_gemm(p, (int)bl, c_dtype == TBG_BF16, s);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal layout of tbg_tensor_desc (128 bytes), shared by the host encoder and the kernels.
+//
+// The descriptor records what "2 · Le Tensor Memory Accelerator" §2.2 and "H100 · cuTensorMap"
+// §5 list: base address, rank (<= 5), elements per dimension, byte strides, the box, element
+// strides, the swizzle, the out-of-bounds fill and the element type.  The layout is this
+// library's own; only the information matches the pages.
+#pragma once
+#include <stdint.h>
+
+namespace tbg {
+
+constexpr uint32_t kDescMagic = 0x44474254u;  // "TBGD"
+constexpr int kMaxRank = 5;
+constexpr uint32_t kMaxBox = 256;
+constexpr uint32_t kMaxEstride = 8;
+constexpr uint64_t kMaxImageBytes = 64u * 1024u;
+
+struct DescImpl {
+  uint32_t magic;
+  uint8_t dtype;     // tbg_dtype
+  uint8_t elsize;    // bytes per element: 1, 2 or 4
+  uint8_t rank;      // 1..5
+  uint8_t swizzle;   // tbg_swizzle
+  uint8_t oob;       // tbg_oob_fill
+  uint8_t l2;        // tbg_l2_hint (recorded, no effect)
+  uint8_t estr[5];   // element strides, 1..8 (unused dims: 1)
+  uint8_t pad0;
+  uint64_t base;          // device address of element (0, ..., 0)
+  uint64_t dim[5];        // elements per dimension, innermost first (unused dims: 1)
+  uint64_t stride[5];     // byte stride per dimension; stride[0] = elsize (unused dims: 0)
+  uint16_t box[5];        // traversal box in elements (unused dims: 1)
+  uint16_t n[5];          // copied elements per dimension, ceil(box / estr)
+  uint32_t image_bytes;   // elsize * prod(n)
+};
+static_assert(sizeof(DescImpl) == 128, "descriptor must stay 128 bytes");
+
+// Extension swizzle mode for gfx950's 64-bank LDS (see tbg.h): a[6:4] ^= a[10:8].
+constexpr int kSwizzle128B2Row = 4;
+
+}  // namespace tbg

@@ -1,0 +1,88 @@
+"""Torch-facing helpers over the C ABI: device memory and streams come from PyTorch, every step
+of the computation runs in the library's kernels.  Marshalling only."""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+import tiled_bf16_gemm_amd as tbg
+
+_TORCH_OF = {"u8": torch.uint8, "u16": torch.int16, "u32": torch.int32, "f16": torch.float16,
+             "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major view (unit inner stride)")
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str = "bf16",
+         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """C = A·B through tbg_gemm.  A: (M, K) bf16 view; B: (K, N) for "kn" or (N, K) for "nk".
+    Row strides become the leading dimensions.  `out` (M, N) may be a strided view."""
+    _require(A, "A")
+    _require(B, "B")
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    M, K = A.shape
+    if b_layout == "kn":
+        Kb, N = B.shape
+    else:
+        N, Kb = B.shape
+    if Kb != K:
+        raise ValueError(f"inner sizes differ: {K} vs {Kb}")
+    if out is None:
+        out = torch.empty((M, N), dtype=_TORCH_OF[out_dtype], device=A.device)
+    _require(out, "out")
+    lda, ldb, ldc = A.stride(0), B.stride(0), out.stride(0)
+    need = tbg.gemm_workspace_bytes(M, N, K, lda, ldb, b_layout)
+    if (A.data_ptr() % 16) or (B.data_ptr() % 16):
+        # an operand that starts off a 16-byte boundary is repacked too
+        rows_a, rows_b = M, (K if b_layout == "kn" else N)
+        kext = (K + 7) // 8 * 8
+        nb = (N + 7) // 8 * 8 if b_layout == "kn" else kext
+        need = ((rows_a * kext * 2 + 255) // 256 * 256) + ((rows_b * nb * 2 + 255) // 256 * 256)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    tbg.gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, out.data_ptr(), ldc, out_dtype,
+             ws_ptr, ws_bytes, stream_handle(stream))
+    return out
+
+
+def encode(t: torch.Tensor, dtype: str, dims: Sequence[int], strides_bytes: Sequence[int], box: Sequence[int],
+           estr: Sequence[int], swizzle: str = "none", oob: str = "zero", l2: str = "none") -> tbg.TensorDesc:
+    """Descriptor for the tensor whose element (0, ..., 0) is t's first element."""
+    return tbg.encode_tiled(dtype, len(dims), t.data_ptr(), dims, list(strides_bytes), box, estr, swizzle, l2, oob)
+
+
+def tiled_copy(desc: tbg.TensorDesc, coords: Sequence[int], out: Optional[torch.Tensor] = None,
+               device="cuda", stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    nbytes = tbg.box_bytes(desc)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    tbg.tiled_copy(desc, coords, out.data_ptr(), stream_handle(stream))
+    return out
+
+
+def tiled_copy_many(desc: tbg.TensorDesc, coords: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """coords: (n, rank) int32 CUDA tensor.  Returns n images of box_bytes each (uint8, flat)."""
+    if coords.dtype != torch.int32 or not coords.is_cuda or not coords.is_contiguous():
+        raise ValueError("coords must be a contiguous int32 CUDA tensor")
+    n = coords.shape[0]
+    nbytes = tbg.box_bytes(desc)
+    if out is None:
+        out = torch.empty(n * nbytes, dtype=torch.uint8, device=coords.device)
+    tbg.tiled_copy_many(desc, coords.data_ptr(), n, out.data_ptr(), stream_handle(stream))
+    return out
