@@ -1,0 +1,286 @@
+"""Benchmark of the bf16 GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+
+A step is one tbg_gemm call on the 8192³ workload (bf16 A row-major, B row-major K×N, fp32
+accumulation, bf16 out): host-side descriptor encoding, the tiled copies into LDS, the MFMA
+main loop and the masked epilogue, with operands already resident in HBM.  W untimed steps,
+then K timed steps bracketed by device synchronisation; one JSON line is printed.
+
+Also reported in the same line:
+  roofline      the GEMM kernel against the bf16 dense MFMA peak: algorithmic flops per launch
+                (2MNK) over the average launch time from HIP events on the launch stream;
+                `traffic` is the HBM bytes per launch from the committed rocprofv3 counter
+                summary when it was taken on the current kernel source, else null.
+  cpu_baseline  the CPU oracle on a bounded sample of the same product (the first rows of C),
+                timed on this host's cores.
+  per_config    TFLOP/s and % of peak on all five workloads (timed the same way, fewer steps).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz ("2.5 PF")
+METRIC = "bf16 GEMM TFLOP/s and % of MI355X MFMA peak at M=N=K=8192, 1 GPU"
+KERNEL_SOURCES = ["tiled_bf16_gemm_amd/csrc/gemm_kernel.hip", "tiled_bf16_gemm_amd/csrc/tile_loader.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_8192_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_gemm(torch, torch_ops, w, steps, warmup):
+    """Returns (ms per step over the whole timed region, mean per-launch ms from events)."""
+    import workloads
+    A, B = workloads.gemm_inputs(w)
+    lda, ldb, ldc = w.lds()
+    A = A.cuda()
+    B = B.cuda()
+    Av = A[:, :w.K]
+    Bv = B[:, :w.N] if w.b_layout == "kn" else B[:, :w.K]
+    C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
+    import tiled_bf16_gemm_amd as tbg
+    need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    region = starts[0].elapsed_time(ends[-1])
+    del A, B, C, ws
+    return region / steps, sum(per) / len(per), wall_ms / steps
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The oracle on the first rows of the product; grows the sample until it takes ~target_s."""
+    import oracle
+    import workloads
+    orc = oracle.get()
+    A, B = workloads.gemm_inputs(w)
+    Ab, Bb = workloads.bits(A), workloads.bits(B)
+    lda, ldb, _ = w.lds()
+    threads = orc.max_threads()
+    rows = 8
+    t = orc.gemm  # noqa
+    t0 = time.perf_counter()
+    orc.gemm(Ab, Bb, w.M, w.N, w.K, lda, ldb, w.b_layout, rows=(0, rows), threads=threads)
+    dt = time.perf_counter() - t0
+    rows2 = max(rows, min(w.M, int(rows * target_s / max(dt, 1e-3))))
+    rows2 = max(threads, (rows2 // threads) * threads)
+    t0 = time.perf_counter()
+    orc.gemm(Ab, Bb, w.M, w.N, w.K, lda, ldb, w.b_layout, rows=(0, rows2), threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows2 * w.N * w.K
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows2 - 1} of the {w.M}x{w.N}x{w.K} product ({rows2}x{w.N}x{w.K} MACs, "
+                  f"binary64 accumulation), {dt:.1f} s on {threads} host threads",
+        "seconds": round(dt, 2),
+    }
+
+
+def counters_driver(torch, torch_ops, w):
+    """Fixed launches for counter collection: the GEMM, then a copy of known size."""
+    import workloads
+    A, B = workloads.gemm_inputs(w)
+    A = A.cuda()
+    B = B.cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        torch_ops.gemm(A, B, w.b_layout, w.out_dtype, out=C)
+    torch.cuda.synchronize()
+    src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("counters driver: 5 gemm launches (8192^3), 5 copies of 536870912 bytes", flush=True)
+
+
+def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str, commands: dict) -> dict:
+    """Write the short text summaries of rocprofv3 runs into profiles/ (and the traffic figure
+    bench.py reports).  Reads rocprofv3's SQLite output with the standard library only."""
+    import sqlite3
+    import statistics
+
+    def rows(db, q):
+        c = sqlite3.connect(db)
+        try:
+            return list(c.execute(q))
+        finally:
+            c.close()
+
+    gemm_name = "gemm_bf16_kernel"
+    top = rows(trace_db, "select name, total_calls, total_duration, average, percentage from top_kernels")
+    lines = ["# GEMM kernel trace, 8192^3 workload (bf16 in, fp32 accumulate, bf16 out)", "",
+             "Command (<repo> is the repository root on the GPU box):", "", "```", commands["trace"], "```", "",
+             "rocprofv3 kernel statistics (durations in microseconds):", "",
+             "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for name, calls, total, avg, pct in top:
+        lines.append(f"| `{name}` | {calls} | {total:.1f} | {avg:.3f} | {pct:.1f} |")
+    gemm_avg = [avg for name, _, _, avg, _ in top if gemm_name in name]
+    lines += ["", f"bench.py's HIP-event average for the same kernel: {commands.get('bench_kernel_us', 'n/a')} us."]
+    with open(os.path.join(out_dir, "gemm_8192_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(db, counter):
+        vals = {}
+        for name, value in rows(db, f"select kernel_name, value from counters_collection where counter_name = '{counter}'"):
+            vals.setdefault(name, []).append(value)
+        return vals
+
+    fetch = per_kernel(fetch_db, "FETCH_SIZE")
+    write = per_kernel(write_db, "WRITE_SIZE")
+    copy_bytes = 512 << 20
+    calib_f = [v for k, v in fetch.items() if "copyBuffer" in k][0]
+    calib_w = [v for k, v in write.items() if "copyBuffer" in k][0]
+    gemm_f = [v for k, v in fetch.items() if gemm_name in k][0]
+    gemm_w = [v for k, v in write.items() if gemm_name in k][0]
+    sf = copy_bytes / (statistics.median(calib_f) * 1024)
+    sw = copy_bytes / (statistics.median(calib_w) * 1024)
+    fb = statistics.median(gemm_f) * 1024 * sf
+    wb = statistics.median(gemm_w) * 1024 * sw
+    total = fb + wb
+    algo = 2 * 8192 * 8192 * 2 + 8192 * 8192 * 2
+    lines = ["# HBM traffic of the GEMM kernel, 8192^3 workload", "",
+             "Commands (one counter per run; <repo> is the repository root on the GPU box):", "", "```",
+             commands["fetch"], commands["write"], "```", "",
+             "Calibration: the same runs end with five device copies of 536870912 bytes (`__amd_rocclr_copyBuffer`)",
+             "that read and write exactly that many bytes; each counter is scaled by bytes/counter of that copy.", "",
+             "| kernel | counter | median KiB per dispatch | dispatches | scale | bytes per dispatch |",
+             "|---|---|---|---|---|---|",
+             f"| calibration copy | FETCH_SIZE | {statistics.median(calib_f):.1f} | {len(calib_f)} | {sf:.4f} | {copy_bytes} |",
+             f"| calibration copy | WRITE_SIZE | {statistics.median(calib_w):.1f} | {len(calib_w)} | {sw:.4f} | {copy_bytes} |",
+             f"| GEMM | FETCH_SIZE | {statistics.median(gemm_f):.1f} | {len(gemm_f)} | {sf:.4f} | {fb:.4g} |",
+             f"| GEMM | WRITE_SIZE | {statistics.median(gemm_w):.1f} | {len(gemm_w)} | {sw:.4f} | {wb:.4g} |", "",
+             f"HBM bytes per GEMM launch: {total:.4g} (algorithmic minimum A + B + C once: {algo:.4g}; "
+             f"ratio {total / algo:.2f}).",
+             f"Kernel source hash at collection: {kernel_source_hash()}"]
+    with open(os.path.join(out_dir, "gemm_8192_hbm_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    traffic = {"kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": round(total),
+               "fetch_bytes": round(fb), "write_bytes": round(wb), "fetch_scale": sf, "write_scale": sw,
+               "algorithmic_bytes": algo, "gemm_trace_avg_us": gemm_avg[0] if gemm_avg else None}
+    with open(os.path.join(out_dir, "gemm_8192_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    return traffic
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
+                         "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the GEMM shards across GPUs "
+              "by rows or columns of C with no exchange, which this single-GPU build does not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_bf16_gemm_amd import torch_ops
+    import workloads
+
+    torch.cuda.set_device(0)
+    w = workloads.GEMMS["c4"]
+    if args.counters:
+        counters_driver(torch, torch_ops, w)
+        return
+    ms_step, ms_kernel, wall_ms = time_gemm(torch, torch_ops, w, args.steps, args.warmup)
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    achieved = w.flops / (ms_kernel * 1e-3) / 1e12
+
+    per_config = {}
+    if not args.no_configs:
+        for name in ("c1", "c2", "c3", "c5"):
+            cw = workloads.GEMMS[name]
+            s, k, _ = time_gemm(torch, torch_ops, cw, 20, 5)
+            tf = cw.flops / (s * 1e-3) / 1e12
+            per_config[name] = {"M": cw.M, "N": cw.N, "K": cw.K, "b_layout": cw.b_layout, "out": cw.out_dtype,
+                                "ms": round(s, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+            torch.cuda.empty_cache()
+        per_config["c4"] = {"M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "out": w.out_dtype,
+                            "ms": round(ms_step, 5), "tflops": round(tflops, 2),
+                            "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": "gemm M=N=K=8192, A bf16 row-major, B bf16 row-major KxN, uniform[-1,1] "
+                               "(seeds 4001/4002), fp32 accumulate, bf16 out",
+                   "M": w.M, "N": w.N, "K": w.K, "global_batch": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(),
+            "kernel_ms": round(ms_kernel, 5),
+            "flops_per_launch": w.flops,
+        },
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
