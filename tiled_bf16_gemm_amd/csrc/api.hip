@@ -336,7 +336,7 @@ tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
   p.tiles_n = (int)((N + tbg::gemm_tile_n() - 1) / tbg::gemm_tile_n());
   p.group_m = env_int("TBG_GROUP_M", 8);
   if (p.group_m < 1) p.group_m = 1;
-  p.vec_store = (((uintptr_t)C) % 16 == 0) && (ldc % 4 == 0);
+  p.vec_store = (((uintptr_t)C) % 16 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
   e = tbg::launch_gemm(p, (int)bl, c_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;

@@ -21,8 +21,8 @@
 //  * fragments come from LDS with ds_read_b128 (k-contiguous rows) or, for B stored K×N, with
 //    ds_read_b64_tr_b16, which transposes 4×16 blocks of 16-bit values across 16 lanes;
 //  * v_mfma_f32_16x16x32_bf16 with the operands swapped (B fragment first), so each lane ends
-//    with four consecutive columns of one row of C, which the epilogue stores as one 8- or
-//    16-byte write, masked at the M and N edges;
+//    with four consecutive columns of one row of C; the epilogue regroups them through LDS into
+//    whole-row 16-byte stores, masked at the M and N edges;
 //  * workgroup ids are remapped so that the tiles resident on one XCD (ids are dealt round-robin
 //    over the 8 XCDs) form a compact group of tile-rows and share operand tiles in that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -37,6 +37,7 @@ namespace tbg {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
@@ -301,39 +302,80 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmParams p) {
   // The loop's last product ends with the drain wait states (mfma16<true>): the accumulators
   // are now safe to read.
 
-  // ---- epilogue: lane holds C[m][n..n+3] for m = .. + (lane & 15), n = .. + 4*(lane >> 4) -------
-  const int gm0 = m0 + wm * kTM + (lane & 15);
-  const int gn0 = n0 + wn * kTN + 4 * (lane >> 4);
+  // ---- epilogue: C leaves through LDS as whole rows ------------------------------------------
+  // A lane holds C[m][n..n+3] of each fragment, so storing fragments directly writes 16 rows ×
+  // 32 bytes per instruction.  Instead each wave parks its 128×128 block in its own quarter of
+  // the (now idle) ring, then reads it back as 16-byte pieces of whole rows: a store instruction
+  // writes four (bf16) or two (fp32) rows of 256 contiguous bytes, whole cache lines.  The LDS
+  // image keeps 16-byte chunks whole and XORs the chunk index with (row & 15), so both the
+  // fragment writes (16 rows at one logical chunk) and the row reads (16 chunks of one row) fall
+  // on 16 distinct 16-byte bank groups.  Whole-row stores are non-temporal: C is written once and
+  // not read again here, so it should not push operand tiles out of the caches.  The ring is
+  // drained first: the last iteration's masked copies still write zeros into a stage, and the
+  // other waves may still read their fragments.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint8_t* park = smem + wave * 32768;
+  const int row0 = m0 + wm * kTM, col0 = n0 + wn * kTN;
+  if (OUT == 1) {
 #pragma unroll
-  for (int fm = 0; fm < kFM; ++fm) {
-    const int gm = gm0 + 16 * fm;
-    if (gm >= p.M) continue;
+    for (int fm = 0; fm < kFM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < kFN; ++fn) {
-      const int gn = gn0 + 16 * fn;
-      const f32x4_t v = acc[fn][fm];
-      if (OUT == 0) {
-        float* row = (float*)p.C + (uint64_t)gm * p.ldc;
-        if (p.vec_store && gn + 3 < p.N) {
-          *(f32x4_t*)(row + gn) = v;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (gn + r < p.N) row[gn + r] = v[r];
-        }
-      } else {
-        __bf16* row = (__bf16*)p.C + (uint64_t)gm * p.ldc;
+      for (int fn = 0; fn < kFN; ++fn) {
+        const int r = 16 * fm + (lane & 15);
+        const int c = 2 * fn + (lane >> 5);
         bf16x4_t h;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = (__bf16)v[r];
+        for (int e = 0; e < 4; ++e) h[e] = (__bf16)acc[fn][fm][e];
+        *(bf16x4_t*)(park + r * 256 + ((c ^ (r & 15)) << 4) + ((lane >> 4) & 1) * 8) = h;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int r = 4 * i + (lane >> 4), c = lane & 15;
+      const uint4 v = *(const uint4*)(park + r * 256 + ((c ^ (r & 15)) << 4));
+      const int gm = row0 + r, gn = col0 + 8 * c;
+      if (gm >= p.M) continue;
+      __bf16* dst = (__bf16*)p.C + (uint64_t)gm * p.ldc + gn;
+      if (p.vec_store && gn + 7 < p.N) {
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)dst);
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gn + e < p.N) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  } else {
+    // fp32: 64 KiB per wave, parked in two halves of 64 rows.
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int f = 0; f < kFM / 2; ++f)
+#pragma unroll
+        for (int fn = 0; fn < kFN; ++fn) {
+          const int r = 16 * f + (lane & 15);
+          const int c = 4 * fn + (lane >> 4);
+          *(f32x4_t*)(park + r * 512 + ((c ^ (r & 15)) << 4)) = acc[fn][half * (kFM / 2) + f];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int r = 2 * i + (lane >> 5), c = lane & 31;
+        const f32x4_t v = *(const f32x4_t*)(park + r * 512 + ((c ^ (r & 15)) << 4));
+        const int gm = row0 + 64 * half + r, gn = col0 + 4 * c;
+        if (gm >= p.M) continue;
+        float* dst = (float*)p.C + (uint64_t)gm * p.ldc + gn;
         if (p.vec_store && gn + 3 < p.N) {
-          *(bf16x4_t*)(row + gn) = h;
+          __builtin_nontemporal_store(v, (f32x4_t*)dst);
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (gn + r < p.N) row[gn + r] = h[r];
+          for (int e = 0; e < 4; ++e)
+            if (gn + e < p.N) dst[e] = v[e];
         }
       }
+      // The second half overwrites the same LDS: its writes follow this wave's reads in LDS
+      // order, and the reads' values are already in registers.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 }
@@ -391,3 +433,4 @@ int gemm_tile_m() { return kBM; }
 int gemm_tile_n() { return kBN; }
 
 }  // namespace tbg
+

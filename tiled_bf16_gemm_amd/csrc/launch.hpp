@@ -16,7 +16,7 @@ struct GemmParams {
   int M, N, K;
   int kchunks;     // 16-byte chunks along K present in memory (ceil(K/8)); data past K there is zero
   int tiles_m, tiles_n, group_m;
-  int vec_store;   // C rows allow whole 4-element stores
+  int vec_store;   // C and its rows are 16-byte aligned: whole 16-byte stores allowed
 };
 
 hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
