@@ -178,3 +178,48 @@ def test_degenerate_sizes(ops):
     C = ops.gemm(A[:1, :1], B[:1, :1], "kn", "f32")
     torch.cuda.synchronize()
     assert float(C[0, 0]) == float(A[0, 0].float() * B[0, 0].float())
+
+
+TILES = ["256x256", "256x128", "128x256", "128x128", "64x64"]
+
+
+@pytest.fixture
+def force_tile(request):
+    import os
+    old = os.environ.get("TBG_TILE")
+    os.environ["TBG_TILE"] = request.param
+    yield request.param
+    if old is None:
+        del os.environ["TBG_TILE"]
+    else:
+        os.environ["TBG_TILE"] = old
+
+
+@gpu
+@pytest.mark.parametrize("force_tile", TILES, indirect=True)
+def test_every_tile(ops, orc, force_tile):
+    """Each workgroup tile the library can pick, forced through TBG_TILE: ragged shapes against
+    the oracle (both B layouts, both output types, a padded ldc), and small-integer operands bit
+    for bit."""
+    cases = [(700, 520, 300, "kn", "f32"), (333, 190, 200, "nk", "bf16"), (130, 70, 1, "kn", "bf16"),
+             (64, 64, 64, "nk", "f32")]
+    for i, (M, N, K, bl, out) in enumerate(cases):
+        A = workloads.matrix(M, K, K, ("normal", 1.0), 300 + i)
+        B = workloads.matrix(K, N, N, ("normal", 1.0), 400 + i) if bl == "kn" else \
+            workloads.matrix(N, K, K, ("normal", 1.0), 400 + i)
+        ldc = N + 3
+        _say(f"tile {force_tile}: gemm M={M} N={N} K={K} {bl} {out} ldc={ldc}")
+        Cbuf = _run(ops, A, B, M, N, K, bl, out, ldc=ldc)
+        ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl)
+        got = _to_f32(Cbuf)
+        _check(got[:, :N], ref, f"tile {force_tile} case {i}")
+        assert np.all(np.isnan(got[:, N:])), "columns past N were written"
+    for M, N, K, bl in [(300, 257, 136, "kn"), (300, 257, 136, "nk")]:
+        rng = np.random.default_rng(M + N + K)
+        Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
+        shape_b = (K, N) if bl == "kn" else (N, K)
+        Bi = torch.from_numpy(rng.integers(-8, 9, shape_b).astype(np.float32)).to(torch.bfloat16)
+        _say(f"tile {force_tile}: integer gemm M={M} N={N} K={K} {bl}")
+        got = _to_f32(_run(ops, Ai, Bi, M, N, K, bl, "f32"))
+        ref = orc.gemm(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, shape_b[1], bl)
+        assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"

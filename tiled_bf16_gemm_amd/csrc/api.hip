@@ -51,8 +51,9 @@ uint32_t swizzle_span(int mode) {
   }
 }
 
-// A usable device: the current HIP device must be gfx950.  Checked once per device id.
-tbg_status check_device() {
+// A usable device: the current HIP device must be gfx950.  Checked once per device id, which
+// also records the device's compute-unit count (returned through num_cus when given).
+tbg_status check_device(int* num_cus = nullptr) {
   int dev = -1;
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
@@ -65,6 +66,7 @@ tbg_status check_device() {
   }
   static std::mutex mu;
   static int checked[64] = {0};  // 0 unknown, 1 ok, 2 wrong architecture
+  static int cus[64] = {0};
   std::lock_guard<std::mutex> lock(mu);
   if (dev < 0 || dev >= 64) return fail(TBG_ERR_NO_DEVICE, "device id %d out of range", dev);
   if (checked[dev] == 0) {
@@ -74,9 +76,11 @@ tbg_status check_device() {
       return fail(TBG_ERR_NO_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
     }
     checked[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cus[dev] = prop.multiProcessorCount;
     if (checked[dev] == 2) g_last_error = std::string("device is ") + prop.gcnArchName + ", not gfx950";
   }
   if (checked[dev] != 1) return fail(TBG_ERR_NO_DEVICE, "current device %d is not a gfx950 GPU", dev);
+  if (num_cus) *num_cus = cus[dev];
   return TBG_OK;
 }
 
@@ -289,7 +293,8 @@ tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
   if (M == 0 || N == 0) return TBG_OK;
   if (!C) return fail(TBG_ERR_INVALID_VALUE, "C is NULL");
   if (K > 0 && (!A || !B)) return fail(TBG_ERR_INVALID_VALUE, "A or B is NULL");
-  tbg_status st = check_device();
+  int num_cus = 0;
+  tbg_status st = check_device(&num_cus);
   if (st != TBG_OK) return st;
 
   const bool a_aligned = ((uintptr_t)A % 16) == 0, b_aligned = ((uintptr_t)B % 16) == 0;
@@ -332,12 +337,24 @@ tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
   p.N = (int)N;
   p.K = (int)K;
   p.kchunks = (int)(pl.kext / 8);
-  p.tiles_m = (int)((M + tbg::gemm_tile_m() - 1) / tbg::gemm_tile_m());
-  p.tiles_n = (int)((N + tbg::gemm_tile_n() - 1) / tbg::gemm_tile_n());
+  // Workgroup tile: chosen from the shape and the device, or forced by TBG_TILE="BMxBN" (one of
+  // 256x256, 256x128, 128x256, 128x128, 64x64) for measurements.
+  int bm = 256, bn = 256;
+  tbg::choose_tile(M, N, num_cus, bm, bn);
+  if (const char* tv = getenv("TBG_TILE")) {
+    int fm = 0, fn = 0;
+    if (sscanf(tv, "%dx%d", &fm, &fn) == 2 &&
+        ((fm == 256 && (fn == 256 || fn == 128)) || (fm == 128 && (fn == 256 || fn == 128)) || (fm == 64 && fn == 64))) {
+      bm = fm;
+      bn = fn;
+    }
+  }
+  p.tiles_m = 0;
+  p.tiles_n = 0;
   p.group_m = env_int("TBG_GROUP_M", 8);
   if (p.group_m < 1) p.group_m = 1;
   p.vec_store = (((uintptr_t)C) % 16 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
-  e = tbg::launch_gemm(p, (int)bl, c_dtype == TBG_BF16, s);
+  e = tbg::launch_gemm(p, bm, bn, (int)bl, c_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
 }

@@ -21,10 +21,11 @@ struct GemmParams {
 
 hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
                              void* dst, hipStream_t stream);
-hipError_t launch_gemm(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
+// Workgroup tile (bm × bn) for an M×N product on a device with num_cus compute units.
+void choose_tile(int64_t M, int64_t N, int num_cus, int& bm, int& bn);
+// Launch with tile bm × bn (256×256, 256×128, 128×256, 128×128 or 64×64); fills tiles_m/tiles_n.
+hipError_t launch_gemm(GemmParams p, int bm, int bn, int b_layout, int out_bf16, hipStream_t stream);
 hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ld_dst,
                        hipStream_t stream);
-int gemm_tile_m();
-int gemm_tile_n();
 
 }  // namespace tbg
