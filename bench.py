@@ -206,8 +206,8 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -237,7 +237,7 @@ def main():
     if not args.no_configs:
         for name in ("c1", "c2", "c3", "c5"):
             cw = workloads.GEMMS[name]
-            s, k, _ = time_gemm(torch, torch_ops, cw, 20, 5)
+            s, k, _ = time_gemm(torch, torch_ops, cw, 50, 50)
             tf = cw.flops / (s * 1e-3) / 1e12
             per_config[name] = {"M": cw.M, "N": cw.N, "K": cw.K, "b_layout": cw.b_layout, "out": cw.out_dtype,
                                 "ms": round(s, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
