@@ -59,6 +59,9 @@ class Oracle:
         lib.oracle_tiled_copy.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, _u64p, _u64p,
                                           _u32p, _u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           _i32p, ctypes.c_void_p]
+        lib.oracle_tiled_store.restype = ctypes.c_uint64
+        lib.oracle_tiled_store.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, _u64p, _u64p, _u32p,
+                                           _u32p, ctypes.c_int, _i32p, ctypes.c_void_p, ctypes.c_uint64]
         lib.oracle_gemm_rows.restype = None
         lib.oracle_gemm_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _u16p,
                                          ctypes.c_int64, _u16p, ctypes.c_int64, ctypes.c_int,
@@ -113,6 +116,30 @@ class Oracle:
         assert got == image
         return dst[:image]
 
+    def tiled_store(self, tensor: np.ndarray, dtype: str, dims: Sequence[int], strides_bytes: Sequence[int],
+                    box: Sequence[int], estr: Sequence[int], swizzle: str | int, coords: Sequence[int],
+                    image: np.ndarray) -> np.ndarray:
+        """Store one box image into ``tensor`` (raw bytes; dims innermost first): the other
+        direction of ``tiled_copy`` ("2 · Le Tensor Memory Accelerator" §2.5).  Returns a new
+        uint8 array; positions of the box outside the tensor are not written."""
+        elsize, _ = DTYPES[dtype]
+        rank = len(dims)
+        m = SWIZZLE_MODES[swizzle] if isinstance(swizzle, str) else int(swizzle)
+        out = np.array(np.ascontiguousarray(tensor).view(np.uint8).reshape(-1), copy=True)
+        img = np.ascontiguousarray(image).view(np.uint8).reshape(-1)
+        d = np.array(list(dims) + [1] * (5 - rank), dtype=np.uint64)
+        s = np.array(list(strides_bytes) + [0] * (5 - len(strides_bytes)), dtype=np.uint64)
+        b = np.array(list(box) + [1] * (5 - rank), dtype=np.uint32)
+        e = np.array(list(estr) + [1] * (5 - rank), dtype=np.uint32)
+        c = np.array(list(coords) + [0] * (5 - rank), dtype=np.int32)
+        got = self.lib.oracle_tiled_store(elsize, rank, out.ctypes.data, d.ctypes.data_as(_u64p),
+                                          s.ctypes.data_as(_u64p), b.ctypes.data_as(_u32p),
+                                          e.ctypes.data_as(_u32p), m, c.ctypes.data_as(_i32p),
+                                          img.ctypes.data, img.size)
+        if got == 0:
+            raise ValueError("oracle_tiled_store declined these arguments")
+        return out
+
     # -- O3 ---------------------------------------------------------------------------------
     def gemm(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, lda: int, ldb: int,
              b_layout: str = "kn", rows: Optional[tuple] = None, want64: bool = False,
@@ -133,6 +160,22 @@ class Oracle:
                                       out64.ctypes.data_as(_f64p) if want64 else None,
                                       out32.ctypes.data_as(_f32p), N, nthr, scratch.ctypes.data_as(_f64p))
         return (out32, out64) if want64 else out32
+
+    def gemm_ex(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, lda: int, ldb: int,
+                b_layout: str, alpha: float, beta: float, C_old: Optional[np.ndarray] = None,
+                rows: Optional[tuple] = None, threads: int = 0) -> np.ndarray:
+        """C <- alpha·A·B + beta·C, the general BLAS form the "GEMM" page's tensor-core section
+        gives for the matrix units.  alpha and beta are binary32 values; the sum S is gemm()'s
+        binary64 sum; alpha·S + beta·C_old is formed in binary64 and rounded once to binary32.
+        With beta == 0, C_old is not read (a NaN in it does not reach the result).  C_old: the
+        old C rows as float32 (bf16 values widen exactly)."""
+        _, s64 = self.gemm(A, B, M, N, K, lda, ldb, b_layout, rows=rows, want64=True, threads=threads)
+        a = float(np.float32(alpha))
+        b = float(np.float32(beta))
+        r = a * s64
+        if b != 0.0:
+            r = r + b * np.asarray(C_old, dtype=np.float64)
+        return r.astype(np.float32)
 
     def gemm_points(self, A: np.ndarray, B: np.ndarray, K: int, lda: int, ldb: int, ms, ns,
                     b_layout: str = "kn", want64: bool = False):

@@ -147,6 +147,61 @@ uint64_t oracle_tiled_copy(int elsize, int rank, const void* src, const uint64_t
 }
 
 /* ------------------------------------------------------------------------------------------
+ * O2s — tiled store, the other direction of the same copy.  [TMA] §2.5: the copy engine also
+ * moves shared memory to global memory, with the same descriptors (the store of a GEMM
+ * epilogue).  Box position j takes its value from the image at byte offset
+ * swizzle(elsize * lin(j)), exactly where a load of that box puts it, and goes to tensor
+ * coordinates coords[i] + j[i]*estr[i].
+ * Reading (pages silent on the store's edges): a position outside the tensor is not written —
+ * the fill of [MAP] §14 exists only on the load side, and a store never touches memory outside
+ * the tensor.
+ *   dst: the tensor's bytes (modified in place); image: image_len bytes.
+ * Returns the image size in bytes, or 0 on an argument this plain reference does not take.
+ * ---------------------------------------------------------------------------------------- */
+uint64_t oracle_tiled_store(int elsize, int rank, void* dst, const uint64_t* dims,
+                            const uint64_t* strides_bytes, const uint32_t* box, const uint32_t* estr,
+                            int swizzle, const int32_t* coords, const void* image, uint64_t image_len) {
+    if (rank < 1 || rank > 5 || (elsize != 1 && elsize != 2 && elsize != 4)) return 0;
+    uint64_t S[5], n[5], dim[5];
+    int64_t c[5];
+    for (int i = 0; i < 5; ++i) { S[i] = 0; n[i] = 1; dim[i] = 1; c[i] = 0; }
+    S[0] = (uint64_t)elsize;
+    for (int i = 1; i < rank; ++i) S[i] = strides_bytes[i - 1];
+    for (int i = 0; i < rank; ++i) {
+        if (estr[i] == 0) return 0;
+        n[i] = (box[i] + estr[i] - 1) / estr[i];
+        dim[i] = dims[i];
+        c[i] = coords[i];
+    }
+    uint64_t size = (uint64_t)elsize * n[0] * n[1] * n[2] * n[3] * n[4];
+    if (size > image_len) return 0;
+    if (swizzle != 0 && size % swizzle_span(swizzle) != 0) return 0;
+    const uint8_t* img = (const uint8_t*)image;
+    uint8_t* d = (uint8_t*)dst;
+
+    uint64_t j[5];
+    for (j[4] = 0; j[4] < n[4]; ++j[4])
+    for (j[3] = 0; j[3] < n[3]; ++j[3])
+    for (j[2] = 0; j[2] < n[2]; ++j[2])
+    for (j[1] = 0; j[1] < n[1]; ++j[1])
+    for (j[0] = 0; j[0] < n[0]; ++j[0]) {
+        int inside = 1;
+        uint64_t dst_off = 0;
+        for (int i = 0; i < rank; ++i) {
+            int64_t x = c[i] + (int64_t)j[i] * (int64_t)estr[i];
+            if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;
+            else dst_off += (uint64_t)x * S[i];
+        }
+        if (!inside) continue;
+        uint64_t lin = j[0] + n[0] * (j[1] + n[1] * (j[2] + n[2] * (j[3] + n[3] * j[4])));
+        uint64_t off = oracle_swizzle(lin * (uint64_t)elsize, swizzle);
+        if (off + (uint64_t)elsize > size) return 0;
+        memcpy(d + dst_off, img + off, (size_t)elsize);
+    }
+    return size;
+}
+
+/* ------------------------------------------------------------------------------------------
  * O3 — GEMM.  [GEMM] "Il conto": C = A·B, A (M,K), B (K,N), C (M,N), C_ij = Σ_k A_ik B_kj.
  * [GEMM] tensor-core section: 16-bit inputs, the sum kept in a wide format.  Here every
  * bf16·bf16 product is exact in binary64, the sum runs over k in ascending order in binary64,

@@ -243,6 +243,99 @@ def pin_fill_and_source(o):
         assert np.array_equal(src, before)
 
 
+def _store_case(o, dims, box, estr, coords, dtype, padded_rows=0):
+    """Store an image of distinct tags into a tensor of sentinels; every box position inside the
+    tensor must land at the coordinates it names, and nothing else may change."""
+    rank = len(dims)
+    elsize = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4}[dtype]
+    npdt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[elsize]
+    pitch = [elsize * (dims[0] + padded_rows)]
+    for i in range(2, rank):
+        pitch.append(pitch[-1] * dims[i - 1])
+    total = (pitch[-1] * dims[rank - 1]) // elsize if rank > 1 else dims[0]
+    sentinel = {1: 0xAB, 2: 0xABCD, 4: 0xABCDEF01}[elsize]
+    tensor = np.full(total, sentinel, dtype=npdt)
+    n = [(b + e - 1) // e for b, e in zip(box, estr)]
+    count = int(np.prod(n))
+    tags = ((np.arange(count, dtype=np.int64) % (sentinel - 1)) + 1).astype(npdt)  # never the sentinel
+    out = o.tiled_store(tensor, dtype, dims, pitch[:rank - 1], box, estr, "none", coords, tags).view(npdt)
+    want = tensor.copy()
+    jj = np.indices(n[::-1]).reshape(rank, -1)[::-1]
+    x = np.stack([coords[i] + jj[i] * estr[i] for i in range(rank)])
+    inside = np.all([(x[i] >= 0) & (x[i] < dims[i]) for i in range(rank)], axis=0)
+    lin = x[0].astype(np.int64)
+    for i in range(1, rank):
+        lin = lin + x[i].astype(np.int64) * (pitch[i - 1] // elsize)
+    want[lin[inside]] = tags[inside]
+    assert np.array_equal(out, want)
+
+
+def pin_store_decode(o):
+    """"2 · Le Tensor Memory Accelerator" §2.5, the store direction with the same descriptor:
+    brute-force index decoding of every box position, edges not written."""
+    rng = np.random.default_rng(17)
+    _store_case(o, [40, 9, 3], [16, 4, 2], [1, 2, 1], [32, -2, 1], "u16")
+    _store_case(o, [17, 5, 4, 3, 2], [8, 3, 2, 2, 2], [3, 1, 2, 1, 1], [-5, 3, 2, 2, 1], "f16")
+    _store_case(o, [33], [20], [4], [20], "f32")
+    _store_case(o, [64, 10], [64, 8], [1, 1], [-8, -4], "bf16", padded_rows=8)
+    for _ in range(40):
+        rank = int(rng.integers(1, 6))
+        dims = [int(rng.integers(1, 12)) for _ in range(rank)]
+        box = [int(rng.integers(1, 10)) for _ in range(rank)]
+        estr = [int(rng.integers(1, 9)) for _ in range(rank)]
+        coords = [int(rng.integers(-6, d + 3)) for d in dims]
+        dtype = ["u8", "u16", "u32", "f16", "bf16", "f32"][int(rng.integers(0, 6))]
+        _store_case(o, dims, box, estr, coords, dtype, padded_rows=int(rng.integers(0, 3)) * 8)
+
+
+def pin_store_hand_example(o):
+    """A 4×4 u16 tensor (row pitch 16 bytes after padding to 8 elements), box {2, 2} at (-1, 3):
+    of the four positions only j = (1, 0) is inside, at x = (0, 3)."""
+    t = np.zeros(4 * 8, dtype=np.uint16)
+    out = o.tiled_store(t, "u16", [4, 4], [16], [2, 2], [1, 1], "none", [-1, 3],
+                        np.array([10, 11, 12, 13], dtype=np.uint16)).view(np.uint16)
+    want = np.zeros(4 * 8, dtype=np.uint16)
+    want[3 * 8 + 0] = 11
+    assert np.array_equal(out, want)
+
+
+def pin_store_swizzle_and_roundtrip(o):
+    """A swizzled image stores like its unswizzled permutation (logical element k sits at image
+    byte swizzle(k)); storing an image and loading the same box back returns the image at the
+    positions inside the tensor and the fill elsewhere."""
+    rng = np.random.default_rng(23)
+    for swz, box0 in (("128B", 64), ("64B", 32), ("32B", 16), ("128B_2ROW", 64)):
+        dims, box, coords = [box0 + 8, 20], [box0, 16], [0, 7]
+        t = np.zeros((dims[1], dims[0]), dtype=np.uint16)
+        img = rng.integers(1, 60000, box0 * 16).astype(np.uint16)
+        out_s = o.tiled_store(t, "bf16", dims, [dims[0] * 2], box, [1, 1], swz, coords, img)
+        offs = np.arange(img.size * 2, dtype=np.uint64)
+        plain = img.view(np.uint8)[o.swizzle(offs, swz)]
+        out_p = o.tiled_store(t, "bf16", dims, [dims[0] * 2], box, [1, 1], "none", coords, plain)
+        assert np.array_equal(out_s, out_p), swz
+    for _ in range(30):
+        rank = int(rng.integers(1, 5))
+        dims = [int(rng.integers(1, 10)) for _ in range(rank)]
+        box = [int(rng.integers(1, 8)) for _ in range(rank)]
+        estr = [int(rng.integers(1, 4)) for _ in range(rank)]
+        coords = [int(rng.integers(-4, d + 2)) for d in dims]
+        strides = [2 * dims[0]]
+        for i in range(2, rank):
+            strides.append(strides[-1] * dims[i - 1])
+        total = int(np.prod(dims))
+        n = [(b + e - 1) // e for b, e in zip(box, estr)]
+        img = rng.integers(1, 60000, int(np.prod(n))).astype(np.uint16)
+        t = np.zeros(total, dtype=np.uint16)
+        stored = o.tiled_store(t, "u16", dims, strides[:rank - 1], box, estr, "none", coords, img)
+        back = o.tiled_copy(stored.view(np.uint16), "u16", dims, strides[:rank - 1], box, estr, "none", False,
+                            coords).view(np.uint16)
+        jj = np.indices(n[::-1]).reshape(rank, -1)[::-1]
+        inside = np.all([(coords[i] + jj[i] * estr[i] >= 0) & (coords[i] + jj[i] * estr[i] < dims[i])
+                         for i in range(rank)], axis=0)
+        assert np.array_equal(back[inside], img[inside])
+        assert np.all(back[~inside] == 0)
+
+
 # ---------------------------------------------------------------------------------------------
 # GEMM ("GEMM: la moltiplicazione di matrici sull'hardware")
 # ---------------------------------------------------------------------------------------------
@@ -358,6 +451,30 @@ def pin_f32_to_bf16(o):
     assert np.all(np.isnan(back))
 
 
+def pin_gemm_ex(o):
+    """C <- alpha·A·B + beta·C ("GEMM" page, tensor-core section: the BLAS form).  alpha = 1,
+    beta = 0 is the plain product; beta = 0 does not read C (NaN there stays out); alpha = 0 gives
+    beta·C; on small-integer operands the result is exact and equals integer arithmetic."""
+    rng = np.random.default_rng(31)
+    M, N, K = 7, 9, 13
+    A = _bits_of(rng.normal(size=(M, K)))
+    B = _bits_of(rng.normal(size=(K, N)))
+    plain = o.gemm(A, B, M, N, K, K, N, "kn")
+    assert np.array_equal(o.gemm_ex(A, B, M, N, K, K, N, "kn", 1.0, 0.0), plain)
+    nanC = np.full((M, N), np.nan, dtype=np.float32)
+    assert np.array_equal(o.gemm_ex(A, B, M, N, K, K, N, "kn", 1.0, 0.0, nanC), plain)
+    Cold = rng.normal(size=(M, N)).astype(np.float32)
+    assert np.array_equal(o.gemm_ex(A, B, M, N, K, K, N, "kn", 0.0, 0.5, Cold), Cold * np.float32(0.5))
+    Ai = rng.integers(-8, 9, (M, K))
+    Bi = rng.integers(-8, 9, (N, K))
+    Ci = rng.integers(-100, 101, (M, N))
+    got = o.gemm_ex(_bits_of(Ai.astype(np.float64)), _bits_of(Bi.astype(np.float64)), M, N, K, K, K, "nk", 2.0,
+                    -3.0, Ci.astype(np.float32))
+    want = 2 * (Ai @ Bi.T) - 3 * Ci
+    assert np.array_equal(got.astype(np.int64), want)
+
+
 ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_structure, pin_bank_spread,
-            pin_worked_descriptor, pin_copy_decode, pin_fill_and_source, pin_gemm_exact_rationals,
-            pin_gemm_closed_forms, pin_gemm_tiled_equals_direct, pin_f32_to_bf16]
+            pin_worked_descriptor, pin_copy_decode, pin_fill_and_source, pin_store_decode, pin_store_hand_example,
+            pin_store_swizzle_and_roundtrip, pin_gemm_exact_rationals, pin_gemm_closed_forms,
+            pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16]

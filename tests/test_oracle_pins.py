@@ -43,6 +43,11 @@ MUTANTS = [
     ("ties rounded up", "u += 0x7FFFu + lsb;", "u += 0x8000u;"),
     ("points use the wrong layout", "uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[n * ldb + k];",
      "uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[k * ldb + n];"),
+    ("store writes positions outside the tensor", "if (!inside) continue;", "if (0) continue;"),
+    ("store skips the swizzle", "uint64_t off = oracle_swizzle(lin * (uint64_t)elsize, swizzle);\n        if (off + (uint64_t)elsize > size)",
+     "uint64_t off = lin * (uint64_t)elsize;\n        if (off + (uint64_t)elsize > size)"),
+    ("store drops the element stride", "int64_t x = c[i] + (int64_t)j[i] * (int64_t)estr[i];\n            if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;\n            else dst_off",
+     "int64_t x = c[i] + (int64_t)j[i];\n            if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;\n            else dst_off"),
 ]
 
 
