@@ -126,6 +126,25 @@ tbg_status tbg_tiled_copy(const tbg_tensor_desc* d, const int32_t* coords, void*
 tbg_status tbg_tiled_copy_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n, void* dst_images,
                                void* stream);
 
+/* Store one box: the other direction of tbg_tiled_copy ([TMA] §2.5: the copy engine also moves
+ * shared memory to global memory, with the same descriptors, as a GEMM epilogue does).  Box
+ * position j takes the element at image byte offset swizzle(elsize * lin(j)), where a load of
+ * the same box puts it, and writes it at tensor coordinates coords[i] + j[i] * element_strides[i].
+ * Positions outside the tensor are not written (the fill mode applies to loads only; this
+ * reading is the library's, the pages do not describe the store's edges).  The image passes
+ * through LDS on its way to the tensor.
+ *   coords     [rank] signed int32 coordinates in host memory (negative values allowed).
+ *   src_image  device memory of tbg_box_bytes(d) bytes, 16-byte aligned; not modified.
+ * Returns INVALID_VALUE for null arguments or a bad descriptor, MISALIGNED for src_image,
+ * NO_DEVICE / HIP for runtime failures. */
+tbg_status tbg_tiled_store(const tbg_tensor_desc* d, const int32_t* coords, const void* src_image, void* stream);
+
+/* Store n boxes of the same descriptor: box b uses coords_dev[b*rank .. b*rank+rank-1] (device
+ * memory, int32) and reads its image at src_images + b * tbg_box_bytes(d).  n == 0 is a no-op.
+ * Boxes that overlap in the tensor are written in an unspecified order. */
+tbg_status tbg_tiled_store_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n,
+                                const void* src_images, void* stream);
+
 /* Workspace bytes tbg_gemm needs for these sizes, assuming A and B start on 16-byte
  * boundaries.  It is non-zero only when an operand has to be repacked first ([GEMM] section
  * "I tensor core", packing of a block into a contiguous area; "In pratica", 16-byte alignment of
@@ -149,6 +168,18 @@ size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, in
 tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                     tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* C <- alpha·A·B + beta·C, the general form of the BLAS product that [GEMM]'s tensor-core section
+ * gives for the matrix units.  Arguments, layouts, checks and workspace as tbg_gemm, plus:
+ *   alpha, beta  binary32 scalars.  The product's fp32 sum S is combined as alpha·S + beta·C_old
+ *                in binary32 and rounded once to C's type.
+ *   beta == 0    C is not read: whatever it holds (NaN included) does not reach the result.
+ *   alpha == 0   the product is skipped and A and B are not read (they may be NULL); C becomes
+ *                beta·C.
+ * tbg_gemm is tbg_gemm_ex with alpha = 1 and beta = 0. */
+tbg_status tbg_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* tbg_status_string(tbg_status s);

@@ -16,7 +16,8 @@ BASE = 0x7F00_0000_0000  # any 16-byte-aligned address: encoding never touches m
 def test_library_exports_every_declared_function():
     names = tbg.declared_functions()
     assert set(names) >= {"tbg_encode_tiled", "tbg_box_bytes", "tbg_tiled_copy", "tbg_tiled_copy_many",
-                          "tbg_gemm_workspace_bytes", "tbg_gemm", "tbg_status_string", "tbg_last_error"}
+                          "tbg_tiled_store", "tbg_tiled_store_many", "tbg_gemm_workspace_bytes", "tbg_gemm",
+                          "tbg_gemm_ex", "tbg_status_string", "tbg_last_error"}
     lib = ctypes.CDLL(tbg.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -146,3 +147,52 @@ def test_calls_without_a_device_fail_cleanly():
         tbg.tiled_copy(d, [0, 0], BASE + 8)
     assert e.value.status == tbg.ERR_MISALIGNED
     assert tbg.gemm_status(64, 64, 64, BASE, 64, BASE, 64, "kn", BASE, 64, "f32") == tbg.ERR_NO_DEVICE
+
+
+def _gemm_ex_status(**kw):
+    try:
+        tbg.gemm_ex(**kw)
+        return tbg.OK
+    except tbg.Error as e:
+        return e.status
+
+
+def test_gemm_ex_argument_errors():
+    """tbg_gemm_ex checks what tbg_gemm checks; alpha = 0 takes no operand (the product is skipped)."""
+    g = dict(M=64, N=64, K=64, alpha=2.0, A=BASE, lda=64, B=BASE, ldb=64, b_layout="kn", beta=0.5, C=BASE, ldc=64,
+             c_dtype="f32")
+    assert _gemm_ex_status(**{**g, "M": -1}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "lda": 63}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "ldc": 10}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "c_dtype": "u16"}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "b_layout": 7}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "A": 0}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "C": 0}) == tbg.ERR_INVALID_VALUE
+    assert _gemm_ex_status(**{**g, "N": 0, "C": 0}) == tbg.OK
+    import torch
+    if not torch.cuda.is_available():
+        # alpha = 0: null operands and any leading dimensions pass the host checks
+        st = _gemm_ex_status(**{**g, "alpha": 0.0, "A": 0, "B": 0, "lda": 0, "ldb": 0})
+        assert st == tbg.ERR_NO_DEVICE, tbg.last_error()
+
+
+def test_tiled_store_argument_errors():
+    d = tbg.encode_tiled(**_c1_args())
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_store(tbg.TensorDesc(), [0, 0], BASE)
+    assert e.value.status == tbg.ERR_INVALID_VALUE
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_store(d, [0, 0], 0)
+    assert e.value.status == tbg.ERR_INVALID_VALUE
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_store(d, [0, 0], BASE + 4)
+    assert e.value.status == tbg.ERR_MISALIGNED
+    tbg.tiled_store_many(d, 0, 0, 0)  # n == 0: nothing to do
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_store_many(d, 0, 3, BASE)
+    assert e.value.status == tbg.ERR_INVALID_VALUE
+    import torch
+    if not torch.cuda.is_available():
+        with pytest.raises(tbg.Error) as e:
+            tbg.tiled_store(d, [0, 0], BASE)
+        assert e.value.status == tbg.ERR_NO_DEVICE

@@ -186,3 +186,88 @@ def test_copy_is_deterministic_and_leaves_source(ops):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(src.view(torch.int16), before.view(torch.int16))
+
+
+# ---- store direction ("2 · Le Tensor Memory Accelerator" §2.5) -----------------------------------
+def _store_case(ops, orc, dtype, dims, strides, box, estr, swizzle, coords_list, many, seed):
+    """Store random images into a tensor of sentinel bytes on the GPU, one box after another (or
+    all at once), and compare every byte of the tensor with the oracle's stores."""
+    es = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4}[dtype]
+    rank = len(dims)
+    total_bytes = (strides[-1] * dims[-1]) if rank > 1 else dims[0] * es
+    rng = np.random.default_rng(seed)
+    d_tensor = torch.full((total_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    desc = ops.encode(d_tensor, dtype, dims, strides, box, estr, swizzle, "zero")
+    nb = tbg_box_bytes(desc)
+    images = rng.integers(0, 256, nb * len(coords_list), dtype=np.uint8)
+    d_images = torch.from_numpy(images).cuda()
+    if many:
+        d_coords = torch.tensor(coords_list, dtype=torch.int32, device="cuda")
+        ops.tiled_store_many(desc, d_coords, d_images)
+    else:
+        for b, c in enumerate(coords_list):
+            ops.tiled_store(desc, c, d_images[b * nb:(b + 1) * nb].clone())  # own, 16-byte aligned buffer
+    torch.cuda.synchronize()
+    want = np.full(total_bytes, 0xA5, dtype=np.uint8)
+    for b, c in enumerate(coords_list):
+        want = orc.tiled_store(want, dtype, dims, strides, box, estr, swizzle, c, images[b * nb:(b + 1) * nb])
+    got = d_tensor.cpu().numpy()
+    bad = int((got != want).sum())
+    assert bad == 0, f"{bad} tensor bytes differ"
+
+
+def tbg_box_bytes(desc):
+    import tiled_bf16_gemm_amd as tbg
+    return tbg.box_bytes(desc)
+
+
+@gpu
+def test_store_c1_and_c3_boxes(ops, orc):
+    _say("store: c1 box {64,128} bf16 128B swizzle, in bounds, overhanging and negative")
+    for c in ([0, 0], [64, 128], [224, 192], [-32, -64]):
+        _store_case(ops, orc, "bf16", [256, 256], [512], [64, 128], [1, 1], "128B", [c], False, 11)
+    _say("store: c3 5-D boxes {64,16,4,2,2}, element strides {1,2,1,1,1}, 432 boxes in one call")
+    coords = [[x, y, z, w, v] for v in (0, 2) for w in (0, 2, 4) for z in (0, 4) for y in range(0, 129, 16)
+              for x in (0, 64, 128, 192)]
+    assert len(coords) == 432
+    _store_case(ops, orc, "bf16", [200, 129, 7, 5, 3], [400, 51600, 361200, 1806000], [64, 16, 4, 2, 2],
+                [1, 2, 1, 1, 1], "none", coords, True, 12)
+
+
+@gpu
+def test_store_random_descriptors(ops, orc):
+    """Seeded random descriptors for the store: rank 1..5, every element type, element strides,
+    every swizzle the box allows, coordinates inside, overhanging and negative."""
+    rng = np.random.default_rng(4321)
+    types = ["u8", "u16", "u32", "f16", "bf16", "f32"]
+    done = 0
+    while done < 60:
+        dtype = types[int(rng.integers(0, len(types)))]
+        es = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4}[dtype]
+        rank = int(rng.integers(1, 6))
+        dims = [int(rng.integers(1, 40)) for _ in range(rank)]
+        pitch0 = ((dims[0] * es + 15) // 16) * 16 + 16 * int(rng.integers(0, 2))
+        strides = []
+        if rank > 1:
+            strides.append(pitch0)
+            for i in range(2, rank):
+                strides.append(strides[-1] * dims[i - 1])
+        box = [int(rng.integers(1, 17)) for _ in range(rank)]
+        estr = [int(rng.integers(1, 9)) for _ in range(rank)]
+        swizzle = "none"
+        span = {"32B": 32, "64B": 64, "128B": 128, "128B_2ROW": 128}
+        if rng.integers(0, 2):
+            swizzle = ["32B", "64B", "128B", "128B_2ROW"][int(rng.integers(0, 4))]
+            box[0] = max(1, span[swizzle] // es)
+            estr[0] = 1
+        n = [(b + e - 1) // e for b, e in zip(box, estr)]
+        image = es * int(np.prod(n))
+        if (swizzle != "none" and image % span[swizzle]) or image > 65536:
+            continue
+        coords = [[int(rng.integers(-10, d + 5)) for d in dims] for _ in range(3)]
+        many = bool(done % 2)
+        if many:
+            coords = coords[:1]  # one box per call: overlapping boxes are written in no set order
+        _say(f"random store {done}: {dtype} rank={rank} dims={dims} box={box} estr={estr} {swizzle}")
+        _store_case(ops, orc, dtype, dims, strides, box, estr, swizzle, coords, many, 100 + done)
+        done += 1

@@ -223,3 +223,62 @@ def test_every_tile(ops, orc, force_tile):
         got = _to_f32(_run(ops, Ai, Bi, M, N, K, bl, "f32"))
         ref = orc.gemm(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, shape_b[1], bl)
         assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"
+
+
+def _run_ex(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, alpha, beta, C_old):
+    """C_old: (M, ldc) CPU tensor of the output type; returns the GPU result buffer."""
+    A = A_cpu.cuda()[:, :K]
+    B = B_cpu.cuda()
+    B = B[:, :N] if b_layout == "kn" else B[:, :K]
+    Cbuf = C_old.clone().cuda()
+    ops.gemm(A, B, b_layout, out_dtype, out=Cbuf[:, :N], alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    return Cbuf
+
+
+@gpu
+@pytest.mark.parametrize("tile", ["auto", "256x256", "128x128", "64x64", "256x128"])
+def test_gemm_alpha_beta(ops, orc, tile):
+    """C <- alpha·A·B + beta·C against the oracle: both layouts and output types, beta = 0 with NaN
+    in C (C not read), alpha = 0 (the product skipped), and exact small-integer cases."""
+    import os
+    old_tile = os.environ.pop("TBG_TILE", None)
+    if tile != "auto":
+        os.environ["TBG_TILE"] = tile
+    try:
+        cases = [(700, 520, 300, "kn", "f32", 1.5, -0.75), (333, 190, 200, "nk", "bf16", 0.5, 2.0),
+                 (257, 129, 64, "kn", "bf16", -1.25, 0.0), (96, 80, 40, "nk", "f32", 0.0, 0.5),
+                 (64, 64, 0, "kn", "f32", 3.0, -2.0)]
+        for i, (M, N, K, bl, out, alpha, beta) in enumerate(cases):
+            A = workloads.matrix(M, K, K, ("normal", 1.0), 500 + i)
+            B = workloads.matrix(K, N, N, ("normal", 1.0), 600 + i) if bl == "kn" else \
+                workloads.matrix(N, K, K, ("normal", 1.0), 600 + i)
+            tdt = torch.float32 if out == "f32" else torch.bfloat16
+            ldc = N + 5
+            if beta == 0.0:
+                C_old = torch.full((M, ldc), float("nan"), dtype=tdt)
+            else:
+                C_old = torch.from_numpy(np.random.default_rng(700 + i).normal(size=(M, ldc)).astype(np.float32)).to(tdt)
+            _say(f"gemm_ex tile {tile}: M={M} N={N} K={K} {bl} {out} alpha={alpha} beta={beta}")
+            Cbuf = _run_ex(ops, A, B, M, N, K, bl, out, alpha, beta, C_old)
+            ref = orc.gemm_ex(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl, alpha, beta,
+                              C_old[:, :N].float().numpy())
+            got = _to_f32(Cbuf)
+            _check(got[:, :N], ref, f"gemm_ex case {i}")
+            assert np.array_equal(got[:, N:], C_old[:, N:].float().numpy(), equal_nan=True), "columns past N changed"
+            if alpha == 0.0:
+                want = (C_old[:, :N].float() * beta).to(tdt).float().numpy()
+                assert np.array_equal(got[:, :N], want), "alpha = 0 must give beta·C exactly"
+        # small integers: alpha·S + beta·C is exact in binary32, so the bits must match
+        M, N, K = 300, 257, 136
+        rng = np.random.default_rng(77)
+        Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
+        Bi = torch.from_numpy(rng.integers(-8, 9, (N, K)).astype(np.float32)).to(torch.bfloat16)
+        Ci = torch.from_numpy(rng.integers(-100, 101, (M, N)).astype(np.float32))
+        Cbuf = _run_ex(ops, Ai, Bi, M, N, K, "nk", "f32", 2.0, -3.0, Ci)
+        ref = orc.gemm_ex(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, K, "nk", 2.0, -3.0, Ci.numpy())
+        assert np.array_equal(_to_f32(Cbuf), ref)
+    finally:
+        os.environ.pop("TBG_TILE", None)
+        if old_tile is not None:
+            os.environ["TBG_TILE"] = old_tile

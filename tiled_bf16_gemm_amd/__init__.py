@@ -72,6 +72,13 @@ _lib.tbg_tiled_copy.argtypes = [ctypes.POINTER(TensorDesc), _i32p, _vp, _vp]
 _lib.tbg_tiled_copy_many.restype = ctypes.c_int
 _lib.tbg_tiled_copy_many.argtypes = [ctypes.POINTER(TensorDesc), _vp, ctypes.c_uint32, _vp, _vp]
 _lib.tbg_gemm_workspace_bytes.restype = ctypes.c_size_t
+_lib.tbg_tiled_store.restype = ctypes.c_int
+_lib.tbg_tiled_store.argtypes = [ctypes.POINTER(TensorDesc), _i32p, _vp, _vp]
+_lib.tbg_tiled_store_many.restype = ctypes.c_int
+_lib.tbg_tiled_store_many.argtypes = [ctypes.POINTER(TensorDesc), _vp, ctypes.c_uint32, _vp, _vp]
+_lib.tbg_gemm_ex.restype = ctypes.c_int
+_lib.tbg_gemm_ex.argtypes = [_i64, _i64, _i64, ctypes.c_float, _vp, _i64, _vp, _i64, ctypes.c_int, ctypes.c_float, _vp,
+                             _i64, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
 _lib.tbg_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int]
 _lib.tbg_gemm.restype = ctypes.c_int
 _lib.tbg_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, ctypes.c_int, _vp,
@@ -141,6 +148,16 @@ def tiled_copy_many(desc: TensorDesc, coords_dev: int, n: int, dst_images: int, 
                                     _vp(stream or 0)))
 
 
+def tiled_store(desc: TensorDesc, coords: Sequence[int], src_image: int, stream: Optional[int] = None) -> None:
+    _check(_lib.tbg_tiled_store(ctypes.byref(desc), _arr(ctypes.c_int32, coords), _vp(int(src_image)),
+                                _vp(stream or 0)))
+
+
+def tiled_store_many(desc: TensorDesc, coords_dev: int, n: int, src_images: int, stream: Optional[int] = None) -> None:
+    _check(_lib.tbg_tiled_store_many(ctypes.byref(desc), _vp(int(coords_dev)), int(n), _vp(int(src_images)),
+                                     _vp(stream or 0)))
+
+
 def gemm_workspace_bytes(M: int, N: int, K: int, lda: int, ldb: int, b_layout="kn") -> int:
     return int(_lib.tbg_gemm_workspace_bytes(M, N, K, lda, ldb, _enum(B_LAYOUTS, b_layout)))
 
@@ -150,6 +167,14 @@ def gemm(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C
     """tbg_gemm: C = A·B (bf16 in, fp32 accumulate, fp32 or bf16 out) on `stream`."""
     _check(_lib.tbg_gemm(M, N, K, _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout), _vp(int(C)), ldc,
                          _enum(DTYPES, c_dtype), _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_ex(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, beta: float, C: int,
+            ldc: int, c_dtype, workspace: int = 0, workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
+    """tbg_gemm_ex: C = alpha·A·B + beta·C on `stream`."""
+    _check(_lib.tbg_gemm_ex(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout),
+                            float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype), _vp(int(workspace)),
+                            int(workspace_bytes), _vp(stream or 0)))
 
 
 def gemm_status(*args, **kwargs) -> int:

@@ -226,6 +226,32 @@ tbg_status tbg_tiled_copy_many(const tbg_tensor_desc* d, const int32_t* coords_d
   return TBG_OK;
 }
 
+tbg_status tbg_tiled_store(const tbg_tensor_desc* d, const int32_t* coords, const void* src_image, void* stream) {
+  const DescImpl* di = nullptr;
+  if (!valid_desc(d, &di)) return fail(TBG_ERR_INVALID_VALUE, "not an encoded descriptor");
+  if (!coords || !src_image) return fail(TBG_ERR_INVALID_VALUE, "coords or src_image is NULL");
+  if (((uintptr_t)src_image) % 16 != 0) return fail(TBG_ERR_MISALIGNED, "src_image is not 16-byte aligned");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  hipError_t e = tbg::launch_tiled_store(*di, coords, nullptr, 1, src_image, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "tiled store launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
+tbg_status tbg_tiled_store_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n,
+                                const void* src_images, void* stream) {
+  const DescImpl* di = nullptr;
+  if (!valid_desc(d, &di)) return fail(TBG_ERR_INVALID_VALUE, "not an encoded descriptor");
+  if (n == 0) return TBG_OK;
+  if (!coords_dev || !src_images) return fail(TBG_ERR_INVALID_VALUE, "coords_dev or src_images is NULL");
+  if (((uintptr_t)src_images) % 16 != 0) return fail(TBG_ERR_MISALIGNED, "src_images is not 16-byte aligned");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  hipError_t e = tbg::launch_tiled_store(*di, nullptr, coords_dev, n, src_images, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "tiled store launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -275,13 +301,25 @@ size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, in
   return pl.a_bytes + pl.b_bytes;
 }
 
-tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                    tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// C = alpha·A·B + beta·C (scaled) or C = A·B.  With alpha == 0 the product is skipped: K is taken
+// as 0 and A, B and their leading dimensions are not looked at.
+tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, bool scaled) {
   if (M < 0 || N < 0 || K < 0) return fail(TBG_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                                           (long long)M, (long long)N, (long long)K);
-  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(TBG_ERR_UNSUPPORTED, "sizes must stay below 2^31");
   if ((int)bl != TBG_B_KN && (int)bl != TBG_B_NK) return fail(TBG_ERR_INVALID_VALUE, "unknown b_layout %d", (int)bl);
+  if (scaled && alpha == 0.f) {  // the empty product: nothing of A or B is used
+    K = 0;
+    A = B = nullptr;
+    lda = ldb = 1;
+    bl = TBG_B_NK;
+  }
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(TBG_ERR_UNSUPPORTED, "sizes must stay below 2^31");
   if (c_dtype != TBG_F32 && c_dtype != TBG_BF16) return fail(TBG_ERR_INVALID_VALUE, "C must be TBG_F32 or TBG_BF16");
   if (lda < (K > 0 ? K : 1)) return fail(TBG_ERR_INVALID_VALUE, "lda=%lld < K=%lld", (long long)lda, (long long)K);
   const int64_t ldb_min = bl == TBG_B_KN ? N : K;
@@ -354,9 +392,30 @@ tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
   p.group_m = env_int("TBG_GROUP_M", 8);
   if (p.group_m < 1) p.group_m = 1;
   p.vec_store = (((uintptr_t)C) % 16 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
+  p.alpha = alpha;
+  p.beta = beta;
+  p.scaled = scaled ? 1 : 0;
   e = tbg::launch_gemm(p, bm, bn, (int)bl, c_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                    tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return gemm_impl(M, N, K, 1.f, A, lda, B, ldb, bl, 0.f, C, ldc, c_dtype, workspace, workspace_bytes, stream, false);
+}
+
+tbg_status tbg_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const bool scaled = !(alpha == 1.f && beta == 0.f);
+  return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, workspace, workspace_bytes, stream,
+                   scaled);
 }
 
 }  // extern "C"

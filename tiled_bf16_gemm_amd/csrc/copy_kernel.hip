@@ -1,5 +1,6 @@
-// Tiled copy kernel: one workgroup per box; the box is built in LDS (the page's "shared memory"
-// destination) and then written out as a dense image so that it can be checked byte for byte.
+// Tiled copy kernels, one workgroup per box.  Load: the box is built in LDS (the page's "shared
+// memory" destination) and then written out as a dense image so that it can be checked byte for
+// byte.  Store: an image is brought into LDS and scattered into the box's tensor positions.
 //
 // "2 · Le Tensor Memory Accelerator" §2.2, §2.4, §2.5 and "H100 · cuTensorMap" §8, §9, §11, §14
 // define what a copy produces; this file decides how gfx950 produces it:
@@ -148,6 +149,113 @@ __global__ void __launch_bounds__(256) tiled_copy_kernel(DescImpl d, Coords5 hos
   } else {
     for (uint32_t i = threadIdx.x; i < nbytes; i += blockDim.x) out[i] = smem[i];
   }
+}
+
+// ---- store direction ("2 · Le Tensor Memory Accelerator" §2.5) -----------------------------
+__device__ __forceinline__ void global_store_elem(uint8_t* dst, const uint8_t* lds, uint32_t off, int elsize) {
+  if (elsize == 1) *dst = lds[off];
+  else if (elsize == 2) *(uint16_t*)dst = *(const uint16_t*)(lds + off);
+  else *(uint32_t*)dst = *(const uint32_t*)(lds + off);
+}
+
+// Scatter the LDS image of one box into the tensor: each position inside the tensor is written
+// from the image offset a load of the same box would fill; positions outside are skipped.
+// Whole 16-byte chunks go out as one store where the box row is chunk-aligned and the chunk
+// lies inside the tensor (the swizzle moves 16-byte units whole, so a chunk is contiguous in
+// the image too); ragged chunks and element-strided boxes go element by element.
+__device__ void scatter_box(const DescImpl& d, const int64_t* c, const uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int es = d.elsize;
+  const uint32_t row_bytes = (uint32_t)d.n[0] * es;
+  const bool chunked = d.estr[0] == 1 && (row_bytes % 16u) == 0 && ((c[0] * es) % 16) == 0;
+  if (!chunked) {
+    const uint64_t total = d.image_bytes / es;
+    for (uint64_t e = tid; e < total; e += blockDim.x) {
+      uint64_t rem = e;
+      bool inside = true;
+      uint64_t dst = d.base;
+      for (int i = 0; i < kMaxRank; ++i) {
+        const uint64_t ni = d.n[i];
+        const uint64_t j = rem % ni;
+        rem /= ni;
+        if (i < d.rank) {
+          const int64_t x = c[i] + (int64_t)j * (int64_t)d.estr[i];
+          if (x < 0 || (uint64_t)x >= d.dim[i]) inside = false;
+          else dst += (uint64_t)x * d.stride[i];
+        }
+      }
+      if (inside) global_store_elem((uint8_t*)dst, lds, swizzle_offset((uint32_t)(e * es), d.swizzle), es);
+    }
+    return;
+  }
+  const uint32_t chunks_per_row = row_bytes / 16u;
+  const int epc = 16 / es;
+  const uint32_t total_chunks = d.image_bytes / 16u;
+  for (uint32_t ch = tid; ch < total_chunks; ch += blockDim.x) {
+    const uint32_t row = ch / chunks_per_row;
+    const uint32_t cr = ch % chunks_per_row;
+    uint32_t rem = row;
+    bool row_inside = true;
+    uint64_t dst = d.base;
+    for (int i = 1; i < kMaxRank; ++i) {
+      const uint32_t ni = d.n[i];
+      const uint32_t j = rem % ni;
+      rem /= ni;
+      if (i < d.rank) {
+        const int64_t x = c[i] + (int64_t)j * (int64_t)d.estr[i];
+        if (x < 0 || (uint64_t)x >= d.dim[i]) row_inside = false;
+        else dst += (uint64_t)x * d.stride[i];
+      }
+    }
+    if (!row_inside) continue;
+    const int64_t x0 = c[0] + (int64_t)cr * epc;
+    const uint32_t off = swizzle_offset(ch * 16u, d.swizzle);
+    if (x0 >= 0 && (uint64_t)(x0 + epc) <= d.dim[0]) {
+      *(uint4*)(dst + (uint64_t)x0 * es) = *(const uint4*)(lds + off);
+    } else {
+      for (int q = 0; q < epc; ++q) {
+        const int64_t x = x0 + q;
+        if (x >= 0 && (uint64_t)x < d.dim[0]) global_store_elem((uint8_t*)(dst + (uint64_t)x * es), lds, off + q * es, es);
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) tiled_store_kernel(DescImpl d, Coords5 host_coords, const int32_t* coords_dev,
+                                                          const uint8_t* src, uint32_t box_offset) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const uint32_t b = blockIdx.x + box_offset;
+  int64_t c[kMaxRank];
+  for (int i = 0; i < kMaxRank; ++i) {
+    c[i] = 0;
+    if (i < d.rank) c[i] = coords_dev ? coords_dev[(uint64_t)b * d.rank + i] : host_coords.c[i];
+  }
+  const uint8_t* in = src + (uint64_t)b * d.image_bytes;
+  const uint32_t nbytes = d.image_bytes;
+  if ((((uintptr_t)in) % 16u) == 0 && (nbytes % 16u) == 0) {
+    for (uint32_t i = threadIdx.x; i < nbytes / 16u; i += blockDim.x) ((uint4*)smem)[i] = ((const uint4*)in)[i];
+  } else {
+    for (uint32_t i = threadIdx.x; i < nbytes; i += blockDim.x) smem[i] = in[i];
+  }
+  __syncthreads();
+  scatter_box(d, c, smem);
+}
+
+hipError_t launch_tiled_store(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
+                              const void* src, hipStream_t stream) {
+  Coords5 hc{};
+  if (host_coords)
+    for (int i = 0; i < d.rank; ++i) hc.c[i] = host_coords[i];
+  const size_t lds_bytes = ((size_t)d.image_bytes + 1023u) & ~(size_t)1023u;
+  const uint32_t kMaxGrid = 1u << 20;
+  for (uint32_t done = 0; done < n; done += kMaxGrid) {
+    const uint32_t cnt = (n - done) < kMaxGrid ? (n - done) : kMaxGrid;
+    hipLaunchKernelGGL(tiled_store_kernel, dim3(cnt), dim3(256), lds_bytes, stream, d, hc, coords_dev,
+                       (const uint8_t*)src, done);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Host launcher.  Returns the HIP error of the launch.

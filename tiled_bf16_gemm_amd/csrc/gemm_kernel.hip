@@ -201,15 +201,18 @@ __device__ __forceinline__ int park_xor(int r) {
 // so storing fragments directly would write 16 rows × 32 bytes per instruction.  Instead each
 // wave parks its block (in one or two bands of rows) in its own quarter of the now idle ring,
 // then reads it back as 16-byte pieces of whole rows, so every store instruction writes whole
-// row segments of TN elements.  Whole-row stores are non-temporal: C is written once and not
-// read again here, so it should not push operand tiles out of the caches.
-template <class T, int OUT>
+// row segments.  Whole-row stores are non-temporal: C is written once and not read again here,
+// so it should not push operand tiles out of the caches.  With SCALED the park keeps the fp32
+// sums and each piece becomes alpha·S + beta·C_old (C_old read only when beta != 0) before it is
+// rounded to C's type ("GEMM" page, tensor-core section: C <- alpha·A·B + beta·C).
+template <class T, int OUT, int SCALED>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], uint8_t* park, const GemmParams& p,
                                           int row0, int col0, int lane) {
-  constexpr int ES = OUT == 1 ? 2 : 4;
-  constexpr int RowBytes = T::TN * ES;
+  constexpr int ES = OUT == 1 ? 2 : 4;                     // element size of C
+  constexpr int PES = (OUT == 1 && !SCALED) ? 2 : 4;       // element size in the park
+  constexpr int RowBytes = T::TN * PES;
   constexpr int CPR = RowBytes / 16;
-  constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
+  constexpr int EPC = 16 / PES;  // elements per 16-byte park chunk
   constexpr int ParkBytes = T::RingBytes / 4;
   constexpr int Bands = (T::TM * RowBytes + ParkBytes - 1) / ParkBytes;
   constexpr int BandFM = T::FM / Bands;
@@ -225,7 +228,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], u
       for (int fn = 0; fn < T::FN; ++fn) {
         const int r = 16 * f + (lane & 15);
         const f32x4_t v = acc[fn][band * BandFM + f];
-        if (OUT == 1) {
+        if (PES == 2) {
           const int c = 2 * fn + (lane >> 5);
           bf16x4_t h;
 #pragma unroll
@@ -244,15 +247,67 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], u
       const int gm = row0 + BandRows * band + r, gn = col0 + EPC * c;
       if (gm >= p.M) continue;
       uint8_t* dst = (uint8_t*)p.C + ((uint64_t)gm * p.ldc + gn) * ES;
-      if (p.vec_store && gn + EPC - 1 < p.N) {
-        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)dst);
-      } else {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const bool whole = p.vec_store && gn + EPC - 1 < p.N;
+      if (!SCALED) {
+        if (whole) {
+          __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)dst);
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if (gn + e >= p.N) continue;
-          if (OUT == 1) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-          else ((uint32_t*)dst)[e] = w[e];
+          for (int e = 0; e < EPC; ++e) {
+            if (gn + e >= p.N) continue;
+            if (OUT == 1) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            else ((uint32_t*)dst)[e] = w[e];
+          }
+        }
+      } else {
+        // four fp32 sums per piece
+        float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+        float old[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.beta != 0.f) {
+          if (whole) {
+            if (OUT == 1) {
+              const uint2 o = *(const uint2*)dst;
+              old[0] = __uint_as_float(o.x << 16);
+              old[1] = __uint_as_float(o.x & 0xFFFF0000u);
+              old[2] = __uint_as_float(o.y << 16);
+              old[3] = __uint_as_float(o.y & 0xFFFF0000u);
+            } else {
+              const uint4 o = *(const uint4*)dst;
+              old[0] = __uint_as_float(o.x);
+              old[1] = __uint_as_float(o.y);
+              old[2] = __uint_as_float(o.z);
+              old[3] = __uint_as_float(o.w);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (gn + e >= p.N) continue;
+              old[e] = OUT == 1 ? __uint_as_float((uint32_t)((const uint16_t*)dst)[e] << 16) : ((const float*)dst)[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = p.beta != 0.f ? p.alpha * x[e] + p.beta * old[e] : p.alpha * x[e];
+        if (OUT == 1) {
+          bf16x4_t h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (__bf16)x[e];
+          if (whole) {
+            *(bf16x4_t*)dst = h;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < p.N) ((__bf16*)dst)[e] = h[e];
+          }
+        } else {
+          if (whole) {
+            *(f32x4_t*)dst = f32x4_t{x[0], x[1], x[2], x[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < p.N) ((float*)dst)[e] = x[e];
+          }
         }
       }
     }
@@ -261,7 +316,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], u
   }
 }
 
-template <int BM, int BN, int BL, int OUT>
+template <int BM, int BN, int BL, int OUT, int SCALED>
 __global__ void __launch_bounds__(kThreads, (TileCfg<BM, BN>::MinBlocks)) gemm_bf16_kernel(GemmParams p) {
   using T = TileCfg<BM, BN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::RingBytes];
@@ -409,7 +464,7 @@ __global__ void __launch_bounds__(kThreads, (TileCfg<BM, BN>::MinBlocks)) gemm_b
   // becomes the park: the last iteration's masked copies still write zeros into a stage, and the
   // other waves may still read their fragments.
   stage_barrier<0>();
-  store_tile<T, OUT>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
+  store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
 }
 
 // Copy `rows` rows of `cols` bf16 values into a buffer of pitch ld_dst (a multiple of 8),
@@ -447,18 +502,24 @@ hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int SCALED>
 static hipError_t launch_tile(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
   const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
   if (b_layout == 0 && !out_bf16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0, 0, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
   else if (b_layout == 0)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0, 1, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
   else if (!out_bf16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 0, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int BM, int BN>
+static hipError_t launch_tile(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
+  return p.scaled ? launch_tile<BM, BN, 1>(p, b_layout, out_bf16, stream)
+                  : launch_tile<BM, BN, 0>(p, b_layout, out_bf16, stream);
 }
 
 // Workgroup tile for an M×N problem on `num_cus` compute units.  Each candidate's cost is the

@@ -17,8 +17,12 @@ struct GemmParams {
   int kchunks;     // 16-byte chunks along K present in memory (ceil(K/8)); data past K there is zero
   int tiles_m, tiles_n, group_m;
   int vec_store;   // C and its rows are 16-byte aligned: whole 16-byte stores allowed
+  float alpha, beta;
+  int scaled;      // 0: C = A·B; 1: C = alpha·A·B + beta·C (C read only when beta != 0)
 };
 
+hipError_t launch_tiled_store(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
+                              const void* src, hipStream_t stream);
 hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
                              void* dst, hipStream_t stream);
 // Workgroup tile (bm × bn) for an M×N product on a device with num_cus compute units.

@@ -26,9 +26,10 @@ def _require(t: torch.Tensor, name: str):
 
 def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str = "bf16",
          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """C = A·B through tbg_gemm.  A: (M, K) bf16 view; B: (K, N) for "kn" or (N, K) for "nk".
-    Row strides become the leading dimensions.  `out` (M, N) may be a strided view."""
+         stream: Optional[torch.cuda.Stream] = None, alpha: float = 1.0, beta: float = 0.0) -> torch.Tensor:
+    """C = alpha·A·B + beta·C through tbg_gemm (alpha = 1, beta = 0) or tbg_gemm_ex.  A: (M, K)
+    bf16 view; B: (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading dimensions.
+    `out` (M, N) may be a strided view; with beta != 0 it must hold the old C."""
     _require(A, "A")
     _require(B, "B")
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -55,8 +56,12 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    tbg.gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, out.data_ptr(), ldc, out_dtype,
-             ws_ptr, ws_bytes, stream_handle(stream))
+    if alpha == 1.0 and beta == 0.0:
+        tbg.gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, out.data_ptr(), ldc, out_dtype,
+                 ws_ptr, ws_bytes, stream_handle(stream))
+    else:
+        tbg.gemm_ex(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, beta, out.data_ptr(), ldc,
+                    out_dtype, ws_ptr, ws_bytes, stream_handle(stream))
     return out
 
 
@@ -86,3 +91,22 @@ def tiled_copy_many(desc: tbg.TensorDesc, coords: torch.Tensor, out: Optional[to
         out = torch.empty(n * nbytes, dtype=torch.uint8, device=coords.device)
     tbg.tiled_copy_many(desc, coords.data_ptr(), n, out.data_ptr(), stream_handle(stream))
     return out
+
+
+def tiled_store(desc: tbg.TensorDesc, coords: Sequence[int], image: torch.Tensor,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Store one box image (a CUDA tensor of box_bytes bytes) into the descriptor's tensor."""
+    if not image.is_cuda or image.numel() * image.element_size() < tbg.box_bytes(desc):
+        raise ValueError("image must be a CUDA tensor of at least box_bytes bytes")
+    tbg.tiled_store(desc, coords, image.data_ptr(), stream_handle(stream))
+
+
+def tiled_store_many(desc: tbg.TensorDesc, coords: torch.Tensor, images: torch.Tensor,
+                     stream: Optional[torch.cuda.Stream] = None) -> None:
+    """coords: (n, rank) int32 CUDA tensor; images: n images of box_bytes each, back to back."""
+    if coords.dtype != torch.int32 or not coords.is_cuda or not coords.is_contiguous():
+        raise ValueError("coords must be a contiguous int32 CUDA tensor")
+    n = coords.shape[0]
+    if images.numel() * images.element_size() < n * tbg.box_bytes(desc):
+        raise ValueError("images holds fewer than n box images")
+    tbg.tiled_store_many(desc, coords.data_ptr(), n, images.data_ptr(), stream_handle(stream))
