@@ -181,6 +181,46 @@ tbg_status tbg_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const void*
                        int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Operand-copy pipeline of the GEMM ([PIPE] §1.3-§1.5: an S-stage ring in on-chip memory whose
+ * stages are filled by asynchronous copies while earlier stages are multiplied).
+ *   TBG_PIPE_RING      every compute wave copies its share of each stage; one workgroup barrier
+ *                      per K tile both publishes the next stage and frees the oldest one.
+ *   TBG_PIPE_PRODUCER  dedicated producer waves copy every stage ([TMA] §2.1: the copy is issued
+ *                      by one thread); the compute waves issue no copies.  Each stage has a full
+ *                      and an empty counter in LDS ([PIPE] §1.5: the two barriers per stage),
+ *                      polled with short sleeps.
+ *   TBG_PIPE_AUTO      the library's choice (currently the ring). */
+typedef enum { TBG_PIPE_AUTO = 0, TBG_PIPE_RING = 1, TBG_PIPE_PRODUCER = 2 } tbg_pipeline;
+
+/* Kernel configuration of tbg_gemm_configured.  Zero fields are left to the library.
+ *   tile_m, tile_n  workgroup tile of C ([GEMM] "Tiling"): both 0 (chosen from the shape), or
+ *                   one of 256x256, 256x128, 128x256, 128x128, 64x64.
+ *   stages          LDS stages of the ring: 0 (default, 2) or >= 2.  Each stage holds one
+ *                   tile_m x 64 block of A and one 64 x tile_n block of B in bf16, so the count
+ *                   is bounded by the 160 KiB of LDS.
+ *   pipeline        a tbg_pipeline value.
+ * Built configurations (tile / stages):
+ *   ring:      256x256/2; 256x128 and 128x256/2-3; 128x128/2-5; 64x64/2-6
+ *   producer:  256x128 and 128x256/2-3; 128x128/2-4; 64x64/2-6
+ * (the 256x256 tile needs every register of its four compute waves and leaves none for
+ * producer waves). */
+typedef struct {
+    int32_t tile_m, tile_n;
+    int32_t stages;
+    int32_t pipeline;
+} tbg_gemm_config;
+
+/* tbg_gemm_ex with an explicit kernel configuration; same arguments, layouts, results and checks,
+ * plus cfg (host memory, not retained).  Every configuration accumulates each C element over K in
+ * the same ascending order of 32-wide steps, so all configurations give bit-identical results.
+ * Returns INVALID_VALUE for a NULL cfg or a malformed field (unknown pipeline, only one tile
+ * size set, stages == 1 or negative) and UNSUPPORTED for a configuration that is not built (the
+ * detail lists the built ones); these checks come before any device check. */
+tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc,
+                               tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* tbg_status_string(tbg_status s);
 

@@ -196,3 +196,64 @@ def test_tiled_store_argument_errors():
         with pytest.raises(tbg.Error) as e:
             tbg.tiled_store(d, [0, 0], BASE)
         assert e.value.status == tbg.ERR_NO_DEVICE
+
+
+# Every configuration tbg.h lists as built, and some it does not.
+BUILT_CONFIGS = ([("ring", "256x256", 2)] + [("ring", t, s) for t in ("256x128", "128x256") for s in (2, 3)]
+                 + [("ring", "128x128", s) for s in (2, 3, 4, 5)] + [("ring", "64x64", s) for s in range(2, 7)]
+                 + [("producer", t, s) for t in ("256x128", "128x256") for s in (2, 3)]
+                 + [("producer", "128x128", s) for s in (2, 3, 4)] + [("producer", "64x64", s) for s in range(2, 7)])
+NOT_BUILT = [("ring", "256x256", 3), ("producer", "256x256", 2), ("ring", "128x128", 6), ("producer", "128x128", 5),
+             ("ring", "64x64", 7), ("ring", "96x96", 2), ("ring", "128x64", 2), ("producer", "64x64", 9)]
+
+
+def test_gemm_configured_checks():
+    """tbg_gemm_configured: malformed configurations are INVALID_VALUE, configurations that are not
+    built are UNSUPPORTED, both before any device check; built ones pass the host checks."""
+    import torch
+    g = dict(M=64, N=64, K=64, alpha=1.0, A=BASE, lda=64, B=BASE, ldb=64, b_layout="kn", beta=0.0, C=BASE, ldc=64,
+             c_dtype="f32")
+    assert tbg.gemm_configured_status(**g, config=None) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_configured_status(**g, config=tbg.GemmConfig(0, 0, 0, 7)) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_configured_status(**g, config=tbg.GemmConfig(128, 0, 0, 1)) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_configured_status(**g, config=tbg.GemmConfig(128, 128, 1, 1)) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_configured_status(**g, config=tbg.GemmConfig(128, 128, -2, 1)) == tbg.ERR_INVALID_VALUE
+    for pipe, tile, st in NOT_BUILT:
+        s = tbg.gemm_configured_status(**g, config=tbg.gemm_config(tile, st, pipe))
+        assert s == tbg.ERR_UNSUPPORTED, (pipe, tile, st, tbg.status_string(s))
+        assert "built:" in tbg.last_error()
+    # the usual argument checks still apply
+    cfg = tbg.gemm_config("128x128", 2, "ring")
+    assert tbg.gemm_configured_status(**{**g, "lda": 63}, config=cfg) == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_configured_status(**{**g, "M": 0}, config=cfg) == tbg.OK
+    if not torch.cuda.is_available():
+        for pipe, tile, st in BUILT_CONFIGS + [("auto", None, 0), ("producer", None, 0), ("ring", None, 4)]:
+            s = tbg.gemm_configured_status(**g, config=tbg.gemm_config(tile, st, pipe))
+            if pipe == "ring" and tile is None and st == 4:
+                # the tile chosen for 64×64 is 64×64, built with 4 stages
+                assert s == tbg.ERR_NO_DEVICE, tbg.last_error()
+                continue
+            assert s == tbg.ERR_NO_DEVICE, (pipe, tile, st, tbg.last_error())
+
+
+def test_header_lists_the_built_configurations():
+    """The configurations tbg.h documents are the ones the library accepts (and no more)."""
+    import re
+    text = open(tbg.HEADER_PATH).read()
+    block = text[text.index("Built configurations"):text.index("typedef struct {\n    int32_t tile_m")]
+    ring = block[block.index("ring:"):block.index("producer:")]
+    prod = block[block.index("producer:"):]
+
+    def expand(line):
+        out = set()
+        for part in line.split(";"):
+            m = re.search(r"((?:\d+x\d+(?: and )?)+)/(\d)(?:-(\d))?", part)
+            if not m:
+                continue
+            tiles = re.findall(r"\d+x\d+", m.group(1))
+            lo, hi = int(m.group(2)), int(m.group(3) or m.group(2))
+            out |= {(t, s) for t in tiles for s in range(lo, hi + 1)}
+        return out
+
+    assert expand(ring) == {(t, s) for p, t, s in BUILT_CONFIGS if p == "ring"}
+    assert expand(prod) == {(t, s) for p, t, s in BUILT_CONFIGS if p == "producer"}

@@ -31,7 +31,7 @@ def ops():
     return torch_ops
 
 
-def _run(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, ldc=None, a_offset=0, b_offset=0):
+def _run(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, ldc=None, a_offset=0, b_offset=0, config=None):
     """A_cpu/B_cpu: row-major buffers (rows × ld).  Offsets shift the operands' start by whole
     elements inside a larger device buffer (to test bases off a 16-byte boundary)."""
     lda, ldb = A_cpu.shape[1], B_cpu.shape[1]
@@ -46,7 +46,7 @@ def _run(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, ldc=None, a_offset=0, 
     ldc = ldc or N
     Cbuf = torch.full((M, ldc), float("nan"), dtype=tdt, device="cuda")
     C = Cbuf[:, :N]
-    ops.gemm(A, B, b_layout, out_dtype, out=C)
+    ops.gemm(A, B, b_layout, out_dtype, out=C, config=config)
     torch.cuda.synchronize()
     return Cbuf
 
@@ -183,24 +183,18 @@ def test_degenerate_sizes(ops):
 TILES = ["256x256", "256x128", "128x256", "128x128", "64x64"]
 
 
-@pytest.fixture
-def force_tile(request):
-    import os
-    old = os.environ.get("TBG_TILE")
-    os.environ["TBG_TILE"] = request.param
-    yield request.param
-    if old is None:
-        del os.environ["TBG_TILE"]
-    else:
-        os.environ["TBG_TILE"] = old
+def _cfg(tile, stages=0, pipeline="ring"):
+    import tiled_bf16_gemm_amd as tbg
+    return None if tile == "auto" else tbg.gemm_config(tile, stages, pipeline)
 
 
 @gpu
-@pytest.mark.parametrize("force_tile", TILES, indirect=True)
-def test_every_tile(ops, orc, force_tile):
-    """Each workgroup tile the library can pick, forced through TBG_TILE: ragged shapes against
-    the oracle (both B layouts, both output types, a padded ldc), and small-integer operands bit
-    for bit."""
+@pytest.mark.parametrize("tile", TILES)
+def test_every_tile(ops, orc, tile):
+    """Each workgroup tile the library can pick, forced through tbg_gemm_configured: ragged shapes
+    against the oracle (both B layouts, both output types, a padded ldc), and small-integer
+    operands bit for bit."""
+    cfg = _cfg(tile)
     cases = [(700, 520, 300, "kn", "f32"), (333, 190, 200, "nk", "bf16"), (130, 70, 1, "kn", "bf16"),
              (64, 64, 64, "nk", "f32")]
     for i, (M, N, K, bl, out) in enumerate(cases):
@@ -208,77 +202,128 @@ def test_every_tile(ops, orc, force_tile):
         B = workloads.matrix(K, N, N, ("normal", 1.0), 400 + i) if bl == "kn" else \
             workloads.matrix(N, K, K, ("normal", 1.0), 400 + i)
         ldc = N + 3
-        _say(f"tile {force_tile}: gemm M={M} N={N} K={K} {bl} {out} ldc={ldc}")
-        Cbuf = _run(ops, A, B, M, N, K, bl, out, ldc=ldc)
+        _say(f"tile {tile}: gemm M={M} N={N} K={K} {bl} {out} ldc={ldc}")
+        Cbuf = _run(ops, A, B, M, N, K, bl, out, ldc=ldc, config=cfg)
         ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl)
         got = _to_f32(Cbuf)
-        _check(got[:, :N], ref, f"tile {force_tile} case {i}")
+        _check(got[:, :N], ref, f"tile {tile} case {i}")
         assert np.all(np.isnan(got[:, N:])), "columns past N were written"
     for M, N, K, bl in [(300, 257, 136, "kn"), (300, 257, 136, "nk")]:
         rng = np.random.default_rng(M + N + K)
         Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
         shape_b = (K, N) if bl == "kn" else (N, K)
         Bi = torch.from_numpy(rng.integers(-8, 9, shape_b).astype(np.float32)).to(torch.bfloat16)
-        _say(f"tile {force_tile}: integer gemm M={M} N={N} K={K} {bl}")
-        got = _to_f32(_run(ops, Ai, Bi, M, N, K, bl, "f32"))
+        _say(f"tile {tile}: integer gemm M={M} N={N} K={K} {bl}")
+        got = _to_f32(_run(ops, Ai, Bi, M, N, K, bl, "f32", config=cfg))
         ref = orc.gemm(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, shape_b[1], bl)
         assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"
 
 
-def _run_ex(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, alpha, beta, C_old):
+# Every built (pipeline, tile, stages) configuration, as include/tbg.h lists them.
+CONFIGS = ([("ring", "256x256", 2)] + [("ring", t, s) for t in ("256x128", "128x256") for s in (2, 3)]
+           + [("ring", "128x128", s) for s in (2, 3, 4, 5)] + [("ring", "64x64", s) for s in range(2, 7)]
+           + [("producer", t, s) for t in ("256x128", "128x256") for s in (2, 3)]
+           + [("producer", "128x128", s) for s in (2, 3, 4)] + [("producer", "64x64", s) for s in range(2, 7)])
+
+# (M, N, K, B layout, C type): ragged edges everywhere; K from one partial tile (fewer K tiles
+# than stages) to 16 tiles (the ring wraps several times).
+CONFIG_CASES = [(700, 520, 1000, "kn", "f32"), (333, 190, 200, "nk", "bf16"), (130, 70, 1, "kn", "bf16"),
+                (257, 300, 64, "nk", "f32"), (300, 257, 520, "kn", "bf16")]
+_config_refs = {}
+
+
+def _config_case(orc, i):
+    """Inputs, oracle result and the default configuration's bits for case i (computed once)."""
+    if i not in _config_refs:
+        M, N, K, bl, out = CONFIG_CASES[i]
+        A = workloads.matrix(M, K, K, ("normal", 1.0), 800 + i)
+        B = workloads.matrix(K, N, N, ("normal", 1.0), 900 + i) if bl == "kn" else \
+            workloads.matrix(N, K, K, ("normal", 1.0), 900 + i)
+        ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl)
+        _config_refs[i] = (A, B, ref, None)
+    return _config_refs[i]
+
+
+@gpu
+@pytest.mark.parametrize("pipeline,tile,stages", CONFIGS)
+def test_every_configuration(ops, orc, pipeline, tile, stages):
+    """Each built pipeline × tile × stage count: ragged shapes against the oracle, bit-identical to
+    the default configuration (every configuration adds the same products in the same order),
+    columns past N untouched, and small-integer operands bit for bit."""
+    cfg = _cfg(tile, stages, pipeline)
+    for i, (M, N, K, bl, out) in enumerate(CONFIG_CASES):
+        A, B, ref, base = _config_case(orc, i)
+        ldc = N + 3
+        _say(f"{pipeline} {tile}/{stages}: gemm M={M} N={N} K={K} {bl} {out}")
+        Cbuf = _run(ops, A, B, M, N, K, bl, out, ldc=ldc, config=cfg)
+        got = _to_f32(Cbuf)
+        _check(got[:, :N], ref, f"{pipeline} {tile}/{stages} case {i}")
+        assert np.all(np.isnan(got[:, N:])), "columns past N were written"
+        if base is None:
+            base = _to_f32(_run(ops, A, B, M, N, K, bl, out, ldc=ldc))
+            _config_refs[i] = (A, B, ref, base)
+        assert np.array_equal(got[:, :N], base[:, :N]), \
+            f"{int((got[:, :N] != base[:, :N]).sum())} entries differ from the default configuration"
+    M, N, K = 300, 257, 392
+    for bl in ("kn", "nk"):
+        rng = np.random.default_rng(4242)
+        Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
+        shape_b = (K, N) if bl == "kn" else (N, K)
+        Bi = torch.from_numpy(rng.integers(-8, 9, shape_b).astype(np.float32)).to(torch.bfloat16)
+        _say(f"{pipeline} {tile}/{stages}: integer gemm M={M} N={N} K={K} {bl}")
+        got = _to_f32(_run(ops, Ai, Bi, M, N, K, bl, "f32", config=cfg))
+        ref = orc.gemm(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, shape_b[1], bl)
+        assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"
+
+
+def _run_ex(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, alpha, beta, C_old, config=None):
     """C_old: (M, ldc) CPU tensor of the output type; returns the GPU result buffer."""
     A = A_cpu.cuda()[:, :K]
     B = B_cpu.cuda()
     B = B[:, :N] if b_layout == "kn" else B[:, :K]
     Cbuf = C_old.clone().cuda()
-    ops.gemm(A, B, b_layout, out_dtype, out=Cbuf[:, :N], alpha=alpha, beta=beta)
+    ops.gemm(A, B, b_layout, out_dtype, out=Cbuf[:, :N], alpha=alpha, beta=beta, config=config)
     torch.cuda.synchronize()
     return Cbuf
 
 
 @gpu
-@pytest.mark.parametrize("tile", ["auto", "256x256", "128x128", "64x64", "256x128"])
-def test_gemm_alpha_beta(ops, orc, tile):
+@pytest.mark.parametrize("pipeline,tile", [("ring", "auto"), ("ring", "256x256"), ("ring", "128x128"),
+                                           ("ring", "64x64"), ("ring", "256x128"), ("producer", "128x128"),
+                                           ("producer", "64x64")])
+def test_gemm_alpha_beta(ops, orc, pipeline, tile):
     """C <- alpha·A·B + beta·C against the oracle: both layouts and output types, beta = 0 with NaN
     in C (C not read), alpha = 0 (the product skipped), and exact small-integer cases."""
-    import os
-    old_tile = os.environ.pop("TBG_TILE", None)
-    if tile != "auto":
-        os.environ["TBG_TILE"] = tile
-    try:
-        cases = [(700, 520, 300, "kn", "f32", 1.5, -0.75), (333, 190, 200, "nk", "bf16", 0.5, 2.0),
-                 (257, 129, 64, "kn", "bf16", -1.25, 0.0), (96, 80, 40, "nk", "f32", 0.0, 0.5),
-                 (64, 64, 0, "kn", "f32", 3.0, -2.0)]
-        for i, (M, N, K, bl, out, alpha, beta) in enumerate(cases):
-            A = workloads.matrix(M, K, K, ("normal", 1.0), 500 + i)
-            B = workloads.matrix(K, N, N, ("normal", 1.0), 600 + i) if bl == "kn" else \
-                workloads.matrix(N, K, K, ("normal", 1.0), 600 + i)
-            tdt = torch.float32 if out == "f32" else torch.bfloat16
-            ldc = N + 5
-            if beta == 0.0:
-                C_old = torch.full((M, ldc), float("nan"), dtype=tdt)
-            else:
-                C_old = torch.from_numpy(np.random.default_rng(700 + i).normal(size=(M, ldc)).astype(np.float32)).to(tdt)
-            _say(f"gemm_ex tile {tile}: M={M} N={N} K={K} {bl} {out} alpha={alpha} beta={beta}")
-            Cbuf = _run_ex(ops, A, B, M, N, K, bl, out, alpha, beta, C_old)
-            ref = orc.gemm_ex(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl, alpha, beta,
-                              C_old[:, :N].float().numpy())
-            got = _to_f32(Cbuf)
-            _check(got[:, :N], ref, f"gemm_ex case {i}")
-            assert np.array_equal(got[:, N:], C_old[:, N:].float().numpy(), equal_nan=True), "columns past N changed"
-            if alpha == 0.0:
-                want = (C_old[:, :N].float() * beta).to(tdt).float().numpy()
-                assert np.array_equal(got[:, :N], want), "alpha = 0 must give beta·C exactly"
-        # small integers: alpha·S + beta·C is exact in binary32, so the bits must match
-        M, N, K = 300, 257, 136
-        rng = np.random.default_rng(77)
-        Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
-        Bi = torch.from_numpy(rng.integers(-8, 9, (N, K)).astype(np.float32)).to(torch.bfloat16)
-        Ci = torch.from_numpy(rng.integers(-100, 101, (M, N)).astype(np.float32))
-        Cbuf = _run_ex(ops, Ai, Bi, M, N, K, "nk", "f32", 2.0, -3.0, Ci)
-        ref = orc.gemm_ex(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, K, "nk", 2.0, -3.0, Ci.numpy())
-        assert np.array_equal(_to_f32(Cbuf), ref)
-    finally:
-        os.environ.pop("TBG_TILE", None)
-        if old_tile is not None:
-            os.environ["TBG_TILE"] = old_tile
+    cfg = _cfg(tile, 0, pipeline)
+    cases = [(700, 520, 300, "kn", "f32", 1.5, -0.75), (333, 190, 200, "nk", "bf16", 0.5, 2.0),
+             (257, 129, 64, "kn", "bf16", -1.25, 0.0), (96, 80, 40, "nk", "f32", 0.0, 0.5),
+             (64, 64, 0, "kn", "f32", 3.0, -2.0)]
+    for i, (M, N, K, bl, out, alpha, beta) in enumerate(cases):
+        A = workloads.matrix(M, K, K, ("normal", 1.0), 500 + i)
+        B = workloads.matrix(K, N, N, ("normal", 1.0), 600 + i) if bl == "kn" else \
+            workloads.matrix(N, K, K, ("normal", 1.0), 600 + i)
+        tdt = torch.float32 if out == "f32" else torch.bfloat16
+        ldc = N + 5
+        if beta == 0.0:
+            C_old = torch.full((M, ldc), float("nan"), dtype=tdt)
+        else:
+            C_old = torch.from_numpy(np.random.default_rng(700 + i).normal(size=(M, ldc)).astype(np.float32)).to(tdt)
+        _say(f"gemm_ex {pipeline} {tile}: M={M} N={N} K={K} {bl} {out} alpha={alpha} beta={beta}")
+        Cbuf = _run_ex(ops, A, B, M, N, K, bl, out, alpha, beta, C_old, config=cfg)
+        ref = orc.gemm_ex(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl, alpha, beta,
+                          C_old[:, :N].float().numpy())
+        got = _to_f32(Cbuf)
+        _check(got[:, :N], ref, f"gemm_ex case {i}")
+        assert np.array_equal(got[:, N:], C_old[:, N:].float().numpy(), equal_nan=True), "columns past N changed"
+        if alpha == 0.0:
+            want = (C_old[:, :N].float() * beta).to(tdt).float().numpy()
+            assert np.array_equal(got[:, :N], want), "alpha = 0 must give beta·C exactly"
+    # small integers: alpha·S + beta·C is exact in binary32, so the bits must match
+    M, N, K = 300, 257, 136
+    rng = np.random.default_rng(77)
+    Ai = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
+    Bi = torch.from_numpy(rng.integers(-8, 9, (N, K)).astype(np.float32)).to(torch.bfloat16)
+    Ci = torch.from_numpy(rng.integers(-100, 101, (M, N)).astype(np.float32))
+    Cbuf = _run_ex(ops, Ai, Bi, M, N, K, "nk", "f32", 2.0, -3.0, Ci, config=cfg)
+    ref = orc.gemm_ex(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, K, "nk", 2.0, -3.0, Ci.numpy())
+    assert np.array_equal(_to_f32(Cbuf), ref)

@@ -42,11 +42,29 @@ SWIZZLES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
 OOB = {"zero": 0, "nan": 1}
 L2 = {"none": 0, "64B": 1, "128B": 2, "256B": 3}
 B_LAYOUTS = {"kn": 0, "nk": 1}
+PIPELINES = {"auto": 0, "ring": 1, "producer": 2}
 
 
 class TensorDesc(ctypes.Structure):
     """tbg_tensor_desc: 128 bytes, plain data."""
     _fields_ = [("opaque", ctypes.c_uint64 * 16)]
+
+
+class GemmConfig(ctypes.Structure):
+    """tbg_gemm_config: workgroup tile, ring stages and copy pipeline (0 = the library's choice)."""
+    _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("pipeline", ctypes.c_int32)]
+
+
+def gemm_config(tile=None, stages: int = 0, pipeline="auto") -> GemmConfig:
+    """Build a GemmConfig; tile is None, (bm, bn) or "BMxBN"."""
+    if tile is None:
+        bm = bn = 0
+    elif isinstance(tile, str):
+        bm, bn = (int(x) for x in tile.lower().split("x"))
+    else:
+        bm, bn = tile
+    return GemmConfig(int(bm), int(bn), int(stages), _enum(PIPELINES, pipeline))
 
 
 class Error(RuntimeError):
@@ -83,6 +101,10 @@ _lib.tbg_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c
 _lib.tbg_gemm.restype = ctypes.c_int
 _lib.tbg_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, ctypes.c_int, _vp,
                           ctypes.c_size_t, _vp]
+_lib.tbg_gemm_configured.restype = ctypes.c_int
+_lib.tbg_gemm_configured.argtypes = [_i64, _i64, _i64, ctypes.c_float, _vp, _i64, _vp, _i64, ctypes.c_int,
+                                     ctypes.c_float, _vp, _i64, ctypes.c_int, ctypes.POINTER(GemmConfig), _vp,
+                                     ctypes.c_size_t, _vp]
 _lib.tbg_status_string.restype = ctypes.c_char_p
 _lib.tbg_status_string.argtypes = [ctypes.c_int]
 _lib.tbg_last_error.restype = ctypes.c_char_p
@@ -175,6 +197,25 @@ def gemm_ex(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb:
     _check(_lib.tbg_gemm_ex(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout),
                             float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype), _vp(int(workspace)),
                             int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_configured(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, beta: float,
+                    C: int, ldc: int, c_dtype, config: Optional[GemmConfig], workspace: int = 0,
+                    workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
+    """tbg_gemm_configured: C = alpha·A·B + beta·C with an explicit kernel configuration."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(_lib.tbg_gemm_configured(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb,
+                                    _enum(B_LAYOUTS, b_layout), float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype),
+                                    cfg, _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_configured_status(*args, **kwargs) -> int:
+    """Like gemm_configured but returns the status code instead of raising."""
+    try:
+        gemm_configured(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
 
 
 def gemm_status(*args, **kwargs) -> int:

@@ -37,8 +37,30 @@ def sources():
 
 
 def build(out: str = LIB, verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to an object in parallel (one hipcc per file), then link."""
+    import concurrent.futures
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
+        cmd = [hipcc(), *flags(), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+        if msg.strip() and verbose:
+            print(msg, flush=True)
+        return obj
+
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 4)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), "-shared", *sources(), "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

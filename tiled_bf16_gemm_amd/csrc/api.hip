@@ -309,10 +309,31 @@ namespace {
 // as 0 and A, B and their leading dimensions are not looked at.
 tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                      int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
-                     void* workspace, size_t workspace_bytes, void* stream, bool scaled) {
+                     const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes, void* stream, bool scaled) {
   if (M < 0 || N < 0 || K < 0) return fail(TBG_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                                           (long long)M, (long long)N, (long long)K);
   if ((int)bl != TBG_B_KN && (int)bl != TBG_B_NK) return fail(TBG_ERR_INVALID_VALUE, "unknown b_layout %d", (int)bl);
+  // Kernel configuration: checked in full before anything else can fail on a machine without a
+  // device, so that the checks are the same everywhere.
+  int pipeline = tbg::kPipeRing, bm = 0, bn = 0, stages = 0;
+  if (cfg) {
+    if (cfg->pipeline != TBG_PIPE_AUTO && cfg->pipeline != TBG_PIPE_RING && cfg->pipeline != TBG_PIPE_PRODUCER)
+      return fail(TBG_ERR_INVALID_VALUE, "unknown pipeline %d", (int)cfg->pipeline);
+    if ((cfg->tile_m == 0) != (cfg->tile_n == 0))
+      return fail(TBG_ERR_INVALID_VALUE, "tile_m and tile_n must both be 0 or both be set");
+    if (cfg->stages < 0 || cfg->stages == 1) return fail(TBG_ERR_INVALID_VALUE, "stages must be 0 or >= 2");
+    if (cfg->pipeline == TBG_PIPE_PRODUCER) pipeline = tbg::kPipeProducer;
+    bm = cfg->tile_m;
+    bn = cfg->tile_n;
+    stages = cfg->stages;
+    if (bm != 0) {
+      const int st = stages ? stages : tbg::default_stages(pipeline, bm, bn);
+      if (!tbg::find_gemm(pipeline, bm, bn, st))
+        return fail(TBG_ERR_UNSUPPORTED, "no %s kernel with tile %dx%d and %d stages (built: %s)",
+                    pipeline == tbg::kPipeProducer ? "producer/consumer" : "ring", bm, bn, st,
+                    tbg::gemm_configs_text(pipeline));
+    }
+  }
   if (scaled && alpha == 0.f) {  // the empty product: nothing of A or B is used
     K = 0;
     A = B = nullptr;
@@ -375,18 +396,12 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.N = (int)N;
   p.K = (int)K;
   p.kchunks = (int)(pl.kext / 8);
-  // Workgroup tile: chosen from the shape and the device, or forced by TBG_TILE="BMxBN" (one of
-  // 256x256, 256x128, 128x256, 128x128, 64x64) for measurements.
-  int bm = 256, bn = 256;
-  tbg::choose_tile(M, N, num_cus, bm, bn);
-  if (const char* tv = getenv("TBG_TILE")) {
-    int fm = 0, fn = 0;
-    if (sscanf(tv, "%dx%d", &fm, &fn) == 2 &&
-        ((fm == 256 && (fn == 256 || fn == 128)) || (fm == 128 && (fn == 256 || fn == 128)) || (fm == 64 && fn == 64))) {
-      bm = fm;
-      bn = fn;
-    }
-  }
+  // Workgroup tile: the caller's, or chosen from the shape and the device among the tiles the
+  // pipeline is built for; then the stage count.
+  if (bm == 0) tbg::choose_tile(M, N, num_cus, pipeline, bm, bn);
+  if (stages == 0) stages = tbg::default_stages(pipeline, bm, bn);
+  if (!tbg::find_gemm(pipeline, bm, bn, stages))
+    return fail(TBG_ERR_UNSUPPORTED, "no kernel with tile %dx%d and %d stages", bm, bn, stages);
   p.tiles_m = 0;
   p.tiles_n = 0;
   p.group_m = env_int("TBG_GROUP_M", 8);
@@ -395,7 +410,7 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
-  e = tbg::launch_gemm(p, bm, bn, (int)bl, c_dtype == TBG_BF16, s);
+  e = tbg::launch_gemm(p, pipeline, bm, bn, stages, (int)bl, c_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
 }
@@ -407,14 +422,25 @@ extern "C" {
 tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                     tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  return gemm_impl(M, N, K, 1.f, A, lda, B, ldb, bl, 0.f, C, ldc, c_dtype, workspace, workspace_bytes, stream, false);
+  return gemm_impl(M, N, K, 1.f, A, lda, B, ldb, bl, 0.f, C, ldc, c_dtype, nullptr, workspace, workspace_bytes, stream,
+                   false);
 }
 
 tbg_status tbg_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                        int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
   const bool scaled = !(alpha == 1.f && beta == 0.f);
-  return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, workspace, workspace_bytes, stream,
+  return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, nullptr, workspace, workspace_bytes,
+                   stream, scaled);
+}
+
+tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc,
+                               tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!cfg) return fail(TBG_ERR_INVALID_VALUE, "cfg is NULL");
+  const bool scaled = !(alpha == 1.f && beta == 0.f);
+  return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, cfg, workspace, workspace_bytes, stream,
                    scaled);
 }
 

@@ -1,0 +1,425 @@
+// Device building blocks shared by the GEMM kernels (gemm_ring.hpp, gemm_pc.hpp): the
+// workgroup tile shape, the XCD-aware tile order, the 16×16×32 bf16 product, fragment reads from
+// LDS, the copy atoms of a ring stage, one k-step of products with its interleaved reads and
+// copies, and the epilogue.
+//
+// "GEMM: la moltiplicazione di matrici sull'hardware" fixes the product (section "Il conto"),
+// the tiling argument (section "Tiling": a B_M×B_N tile of C, operand blocks loaded once into
+// on-chip memory and reused, grouped launch order for L2 reuse, a second level of tiles in
+// registers) and the mixed precision of the matrix units (tensor-core section).  The descriptor
+// pages fix how operand tiles reach on-chip memory (a box copy with out-of-bounds zero fill and
+// an XOR swizzle).  Layouts used by every kernel:
+//
+//  * workgroup tile BM×BN×64, 4 compute waves in a 2×2 arrangement, each owning a
+//    (BM/2)×(BN/2) block of C whose 16×16 fp32 accumulator fragments stay in registers for the
+//    whole K loop (256 per lane at 256×256);
+//  * a ring stage holds the A box {64 k, BM m} with the 2-row swizzle, then B: stored N×K the
+//    same way, stored K×N as BN/64 boxes {64 n, 64 k} with the 128B swizzle;
+//  * fragments come from LDS with ds_read_b128 (k-contiguous rows) or, for B stored K×N, with
+//    ds_read_b64_tr_b16, which transposes 4×16 blocks of 16-bit values across 16 lanes;
+//  * v_mfma_f32_16x16x32_bf16 with the operands swapped (B fragment first), so each lane ends
+//    with four consecutive columns of one row of C; the epilogue regroups them through LDS into
+//    whole-row 16-byte stores, masked at the M and N edges.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "tbg_desc.hpp"
+#include "tile_loader.hpp"
+
+namespace tbg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBK = 64, kThreads = 256;
+
+// Shape of one workgroup tile and everything derived from it.
+template <int BM_, int BN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int TM = BM / 2, TN = BN / 2;    // block of C per wave (2×2 waves)
+  static constexpr int FM = TM / 16, FN = TN / 16;  // 16×16 fragments per wave
+  static constexpr int ABytes = BM * kBK * 2, BBytes = BN * kBK * 2;
+  static constexpr int StageBytes = ABytes + BBytes;
+  // A ring has at least two stages; the epilogue parks each wave's block of C in its own
+  // quarter of the first two.
+  static constexpr int RingBytes = 2 * StageBytes;
+  static constexpr int AtomsA = BM / 32, AtomsB = BN / 32;  // 1 KiB copy atoms per wave per K tile
+  static constexpr int Atoms = AtomsA + AtomsB;
+  static constexpr int Reads = FM + FN;     // fragment reads per k-step of 32
+  static constexpr int Products = FM * FN;  // products per k-step
+  // 256 accumulators per lane only fit if they are pinned to AGPRs (inline assembly); smaller
+  // blocks use the compiler's builtin, which also inserts the dependency waits that the
+  // short accumulator reuse distance of a small block needs.
+  static constexpr bool AsmMfma = Products >= 64;
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile sizes 64, 128, 256");
+};
+
+// Workgroup id -> (tile row, tile column).  Ids are dealt round-robin to the 8 XCDs; the first
+// step gives each XCD a contiguous range of logical ids (a bijection for any grid size), the
+// second orders logical ids column-major inside groups of `group_m` tile-rows ("GEMM" page,
+// section "Tiling": blocks launched together reuse the same operand tiles from L2).
+__device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int q = nwg >> 3, r = nwg & 7;
+  const int x = bid & 7, i = bid >> 3;
+  const int lid = x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+  const int per_group = group_m * tiles_n;
+  const int g = lid / per_group;
+  const int first = g * group_m;
+  const int gsz = min(tiles_m - first, group_m);
+  const int in = lid - g * per_group;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+// One 16×16×32 bf16 product-accumulate.  For the 256×256 tile it is inline assembly with the
+// accumulator pinned to AGPRs ("+a"): the 256 accumulators of a wave then stay in the
+// accumulation registers for the whole K loop and the 256 architectural VGPRs hold the fragments
+// and addresses.  Consecutive products there never reuse an accumulator within 63 instructions,
+// so no dependency wait is needed between them.  The last product of a loop iteration (DRAIN)
+// is followed by 24 wait states, more than a matrix result needs before another instruction may
+// read it, so whatever follows the loop can read the accumulators.
+template <bool ASM, bool DRAIN = false>
+__device__ __forceinline__ void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if (!ASM)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  else if (DRAIN)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait for this wave's outstanding tile copies (down to `N` in flight) and its LDS reads, then
+// meet the other waves: afterwards every wave's copies of the awaited tile are visible in LDS
+// and no wave still reads the stage that the next copies overwrite ("1 · Asynchronisme et
+// mbarrier" §1.5: the full/empty hand-off of a ring stage, done here with one barrier).
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <class T>
+struct Frags {
+  bf16x8_t a[T::FM];
+  bf16x8_t b[T::FN];
+};
+
+// Per-lane LDS byte offsets of the fragment reads (see the kernel for the layouts).
+template <class T>
+struct FragAddr {
+  static constexpr int Q = T::FN < 4 ? T::FN : 4;
+  uint32_t a_lane, a_col[2];
+  uint32_t b_lane, b_col[2];
+  uint32_t b_tr[Q][2];
+  int wn;
+};
+
+// Read fragment `idx` (0..FM-1: A fragments, FM..FM+FN-1: B fragments) of k-step `kk` of a stage.
+template <class T, int BL>
+__device__ __forceinline__ void read_frag(Frags<T>& f, const FragAddr<T>& fa, const uint8_t* sA, const uint8_t* sB,
+                                          int kk, int idx) {
+  if (idx < T::FM) {
+    f.a[idx] = *(const bf16x8_t*)(sA + fa.a_lane + idx * 2048 + fa.a_col[kk]);
+  } else {
+    const int fn = idx - T::FM;
+    if (BL == 1) {
+      f.b[fn] = *(const bf16x8_t*)(sB + fa.b_lane + fn * 2048 + fa.b_col[kk]);
+    } else {
+      // The wave's columns wn*TN .. +TN-1 lie in boxes of 64 columns; fragment fn is 16 of them.
+      const int box = T::TN >= 64 ? fa.wn * (T::TN / 64) + (fn >> 2) : 0;
+      const int q = T::TN >= 64 ? (fn & 3) : fn;
+      const uint8_t* base = sB + box * 8192 + kk * 4096;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4_t*)(base + fa.b_tr[q][0]));
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4_t*)(base + fa.b_tr[q][1]));
+      f.b[fn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
+// Copies of one operand tile pair (A and B boxes of one K tile) into one ring stage: T::Atoms
+// atoms per wave, issued one at a time between the products of a k-step.
+struct TileCopy {
+  rsrc_t ra, rb;
+  uint32_t lds_a, lds_b;  // LDS byte address of this wave's first atom of A and of B
+  int cvalid_a, cvalid_b;
+};
+
+template <class T>
+__device__ __forceinline__ void copy_atom(const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb, int j) {
+  if (j < T::AtomsA) issue_atom(tc.ra, tc.lds_a + j * 1024, la[j], tc.cvalid_a);
+  else issue_atom(tc.rb, tc.lds_b + (j - T::AtomsA) * 1024, lb[j - T::AtomsA], tc.cvalid_b);
+}
+
+// One k-step: the products on `cur`, with the fragment reads of the next k-step and (if COPY)
+// the copy atoms of a later tile spread evenly between them.  The COPY step closes a loop
+// iteration, so its last product drains.
+template <class T, int BL, bool COPY>
+__device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<T>& cur, Frags<T>& nxt,
+                                      const FragAddr<T>& fa, const uint8_t* nA, const uint8_t* nB, int nkk,
+                                      const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb) {
+  // Read r goes before product (r * Products) / Reads, atom j before (j * Products) / Atoms:
+  // before product i come reads [ceil(i*R/P), ceil((i+1)*R/P)) and likewise atoms.
+  constexpr int P = T::Products, R = T::Reads, A = T::Atoms;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+#pragma unroll
+    for (int r = (i * R + P - 1) / P; r < ((i + 1) * R + P - 1) / P; ++r) read_frag<T, BL>(nxt, fa, nA, nB, nkk, r);
+    if (COPY) {
+#pragma unroll
+      for (int j = (i * A + P - 1) / P; j < ((i + 1) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
+    }
+    const int fn = i / T::FM, fm = i % T::FM;
+    if (COPY && i == T::Products - 1) mfma16<T::AsmMfma, true>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    else mfma16<T::AsmMfma>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+  }
+}
+
+// LDS chunk swizzle of the epilogue's park: rows of `cpr` 16-byte chunks; XOR the chunk index
+// so that 16 rows at one chunk (the fragment writes) and 16 consecutive chunks (the row reads)
+// fall on 16 distinct 16-byte bank groups of the 256-byte bank window.
+template <int CPR>
+__device__ __forceinline__ int park_xor(int r) {
+  if (CPR >= 16) return r & 15;
+  if (CPR == 8) return (r >> 1) & 7;
+  return (r >> 2) & 3;  // CPR == 4
+}
+
+// The epilogue: C leaves through LDS as whole rows.  A lane holds C[m][n..n+3] of each fragment,
+// so storing fragments directly would write 16 rows × 32 bytes per instruction.  Instead each
+// wave parks its block (in one or two bands of rows) in its own quarter of the now idle ring,
+// then reads it back as 16-byte pieces of whole rows, so every store instruction writes whole
+// row segments.  Whole-row stores are non-temporal: C is written once and not read again here,
+// so it should not push operand tiles out of the caches.  With SCALED the park keeps the fp32
+// sums and each piece becomes alpha·S + beta·C_old (C_old read only when beta != 0) before it is
+// rounded to C's type ("GEMM" page, tensor-core section: C <- alpha·A·B + beta·C).
+template <class T, int OUT, int SCALED>
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], uint8_t* park, const GemmParams& p,
+                                          int row0, int col0, int lane) {
+  constexpr int ES = OUT == 1 ? 2 : 4;                     // element size of C
+  constexpr int PES = (OUT == 1 && !SCALED) ? 2 : 4;       // element size in the park
+  constexpr int RowBytes = T::TN * PES;
+  constexpr int CPR = RowBytes / 16;
+  constexpr int EPC = 16 / PES;  // elements per 16-byte park chunk
+  constexpr int ParkBytes = T::RingBytes / 4;
+  constexpr int Bands = (T::TM * RowBytes + ParkBytes - 1) / ParkBytes;
+  constexpr int BandFM = T::FM / Bands;
+  constexpr int BandRows = 16 * BandFM;
+  constexpr int RowsPerRead = 64 / CPR;
+  constexpr int ReadsPerBand = BandRows / RowsPerRead;
+  static_assert(T::FM % Bands == 0 && BandRows % RowsPerRead == 0, "epilogue bands");
+#pragma unroll
+  for (int band = 0; band < Bands; ++band) {
+#pragma unroll
+    for (int f = 0; f < BandFM; ++f)
+#pragma unroll
+      for (int fn = 0; fn < T::FN; ++fn) {
+        const int r = 16 * f + (lane & 15);
+        const f32x4_t v = acc[fn][band * BandFM + f];
+        if (PES == 2) {
+          const int c = 2 * fn + (lane >> 5);
+          bf16x4_t h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (__bf16)v[e];
+          *(bf16x4_t*)(park + r * RowBytes + ((c ^ park_xor<CPR>(r)) << 4) + ((lane >> 4) & 1) * 8) = h;
+        } else {
+          const int c = 4 * fn + (lane >> 4);
+          *(f32x4_t*)(park + r * RowBytes + ((c ^ park_xor<CPR>(r)) << 4)) = v;
+        }
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < ReadsPerBand; ++i) {
+      const int r = RowsPerRead * i + lane / CPR, c = lane % CPR;
+      const uint4 v = *(const uint4*)(park + r * RowBytes + ((c ^ park_xor<CPR>(r)) << 4));
+      const int gm = row0 + BandRows * band + r, gn = col0 + EPC * c;
+      if (gm >= p.M) continue;
+      uint8_t* dst = (uint8_t*)p.C + ((uint64_t)gm * p.ldc + gn) * ES;
+      const bool whole = p.vec_store && gn + EPC - 1 < p.N;
+      if (!SCALED) {
+        if (whole) {
+          __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)dst);
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            if (gn + e >= p.N) continue;
+            if (OUT == 1) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            else ((uint32_t*)dst)[e] = w[e];
+          }
+        }
+      } else {
+        // four fp32 sums per piece
+        float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+        float old[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.beta != 0.f) {
+          if (whole) {
+            if (OUT == 1) {
+              const uint2 o = *(const uint2*)dst;
+              old[0] = __uint_as_float(o.x << 16);
+              old[1] = __uint_as_float(o.x & 0xFFFF0000u);
+              old[2] = __uint_as_float(o.y << 16);
+              old[3] = __uint_as_float(o.y & 0xFFFF0000u);
+            } else {
+              const uint4 o = *(const uint4*)dst;
+              old[0] = __uint_as_float(o.x);
+              old[1] = __uint_as_float(o.y);
+              old[2] = __uint_as_float(o.z);
+              old[3] = __uint_as_float(o.w);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (gn + e >= p.N) continue;
+              old[e] = OUT == 1 ? __uint_as_float((uint32_t)((const uint16_t*)dst)[e] << 16) : ((const float*)dst)[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = p.beta != 0.f ? p.alpha * x[e] + p.beta * old[e] : p.alpha * x[e];
+        if (OUT == 1) {
+          bf16x4_t h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (__bf16)x[e];
+          if (whole) {
+            *(bf16x4_t*)dst = h;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < p.N) ((__bf16*)dst)[e] = h[e];
+          }
+        } else {
+          if (whole) {
+            *(f32x4_t*)dst = f32x4_t{x[0], x[1], x[2], x[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < p.N) ((float*)dst)[e] = x[e];
+          }
+        }
+      }
+    }
+    // The next band's writes follow these reads in this wave's LDS order.
+    if (Bands > 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+
+// Buffer resources of the A box and the B box (or boxes) of K tile `kt` of the workgroup tile at
+// (m0, n0).  A tile past the end of K (`live` false) gets empty ranges and cvalid_a = -1: its
+// copies are fully masked and land zeros in a stage nobody reads.  cvalid_a counts the 16-byte
+// chunks along K that exist from this tile's first column (A, and B stored N×K).
+struct OperandTiles {
+  rsrc_t ra, rb;
+  int cvalid_a;
+  bool live;
+};
+
+template <int BL>
+__device__ __forceinline__ OperandTiles operand_tiles(const GemmParams& p, int m0, int n0, int kt, int ktiles) {
+  OperandTiles o;
+  const int k0 = kt * kBK;
+  const int kext = p.kchunks * 8;
+  o.live = kt < ktiles;
+  o.cvalid_a = o.live ? p.kchunks - (k0 >> 3) : -1;
+  {
+    const uint16_t* origin = p.A + (uint64_t)m0 * p.lda + (o.live ? k0 : 0);
+    const int64_t rem = o.live ? ((int64_t)(p.M - 1 - m0) * p.lda + (kext - k0)) * 2 : 0;
+    o.ra = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+  }
+  if (BL == 1) {
+    const uint16_t* origin = p.B + (uint64_t)n0 * p.ldb + (o.live ? k0 : 0);
+    const int64_t rem = o.live ? ((int64_t)(p.N - 1 - n0) * p.ldb + (kext - k0)) * 2 : 0;
+    o.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+  } else {
+    const uint16_t* origin = p.B + (uint64_t)(o.live ? k0 : 0) * p.ldb + n0;
+    // The range check works on whole dwords: round the last row's end up to one, so a last
+    // element in the low half of a dword is still fetched.  The two bytes past it share that
+    // dword (and its page) and only reach columns past N.
+    const int64_t rem = o.live ? (((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2 + 3) & ~(int64_t)3 : 0;
+    o.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+  }
+  return o;
+}
+
+// 16-byte chunks of columns that exist in the K×N box b (64 columns from n0 + 64 b).  The chunk
+// that straddles column N is loaded whole: its columns past N only feed outputs that are never
+// written.
+__device__ __forceinline__ int kn_box_cvalid(const GemmParams& p, int n0, int b) { return (p.N - n0 - 64 * b + 7) >> 3; }
+
+// Per-lane fragment read addresses of compute wave (wm, wn).
+// A (and B stored N×K): lane l reads row (l & 15) of a 16-row fragment, logical chunk
+// 4*kk + (l >> 4) (eight consecutive k), at its 2-row-swizzled place.
+// B stored K×N, transposing reads: lane 16g + 4e + q supplies the 8 bytes at k row 8g + 4h + e,
+// columns 4q..4q+3 of a 16-column group; lane 16g + i then holds column i.  Group f4 of a box is
+// the wave's fragment (f4 of its first box, or 2*wn + fn when the wave's 32 columns are half of
+// the single box).
+template <class T>
+__device__ __forceinline__ FragAddr<T> make_frag_addr(int wm, int wn, int lane) {
+  FragAddr<T> fa;
+  const int arow = wm * T::TM + (lane & 15);
+  const int ax = (arow >> 1) & 7;
+  fa.a_lane = (uint32_t)arow * 128u;
+  fa.a_col[0] = (uint32_t)((lane >> 4) ^ ax) * 16u;
+  fa.a_col[1] = (uint32_t)((4 + (lane >> 4)) ^ ax) * 16u;
+  const int brow = wn * T::TN + (lane & 15);
+  const int bx = (brow >> 1) & 7;
+  fa.b_lane = (uint32_t)brow * 128u;
+  fa.b_col[0] = (uint32_t)((lane >> 4) ^ bx) * 16u;
+  fa.b_col[1] = (uint32_t)((4 + (lane >> 4)) ^ bx) * 16u;
+  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+#pragma unroll
+  for (int q = 0; q < FragAddr<T>::Q; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int f4 = T::TN >= 64 ? q : 2 * wn + q;
+      const int r = 8 * tg + 4 * h + te;  // row within a 32-row k step
+      const int c = f4 * 2 + (tq >> 1);
+      fa.b_tr[q][h] = (uint32_t)r * 128u + (uint32_t)((c ^ (r & 7)) * 16) + (uint32_t)((tq & 1) * 8);
+    }
+  fa.wn = wn;
+  return fa;
+}
+
+template <class T>
+__device__ __forceinline__ void zero_acc(f32x4_t (&acc)[T::FN][T::FM]) {
+#pragma unroll
+  for (int i = 0; i < T::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// One launcher per kernel configuration: picks the B layout / C type / scaling instance.
+#define TBG_LAUNCH_INSTANCES(KERNEL, THREADS, ...)                                                              \
+  do {                                                                                                         \
+    const unsigned grid_ = (unsigned)p.tiles_m * (unsigned)p.tiles_n;                                          \
+    if (p.scaled) {                                                                                            \
+      if (b_layout == 0 && !out_bf16)                                                                          \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 0, 0, 1>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+      else if (b_layout == 0)                                                                                  \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 0, 1, 1>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+      else if (!out_bf16)                                                                                      \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 1, 0, 1>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+      else                                                                                                     \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 1, 1, 1>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+    } else {                                                                                                   \
+      if (b_layout == 0 && !out_bf16)                                                                          \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 0, 0, 0>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+      else if (b_layout == 0)                                                                                  \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 0, 1, 0>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+      else if (!out_bf16)                                                                                      \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 1, 0, 0>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+      else                                                                                                     \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 1, 1, 0>), dim3(grid_), dim3(THREADS), 0, stream, p);          \
+    }                                                                                                          \
+    return hipGetLastError();                                                                                  \
+  } while (0)
+
+}  // namespace tbg

@@ -1,471 +1,17 @@
-// bf16 GEMM for gfx950: C = A·B with fp32 accumulation in the matrix cores.
-//
-// "GEMM: la moltiplicazione di matrici sull'hardware" fixes the product (section "Il conto"),
-// the tiling argument (section "Tiling": a B_M×B_N tile of C, operand blocks loaded once into
-// on-chip memory and reused, grouped launch order for L2 reuse, a second level of tiles in
-// registers) and the mixed precision of the matrix units (tensor-core section).  The descriptor
-// pages fix how operand tiles reach on-chip memory (a box copy with out-of-bounds zero fill and
-// an XOR swizzle), and "1 · Asynchronisme et mbarrier" §1.3–§1.5 the multi-stage ring that loads
-// tile t+1 while tile t is multiplied.  The mapping onto gfx950:
-//
-//  * workgroup tile BM×BN×64 (256×256 for large problems; 256×128, 128×256, 128×128 or 64×64
-//    when the large tile would leave compute units idle), 4 waves (one per SIMD) in a 2×2
-//    arrangement, each owning a (BM/2)×(BN/2) block of C whose 16×16 fp32 accumulator
-//    fragments stay in registers for the whole K loop (256 per lane at 256×256);
-//  * operand tiles are boxes copied straight into LDS by `buffer_load_dwordx4 ... lds` atoms
-//    (tile_loader.hpp): A as {64 k, BM m} with the 2-row swizzle, B stored N×K likewise, B
-//    stored K×N as BN/64 boxes {64 n, 64 k} with the 128B swizzle;
-//  * a 2-stage LDS ring: at the top of iteration t every wave waits for its own copies of tile
-//    t+1 (`s_waitcnt vmcnt(0)`), one barrier publishes them to all waves and retires everyone's
-//    reads of the other stage, then tile t+2's copies are issued into that stage while tile t is
-//    multiplied — the loads overlap the math;
-//  * fragments come from LDS with ds_read_b128 (k-contiguous rows) or, for B stored K×N, with
-//    ds_read_b64_tr_b16, which transposes 4×16 blocks of 16-bit values across 16 lanes;
-//  * v_mfma_f32_16x16x32_bf16 with the operands swapped (B fragment first), so each lane ends
-//    with four consecutive columns of one row of C; the epilogue regroups them through LDS into
-//    whole-row 16-byte stores, masked at the M and N edges;
-//  * workgroup ids are remapped so that the tiles resident on one XCD (ids are dealt round-robin
-//    over the 8 XCDs) form a compact group of tile-rows and share operand tiles in that XCD's L2.
+// GEMM dispatch: the table of built kernel configurations (pipeline × workgroup tile × ring
+// stages), the choice of a tile for a shape, and the packing kernel for operands whose rows are
+// not 16-byte aligned.  The kernels themselves are in gemm_ring.hpp (every compute wave copies
+// its share of each stage, one barrier per stage) and gemm_pc.hpp (dedicated producer waves,
+// per-stage full/empty counters), instantiated in gemm_ring_*.hip and gemm_pc_*.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
+#include <string>
+
 #include "launch.hpp"
-#include "tbg_desc.hpp"
-#include "tile_loader.hpp"
 
 namespace tbg {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kBK = 64, kThreads = 256;
-
-// Shape of one workgroup tile and everything derived from it.
-template <int BM_, int BN_>
-struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr int TM = BM / 2, TN = BN / 2;    // block of C per wave (2×2 waves)
-  static constexpr int FM = TM / 16, FN = TN / 16;  // 16×16 fragments per wave
-  static constexpr int ABytes = BM * kBK * 2, BBytes = BN * kBK * 2;
-  static constexpr int StageBytes = ABytes + BBytes;
-  static constexpr int RingBytes = 2 * StageBytes;
-  static constexpr int AtomsA = BM / 32, AtomsB = BN / 32;  // 1 KiB copy atoms per wave per K tile
-  static constexpr int Atoms = AtomsA + AtomsB;
-  static constexpr int Reads = FM + FN;     // fragment reads per k-step of 32
-  static constexpr int Products = FM * FN;  // products per k-step
-  // 256 accumulators per lane only fit if they are pinned to AGPRs (inline assembly); smaller
-  // blocks use the compiler's builtin, which also inserts the dependency waits that the
-  // short accumulator reuse distance of a small block needs.
-  static constexpr bool AsmMfma = Products >= 64;
-  // Two workgroups per compute unit when the ring leaves room.
-  static constexpr int MinBlocks = RingBytes <= 64 * 1024 ? 2 : 1;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile sizes 64, 128, 256");
-};
-
-// Workgroup id -> (tile row, tile column).  Ids are dealt round-robin to the 8 XCDs; the first
-// step gives each XCD a contiguous range of logical ids (a bijection for any grid size), the
-// second orders logical ids column-major inside groups of `group_m` tile-rows ("GEMM" page,
-// section "Tiling": blocks launched together reuse the same operand tiles from L2).
-__device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
-  const int q = nwg >> 3, r = nwg & 7;
-  const int x = bid & 7, i = bid >> 3;
-  const int lid = x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-  const int per_group = group_m * tiles_n;
-  const int g = lid / per_group;
-  const int first = g * group_m;
-  const int gsz = min(tiles_m - first, group_m);
-  const int in = lid - g * per_group;
-  tm = first + in % gsz;
-  tn = in / gsz;
-}
-
-// One 16×16×32 bf16 product-accumulate.  For the 256×256 tile it is inline assembly with the
-// accumulator pinned to AGPRs ("+a"): the 256 accumulators of a wave then stay in the
-// accumulation registers for the whole K loop and the 256 architectural VGPRs hold the fragments
-// and addresses.  Consecutive products there never reuse an accumulator within 63 instructions,
-// so no dependency wait is needed between them.  The last product of a loop iteration (DRAIN)
-// is followed by 24 wait states, more than a matrix result needs before another instruction may
-// read it, so whatever follows the loop can read the accumulators.
-template <bool ASM, bool DRAIN = false>
-__device__ __forceinline__ void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  if (!ASM)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-  else if (DRAIN)
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc)
-                 : "v"(a), "v"(b));
-  else
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Wait for this wave's outstanding tile copies (down to `N` in flight) and its LDS reads, then
-// meet the other waves: afterwards every wave's copies of the awaited tile are visible in LDS
-// and no wave still reads the stage that the next copies overwrite ("1 · Asynchronisme et
-// mbarrier" §1.5: the full/empty hand-off of a ring stage, done here with one barrier).
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-template <class T>
-struct Frags {
-  bf16x8_t a[T::FM];
-  bf16x8_t b[T::FN];
-};
-
-// Per-lane LDS byte offsets of the fragment reads (see the kernel for the layouts).
-template <class T>
-struct FragAddr {
-  static constexpr int Q = T::FN < 4 ? T::FN : 4;
-  uint32_t a_lane, a_col[2];
-  uint32_t b_lane, b_col[2];
-  uint32_t b_tr[Q][2];
-  int wn;
-};
-
-// Read fragment `idx` (0..FM-1: A fragments, FM..FM+FN-1: B fragments) of k-step `kk` of a stage.
-template <class T, int BL>
-__device__ __forceinline__ void read_frag(Frags<T>& f, const FragAddr<T>& fa, const uint8_t* sA, const uint8_t* sB,
-                                          int kk, int idx) {
-  if (idx < T::FM) {
-    f.a[idx] = *(const bf16x8_t*)(sA + fa.a_lane + idx * 2048 + fa.a_col[kk]);
-  } else {
-    const int fn = idx - T::FM;
-    if (BL == 1) {
-      f.b[fn] = *(const bf16x8_t*)(sB + fa.b_lane + fn * 2048 + fa.b_col[kk]);
-    } else {
-      // The wave's columns wn*TN .. +TN-1 lie in boxes of 64 columns; fragment fn is 16 of them.
-      const int box = T::TN >= 64 ? fa.wn * (T::TN / 64) + (fn >> 2) : 0;
-      const int q = T::TN >= 64 ? (fn & 3) : fn;
-      const uint8_t* base = sB + box * 8192 + kk * 4096;
-      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4_t*)(base + fa.b_tr[q][0]));
-      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4_t*)(base + fa.b_tr[q][1]));
-      f.b[fn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  }
-}
-
-// Copies of one operand tile pair (A and B boxes of one K tile) into one ring stage: T::Atoms
-// atoms per wave, issued one at a time between the products of a k-step.
-struct TileCopy {
-  rsrc_t ra, rb;
-  uint32_t lds_a, lds_b;  // LDS byte address of this wave's first atom of A and of B
-  int cvalid_a, cvalid_b;
-};
-
-template <class T>
-__device__ __forceinline__ void copy_atom(const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb, int j) {
-  if (j < T::AtomsA) issue_atom(tc.ra, tc.lds_a + j * 1024, la[j], tc.cvalid_a);
-  else issue_atom(tc.rb, tc.lds_b + (j - T::AtomsA) * 1024, lb[j - T::AtomsA], tc.cvalid_b);
-}
-
-// One k-step: the products on `cur`, with the fragment reads of the next k-step and (if COPY)
-// the copy atoms of a later tile spread evenly between them.  The COPY step closes a loop
-// iteration, so its last product drains.
-template <class T, int BL, bool COPY>
-__device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<T>& cur, Frags<T>& nxt,
-                                      const FragAddr<T>& fa, const uint8_t* nA, const uint8_t* nB, int nkk,
-                                      const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb) {
-  // Read r goes before product (r * Products) / Reads, atom j before (j * Products) / Atoms:
-  // before product i come reads [ceil(i*R/P), ceil((i+1)*R/P)) and likewise atoms.
-  constexpr int P = T::Products, R = T::Reads, A = T::Atoms;
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-#pragma unroll
-    for (int r = (i * R + P - 1) / P; r < ((i + 1) * R + P - 1) / P; ++r) read_frag<T, BL>(nxt, fa, nA, nB, nkk, r);
-    if (COPY) {
-#pragma unroll
-      for (int j = (i * A + P - 1) / P; j < ((i + 1) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
-    }
-    const int fn = i / T::FM, fm = i % T::FM;
-    if (COPY && i == T::Products - 1) mfma16<T::AsmMfma, true>(acc[fn][fm], cur.b[fn], cur.a[fm]);
-    else mfma16<T::AsmMfma>(acc[fn][fm], cur.b[fn], cur.a[fm]);
-  }
-}
-
-// LDS chunk swizzle of the epilogue's park: rows of `cpr` 16-byte chunks; XOR the chunk index
-// so that 16 rows at one chunk (the fragment writes) and 16 consecutive chunks (the row reads)
-// fall on 16 distinct 16-byte bank groups of the 256-byte bank window.
-template <int CPR>
-__device__ __forceinline__ int park_xor(int r) {
-  if (CPR >= 16) return r & 15;
-  if (CPR == 8) return (r >> 1) & 7;
-  return (r >> 2) & 3;  // CPR == 4
-}
-
-// The epilogue: C leaves through LDS as whole rows.  A lane holds C[m][n..n+3] of each fragment,
-// so storing fragments directly would write 16 rows × 32 bytes per instruction.  Instead each
-// wave parks its block (in one or two bands of rows) in its own quarter of the now idle ring,
-// then reads it back as 16-byte pieces of whole rows, so every store instruction writes whole
-// row segments.  Whole-row stores are non-temporal: C is written once and not read again here,
-// so it should not push operand tiles out of the caches.  With SCALED the park keeps the fp32
-// sums and each piece becomes alpha·S + beta·C_old (C_old read only when beta != 0) before it is
-// rounded to C's type ("GEMM" page, tensor-core section: C <- alpha·A·B + beta·C).
-template <class T, int OUT, int SCALED>
-__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], uint8_t* park, const GemmParams& p,
-                                          int row0, int col0, int lane) {
-  constexpr int ES = OUT == 1 ? 2 : 4;                     // element size of C
-  constexpr int PES = (OUT == 1 && !SCALED) ? 2 : 4;       // element size in the park
-  constexpr int RowBytes = T::TN * PES;
-  constexpr int CPR = RowBytes / 16;
-  constexpr int EPC = 16 / PES;  // elements per 16-byte park chunk
-  constexpr int ParkBytes = T::RingBytes / 4;
-  constexpr int Bands = (T::TM * RowBytes + ParkBytes - 1) / ParkBytes;
-  constexpr int BandFM = T::FM / Bands;
-  constexpr int BandRows = 16 * BandFM;
-  constexpr int RowsPerRead = 64 / CPR;
-  constexpr int ReadsPerBand = BandRows / RowsPerRead;
-  static_assert(T::FM % Bands == 0 && BandRows % RowsPerRead == 0, "epilogue bands");
-#pragma unroll
-  for (int band = 0; band < Bands; ++band) {
-#pragma unroll
-    for (int f = 0; f < BandFM; ++f)
-#pragma unroll
-      for (int fn = 0; fn < T::FN; ++fn) {
-        const int r = 16 * f + (lane & 15);
-        const f32x4_t v = acc[fn][band * BandFM + f];
-        if (PES == 2) {
-          const int c = 2 * fn + (lane >> 5);
-          bf16x4_t h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (__bf16)v[e];
-          *(bf16x4_t*)(park + r * RowBytes + ((c ^ park_xor<CPR>(r)) << 4) + ((lane >> 4) & 1) * 8) = h;
-        } else {
-          const int c = 4 * fn + (lane >> 4);
-          *(f32x4_t*)(park + r * RowBytes + ((c ^ park_xor<CPR>(r)) << 4)) = v;
-        }
-      }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < ReadsPerBand; ++i) {
-      const int r = RowsPerRead * i + lane / CPR, c = lane % CPR;
-      const uint4 v = *(const uint4*)(park + r * RowBytes + ((c ^ park_xor<CPR>(r)) << 4));
-      const int gm = row0 + BandRows * band + r, gn = col0 + EPC * c;
-      if (gm >= p.M) continue;
-      uint8_t* dst = (uint8_t*)p.C + ((uint64_t)gm * p.ldc + gn) * ES;
-      const bool whole = p.vec_store && gn + EPC - 1 < p.N;
-      if (!SCALED) {
-        if (whole) {
-          __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)dst);
-        } else {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            if (gn + e >= p.N) continue;
-            if (OUT == 1) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-            else ((uint32_t*)dst)[e] = w[e];
-          }
-        }
-      } else {
-        // four fp32 sums per piece
-        float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-        float old[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.beta != 0.f) {
-          if (whole) {
-            if (OUT == 1) {
-              const uint2 o = *(const uint2*)dst;
-              old[0] = __uint_as_float(o.x << 16);
-              old[1] = __uint_as_float(o.x & 0xFFFF0000u);
-              old[2] = __uint_as_float(o.y << 16);
-              old[3] = __uint_as_float(o.y & 0xFFFF0000u);
-            } else {
-              const uint4 o = *(const uint4*)dst;
-              old[0] = __uint_as_float(o.x);
-              old[1] = __uint_as_float(o.y);
-              old[2] = __uint_as_float(o.z);
-              old[3] = __uint_as_float(o.w);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (gn + e >= p.N) continue;
-              old[e] = OUT == 1 ? __uint_as_float((uint32_t)((const uint16_t*)dst)[e] << 16) : ((const float*)dst)[e];
-            }
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = p.beta != 0.f ? p.alpha * x[e] + p.beta * old[e] : p.alpha * x[e];
-        if (OUT == 1) {
-          bf16x4_t h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (__bf16)x[e];
-          if (whole) {
-            *(bf16x4_t*)dst = h;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gn + e < p.N) ((__bf16*)dst)[e] = h[e];
-          }
-        } else {
-          if (whole) {
-            *(f32x4_t*)dst = f32x4_t{x[0], x[1], x[2], x[3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gn + e < p.N) ((float*)dst)[e] = x[e];
-          }
-        }
-      }
-    }
-    // The next band's writes follow these reads in this wave's LDS order.
-    if (Bands > 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  }
-}
-
-template <int BM, int BN, int BL, int OUT, int SCALED>
-__global__ void __launch_bounds__(kThreads, (TileCfg<BM, BN>::MinBlocks)) gemm_bf16_kernel(GemmParams p) {
-  using T = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::RingBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  int tm, tn;
-  map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // ---- loader: each wave copies AtomsA atoms (1 KiB each) of A and AtomsB of B per K tile ----
-  // A: box {64 k, BM m} at (k0, m0), 2-row swizzle; this wave owns box rows (BM/4)*wave .. +BM/4-1.
-  // B stored N×K: the same with n.  B stored K×N: BN/64 boxes {64 n, 64 k} at (n0 + 64*b, k0),
-  // 128B swizzle, 8 atoms each; this wave owns atoms AtomsB*wave .. +AtomsB-1 of the boxes in
-  // order, all inside one box.
-  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
-  const int b_box = (wave * T::AtomsB) >> 3;  // K×N box of this wave's B atoms
-  LaneChunk la[T::AtomsA], lb[T::AtomsB];
-#pragma unroll
-  for (int i = 0; i < T::AtomsA; ++i) la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
-#pragma unroll
-  for (int i = 0; i < T::AtomsB; ++i) {
-    if (BL == 1) {
-      lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
-    } else {
-      lb[i] = lane_chunk<3>(8 * ((wave * T::AtomsB + i) & 7), lane, pitch_b);
-      lb[i].offset += 128u * b_box;
-    }
-  }
-  const int kext = p.kchunks * 8;
-  // Columns past N in the straddling chunk are loaded as they are: they only feed outputs that
-  // are never written.
-  const int b_kn_cvalid = (p.N - n0 - 64 * b_box + 7) >> 3;
-  // At least one tile: with K = 0 every copy lane is masked, the products add zeros and the
-  // empty sum is stored.  Keeping one straight path from the accumulator initialisation to the
-  // epilogue also keeps the accumulators in fixed AGPRs (no register copies next to in-flight
-  // products).
-  const int ktiles = p.K > 0 ? (p.K + kBK - 1) / kBK : 1;
-  const uint32_t smem_addr = lds_addr_of(smem);
-
-  // Copies of tile kt into `stage`.  A tile past the end of K is issued with every lane masked
-  // (zeros land in a stage nobody reads), which keeps the loop body a single path.
-  auto make_copy = [&](int kt, int stage) {
-    TileCopy tc;
-    const int k0 = kt * kBK;
-    const bool live = kt < ktiles;
-    const uint32_t sa = smem_addr + stage * T::StageBytes;
-    const uint32_t sb = sa + T::ABytes;
-    tc.cvalid_a = live ? p.kchunks - (k0 >> 3) : -1;
-    {
-      const uint16_t* origin = p.A + (uint64_t)m0 * p.lda + (live ? k0 : 0);
-      const int64_t rem = live ? ((int64_t)(p.M - 1 - m0) * p.lda + (kext - k0)) * 2 : 0;
-      tc.ra = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
-      tc.lds_a = sa + (BM / 4) * wave * 128;
-    }
-    if (BL == 1) {
-      const uint16_t* origin = p.B + (uint64_t)n0 * p.ldb + (live ? k0 : 0);
-      const int64_t rem = live ? ((int64_t)(p.N - 1 - n0) * p.ldb + (kext - k0)) * 2 : 0;
-      tc.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
-      tc.lds_b = sb + (BN / 4) * wave * 128;
-      tc.cvalid_b = tc.cvalid_a;
-    } else {
-      const uint16_t* origin = p.B + (uint64_t)(live ? k0 : 0) * p.ldb + n0;
-      // The range check works on whole dwords: round the last row's end up to one, so a last
-      // element in the low half of a dword is still fetched.  The two bytes past it share that
-      // dword (and its page) and only reach columns past N.
-      const int64_t rem = live ? (((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2 + 3) & ~(int64_t)3 : 0;
-      tc.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
-      tc.lds_b = sb + wave * T::AtomsB * 1024;
-      tc.cvalid_b = live ? b_kn_cvalid : -1;
-    }
-    return tc;
-  };
-  auto copy_tile = [&](int kt, int stage) {
-    const TileCopy tc = make_copy(kt, stage);
-#pragma unroll
-    for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
-  };
-
-  // ---- fragment addresses ---------------------------------------------------------------------
-  // A (and B stored N×K): lane l reads row (l & 15) of a 16-row fragment, logical chunk
-  // 4*kk + (l >> 4) (eight consecutive k), at its 2-row-swizzled place.
-  FragAddr<T> fa;
-  {
-    const int arow = wm * T::TM + (lane & 15);
-    const int ax = (arow >> 1) & 7;
-    fa.a_lane = (uint32_t)arow * 128u;
-    fa.a_col[0] = (uint32_t)((lane >> 4) ^ ax) * 16u;
-    fa.a_col[1] = (uint32_t)((4 + (lane >> 4)) ^ ax) * 16u;
-    const int brow = wn * T::TN + (lane & 15);
-    const int bx = (brow >> 1) & 7;
-    fa.b_lane = (uint32_t)brow * 128u;
-    fa.b_col[0] = (uint32_t)((lane >> 4) ^ bx) * 16u;
-    fa.b_col[1] = (uint32_t)((4 + (lane >> 4)) ^ bx) * 16u;
-    // B stored K×N, transposing reads: lane 16g + 4e + q supplies the 8 bytes at k row
-    // 8g + 4h + e, columns 4q..4q+3 of a 16-column group; lane 16g + i then holds column i.
-    // Group f4 of a box is the wave's fragment (f4 of its first box, or 2*wn + fn when the
-    // wave's 32 columns are half of the single box).
-    const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
-#pragma unroll
-    for (int q = 0; q < FragAddr<T>::Q; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int f4 = T::TN >= 64 ? q : 2 * wn + q;
-        const int r = 8 * tg + 4 * h + te;  // row within a 32-row k step
-        const int c = f4 * 2 + (tq >> 1);
-        fa.b_tr[q][h] = (uint32_t)r * 128u + (uint32_t)((c ^ (r & 7)) * 16) + (uint32_t)((tq & 1) * 8);
-      }
-    fa.wn = wn;
-  }
-
-  f32x4_t acc[T::FN][T::FM];
-#pragma unroll
-  for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // ---- the ring: 2 stages of {A tile, B tile}, 2 k-steps of 32 per tile ------------------------
-  // Iteration kt: k-step 0 of tile kt (reading k-step 1's fragments), the stage barrier (tile
-  // kt+1 landed everywhere, stage kt&1 free), k-step 1 of tile kt (reading tile kt+1's first
-  // fragments and copying tile kt+2 into stage kt&1).  Every iteration runs the same code —
-  // the last one reads fragments nobody uses and issues fully masked copies — so all products
-  // sit in one loop body and the accumulators keep one register assignment throughout.
-  {
-    Frags<T> f0, f1;
-    const TileCopy none{};
-    copy_tile(0, 0);
-    copy_tile(1, 1);
-    stage_barrier<T::Atoms>();
-#pragma unroll
-    for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const uint8_t* sA = smem + (kt & 1) * T::StageBytes;
-      kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
-      stage_barrier<0>();
-      const uint8_t* nA = smem + ((kt + 1) & 1) * T::StageBytes;
-      const TileCopy tc = make_copy(kt + 2, kt & 1);
-      kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
-    }
-  }
-
-  // The loop's last product ends with the drain wait states (or, for the builtin, the
-  // compiler's own waits): the accumulators are now safe to read.  The ring is drained before it
-  // becomes the park: the last iteration's masked copies still write zeros into a stage, and the
-  // other waves may still read their fragments.
-  stage_barrier<0>();
-  store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
-}
 
 // Copy `rows` rows of `cols` bf16 values into a buffer of pitch ld_dst (a multiple of 8),
 // zero-filling columns cols..ld_dst-1: the packing step for operands whose rows are not 16-byte
@@ -502,24 +48,76 @@ hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_
   return hipGetLastError();
 }
 
-template <int BM, int BN, int SCALED>
-static hipError_t launch_tile(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
-  const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-  if (b_layout == 0 && !out_bf16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0, 0, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (b_layout == 0)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0, 1, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (!out_bf16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 0, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1, SCALED>), dim3(grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+namespace {
+
+struct GemmVariant {
+  int pipeline, bm, bn, stages;
+  GemmLauncher fn;
+};
+
+// Every built configuration.  The ring runs every tile; 256×256 has room for two stages only
+// (2 × 64 KiB of the 160 KiB of LDS).  The producer/consumer ring needs registers for its producer
+// waves next to the compute waves, which the 256×256 tile does not leave.
+const GemmVariant kVariants[] = {
+    {kPipeRing, 256, 256, 2, &launch_ring<256, 256, 2>},
+    {kPipeRing, 256, 128, 2, &launch_ring<256, 128, 2>},
+    {kPipeRing, 256, 128, 3, &launch_ring<256, 128, 3>},
+    {kPipeRing, 128, 256, 2, &launch_ring<128, 256, 2>},
+    {kPipeRing, 128, 256, 3, &launch_ring<128, 256, 3>},
+    {kPipeRing, 128, 128, 2, &launch_ring<128, 128, 2>},
+    {kPipeRing, 128, 128, 3, &launch_ring<128, 128, 3>},
+    {kPipeRing, 128, 128, 4, &launch_ring<128, 128, 4>},
+    {kPipeRing, 128, 128, 5, &launch_ring<128, 128, 5>},
+    {kPipeRing, 64, 64, 2, &launch_ring<64, 64, 2>},
+    {kPipeRing, 64, 64, 3, &launch_ring<64, 64, 3>},
+    {kPipeRing, 64, 64, 4, &launch_ring<64, 64, 4>},
+    {kPipeRing, 64, 64, 5, &launch_ring<64, 64, 5>},
+    {kPipeRing, 64, 64, 6, &launch_ring<64, 64, 6>},
+    {kPipeProducer, 256, 128, 2, &launch_pc<256, 128, 2>},
+    {kPipeProducer, 256, 128, 3, &launch_pc<256, 128, 3>},
+    {kPipeProducer, 128, 256, 2, &launch_pc<128, 256, 2>},
+    {kPipeProducer, 128, 256, 3, &launch_pc<128, 256, 3>},
+    {kPipeProducer, 128, 128, 2, &launch_pc<128, 128, 2>},
+    {kPipeProducer, 128, 128, 3, &launch_pc<128, 128, 3>},
+    {kPipeProducer, 128, 128, 4, &launch_pc<128, 128, 4>},
+    {kPipeProducer, 64, 64, 2, &launch_pc<64, 64, 2>},
+    {kPipeProducer, 64, 64, 3, &launch_pc<64, 64, 3>},
+    {kPipeProducer, 64, 64, 4, &launch_pc<64, 64, 4>},
+    {kPipeProducer, 64, 64, 5, &launch_pc<64, 64, 5>},
+    {kPipeProducer, 64, 64, 6, &launch_pc<64, 64, 6>},
+};
+
+}  // namespace
+
+GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages) {
+  for (const GemmVariant& v : kVariants)
+    if (v.pipeline == pipeline && v.bm == bm && v.bn == bn && v.stages == stages) return v.fn;
+  return nullptr;
 }
 
-template <int BM, int BN>
-static hipError_t launch_tile(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
-  return p.scaled ? launch_tile<BM, BN, 1>(p, b_layout, out_bf16, stream)
-                  : launch_tile<BM, BN, 0>(p, b_layout, out_bf16, stream);
+int default_stages(int pipeline, int bm, int bn) {
+  (void)pipeline;
+  (void)bm;
+  (void)bn;
+  return 2;
+}
+
+namespace {
+std::string configs_of(int pipeline) {
+  std::string t;
+  for (const GemmVariant& v : kVariants) {
+    if (v.pipeline != pipeline) continue;
+    char buf[48];
+    snprintf(buf, sizeof(buf), "%s%dx%d/%d", t.empty() ? "" : ", ", v.bm, v.bn, v.stages);
+    t += buf;
+  }
+  return t;
+}
+}  // namespace
+
+const char* gemm_configs_text(int pipeline) {
+  static const std::string ring = configs_of(kPipeRing), pc = configs_of(kPipeProducer);
+  return pipeline == kPipeProducer ? pc.c_str() : ring.c_str();
 }
 
 // Workgroup tile for an M×N problem on `num_cus` compute units.  Each candidate's cost is the
@@ -528,13 +126,14 @@ static hipError_t launch_tile(const GemmParams& p, int b_layout, int out_bf16, h
 // relative to the 256×256 tile (measured; fragment reads and copies per product grow as the
 // tile shrinks, and the 128×128 and 64×64 tiles run two workgroups per compute unit).  The
 // 256×256 tile wins whenever it fills the machine.
-void choose_tile(int64_t M, int64_t N, int num_cus, int& bm, int& bn) {
+void choose_tile(int64_t M, int64_t N, int num_cus, int pipeline, int& bm, int& bn) {
   struct Cand { int bm, bn; double eff; };
   static const Cand cands[] = {{256, 256, 1.00}, {128, 128, 0.80}, {256, 128, 0.69}, {128, 256, 0.66}, {64, 64, 0.49}};
   const int cus = num_cus > 0 ? num_cus : 256;
   double best = 0;
-  bm = bn = 256;
+  bm = bn = 0;
   for (const Cand& c : cands) {
+    if (!find_gemm(pipeline, c.bm, c.bn, default_stages(pipeline, c.bm, c.bn))) continue;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const int64_t rounds = (tiles + cus - 1) / cus;
     const double cost = (double)rounds * c.bm * c.bn / c.eff;
@@ -546,16 +145,14 @@ void choose_tile(int64_t M, int64_t N, int num_cus, int& bm, int& bn) {
   }
 }
 
-hipError_t launch_gemm(GemmParams p, int bm, int bn, int b_layout, int out_bf16, hipStream_t stream) {
+hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,
+                       hipStream_t stream) {
+  const GemmLauncher fn = find_gemm(pipeline, bm, bn, stages);
+  if (!fn) return hipErrorInvalidValue;
   p.tiles_m = (int)((p.M + bm - 1) / bm);
   p.tiles_n = (int)((p.N + bn - 1) / bn);
   if ((int64_t)p.tiles_m * p.tiles_n == 0) return hipSuccess;
-  if (bm == 256 && bn == 256) return launch_tile<256, 256>(p, b_layout, out_bf16, stream);
-  if (bm == 256 && bn == 128) return launch_tile<256, 128>(p, b_layout, out_bf16, stream);
-  if (bm == 128 && bn == 256) return launch_tile<128, 256>(p, b_layout, out_bf16, stream);
-  if (bm == 128 && bn == 128) return launch_tile<128, 128>(p, b_layout, out_bf16, stream);
-  if (bm == 64 && bn == 64) return launch_tile<64, 64>(p, b_layout, out_bf16, stream);
-  return hipErrorInvalidValue;
+  return fn(p, b_layout, out_bf16, stream);
 }
 
 }  // namespace tbg

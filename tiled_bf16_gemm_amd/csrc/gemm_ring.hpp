@@ -1,0 +1,133 @@
+// The barrier ring: S LDS stages, every compute wave copies its share of each stage.
+//
+// "1 · Asynchronisme et mbarrier" §1.3–§1.5 describes a multi-stage ring that loads tile t+S-1
+// while tile t is multiplied, with a full and an empty hand-off per stage.  Here the four compute
+// waves are also the copiers: each issues T::Atoms direct-to-LDS atoms of every K tile
+// (tile_loader.hpp), and one workgroup barrier per tile does both hand-offs at once — before
+// it, every wave waits for its own copies of the next tile (`s_waitcnt vmcnt`, leaving the S-2
+// newer tiles in flight); after it, those copies are visible to all waves and every wave's
+// reads of the stage that the next copies overwrite have completed.
+//
+// Iteration kt: k-step 0 of tile kt (its products, with the fragment reads of k-step 1), the
+// stage barrier (tile kt+1 landed everywhere, stage kt%S free), k-step 1 of tile kt (its
+// products, with the reads of tile kt+1's first fragments and the copies of tile kt+S into stage
+// kt%S interleaved).  Every iteration runs the same code — the last ones read fragments nobody
+// uses and issue fully masked copies — so all products sit in one loop body and the
+// accumulators keep one register assignment throughout.
+#pragma once
+#include "gemm_common.hpp"
+
+namespace tbg {
+
+template <int BM, int BN, int S>
+struct RingCfg {
+  using T = TileCfg<BM, BN>;
+  static constexpr int LdsBytes = S * T::StageBytes;
+  // Two workgroups per compute unit when two rings fit in the 160 KiB of LDS.
+  static constexpr int MinBlocks = 2 * LdsBytes <= 160 * 1024 ? 2 : 1;
+  static_assert(S >= 2, "a ring has at least two stages");
+  static_assert(LdsBytes <= 160 * 1024, "the ring must fit in LDS");
+  static_assert(T::Atoms * (S - 2) <= 63, "tiles in flight must fit the vmcnt counter");
+};
+
+template <int BM, int BN, int S, int BL, int OUT, int SCALED>
+__global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gemm_ring_kernel(GemmParams p) {
+  using T = TileCfg<BM, BN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RingCfg<BM, BN, S>::LdsBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // ---- copies: each wave copies AtomsA atoms (1 KiB each) of A and AtomsB of B per K tile ----
+  // A: box {64 k, BM m} at (k0, m0), 2-row swizzle; this wave owns box rows (BM/4)*wave .. +BM/4-1.
+  // B stored N×K: the same with n.  B stored K×N: BN/64 boxes {64 n, 64 k} at (n0 + 64*b, k0),
+  // 128B swizzle, 8 atoms each; this wave owns atoms AtomsB*wave .. +AtomsB-1 of the boxes in
+  // order, all inside one box.
+  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
+  const int b_box = (wave * T::AtomsB) >> 3;  // K×N box of this wave's B atoms
+  LaneChunk la[T::AtomsA], lb[T::AtomsB];
+#pragma unroll
+  for (int i = 0; i < T::AtomsA; ++i) la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
+#pragma unroll
+  for (int i = 0; i < T::AtomsB; ++i) {
+    if (BL == 1) {
+      lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+    } else {
+      lb[i] = lane_chunk<3>(8 * ((wave * T::AtomsB + i) & 7), lane, pitch_b);
+      lb[i].offset += 128u * b_box;
+    }
+  }
+  const int b_kn_cvalid = kn_box_cvalid(p, n0, b_box);
+  // At least one tile: with K = 0 every copy lane is masked, the products add zeros and the
+  // empty sum is stored.  Keeping one straight path from the accumulator initialisation to the
+  // epilogue also keeps the accumulators in fixed AGPRs (no register copies next to in-flight
+  // products).
+  const int ktiles = p.K > 0 ? (p.K + kBK - 1) / kBK : 1;
+  const uint32_t smem_addr = lds_addr_of(smem);
+
+  auto make_copy = [&](int kt, int stage) {
+    const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
+    TileCopy tc;
+    const uint32_t sa = smem_addr + stage * T::StageBytes;
+    const uint32_t sb = sa + T::ABytes;
+    tc.ra = o.ra;
+    tc.rb = o.rb;
+    tc.cvalid_a = o.cvalid_a;
+    tc.lds_a = sa + (BM / 4) * wave * 128;
+    if (BL == 1) {
+      tc.lds_b = sb + (BN / 4) * wave * 128;
+      tc.cvalid_b = o.cvalid_a;
+    } else {
+      tc.lds_b = sb + wave * T::AtomsB * 1024;
+      tc.cvalid_b = o.live ? b_kn_cvalid : -1;
+    }
+    return tc;
+  };
+
+  const FragAddr<T> fa = make_frag_addr<T>(wm, wn, lane);
+  f32x4_t acc[T::FN][T::FM];
+  zero_acc<T>(acc);
+
+  {
+    Frags<T> f0, f1;
+    const TileCopy none{};
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const TileCopy tc = make_copy(t, t);
+#pragma unroll
+      for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
+    }
+    stage_barrier<T::Atoms*(S - 1)>();  // tile 0 landed; tiles 1..S-1 may be in flight
+#pragma unroll
+    for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
+    int cur = 0;  // stage of tile kt
+    for (int kt = 0; kt < ktiles; ++kt) {
+      const int nxt = cur + 1 == S ? 0 : cur + 1;
+      const uint8_t* sA = smem + cur * T::StageBytes;
+      kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
+      stage_barrier<T::Atoms*(S - 2)>();  // tile kt+1 landed; tiles kt+2..kt+S-1 may be in flight
+      const uint8_t* nA = smem + nxt * T::StageBytes;
+      const TileCopy tc = make_copy(kt + S, cur);
+      kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
+      cur = nxt;
+    }
+  }
+
+  // The loop's last product ends with the drain wait states (or, for the builtin, the
+  // compiler's own waits): the accumulators are now safe to read.  The ring is drained before it
+  // becomes the park: the last iterations' masked copies still write zeros into stages, and the
+  // other waves may still read their fragments.
+  stage_barrier<0>();
+  store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
+}
+
+template <int BM, int BN, int S>
+hipError_t launch_ring(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
+  TBG_LAUNCH_INSTANCES(gemm_ring_kernel, kThreads, BM, BN, S);
+}
+
+}  // namespace tbg

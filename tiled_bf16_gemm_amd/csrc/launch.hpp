@@ -25,10 +25,29 @@ hipError_t launch_tiled_store(const DescImpl& d, const int32_t* host_coords, con
                               const void* src, hipStream_t stream);
 hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
                              void* dst, hipStream_t stream);
-// Workgroup tile (bm × bn) for an M×N product on a device with num_cus compute units.
-void choose_tile(int64_t M, int64_t N, int num_cus, int& bm, int& bn);
-// Launch with tile bm × bn (256×256, 256×128, 128×256, 128×128 or 64×64); fills tiles_m/tiles_n.
-hipError_t launch_gemm(GemmParams p, int bm, int bn, int b_layout, int out_bf16, hipStream_t stream);
+// Operand-copy pipelines of the GEMM (values of tbg_pipeline).
+enum GemmPipeline { kPipeRing = 1, kPipeProducer = 2 };
+
+// One built kernel configuration; tiles_m / tiles_n of `p` must be set.
+typedef hipError_t (*GemmLauncher)(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
+template <int BM, int BN, int S>
+hipError_t launch_ring(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
+template <int BM, int BN, int S>
+hipError_t launch_pc(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
+
+// The launcher of (pipeline, tile bm × bn, stages), or nullptr when that configuration is not built.
+GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages);
+// Stage count used when the caller leaves it open.
+int default_stages(int pipeline, int bm, int bn);
+// Workgroup tile (bm × bn) for an M×N product on a device with num_cus compute units, among the
+// tiles the pipeline is built for.
+void choose_tile(int64_t M, int64_t N, int num_cus, int pipeline, int& bm, int& bn);
+// Readable list of the built configurations of a pipeline (for error messages).
+const char* gemm_configs_text(int pipeline);
+// Launch a built configuration; fills tiles_m / tiles_n.  Returns hipErrorInvalidValue for a
+// configuration find_gemm does not know.
+hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,
+                       hipStream_t stream);
 hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ld_dst,
                        hipStream_t stream);
 

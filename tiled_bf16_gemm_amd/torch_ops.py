@@ -26,10 +26,12 @@ def _require(t: torch.Tensor, name: str):
 
 def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str = "bf16",
          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-         stream: Optional[torch.cuda.Stream] = None, alpha: float = 1.0, beta: float = 0.0) -> torch.Tensor:
-    """C = alpha·A·B + beta·C through tbg_gemm (alpha = 1, beta = 0) or tbg_gemm_ex.  A: (M, K)
-    bf16 view; B: (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading dimensions.
-    `out` (M, N) may be a strided view; with beta != 0 it must hold the old C."""
+         stream: Optional[torch.cuda.Stream] = None, alpha: float = 1.0, beta: float = 0.0,
+         config: Optional[tbg.GemmConfig] = None) -> torch.Tensor:
+    """C = alpha·A·B + beta·C through tbg_gemm (alpha = 1, beta = 0), tbg_gemm_ex, or
+    tbg_gemm_configured when `config` (tbg.gemm_config(...)) is given.  A: (M, K) bf16 view; B:
+    (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading dimensions.  `out` (M, N)
+    may be a strided view; with beta != 0 it must hold the old C."""
     _require(A, "A")
     _require(B, "B")
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -56,7 +58,10 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if alpha == 1.0 and beta == 0.0:
+    if config is not None:
+        tbg.gemm_configured(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, beta, out.data_ptr(), ldc,
+                            out_dtype, config, ws_ptr, ws_bytes, stream_handle(stream))
+    elif alpha == 1.0 and beta == 0.0:
         tbg.gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, out.data_ptr(), ldc, out_dtype,
                  ws_ptr, ws_bytes, stream_handle(stream))
     else:
