@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz ("2.5 PF")
 METRIC = "bf16 GEMM TFLOP/s and % of MI355X MFMA peak at M=N=K=8192, 1 GPU"
-KERNEL_SOURCES = ["tiled_bf16_gemm_amd/csrc/gemm_kernel.hip", "tiled_bf16_gemm_amd/csrc/tile_loader.hpp"]
+KERNEL_SOURCES = ["tiled_bf16_gemm_amd/csrc/gemm_common.hpp", "tiled_bf16_gemm_amd/csrc/gemm_ring.hpp",
+                  "tiled_bf16_gemm_amd/csrc/tile_loader.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_8192_traffic.json")
 
 
@@ -54,7 +55,7 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def time_gemm(torch, torch_ops, w, steps, warmup):
+def time_gemm(torch, torch_ops, w, steps, warmup, config=None):
     """Returns (ms per step over the whole timed region, mean per-launch ms from events)."""
     import workloads
     A, B = workloads.gemm_inputs(w)
@@ -68,14 +69,14 @@ def time_gemm(torch, torch_ops, w, steps, warmup):
     need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
-        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws, config=config)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
-        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws, config=config)
         ends[i].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
@@ -147,7 +148,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
         finally:
             c.close()
 
-    gemm_name = "gemm_bf16_kernel"
+    gemm_name = "gemm_ring_kernel"
     top = rows(trace_db, "select name, total_calls, total_duration, average, percentage from top_kernels")
     lines = ["# GEMM kernel trace, 8192^3 workload (bf16 in, fp32 accumulate, bf16 out)", "",
              "Command (<repo> is the repository root on the GPU box):", "", "```", commands["trace"], "```", "",
@@ -203,6 +204,33 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
     return traffic
 
 
+# Every built (pipeline, tile, stages) configuration, as include/tbg.h lists them.
+SWEEP_CONFIGS = ([("ring", "256x256", 2)] + [("ring", t, st) for t in ("256x128", "128x256") for st in (2, 3)]
+                 + [("ring", "128x128", st) for st in (2, 3, 4, 5)] + [("ring", "64x64", st) for st in range(2, 7)]
+                 + [("producer", t, st) for t in ("256x128", "128x256") for st in (2, 3)]
+                 + [("producer", "128x128", st) for st in (2, 3, 4)]
+                 + [("producer", "64x64", st) for st in range(2, 7)])
+
+
+def sweep(torch, torch_ops, names, steps, warmup):
+    """Time every built configuration on the named workloads; one JSON line per measurement."""
+    import tiled_bf16_gemm_amd as tbg
+    import workloads
+    results = []
+    for name in names:
+        w = workloads.GEMMS[name]
+        for pipe, tile, st in SWEEP_CONFIGS:
+            cfg = tbg.gemm_config(tile, st, pipe)
+            ms, kms, _ = time_gemm(torch, torch_ops, w, steps, warmup, config=cfg)
+            tf = w.flops / (ms * 1e-3) / 1e12
+            r = {"workload": name, "pipeline": pipe, "tile": tile, "stages": st, "ms": round(ms, 5),
+                 "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+            print(json.dumps(r), flush=True)
+            results.append(r)
+        torch.cuda.empty_cache()
+    return results
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +241,9 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated workloads (c1..c5): time every built pipeline/tile/stages configuration "
+                         "on each and print one JSON line per measurement instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the GEMM shards across GPUs "
@@ -228,6 +259,9 @@ def main():
     w = workloads.GEMMS["c4"]
     if args.counters:
         counters_driver(torch, torch_ops, w)
+        return
+    if args.sweep:
+        sweep(torch, torch_ops, args.sweep.split(","), 20, 5)
         return
     ms_step, ms_kernel, wall_ms = time_gemm(torch, torch_ops, w, args.steps, args.warmup)
     tflops = w.flops / (ms_step * 1e-3) / 1e12

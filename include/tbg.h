@@ -189,15 +189,18 @@ tbg_status tbg_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const void*
  *                      by one thread); the compute waves issue no copies.  Each stage has a full
  *                      and an empty counter in LDS ([PIPE] §1.5: the two barriers per stage),
  *                      polled with short sleeps.
- *   TBG_PIPE_AUTO      the library's choice (currently the ring). */
+ *   TBG_PIPE_AUTO      the library's choice, made with the tile from measured throughput: the
+ *                      ring for 256x256, 128x128 and 64x64 tiles, producer waves for 256x128 and
+ *                      128x256 tiles. */
 typedef enum { TBG_PIPE_AUTO = 0, TBG_PIPE_RING = 1, TBG_PIPE_PRODUCER = 2 } tbg_pipeline;
 
 /* Kernel configuration of tbg_gemm_configured.  Zero fields are left to the library.
  *   tile_m, tile_n  workgroup tile of C ([GEMM] "Tiling"): both 0 (chosen from the shape), or
  *                   one of 256x256, 256x128, 128x256, 128x128, 64x64.
- *   stages          LDS stages of the ring: 0 (default, 2) or >= 2.  Each stage holds one
- *                   tile_m x 64 block of A and one 64 x tile_n block of B in bf16, so the count
- *                   is bounded by the 160 KiB of LDS.
+ *   stages          LDS stages of the ring: 0 (default: 2; 3 for the producer pipeline's 128x128
+ *                   and 64x64 tiles) or >= 2.  Each stage holds one tile_m x 64 block of A and
+ *                   one 64 x tile_n block of B in bf16, so the count is bounded by the 160 KiB
+ *                   of LDS.
  *   pipeline        a tbg_pipeline value.
  * Built configurations (tile / stages):
  *   ring:      256x256/2; 256x128 and 128x256/2-3; 128x128/2-5; 64x64/2-6

@@ -315,24 +315,24 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   if ((int)bl != TBG_B_KN && (int)bl != TBG_B_NK) return fail(TBG_ERR_INVALID_VALUE, "unknown b_layout %d", (int)bl);
   // Kernel configuration: checked in full before anything else can fail on a machine without a
   // device, so that the checks are the same everywhere.
-  int pipeline = tbg::kPipeRing, bm = 0, bn = 0, stages = 0;
+  int pipeline = 0, bm = 0, bn = 0, stages = 0;  // 0: left to the library
   if (cfg) {
     if (cfg->pipeline != TBG_PIPE_AUTO && cfg->pipeline != TBG_PIPE_RING && cfg->pipeline != TBG_PIPE_PRODUCER)
       return fail(TBG_ERR_INVALID_VALUE, "unknown pipeline %d", (int)cfg->pipeline);
     if ((cfg->tile_m == 0) != (cfg->tile_n == 0))
       return fail(TBG_ERR_INVALID_VALUE, "tile_m and tile_n must both be 0 or both be set");
     if (cfg->stages < 0 || cfg->stages == 1) return fail(TBG_ERR_INVALID_VALUE, "stages must be 0 or >= 2");
-    if (cfg->pipeline == TBG_PIPE_PRODUCER) pipeline = tbg::kPipeProducer;
+    pipeline = cfg->pipeline == TBG_PIPE_RING ? tbg::kPipeRing
+               : cfg->pipeline == TBG_PIPE_PRODUCER ? tbg::kPipeProducer : 0;
     bm = cfg->tile_m;
     bn = cfg->tile_n;
     stages = cfg->stages;
-    if (bm != 0) {
-      const int st = stages ? stages : tbg::default_stages(pipeline, bm, bn);
-      if (!tbg::find_gemm(pipeline, bm, bn, st))
-        return fail(TBG_ERR_UNSUPPORTED, "no %s kernel with tile %dx%d and %d stages (built: %s)",
-                    pipeline == tbg::kPipeProducer ? "producer/consumer" : "ring", bm, bn, st,
-                    tbg::gemm_configs_text(pipeline));
-    }
+    tbg::GemmChoice probe;
+    // Whether anything built matches what is fixed does not depend on the shape or the device.
+    if (!tbg::choose_gemm(256, 256, 256, pipeline, bm, bn, stages, probe))
+      return fail(TBG_ERR_UNSUPPORTED, "no %skernel with tile %dx%d and %d stages (built: ring %s; producer %s)",
+                  pipeline == tbg::kPipeProducer ? "producer/consumer " : pipeline == tbg::kPipeRing ? "ring " : "",
+                  bm, bn, stages, tbg::gemm_configs_text(tbg::kPipeRing), tbg::gemm_configs_text(tbg::kPipeProducer));
   }
   if (scaled && alpha == 0.f) {  // the empty product: nothing of A or B is used
     K = 0;
@@ -396,12 +396,10 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.N = (int)N;
   p.K = (int)K;
   p.kchunks = (int)(pl.kext / 8);
-  // Workgroup tile: the caller's, or chosen from the shape and the device among the tiles the
-  // pipeline is built for; then the stage count.
-  if (bm == 0) tbg::choose_tile(M, N, num_cus, pipeline, bm, bn);
-  if (stages == 0) stages = tbg::default_stages(pipeline, bm, bn);
-  if (!tbg::find_gemm(pipeline, bm, bn, stages))
-    return fail(TBG_ERR_UNSUPPORTED, "no kernel with tile %dx%d and %d stages", bm, bn, stages);
+  // Kernel configuration: what the caller fixed, the rest chosen from the shape and the device.
+  tbg::GemmChoice ch;
+  if (!tbg::choose_gemm(M, N, num_cus, pipeline, bm, bn, stages, ch))
+    return fail(TBG_ERR_UNSUPPORTED, "no built kernel matches tile %dx%d with %d stages", bm, bn, stages);
   p.tiles_m = 0;
   p.tiles_n = 0;
   p.group_m = env_int("TBG_GROUP_M", 8);
@@ -410,7 +408,7 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
-  e = tbg::launch_gemm(p, pipeline, bm, bn, stages, (int)bl, c_dtype == TBG_BF16, s);
+  e = tbg::launch_gemm(p, ch.pipeline, ch.bm, ch.bn, ch.stages, (int)bl, c_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
 }

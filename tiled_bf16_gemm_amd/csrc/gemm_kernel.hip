@@ -95,13 +95,6 @@ GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages) {
   return nullptr;
 }
 
-int default_stages(int pipeline, int bm, int bn) {
-  (void)pipeline;
-  (void)bm;
-  (void)bn;
-  return 2;
-}
-
 namespace {
 std::string configs_of(int pipeline) {
   std::string t;
@@ -120,29 +113,48 @@ const char* gemm_configs_text(int pipeline) {
   return pipeline == kPipeProducer ? pc.c_str() : ring.c_str();
 }
 
-// Workgroup tile for an M×N problem on `num_cus` compute units.  Each candidate's cost is the
-// number of tiles the busiest compute unit computes times the work of one tile divided by the
-// tile's relative efficiency: its throughput on the 8192³ and 16384×14336×4096 products
-// relative to the 256×256 tile (measured; fragment reads and copies per product grow as the
-// tile shrinks, and the 128×128 and 64×64 tiles run two workgroups per compute unit).  The
-// 256×256 tile wins whenever it fills the machine.
-void choose_tile(int64_t M, int64_t N, int num_cus, int pipeline, int& bm, int& bn) {
-  struct Cand { int bm, bn; double eff; };
-  static const Cand cands[] = {{256, 256, 1.00}, {128, 128, 0.80}, {256, 128, 0.69}, {128, 256, 0.66}, {64, 64, 0.49}};
+// Candidates of the automatic choice: every built (pipeline, tile) pair with its default stage
+// count and its efficiency — throughput on the 8192³ and 16384×14336×4096 products relative to
+// the 256×256 ring (measured with the configuration sweep of bench.py).  Fragment reads and copies
+// per product grow as the tile shrinks; the 128×128 ring and the 64×64 tiles run two workgroups
+// per compute unit; with dedicated producer waves the 256×128 and 128×256 tiles keep their
+// compute waves free of copy instructions and run 18 % faster than as a ring, while the 128×128
+// and 64×64 tiles lose the second workgroup per compute unit to the extra waves or the deeper
+// ring and run slower.  Deeper rings lose occupancy and never win at the default.
+namespace {
+struct Candidate {
+  int pipeline, bm, bn, stages;
+  double eff;
+};
+const Candidate kCandidates[] = {
+    {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 256, 128, 2, 0.86}, {kPipeProducer, 128, 256, 2, 0.86},
+    {kPipeRing, 128, 128, 2, 0.82},     {kPipeRing, 256, 128, 2, 0.73},     {kPipeRing, 128, 256, 2, 0.72},
+    {kPipeProducer, 128, 128, 3, 0.69}, {kPipeRing, 64, 64, 2, 0.52},       {kPipeProducer, 64, 64, 3, 0.34},
+};
+}  // namespace
+
+// Each candidate's cost is the number of tiles the busiest compute unit computes times the work
+// of one tile divided by the candidate's efficiency; the cheapest wins (the 256×256 ring whenever
+// it fills the machine).
+bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn, int stages, GemmChoice& out) {
   const int cus = num_cus > 0 ? num_cus : 256;
   double best = 0;
-  bm = bn = 0;
-  for (const Cand& c : cands) {
-    if (!find_gemm(pipeline, c.bm, c.bn, default_stages(pipeline, c.bm, c.bn))) continue;
+  bool found = false;
+  for (const Candidate& c : kCandidates) {
+    if (pipeline != 0 && c.pipeline != pipeline) continue;
+    if (bm != 0 && (c.bm != bm || c.bn != bn)) continue;
+    const int st = stages != 0 ? stages : c.stages;
+    if (!find_gemm(c.pipeline, c.bm, c.bn, st)) continue;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const int64_t rounds = (tiles + cus - 1) / cus;
-    const double cost = (double)rounds * c.bm * c.bn / c.eff;
-    if (best == 0 || cost < best * 0.999) {
+    const double cost = (double)(rounds > 0 ? rounds : 1) * c.bm * c.bn / c.eff;
+    if (!found || cost < best * 0.999) {
       best = cost;
-      bm = c.bm;
-      bn = c.bn;
+      out = GemmChoice{c.pipeline, c.bm, c.bn, st};
+      found = true;
     }
   }
+  return found;
 }
 
 hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,

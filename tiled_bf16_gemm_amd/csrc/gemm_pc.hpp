@@ -58,6 +58,67 @@ __device__ __forceinline__ void arrive(uint32_t* counter, int lane) {
   if (lane == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Producer wave PW: atoms PW*PA .. PW*PA+PA-1 of every K tile.  Atom j < BM/8 is rows 8j..8j+7
+// of the A box; atom j = BM/8 + i is rows 8i.. of the N×K B box, or atom i%8 of the K×N box i/8.
+// Atom j lands at stage byte 1024 j (the layout the compute waves read, the same as the barrier
+// ring's).  Tile t is issued once every compute wave has released the stage's previous tile, and
+// marked full once the copies of tile t landed, S-2 tiles later.
+template <int BM, int BN, int S, int BL, int PW>
+__device__ __forceinline__ void produce(const GemmParams& p, const uint8_t* smem, uint32_t* full, uint32_t* empty,
+                                        int m0, int n0, int ktiles, int lane) {
+  using C = PcCfg<BM, BN, S>;
+  using T = TileCfg<BM, BN>;
+  static_assert(PW < C::NP, "producer wave index");
+  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
+  const uint32_t smem_addr = lds_addr_of(smem);
+  LaneChunk ch[C::PA];
+#pragma unroll
+  for (int i = 0; i < C::PA; ++i) {
+    const int j = PW * C::PA + i;
+    if (j < BM / 8) {
+      ch[i] = lane_chunk<kSwizzle128B2Row>(8 * j, lane, pitch_a);
+    } else if (BL == 1) {
+      ch[i] = lane_chunk<kSwizzle128B2Row>(8 * (j - BM / 8), lane, pitch_b);
+    } else {
+      const int jb = j - BM / 8;
+      ch[i] = lane_chunk<3>(8 * (jb & 7), lane, pitch_b);
+      ch[i].offset += 128u * (uint32_t)(jb >> 3);
+    }
+  }
+  int st = 0, fill = 0;     // stage and fill round of tile kt
+  int sig = 0, sig_st = 0;  // next tile to mark full, and its stage
+  for (int kt = 0; kt < ktiles; ++kt) {
+    if (fill > 0) wait_counter(&empty[st], 4u * (uint32_t)fill);
+    const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
+    const uint32_t base = smem_addr + (uint32_t)(st * T::StageBytes);
+#pragma unroll
+    for (int i = 0; i < C::PA; ++i) {
+      const int j = PW * C::PA + i;
+      if (j < BM / 8) {
+        issue_atom(o.ra, base + 1024u * j, ch[i], o.cvalid_a);
+      } else {
+        const int cv = BL == 1 ? o.cvalid_a : (o.live ? kn_box_cvalid(p, n0, (j - BM / 8) >> 3) : -1);
+        issue_atom(o.rb, base + 1024u * j, ch[i], cv);
+      }
+    }
+    if (kt >= S - 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::PA * (S - 2)) : "memory");
+      arrive(&full[sig_st], lane);
+      ++sig;
+      sig_st = sig_st + 1 == S ? 0 : sig_st + 1;
+    }
+    if (++st == S) {
+      st = 0;
+      ++fill;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (; sig < ktiles; ++sig) {
+    arrive(&full[sig_st], lane);
+    sig_st = sig_st + 1 == S ? 0 : sig_st + 1;
+  }
+}
+
 template <int BM, int BN, int S, int BL, int OUT, int SCALED>
 __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>::MinBlocks))
     gemm_pc_kernel(GemmParams p) {
@@ -66,7 +127,9 @@ __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LdsBytes];
   __shared__ uint32_t full[S], empty[S];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform across the wave: keeping it scalar turns every role and atom-kind
+  // test below into a scalar branch instead of an exec-mask region.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (threadIdx.x < S) {
     full[threadIdx.x] = 0;
     empty[threadIdx.x] = 0;
@@ -79,58 +142,13 @@ __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>
   const int ktiles = p.K > 0 ? (p.K + kBK - 1) / kBK : 1;
 
   if (wave >= 4) {
-    // ---- producer wave pw: atoms pw*PA .. pw*PA+PA-1 of every tile --------------------------
-    // Atom j < BM/8 is rows 8j..8j+7 of the A box; atom j = BM/8 + i is rows 8i.. of the N×K B
-    // box, or atom i%8 of the K×N box i/8.  Atom j lands at stage byte 1024 j.
+    // Producer wave pw runs a copy of the loop specialised to its atoms (all index arithmetic
+    // and atom kinds then fold at compile time).
     const int pw = wave - 4;
-    const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
-    const uint32_t smem_addr = lds_addr_of(smem);
-    LaneChunk ch[C::PA];
-#pragma unroll
-    for (int i = 0; i < C::PA; ++i) {
-      const int j = pw * C::PA + i;
-      if (j < BM / 8) {
-        ch[i] = lane_chunk<kSwizzle128B2Row>(8 * j, lane, pitch_a);
-      } else if (BL == 1) {
-        ch[i] = lane_chunk<kSwizzle128B2Row>(8 * (j - BM / 8), lane, pitch_b);
-      } else {
-        const int jb = j - BM / 8;
-        ch[i] = lane_chunk<3>(8 * (jb & 7), lane, pitch_b);
-        ch[i].offset += 128u * (uint32_t)(jb >> 3);
-      }
-    }
-    int st = 0, fill = 0;      // stage and fill round of tile kt
-    int sig = 0, sig_st = 0;   // next tile to mark full, and its stage
-    for (int kt = 0; kt < ktiles; ++kt) {
-      if (fill > 0) wait_counter(&empty[st], 4u * (uint32_t)fill);
-      const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
-      const uint32_t base = smem_addr + (uint32_t)(st * T::StageBytes);
-#pragma unroll
-      for (int i = 0; i < C::PA; ++i) {
-        const int j = pw * C::PA + i;
-        if (j < BM / 8) {
-          issue_atom(o.ra, base + 1024u * j, ch[i], o.cvalid_a);
-        } else {
-          const int cv = BL == 1 ? o.cvalid_a : (o.live ? kn_box_cvalid(p, n0, (j - BM / 8) >> 3) : -1);
-          issue_atom(o.rb, base + 1024u * j, ch[i], cv);
-        }
-      }
-      if (kt >= S - 2) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::PA * (S - 2)) : "memory");
-        arrive(&full[sig_st], lane);
-        ++sig;
-        sig_st = sig_st + 1 == S ? 0 : sig_st + 1;
-      }
-      if (++st == S) {
-        st = 0;
-        ++fill;
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    for (; sig < ktiles; ++sig) {
-      arrive(&full[sig_st], lane);
-      sig_st = sig_st + 1 == S ? 0 : sig_st + 1;
-    }
+    if (pw == 0) produce<BM, BN, S, BL, 0>(p, smem, full, empty, m0, n0, ktiles, lane);
+    if (C::NP > 1 && pw == 1) produce<BM, BN, S, BL, (C::NP > 1 ? 1 : 0)>(p, smem, full, empty, m0, n0, ktiles, lane);
+    if (C::NP > 2 && pw == 2) produce<BM, BN, S, BL, (C::NP > 2 ? 2 : 0)>(p, smem, full, empty, m0, n0, ktiles, lane);
+    if (C::NP > 3 && pw == 3) produce<BM, BN, S, BL, (C::NP > 3 ? 3 : 0)>(p, smem, full, empty, m0, n0, ktiles, lane);
     __syncthreads();
     return;
   }

@@ -37,13 +37,16 @@ hipError_t launch_pc(const GemmParams& p, int b_layout, int out_bf16, hipStream_
 
 // The launcher of (pipeline, tile bm × bn, stages), or nullptr when that configuration is not built.
 GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages);
-// Stage count used when the caller leaves it open.
-int default_stages(int pipeline, int bm, int bn);
-// Workgroup tile (bm × bn) for an M×N product on a device with num_cus compute units, among the
-// tiles the pipeline is built for.
-void choose_tile(int64_t M, int64_t N, int num_cus, int pipeline, int& bm, int& bn);
 // Readable list of the built configurations of a pipeline (for error messages).
 const char* gemm_configs_text(int pipeline);
+
+// A kernel configuration for an M×N product on a device with num_cus compute units.  Zero
+// arguments are open: pipeline 0 = either pipeline, bm = bn = 0 = any tile, stages 0 = each
+// candidate's default.  Returns false when no built configuration matches what is fixed.
+struct GemmChoice {
+  int pipeline, bm, bn, stages;
+};
+bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn, int stages, GemmChoice& out);
 // Launch a built configuration; fills tiles_m / tiles_n.  Returns hipErrorInvalidValue for a
 // configuration find_gemm does not know.
 hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,
