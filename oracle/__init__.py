@@ -12,6 +12,9 @@ this module only marshals numpy arrays into it.  Every routine cites the passage
 * ``gemm`` / ``gemm_points`` — "GEMM: la moltiplicazione di matrici sull'hardware", section
   "Il conto, e il problema della versione ingenua" (C = A·B, 2MNK) and the tensor-core section
   (16-bit inputs, wide accumulation).
+* ``im2col_copy`` / ``conv2d`` — "2 · Le Tensor Memory Accelerator", section "im2col" (a copy
+  mode that forms the im2col matrix of a convolution on the fly, so the convolution becomes a
+  GEMM); the convolution itself by its definition.
 
 Parity status: all routines pinned by ``tests/test_oracle_pins.py``; the GEMM is exact only up
 to the summation order, which the pages leave open (tolerance 1e-2 relative / 1e-3 absolute).
@@ -73,6 +76,16 @@ class Oracle:
                                            _i64p, _f64p, _f32p]
         lib.oracle_f32_to_bf16_array.restype = None
         lib.oracle_f32_to_bf16_array.argtypes = [_f32p, _u16p, ctypes.c_int64]
+        lib.oracle_conv_out_dim.restype = ctypes.c_int64
+        lib.oracle_conv_out_dim.argtypes = [ctypes.c_int64] * 6
+        lib.oracle_im2col_copy.restype = ctypes.c_uint64
+        lib.oracle_im2col_copy.argtypes = [ctypes.c_int, ctypes.c_void_p, _u64p, _u64p, _i32p, _i32p, _i32p, _i32p,
+                                           _i32p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, _i32p, ctypes.c_void_p]
+        lib.oracle_conv2d_rows.restype = None
+        lib.oracle_conv2d_rows.argtypes = [_u16p, _u16p] + [ctypes.c_int64] * 7 + [_i32p, ctypes.c_int64,
+                                                                                     ctypes.c_int64, _f64p, _f32p,
+                                                                                     ctypes.c_int64, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         self.lib = lib
@@ -189,6 +202,58 @@ class Oracle:
                                     {"kn": 0, "nk": 1}[b_layout], ms.size, ms.ctypes.data_as(_i64p),
                                     ns.ctypes.data_as(_i64p), out64.ctypes.data_as(_f64p),
                                     out32.ctypes.data_as(_f32p))
+        return (out32, out64) if want64 else out32
+
+    # -- O2i / O5 ----------------------------------------------------------------------------
+    def conv_out_dim(self, n: int, pad_lo: int, pad_hi: int, stride: int, dil: int, filt: int) -> int:
+        return int(self.lib.oracle_conv_out_dim(n, pad_lo, pad_hi, stride, dil, filt))
+
+    def im2col_copy(self, src: np.ndarray, dtype: str, dims: Sequence[int], strides_bytes: Sequence[int],
+                    pad_lo: Sequence[int], pad_hi: Sequence[int], cstride: Sequence[int], dil: Sequence[int],
+                    filt: Sequence[int], channels: int, pixels: int, swizzle: str | int, oob_nan: bool,
+                    coords: Sequence[int]) -> np.ndarray:
+        """One im2col block of the NHWC tensor ``src`` (raw bytes; dims {C, W, H, N}, strides
+        {sW, sH, sN} in bytes; per-spatial arrays {along W, along H}; coords {c0, m0, s, r}).
+        Returns the image as uint8 (pixels rows of channels elements, channel fastest)."""
+        elsize, nan_kind = DTYPES[dtype]
+        m = SWIZZLE_MODES[swizzle] if isinstance(swizzle, str) else int(swizzle)
+        image = elsize * int(channels) * int(pixels)
+        dst = np.zeros(max(image, 1), dtype=np.uint8)
+        srcb = np.ascontiguousarray(src).view(np.uint8)
+        arr = lambda v, t: np.array(list(v), dtype=t)  # noqa: E731
+        d, st = arr(dims, np.uint64), arr(strides_bytes, np.uint64)
+        pl, ph, cs, dl, fl, c = (arr(v, np.int32) for v in (pad_lo, pad_hi, cstride, dil, filt, coords))
+        got = self.lib.oracle_im2col_copy(elsize, srcb.ctypes.data, d.ctypes.data_as(_u64p), st.ctypes.data_as(_u64p),
+                                          pl.ctypes.data_as(_i32p), ph.ctypes.data_as(_i32p),
+                                          cs.ctypes.data_as(_i32p), dl.ctypes.data_as(_i32p),
+                                          fl.ctypes.data_as(_i32p), int(channels), int(pixels), m,
+                                          int(bool(oob_nan)), nan_kind, c.ctypes.data_as(_i32p), dst.ctypes.data)
+        if got == 0:
+            raise ValueError("oracle_im2col_copy declined these arguments")
+        assert got == image
+        return dst[:image]
+
+    def conv2d(self, X: np.ndarray, Wt: np.ndarray, n: int, h: int, w: int, c: int, k: int, r: int, s: int,
+               pad=(0, 0, 0, 0), stride=(1, 1), dil=(1, 1), rows: Optional[tuple] = None, want64: bool = False,
+               threads: int = 0):
+        """Rows [m0, m1) of the 2-D convolution Y (N*OH*OW × K), X NHWC and Wt KRSC as uint16
+        bf16 bits.  pad = (top, left, bottom, right), stride/dil = (h, w).  Returns float32
+        rows (and the float64 sums if asked)."""
+        X = np.ascontiguousarray(X, dtype=np.uint16).reshape(-1)
+        Wt = np.ascontiguousarray(Wt, dtype=np.uint16).reshape(-1)
+        geom = np.array([pad[0], pad[1], pad[2], pad[3], stride[0], stride[1], dil[0], dil[1]], dtype=np.int32)
+        oh = self.conv_out_dim(h, pad[0], pad[2], stride[0], dil[0], r)
+        ow = self.conv_out_dim(w, pad[1], pad[3], stride[1], dil[1], s)
+        M = n * oh * ow
+        m0, m1 = rows if rows is not None else (0, M)
+        out32 = np.empty((m1 - m0, k), dtype=np.float32)
+        out64 = np.empty((m1 - m0, k), dtype=np.float64) if want64 else None
+        nthr = threads if threads > 0 else self.lib.oracle_max_threads()
+        if m1 > m0 and k > 0:
+            self.lib.oracle_conv2d_rows(X.ctypes.data_as(_u16p), Wt.ctypes.data_as(_u16p), n, h, w, c, k, r, s,
+                                        geom.ctypes.data_as(_i32p), m0, m1,
+                                        out64.ctypes.data_as(_f64p) if want64 else None,
+                                        out32.ctypes.data_as(_f32p), k, nthr)
         return (out32, out64) if want64 else out32
 
     def f32_to_bf16(self, x: np.ndarray) -> np.ndarray:

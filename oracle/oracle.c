@@ -1,5 +1,6 @@
 /*
- * oracle.c — plain, slow CPU reference for the tiled copy and the bf16 GEMM.
+ * oracle.c — plain, slow CPU reference for the tiled copy, the bf16 GEMM, the im2col copy and
+ * the 2-D convolution.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load this file's
  * library: only the test suite, the smoke check and the CPU-baseline leg of the benchmark do.
@@ -273,6 +274,129 @@ void oracle_gemm_points(int64_t K, const uint16_t* A, int64_t lda, const uint16_
         }
         if (out64) out64[p] = acc;
         if (out32) out32[p] = (float)acc;
+    }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Output extent of a convolution along one spatial dimension: the number of window positions
+ * p >= 0 with p*stride - pad_lo + dil*(filt-1) <= in - 1 + pad_hi, i.e.
+ * floor((in + pad_lo + pad_hi - dil*(filt-1) - 1) / stride) + 1, or 0 if the window never fits.
+ * ---------------------------------------------------------------------------------------- */
+int64_t oracle_conv_out_dim(int64_t in, int64_t pad_lo, int64_t pad_hi, int64_t stride, int64_t dil,
+                            int64_t filt) {
+    int64_t span = in + pad_lo + pad_hi - dil * (filt - 1) - 1;
+    if (stride < 1 || dil < 1 || filt < 1 || span < 0) return 0;
+    return span / stride + 1;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * O2i — im2col copy: one block of the im2col matrix of a 2-D convolution.
+ * [TMA] section "im2col": a copy mode dedicated to convolution performs the im2col transform
+ * while copying, so the convolution becomes a GEMM and the intermediate matrix is never stored.
+ * The page gives nothing more; the reading taken (plain im2col with the tiled mode's image,
+ * swizzle and fill rules):
+ *   - the tensor X is NHWC: dims = {C, W, H, N} innermost first, byte strides {sW, sH, sN}
+ *     (the channel stride is the element size);
+ *   - row m of the im2col matrix is output pixel m = (n*OH + oh)*OW + ow; column (r, s, c) is
+ *     filter tap (r along H, s along W) and channel c; its element is
+ *     X[n, oh*sh - ph + r*dh, ow*sw - pw + s*dw, c], zero (or the fill) where that position is
+ *     outside the tensor — the zero padding of the convolution — and for rows m outside
+ *     0..N*OH*OW-1 and channels outside 0..C-1;
+ *   - one copy takes `pixels` consecutive rows from m0 and `channels` consecutive channels from
+ *     c0 at one tap (r, s): coords = {c0, m0, s, r}; the image is dense, channel fastest
+ *     (element (i, j) at byte elsize*(j + channels*i)), through the swizzle like a tiled copy.
+ *   pad_lo/pad_hi/cstride/dil/filt: {along W, along H}.  elsize, nan_kind as oracle_tiled_copy.
+ * Returns the image size in bytes, or 0 on an argument this plain reference does not take.
+ * ---------------------------------------------------------------------------------------- */
+uint64_t oracle_im2col_copy(int elsize, const void* src, const uint64_t* dims, const uint64_t* strides_bytes,
+                            const int32_t* pad_lo, const int32_t* pad_hi, const int32_t* cstride,
+                            const int32_t* dil, const int32_t* filt, uint32_t channels, uint32_t pixels,
+                            int swizzle, int oob_nan, int nan_kind, const int32_t* coords, void* dst) {
+    if (elsize != 1 && elsize != 2 && elsize != 4) return 0;
+    const int64_t C = (int64_t)dims[0], W = (int64_t)dims[1], H = (int64_t)dims[2], N = (int64_t)dims[3];
+    const int64_t OW = oracle_conv_out_dim(W, pad_lo[0], pad_hi[0], cstride[0], dil[0], filt[0]);
+    const int64_t OH = oracle_conv_out_dim(H, pad_lo[1], pad_hi[1], cstride[1], dil[1], filt[1]);
+    if (OW < 1 || OH < 1) return 0;
+    const uint64_t image = (uint64_t)elsize * channels * pixels;
+    if (swizzle != 0 && image % swizzle_span(swizzle) != 0) return 0;
+    uint8_t fill[4] = {0, 0, 0, 0};
+    if (oob_nan) {
+        if (nan_kind == 1) { fill[0] = 0xC0; fill[1] = 0x7F; }
+        else if (nan_kind == 2) { fill[0] = 0x00; fill[1] = 0x7E; }
+        else if (nan_kind == 3) { fill[2] = 0xC0; fill[3] = 0x7F; }
+        else return 0;
+    }
+    const int64_t c0 = coords[0], m0 = coords[1], tap_s = coords[2], tap_r = coords[3];
+    const uint8_t* x = (const uint8_t*)src;
+    uint8_t* d = (uint8_t*)dst;
+    for (uint64_t i = 0; i < pixels; ++i) {
+        const int64_t m = m0 + (int64_t)i;
+        int row_inside = m >= 0 && m < N * OH * OW;
+        int64_t n = 0, ih = 0, iw = 0;
+        if (row_inside) {
+            const int64_t ow = m % OW, oh = (m / OW) % OH;
+            n = m / (OW * OH);
+            ih = oh * cstride[1] - pad_lo[1] + tap_r * dil[1];
+            iw = ow * cstride[0] - pad_lo[0] + tap_s * dil[0];
+            row_inside = ih >= 0 && ih < H && iw >= 0 && iw < W;
+        }
+        for (uint64_t j = 0; j < channels; ++j) {
+            const int64_t c = c0 + (int64_t)j;
+            const uint64_t off = oracle_swizzle((uint64_t)elsize * (j + (uint64_t)channels * i), swizzle);
+            if (off + (uint64_t)elsize > image) return 0;
+            if (row_inside && c >= 0 && c < C) {
+                const uint64_t so = (uint64_t)c * (uint64_t)elsize + (uint64_t)iw * strides_bytes[0] +
+                                    (uint64_t)ih * strides_bytes[1] + (uint64_t)n * strides_bytes[2];
+                memcpy(d + off, x + so, (size_t)elsize);
+            } else {
+                memcpy(d + off, fill, (size_t)elsize);
+            }
+        }
+    }
+    return image;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * O5 — 2-D convolution, by its definition (the product that [TMA]'s im2col mode turns into a
+ * GEMM):  Y[n, oh, ow, k] = Σ_r Σ_s Σ_c X[n, oh*sh - ph + r*dh, ow*sw - pw + s*dw, c] · Wt[k, r, s, c],
+ * terms whose input position lies outside X counting as zero (zero padding).  Layouts: X NHWC
+ * dense, Wt KRSC dense, Y row-major (N*OH*OW) × K with leading dimension ldy (row m = output
+ * pixel (n*OH + oh)*OW + ow).  Every bf16·bf16 product is exact in binary64; each sum runs over
+ * (r, s, c) in ascending order in binary64 and is rounded once to binary32.  Rows [m0, m1) of Y
+ * are produced (indexed from m0 in out32 / out64, either may be null).
+ *   geom: {pad_h, pad_w, pad_h_end, pad_w_end, stride_h, stride_w, dil_h, dil_w}.
+ * ---------------------------------------------------------------------------------------- */
+void oracle_conv2d_rows(const uint16_t* X, const uint16_t* Wt, int64_t N, int64_t H, int64_t Wd, int64_t C,
+                        int64_t K, int64_t R, int64_t S, const int32_t* geom, int64_t m0, int64_t m1,
+                        double* out64, float* out32, int64_t ldy, int threads) {
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+    const int64_t ph = geom[0], pw = geom[1], sh = geom[4], sw = geom[5], dh = geom[6], dw = geom[7];
+    const int64_t OH = oracle_conv_out_dim(H, geom[0], geom[2], sh, dh, R);
+    const int64_t OW = oracle_conv_out_dim(Wd, geom[1], geom[3], sw, dw, S);
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = m0; m < m1; ++m) {
+        const int64_t ow = m % OW, oh = (m / OW) % OH, n = m / (OW * OH);
+        for (int64_t k = 0; k < K; ++k) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < R; ++r) {
+                const int64_t ih = oh * sh - ph + r * dh;
+                if (ih < 0 || ih >= H) continue;
+                for (int64_t s = 0; s < S; ++s) {
+                    const int64_t iw = ow * sw - pw + s * dw;
+                    if (iw < 0 || iw >= Wd) continue;
+                    const uint16_t* xp = X + ((n * H + ih) * Wd + iw) * C;
+                    const uint16_t* wp = Wt + ((k * R + r) * S + s) * C;
+                    for (int64_t c = 0; c < C; ++c) acc += bf16_to_f64(xp[c]) * bf16_to_f64(wp[c]);
+                }
+            }
+            if (out64) out64[(m - m0) * ldy + k] = acc;
+            if (out32) out32[(m - m0) * ldy + k] = (float)acc;
+        }
     }
 }
 

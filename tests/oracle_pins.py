@@ -474,7 +474,169 @@ def pin_gemm_ex(o):
     assert np.array_equal(got.astype(np.int64), want)
 
 
+# ---------------------------------------------------------------------------------------------
+# im2col copy and 2-D convolution ("2 · Le Tensor Memory Accelerator", section "im2col": the
+# convolution becomes a GEMM over an im2col matrix formed during the copy)
+# ---------------------------------------------------------------------------------------------
+def _im2col_numpy(X, R, S, pad, stride, dil):
+    """Textbook im2col through explicit zero padding and slicing (no bounds tests): X (N,H,W,C)
+    -> (N*OH*OW, R, S, C)."""
+    N, H, W, C = X.shape
+    top, left, bottom, right = pad
+    Xp = np.pad(X, ((0, 0), (top, bottom), (left, right), (0, 0)))
+    OH = (H + top + bottom - dil[0] * (R - 1) - 1) // stride[0] + 1
+    OW = (W + left + right - dil[1] * (S - 1) - 1) // stride[1] + 1
+    out = np.zeros((N, OH, OW, R, S, C), dtype=X.dtype)
+    for r in range(R):
+        for s_ in range(S):
+            h0, w0 = r * dil[0], s_ * dil[1]
+            out[:, :, :, r, s_, :] = Xp[:, h0:h0 + stride[0] * (OH - 1) + 1:stride[0],
+                                        w0:w0 + stride[1] * (OW - 1) + 1:stride[1], :]
+    return out.reshape(N * OH * OW, R, S, C), OH, OW
+
+
+def pin_conv_out_dim(o):
+    """Output extents against torch's convolution shapes and two hand values (56×56 with a 3×3
+    filter and padding 1 keeps 56; 7 with a 3-tap window at stride 2 gives 3)."""
+    assert o.conv_out_dim(56, 1, 1, 1, 1, 3) == 56
+    assert o.conv_out_dim(7, 0, 0, 2, 1, 3) == 3
+    assert o.conv_out_dim(2, 0, 0, 1, 1, 3) == 0
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        n = int(rng.integers(1, 20)); p = int(rng.integers(0, 4)); st = int(rng.integers(1, 4))
+        d = int(rng.integers(1, 3)); f = int(rng.integers(1, 5))
+        if n + 2 * p < d * (f - 1) + 1:
+            continue
+        t = torch.nn.functional.conv1d(torch.zeros(1, 1, n), torch.zeros(1, 1, f), stride=st, padding=p, dilation=d)
+        assert o.conv_out_dim(n, p, p, st, d, f) == t.shape[-1], (n, p, st, d, f)
+
+
+def pin_im2col_hand_example(o):
+    """A 3×3 single-channel image holding 1..9, a 2×2 filter, stride 1, no padding: the four
+    im2col rows are the four 2×2 windows read row by row."""
+    X = np.arange(1, 10, dtype=np.uint32).reshape(1, 3, 3, 1)
+    want = np.array([[1, 2, 4, 5], [2, 3, 5, 6], [4, 5, 7, 8], [5, 6, 8, 9]], dtype=np.uint32)
+    got = np.zeros((4, 4), dtype=np.uint32)
+    for r in range(2):
+        for s_ in range(2):
+            img = o.im2col_copy(X, "u32", [1, 3, 3, 1], [4, 12, 36], [0, 0], [0, 0], [1, 1], [1, 1], [2, 2], 1, 4,
+                                "none", False, [0, 0, s_, r])
+            got[:, 2 * r + s_] = img.view(np.uint32)
+    assert np.array_equal(got, want)
+
+
+def pin_im2col_decode(o):
+    """Every image slot of random im2col copies decodes to the element the textbook im2col (zero
+    padding by np.pad, windows by slicing) puts there, or to the fill."""
+    rng = np.random.default_rng(11)
+    cases = [((2, 6, 7, 5), 3, 3, (1, 1, 1, 1), (1, 1), (1, 1)), ((1, 9, 8, 3), 3, 2, (0, 2, 1, 0), (2, 1), (1, 2)),
+             ((3, 5, 5, 4), 1, 1, (0, 0, 0, 0), (2, 2), (1, 1)), ((1, 7, 6, 2), 2, 3, (2, 0, 0, 3), (1, 2), (2, 1))]
+    for (N, H, W, C), R, S, pad, stride, dil in cases:
+        X = (np.arange(N * H * W * C, dtype=np.uint32) + 1).reshape(N, H, W, C)
+        cols, OH, OW = _im2col_numpy(X, R, S, pad, stride, dil)
+        M = N * OH * OW
+        for _ in range(6):
+            ch = int(rng.integers(1, 9)); px = int(rng.integers(1, 12))
+            c0 = int(rng.integers(-2, C + 1)); m0 = int(rng.integers(-3, M + 2))
+            r = int(rng.integers(0, R)); s_ = int(rng.integers(0, S))
+            img = o.im2col_copy(X, "u32", [C, W, H, N], [4 * C, 4 * C * W, 4 * C * W * H], [pad[1], pad[0]],
+                                [pad[3], pad[2]], [stride[1], stride[0]], [dil[1], dil[0]], [S, R], ch, px, "none",
+                                False, [c0, m0, s_, r]).view(np.uint32).reshape(px, ch)
+            for i in range(px):
+                for j in range(ch):
+                    m, c = m0 + i, c0 + j
+                    want = cols[m, r, s_, c] if (0 <= m < M and 0 <= c < C) else 0
+                    assert img[i, j] == want, ((N, H, W, C), R, S, pad, stride, dil, c0, m0, r, s_, i, j)
+    # NaN fill of a bf16 tensor, and the swizzle of a 64-channel (128-byte) row
+    X = np.ones((1, 4, 4, 64), dtype=np.uint16) * 0x3F80
+    img = o.im2col_copy(X, "bf16", [64, 4, 4, 1], [128, 512, 2048], [1, 1], [1, 1], [1, 1], [1, 1], [3, 3], 64, 8,
+                        "none", True, [0, 0, 0, 0]).view(np.uint16).reshape(8, 64)
+    assert np.all(img[0] == 0x7FC0) and np.all(img[1:4] == 0x7FC0) and np.all(img[4] == 0x7FC0)
+    assert np.all(img[5:8] == 0x3F80)
+    X = (np.arange(2 * 4 * 4 * 64, dtype=np.uint32) % 65521).astype(np.uint16).reshape(2, 4, 4, 64)
+    plain = o.im2col_copy(X, "u16", [64, 4, 4, 2], [128, 512, 2048], [1, 1], [1, 1], [1, 1], [1, 1], [3, 3], 64,
+                          16, "none", False, [0, 3, 1, 2])
+    swz = o.im2col_copy(X, "u16", [64, 4, 4, 2], [128, 512, 2048], [1, 1], [1, 1], [1, 1], [1, 1], [3, 3], 64, 16,
+                        "128B", False, [0, 3, 1, 2])
+    perm = o.swizzle(np.arange(plain.size, dtype=np.uint64), "128B")
+    assert np.array_equal(swz[perm.astype(np.int64)], plain)
+
+
+def _conv_case(rng, N, H, W, C, K, R, S, integer):
+    if integer:
+        Xv = rng.integers(-4, 5, (N, H, W, C)).astype(np.float32)
+        Wv = rng.integers(-4, 5, (K, R, S, C)).astype(np.float32)
+    else:
+        Xv = rng.standard_normal((N, H, W, C)).astype(np.float32)
+        Wv = rng.standard_normal((K, R, S, C)).astype(np.float32)
+    Xb = _bits_of(Xv)
+    Wb = _bits_of(Wv)
+    return Xb, Wb
+
+
+def pin_conv_torch(o):
+    """The convolution against torch's float64 conv2d on the CPU (a library routine, NCHW):
+    bit for bit on small integers (every sum exact in any order), within 1e-12 relative on
+    random values; padding is applied with F.pad so it may be asymmetric."""
+    rng = np.random.default_rng(21)
+    cases = [(2, 7, 6, 5, 4, 3, 3, (1, 1, 1, 1), (1, 1), (1, 1)), (1, 9, 8, 3, 2, 3, 2, (0, 2, 1, 0), (2, 1), (1, 2)),
+             (2, 5, 5, 4, 3, 1, 1, (0, 0, 0, 0), (2, 2), (1, 1)), (1, 7, 6, 2, 5, 2, 3, (2, 0, 0, 3), (1, 2), (2, 1))]
+    for integer in (True, False):
+        for N, H, W, C, K, R, S, pad, stride, dil in cases:
+            Xb, Wb = _conv_case(rng, N, H, W, C, K, R, S, integer)
+            got32, got64 = o.conv2d(Xb, Wb, N, H, W, C, K, R, S, pad, stride, dil, want64=True)
+            xt = torch.from_numpy(_f64(Xb).reshape(N, H, W, C)).permute(0, 3, 1, 2)
+            wt = torch.from_numpy(_f64(Wb).reshape(K, R, S, C)).permute(0, 3, 1, 2)
+            xt = torch.nn.functional.pad(xt, (pad[1], pad[3], pad[0], pad[2]))
+            yt = torch.nn.functional.conv2d(xt, wt, stride=stride, dilation=dil)
+            ref = yt.permute(0, 2, 3, 1).reshape(-1, K).numpy()
+            assert got64.shape == ref.shape
+            if integer:
+                assert np.array_equal(got64, ref) and np.array_equal(got32, ref.astype(np.float32))
+            else:
+                assert np.allclose(got64, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_conv_1x1_is_gemm(o):
+    """A 1×1 convolution at stride 1 without padding is the GEMM X(NHW × C) · W(K × C)ᵀ: the
+    same sums in the same order, so the binary32 results agree bit for bit."""
+    rng = np.random.default_rng(31)
+    N, H, W, C, K = 2, 5, 7, 24, 9
+    Xb, Wb = _conv_case(rng, N, H, W, C, K, 1, 1, False)
+    y = o.conv2d(Xb, Wb, N, H, W, C, K, 1, 1)
+    g = o.gemm(Xb, Wb, N * H * W, K, C, C, C, "nk")
+    assert np.array_equal(y, g)
+
+
+def pin_conv_equals_im2col_gemm(o):
+    """The page's identity: the convolution equals the GEMM of its im2col matrix (built from
+    im2col copies, one per tap and channel block) with the filters as a K × (R·S·C) matrix; the
+    sums run in the same (r, s, c) order, so the results agree bit for bit."""
+    rng = np.random.default_rng(41)
+    N, H, W, C, K, R, S = 2, 6, 7, 10, 6, 3, 2
+    pad, stride, dil = (1, 0, 2, 1), (2, 1), (1, 2)
+    Xb, Wb = _conv_case(rng, N, H, W, C, K, R, S, False)
+    OH = o.conv_out_dim(H, pad[0], pad[2], stride[0], dil[0], R)
+    OW = o.conv_out_dim(W, pad[1], pad[3], stride[1], dil[1], S)
+    M = N * OH * OW
+    cols = np.zeros((M, R, S, C), dtype=np.uint16)
+    for r in range(R):
+        for s_ in range(S):
+            for m0 in range(0, M, 16):
+                for c0 in range(0, C, 4):
+                    img = o.im2col_copy(Xb.reshape(N, H, W, C), "bf16", [C, W, H, N], [2 * C, 2 * C * W, 2 * C * W * H],
+                                        [pad[1], pad[0]], [pad[3], pad[2]], [stride[1], stride[0]],
+                                        [dil[1], dil[0]], [S, R], 4, 16, "none", False, [c0, m0, s_, r])
+                    blk = img.view(np.uint16).reshape(16, 4)
+                    rows = min(16, M - m0); chs = min(4, C - c0)
+                    cols[m0:m0 + rows, r, s_, c0:c0 + chs] = blk[:rows, :chs]
+    y = o.conv2d(Xb, Wb, N, H, W, C, K, R, S, pad, stride, dil)
+    g = o.gemm(cols.reshape(M, -1), Wb.reshape(K, -1), M, K, R * S * C, R * S * C, R * S * C, "nk")
+    assert np.array_equal(y, g)
+
+
 ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_structure, pin_bank_spread,
             pin_worked_descriptor, pin_copy_decode, pin_fill_and_source, pin_store_decode, pin_store_hand_example,
             pin_store_swizzle_and_roundtrip, pin_gemm_exact_rationals, pin_gemm_closed_forms,
-            pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16]
+            pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16, pin_conv_out_dim, pin_im2col_hand_example,
+            pin_im2col_decode, pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_equals_im2col_gemm]

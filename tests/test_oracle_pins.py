@@ -48,6 +48,20 @@ MUTANTS = [
      "uint64_t off = lin * (uint64_t)elsize;\n        if (off + (uint64_t)elsize > size)"),
     ("store drops the element stride", "int64_t x = c[i] + (int64_t)j[i] * (int64_t)estr[i];\n            if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;\n            else dst_off",
      "int64_t x = c[i] + (int64_t)j[i];\n            if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;\n            else dst_off"),
+    ("im2col tap ignores the dilation", "ih = oh * cstride[1] - pad_lo[1] + tap_r * dil[1];",
+     "ih = oh * cstride[1] - pad_lo[1] + tap_r;"),
+    ("im2col pixel order transposed", "const int64_t ow = m % OW, oh = (m / OW) % OH;\n            n = m / (OW * OH);",
+     "const int64_t oh = m % OH, ow = (m / OH) % OW;\n            n = m / (OW * OH);"),
+    ("im2col padding added instead of subtracted", "iw = ow * cstride[0] - pad_lo[0] + tap_s * dil[0];",
+     "iw = ow * cstride[0] + pad_lo[0] + tap_s * dil[0];"),
+    ("im2col channel bound off by one", "if (row_inside && c >= 0 && c < C) {", "if (row_inside && c >= 0 && c <= C) {"),
+    ("im2col image rows use the pixel count", "(uint64_t)elsize * (j + (uint64_t)channels * i)",
+     "(uint64_t)elsize * (j + (uint64_t)pixels * i)"),
+    ("output extent loses the last position", "return span / stride + 1;", "return span / stride;"),
+    ("convolution flips the filter", "const uint16_t* wp = Wt + ((k * R + r) * S + s) * C;",
+     "const uint16_t* wp = Wt + ((k * R + (R - 1 - r)) * S + (S - 1 - s)) * C;"),
+    ("convolution ignores the stride", "const int64_t ih = oh * sh - ph + r * dh;", "const int64_t ih = oh - ph + r * dh;"),
+    ("convolution drops the last channel", "for (int64_t c = 0; c < C; ++c) acc +=", "for (int64_t c = 0; c + 1 < C; ++c) acc +="),
 ]
 
 
