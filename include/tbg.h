@@ -107,7 +107,8 @@ tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank
                             const uint32_t* element_strides, tbg_swizzle swizzle, tbg_l2_hint l2,
                             tbg_oob_fill oob);
 
-/* Bytes of one copy's image for an encoded descriptor; 0 if `d` is not a valid descriptor. */
+/* Bytes of one copy's image for an encoded descriptor (tiled or im2col); 0 if `d` is not a valid
+ * descriptor. */
 size_t tbg_box_bytes(const tbg_tensor_desc* d);
 
 /* Copy one box ([TMA] §2.2, §2.4): the element at box position j (innermost first) comes from
@@ -223,6 +224,92 @@ tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, con
                                const void* B, int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc,
                                tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Encode an im2col descriptor ([TMA] section "im2col": a copy mode dedicated to convolution that
+ * performs the im2col transform during the copy, so that a convolution becomes a GEMM whose
+ * im2col matrix is never stored).  The page gives no more than that; this library's reading:
+ *   - the tensor X is NHWC: global_dim = {C, W, H, N} (innermost first), global_strides = byte
+ *     strides of W, H and N (each a multiple of 16; the channel stride is the element size);
+ *   - pad_lo, pad_hi, conv_stride, dilation, filter: {along W, along H}; the convolution has
+ *     OW = floor((W + pad_lo[0] + pad_hi[0] - dilation[0]*(filter[0]-1) - 1) / conv_stride[0]) + 1
+ *     output columns, OH likewise; the window must fit (OW, OH >= 1);
+ *   - row m of the im2col matrix is output pixel m = (n*OH + oh)*OW + ow, column (r, s, c) is
+ *     filter tap r (along H), s (along W) and channel c; its element is
+ *     X[n, oh*sh - ph + r*dh, ow*sw - pw + s*dw, c], or the fill where that position is outside
+ *     the tensor (the convolution's padding), where m >= N*OH*OW or m < 0, and where c is
+ *     outside 0..C-1;
+ *   - a copy takes `pixels` consecutive rows (1..256) and `channels` consecutive channels
+ *     (1..256) at one tap; its image is dense, channel fastest (element (i, j) at byte
+ *     elsize*(j + channels*i)), through `swizzle` like a tiled copy (channels*elsize must fit the
+ *     swizzle span and the image must be a whole number of spans), at most 64 KiB.
+ * Limits: each dimension below 2^31, strides below 2^40, filter, stride and dilation 1..256,
+ * padding 0..65535, fewer than 2^31 output pixels.
+ * Returns MISALIGNED (base/strides), OUT_OF_RANGE (dims, strides, box, geometry), INVALID_VALUE
+ * (null pointers, enum values, a window that does not fit, swizzle width, NaN fill of an integer
+ * type), UNSUPPORTED (too many output pixels). */
+tbg_status tbg_encode_im2col(tbg_tensor_desc* out, tbg_dtype dtype, const void* global_address,
+                             const uint64_t* global_dim, const uint64_t* global_strides, const int32_t* pad_lo,
+                             const int32_t* pad_hi, const int32_t* conv_stride, const int32_t* dilation,
+                             const int32_t* filter, uint32_t channels, uint32_t pixels, tbg_swizzle swizzle,
+                             tbg_l2_hint l2, tbg_oob_fill oob);
+
+/* Copy one im2col block: coords = {c0, m0, s, r} in host memory (first channel, first output
+ * pixel, filter tap along W, filter tap along H; signed).  dst_image: tbg_box_bytes(d) bytes of
+ * device memory, 16-byte aligned.  The block passes through LDS.  Errors as tbg_tiled_copy
+ * (a tiled descriptor here is INVALID_VALUE). */
+tbg_status tbg_im2col_copy(const tbg_tensor_desc* d, const int32_t* coords, void* dst_image, void* stream);
+
+/* n im2col blocks of one descriptor: block b uses coords_dev[4b .. 4b+3] (device memory, int32)
+ * and writes its image at dst_images + b * tbg_box_bytes(d).  n == 0 is a no-op. */
+tbg_status tbg_im2col_copy_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n, void* dst_images,
+                                void* stream);
+
+/* Shape of a 2-D convolution (cross-correlation, as deep-learning frameworks define it):
+ *   Y[n, oh, ow, k] = sum over r < R, s < S, c < C of
+ *                     X[n, oh*stride_h - pad_h + r*dil_h, ow*stride_w - pad_w + s*dil_w, c] * W[k, r, s, c],
+ * with X read as zero outside its H x W extent.  OH = floor((h + pad_h + pad_h_end - dil_h*(r-1)
+ * - 1) / stride_h) + 1, OW likewise.  X is NHWC, W is KRSC (both bf16, dense), Y is row-major
+ * (N*OH*OW) x K (NHWK) with leading dimension ldy. */
+typedef struct {
+    int64_t n, h, w, c;            /* input batch, height, width, channels */
+    int64_t k;                     /* output channels */
+    int32_t r, s;                  /* filter height and width */
+    int32_t pad_h, pad_w;          /* zero padding before the first row and column */
+    int32_t pad_h_end, pad_w_end;  /* zero padding after the last row and column */
+    int32_t stride_h, stride_w;
+    int32_t dil_h, dil_w;
+} tbg_conv2d_shape;
+
+/* Output extents OH, OW of a shape (either pointer may be NULL).  Returns INVALID_VALUE for a
+ * size, stride or dilation below 1, negative padding or a window that does not fit;
+ * UNSUPPORTED beyond the limits of tbg_conv2d_fwd. */
+tbg_status tbg_conv2d_out_dims(const tbg_conv2d_shape* shape, int64_t* oh, int64_t* ow);
+
+/* Workspace bytes tbg_conv2d_fwd needs: 0 when c is a multiple of 8 (and x, w are 16-byte
+ * aligned, which this function assumes); else room to repack X and W with the channel pitch
+ * rounded up to 8 (zero channels added), 256-byte aligned.  0 for an invalid shape. */
+size_t tbg_conv2d_workspace_bytes(const tbg_conv2d_shape* shape);
+
+/* Y <- alpha * conv2d(X, W) + beta * Y as an implicit GEMM ([TMA] section "im2col": the im2col
+ * matrix of X is formed tile by tile by the operand copies and never stored; [GEMM] the product).
+ * The GEMM is (N*OH*OW) x K with reduction R*S*C over filter taps and channels; bf16 inputs,
+ * fp32 accumulation, fp32 or bf16 (RNE) output; alpha/beta as tbg_gemm_ex (beta == 0 does not
+ * read Y; alpha == 0 reads neither X nor W).
+ *   x, w       device memory, NHWC and KRSC bf16; any c (c % 8 != 0, or an operand not 16-byte
+ *              aligned, needs the workspace of tbg_conv2d_workspace_bytes, plus that much again
+ *              for a misaligned operand).
+ *   y          fp32 or bf16 device memory, (N*OH*OW) rows of ldy >= k elements; only the first k
+ *              of each row are written.
+ *   cfg        NULL (the library's choice) or a tbg_gemm_config with pipeline AUTO or RING, stages
+ *              0 or 2 and tile 0x0, 256x256, 256x128, 128x128 or 64x64 (else UNSUPPORTED);
+ *              every tile gives bit-identical results.
+ * Limits: h, w below 2^16; N*OH*OW and k below 2^31; X (with its channel pitch rounded up to 8)
+ * below 2 GiB; r*s*c below 2^22; filter, stride, dilation up to 256; padding up to 65535.
+ * Returns INVALID_VALUE (bad shape, ldy < k, null pointers, y type), UNSUPPORTED (limits),
+ * OUT_OF_RANGE (workspace too small), MISALIGNED (workspace), NO_DEVICE / HIP. */
+tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void* x, const void* w, float beta,
+                          void* y, int64_t ldy, tbg_dtype y_dtype, const tbg_gemm_config* cfg, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* tbg_status_string(tbg_status s);

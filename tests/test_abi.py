@@ -6,6 +6,8 @@ The encoder's rules come from "2 · Le Tensor Memory Accelerator" §2.2–§2.3 
 import ctypes
 import subprocess
 
+import numpy as np
+
 import pytest
 
 import tiled_bf16_gemm_amd as tbg
@@ -257,3 +259,107 @@ def test_header_lists_the_built_configurations():
 
     assert expand(ring) == {(t, s) for p, t, s in BUILT_CONFIGS if p == "ring"}
     assert expand(prod) == {(t, s) for p, t, s in BUILT_CONFIGS if p == "producer"}
+
+
+def _im2col_args(**over):
+    a = dict(dtype="bf16", global_address=BASE, global_dim=[64, 56, 56, 32], global_strides=[128, 128 * 56, 128 * 56 * 56],
+             pad_lo=[1, 1], pad_hi=[1, 1], conv_stride=[1, 1], dilation=[1, 1], filter=[3, 3], channels=64,
+             pixels=128, swizzle="128B", l2="none", oob="zero")
+    a.update(over)
+    return a
+
+
+def test_im2col_descriptor():
+    """tbg_encode_im2col ("2 · Le Tensor Memory Accelerator", section "im2col"): image size and the
+    checks the tiled encoder makes, plus the convolution geometry."""
+    d = tbg.encode_im2col(**_im2col_args())
+    assert tbg.box_bytes(d) == 64 * 128 * 2
+    d = tbg.encode_im2col(**_im2col_args(channels=3, pixels=5, swizzle="none", dtype="f32", oob="nan"))
+    assert tbg.box_bytes(d) == 3 * 5 * 4
+    bad = [
+        (dict(global_address=BASE + 8), tbg.ERR_MISALIGNED),
+        (dict(global_strides=[128, 128 * 56 + 8, 128 * 56 * 56]), tbg.ERR_MISALIGNED),
+        (dict(global_dim=[0, 56, 56, 32]), tbg.ERR_OUT_OF_RANGE),
+        (dict(filter=[0, 3]), tbg.ERR_OUT_OF_RANGE),
+        (dict(conv_stride=[1, 0]), tbg.ERR_OUT_OF_RANGE),
+        (dict(dilation=[300, 1]), tbg.ERR_OUT_OF_RANGE),
+        (dict(pad_lo=[-1, 0]), tbg.ERR_OUT_OF_RANGE),
+        (dict(filter=[59, 3]), tbg.ERR_INVALID_VALUE),          # the window does not fit 56 + 2
+        (dict(channels=0), tbg.ERR_OUT_OF_RANGE),
+        (dict(pixels=257), tbg.ERR_OUT_OF_RANGE),
+        (dict(channels=128, pixels=256, swizzle="none", dtype="f32"), tbg.ERR_OUT_OF_RANGE),  # 128 KiB image
+        (dict(channels=128), tbg.ERR_INVALID_VALUE),            # 256-byte rows under a 128B swizzle
+        (dict(oob="nan", dtype="u16"), tbg.ERR_INVALID_VALUE),
+        (dict(swizzle=9), tbg.ERR_INVALID_VALUE),
+        (dict(global_address=0), tbg.ERR_INVALID_VALUE),
+    ]
+    for over, status in bad:
+        assert tbg.encode_im2col_status(**_im2col_args(**over)) == status, (over, tbg.last_error())
+    # a descriptor of the other kind is refused by each copy call
+    dt = tbg.encode_tiled(**_c1_args())
+    with pytest.raises(tbg.Error) as e:
+        tbg.im2col_copy(dt, [0, 0, 0, 0], BASE)
+    assert e.value.status == tbg.ERR_INVALID_VALUE
+    with pytest.raises(tbg.Error) as e:
+        tbg.tiled_copy(d, [0, 0], BASE)
+    assert e.value.status == tbg.ERR_INVALID_VALUE
+    with pytest.raises(tbg.Error) as e:
+        tbg.im2col_copy(d, [0, 0, 0, 0], BASE + 4)
+    assert e.value.status == tbg.ERR_MISALIGNED
+    tbg.im2col_copy_many(d, 0, 0, 0)
+
+
+def test_conv2d_shapes_and_errors(orc):
+    """Output extents agree with the oracle's; workspace only when c is not a multiple of 8;
+    malformed shapes are INVALID_VALUE and limits UNSUPPORTED, before any device check."""
+    import torch
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        h, w = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        r, s = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        pad = tuple(int(x) for x in rng.integers(0, 4, 4))
+        st, dl = tuple(int(x) for x in rng.integers(1, 4, 2)), tuple(int(x) for x in rng.integers(1, 3, 2))
+        shp = tbg.conv2d_shape(2, h, w, 8, 4, r, s, pad, st, dl)
+        oh = orc.conv_out_dim(h, pad[0], pad[2], st[0], dl[0], r)
+        ow = orc.conv_out_dim(w, pad[1], pad[3], st[1], dl[1], s)
+        if oh < 1 or ow < 1:
+            with pytest.raises(tbg.Error) as e:
+                tbg.conv2d_out_dims(shp)
+            assert e.value.status == tbg.ERR_INVALID_VALUE
+        else:
+            assert tbg.conv2d_out_dims(shp) == (oh, ow)
+    assert tbg.conv2d_workspace_bytes(tbg.conv2d_shape(2, 9, 9, 64, 4, 3, 3)) == 0
+    c8 = 8
+    want = ((2 * 9 * 9 * c8 * 2 + 255) // 256 * 256) + ((4 * 3 * 3 * c8 * 2 + 255) // 256 * 256)
+    assert tbg.conv2d_workspace_bytes(tbg.conv2d_shape(2, 9, 9, 3, 4, 3, 3)) == want
+    good = tbg.conv2d_shape(2, 9, 9, 16, 4, 3, 3, (1, 1, 1, 1))
+    args = dict(alpha=1.0, x=BASE, w=BASE, beta=0.0, y=BASE, ldy=4, y_dtype="f32")
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(0, 9, 9, 16, 4, 3, 3), **args) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(2, 9, 9, 16, 4, 3, 3, stride=(0, 1)), **args) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(2, 9, 9, 16, 4, 3, 3, pad=(-1, 0, 0, 0)), **args) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(2, 2, 9, 16, 4, 3, 3), **args) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(2, 70000, 9, 16, 4, 3, 3), **args) == tbg.ERR_UNSUPPORTED
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(2, 9, 9, 16, 4, 300, 3), **args) == tbg.ERR_UNSUPPORTED
+    assert tbg.conv2d_fwd_status(good, **{**args, "ldy": 3}) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(good, **{**args, "y_dtype": "u8"}) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(good, **{**args, "y": 0}) == tbg.ERR_INVALID_VALUE
+    assert tbg.conv2d_fwd_status(good, **{**args, "x": 0}) == tbg.ERR_INVALID_VALUE
+    # c % 8 != 0 needs the repack workspace
+    assert tbg.conv2d_fwd_status(tbg.conv2d_shape(2, 9, 9, 3, 4, 3, 3), **args) == tbg.ERR_OUT_OF_RANGE
+    if not torch.cuda.is_available():
+        assert tbg.conv2d_fwd_status(good, **args) == tbg.ERR_NO_DEVICE
+        # alpha == 0 needs neither operand
+        assert tbg.conv2d_fwd_status(good, **{**args, "alpha": 0.0, "beta": 1.0, "x": 0, "w": 0}) == tbg.ERR_NO_DEVICE
+
+
+def test_conv2d_config_checks():
+    import torch
+    good = tbg.conv2d_shape(2, 9, 9, 16, 4, 3, 3, (1, 1, 1, 1))
+    args = dict(alpha=1.0, x=BASE, w=BASE, beta=0.0, y=BASE, ldy=4, y_dtype="f32")
+    assert tbg.conv2d_fwd_status(good, **args, config=tbg.gemm_config("128x256")) == tbg.ERR_UNSUPPORTED
+    assert tbg.conv2d_fwd_status(good, **args, config=tbg.gemm_config("128x128", 3)) == tbg.ERR_UNSUPPORTED
+    assert tbg.conv2d_fwd_status(good, **args, config=tbg.gemm_config("128x128", 0, "producer")) == tbg.ERR_UNSUPPORTED
+    assert tbg.conv2d_fwd_status(good, **args, config=tbg.GemmConfig(64, 0, 0, 0)) == tbg.ERR_INVALID_VALUE
+    if not torch.cuda.is_available():
+        for t in ("256x256", "256x128", "128x128", "64x64", None):
+            assert tbg.conv2d_fwd_status(good, **args, config=tbg.gemm_config(t, 2, "ring")) == tbg.ERR_NO_DEVICE

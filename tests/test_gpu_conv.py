@@ -1,0 +1,190 @@
+"""im2col copies and the implicit-GEMM convolution on the GPU against the oracle.
+
+"2 · Le Tensor Memory Accelerator", section "im2col": a copy mode forms the im2col matrix of a
+convolution during the copy, so the convolution becomes a GEMM.  Bars: im2col images bit for bit
+(they move bits); convolutions within max(1e-2·|r|, 1e-3) of the oracle's binary32 result r,
+bit for bit on small-integer inputs (every partial sum exact), bit-identical across workgroup
+tiles (the same products in the same order), output columns past K untouched."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+gpu = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tiled_bf16_gemm_amd import torch_ops
+    return torch_ops
+
+
+TORCH_DT = {"bf16": torch.bfloat16, "u16": torch.int16, "f32": torch.float32, "u8": torch.uint8, "f16": torch.float16}
+
+
+@gpu
+def test_im2col_copies(ops, orc):
+    """Random geometries, element types, swizzles and fills; boxes at negative and past-the-end
+    pixel and channel coordinates; one call per box and many boxes per call."""
+    rng = np.random.default_rng(123)
+    cases = [("bf16", (2, 9, 11, 64), 3, 3, (1, 1, 1, 1), (1, 1), (1, 1), 64, 16, "128B", "zero"),
+             ("bf16", (1, 13, 7, 24), 3, 2, (0, 2, 1, 0), (2, 1), (1, 2), 24, 8, "none", "nan"),
+             ("f32", (3, 5, 6, 8), 2, 2, (1, 0, 0, 1), (1, 2), (2, 1), 5, 7, "none", "zero"),
+             ("u16", (2, 8, 8, 128), 1, 1, (0, 0, 0, 0), (2, 2), (1, 1), 64, 32, "128B_2ROW", "zero"),
+             ("u8", (2, 7, 9, 32), 3, 3, (2, 2, 2, 2), (1, 1), (2, 2), 32, 12, "32B", "zero"),
+             ("bf16", (4, 6, 6, 40), 5, 5, (2, 2, 2, 2), (1, 1), (1, 1), 16, 64, "32B", "nan")]
+    for dt, (N, H, W, C), R, S, pad, stride, dil, ch, px, swz, oob in cases:
+        es = torch.empty(0, dtype=TORCH_DT[dt]).element_size()
+        raw = rng.integers(0, 256, N * H * W * C * es, dtype=np.uint8)
+        if dt in ("bf16", "f32", "f16"):  # keep every element finite so a NaN only comes from the fill
+            if dt == "f32":
+                raw = rng.standard_normal(N * H * W * C).astype(np.float32).view(np.uint8)
+            else:
+                raw = workloads.bits(torch.randn(N * H * W * C).to(torch.bfloat16)).view(np.uint8)
+        x = torch.from_numpy(raw.copy()).cuda().view(TORCH_DT[dt]).view(N, H, W, C)
+        desc = ops.encode_im2col(x, dt, pad, stride, dil, (R, S), ch, px, swz, oob)
+        OH = orc.conv_out_dim(H, pad[0], pad[2], stride[0], dil[0], R)
+        OW = orc.conv_out_dim(W, pad[1], pad[3], stride[1], dil[1], S)
+        M = N * OH * OW
+        coords = [(c0, m0, s_, r) for r in range(R) for s_ in range(S)
+                  for m0 in (-3, 0, M - px + 2, int(rng.integers(0, M)))
+                  for c0 in (0, C - ch, -8 if ch >= 8 else -1)]
+        _say(f"im2col {dt} {(N, H, W, C)} R={R} S={S} pad={pad} stride={stride} dil={dil} box {ch}x{px} {swz} "
+             f"{oob}: {len(coords)} boxes")
+        ct = torch.tensor(coords, dtype=torch.int32, device="cuda")
+        imgs = ops.im2col_copy_many(desc, ct)
+        one = ops.im2col_copy(desc, list(coords[len(coords) // 2]))
+        torch.cuda.synchronize()
+        imgs = imgs.cpu().numpy()
+        nb = ch * px * es
+        for b, cc in enumerate(coords):
+            want = orc.im2col_copy(raw, dt, [C, W, H, N], [C * es, C * es * W, C * es * W * H], [pad[1], pad[0]],
+                                   [pad[3], pad[2]], [stride[1], stride[0]], [dil[1], dil[0]], [S, R], ch, px, swz,
+                                   oob == "nan", list(cc))
+            assert np.array_equal(imgs[b * nb:(b + 1) * nb], want), (cc, "image differs")
+        want = orc.im2col_copy(raw, dt, [C, W, H, N], [C * es, C * es * W, C * es * W * H], [pad[1], pad[0]],
+                               [pad[3], pad[2]], [stride[1], stride[0]], [dil[1], dil[0]], [S, R], ch, px, swz,
+                               oob == "nan", list(coords[len(coords) // 2]))
+        assert np.array_equal(one.cpu().numpy(), want)
+
+
+def _conv(ops, w, x_cpu, f_cpu, out_dtype, config=None, ldy_pad=3, x_offset=0, alpha=1.0, beta=0.0, y_old=None):
+    """Run tbg_conv2d_fwd; returns the (M, ldy) output buffer on the CPU as float32."""
+    if x_offset:
+        buf = torch.empty(x_cpu.numel() + 8, dtype=torch.bfloat16, device="cuda")
+        buf[x_offset:x_offset + x_cpu.numel()] = x_cpu.reshape(-1).cuda()
+        x = buf[x_offset:x_offset + x_cpu.numel()].view(x_cpu.shape)
+    else:
+        x = x_cpu.cuda()
+    f = f_cpu.cuda()
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    ldy = w.k + ldy_pad
+    if y_old is None:
+        ybuf = torch.full((w.M, ldy), float("nan"), dtype=tdt, device="cuda")
+    else:
+        ybuf = y_old.clone().to(tdt).cuda()
+    ops.conv2d(x, f, w.pad, w.stride, w.dil, out_dtype, out=ybuf[:, :w.k], alpha=alpha, beta=beta, config=config)
+    torch.cuda.synchronize()
+    return ybuf.float().cpu().numpy()
+
+
+def _ref(orc, w, x_cpu, f_cpu, rows=None):
+    return orc.conv2d(workloads.bits(x_cpu), workloads.bits(f_cpu), w.n, w.h, w.w, w.c, w.k, w.r, w.s, w.pad,
+                      w.stride, w.dil, rows=rows)
+
+
+SMALL = ["conv_3x3", "conv_c20", "conv_stride2", "conv_dil2", "conv_1x1", "conv_stem"]
+
+
+@gpu
+@pytest.mark.parametrize("name", SMALL)
+def test_conv_workloads(ops, orc, name):
+    """Each small convolution workload in full against the oracle, on every workgroup tile (the
+    results must also be bit-identical across tiles), with the output rows padded."""
+    import tiled_bf16_gemm_amd as tbg
+    w = workloads.CONVS[name]
+    x, f = workloads.conv_inputs(w)
+    ref = _ref(orc, w, x, f)
+    base = None
+    for tile in (None, "256x256", "256x128", "128x128", "64x64"):
+        cfg = None if tile is None else tbg.gemm_config(tile, 0, "ring")
+        _say(f"conv {name} (M={w.M} K={w.k} RSC={w.r * w.s * w.c}) tile {tile or 'auto'} out {w.out_dtype}")
+        got = _conv(ops, w, x, f, w.out_dtype, config=cfg)
+        r = oracle.gemm_check(got[:, :w.k], ref)
+        _say(f"  max_abs={r['max_abs_err']:.3g} max_rel={r['max_rel_err']:.3g} fail={r['n_fail']}")
+        assert r["pass"], r
+        assert np.all(np.isnan(got[:, w.k:])), "columns past K were written"
+        if base is None:
+            base = got
+        else:
+            assert np.array_equal(got[:, :w.k], base[:, :w.k]), "tiles disagree"
+
+
+@gpu
+def test_conv_integer_bit_exact(ops, orc):
+    """Small-integer inputs: every partial sum is exact in binary32, so the bits must match."""
+    rng = np.random.default_rng(9)
+    for name in ("conv_c20", "conv_stride2", "conv_dil2", "conv_stem"):
+        w = workloads.CONVS[name]
+        x = torch.from_numpy(rng.integers(-4, 5, (w.n, w.h, w.w, w.c)).astype(np.float32)).to(torch.bfloat16)
+        f = torch.from_numpy(rng.integers(-4, 5, (w.k, w.r, w.s, w.c)).astype(np.float32)).to(torch.bfloat16)
+        _say(f"integer conv {name}")
+        got = _conv(ops, w, x, f, "f32")
+        ref = _ref(orc, w, x, f)
+        assert np.array_equal(got[:, :w.k], ref), f"{int((got[:, :w.k] != ref).sum())} entries differ"
+
+
+@gpu
+def test_conv_alpha_beta_and_misaligned_input(ops, orc):
+    """Y <- alpha·conv + beta·Y; beta = 0 leaves a NaN-filled Y unread; an input that starts off a
+    16-byte boundary goes through the repack path."""
+    w = workloads.CONVS["conv_stride2"]
+    x, f = workloads.conv_inputs(w)
+    s32, s64 = orc.conv2d(workloads.bits(x), workloads.bits(f), w.n, w.h, w.w, w.c, w.k, w.r, w.s, w.pad, w.stride,
+                          w.dil, want64=True)
+    y_old = torch.from_numpy(np.random.default_rng(4).standard_normal((w.M, w.k + 3)).astype(np.float32))
+    _say("conv alpha=1.5 beta=-0.5")
+    got = _conv(ops, w, x, f, "f32", alpha=1.5, beta=-0.5, y_old=y_old)
+    ref = (1.5 * s64 + (-0.5) * y_old[:, :w.k].double().numpy()).astype(np.float32)
+    assert oracle.gemm_check(got[:, :w.k], ref)["pass"]
+    assert np.array_equal(got[:, w.k:], y_old[:, w.k:].numpy())
+    _say("conv alpha=0 beta=2")
+    got = _conv(ops, w, x, f, "f32", alpha=0.0, beta=2.0, y_old=y_old)
+    assert np.array_equal(got[:, :w.k], 2.0 * y_old[:, :w.k].numpy())
+    _say("conv misaligned input")
+    got = _conv(ops, w, x, f, "f32", x_offset=3)
+    assert oracle.gemm_check(got[:, :w.k], s32)["pass"]
+
+
+@gpu
+def test_conv_benchmark_layer_sampled(ops, orc):
+    """The benchmark layer (batch 32, 56×56, 128 → 128 channels, 3×3, padding 1) in the launch
+    configuration the benchmark times: sampled row ranges (first, middle and last images,
+    including the padded borders) against the oracle, every output finite, and deterministic."""
+    w = workloads.CONVS["conv_b"]
+    x, f = workloads.conv_inputs(w)
+    xd, fd = x.cuda(), f.cuda()
+    _say(f"conv_b M={w.M} K={w.k}")
+    y = ops.conv2d(xd, fd, w.pad, w.stride, w.dil, "bf16")
+    y2 = ops.conv2d(xd, fd, w.pad, w.stride, w.dil, "bf16")
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    yc = y.float().cpu().numpy()
+    per_img = w.M // w.n
+    for m0, m1 in ((0, 200), (per_img * 15 + 3000, per_img * 15 + 3200), (w.M - 200, w.M)):
+        ref = _ref(orc, w, x, f, rows=(m0, m1))
+        r = oracle.gemm_check(yc[m0:m1], ref)
+        _say(f"  rows {m0}..{m1}: max_abs={r['max_abs_err']:.3g} fail={r['n_fail']}")
+        assert r["pass"], r

@@ -67,6 +67,20 @@ def gemm_config(tile=None, stages: int = 0, pipeline="auto") -> GemmConfig:
     return GemmConfig(int(bm), int(bn), int(stages), _enum(PIPELINES, pipeline))
 
 
+class Conv2dShape(ctypes.Structure):
+    """tbg_conv2d_shape: NHWC input, KRSC filters, padding (before/after), strides, dilations."""
+    _fields_ = [("n", ctypes.c_int64), ("h", ctypes.c_int64), ("w", ctypes.c_int64), ("c", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("r", ctypes.c_int32), ("s", ctypes.c_int32), ("pad_h", ctypes.c_int32),
+                ("pad_w", ctypes.c_int32), ("pad_h_end", ctypes.c_int32), ("pad_w_end", ctypes.c_int32),
+                ("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32), ("dil_h", ctypes.c_int32),
+                ("dil_w", ctypes.c_int32)]
+
+
+def conv2d_shape(n, h, w, c, k, r, s, pad=(0, 0, 0, 0), stride=(1, 1), dil=(1, 1)) -> Conv2dShape:
+    """pad = (top, left, bottom, right); stride and dil = (h, w)."""
+    return Conv2dShape(n, h, w, c, k, r, s, pad[0], pad[1], pad[2], pad[3], stride[0], stride[1], dil[0], dil[1])
+
+
 class Error(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{status_string(status)}: {message}")
@@ -105,6 +119,22 @@ _lib.tbg_gemm_configured.restype = ctypes.c_int
 _lib.tbg_gemm_configured.argtypes = [_i64, _i64, _i64, ctypes.c_float, _vp, _i64, _vp, _i64, ctypes.c_int,
                                      ctypes.c_float, _vp, _i64, ctypes.c_int, ctypes.POINTER(GemmConfig), _vp,
                                      ctypes.c_size_t, _vp]
+_lib.tbg_encode_im2col.restype = ctypes.c_int
+_lib.tbg_encode_im2col.argtypes = [ctypes.POINTER(TensorDesc), ctypes.c_int, _vp, _u64p, _u64p, _i32p, _i32p, _i32p,
+                                   _i32p, _i32p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int]
+_lib.tbg_im2col_copy.restype = ctypes.c_int
+_lib.tbg_im2col_copy.argtypes = [ctypes.POINTER(TensorDesc), _i32p, _vp, _vp]
+_lib.tbg_im2col_copy_many.restype = ctypes.c_int
+_lib.tbg_im2col_copy_many.argtypes = [ctypes.POINTER(TensorDesc), _vp, ctypes.c_uint32, _vp, _vp]
+_lib.tbg_conv2d_out_dims.restype = ctypes.c_int
+_lib.tbg_conv2d_out_dims.argtypes = [ctypes.POINTER(Conv2dShape), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_int64)]
+_lib.tbg_conv2d_workspace_bytes.restype = ctypes.c_size_t
+_lib.tbg_conv2d_workspace_bytes.argtypes = [ctypes.POINTER(Conv2dShape)]
+_lib.tbg_conv2d_fwd.restype = ctypes.c_int
+_lib.tbg_conv2d_fwd.argtypes = [ctypes.POINTER(Conv2dShape), ctypes.c_float, _vp, _vp, ctypes.c_float, _vp, _i64,
+                                ctypes.c_int, ctypes.POINTER(GemmConfig), _vp, ctypes.c_size_t, _vp]
 _lib.tbg_status_string.restype = ctypes.c_char_p
 _lib.tbg_status_string.argtypes = [ctypes.c_int]
 _lib.tbg_last_error.restype = ctypes.c_char_p
@@ -180,6 +210,70 @@ def tiled_store_many(desc: TensorDesc, coords_dev: int, n: int, src_images: int,
                                      _vp(stream or 0)))
 
 
+def encode_im2col(dtype, global_address: int, global_dim: Sequence[int], global_strides: Sequence[int],
+                  pad_lo: Sequence[int], pad_hi: Sequence[int], conv_stride: Sequence[int], dilation: Sequence[int],
+                  filter: Sequence[int], channels: int, pixels: int, swizzle="none", l2="none",
+                  oob="zero") -> TensorDesc:
+    """tbg_encode_im2col.  dims {C, W, H, N}; strides {W, H, N} in bytes; per-spatial arrays
+    {along W, along H}."""
+    d = TensorDesc()
+    st = _lib.tbg_encode_im2col(ctypes.byref(d), _enum(DTYPES, dtype), _vp(int(global_address)),
+                                _arr(ctypes.c_uint64, global_dim), _arr(ctypes.c_uint64, global_strides),
+                                _arr(ctypes.c_int32, pad_lo), _arr(ctypes.c_int32, pad_hi),
+                                _arr(ctypes.c_int32, conv_stride), _arr(ctypes.c_int32, dilation),
+                                _arr(ctypes.c_int32, filter), int(channels), int(pixels), _enum(SWIZZLES, swizzle),
+                                _enum(L2, l2), _enum(OOB, oob))
+    _check(st)
+    return d
+
+
+def encode_im2col_status(*args, **kwargs) -> int:
+    try:
+        encode_im2col(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
+
+
+def im2col_copy(desc: TensorDesc, coords: Sequence[int], dst_image: int, stream: Optional[int] = None) -> None:
+    """tbg_im2col_copy: coords = {c0, m0, s, r}."""
+    _check(_lib.tbg_im2col_copy(ctypes.byref(desc), _arr(ctypes.c_int32, coords), _vp(int(dst_image)),
+                                _vp(stream or 0)))
+
+
+def im2col_copy_many(desc: TensorDesc, coords_dev: int, n: int, dst_images: int, stream: Optional[int] = None) -> None:
+    _check(_lib.tbg_im2col_copy_many(ctypes.byref(desc), _vp(int(coords_dev)), int(n), _vp(int(dst_images)),
+                                     _vp(stream or 0)))
+
+
+def conv2d_out_dims(shape: Conv2dShape):
+    oh, ow = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.tbg_conv2d_out_dims(ctypes.byref(shape), ctypes.byref(oh), ctypes.byref(ow)))
+    return oh.value, ow.value
+
+
+def conv2d_workspace_bytes(shape: Conv2dShape) -> int:
+    return int(_lib.tbg_conv2d_workspace_bytes(ctypes.byref(shape)))
+
+
+def conv2d_fwd(shape: Conv2dShape, alpha: float, x: int, w: int, beta: float, y: int, ldy: int, y_dtype,
+               config: Optional[GemmConfig] = None, workspace: int = 0, workspace_bytes: int = 0,
+               stream: Optional[int] = None) -> None:
+    """tbg_conv2d_fwd: Y <- alpha·conv2d(X, W) + beta·Y (X NHWC, W KRSC, Y (N·OH·OW) × K)."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(_lib.tbg_conv2d_fwd(ctypes.byref(shape), float(alpha), _vp(int(x)), _vp(int(w)), float(beta), _vp(int(y)),
+                               int(ldy), _enum(DTYPES, y_dtype), cfg, _vp(int(workspace)), int(workspace_bytes),
+                               _vp(stream or 0)))
+
+
+def conv2d_fwd_status(*args, **kwargs) -> int:
+    try:
+        conv2d_fwd(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
+
+
 def gemm_workspace_bytes(M: int, N: int, K: int, lda: int, ldb: int, b_layout="kn") -> int:
     return int(_lib.tbg_gemm_workspace_bytes(M, N, K, lda, ldb, _enum(B_LAYOUTS, b_layout)))
 
@@ -231,7 +325,7 @@ def declared_functions() -> list:
     """Names of the functions include/tbg.h declares (used to check the library's exports)."""
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tbg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tbg_[a-z0-9_]+)\s*\(", text)))
 
 
 def library_path() -> str:

@@ -92,6 +92,21 @@ bool valid_desc(const tbg_tensor_desc* d, const DescImpl** out) {
   return true;
 }
 
+bool valid_im2col(const tbg_tensor_desc* d, const tbg::DescIm2col** out) {
+  if (!d) return false;
+  const tbg::DescIm2col* di = reinterpret_cast<const tbg::DescIm2col*>(d);
+  if (di->magic != tbg::kIm2colMagic || di->image_bytes == 0) return false;
+  *out = di;
+  return true;
+}
+
+// Output extent of a convolution along one dimension (0 when the window never fits).
+int64_t conv_out_dim(int64_t in, int64_t pad_lo, int64_t pad_hi, int64_t stride, int64_t dil, int64_t filt) {
+  const int64_t span = in + pad_lo + pad_hi - dil * (filt - 1) - 1;
+  if (stride < 1 || dil < 1 || filt < 1 || span < 0) return 0;
+  return span / stride + 1;
+}
+
 int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
@@ -196,8 +211,10 @@ tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank
 
 size_t tbg_box_bytes(const tbg_tensor_desc* d) {
   const DescImpl* di = nullptr;
-  if (!valid_desc(d, &di)) return 0;
-  return di->image_bytes;
+  if (valid_desc(d, &di)) return di->image_bytes;
+  const tbg::DescIm2col* ii = nullptr;
+  if (valid_im2col(d, &ii)) return ii->image_bytes;
+  return 0;
 }
 
 tbg_status tbg_tiled_copy(const tbg_tensor_desc* d, const int32_t* coords, void* dst_image, void* stream) {
@@ -249,6 +266,118 @@ tbg_status tbg_tiled_store_many(const tbg_tensor_desc* d, const int32_t* coords_
   if (st != TBG_OK) return st;
   hipError_t e = tbg::launch_tiled_store(*di, nullptr, coords_dev, n, src_images, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "tiled store launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
+tbg_status tbg_encode_im2col(tbg_tensor_desc* out, tbg_dtype dtype, const void* global_address,
+                             const uint64_t* global_dim, const uint64_t* global_strides, const int32_t* pad_lo,
+                             const int32_t* pad_hi, const int32_t* conv_stride, const int32_t* dilation,
+                             const int32_t* filter, uint32_t channels, uint32_t pixels, tbg_swizzle swizzle,
+                             tbg_l2_hint l2, tbg_oob_fill oob) {
+  if (!out) return fail(TBG_ERR_INVALID_VALUE, "out is NULL");
+  const int es = elsize_of(dtype);
+  if (es == 0) return fail(TBG_ERR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
+  if (!global_address) return fail(TBG_ERR_INVALID_VALUE, "global_address is NULL");
+  if (!global_dim || !global_strides || !pad_lo || !pad_hi || !conv_stride || !dilation || !filter)
+    return fail(TBG_ERR_INVALID_VALUE, "a per-dimension array is NULL");
+  if (((uintptr_t)global_address) % 16 != 0)
+    return fail(TBG_ERR_MISALIGNED, "global_address %p is not a multiple of 16 bytes", global_address);
+  if ((int)swizzle < TBG_SWIZZLE_NONE || (int)swizzle > TBG_SWIZZLE_128B_2ROW)
+    return fail(TBG_ERR_INVALID_VALUE, "unknown swizzle %d", (int)swizzle);
+  if ((int)l2 < TBG_L2_NONE || (int)l2 > TBG_L2_256B) return fail(TBG_ERR_INVALID_VALUE, "unknown l2 hint %d", (int)l2);
+  if ((int)oob != TBG_OOB_ZERO && (int)oob != TBG_OOB_NAN)
+    return fail(TBG_ERR_INVALID_VALUE, "unknown oob fill %d", (int)oob);
+  if (oob == TBG_OOB_NAN && !(dtype == TBG_F16 || dtype == TBG_BF16 || dtype == TBG_F32))
+    return fail(TBG_ERR_INVALID_VALUE, "NaN fill needs a floating-point element type");
+  for (int i = 0; i < 4; ++i)
+    if (global_dim[i] < 1 || global_dim[i] > (1ull << 31) - 1)
+      return fail(TBG_ERR_OUT_OF_RANGE, "global_dim[%d] = %llu not in 1..2^31-1", i, (unsigned long long)global_dim[i]);
+  for (int i = 0; i < 3; ++i) {
+    if (global_strides[i] % 16 != 0)
+      return fail(TBG_ERR_MISALIGNED, "global_strides[%d] = %llu is not a multiple of 16 bytes", i,
+                  (unsigned long long)global_strides[i]);
+    if (global_strides[i] == 0 || global_strides[i] >= (1ull << 40))
+      return fail(TBG_ERR_OUT_OF_RANGE, "global_strides[%d] = %llu not in 16..2^40", i,
+                  (unsigned long long)global_strides[i]);
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (filter[i] < 1 || filter[i] > 256) return fail(TBG_ERR_OUT_OF_RANGE, "filter[%d] = %d not in 1..256", i, filter[i]);
+    if (conv_stride[i] < 1 || conv_stride[i] > 256)
+      return fail(TBG_ERR_OUT_OF_RANGE, "conv_stride[%d] = %d not in 1..256", i, conv_stride[i]);
+    if (dilation[i] < 1 || dilation[i] > 256)
+      return fail(TBG_ERR_OUT_OF_RANGE, "dilation[%d] = %d not in 1..256", i, dilation[i]);
+    if (pad_lo[i] < 0 || pad_lo[i] > 65535 || pad_hi[i] < 0 || pad_hi[i] > 65535)
+      return fail(TBG_ERR_OUT_OF_RANGE, "padding along dimension %d not in 0..65535", i);
+  }
+  const int64_t ow = conv_out_dim((int64_t)global_dim[1], pad_lo[0], pad_hi[0], conv_stride[0], dilation[0], filter[0]);
+  const int64_t oh = conv_out_dim((int64_t)global_dim[2], pad_lo[1], pad_hi[1], conv_stride[1], dilation[1], filter[1]);
+  if (ow < 1 || oh < 1) return fail(TBG_ERR_INVALID_VALUE, "the filter window does not fit the padded image");
+  if ((int64_t)global_dim[3] * oh * ow > INT32_MAX)
+    return fail(TBG_ERR_UNSUPPORTED, "more than 2^31-1 output pixels");
+  if (channels < 1 || channels > tbg::kMaxBox || pixels < 1 || pixels > tbg::kMaxBox)
+    return fail(TBG_ERR_OUT_OF_RANGE, "channels %u and pixels %u must be in 1..256", channels, pixels);
+  const uint64_t image = (uint64_t)es * channels * pixels;
+  if (image > tbg::kMaxImageBytes)
+    return fail(TBG_ERR_OUT_OF_RANGE, "box image of %llu bytes exceeds 64 KiB", (unsigned long long)image);
+  if (swizzle != TBG_SWIZZLE_NONE) {
+    const uint32_t span = swizzle_span(swizzle);
+    if ((uint64_t)channels * es > span)
+      return fail(TBG_ERR_INVALID_VALUE, "swizzled box inner extent %u bytes exceeds the %u-byte span",
+                  (unsigned)(channels * es), span);
+    if (image % span != 0)
+      return fail(TBG_ERR_INVALID_VALUE, "swizzled image of %llu bytes is not a multiple of the %u-byte span",
+                  (unsigned long long)image, span);
+  }
+  tbg::DescIm2col d;
+  memset(&d, 0, sizeof(d));
+  d.magic = tbg::kIm2colMagic;
+  d.dtype = (uint8_t)dtype;
+  d.elsize = (uint8_t)es;
+  d.swizzle = (uint8_t)swizzle;
+  d.oob = (uint8_t)oob;
+  d.l2 = (uint8_t)l2;
+  d.base = (uint64_t)(uintptr_t)global_address;
+  for (int i = 0; i < 4; ++i) d.dim[i] = (uint32_t)global_dim[i];
+  for (int i = 0; i < 3; ++i) d.stride[i] = global_strides[i];
+  for (int i = 0; i < 2; ++i) {
+    d.pad_lo[i] = pad_lo[i];
+    d.pad_hi[i] = pad_hi[i];
+    d.cstride[i] = conv_stride[i];
+    d.dil[i] = dilation[i];
+    d.filt[i] = filter[i];
+  }
+  d.out[0] = (uint32_t)ow;
+  d.out[1] = (uint32_t)oh;
+  d.channels = channels;
+  d.pixels = pixels;
+  d.image_bytes = (uint32_t)image;
+  memcpy(out, &d, sizeof(d));
+  return TBG_OK;
+}
+
+tbg_status tbg_im2col_copy(const tbg_tensor_desc* d, const int32_t* coords, void* dst_image, void* stream) {
+  const tbg::DescIm2col* di = nullptr;
+  if (!valid_im2col(d, &di)) return fail(TBG_ERR_INVALID_VALUE, "not an encoded im2col descriptor");
+  if (!coords || !dst_image) return fail(TBG_ERR_INVALID_VALUE, "coords or dst_image is NULL");
+  if (((uintptr_t)dst_image) % 16 != 0) return fail(TBG_ERR_MISALIGNED, "dst_image is not 16-byte aligned");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  hipError_t e = tbg::launch_im2col_copy(*di, coords, nullptr, 1, dst_image, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "im2col copy launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
+tbg_status tbg_im2col_copy_many(const tbg_tensor_desc* d, const int32_t* coords_dev, uint32_t n, void* dst_images,
+                                void* stream) {
+  const tbg::DescIm2col* di = nullptr;
+  if (!valid_im2col(d, &di)) return fail(TBG_ERR_INVALID_VALUE, "not an encoded im2col descriptor");
+  if (n == 0) return TBG_OK;
+  if (!coords_dev || !dst_images) return fail(TBG_ERR_INVALID_VALUE, "coords_dev or dst_images is NULL");
+  if (((uintptr_t)dst_images) % 16 != 0) return fail(TBG_ERR_MISALIGNED, "dst_images is not 16-byte aligned");
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  hipError_t e = tbg::launch_im2col_copy(*di, nullptr, coords_dev, n, dst_images, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "im2col copy launch: %s", hipGetErrorString(e));
   return TBG_OK;
 }
 
@@ -440,6 +569,182 @@ tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, con
   const bool scaled = !(alpha == 1.f && beta == 0.f);
   return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, cfg, workspace, workspace_bytes, stream,
                    scaled);
+}
+
+
+}  // extern "C"
+
+namespace {
+
+struct ConvPlan {
+  int64_t oh = 0, ow = 0, m = 0, c8 = 0;
+  bool pack = false;
+  size_t x_bytes = 0, w_bytes = 0;  // packed sizes (256-byte rounded) when pack
+};
+
+tbg_status conv_plan(const tbg_conv2d_shape* sh, bool x_aligned, bool w_aligned, ConvPlan& pl) {
+  if (!sh) return fail(TBG_ERR_INVALID_VALUE, "shape is NULL");
+  if (sh->n < 1 || sh->h < 1 || sh->w < 1 || sh->c < 1 || sh->k < 1)
+    return fail(TBG_ERR_INVALID_VALUE, "n, h, w, c and k must be at least 1");
+  if (sh->r < 1 || sh->s < 1 || sh->stride_h < 1 || sh->stride_w < 1 || sh->dil_h < 1 || sh->dil_w < 1)
+    return fail(TBG_ERR_INVALID_VALUE, "filter sizes, strides and dilations must be at least 1");
+  if (sh->pad_h < 0 || sh->pad_w < 0 || sh->pad_h_end < 0 || sh->pad_w_end < 0)
+    return fail(TBG_ERR_INVALID_VALUE, "padding must not be negative");
+  if (sh->r > 256 || sh->s > 256 || sh->stride_h > 256 || sh->stride_w > 256 || sh->dil_h > 256 || sh->dil_w > 256 ||
+      sh->pad_h > 65535 || sh->pad_w > 65535 || sh->pad_h_end > 65535 || sh->pad_w_end > 65535)
+    return fail(TBG_ERR_UNSUPPORTED, "filter, stride and dilation are limited to 256, padding to 65535");
+  pl.oh = conv_out_dim(sh->h, sh->pad_h, sh->pad_h_end, sh->stride_h, sh->dil_h, sh->r);
+  pl.ow = conv_out_dim(sh->w, sh->pad_w, sh->pad_w_end, sh->stride_w, sh->dil_w, sh->s);
+  if (pl.oh < 1 || pl.ow < 1) return fail(TBG_ERR_INVALID_VALUE, "the filter window does not fit the padded image");
+  pl.m = sh->n * pl.oh * pl.ow;
+  pl.c8 = (sh->c + 7) / 8 * 8;
+  if (pl.m > INT32_MAX || sh->k > INT32_MAX || sh->h > 65535 || sh->w > 65535)
+    return fail(TBG_ERR_UNSUPPORTED, "sizes beyond this library's limits (output pixels and k below 2^31, h and w below 2^16)");
+  const int64_t x_elems = sh->n * sh->h * sh->w * pl.c8;
+  const int64_t ldw = (int64_t)sh->r * sh->s * pl.c8;
+  if (x_elems * 2 >= (1ll << 31)) return fail(TBG_ERR_UNSUPPORTED, "the input tensor must stay below 2 GiB");
+  if (ldw > (1ll << 22) - 1) return fail(TBG_ERR_UNSUPPORTED, "r*s*c is limited to 2^22-1");
+  pl.pack = (sh->c % 8) != 0 || !x_aligned || !w_aligned;
+  if (pl.pack) {
+    pl.x_bytes = (size_t)((x_elems * 2 + 255) / 256 * 256);
+    pl.w_bytes = (size_t)((sh->k * ldw * 2 + 255) / 256 * 256);
+  }
+  return TBG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tbg_status tbg_conv2d_out_dims(const tbg_conv2d_shape* shape, int64_t* oh, int64_t* ow) {
+  ConvPlan pl;
+  tbg_status st = conv_plan(shape, true, true, pl);
+  if (st != TBG_OK) return st;
+  if (oh) *oh = pl.oh;
+  if (ow) *ow = pl.ow;
+  return TBG_OK;
+}
+
+size_t tbg_conv2d_workspace_bytes(const tbg_conv2d_shape* shape) {
+  ConvPlan pl;
+  if (conv_plan(shape, true, true, pl) != TBG_OK) return 0;
+  return pl.x_bytes + pl.w_bytes;
+}
+
+tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void* x, const void* w, float beta,
+                          void* y, int64_t ldy, tbg_dtype y_dtype, const tbg_gemm_config* cfg, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const bool x_aligned = ((uintptr_t)x % 16) == 0, w_aligned = ((uintptr_t)w % 16) == 0;
+  ConvPlan pl;
+  tbg_status st = conv_plan(shape, x_aligned, w_aligned, pl);
+  if (st != TBG_OK) return st;
+  if (cfg) {
+    if (cfg->pipeline != TBG_PIPE_AUTO && cfg->pipeline != TBG_PIPE_RING)
+      return fail(TBG_ERR_UNSUPPORTED, "the convolution runs on the barrier ring only");
+    if (cfg->stages != 0 && cfg->stages != 2)
+      return fail(TBG_ERR_UNSUPPORTED, "the convolution ring has 2 stages");
+    if ((cfg->tile_m == 0) != (cfg->tile_n == 0))
+      return fail(TBG_ERR_INVALID_VALUE, "tile_m and tile_n must both be 0 or both be set");
+    if (cfg->tile_m != 0 && !tbg::conv_tile_built(cfg->tile_m, cfg->tile_n))
+      return fail(TBG_ERR_UNSUPPORTED, "no convolution kernel with tile %dx%d (built: 256x256, 256x128, 128x128, 64x64)",
+                  cfg->tile_m, cfg->tile_n);
+  }
+  if (y_dtype != TBG_F32 && y_dtype != TBG_BF16) return fail(TBG_ERR_INVALID_VALUE, "y must be TBG_F32 or TBG_BF16");
+  if (ldy < shape->k) return fail(TBG_ERR_INVALID_VALUE, "ldy=%lld < k=%lld", (long long)ldy, (long long)shape->k);
+  if (ldy > (1ll << 40)) return fail(TBG_ERR_UNSUPPORTED, "ldy is limited to 2^40");
+  if (!y) return fail(TBG_ERR_INVALID_VALUE, "y is NULL");
+  const bool scaled = !(alpha == 1.f && beta == 0.f);
+  const bool skip_product = scaled && alpha == 0.f;
+  if (!skip_product && (!x || !w)) return fail(TBG_ERR_INVALID_VALUE, "x or w is NULL");
+  const size_t need = pl.x_bytes + pl.w_bytes;
+  if (!skip_product && need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(TBG_ERR_OUT_OF_RANGE, "workspace of %zu bytes needed to repack the channels (have %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256 != 0) return fail(TBG_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  }
+  int num_cus = 0;
+  st = check_device(&num_cus);
+  if (st != TBG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (skip_product) {
+    // alpha == 0: C <- beta·C through the GEMM's epilogue with an empty product
+    return gemm_impl(pl.m, shape->k, 0, 0.f, nullptr, 1, nullptr, 1, TBG_B_NK, beta, y, ldy, y_dtype, nullptr,
+                     nullptr, 0, stream, true);
+  }
+  const uint16_t* X = (const uint16_t*)x;
+  const uint16_t* W = (const uint16_t*)w;
+  const int64_t ldw = (int64_t)shape->r * shape->s * pl.c8;
+  if (pl.pack) {
+    uint16_t* xp = (uint16_t*)workspace;
+    uint16_t* wp = (uint16_t*)((uint8_t*)workspace + pl.x_bytes);
+    e = tbg::launch_pack(X, shape->c, shape->n * shape->h * shape->w, shape->c, xp, pl.c8, s);
+    if (e == hipSuccess) e = tbg::launch_pack(W, shape->c, shape->k * shape->r * shape->s, shape->c, wp, pl.c8, s);
+    if (e != hipSuccess) return fail(TBG_ERR_HIP, "channel repack: %s", hipGetErrorString(e));
+    X = xp;
+    W = wp;
+  }
+  tbg::ConvParams cp;
+  memset(&cp, 0, sizeof(cp));
+  cp.g.A = X;
+  cp.g.B = W;
+  cp.g.C = y;
+  cp.g.lda = pl.c8;
+  cp.g.ldb = ldw;
+  cp.g.ldc = ldy;
+  cp.g.M = (int)pl.m;
+  cp.g.N = (int)shape->k;
+  cp.g.K = (int)(ldw);
+  cp.g.kchunks = (int)(ldw / 8);
+  cp.g.group_m = 8;
+  cp.g.vec_store = (((uintptr_t)y) % 16 == 0) && ((ldy * (y_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
+  cp.g.alpha = alpha;
+  cp.g.beta = beta;
+  cp.g.scaled = scaled ? 1 : 0;
+  cp.X = X;
+  cp.W = W;
+  cp.ldw = ldw;
+  cp.x_bytes = (uint32_t)(shape->n * shape->h * shape->w * pl.c8 * 2);
+  cp.n = (int)shape->n;
+  cp.h = (int)shape->h;
+  cp.w = (int)shape->w;
+  cp.c8 = (int)pl.c8;
+  cp.r = shape->r;
+  cp.s = shape->s;
+  cp.oh = (int)pl.oh;
+  cp.ow = (int)pl.ow;
+  cp.ph = shape->pad_h;
+  cp.pw = shape->pad_w;
+  cp.sh = shape->stride_h;
+  cp.sw = shape->stride_w;
+  cp.dh = shape->dil_h;
+  cp.dw = shape->dil_w;
+  cp.cblocks = (int)((pl.c8 + 63) / 64);
+  // Workgroup tile: the GEMM ring's cost model (tiles per busiest CU × tile work / measured
+  // efficiency relative to 256×256) over the tiles built for convolution.
+  int bm = 256, bn = 256;
+  double best = 0;
+  const struct { int bm, bn; double eff; } tiles[] = {{256, 256, 1.0}, {128, 128, 0.82}, {256, 128, 0.73},
+                                                      {64, 64, 0.52}};
+  const int cus = num_cus > 0 ? num_cus : 256;
+  for (const auto& t : tiles) {
+    const int64_t ntiles = ((pl.m + t.bm - 1) / t.bm) * ((shape->k + t.bn - 1) / t.bn);
+    const int64_t rounds = (ntiles + cus - 1) / cus;
+    const double cost = (double)rounds * t.bm * t.bn / t.eff;
+    if (best == 0 || cost < best * 0.999) {
+      best = cost;
+      bm = t.bm;
+      bn = t.bn;
+    }
+  }
+  if (cfg && cfg->tile_m != 0) {
+    bm = cfg->tile_m;
+    bn = cfg->tile_n;
+  }
+  e = tbg::launch_conv(cp, bm, bn, y_dtype == TBG_BF16, s);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "convolution launch: %s", hipGetErrorString(e));
+  return TBG_OK;
 }
 
 }  // extern "C"

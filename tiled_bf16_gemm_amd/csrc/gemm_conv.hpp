@@ -1,0 +1,129 @@
+// Implicit-GEMM 2-D convolution: the barrier ring of gemm_ring.hpp (two stages) whose A tiles
+// are blocks of the im2col matrix, formed by the copy itself.
+//
+// "2 · Le Tensor Memory Accelerator", section "im2col": the copy performs the im2col transform,
+// so the convolution becomes a GEMM and the im2col matrix is never stored.  The GEMM here is
+//   Y (N·OH·OW × K) = im2col(X) (N·OH·OW × R·S·C) · Wᵀ,  W viewed as K × (R·S·C),
+// its K loop running over filter taps (r, s) and, inside each tap, 64-channel blocks.  For the
+// A tile of output pixels m0..m0+BM-1 at tap (r, s) and channels c0..c0+63, each lane's 16-byte
+// atom chunk comes from X[n, oh·sh − ph + r·dh, ow·sw − pw + s·dw, c0 + 8·chunk .. +7] of its
+// pixel; a window position outside the image (the zero padding), a pixel past the output and a
+// chunk past the channels all take the buffer's out-of-range offset and land zeros — the
+// out-of-bounds fill that "removes the edge guards of convolutions" in the same page.  The B
+// tile is the filters' N×K box at column (r·S + s)·c8 + c0.  Fragment reads, products and the
+// epilogue are the GEMM's.
+#pragma once
+#include "gemm_common.hpp"
+#include "gemm_ring.hpp"
+
+namespace tbg {
+
+template <int BM, int BN, int OUT, int SCALED>
+__global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gemm_conv_kernel(ConvParams cp) {
+  using T = TileCfg<BM, BN>;
+  constexpr int BL = 1;  // the filters are stored K × (R·S·c8): the GEMM's B stored N×K
+  const GemmParams& p = cp.g;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::StageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // ---- im2col atoms of A: this wave owns box rows (BM/4)*wave .. +BM/4-1 (as the ring) ----------
+  // Per atom, the lane's output pixel as its window origin (ih0, iw0) and the byte offset of
+  // X[n, ih0, iw0, 0] (negative when the origin is in the padding); a pixel past the output gets
+  // an origin no tap can bring inside.
+  const int cpix = cp.c8 * 2;  // bytes per pixel
+  int ih0[T::AtomsA], iw0[T::AtomsA], pix[T::AtomsA];
+#pragma unroll
+  for (int j = 0; j < T::AtomsA; ++j) {
+    const int row = (BM / 4) * wave + 8 * j + (lane >> 3);
+    const int m = m0 + row;
+    if (m < p.M) {
+      const int per_img = cp.oh * cp.ow;
+      const int n = m / per_img;
+      const int rem = m - n * per_img;
+      const int oh = rem / cp.ow;
+      const int ow = rem - oh * cp.ow;
+      ih0[j] = oh * cp.sh - cp.ph;
+      iw0[j] = ow * cp.sw - cp.pw;
+      pix[j] = ((n * cp.h + ih0[j]) * cp.w + iw0[j]) * cpix;
+    } else {
+      ih0[j] = -(1 << 28);
+      iw0[j] = 0;
+      pix[j] = 0;
+    }
+  }
+  const uint32_t pitch_b = (uint32_t)(cp.ldw * 2);
+  LaneChunk lb[T::AtomsB];
+#pragma unroll
+  for (int i = 0; i < T::AtomsB; ++i) lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+  const int ktiles = cp.r * cp.s * cp.cblocks;
+  const uint32_t smem_addr = lds_addr_of(smem);
+  const rsrc_t rx = make_rsrc(cp.X, cp.x_bytes);
+
+  // Copies of K tile kt (tap kt / cblocks, channel block kt % cblocks) into `stage`; la receives
+  // this tile's per-lane A sources.  A tile past the end is issued fully masked.
+  auto make_copy = [&](int kt, int stage, LaneChunk* la) {
+    const bool live = kt < ktiles;
+    const int tap = live ? kt / cp.cblocks : 0;
+    const int cb = live ? kt - tap * cp.cblocks : 0;
+    const int rr = tap / cp.s, ss = tap - rr * cp.s;
+    const int c0 = cb * 64;
+    const int dy = rr * cp.dh, dx = ss * cp.dw;
+    const int tap_off = (dy * cp.w + dx) * cpix + c0 * 2;
+#pragma unroll
+    for (int j = 0; j < T::AtomsA; ++j) {
+      const int row = (BM / 4) * wave + 8 * j + (lane >> 3);
+      const int chunk = (lane & 7) ^ row_xor<kSwizzle128B2Row>(row);
+      const bool ok = live && (unsigned)(ih0[j] + dy) < (unsigned)cp.h && (unsigned)(iw0[j] + dx) < (unsigned)cp.w;
+      la[j].chunk = chunk;
+      la[j].offset = ok ? (uint32_t)(pix[j] + tap_off + chunk * 16) : kOobOffset;
+    }
+    TileCopy tc;
+    const uint32_t sa = smem_addr + stage * T::StageBytes;
+    tc.ra = rx;
+    tc.lds_a = sa + (BM / 4) * wave * 128;
+    tc.cvalid_a = live ? (cp.c8 - c0) >> 3 : -1;
+    const uint16_t* origin = cp.W + (uint64_t)n0 * cp.ldw + (live ? tap * cp.c8 + c0 : 0);
+    const int64_t rem = live ? ((int64_t)(p.N - 1 - n0) * cp.ldw + (cp.c8 - c0)) * 2 : 0;
+    tc.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+    tc.lds_b = sa + T::ABytes + (BN / 4) * wave * 128;
+    tc.cvalid_b = tc.cvalid_a;
+    return tc;
+  };
+
+  const FragAddr<T> fa = make_frag_addr<T>(wm, wn, lane);
+  f32x4_t acc[T::FN][T::FM];
+  zero_acc<T>(acc);
+  {
+    Frags<T> f0, f1;
+    const TileCopy none{};
+    LaneChunk la[T::AtomsA];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const TileCopy tc = make_copy(t, t, la);
+#pragma unroll
+      for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
+    }
+    stage_barrier<T::Atoms>();  // tile 0 landed; tile 1 may be in flight
+#pragma unroll
+    for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
+    for (int kt = 0; kt < ktiles; ++kt) {
+      const int cur = kt & 1;
+      const uint8_t* sA = smem + cur * T::StageBytes;
+      kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
+      stage_barrier<0>();  // tile kt+1 landed everywhere; stage kt&1 free
+      const uint8_t* nA = smem + (cur ^ 1) * T::StageBytes;
+      const TileCopy tc = make_copy(kt + 2, cur, la);
+      kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
+    }
+  }
+  stage_barrier<0>();
+  store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
+}
+
+}  // namespace tbg

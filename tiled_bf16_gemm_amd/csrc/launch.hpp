@@ -21,6 +21,27 @@ struct GemmParams {
   int scaled;      // 0: C = A·B; 1: C = alpha·A·B + beta·C (C read only when beta != 0)
 };
 
+// Arguments of one implicit-GEMM convolution launch (gemm_conv.hpp).  `g` carries what the
+// GEMM epilogue needs: M = N*OH*OW output pixels, N = K output channels, C = Y, ldc = ldy,
+// vec_store, alpha/beta/scaled, and the tile grid.  X and W have a channel pitch of c8 (a
+// multiple of 8; channels c8 > c >= C hold zeros after packing).
+struct ConvParams {
+  GemmParams g;
+  const uint16_t* X;   // NHWC, channel pitch c8
+  const uint16_t* W;   // K × (R·S·c8): filter k, tap (r, s), channel c at k*ldw + (r*S + s)*c8 + c
+  int64_t ldw;         // R * S * c8
+  uint32_t x_bytes;    // bytes of X (below 2^31)
+  int n, h, w, c8, r, s, oh, ow;
+  int ph, pw, sh, sw, dh, dw;
+  int cblocks;         // ceil(c8 / 64): 64-channel blocks per tap
+};
+
+hipError_t launch_im2col_copy(const DescIm2col& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
+                              void* dst, hipStream_t stream);
+// Convolution with workgroup tile bm × bn (256×256, 256×128, 128×128 or 64×64); fills the grid.
+hipError_t launch_conv(ConvParams cp, int bm, int bn, int out_bf16, hipStream_t stream);
+bool conv_tile_built(int bm, int bn);
+
 hipError_t launch_tiled_store(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
                               const void* src, hipStream_t stream);
 hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,

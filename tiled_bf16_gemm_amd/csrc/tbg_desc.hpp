@@ -34,6 +34,27 @@ struct DescImpl {
 };
 static_assert(sizeof(DescImpl) == 128, "descriptor must stay 128 bytes");
 
+// Layout of an im2col descriptor (also 128 bytes, told apart by its magic): the NHWC tensor,
+// the convolution's window geometry and the box ({channels, pixels}) of one copy.  Per-spatial
+// arrays are {along W, along H}.  "2 · Le Tensor Memory Accelerator", section "im2col".
+constexpr uint32_t kIm2colMagic = 0x49474254u;  // "TBGI"
+
+struct DescIm2col {
+  uint32_t magic;
+  uint8_t dtype, elsize, swizzle, oob;
+  uint8_t l2;
+  uint8_t pad0[7];
+  uint64_t base;          // device address of element (n, h, w, c) = (0, 0, 0, 0)
+  uint32_t dim[4];        // C, W, H, N
+  uint64_t stride[3];     // byte strides of W, H, N (the channel stride is the element size)
+  int32_t pad_lo[2], pad_hi[2], cstride[2], dil[2], filt[2];
+  uint32_t out[2];        // OW, OH: output extents of the convolution
+  uint32_t channels, pixels;
+  uint32_t image_bytes;   // elsize * channels * pixels
+  uint32_t pad1;
+};
+static_assert(sizeof(DescIm2col) == 128, "im2col descriptor must stay 128 bytes");
+
 // Extension swizzle mode for gfx950's 64-bank LDS (see tbg.h): a[6:4] ^= a[10:8].
 constexpr int kSwizzle128B2Row = 4;
 

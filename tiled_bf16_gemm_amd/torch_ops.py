@@ -115,3 +115,69 @@ def tiled_store_many(desc: tbg.TensorDesc, coords: torch.Tensor, images: torch.T
     if images.numel() * images.element_size() < n * tbg.box_bytes(desc):
         raise ValueError("images holds fewer than n box images")
     tbg.tiled_store_many(desc, coords.data_ptr(), n, images.data_ptr(), stream_handle(stream))
+
+
+def conv2d(x: torch.Tensor, w: torch.Tensor, pad=(0, 0, 0, 0), stride=(1, 1), dil=(1, 1), out_dtype: str = "bf16",
+           out: Optional[torch.Tensor] = None, alpha: float = 1.0, beta: float = 0.0,
+           workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
+           config: Optional[tbg.GemmConfig] = None) -> torch.Tensor:
+    """Y = alpha·conv2d(x, w) + beta·Y through tbg_conv2d_fwd.  x: (N, H, W, C) bf16 contiguous
+    (NHWC); w: (K, R, S, C) bf16 contiguous (KRSC); pad = (top, left, bottom, right); stride and
+    dil = (h, w).  Returns / fills out: (N·OH·OW, K) rows, row stride = ldy."""
+    for t, name in ((x, "x"), (w, "w")):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 CUDA tensor")
+    n, h, wd, c = x.shape
+    k, r, s, c2 = w.shape
+    if c2 != c:
+        raise ValueError(f"channel counts differ: {c} vs {c2}")
+    shp = tbg.conv2d_shape(n, h, wd, c, k, r, s, pad, stride, dil)
+    oh, ow = tbg.conv2d_out_dims(shp)
+    if out is None:
+        out = torch.empty((n * oh * ow, k), dtype=_TORCH_OF[out_dtype], device=x.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != n * oh * ow or out.shape[1] != k:
+        raise ValueError("out must be a (N·OH·OW, K) row-major view")
+    need = tbg.conv2d_workspace_bytes(shp)
+    if (x.data_ptr() % 16) or (w.data_ptr() % 16):
+        c8 = (c + 7) // 8 * 8
+        need = ((n * h * wd * c8 * 2 + 255) // 256 * 256) + ((k * r * s * c8 * 2 + 255) // 256 * 256)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    tbg.conv2d_fwd(shp, alpha, x.data_ptr(), w.data_ptr(), beta, out.data_ptr(), out.stride(0), out_dtype, config,
+                   ws_ptr, ws_bytes, stream_handle(stream))
+    return out
+
+
+def encode_im2col(t: torch.Tensor, dtype: str, pad=(0, 0, 0, 0), stride=(1, 1), dil=(1, 1), filt=(1, 1),
+                  channels: int = 64, pixels: int = 64, swizzle: str = "none", oob: str = "zero") -> tbg.TensorDesc:
+    """im2col descriptor of a contiguous NHWC tensor t; pad = (top, left, bottom, right), stride,
+    dil and filt = (h, w)."""
+    n, h, w, c = t.shape
+    es = t.element_size()
+    return tbg.encode_im2col(dtype, t.data_ptr(), [c, w, h, n], [c * es, c * es * w, c * es * w * h],
+                             [pad[1], pad[0]], [pad[3], pad[2]], [stride[1], stride[0]], [dil[1], dil[0]],
+                             [filt[1], filt[0]], channels, pixels, swizzle, "none", oob)
+
+
+def im2col_copy(desc: tbg.TensorDesc, coords, out: Optional[torch.Tensor] = None, device="cuda",
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    nbytes = tbg.box_bytes(desc)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    tbg.im2col_copy(desc, coords, out.data_ptr(), stream_handle(stream))
+    return out
+
+
+def im2col_copy_many(desc: tbg.TensorDesc, coords: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """coords: (n, 4) int32 CUDA tensor of {c0, m0, s, r}.  Returns n images back to back."""
+    if coords.dtype != torch.int32 or not coords.is_cuda or not coords.is_contiguous() or coords.shape[1] != 4:
+        raise ValueError("coords must be a contiguous (n, 4) int32 CUDA tensor")
+    n = coords.shape[0]
+    nbytes = tbg.box_bytes(desc)
+    if out is None:
+        out = torch.empty(n * nbytes, dtype=torch.uint8, device=coords.device)
+    tbg.im2col_copy_many(desc, coords.data_ptr(), n, out.data_ptr(), stream_handle(stream))
+    return out

@@ -15,6 +15,13 @@ with element strides and NaN fill):
   c4  8192³ GEMM, uniform[-1,1], bf16 out
   c5  M=16384, K=4096, N=14336; activations N(0,1); weights N(0, sd 0.02) stored N×K; bf16 out
 
+Convolution workloads (the im2col copy mode of "2 · Le Tensor Memory Accelerator" turns a 2-D
+convolution into a GEMM; the pages give no convolution sizes): layers in the shape of an image
+network's — 3×3 filters with padding 1, a strided 3×3, a dilated 3×3, a 1×1, a 7×7 stem on three
+channels — plus the benchmark layer conv_b (batch 32, 56×56, 128 → 128 channels, 3×3).  Inputs
+and filters are N(0,1) scaled by 1/sqrt(R·S·C) for the filters (the usual initialisation), seeds
+6000+2i and 6000+2i+1 for workload i.
+
 Seeds: workload k draws A from seed 1000k+1 and B from 1000k+2 (torch.Generator, CPU);
 "uniform[-1,1]" is 2·U[0,1)−1 in fp32 and N(0,σ) is σ·randn, both rounded to bf16 by torch's
 round-to-nearest-even conversion.  Padding columns of a padded leading dimension are filled with
@@ -86,6 +93,57 @@ GEMMS = {
     "c4": GemmWorkload("c4", 8192, 8192, 8192, ("uniform", 1.0), ("uniform", 1.0), "kn", "bf16", 4001, 4002),
     "c5": GemmWorkload("c5", 16384, 14336, 4096, ("normal", 1.0), ("normal", 0.02), "nk", "bf16", 5001, 5002),
 }
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    n: int
+    h: int
+    w: int
+    c: int
+    k: int
+    r: int
+    s: int
+    pad: Tuple[int, int, int, int] = (0, 0, 0, 0)   # top, left, bottom, right
+    stride: Tuple[int, int] = (1, 1)                # h, w
+    dil: Tuple[int, int] = (1, 1)                   # h, w
+    out_dtype: str = "bf16"
+    seed: int = 6000
+
+    def out_dims(self):
+        oh = (self.h + self.pad[0] + self.pad[2] - self.dil[0] * (self.r - 1) - 1) // self.stride[0] + 1
+        ow = (self.w + self.pad[1] + self.pad[3] - self.dil[1] * (self.s - 1) - 1) // self.stride[1] + 1
+        return oh, ow
+
+    @property
+    def M(self) -> int:
+        oh, ow = self.out_dims()
+        return self.n * oh * ow
+
+    @property
+    def flops(self) -> int:
+        """2 · (output elements) · (taps inside or outside the image) · C: the GEMM's count."""
+        return 2 * self.M * self.k * self.r * self.s * self.c
+
+
+CONVS = {
+    "conv_3x3": ConvWorkload("conv_3x3", 2, 17, 17, 24, 36, 3, 3, (1, 1, 1, 1), out_dtype="f32", seed=6000),
+    "conv_c20": ConvWorkload("conv_c20", 2, 15, 13, 20, 40, 3, 3, (1, 1, 1, 1), seed=6002),
+    "conv_stride2": ConvWorkload("conv_stride2", 3, 23, 23, 64, 80, 3, 3, (1, 1, 0, 1), (2, 2), out_dtype="f32",
+                                 seed=6004),
+    "conv_dil2": ConvWorkload("conv_dil2", 2, 20, 25, 32, 64, 3, 3, (2, 2, 2, 2), dil=(2, 2), seed=6006),
+    "conv_1x1": ConvWorkload("conv_1x1", 4, 14, 14, 128, 96, 1, 1, out_dtype="f32", seed=6008),
+    "conv_stem": ConvWorkload("conv_stem", 2, 32, 32, 3, 64, 7, 7, (3, 3, 3, 3), (2, 2), seed=6010),
+    "conv_b": ConvWorkload("conv_b", 32, 56, 56, 128, 128, 3, 3, (1, 1, 1, 1), seed=6012),
+}
+
+
+def conv_inputs(w: ConvWorkload):
+    """(X NHWC, W KRSC) as contiguous CPU bf16 tensors."""
+    x = _draw((w.n, w.h, w.w, w.c), ("normal", 1.0), w.seed)
+    f = _draw((w.k, w.r, w.s, w.c), ("normal", 1.0 / float(np.sqrt(w.r * w.s * w.c))), w.seed + 1)
+    return x.contiguous(), f.contiguous()
 
 
 def _c1_copy_coords():
