@@ -14,7 +14,8 @@ Also reported in the same line:
                 summary when it was taken on the current kernel source, else null.
   cpu_baseline  the CPU oracle on a bounded sample of the same product (the first rows of C),
                 timed on this host's cores.
-  per_config    TFLOP/s and % of peak on all five workloads (timed the same way, fewer steps).
+  per_config    TFLOP/s and % of peak on all five GEMM workloads and the benchmark convolution
+                layer (timed the same way, fewer steps).
 """
 from __future__ import annotations
 
@@ -84,6 +85,29 @@ def time_gemm(torch, torch_ops, w, steps, warmup, config=None):
     region = starts[0].elapsed_time(ends[-1])
     del A, B, C, ws
     return region / steps, sum(per) / len(per), wall_ms / steps
+
+
+def time_conv(torch, torch_ops, w, steps, warmup, config=None):
+    """tbg_conv2d_fwd on a convolution workload; returns (ms per call over the timed region,
+    mean per-launch ms from events)."""
+    import workloads
+    x, f = workloads.conv_inputs(w)
+    x, f = x.cuda(), f.cuda()
+    y = torch.empty((w.M, w.k), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        torch_ops.conv2d(x, f, w.pad, w.stride, w.dil, w.out_dtype, out=y, config=config)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record()
+        torch_ops.conv2d(x, f, w.pad, w.stride, w.dil, w.out_dtype, out=y, config=config)
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    region = starts[0].elapsed_time(ends[-1])
+    del x, f, y
+    return region / steps, sum(per) / len(per)
 
 
 def cpu_baseline(w, target_s: float = 15.0):
@@ -218,6 +242,17 @@ def sweep(torch, torch_ops, names, steps, warmup):
     import workloads
     results = []
     for name in names:
+        if name in workloads.CONVS:
+            w = workloads.CONVS[name]
+            for tile in ("256x256", "256x128", "128x128", "64x64"):
+                ms, _ = time_conv(torch, torch_ops, w, steps, warmup, config=tbg.gemm_config(tile, 2, "ring"))
+                tf = w.flops / (ms * 1e-3) / 1e12
+                r = {"workload": name, "pipeline": "ring", "tile": tile, "stages": 2, "ms": round(ms, 5),
+                     "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+                print(json.dumps(r), flush=True)
+                results.append(r)
+            torch.cuda.empty_cache()
+            continue
         w = workloads.GEMMS[name]
         for pipe, tile, st in SWEEP_CONFIGS:
             cfg = tbg.gemm_config(tile, st, pipe)
@@ -242,7 +277,7 @@ def main():
                     help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
     ap.add_argument("--sweep", default="",
-                    help="comma-separated workloads (c1..c5): time every built pipeline/tile/stages configuration "
+                    help="comma-separated workloads (c1..c5, conv_b): time every built pipeline/tile/stages configuration "
                          "on each and print one JSON line per measurement instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -279,6 +314,12 @@ def main():
         per_config["c4"] = {"M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "out": w.out_dtype,
                             "ms": round(ms_step, 5), "tflops": round(tflops, 2),
                             "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
+        cw = workloads.CONVS["conv_b"]
+        s_, _ = time_conv(torch, torch_ops, cw, 50, 20)
+        tf = cw.flops / (s_ * 1e-3) / 1e12
+        per_config["conv_b"] = {"conv": f"N={cw.n} H=W={cw.h} C={cw.c} K={cw.k} {cw.r}x{cw.s} pad 1 (implicit GEMM "
+                                        f"{cw.M}x{cw.k}x{cw.r * cw.s * cw.c})", "out": cw.out_dtype, "ms": round(s_, 5),
+                                "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
