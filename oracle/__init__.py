@@ -69,11 +69,13 @@ class Oracle:
         lib.oracle_gemm_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _u16p,
                                          ctypes.c_int64, _u16p, ctypes.c_int64, ctypes.c_int,
                                          ctypes.c_int64, ctypes.c_int64, _f64p, _f32p,
-                                         ctypes.c_int64, ctypes.c_int, _f64p]
+                                         ctypes.c_int64, ctypes.c_int, _f64p, ctypes.c_int]
         lib.oracle_gemm_points.restype = None
         lib.oracle_gemm_points.argtypes = [ctypes.c_int64, _u16p, ctypes.c_int64, _u16p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_int64, _i64p,
-                                           _i64p, _f64p, _f32p]
+                                           _i64p, _f64p, _f32p, ctypes.c_int]
+        lib.oracle_f16_to_f64_array.restype = None
+        lib.oracle_f16_to_f64_array.argtypes = [_u16p, _f64p, ctypes.c_int64]
         lib.oracle_f32_to_bf16_array.restype = None
         lib.oracle_f32_to_bf16_array.argtypes = [_f32p, _u16p, ctypes.c_int64]
         lib.oracle_conv_out_dim.restype = ctypes.c_int64
@@ -156,9 +158,10 @@ class Oracle:
     # -- O3 ---------------------------------------------------------------------------------
     def gemm(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, lda: int, ldb: int,
              b_layout: str = "kn", rows: Optional[tuple] = None, want64: bool = False,
-             threads: int = 0):
-        """C rows [m0, m1) of A·B.  A, B: uint16 bf16 bit arrays (flat or 2-D, row-major with the
-        given leading dimensions).  Returns float32 (m1-m0, N), plus the float64 sums if asked."""
+             threads: int = 0, ab: str = "bf16"):
+        """C rows [m0, m1) of A·B.  A, B: uint16 bit arrays of bf16 (ab="bf16") or binary16
+        (ab="f16") values (flat or 2-D, row-major with the given leading dimensions).  Returns
+        float32 (m1-m0, N), plus the float64 sums if asked."""
         A = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1)
         B = np.ascontiguousarray(B, dtype=np.uint16).reshape(-1)
         m0, m1 = rows if rows is not None else (0, M)
@@ -171,18 +174,19 @@ class Oracle:
             self.lib.oracle_gemm_rows(M, N, K, A.ctypes.data_as(_u16p), lda, B.ctypes.data_as(_u16p), ldb,
                                       bl, m0, m1,
                                       out64.ctypes.data_as(_f64p) if want64 else None,
-                                      out32.ctypes.data_as(_f32p), N, nthr, scratch.ctypes.data_as(_f64p))
+                                      out32.ctypes.data_as(_f32p), N, nthr, scratch.ctypes.data_as(_f64p),
+                                      {"bf16": 0, "f16": 1}[ab])
         return (out32, out64) if want64 else out32
 
     def gemm_ex(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, lda: int, ldb: int,
                 b_layout: str, alpha: float, beta: float, C_old: Optional[np.ndarray] = None,
-                rows: Optional[tuple] = None, threads: int = 0) -> np.ndarray:
+                rows: Optional[tuple] = None, threads: int = 0, ab: str = "bf16") -> np.ndarray:
         """C <- alpha·A·B + beta·C, the general BLAS form the "GEMM" page's tensor-core section
         gives for the matrix units.  alpha and beta are binary32 values; the sum S is gemm()'s
         binary64 sum; alpha·S + beta·C_old is formed in binary64 and rounded once to binary32.
         With beta == 0, C_old is not read (a NaN in it does not reach the result).  C_old: the
         old C rows as float32 (bf16 values widen exactly)."""
-        _, s64 = self.gemm(A, B, M, N, K, lda, ldb, b_layout, rows=rows, want64=True, threads=threads)
+        _, s64 = self.gemm(A, B, M, N, K, lda, ldb, b_layout, rows=rows, want64=True, threads=threads, ab=ab)
         a = float(np.float32(alpha))
         b = float(np.float32(beta))
         r = a * s64
@@ -191,7 +195,7 @@ class Oracle:
         return r.astype(np.float32)
 
     def gemm_points(self, A: np.ndarray, B: np.ndarray, K: int, lda: int, ldb: int, ms, ns,
-                    b_layout: str = "kn", want64: bool = False):
+                    b_layout: str = "kn", want64: bool = False, ab: str = "bf16"):
         A = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1)
         B = np.ascontiguousarray(B, dtype=np.uint16).reshape(-1)
         ms = np.ascontiguousarray(ms, dtype=np.int64)
@@ -201,7 +205,7 @@ class Oracle:
         self.lib.oracle_gemm_points(K, A.ctypes.data_as(_u16p), lda, B.ctypes.data_as(_u16p), ldb,
                                     {"kn": 0, "nk": 1}[b_layout], ms.size, ms.ctypes.data_as(_i64p),
                                     ns.ctypes.data_as(_i64p), out64.ctypes.data_as(_f64p),
-                                    out32.ctypes.data_as(_f32p))
+                                    out32.ctypes.data_as(_f32p), {"bf16": 0, "f16": 1}[ab])
         return (out32, out64) if want64 else out32
 
     # -- O2i / O5 ----------------------------------------------------------------------------
@@ -255,6 +259,14 @@ class Oracle:
                                         out64.ctypes.data_as(_f64p) if want64 else None,
                                         out32.ctypes.data_as(_f32p), k, nthr)
         return (out32, out64) if want64 else out32
+
+    def f16_to_f64(self, bits: np.ndarray) -> np.ndarray:
+        """binary16 bit patterns -> float64, decoded from the format's definition."""
+        b = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(b.shape, dtype=np.float64)
+        self.lib.oracle_f16_to_f64_array(b.reshape(-1).ctypes.data_as(_u16p), out.reshape(-1).ctypes.data_as(_f64p),
+                                         b.size)
+        return out
 
     def f32_to_bf16(self, x: np.ndarray) -> np.ndarray:
         x = np.ascontiguousarray(x, dtype=np.float32)

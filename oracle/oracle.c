@@ -35,6 +35,25 @@ static double bf16_to_f64(uint16_t h) {
     return (double)f;
 }
 
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.  Exponent field 0:
+ * subnormal, (-1)^s * f * 2^-24; 1..30: (-1)^s * (1024 + f) * 2^(e-25); 31: infinity (f = 0) or
+ * NaN.  Every binary16 value is exact in binary64. */
+static double f16_to_f64(uint16_t h) {
+    const int s = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - 25);
+    return s ? -v : v;
+}
+
+/* A 16-bit input element of the GEMM: kind 0 bfloat16, 1 binary16. */
+static double in_to_f64(uint16_t h, int kind) { return kind == 1 ? f16_to_f64(h) : bf16_to_f64(h); }
+
+void oracle_f16_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_to_f64(in[i]);
+}
+
 /* binary32 -> bfloat16, round to nearest, ties to even.  A NaN stays a NaN (quiet bit set,
  * sign and upper payload kept); everything else follows the rounding definition on the bit
  * pattern: add half an ulp of the kept part, plus one if the kept part is odd, and truncate. */
@@ -204,8 +223,8 @@ uint64_t oracle_tiled_store(int elsize, int rank, void* dst, const uint64_t* dim
 
 /* ------------------------------------------------------------------------------------------
  * O3 — GEMM.  [GEMM] "Il conto": C = A·B, A (M,K), B (K,N), C (M,N), C_ij = Σ_k A_ik B_kj.
- * [GEMM] tensor-core section: 16-bit inputs, the sum kept in a wide format.  Here every
- * bf16·bf16 product is exact in binary64, the sum runs over k in ascending order in binary64,
+ * [GEMM] tensor-core section: 16-bit inputs (bfloat16 or float16, ab_kind 0 or 1), the sum kept in
+ * a wide format.  Here every 16-bit·16-bit product is exact in binary64, the sum runs over k in ascending order in binary64,
  * and the result is rounded once to binary32 (round to nearest even, the C cast).
  *   A: bf16 bits, row-major M×K, leading dimension lda (elements).
  *   B: bf16 bits; b_layout 0: row-major K×N (ldb >= N); 1: N×K with K contiguous (ldb >= K).
@@ -215,7 +234,7 @@ uint64_t oracle_tiled_store(int elsize, int rank, void* dst, const uint64_t* dim
  * ---------------------------------------------------------------------------------------- */
 void oracle_gemm_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                       const uint16_t* B, int64_t ldb, int b_layout, int64_t m0, int64_t m1,
-                      double* out64, float* out32, int64_t ldo, int threads, double* scratch) {
+                      double* out64, float* out32, int64_t ldo, int threads, double* scratch, int ab_kind) {
     (void)M;
 #ifdef _OPENMP
     if (threads > 0) omp_set_num_threads(threads);
@@ -236,9 +255,9 @@ void oracle_gemm_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_
             for (int64_t m = m0; m < m1; ++m) {
                 for (int64_t n = 0; n < N; ++n) acc[n] = 0.0;
                 for (int64_t k = 0; k < K; ++k) {
-                    double a = bf16_to_f64(A[m * lda + k]);
+                    double a = in_to_f64(A[m * lda + k], ab_kind);
                     const uint16_t* brow = B + k * ldb;
-                    for (int64_t n = 0; n < N; ++n) acc[n] += a * bf16_to_f64(brow[n]);
+                    for (int64_t n = 0; n < N; ++n) acc[n] += a * in_to_f64(brow[n], ab_kind);
                 }
                 for (int64_t n = 0; n < N; ++n) {
                     if (out64) out64[(m - m0) * ldo + n] = acc[n];
@@ -252,7 +271,7 @@ void oracle_gemm_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_
             for (int64_t n = 0; n < N; ++n) {
                 double acc = 0.0;
                 for (int64_t k = 0; k < K; ++k)
-                    acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(B[n * ldb + k]);
+                    acc += in_to_f64(A[m * lda + k], ab_kind) * in_to_f64(B[n * ldb + k], ab_kind);
                 if (out64) out64[(m - m0) * ldo + n] = acc;
                 if (out32) out32[(m - m0) * ldo + n] = (float)acc;
             }
@@ -263,14 +282,14 @@ void oracle_gemm_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_
 /* The same sum at individual (m, n) points, for sampled checks of large products. */
 void oracle_gemm_points(int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                         int b_layout, int64_t npts, const int64_t* ms, const int64_t* ns,
-                        double* out64, float* out32) {
+                        double* out64, float* out32, int ab_kind) {
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < npts; ++p) {
         int64_t m = ms[p], n = ns[p];
         double acc = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[n * ldb + k];
-            acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(b);
+            acc += in_to_f64(A[m * lda + k], ab_kind) * in_to_f64(b, ab_kind);
         }
         if (out64) out64[p] = acc;
         if (out32) out32[p] = (float)acc;

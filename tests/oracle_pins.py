@@ -474,6 +474,42 @@ def pin_gemm_ex(o):
     assert np.array_equal(got.astype(np.int64), want)
 
 
+def pin_f16_decode(o):
+    """binary16 decoding against numpy's float16 for all 65536 bit patterns (NaN where numpy
+    has NaN; infinities, subnormals and signed zeros exact)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = o.f16_to_f64(bits)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_gemm_f16(o):
+    """fp16 inputs: small integers (products and sums exact) against numpy's integer matmul, both
+    layouts; values with fractions and the extreme exponents of binary16 (2^-24 subnormals, 2^15)
+    against exact rationals."""
+    rng = np.random.default_rng(61)
+    M, N, K = 33, 29, 71
+    Ai = rng.integers(-16, 17, (M, K))
+    Bi = rng.integers(-16, 17, (K, N))
+    Ab = Ai.astype(np.float16).view(np.uint16)
+    Bb = Bi.astype(np.float16).view(np.uint16)
+    want = (Ai @ Bi).astype(np.float64)
+    assert np.array_equal(o.gemm(Ab, Bb, M, N, K, K, N, "kn", ab="f16"), want.astype(np.float32))
+    BbT = np.ascontiguousarray(Bi.T).astype(np.float16).view(np.uint16)
+    assert np.array_equal(o.gemm(Ab, BbT, M, N, K, K, K, "nk", ab="f16"), want.astype(np.float32))
+    vals = np.array([2.0 ** -24, 3 * 2.0 ** -24, 2.0 ** -14, 1.0 / 3, 0.1, 65504.0, -2.0 ** 15, 1.5], dtype=np.float16)
+    a = rng.choice(vals, (5, 8))
+    b = rng.choice(vals, (8, 4))
+    got = o.gemm(a.view(np.uint16), b.view(np.uint16), 5, 4, 8, 8, 4, "kn", want64=True, ab="f16")[1]
+    for i in range(5):
+        for j in range(4):
+            ex = sum(Fraction(float(a[i, k])) * Fraction(float(b[k, j])) for k in range(8))
+            assert Fraction(got[i, j]) == ex or abs(Fraction(got[i, j]) - ex) <= abs(ex) * Fraction(1, 2 ** 52)
+
+
 # ---------------------------------------------------------------------------------------------
 # im2col copy and 2-D convolution ("2 · Le Tensor Memory Accelerator", section "im2col": the
 # convolution becomes a GEMM over an im2col matrix formed during the copy)
@@ -639,4 +675,5 @@ ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_struct
             pin_worked_descriptor, pin_copy_decode, pin_fill_and_source, pin_store_decode, pin_store_hand_example,
             pin_store_swizzle_and_roundtrip, pin_gemm_exact_rationals, pin_gemm_closed_forms,
             pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16, pin_conv_out_dim, pin_im2col_hand_example,
-            pin_im2col_decode, pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_equals_im2col_gemm]
+            pin_im2col_decode, pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_equals_im2col_gemm,
+            pin_f16_decode, pin_gemm_f16]

@@ -363,3 +363,20 @@ def test_conv2d_config_checks():
     if not torch.cuda.is_available():
         for t in ("256x256", "256x128", "128x128", "64x64", None):
             assert tbg.conv2d_fwd_status(good, **args, config=tbg.gemm_config(t, 2, "ring")) == tbg.ERR_NO_DEVICE
+
+
+def test_gemm_typed_checks():
+    import torch
+    g = dict(M=64, N=64, K=64, alpha=1.0, A=BASE, lda=64, B=BASE, ldb=64, b_layout="kn", beta=0.0, C=BASE, ldc=64,
+             c_dtype="f32")
+    assert tbg.gemm_typed_status(**g, ab_dtype="f32") == tbg.ERR_INVALID_VALUE
+    assert tbg.gemm_typed_status(**g, ab_dtype="u16") == tbg.ERR_INVALID_VALUE
+    # fp16 exists for the automatic choice's configurations only
+    assert tbg.gemm_typed_status(**g, ab_dtype="f16", config=tbg.gemm_config("128x128", 4, "ring")) == tbg.ERR_UNSUPPORTED
+    assert tbg.gemm_typed_status(**g, ab_dtype="f16", config=tbg.gemm_config("64x64", 2, "producer")) == tbg.ERR_UNSUPPORTED
+    assert "fp16" in tbg.last_error()
+    if not torch.cuda.is_available():
+        for ab in ("bf16", "f16"):
+            assert tbg.gemm_typed_status(**g, ab_dtype=ab) == tbg.ERR_NO_DEVICE
+        assert tbg.gemm_typed_status(**g, ab_dtype="f16", config=tbg.gemm_config("64x64", 3, "producer")) == \
+            tbg.ERR_NO_DEVICE

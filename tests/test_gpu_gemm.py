@@ -327,3 +327,55 @@ def test_gemm_alpha_beta(ops, orc, pipeline, tile):
     Cbuf = _run_ex(ops, Ai, Bi, M, N, K, "nk", "f32", 2.0, -3.0, Ci, config=cfg)
     ref = orc.gemm_ex(workloads.bits(Ai), workloads.bits(Bi), M, N, K, K, K, "nk", 2.0, -3.0, Ci.numpy())
     assert np.array_equal(_to_f32(Cbuf), ref)
+
+
+F16_CONFIGS = [("ring", "256x256", 2), ("ring", "256x128", 2), ("ring", "128x256", 2), ("ring", "128x128", 2),
+               ("ring", "64x64", 2), ("producer", "256x128", 2), ("producer", "128x256", 2), ("producer", "128x128", 3),
+               ("producer", "64x64", 3)]
+
+
+def _f16_matrix(rows, cols, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn((rows, cols), generator=g) * scale).to(torch.float16)
+
+
+@gpu
+@pytest.mark.parametrize("pipeline,tile,stages", [(None, None, 0)] + F16_CONFIGS)
+def test_fp16_inputs(ops, orc, pipeline, tile, stages):
+    """fp16 A and B (tbg_gemm_typed) against the oracle's binary16 decoding: ragged shapes, both B
+    layouts, both output types, the automatic choice and every fp16 configuration, bit-identical
+    across configurations; small integers bit for bit."""
+    import tiled_bf16_gemm_amd as tbg
+    cfg = None if pipeline is None else tbg.gemm_config(tile, stages, pipeline)
+    cases = [(700, 520, 1000, "kn", "f32"), (333, 190, 200, "nk", "bf16"), (130, 70, 1, "kn", "bf16"),
+             (257, 300, 64, "nk", "f32")]
+    for i, (M, N, K, bl, out) in enumerate(cases):
+        A = _f16_matrix(M, K, 1100 + i)
+        B = _f16_matrix(K, N, 1200 + i) if bl == "kn" else _f16_matrix(N, K, 1200 + i)
+        _say(f"fp16 {pipeline} {tile}/{stages}: gemm M={M} N={N} K={K} {bl} {out}")
+        tdt = torch.float32 if out == "f32" else torch.bfloat16
+        Cbuf = torch.full((M, N + 3), float("nan"), dtype=tdt, device="cuda")
+        ops.gemm(A.cuda(), B.cuda(), bl, out, out=Cbuf[:, :N], config=cfg)
+        torch.cuda.synchronize()
+        got = _to_f32(Cbuf)
+        ref = orc.gemm(A.view(torch.int16).numpy().view(np.uint16), B.view(torch.int16).numpy().view(np.uint16),
+                       M, N, K, K, B.shape[1], bl, ab="f16")
+        _check(got[:, :N], ref, f"fp16 case {i}")
+        assert np.all(np.isnan(got[:, N:])), "columns past N were written"
+        if cfg is not None:
+            Cd = torch.empty((M, N), dtype=tdt, device="cuda")
+            ops.gemm(A.cuda(), B.cuda(), bl, out, out=Cd)
+            torch.cuda.synchronize()
+            assert np.array_equal(got[:, :N], _to_f32(Cd)), "differs from the automatic configuration"
+    M, N, K = 300, 257, 392
+    rng = np.random.default_rng(88)
+    for bl in ("kn", "nk"):
+        Ai = torch.from_numpy(rng.integers(-16, 17, (M, K)).astype(np.float32)).to(torch.float16)
+        shape_b = (K, N) if bl == "kn" else (N, K)
+        Bi = torch.from_numpy(rng.integers(-16, 17, shape_b).astype(np.float32)).to(torch.float16)
+        _say(f"fp16 {pipeline} {tile}/{stages}: integer gemm {bl}")
+        C = ops.gemm(Ai.cuda(), Bi.cuda(), bl, "f32", config=cfg)
+        torch.cuda.synchronize()
+        ref = orc.gemm(Ai.view(torch.int16).numpy().view(np.uint16), Bi.view(torch.int16).numpy().view(np.uint16),
+                       M, N, K, K, shape_b[1], bl, ab="f16")
+        assert np.array_equal(_to_f32(C), ref)

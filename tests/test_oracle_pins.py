@@ -36,9 +36,9 @@ MUTANTS = [
     ("swizzle skipped on the image", "uint64_t off = oracle_swizzle(lin * (uint64_t)elsize, swizzle);",
      "uint64_t off = lin * (uint64_t)elsize;"),
     ("KN product reads B with lda", "const uint16_t* brow = B + k * ldb;", "const uint16_t* brow = B + k * lda;"),
-    ("wrong sign in accumulation", "acc[n] += a * bf16_to_f64(brow[n]);", "acc[n] -= a * bf16_to_f64(brow[n]);"),
-    ("NK operand transposed", "acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(B[n * ldb + k]);",
-     "acc += bf16_to_f64(A[m * lda + k]) * bf16_to_f64(B[k * ldb + n]);"),
+    ("wrong sign in accumulation", "acc[n] += a * in_to_f64(brow[n], ab_kind);", "acc[n] -= a * in_to_f64(brow[n], ab_kind);"),
+    ("NK operand transposed", "acc += in_to_f64(A[m * lda + k], ab_kind) * in_to_f64(B[n * ldb + k], ab_kind);",
+     "acc += in_to_f64(A[m * lda + k], ab_kind) * in_to_f64(B[k * ldb + n], ab_kind);"),
     ("first term dropped", "for (int64_t k = 0; k < K; ++k) {\n                    double a", "for (int64_t k = 1; k < K; ++k) {\n                    double a"),
     ("ties rounded up", "u += 0x7FFFu + lsb;", "u += 0x8000u;"),
     ("points use the wrong layout", "uint16_t b = b_layout == 0 ? B[k * ldb + n] : B[n * ldb + k];",
@@ -61,6 +61,10 @@ MUTANTS = [
     ("convolution flips the filter", "const uint16_t* wp = Wt + ((k * R + r) * S + s) * C;",
      "const uint16_t* wp = Wt + ((k * R + (R - 1 - r)) * S + (S - 1 - s)) * C;"),
     ("convolution ignores the stride", "const int64_t ih = oh * sh - ph + r * dh;", "const int64_t ih = oh - ph + r * dh;"),
+    ("f16 exponent bias off by one", "else v = ldexp((double)(1024 + f), e - 25);",
+     "else v = ldexp((double)(1024 + f), e - 24);"),
+    ("f16 subnormals scaled like normals", "if (e == 0) v = ldexp((double)f, -24);", "if (e == 0) v = ldexp((double)f, -25);"),
+    ("f16 inputs decoded as bf16", "return kind == 1 ? f16_to_f64(h) : bf16_to_f64(h);", "return bf16_to_f64(h);"),
     ("convolution drops the last channel", "for (int64_t c = 0; c < C; ++c) acc +=", "for (int64_t c = 0; c + 1 < C; ++c) acc +="),
 ]
 
