@@ -225,6 +225,21 @@ tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, con
                                tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* C <- alpha·A·B + beta·C with the input element type given: ab_dtype = TBG_BF16 or TBG_F16 (A and
+ * B both of that type; [GEMM] "Alcune regole pratiche": the matrix units reach their peak with
+ * 16-bit formats, bfloat16 or float16).  Products of two fp16 values are exact in fp32 like those
+ * of bf16 values; accumulation is fp32, output fp32 or bf16.  cfg may be NULL (the library's
+ * choice) or a configuration as for tbg_gemm_configured; fp16 inputs are built for the
+ * configurations the automatic choice uses (ring 256x256, 256x128, 128x256, 128x128, 64x64 with
+ * 2 stages; producer 256x128 and 128x256 with 2 stages, 128x128 and 64x64 with 3), other
+ * configurations are UNSUPPORTED.  Other arguments, layouts and checks as tbg_gemm_ex; an
+ * ab_dtype other than BF16/F16 is INVALID_VALUE.  tbg_gemm_configured is this call with
+ * ab_dtype = TBG_BF16. */
+tbg_status tbg_gemm_typed(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, tbg_b_layout bl, tbg_dtype ab_dtype, float beta, void* C, int64_t ldc,
+                          tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Encode an im2col descriptor ([TMA] section "im2col": a copy mode dedicated to convolution that
  * performs the im2col transform during the copy, so that a convolution becomes a GEMM whose
  * im2col matrix is never stored).  The page gives no more than that; this library's reading:

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libtbg.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tbg.h")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_bf16_gemm_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python tiled_bf16_gemm_amd/build.py` "
                       "(or __graft_entry__.build()); there is no non-GPU fallback")
 
 # The library must bind to the same HIP runtime as the framework that owns the device memory and
@@ -135,6 +135,10 @@ _lib.tbg_conv2d_workspace_bytes.argtypes = [ctypes.POINTER(Conv2dShape)]
 _lib.tbg_conv2d_fwd.restype = ctypes.c_int
 _lib.tbg_conv2d_fwd.argtypes = [ctypes.POINTER(Conv2dShape), ctypes.c_float, _vp, _vp, ctypes.c_float, _vp, _i64,
                                 ctypes.c_int, ctypes.POINTER(GemmConfig), _vp, ctypes.c_size_t, _vp]
+_lib.tbg_gemm_typed.restype = ctypes.c_int
+_lib.tbg_gemm_typed.argtypes = [_i64, _i64, _i64, ctypes.c_float, _vp, _i64, _vp, _i64, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_float, _vp, _i64, ctypes.c_int, ctypes.POINTER(GemmConfig), _vp,
+                                ctypes.c_size_t, _vp]
 _lib.tbg_status_string.restype = ctypes.c_char_p
 _lib.tbg_status_string.argtypes = [ctypes.c_int]
 _lib.tbg_last_error.restype = ctypes.c_char_p
@@ -301,6 +305,24 @@ def gemm_configured(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: i
     _check(_lib.tbg_gemm_configured(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb,
                                     _enum(B_LAYOUTS, b_layout), float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype),
                                     cfg, _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_typed(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, ab_dtype,
+               beta: float, C: int, ldc: int, c_dtype, config: Optional[GemmConfig] = None, workspace: int = 0,
+               workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
+    """tbg_gemm_typed: C = alpha·A·B + beta·C with A, B of type ab_dtype ("bf16" or "f16")."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(_lib.tbg_gemm_typed(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout),
+                               _enum(DTYPES, ab_dtype), float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype), cfg,
+                               _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_typed_status(*args, **kwargs) -> int:
+    try:
+        gemm_typed(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
 
 
 def gemm_configured_status(*args, **kwargs) -> int:

@@ -1,6 +1,6 @@
 """Build ``libtbg.so`` (the C-ABI library) from ``csrc/*.hip`` with hipcc, for gfx950 only.
 
-Run ``python -m tiled_bf16_gemm_amd.build`` (or ``__graft_entry__.build()``).  The library is
+Run ``python tiled_bf16_gemm_amd/build.py`` (or ``__graft_entry__.build()``).  The library is
 built in-tree next to this file.  ``TBG_SAVE_ISA=<dir>`` also writes the device assembly there.
 """
 from __future__ import annotations

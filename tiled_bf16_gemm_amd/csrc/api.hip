@@ -438,7 +438,11 @@ namespace {
 // as 0 and A, B and their leading dimensions are not looked at.
 tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                      int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
-                     const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes, void* stream, bool scaled) {
+                     const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes, void* stream, bool scaled,
+                     tbg_dtype ab_dtype = TBG_BF16) {
+  if (ab_dtype != TBG_BF16 && ab_dtype != TBG_F16)
+    return fail(TBG_ERR_INVALID_VALUE, "A and B must be TBG_BF16 or TBG_F16 (got %d)", (int)ab_dtype);
+  const int in = ab_dtype == TBG_F16 ? 1 : 0;
   if (M < 0 || N < 0 || K < 0) return fail(TBG_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                                           (long long)M, (long long)N, (long long)K);
   if ((int)bl != TBG_B_KN && (int)bl != TBG_B_NK) return fail(TBG_ERR_INVALID_VALUE, "unknown b_layout %d", (int)bl);
@@ -458,10 +462,12 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
     stages = cfg->stages;
     tbg::GemmChoice probe;
     // Whether anything built matches what is fixed does not depend on the shape or the device.
-    if (!tbg::choose_gemm(256, 256, 256, pipeline, bm, bn, stages, probe))
-      return fail(TBG_ERR_UNSUPPORTED, "no %skernel with tile %dx%d and %d stages (built: ring %s; producer %s)",
-                  pipeline == tbg::kPipeProducer ? "producer/consumer " : pipeline == tbg::kPipeRing ? "ring " : "",
-                  bm, bn, stages, tbg::gemm_configs_text(tbg::kPipeRing), tbg::gemm_configs_text(tbg::kPipeProducer));
+    if (!tbg::choose_gemm(256, 256, 256, pipeline, bm, bn, stages, probe, in))
+      return fail(TBG_ERR_UNSUPPORTED, "no %s%s kernel with tile %dx%d and %d stages (built: ring %s; producer %s)",
+                  in ? "fp16 " : "bf16 ",
+                  pipeline == tbg::kPipeProducer ? "producer/consumer" : pipeline == tbg::kPipeRing ? "ring" : "",
+                  bm, bn, stages, tbg::gemm_configs_text(tbg::kPipeRing, in),
+                  tbg::gemm_configs_text(tbg::kPipeProducer, in));
   }
   if (scaled && alpha == 0.f) {  // the empty product: nothing of A or B is used
     K = 0;
@@ -527,7 +533,7 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.kchunks = (int)(pl.kext / 8);
   // Kernel configuration: what the caller fixed, the rest chosen from the shape and the device.
   tbg::GemmChoice ch;
-  if (!tbg::choose_gemm(M, N, num_cus, pipeline, bm, bn, stages, ch))
+  if (!tbg::choose_gemm(M, N, num_cus, pipeline, bm, bn, stages, ch, in))
     return fail(TBG_ERR_UNSUPPORTED, "no built kernel matches tile %dx%d with %d stages", bm, bn, stages);
   p.tiles_m = 0;
   p.tiles_n = 0;
@@ -537,7 +543,7 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
-  e = tbg::launch_gemm(p, ch.pipeline, ch.bm, ch.bn, ch.stages, (int)bl, c_dtype == TBG_BF16, s);
+  e = tbg::launch_gemm(p, ch.pipeline, ch.bm, ch.bn, ch.stages, (int)bl, c_dtype == TBG_BF16, s, in);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
 }
@@ -559,6 +565,15 @@ tbg_status tbg_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const void*
   const bool scaled = !(alpha == 1.f && beta == 0.f);
   return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, nullptr, workspace, workspace_bytes,
                    stream, scaled);
+}
+
+tbg_status tbg_gemm_typed(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, tbg_b_layout bl, tbg_dtype ab_dtype, float beta, void* C, int64_t ldc,
+                          tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const bool scaled = !(alpha == 1.f && beta == 0.f);
+  return gemm_impl(M, N, K, alpha, A, lda, B, ldb, bl, beta, C, ldc, c_dtype, cfg, workspace, workspace_bytes, stream,
+                   scaled, ab_dtype);
 }
 
 tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,

@@ -32,15 +32,18 @@ namespace tbg {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64, kThreads = 256;
 
-// Shape of one workgroup tile and everything derived from it.
-template <int BM_, int BN_>
+// Shape of one workgroup tile and everything derived from it.  IN_ is the input element type of
+// the products: 0 bf16, 1 fp16 (both 16 bits: only the matrix instruction differs).
+template <int BM_, int BN_, int IN_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int In = IN_;
   static constexpr int TM = BM / 2, TN = BN / 2;    // block of C per wave (2×2 waves)
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16×16 fragments per wave
   static constexpr int ABytes = BM * kBK * 2, BBytes = BN * kBK * 2;
@@ -83,8 +86,21 @@ __device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tile
 // so no dependency wait is needed between them.  The last product of a loop iteration (DRAIN)
 // is followed by 24 wait states, more than a matrix result needs before another instruction may
 // read it, so whatever follows the loop can read the accumulators.
-template <bool ASM, bool DRAIN = false>
+template <bool ASM, bool DRAIN = false, int IN = 0>
 __device__ __forceinline__ void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if (IN == 1) {
+    // fp16 operands travel in the same registers as bf16 ones: only the instruction differs.
+    if (!ASM)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc,
+                                                   0, 0, 0);
+    else if (DRAIN)
+      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(acc)
+                   : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    return;
+  }
   if (!ASM)
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
   else if (DRAIN)
@@ -177,8 +193,8 @@ __device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<
       for (int j = (i * A + P - 1) / P; j < ((i + 1) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
     }
     const int fn = i / T::FM, fm = i % T::FM;
-    if (COPY && i == T::Products - 1) mfma16<T::AsmMfma, true>(acc[fn][fm], cur.b[fn], cur.a[fm]);
-    else mfma16<T::AsmMfma>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    if (COPY && i == T::Products - 1) mfma16<T::AsmMfma, true, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    else mfma16<T::AsmMfma, false, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
   }
 }
 

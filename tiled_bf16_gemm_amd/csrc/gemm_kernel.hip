@@ -51,7 +51,7 @@ hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_
 namespace {
 
 struct GemmVariant {
-  int pipeline, bm, bn, stages;
+  int pipeline, bm, bn, stages, in;
   GemmLauncher fn;
 };
 
@@ -59,47 +59,57 @@ struct GemmVariant {
 // (2 × 64 KiB of the 160 KiB of LDS).  The producer/consumer ring needs registers for its producer
 // waves next to the compute waves, which the 256×256 tile does not leave.
 const GemmVariant kVariants[] = {
-    {kPipeRing, 256, 256, 2, &launch_ring<256, 256, 2>},
-    {kPipeRing, 256, 128, 2, &launch_ring<256, 128, 2>},
-    {kPipeRing, 256, 128, 3, &launch_ring<256, 128, 3>},
-    {kPipeRing, 128, 256, 2, &launch_ring<128, 256, 2>},
-    {kPipeRing, 128, 256, 3, &launch_ring<128, 256, 3>},
-    {kPipeRing, 128, 128, 2, &launch_ring<128, 128, 2>},
-    {kPipeRing, 128, 128, 3, &launch_ring<128, 128, 3>},
-    {kPipeRing, 128, 128, 4, &launch_ring<128, 128, 4>},
-    {kPipeRing, 128, 128, 5, &launch_ring<128, 128, 5>},
-    {kPipeRing, 64, 64, 2, &launch_ring<64, 64, 2>},
-    {kPipeRing, 64, 64, 3, &launch_ring<64, 64, 3>},
-    {kPipeRing, 64, 64, 4, &launch_ring<64, 64, 4>},
-    {kPipeRing, 64, 64, 5, &launch_ring<64, 64, 5>},
-    {kPipeRing, 64, 64, 6, &launch_ring<64, 64, 6>},
-    {kPipeProducer, 256, 128, 2, &launch_pc<256, 128, 2>},
-    {kPipeProducer, 256, 128, 3, &launch_pc<256, 128, 3>},
-    {kPipeProducer, 128, 256, 2, &launch_pc<128, 256, 2>},
-    {kPipeProducer, 128, 256, 3, &launch_pc<128, 256, 3>},
-    {kPipeProducer, 128, 128, 2, &launch_pc<128, 128, 2>},
-    {kPipeProducer, 128, 128, 3, &launch_pc<128, 128, 3>},
-    {kPipeProducer, 128, 128, 4, &launch_pc<128, 128, 4>},
-    {kPipeProducer, 64, 64, 2, &launch_pc<64, 64, 2>},
-    {kPipeProducer, 64, 64, 3, &launch_pc<64, 64, 3>},
-    {kPipeProducer, 64, 64, 4, &launch_pc<64, 64, 4>},
-    {kPipeProducer, 64, 64, 5, &launch_pc<64, 64, 5>},
-    {kPipeProducer, 64, 64, 6, &launch_pc<64, 64, 6>},
+    {kPipeRing, 256, 256, 2, 0, &launch_ring<256, 256, 2, 0>},
+    {kPipeRing, 256, 128, 2, 0, &launch_ring<256, 128, 2, 0>},
+    {kPipeRing, 256, 128, 3, 0, &launch_ring<256, 128, 3, 0>},
+    {kPipeRing, 128, 256, 2, 0, &launch_ring<128, 256, 2, 0>},
+    {kPipeRing, 128, 256, 3, 0, &launch_ring<128, 256, 3, 0>},
+    {kPipeRing, 128, 128, 2, 0, &launch_ring<128, 128, 2, 0>},
+    {kPipeRing, 128, 128, 3, 0, &launch_ring<128, 128, 3, 0>},
+    {kPipeRing, 128, 128, 4, 0, &launch_ring<128, 128, 4, 0>},
+    {kPipeRing, 128, 128, 5, 0, &launch_ring<128, 128, 5, 0>},
+    {kPipeRing, 64, 64, 2, 0, &launch_ring<64, 64, 2, 0>},
+    {kPipeRing, 64, 64, 3, 0, &launch_ring<64, 64, 3, 0>},
+    {kPipeRing, 64, 64, 4, 0, &launch_ring<64, 64, 4, 0>},
+    {kPipeRing, 64, 64, 5, 0, &launch_ring<64, 64, 5, 0>},
+    {kPipeRing, 64, 64, 6, 0, &launch_ring<64, 64, 6, 0>},
+    {kPipeProducer, 256, 128, 2, 0, &launch_pc<256, 128, 2, 0>},
+    {kPipeProducer, 256, 128, 3, 0, &launch_pc<256, 128, 3, 0>},
+    {kPipeProducer, 128, 256, 2, 0, &launch_pc<128, 256, 2, 0>},
+    {kPipeProducer, 128, 256, 3, 0, &launch_pc<128, 256, 3, 0>},
+    {kPipeProducer, 128, 128, 2, 0, &launch_pc<128, 128, 2, 0>},
+    {kPipeProducer, 128, 128, 3, 0, &launch_pc<128, 128, 3, 0>},
+    {kPipeProducer, 128, 128, 4, 0, &launch_pc<128, 128, 4, 0>},
+    {kPipeProducer, 64, 64, 2, 0, &launch_pc<64, 64, 2, 0>},
+    {kPipeProducer, 64, 64, 3, 0, &launch_pc<64, 64, 3, 0>},
+    {kPipeProducer, 64, 64, 4, 0, &launch_pc<64, 64, 4, 0>},
+    {kPipeProducer, 64, 64, 5, 0, &launch_pc<64, 64, 5, 0>},
+    {kPipeProducer, 64, 64, 6, 0, &launch_pc<64, 64, 6, 0>},
+    // fp16 inputs: the configurations of the automatic choice
+    {kPipeRing, 256, 256, 2, 1, &launch_ring<256, 256, 2, 1>},
+    {kPipeRing, 256, 128, 2, 1, &launch_ring<256, 128, 2, 1>},
+    {kPipeRing, 128, 256, 2, 1, &launch_ring<128, 256, 2, 1>},
+    {kPipeRing, 128, 128, 2, 1, &launch_ring<128, 128, 2, 1>},
+    {kPipeRing, 64, 64, 2, 1, &launch_ring<64, 64, 2, 1>},
+    {kPipeProducer, 256, 128, 2, 1, &launch_pc<256, 128, 2, 1>},
+    {kPipeProducer, 128, 256, 2, 1, &launch_pc<128, 256, 2, 1>},
+    {kPipeProducer, 128, 128, 3, 1, &launch_pc<128, 128, 3, 1>},
+    {kPipeProducer, 64, 64, 3, 1, &launch_pc<64, 64, 3, 1>},
 };
 
 }  // namespace
 
-GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages) {
+GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages, int in) {
   for (const GemmVariant& v : kVariants)
-    if (v.pipeline == pipeline && v.bm == bm && v.bn == bn && v.stages == stages) return v.fn;
+    if (v.pipeline == pipeline && v.bm == bm && v.bn == bn && v.stages == stages && v.in == in) return v.fn;
   return nullptr;
 }
 
 namespace {
-std::string configs_of(int pipeline) {
+std::string configs_of(int pipeline, int in) {
   std::string t;
   for (const GemmVariant& v : kVariants) {
-    if (v.pipeline != pipeline) continue;
+    if (v.pipeline != pipeline || v.in != in) continue;
     char buf[48];
     snprintf(buf, sizeof(buf), "%s%dx%d/%d", t.empty() ? "" : ", ", v.bm, v.bn, v.stages);
     t += buf;
@@ -108,8 +118,10 @@ std::string configs_of(int pipeline) {
 }
 }  // namespace
 
-const char* gemm_configs_text(int pipeline) {
-  static const std::string ring = configs_of(kPipeRing), pc = configs_of(kPipeProducer);
+const char* gemm_configs_text(int pipeline, int in) {
+  static const std::string ring = configs_of(kPipeRing, 0), pc = configs_of(kPipeProducer, 0);
+  static const std::string ring16 = configs_of(kPipeRing, 1), pc16 = configs_of(kPipeProducer, 1);
+  if (in == 1) return pipeline == kPipeProducer ? pc16.c_str() : ring16.c_str();
   return pipeline == kPipeProducer ? pc.c_str() : ring.c_str();
 }
 
@@ -136,7 +148,8 @@ const Candidate kCandidates[] = {
 // Each candidate's cost is the number of tiles the busiest compute unit computes times the work
 // of one tile divided by the candidate's efficiency; the cheapest wins (the 256×256 ring whenever
 // it fills the machine).
-bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn, int stages, GemmChoice& out) {
+bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn, int stages, GemmChoice& out,
+                 int in) {
   const int cus = num_cus > 0 ? num_cus : 256;
   double best = 0;
   bool found = false;
@@ -144,7 +157,7 @@ bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn
     if (pipeline != 0 && c.pipeline != pipeline) continue;
     if (bm != 0 && (c.bm != bm || c.bn != bn)) continue;
     const int st = stages != 0 ? stages : c.stages;
-    if (!find_gemm(c.pipeline, c.bm, c.bn, st)) continue;
+    if (!find_gemm(c.pipeline, c.bm, c.bn, st, in)) continue;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const int64_t rounds = (tiles + cus - 1) / cus;
     const double cost = (double)(rounds > 0 ? rounds : 1) * c.bm * c.bn / c.eff;
@@ -158,8 +171,8 @@ bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn
 }
 
 hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,
-                       hipStream_t stream) {
-  const GemmLauncher fn = find_gemm(pipeline, bm, bn, stages);
+                       hipStream_t stream, int in) {
+  const GemmLauncher fn = find_gemm(pipeline, bm, bn, stages, in);
   if (!fn) return hipErrorInvalidValue;
   p.tiles_m = (int)((p.M + bm - 1) / bm);
   p.tiles_n = (int)((p.N + bn - 1) / bn);

@@ -119,11 +119,11 @@ __device__ __forceinline__ void produce(const GemmParams& p, const uint8_t* smem
   }
 }
 
-template <int BM, int BN, int S, int BL, int OUT, int SCALED>
+template <int BM, int BN, int S, int IN, int BL, int OUT, int SCALED>
 __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>::MinBlocks))
     gemm_pc_kernel(GemmParams p) {
   using C = PcCfg<BM, BN, S>;
-  using T = TileCfg<BM, BN>;
+  using T = TileCfg<BM, BN, IN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LdsBytes];
   __shared__ uint32_t full[S], empty[S];
   const int lane = threadIdx.x & 63;
@@ -186,9 +186,9 @@ __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
 }
 
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int IN>
 hipError_t launch_pc(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
-  TBG_LAUNCH_INSTANCES(gemm_pc_kernel, (PcCfg<BM, BN, S>::Threads), BM, BN, S);
+  TBG_LAUNCH_INSTANCES(gemm_pc_kernel, (PcCfg<BM, BN, S>::Threads), BM, BN, S, IN);
 }
 
 }  // namespace tbg

@@ -2,9 +2,9 @@
 #include "gemm_pc.hpp"
 
 namespace tbg {
-template hipError_t launch_pc<64, 64, 2>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<64, 64, 3>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<64, 64, 4>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<64, 64, 5>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<64, 64, 6>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<64, 64, 2, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<64, 64, 3, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<64, 64, 4, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<64, 64, 5, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<64, 64, 6, 0>(const GemmParams&, int, int, hipStream_t);
 }  // namespace tbg

@@ -2,8 +2,8 @@
 #include "gemm_pc.hpp"
 
 namespace tbg {
-template hipError_t launch_pc<256, 128, 2>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<256, 128, 3>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<128, 256, 2>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_pc<128, 256, 3>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<256, 128, 2, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<256, 128, 3, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<128, 256, 2, 0>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_pc<128, 256, 3, 0>(const GemmParams&, int, int, hipStream_t);
 }  // namespace tbg

@@ -30,9 +30,9 @@ struct RingCfg {
   static_assert(T::Atoms * (S - 2) <= 63, "tiles in flight must fit the vmcnt counter");
 };
 
-template <int BM, int BN, int S, int BL, int OUT, int SCALED>
+template <int BM, int BN, int S, int IN, int BL, int OUT, int SCALED>
 __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gemm_ring_kernel(GemmParams p) {
-  using T = TileCfg<BM, BN>;
+  using T = TileCfg<BM, BN, IN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RingCfg<BM, BN, S>::LdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -125,9 +125,9 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
 }
 
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int IN>
 hipError_t launch_ring(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream) {
-  TBG_LAUNCH_INSTANCES(gemm_ring_kernel, kThreads, BM, BN, S);
+  TBG_LAUNCH_INSTANCES(gemm_ring_kernel, kThreads, BM, BN, S, IN);
 }
 
 }  // namespace tbg

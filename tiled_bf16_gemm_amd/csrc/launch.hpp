@@ -51,15 +51,17 @@ enum GemmPipeline { kPipeRing = 1, kPipeProducer = 2 };
 
 // One built kernel configuration; tiles_m / tiles_n of `p` must be set.
 typedef hipError_t (*GemmLauncher)(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
-template <int BM, int BN, int S>
+// IN: input element type of the products, 0 bf16, 1 fp16.
+template <int BM, int BN, int S, int IN>
 hipError_t launch_ring(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int IN>
 hipError_t launch_pc(const GemmParams& p, int b_layout, int out_bf16, hipStream_t stream);
 
-// The launcher of (pipeline, tile bm × bn, stages), or nullptr when that configuration is not built.
-GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages);
+// The launcher of (pipeline, tile bm × bn, stages) for input type `in`, or nullptr when that
+// configuration is not built.
+GemmLauncher find_gemm(int pipeline, int bm, int bn, int stages, int in = 0);
 // Readable list of the built configurations of a pipeline (for error messages).
-const char* gemm_configs_text(int pipeline);
+const char* gemm_configs_text(int pipeline, int in = 0);
 
 // A kernel configuration for an M×N product on a device with num_cus compute units.  Zero
 // arguments are open: pipeline 0 = either pipeline, bm = bn = 0 = any tile, stages 0 = each
@@ -67,11 +69,12 @@ const char* gemm_configs_text(int pipeline);
 struct GemmChoice {
   int pipeline, bm, bn, stages;
 };
-bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn, int stages, GemmChoice& out);
+bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn, int stages, GemmChoice& out,
+                 int in = 0);
 // Launch a built configuration; fills tiles_m / tiles_n.  Returns hipErrorInvalidValue for a
 // configuration find_gemm does not know.
 hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,
-                       hipStream_t stream);
+                       hipStream_t stream, int in = 0);
 hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ld_dst,
                        hipStream_t stream);
 

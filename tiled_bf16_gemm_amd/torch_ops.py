@@ -29,13 +29,15 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
          stream: Optional[torch.cuda.Stream] = None, alpha: float = 1.0, beta: float = 0.0,
          config: Optional[tbg.GemmConfig] = None) -> torch.Tensor:
     """C = alpha·A·B + beta·C through tbg_gemm (alpha = 1, beta = 0), tbg_gemm_ex, or
-    tbg_gemm_configured when `config` (tbg.gemm_config(...)) is given.  A: (M, K) bf16 view; B:
+    tbg_gemm_configured when `config` (tbg.gemm_config(...)) is given; fp16 operands go through
+    tbg_gemm_typed.  A: (M, K) bf16 or fp16 view; B:
     (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading dimensions.  `out` (M, N)
     may be a strided view; with beta != 0 it must hold the old C."""
     _require(A, "A")
     _require(B, "B")
-    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
-        raise ValueError("A and B must be bfloat16")
+    if A.dtype not in (torch.bfloat16, torch.float16) or B.dtype != A.dtype:
+        raise ValueError("A and B must both be bfloat16 or both float16")
+    ab = "bf16" if A.dtype == torch.bfloat16 else "f16"
     M, K = A.shape
     if b_layout == "kn":
         Kb, N = B.shape
@@ -58,7 +60,10 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if config is not None:
+    if ab == "f16":
+        tbg.gemm_typed(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, ab, beta, out.data_ptr(), ldc,
+                       out_dtype, config, ws_ptr, ws_bytes, stream_handle(stream))
+    elif config is not None:
         tbg.gemm_configured(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, beta, out.data_ptr(), ldc,
                             out_dtype, config, ws_ptr, ws_bytes, stream_handle(stream))
     elif alpha == 1.0 and beta == 0.0:
