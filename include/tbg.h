@@ -107,6 +107,28 @@ tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank
                             const uint32_t* element_strides, tbg_swizzle swizzle, tbg_l2_hint l2,
                             tbg_oob_fill oob);
 
+/* Interleaved layouts ([MAP] §12): tensors stored NC/xHWCx, i.e. channels cut into slices of x
+ * channels that are 16 or 32 bytes wide, each slice stored contiguously per position
+ * (memory order N, C/x, H, W, x).  The copy that reads them back is a tiled copy; interleave adds
+ * the page's rules (§12.3, §12.4): rank >= 3; base and every stride a multiple of the slice
+ * width; 32-byte slices require the 32B swizzle.  Reading (the page's table of the two modes is
+ * lost in the text): dimension 0 is one channel slice, global_dim[0] * elsize equals the width,
+ * and a box takes whole slices (box_dim[0] = global_dim[0], element_strides[0] = 1); channel
+ * counts that are not a multiple of x carry the zero padding of the last slice in memory, as the
+ * page asks of the tensor's producer. */
+typedef enum { TBG_INTERLEAVE_NONE = 0, TBG_INTERLEAVE_16B = 1, TBG_INTERLEAVE_32B = 2 } tbg_interleave;
+
+/* tbg_encode_tiled with an interleave mode (TBG_INTERLEAVE_NONE is tbg_encode_tiled itself).
+ * Returns what tbg_encode_tiled returns, plus UNSUPPORTED (rank < 3), INVALID_VALUE (dimension 0
+ * not one slice, a box that splits a slice, 32B interleave without the 32B swizzle, unknown
+ * interleave) and MISALIGNED (base or strides not multiples of the slice width).  The descriptor
+ * is used with tbg_tiled_copy / tbg_tiled_store like any tiled descriptor. */
+tbg_status tbg_encode_tiled_interleaved(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank,
+                                        const void* global_address, const uint64_t* global_dim,
+                                        const uint64_t* global_strides, const uint32_t* box_dim,
+                                        const uint32_t* element_strides, tbg_interleave interleave,
+                                        tbg_swizzle swizzle, tbg_l2_hint l2, tbg_oob_fill oob);
+
 /* Bytes of one copy's image for an encoded descriptor (tiled or im2col); 0 if `d` is not a valid
  * descriptor. */
 size_t tbg_box_bytes(const tbg_tensor_desc* d);

@@ -510,6 +510,47 @@ def pin_gemm_f16(o):
             assert Fraction(got[i, j]) == ex or abs(Fraction(got[i, j]) - ex) <= abs(ex) * Fraction(1, 2 ** 52)
 
 
+def _nc_x_hwcx(nchw: np.ndarray, x: int) -> np.ndarray:
+    """NCHW -> NC/xHWCx by numpy: channels cut into slices of x (the last one zero-padded), each
+    slice stored per position: array (N, C/x, H, W, x)."""
+    N, C, H, W = nchw.shape
+    cs = -(-C // x)
+    padded = np.zeros((N, cs * x, H, W), dtype=nchw.dtype)
+    padded[:, :C] = nchw
+    return np.ascontiguousarray(padded.reshape(N, cs, x, H, W).transpose(0, 1, 3, 4, 2))
+
+
+def pin_interleaved_boxes(o):
+    """"H100 · cuTensorMap" §12: a box of an NC/xHWCx tensor (dimension 0 one channel slice, read
+    whole) is the numpy slice of the interleaved array, and a box over every slice of a spatial
+    window, reordered (h, w, slice, x), is that window of the NHWC tensor with the padded
+    channels zero."""
+    rng = np.random.default_rng(71)
+    N, C, H, W, x = 2, 21, 9, 11, 8
+    nchw = rng.integers(1, 60000, (N, C, H, W)).astype(np.uint16)
+    t = _nc_x_hwcx(nchw, x)
+    cs = t.shape[1]
+    dims = [x, W, H, cs, N]
+    strides = [2 * x, 2 * x * W, 2 * x * W * H, 2 * x * W * H * cs]
+    for coords in ([0, 0, 0, 0, 0], [0, 3, 2, 1, 1], [0, 8, 6, 2, 0], [0, -2, -1, 0, 1]):
+        box = [x, 5, 4, cs, 1]
+        img = o.tiled_copy(t, "u16", dims, strides, box, [1] * 5, "none", False, coords).view(np.uint16)
+        img = img.reshape(1, cs, 4, 5, x)
+        want = np.zeros((1, cs, 4, 5, x), dtype=np.uint16)
+        for n in range(1):
+            for c in range(cs):
+                for h in range(4):
+                    for w in range(5):
+                        hh, ww, cc, nn = coords[2] + h, coords[1] + w, coords[3] + c, coords[4] + n
+                        if 0 <= hh < H and 0 <= ww < W and 0 <= cc < cs:
+                            want[n, c, h, w] = t[nn, cc, hh, ww]
+        assert np.array_equal(img, want), coords
+        if coords[1] >= 0 and coords[2] >= 0 and coords[1] + 5 <= W and coords[2] + 4 <= H and coords[3] == 0:
+            nhwc = img[0].transpose(1, 2, 0, 3).reshape(4, 5, cs * x)
+            ref = nchw[coords[4], :, coords[2]:coords[2] + 4, coords[1]:coords[1] + 5].transpose(1, 2, 0)
+            assert np.array_equal(nhwc[:, :, :C], ref) and not nhwc[:, :, C:].any()
+
+
 # ---------------------------------------------------------------------------------------------
 # im2col copy and 2-D convolution ("2 · Le Tensor Memory Accelerator", section "im2col": the
 # convolution becomes a GEMM over an im2col matrix formed during the copy)
@@ -676,4 +717,4 @@ ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_struct
             pin_store_swizzle_and_roundtrip, pin_gemm_exact_rationals, pin_gemm_closed_forms,
             pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16, pin_conv_out_dim, pin_im2col_hand_example,
             pin_im2col_decode, pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_equals_im2col_gemm,
-            pin_f16_decode, pin_gemm_f16]
+            pin_f16_decode, pin_gemm_f16, pin_interleaved_boxes]

@@ -380,3 +380,41 @@ def test_gemm_typed_checks():
             assert tbg.gemm_typed_status(**g, ab_dtype=ab) == tbg.ERR_NO_DEVICE
         assert tbg.gemm_typed_status(**g, ab_dtype="f16", config=tbg.gemm_config("64x64", 3, "producer")) == \
             tbg.ERR_NO_DEVICE
+
+
+def test_interleaved_descriptor_rules():
+    """The interleave rules of "H100 · cuTensorMap" §12.3-§12.4 (rank >= 3, base and strides
+    aligned to the slice, 32B slices with the 32B swizzle), plus this library's reading that
+    dimension 0 is one channel slice taken whole."""
+    # NC/8HW8 bf16: a slice is 8 channels = 16 bytes; dims {8, W, H, C/8, N}
+    dims16 = [8, 20, 12, 3, 2]
+    st16 = [16, 16 * 20, 16 * 20 * 12, 16 * 20 * 12 * 3]
+    d = tbg.encode_tiled_interleaved("bf16", 5, BASE, dims16, st16, [8, 16, 4, 3, 1], [1, 1, 1, 1, 1], "16B")
+    assert tbg.box_bytes(d) == 16 * 16 * 4 * 3
+    # NC/16HW16 bf16: 32-byte slices, with the 32B swizzle
+    dims32 = [16, 20, 12, 2, 2]
+    st32 = [32, 32 * 20, 32 * 20 * 12, 32 * 20 * 12 * 2]
+    d = tbg.encode_tiled_interleaved("bf16", 5, BASE, dims32, st32, [16, 16, 4, 2, 1], [1] * 5, "32B", swizzle="32B")
+    assert tbg.box_bytes(d) == 32 * 16 * 4 * 2
+    bad = [
+        (dict(rank=2, global_dim=[8, 20], global_strides=[16], box_dim=[8, 16], element_strides=[1, 1]),
+         tbg.ERR_UNSUPPORTED),
+        (dict(global_dim=[4] + dims16[1:]), tbg.ERR_INVALID_VALUE),                       # 8-byte "slice"
+        (dict(box_dim=[4, 16, 4, 3, 1]), tbg.ERR_INVALID_VALUE),                          # box splits a slice
+        (dict(element_strides=[2, 1, 1, 1, 1]), tbg.ERR_INVALID_VALUE),
+        (dict(interleave="32B", global_dim=dims32, global_strides=st32, box_dim=[16, 16, 4, 2, 1]),
+         tbg.ERR_INVALID_VALUE),                                                          # 32B needs the 32B swizzle
+        (dict(interleave="32B", global_dim=dims32, global_strides=st32, box_dim=[16, 16, 4, 2, 1], swizzle="32B",
+              global_address=BASE + 16), tbg.ERR_MISALIGNED),
+        (dict(interleave="32B", global_dim=dims32, global_strides=[32, 32 * 20, 32 * 20 * 12 + 16, 99 * 32],
+              box_dim=[16, 16, 4, 2, 1], swizzle="32B"), tbg.ERR_MISALIGNED),
+        (dict(interleave=7), tbg.ERR_INVALID_VALUE),
+    ]
+    base = dict(dtype="bf16", rank=5, global_address=BASE, global_dim=dims16, global_strides=st16,
+                box_dim=[8, 16, 4, 3, 1], element_strides=[1] * 5, interleave="16B")
+    for over, status in bad:
+        assert tbg.encode_tiled_interleaved_status(**{**base, **over}) == status, (over, tbg.last_error())
+    # no interleave: the plain encoder's rules
+    assert tbg.encode_tiled_interleaved_status(**{**base, "interleave": "none", "rank": 2, "global_dim": [64, 8],
+                                                  "global_strides": [128], "box_dim": [64, 8],
+                                                  "element_strides": [1, 1]}) == tbg.OK

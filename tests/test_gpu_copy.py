@@ -271,3 +271,37 @@ def test_store_random_descriptors(ops, orc):
         _say(f"random store {done}: {dtype} rank={rank} dims={dims} box={box} estr={estr} {swizzle}")
         _store_case(ops, orc, dtype, dims, strides, box, estr, swizzle, coords, many, 100 + done)
         done += 1
+
+
+@gpu
+def test_interleaved_copies(ops, orc):
+    """NC/xHWCx tensors ("H100 · cuTensorMap" §12): 16-byte slices (NC/8HW8 bf16) with and without
+    a swizzle, 32-byte slices (NC/16HW16 bf16, NC/8HW8 f32) with the 32B swizzle, zero and NaN
+    fill, boxes overhanging every edge; images byte for byte against the oracle."""
+    import tiled_bf16_gemm_amd as tbg
+    rng = np.random.default_rng(505)
+    cases = [("bf16", 8, 16, "16B", "none", "zero"), ("bf16", 8, 16, "16B", "128B", "zero"),
+             ("bf16", 16, 32, "32B", "32B", "nan"), ("f32", 8, 32, "32B", "32B", "zero")]
+    for dtype, x, width, il, swz, oob in cases:
+        N, CS, H, W = 2, 3, 9, 13
+        es = width // x
+        vals = torch.randn(N * CS * H * W * x)
+        src = (vals.to(torch.bfloat16) if dtype == "bf16" else vals).contiguous()
+        dims = [x, W, H, CS, N]
+        strides = [width, width * W, width * W * H, width * W * H * CS]
+        box = [x, 8, 4, 2, 1]
+        d = src.cuda()
+        desc = tbg.encode_tiled_interleaved(dtype, 5, d.data_ptr(), dims, strides, box, [1] * 5, il, swz, "none", oob)
+        nbytes = tbg.box_bytes(desc)
+        coords = [[0, int(rng.integers(-4, W)), int(rng.integers(-2, H)), int(rng.integers(-1, CS)),
+                   int(rng.integers(0, N))] for _ in range(24)] + [[0, W - 3, H - 2, CS - 1, N - 1], [0, -7, -3, 0, 0]]
+        _say(f"interleave {il} {dtype} swizzle {swz} {oob}: {len(coords)} boxes of {nbytes} bytes")
+        out = torch.full((len(coords) * nbytes + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+        ops.tiled_copy_many(desc, torch.tensor(coords, dtype=torch.int32, device="cuda"), out=out)
+        torch.cuda.synchronize()
+        host = out.cpu().numpy()
+        assert np.all(host[len(coords) * nbytes:] == SENTINEL), "write past the last image"
+        srcb = _src_bytes(src)
+        for i, c in enumerate(coords):
+            want = orc.tiled_copy(srcb, dtype, dims, strides, box, [1] * 5, swz, oob == "nan", c)
+            assert np.array_equal(host[i * nbytes:(i + 1) * nbytes], want), (il, c)

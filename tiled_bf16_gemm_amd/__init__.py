@@ -43,6 +43,7 @@ OOB = {"zero": 0, "nan": 1}
 L2 = {"none": 0, "64B": 1, "128B": 2, "256B": 3}
 B_LAYOUTS = {"kn": 0, "nk": 1}
 PIPELINES = {"auto": 0, "ring": 1, "producer": 2}
+INTERLEAVES = {"none": 0, "16B": 1, "32B": 2}
 
 
 class TensorDesc(ctypes.Structure):
@@ -97,6 +98,10 @@ _i64 = ctypes.c_int64
 _lib.tbg_encode_tiled.restype = ctypes.c_int
 _lib.tbg_encode_tiled.argtypes = [ctypes.POINTER(TensorDesc), ctypes.c_int, ctypes.c_uint32, _vp, _u64p, _u64p,
                                   _u32p, _u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+_lib.tbg_encode_tiled_interleaved.restype = ctypes.c_int
+_lib.tbg_encode_tiled_interleaved.argtypes = [ctypes.POINTER(TensorDesc), ctypes.c_int, ctypes.c_uint32, _vp, _u64p,
+                                              _u64p, _u32p, _u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int]
 _lib.tbg_box_bytes.restype = ctypes.c_size_t
 _lib.tbg_box_bytes.argtypes = [ctypes.POINTER(TensorDesc)]
 _lib.tbg_tiled_copy.restype = ctypes.c_int
@@ -179,6 +184,28 @@ def encode_tiled(dtype, rank: int, global_address: int, global_dim: Sequence[int
                                _enum(OOB, oob))
     _check(st)
     return d
+
+
+def encode_tiled_interleaved(dtype, rank: int, global_address: int, global_dim: Sequence[int],
+                             global_strides: Sequence[int], box_dim: Sequence[int], element_strides: Sequence[int],
+                             interleave="16B", swizzle="none", l2="none", oob="zero") -> TensorDesc:
+    """tbg_encode_tiled_interleaved: an NC/xHWCx tensor, dimension 0 one 16- or 32-byte slice."""
+    d = TensorDesc()
+    st = _lib.tbg_encode_tiled_interleaved(ctypes.byref(d), _enum(DTYPES, dtype), int(rank), _vp(int(global_address)),
+                                           _arr(ctypes.c_uint64, global_dim), _arr(ctypes.c_uint64, global_strides),
+                                           _arr(ctypes.c_uint32, box_dim), _arr(ctypes.c_uint32, element_strides),
+                                           _enum(INTERLEAVES, interleave), _enum(SWIZZLES, swizzle), _enum(L2, l2),
+                                           _enum(OOB, oob))
+    _check(st)
+    return d
+
+
+def encode_tiled_interleaved_status(*args, **kwargs) -> int:
+    try:
+        encode_tiled_interleaved(*args, **kwargs)
+        return OK
+    except Error as e:
+        return e.status
 
 
 def encode_tiled_status(*args, **kwargs) -> int:

@@ -209,6 +209,44 @@ tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank
   return TBG_OK;
 }
 
+tbg_status tbg_encode_tiled_interleaved(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank,
+                                        const void* global_address, const uint64_t* global_dim,
+                                        const uint64_t* global_strides, const uint32_t* box_dim,
+                                        const uint32_t* element_strides, tbg_interleave interleave,
+                                        tbg_swizzle swizzle, tbg_l2_hint l2, tbg_oob_fill oob) {
+  if ((int)interleave < TBG_INTERLEAVE_NONE || (int)interleave > TBG_INTERLEAVE_32B)
+    return fail(TBG_ERR_INVALID_VALUE, "unknown interleave %d", (int)interleave);
+  if (interleave != TBG_INTERLEAVE_NONE) {
+    const uint64_t width = interleave == TBG_INTERLEAVE_16B ? 16 : 32;
+    const int es = elsize_of(dtype);
+    if (es == 0) return fail(TBG_ERR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
+    if (rank < 3) return fail(TBG_ERR_UNSUPPORTED, "an interleaved layout needs rank >= 3 (got %u)", rank);
+    if (rank > (uint32_t)tbg::kMaxRank) return fail(TBG_ERR_UNSUPPORTED, "rank %u not in 3..5", rank);
+    if (!global_dim || !box_dim || !element_strides || !global_strides)
+      return fail(TBG_ERR_INVALID_VALUE, "a per-dimension array is NULL");
+    if (global_dim[0] * (uint64_t)es != width)
+      return fail(TBG_ERR_INVALID_VALUE, "dimension 0 must be one %llu-byte channel slice (%llu elements of %d bytes)",
+                  (unsigned long long)width, (unsigned long long)global_dim[0], es);
+    if (box_dim[0] != global_dim[0] || element_strides[0] != 1)
+      return fail(TBG_ERR_INVALID_VALUE, "an interleaved box takes whole channel slices (box_dim[0] = dim 0, "
+                  "element_strides[0] = 1)");
+    if (((uintptr_t)global_address) % width != 0)
+      return fail(TBG_ERR_MISALIGNED, "global_address must be %llu-byte aligned for this interleave",
+                  (unsigned long long)width);
+    for (uint32_t i = 0; i + 1 < rank; ++i)
+      if (global_strides[i] % width != 0)
+        return fail(TBG_ERR_MISALIGNED, "global_strides[%u] must be a multiple of %llu bytes for this interleave", i,
+                    (unsigned long long)width);
+    if (interleave == TBG_INTERLEAVE_32B && swizzle != TBG_SWIZZLE_32B)
+      return fail(TBG_ERR_INVALID_VALUE, "32-byte interleave requires the 32B swizzle");
+  }
+  tbg_status st = tbg_encode_tiled(out, dtype, rank, global_address, global_dim, global_strides, box_dim,
+                                   element_strides, swizzle, l2, oob);
+  if (st != TBG_OK) return st;
+  reinterpret_cast<DescImpl*>(out)->interleave = (uint8_t)interleave;
+  return TBG_OK;
+}
+
 size_t tbg_box_bytes(const tbg_tensor_desc* d) {
   const DescImpl* di = nullptr;
   if (valid_desc(d, &di)) return di->image_bytes;

@@ -24,7 +24,7 @@ struct DescImpl {
   uint8_t oob;       // tbg_oob_fill
   uint8_t l2;        // tbg_l2_hint (recorded, no effect)
   uint8_t estr[5];   // element strides, 1..8 (unused dims: 1)
-  uint8_t pad0;
+  uint8_t interleave;  // tbg_interleave (recorded; the copy itself is the tiled one)
   uint64_t base;          // device address of element (0, ..., 0)
   uint64_t dim[5];        // elements per dimension, innermost first (unused dims: 1)
   uint64_t stride[5];     // byte stride per dimension; stride[0] = elsize (unused dims: 0)
