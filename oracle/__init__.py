@@ -74,6 +74,12 @@ class Oracle:
         lib.oracle_gemm_points.argtypes = [ctypes.c_int64, _u16p, ctypes.c_int64, _u16p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_int64, _i64p,
                                            _i64p, _f64p, _f32p, ctypes.c_int]
+        lib.oracle_f8_to_f64_array.restype = None
+        lib.oracle_f8_to_f64_array.argtypes = [ctypes.c_void_p, _f64p, ctypes.c_int64, ctypes.c_int]
+        lib.oracle_gemm_f8_rows.restype = None
+        lib.oracle_gemm_f8_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                            ctypes.c_int64, _f64p, _f32p, ctypes.c_int64, ctypes.c_int]
         lib.oracle_f16_to_f64_array.restype = None
         lib.oracle_f16_to_f64_array.argtypes = [_u16p, _f64p, ctypes.c_int64]
         lib.oracle_f32_to_bf16_array.restype = None
@@ -258,6 +264,30 @@ class Oracle:
                                         geom.ctypes.data_as(_i32p), m0, m1,
                                         out64.ctypes.data_as(_f64p) if want64 else None,
                                         out32.ctypes.data_as(_f32p), k, nthr)
+        return (out32, out64) if want64 else out32
+
+    def f8_to_f64(self, bits: np.ndarray, fmt: str) -> np.ndarray:
+        """OCP 8-bit float bit patterns (fmt "e4m3" or "e5m2") -> float64."""
+        b = np.ascontiguousarray(bits, dtype=np.uint8)
+        out = np.empty(b.shape, dtype=np.float64)
+        self.lib.oracle_f8_to_f64_array(b.ctypes.data, out.reshape(-1).ctypes.data_as(_f64p), b.size,
+                                        {"e4m3": 0, "e5m2": 1}[fmt])
+        return out
+
+    def gemm_f8(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, lda: int, ldb: int, fmt: str,
+                rows: Optional[tuple] = None, want64: bool = False, threads: int = 0):
+        """C rows [m0, m1) of A·Bᵀ for 8-bit float inputs: A (M×K, lda) and B stored N×K (ldb) as
+        uint8 bit arrays.  Returns float32 (m1-m0, N), plus the float64 sums if asked."""
+        A = np.ascontiguousarray(A, dtype=np.uint8).reshape(-1)
+        B = np.ascontiguousarray(B, dtype=np.uint8).reshape(-1)
+        m0, m1 = rows if rows is not None else (0, M)
+        out32 = np.empty((m1 - m0, N), dtype=np.float32)
+        out64 = np.empty((m1 - m0, N), dtype=np.float64) if want64 else None
+        nthr = threads if threads > 0 else self.lib.oracle_max_threads()
+        if m1 > m0 and N > 0:
+            self.lib.oracle_gemm_f8_rows(N, K, A.ctypes.data, lda, B.ctypes.data, ldb, {"e4m3": 0, "e5m2": 1}[fmt],
+                                         m0, m1, out64.ctypes.data_as(_f64p) if want64 else None,
+                                         out32.ctypes.data_as(_f32p), N, nthr)
         return (out32, out64) if want64 else out32
 
     def f16_to_f64(self, bits: np.ndarray) -> np.ndarray:

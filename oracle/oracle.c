@@ -419,6 +419,55 @@ void oracle_conv2d_rows(const uint16_t* X, const uint16_t* Wt, int64_t N, int64_
     }
 }
 
+/* ------------------------------------------------------------------------------------------
+ * 8-bit floating point inputs ([GEMM] "Alcune regole pratiche": the matrix units reach their
+ * peak with 16-bit formats "and shorter ones still, like FP8").  The two OCP 8-bit formats:
+ *   E4M3 (fmt 0): 1 sign, 4 exponent bits (bias 7), 3 fraction bits; exponent field 0 is
+ *                 subnormal (f * 2^-9); S.1111.111 is NaN; there is no infinity (max 448).
+ *   E5M2 (fmt 1): 1 sign, 5 exponent bits (bias 15), 2 fraction bits; exponent field 0 is
+ *                 subnormal (f * 2^-16); exponent 31 is infinity (f = 0) or NaN.
+ * Every value is exact in binary64.
+ * ---------------------------------------------------------------------------------------- */
+static double f8_to_f64(uint8_t v, int fmt) {
+    const int s = v >> 7;
+    double r;
+    if (fmt == 0) {
+        const int e = (v >> 3) & 15, f = v & 7;
+        if (e == 15 && f == 7) return NAN;
+        r = e == 0 ? ldexp((double)f, -9) : ldexp((double)(8 + f), e - 10);
+    } else {
+        const int e = (v >> 2) & 31, f = v & 3;
+        if (e == 31) return f ? NAN : (s ? -INFINITY : INFINITY);
+        r = e == 0 ? ldexp((double)f, -16) : ldexp((double)(4 + f), e - 17);
+    }
+    return s ? -r : r;
+}
+
+void oracle_f8_to_f64_array(const uint8_t* in, double* out, int64_t n, int fmt) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f8_to_f64(in[i], fmt);
+}
+
+/* O3 for 8-bit inputs: C rows [m0, m1) of A·Bᵀ with A (M×K, lda) and B stored N×K (ldb), both
+ * in format fmt; products exact in binary64, sums in ascending k in binary64, one rounding to
+ * binary32.  Output layout as oracle_gemm_rows. */
+void oracle_gemm_f8_rows(int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                         int fmt, int64_t m0, int64_t m1, double* out64, float* out32, int64_t ldo, int threads) {
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += f8_to_f64(A[m * lda + k], fmt) * f8_to_f64(B[n * ldb + k], fmt);
+            if (out64) out64[(m - m0) * ldo + n] = acc;
+            if (out32) out32[(m - m0) * ldo + n] = (float)acc;
+        }
+    }
+}
+
 /* binary32 array -> bfloat16 bits (round to nearest even), for bf16 outputs. */
 void oracle_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);

@@ -510,6 +510,52 @@ def pin_gemm_f16(o):
             assert Fraction(got[i, j]) == ex or abs(Fraction(got[i, j]) - ex) <= abs(ex) * Fraction(1, 2 ** 52)
 
 
+def pin_f8_decode(o):
+    """OCP E4M3 and E5M2 decoding for all 256 patterns against torch's float8_e4m3fn and
+    float8_e5m2 conversions, and the formats' landmarks: E4M3 max 448 (0x7E), NaN 0x7F, smallest
+    subnormal 2^-9; E5M2 max 57344 (0x7B), infinity 0x7C, smallest subnormal 2^-16."""
+    bits = np.arange(256, dtype=np.uint8)
+    for fmt, tdt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        got = o.f8_to_f64(bits, fmt)
+        want = torch.from_numpy(bits.copy()).view(tdt).double().numpy()
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), fmt
+        assert np.array_equal(got[~nan], want[~nan]), fmt
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), fmt
+    e4 = o.f8_to_f64(bits, "e4m3")
+    assert e4[0x7E] == 448.0 and np.isnan(e4[0x7F]) and e4[0x01] == 2.0 ** -9 and e4[0x08] == 2.0 ** -6
+    e5 = o.f8_to_f64(bits, "e5m2")
+    assert e5[0x7B] == 57344.0 and e5[0x7C] == np.inf and e5[0x01] == 2.0 ** -16 and np.isnan(e5[0x7D])
+
+
+def _f8_bits(values: np.ndarray, fmt: str) -> np.ndarray:
+    tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    return torch.from_numpy(np.asarray(values, dtype=np.float32)).to(tdt).view(torch.uint8).numpy().copy()
+
+
+def pin_gemm_f8(o):
+    """8-bit inputs: small integers (exact in both formats) against numpy's integer matmul, and
+    values with fractions and subnormals against exact rationals."""
+    rng = np.random.default_rng(81)
+    M, N, K = 21, 19, 150
+    for fmt, lim in (("e4m3", 16), ("e5m2", 8)):
+        Ai = rng.integers(-lim, lim + 1, (M, K))
+        Bi = rng.integers(-lim, lim + 1, (N, K))
+        got = o.gemm_f8(_f8_bits(Ai, fmt), _f8_bits(Bi, fmt), M, N, K, K, K, fmt)
+        assert np.array_equal(got, (Ai @ Bi.T).astype(np.float32)), fmt
+        vals = np.array([2.0 ** -9, 2.0 ** -6, 0.375, -1.75, 3.5, 40.0], dtype=np.float32) if fmt == "e4m3" else \
+            np.array([2.0 ** -16, 2.0 ** -14, 0.75, -1.5, 3.0, 96.0], dtype=np.float32)
+        a = rng.choice(vals, (4, 9))
+        b = rng.choice(vals, (3, 9))
+        ab, bb = _f8_bits(a, fmt), _f8_bits(b, fmt)
+        g64 = o.gemm_f8(ab, bb, 4, 3, 9, 9, 9, fmt, want64=True)[1]
+        av, bv = o.f8_to_f64(ab, fmt), o.f8_to_f64(bb, fmt)
+        for i in range(4):
+            for j in range(3):
+                ex = sum(Fraction(float(av[i, k])) * Fraction(float(bv[j, k])) for k in range(9))
+                assert Fraction(g64[i, j]) == ex, (fmt, i, j)
+
+
 def _nc_x_hwcx(nchw: np.ndarray, x: int) -> np.ndarray:
     """NCHW -> NC/xHWCx by numpy: channels cut into slices of x (the last one zero-padded), each
     slice stored per position: array (N, C/x, H, W, x)."""
@@ -717,4 +763,4 @@ ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_struct
             pin_store_swizzle_and_roundtrip, pin_gemm_exact_rationals, pin_gemm_closed_forms,
             pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16, pin_conv_out_dim, pin_im2col_hand_example,
             pin_im2col_decode, pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_equals_im2col_gemm,
-            pin_f16_decode, pin_gemm_f16, pin_interleaved_boxes]
+            pin_f16_decode, pin_gemm_f16, pin_interleaved_boxes, pin_f8_decode, pin_gemm_f8]

@@ -65,6 +65,13 @@ MUTANTS = [
      "else v = ldexp((double)(1024 + f), e - 24);"),
     ("f16 subnormals scaled like normals", "if (e == 0) v = ldexp((double)f, -24);", "if (e == 0) v = ldexp((double)f, -25);"),
     ("f16 inputs decoded as bf16", "return kind == 1 ? f16_to_f64(h) : bf16_to_f64(h);", "return bf16_to_f64(h);"),
+    ("e4m3 exponent bias off by one", "r = e == 0 ? ldexp((double)f, -9) : ldexp((double)(8 + f), e - 10);",
+     "r = e == 0 ? ldexp((double)f, -9) : ldexp((double)(8 + f), e - 11);"),
+    ("e4m3 top exponent read as NaN", "if (e == 15 && f == 7) return NAN;", "if (e == 15) return NAN;"),
+    ("e5m2 subnormals scaled like e4m3", "r = e == 0 ? ldexp((double)f, -16) : ldexp((double)(4 + f), e - 17);",
+     "r = e == 0 ? ldexp((double)f, -9) : ldexp((double)(4 + f), e - 17);"),
+    ("f8 product reads B transposed", "acc += f8_to_f64(A[m * lda + k], fmt) * f8_to_f64(B[n * ldb + k], fmt);",
+     "acc += f8_to_f64(A[m * lda + k], fmt) * f8_to_f64(B[k * ldb + n], fmt);"),
     ("convolution drops the last channel", "for (int64_t c = 0; c < C; ++c) acc +=", "for (int64_t c = 0; c + 1 < C; ++c) acc +="),
 ]
 
