@@ -43,8 +43,14 @@ typedef enum {
     TBG_ERR_HIP = 6            /* the HIP runtime refused a launch                             */
 } tbg_status;
 
-/* Element type of a copy ([MAP] §7).  A copy moves bits: no conversion, no flush to zero. */
-typedef enum { TBG_U8 = 0, TBG_U16 = 1, TBG_U32 = 2, TBG_F16 = 3, TBG_BF16 = 4, TBG_F32 = 5 } tbg_dtype;
+/* Element type of a copy ([MAP] §7).  A copy moves bits: no conversion, no flush to zero.
+ * TBG_F8_E4M3 and TBG_F8_E5M2 are the two OCP 8-bit floating-point formats (E4M3: 4 exponent
+ * bits, bias 7, no infinity, NaN S.1111.111; E5M2: 5 exponent bits, bias 15, IEEE-style
+ * infinities and NaNs). */
+typedef enum {
+    TBG_U8 = 0, TBG_U16 = 1, TBG_U32 = 2, TBG_F16 = 3, TBG_BF16 = 4, TBG_F32 = 5,
+    TBG_F8_E4M3 = 6, TBG_F8_E5M2 = 7
+} tbg_dtype;
 
 /* Destination swizzle ([MAP] §11.3): for a byte offset a inside the box image,
  *   a' = a ^ ((a & Y_mask) >> 3),  Y_mask = 0x080 (32B), 0x180 (64B), 0x380 (128B),
@@ -65,8 +71,8 @@ typedef enum {
 
 /* Out-of-bounds fill ([MAP] §14; [TMA] §2.5): box elements outside the tensor are written to
  * the destination as zero bytes (TBG_OOB_ZERO, the pages' FILL_NONE) or as the element type's
- * canonical quiet NaN (TBG_OOB_NAN: bf16 0x7FC0, f16 0x7E00, f32 0x7FC00000; floating types
- * only).  The source is never touched outside the tensor. */
+ * canonical quiet NaN (TBG_OOB_NAN: bf16 0x7FC0, f16 0x7E00, f32 0x7FC00000, E4M3 0x7F, E5M2
+ * 0x7E; floating types only).  The source is never touched outside the tensor. */
 typedef enum { TBG_OOB_ZERO = 0, TBG_OOB_NAN = 1 } tbg_oob_fill;
 
 /* L2 promotion hint ([MAP] §13).  Accepted and recorded; it does not change any result. */
@@ -247,16 +253,24 @@ tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, con
                                tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* C <- alpha·A·B + beta·C with the input element type given: ab_dtype = TBG_BF16 or TBG_F16 (A and
- * B both of that type; [GEMM] "Alcune regole pratiche": the matrix units reach their peak with
- * 16-bit formats, bfloat16 or float16).  Products of two fp16 values are exact in fp32 like those
- * of bf16 values; accumulation is fp32, output fp32 or bf16.  cfg may be NULL (the library's
- * choice) or a configuration as for tbg_gemm_configured; fp16 inputs are built for the
- * configurations the automatic choice uses (ring 256x256, 256x128, 128x256, 128x128, 64x64 with
- * 2 stages; producer 256x128 and 128x256 with 2 stages, 128x128 and 64x64 with 3), other
- * configurations are UNSUPPORTED.  Other arguments, layouts and checks as tbg_gemm_ex; an
- * ab_dtype other than BF16/F16 is INVALID_VALUE.  tbg_gemm_configured is this call with
- * ab_dtype = TBG_BF16. */
+/* C <- alpha·A·B + beta·C with the input element type given ([GEMM] "Alcune regole pratiche": the
+ * matrix units reach their peak with 16-bit formats and shorter ones still, like FP8).  A and B
+ * are both of type ab_dtype:
+ *   TBG_BF16, TBG_F16   as tbg_gemm_configured.  fp16 inputs are built for the configurations
+ *                       the automatic choice uses (ring 256x256, 256x128, 128x256, 128x128,
+ *                       64x64 with 2 stages; producer 256x128 and 128x256 with 2 stages, 128x128
+ *                       and 64x64 with 3); others are UNSUPPORTED.
+ *   TBG_F8_E4M3, TBG_F8_E5M2
+ *                       8-bit inputs on the 16x16x128 matrix instruction.  B must be stored N×K
+ *                       (TBG_B_NK; TBG_B_KN is UNSUPPORTED); lda, ldb in elements (bytes); rows
+ *                       whose pitch or K is not a multiple of 16 bytes, or operands off a 16-byte
+ *                       boundary, are repacked into the workspace (tbg_gemm_workspace_bytes
+ *                       with half the leading dimensions and K rounded up to 16 is an upper
+ *                       bound; the OUT_OF_RANGE detail names the size).  Configurations: ring,
+ *                       2 stages, tiles 256x256, 128x128, 64x64.
+ * Every product of two inputs is exact in fp32; accumulation is fp32, output fp32 or bf16.  cfg
+ * may be NULL (the library's choice).  Other arguments, layouts and checks as tbg_gemm_ex; any
+ * other ab_dtype is INVALID_VALUE.  tbg_gemm_configured is this call with ab_dtype = TBG_BF16. */
 tbg_status tbg_gemm_typed(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                           int64_t ldb, tbg_b_layout bl, tbg_dtype ab_dtype, float beta, void* C, int64_t ldc,
                           tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,

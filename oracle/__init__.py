@@ -34,7 +34,7 @@ SWIZZLE_MODES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
 # element type -> (element size, NaN kind understood by oracle.c; 0 = integer, no NaN)
 DTYPES = {
     "u8": (1, 0), "u16": (2, 0), "u32": (4, 0),
-    "f16": (2, 2), "bf16": (2, 1), "f32": (4, 3),
+    "f16": (2, 2), "bf16": (2, 1), "f32": (4, 3), "f8e4m3": (1, 4), "f8e5m2": (1, 5),
 }
 
 _u64p = ctypes.POINTER(ctypes.c_uint64)

@@ -113,7 +113,8 @@ static uint64_t swizzle_span(int mode) {
  * estr[i]-th is copied, so n[i] = ceil(box[i]/estr[i]) land densely, innermost first, with no
  * padding; coordinates are signed; the swizzle acts on the byte offset inside the image.
  * NaN fill writes the canonical quiet NaN of the element type.
- *   elsize: 1, 2 or 4 bytes; nan_kind: 0 none (integer), 1 bf16, 2 f16, 3 f32.
+ *   elsize: 1, 2 or 4 bytes; nan_kind: 0 none (integer), 1 bf16, 2 f16, 3 f32, 4 E4M3 (0x7F),
+ *   5 E5M2 (0x7E, the quiet NaN with the top fraction bit set).
  * Returns the image size in bytes, or 0 on an argument this plain reference does not take.
  * ---------------------------------------------------------------------------------------- */
 uint64_t oracle_tiled_copy(int elsize, int rank, const void* src, const uint64_t* dims,
@@ -139,6 +140,8 @@ uint64_t oracle_tiled_copy(int elsize, int rank, const void* src, const uint64_t
         if (nan_kind == 1) { fill[0] = 0xC0; fill[1] = 0x7F; }                   /* bf16 0x7FC0 */
         else if (nan_kind == 2) { fill[0] = 0x00; fill[1] = 0x7E; }              /* f16  0x7E00 */
         else if (nan_kind == 3) { fill[2] = 0xC0; fill[3] = 0x7F; }              /* f32  0x7FC00000 */
+        else if (nan_kind == 4) { fill[0] = 0x7F; }                              /* E4M3 0x7F */
+        else if (nan_kind == 5) { fill[0] = 0x7E; }                              /* E5M2 0x7E */
         else return 0;
     }
     const uint8_t* s = (const uint8_t*)src;
@@ -343,6 +346,8 @@ uint64_t oracle_im2col_copy(int elsize, const void* src, const uint64_t* dims, c
         if (nan_kind == 1) { fill[0] = 0xC0; fill[1] = 0x7F; }
         else if (nan_kind == 2) { fill[0] = 0x00; fill[1] = 0x7E; }
         else if (nan_kind == 3) { fill[2] = 0xC0; fill[3] = 0x7F; }
+        else if (nan_kind == 4) { fill[0] = 0x7F; }
+        else if (nan_kind == 5) { fill[0] = 0x7E; }
         else return 0;
     }
     const int64_t c0 = coords[0], m0 = coords[1], tap_s = coords[2], tap_r = coords[3];

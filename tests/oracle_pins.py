@@ -528,6 +528,29 @@ def pin_f8_decode(o):
     assert e5[0x7B] == 57344.0 and e5[0x7C] == np.inf and e5[0x01] == 2.0 ** -16 and np.isnan(e5[0x7D])
 
 
+def pin_f8_nan_fill(o):
+    """NaN fill of 8-bit float tensors (tiled and im2col copies): every out-of-bounds byte decodes
+    to NaN under torch's float8_e4m3fn / float8_e5m2 conversions, every in-bounds byte is the
+    source's, and a zero fill stays zero."""
+    rng = np.random.default_rng(88)
+    src = rng.integers(0, 0x70, 6 * 5, dtype=np.uint8)  # finite patterns of both formats
+    for dt, tdt in (("f8e4m3", torch.float8_e4m3fn), ("f8e5m2", torch.float8_e5m2)):
+        img = o.tiled_copy(src, dt, [6, 5], [6], [16, 4], [1, 1], "none", True, [-3, 2])
+        inb = np.zeros((4, 16), dtype=bool)
+        inb[:3, 3:9] = True  # rows 2..4 of 5, columns 0..5 of 6
+        vals = torch.from_numpy(img.copy()).view(tdt).float().numpy().reshape(4, 16)
+        assert np.isnan(vals[~inb]).all(), dt
+        assert np.array_equal(img.reshape(4, 16)[inb], src.reshape(5, 6)[2:5, 0:6].reshape(-1)), dt
+        zero = o.tiled_copy(src, dt, [6, 5], [6], [16, 4], [1, 1], "none", False, [-3, 2])
+        assert (zero.reshape(4, 16)[~inb] == 0).all(), dt
+        im = o.im2col_copy(src, dt, [6, 5, 1, 1], [6, 30, 30], [1, 1], [1, 1], [1, 1], [1, 1], [3, 3], 16, 3, "none",
+                           True, [0, 0, 0, 1])  # tap r = 1: the image row; tap s = 0: pixel 0 in the padding
+        v = torch.from_numpy(im.copy()).view(tdt).float().numpy().reshape(3, 16)
+        assert np.isnan(v[:, 6:]).all() and np.isnan(v[0]).all(), dt  # channels past C; pixel 0 in the padding
+        assert np.array_equal(im.reshape(3, 16)[1, :6], src[0:6]), dt
+        assert np.array_equal(im.reshape(3, 16)[2, :6], src[6:12]), dt
+
+
 def _f8_bits(values: np.ndarray, fmt: str) -> np.ndarray:
     tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
     return torch.from_numpy(np.asarray(values, dtype=np.float32)).to(tdt).view(torch.uint8).numpy().copy()
@@ -763,4 +786,4 @@ ALL_PINS = [pin_swizzle_bit_rules, pin_swizzle_hand_examples, pin_swizzle_struct
             pin_store_swizzle_and_roundtrip, pin_gemm_exact_rationals, pin_gemm_closed_forms,
             pin_gemm_tiled_equals_direct, pin_gemm_ex, pin_f32_to_bf16, pin_conv_out_dim, pin_im2col_hand_example,
             pin_im2col_decode, pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_equals_im2col_gemm,
-            pin_f16_decode, pin_gemm_f16, pin_interleaved_boxes, pin_f8_decode, pin_gemm_f8]
+            pin_f16_decode, pin_gemm_f16, pin_interleaved_boxes, pin_f8_decode, pin_gemm_f8, pin_f8_nan_fill]

@@ -418,3 +418,25 @@ def test_interleaved_descriptor_rules():
     assert tbg.encode_tiled_interleaved_status(**{**base, "interleave": "none", "rank": 2, "global_dim": [64, 8],
                                                   "global_strides": [128], "box_dim": [64, 8],
                                                   "element_strides": [1, 1]}) == tbg.OK
+
+
+def test_gemm_fp8_checks():
+    import torch
+    g = dict(M=64, N=64, K=128, alpha=1.0, A=BASE, lda=128, B=BASE, ldb=128, b_layout="nk", beta=0.0, C=BASE, ldc=64,
+             c_dtype="f32")
+    for ab in ("f8e4m3", "f8e5m2"):
+        assert tbg.gemm_typed_status(**{**g, "b_layout": "kn"}, ab_dtype=ab) == tbg.ERR_UNSUPPORTED
+        assert tbg.gemm_typed_status(**g, ab_dtype=ab, config=tbg.gemm_config("256x128", 2, "ring")) == tbg.ERR_UNSUPPORTED
+        assert tbg.gemm_typed_status(**g, ab_dtype=ab, config=tbg.gemm_config("128x128", 2, "producer")) == \
+            tbg.ERR_UNSUPPORTED
+        assert tbg.gemm_typed_status(**g, ab_dtype=ab, config=tbg.gemm_config("128x128", 3, "ring")) == tbg.ERR_UNSUPPORTED
+        assert tbg.gemm_typed_status(**{**g, "lda": 100}, ab_dtype=ab) == tbg.ERR_INVALID_VALUE
+        # K = 100 is not a whole number of 16-byte chunks: the operands need the repack workspace
+        assert tbg.gemm_typed_status(**{**g, "K": 100}, ab_dtype=ab) == tbg.ERR_OUT_OF_RANGE
+        if not torch.cuda.is_available():
+            assert tbg.gemm_typed_status(**g, ab_dtype=ab) == tbg.ERR_NO_DEVICE
+            for t in ("256x256", "128x128", "64x64"):
+                assert tbg.gemm_typed_status(**g, ab_dtype=ab, config=tbg.gemm_config(t, 2, "ring")) == tbg.ERR_NO_DEVICE
+    # the 8-bit types as copy element types, NaN fill included
+    d = tbg.encode_tiled("f8e4m3", 2, BASE, [256, 64], [256], [128, 8], [1, 1], "128B", "none", "nan")
+    assert tbg.box_bytes(d) == 128 * 8

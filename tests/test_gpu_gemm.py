@@ -379,3 +379,116 @@ def test_fp16_inputs(ops, orc, pipeline, tile, stages):
         ref = orc.gemm(Ai.view(torch.int16).numpy().view(np.uint16), Bi.view(torch.int16).numpy().view(np.uint16),
                        M, N, K, K, shape_b[1], bl, ab="f16")
         assert np.array_equal(_to_f32(C), ref)
+
+
+def _f8(rows, cols, seed, fmt, scale=1.0):
+    """A (rows, cols) matrix of 8-bit floats drawn N(0, scale): (uint8 bits, float32 values)."""
+    g = torch.Generator().manual_seed(seed)
+    tdt = torch.float8_e4m3fn if fmt == "f8e4m3" else torch.float8_e5m2
+    t = (torch.randn((rows, cols), generator=g) * scale).to(tdt)
+    return t.view(torch.uint8).contiguous(), t.float()
+
+
+# gfx950's 8-bit matrix instruction sums its 128 products with about 16 bits of precision relative
+# to the sum of their magnitudes (measured over 262144 outputs: at most 2^-15.6 · Σ|a·b| for one
+# instruction), so fp8 results are checked against the oracle with that forward-error term added
+# to the usual rule, at 2^-13 (six times the largest error seen).
+F8_DOT_BOUND = 2.0 ** -13
+
+
+def _check_f8(got, ref, A_vals, B_vals, what):
+    absum = np.abs(A_vals.astype(np.float64)) @ np.abs(B_vals.astype(np.float64)).T
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    bound = np.maximum(1e-2 * np.abs(r), 1e-3) + F8_DOT_BOUND * absum
+    err = np.abs(g - r)
+    ok = np.isfinite(g) & (err <= bound)
+    _say(f"  {what}: n={g.size} max_abs={err.max():.3g} max(err/sum|ab|)={(err / np.maximum(absum, 1e-30)).max():.3g} "
+         f"fail={int((~ok).sum())}")
+    assert ok.all(), what
+
+
+def _run_f8(M, N, K, A8, B8, fmt, out, cfg=None, lda=None, ldb=None, alpha=1.0, beta=0.0, C_old=None, ldc_pad=3):
+    import tiled_bf16_gemm_amd as tbg
+    lda = lda or A8.shape[1]
+    ldb = ldb or B8.shape[1]
+    Ad, Bd = A8.cuda(), B8.cuda()
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    ldc = N + ldc_pad
+    Cbuf = torch.full((M, ldc), float("nan"), dtype=tdt, device="cuda") if C_old is None else C_old.clone().cuda()
+    ws = torch.empty(((M + N) * ((K + 15) // 16 * 16) + 1024), dtype=torch.uint8, device="cuda")
+    tbg.gemm_typed(M, N, K, alpha, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, "nk", fmt, beta, Cbuf.data_ptr(), ldc, out,
+                   cfg, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return _to_f32(Cbuf)
+
+
+@gpu
+@pytest.mark.parametrize("fmt", ["f8e4m3", "f8e5m2"])
+def test_fp8_inputs(ops, orc, fmt):
+    """OCP 8-bit inputs (tbg_gemm_typed) against the oracle, within the usual rule plus the matrix
+    instruction's own dot-product error (F8_DOT_BOUND): ragged shapes (K not a multiple of 16
+    bytes: repack path; an odd number of 128-wide K tiles), padded leading dimensions, both output
+    types, every fp8 tile, bit-identical across tiles; small integers bit for bit; alpha/beta."""
+    import tiled_bf16_gemm_amd as tbg
+    ofmt = "e4m3" if fmt == "f8e4m3" else "e5m2"
+    cases = [(700, 520, 1000, "f32"), (333, 190, 200, "bf16"), (130, 70, 1, "bf16"), (257, 300, 128, "f32"),
+             (64, 64, 3000, "f32")]
+    for i, (M, N, K, out) in enumerate(cases):
+        A8, Av = _f8(M, K, 1300 + i, fmt)
+        B8, Bv = _f8(N, K, 1400 + i, fmt)
+        ref = orc.gemm_f8(A8.numpy(), B8.numpy(), M, N, K, K, K, ofmt)
+        base = None
+        for tile in (None, "256x256", "128x128", "64x64"):
+            cfg = None if tile is None else tbg.gemm_config(tile, 2, "ring")
+            _say(f"{fmt} gemm M={M} N={N} K={K} {out} tile {tile or 'auto'}")
+            got = _run_f8(M, N, K, A8, B8, fmt, out, cfg)
+            _check_f8(got[:, :N], ref, Av.numpy(), Bv.numpy(), f"{fmt} case {i} tile {tile}")
+            assert np.all(np.isnan(got[:, N:])), "columns past N were written"
+            if base is None:
+                base = got
+            else:
+                assert np.array_equal(got[:, :N], base[:, :N]), "tiles disagree"
+    # padded leading dimensions (multiples of 16: no repack) and a misaligned start (repack)
+    M, N, K = 300, 257, 384
+    A8, Av = _f8(M, K + 32, 1500, fmt)
+    B8, Bv = _f8(N, K + 16, 1501, fmt)
+    ref = orc.gemm_f8(A8.numpy(), B8.numpy(), M, N, K, K + 32, K + 16, ofmt)
+    _say(f"{fmt} gemm padded leading dimensions")
+    _check_f8(_run_f8(M, N, K, A8, B8, fmt, "f32")[:, :N], ref, Av[:, :K].numpy(), Bv[:, :K].numpy(), f"{fmt} padded")
+    # small integers: every product and every partial sum of one instruction (at most 128 · 16)
+    # is an integer well inside the instruction's precision, so the result is exact
+    lim = 4
+    rng = np.random.default_rng(91)
+    Ai = rng.integers(-lim, lim + 1, (M, K)).astype(np.float32)
+    Bi = rng.integers(-lim, lim + 1, (N, K)).astype(np.float32)
+    tdt = torch.float8_e4m3fn if fmt == "f8e4m3" else torch.float8_e5m2
+    A8 = torch.from_numpy(Ai).to(tdt).view(torch.uint8)
+    B8 = torch.from_numpy(Bi).to(tdt).view(torch.uint8)
+    _say(f"{fmt} integer gemm")
+    got = _run_f8(M, N, K, A8, B8, fmt, "f32")
+    assert np.array_equal(got[:, :N], (Ai.astype(np.float64) @ Bi.T.astype(np.float64)).astype(np.float32))
+    # alpha/beta
+    C_old = torch.from_numpy(rng.standard_normal((M, N + 3)).astype(np.float32))
+    _say(f"{fmt} gemm alpha=2 beta=-1")
+    got = _run_f8(M, N, K, A8, B8, fmt, "f32", alpha=2.0, beta=-1.0, C_old=C_old)
+    want = (2.0 * (Ai.astype(np.float64) @ Bi.T.astype(np.float64)) - C_old[:, :N].double().numpy()).astype(np.float32)
+    assert np.array_equal(got[:, :N], want)
+    assert np.array_equal(got[:, N:], C_old[:, N:].numpy())
+
+
+@gpu
+def test_fp8_large_sampled(ops, orc):
+    """The 16384×14336×4096 product (the MLP workload's shape) with E4M3 inputs: sampled rows
+    against the oracle, finite everywhere, deterministic."""
+    M, N, K = 16384, 14336, 4096
+    A8, Av = _f8(M, K, 1600, "f8e4m3")
+    B8, Bv = _f8(N, K, 1601, "f8e4m3", 0.05)
+    _say("fp8 16384x14336x4096")
+    got = _run_f8(M, N, K, A8, B8, "f8e4m3", "bf16", ldc_pad=0)
+    again = _run_f8(M, N, K, A8, B8, "f8e4m3", "bf16", ldc_pad=0)
+    assert np.isfinite(got).all()
+    assert np.array_equal(got, again), "not deterministic"
+    for m0 in (0, 7777, M - 64):
+        ref = orc.gemm_f8(A8.numpy(), B8.numpy(), M, N, K, K, K, "e4m3", rows=(m0, m0 + 64))
+        _check_f8(got[m0:m0 + 64], ref, Av[m0:m0 + 64].numpy(), Bv.numpy(), f"fp8 rows {m0}..{m0 + 64}")

@@ -36,8 +36,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # ---- enums (values as in tbg.h) -------------------------------------------------------------
 OK, ERR_INVALID_VALUE, ERR_MISALIGNED, ERR_UNSUPPORTED, ERR_OUT_OF_RANGE, ERR_NO_DEVICE, ERR_HIP = range(7)
-DTYPES = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5}
-ELSIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4}
+DTYPES = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "f8e4m3": 6, "f8e5m2": 7}
+ELSIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "f8e4m3": 1, "f8e5m2": 1}
 SWIZZLES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
 OOB = {"zero": 0, "nan": 1}
 L2 = {"none": 0, "64B": 1, "128B": 2, "256B": 3}

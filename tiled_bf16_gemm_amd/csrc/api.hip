@@ -35,7 +35,7 @@ tbg_status fail(tbg_status s, const char* fmt, ...) {
 
 int elsize_of(int dtype) {
   switch (dtype) {
-    case TBG_U8: return 1;
+    case TBG_U8: case TBG_F8_E4M3: case TBG_F8_E5M2: return 1;
     case TBG_U16: case TBG_F16: case TBG_BF16: return 2;
     case TBG_U32: case TBG_F32: return 4;
     default: return 0;
@@ -149,7 +149,8 @@ tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank
   if ((int)l2 < TBG_L2_NONE || (int)l2 > TBG_L2_256B) return fail(TBG_ERR_INVALID_VALUE, "unknown l2 hint %d", (int)l2);
   if ((int)oob != TBG_OOB_ZERO && (int)oob != TBG_OOB_NAN)
     return fail(TBG_ERR_INVALID_VALUE, "unknown oob fill %d", (int)oob);
-  if (oob == TBG_OOB_NAN && !(dtype == TBG_F16 || dtype == TBG_BF16 || dtype == TBG_F32))
+  if (oob == TBG_OOB_NAN && !(dtype == TBG_F16 || dtype == TBG_BF16 || dtype == TBG_F32 || dtype == TBG_F8_E4M3 ||
+                              dtype == TBG_F8_E5M2))
     return fail(TBG_ERR_INVALID_VALUE, "NaN fill needs a floating-point element type");
 
   DescImpl d;
@@ -325,7 +326,8 @@ tbg_status tbg_encode_im2col(tbg_tensor_desc* out, tbg_dtype dtype, const void* 
   if ((int)l2 < TBG_L2_NONE || (int)l2 > TBG_L2_256B) return fail(TBG_ERR_INVALID_VALUE, "unknown l2 hint %d", (int)l2);
   if ((int)oob != TBG_OOB_ZERO && (int)oob != TBG_OOB_NAN)
     return fail(TBG_ERR_INVALID_VALUE, "unknown oob fill %d", (int)oob);
-  if (oob == TBG_OOB_NAN && !(dtype == TBG_F16 || dtype == TBG_BF16 || dtype == TBG_F32))
+  if (oob == TBG_OOB_NAN && !(dtype == TBG_F16 || dtype == TBG_BF16 || dtype == TBG_F32 || dtype == TBG_F8_E4M3 ||
+                              dtype == TBG_F8_E5M2))
     return fail(TBG_ERR_INVALID_VALUE, "NaN fill needs a floating-point element type");
   for (int i = 0; i < 4; ++i)
     if (global_dim[i] < 1 || global_dim[i] > (1ull << 31) - 1)
@@ -472,14 +474,128 @@ size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, in
 
 namespace {
 
+tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
+                     const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes, void* stream, bool scaled,
+                     tbg_dtype ab_dtype = TBG_BF16);
+
+// The fp8 product: operands are byte matrices, repacked to 16-byte pitches with zero padding
+// where needed, then handed to the kernel as 16-bit pairs.
+tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, tbg_b_layout bl, tbg_dtype ab_dtype, float beta, void* C, int64_t ldc,
+                         tbg_dtype c_dtype, const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,
+                         void* stream, bool scaled) {
+  if (M < 0 || N < 0 || K < 0) return fail(TBG_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
+                                          (long long)M, (long long)N, (long long)K);
+  if ((int)bl != TBG_B_KN && (int)bl != TBG_B_NK) return fail(TBG_ERR_INVALID_VALUE, "unknown b_layout %d", (int)bl);
+  if (bl != TBG_B_NK) return fail(TBG_ERR_UNSUPPORTED, "8-bit inputs need B stored N×K (TBG_B_NK)");
+  int bm = 0, bn = 0;
+  if (cfg) {
+    if (cfg->pipeline != TBG_PIPE_AUTO && cfg->pipeline != TBG_PIPE_RING)
+      return fail(TBG_ERR_UNSUPPORTED, "the fp8 product runs on the barrier ring only");
+    if (cfg->stages != 0 && cfg->stages != 2) return fail(TBG_ERR_UNSUPPORTED, "the fp8 ring has 2 stages");
+    if ((cfg->tile_m == 0) != (cfg->tile_n == 0))
+      return fail(TBG_ERR_INVALID_VALUE, "tile_m and tile_n must both be 0 or both be set");
+    if (cfg->tile_m != 0 && !tbg::fp8_tile_built(cfg->tile_m, cfg->tile_n))
+      return fail(TBG_ERR_UNSUPPORTED, "no fp8 kernel with tile %dx%d (built: 256x256, 128x128, 64x64)", cfg->tile_m,
+                  cfg->tile_n);
+    bm = cfg->tile_m;
+    bn = cfg->tile_n;
+  }
+  if (scaled && alpha == 0.f)
+    return gemm_impl(M, N, 0, 0.f, nullptr, 1, nullptr, 1, TBG_B_NK, beta, C, ldc, c_dtype, nullptr, nullptr, 0,
+                     stream, true, TBG_BF16);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(TBG_ERR_UNSUPPORTED, "sizes must stay below 2^31");
+  if (c_dtype != TBG_F32 && c_dtype != TBG_BF16) return fail(TBG_ERR_INVALID_VALUE, "C must be TBG_F32 or TBG_BF16");
+  if (lda < (K > 0 ? K : 1)) return fail(TBG_ERR_INVALID_VALUE, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+  if (ldb < (K > 0 ? K : 1)) return fail(TBG_ERR_INVALID_VALUE, "ldb=%lld < K=%lld", (long long)ldb, (long long)K);
+  if (ldc < (N > 0 ? N : 1)) return fail(TBG_ERR_INVALID_VALUE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+  if (lda > 2 * kMaxLd || ldb > 2 * kMaxLd || ldc > (1ll << 40))
+    return fail(TBG_ERR_UNSUPPORTED, "leading dimensions are limited to 2^23-2 bytes");
+  if (M == 0 || N == 0) return TBG_OK;
+  if (!C) return fail(TBG_ERR_INVALID_VALUE, "C is NULL");
+  if (K > 0 && (!A || !B)) return fail(TBG_ERR_INVALID_VALUE, "A or B is NULL");
+  const int64_t k16 = round_up(K > 0 ? K : 1, 16);
+  const bool pack_a = K > 0 && ((lda % 16) != 0 || (K % 16) != 0 || ((uintptr_t)A % 16) != 0);
+  const bool pack_b = K > 0 && ((ldb % 16) != 0 || (K % 16) != 0 || ((uintptr_t)B % 16) != 0);
+  const size_t a_bytes = pack_a ? (size_t)round_up(M * k16, 256) : 0;
+  const size_t b_bytes = pack_b ? (size_t)round_up(N * k16, 256) : 0;
+  if (a_bytes + b_bytes > 0) {
+    if (!workspace || workspace_bytes < a_bytes + b_bytes)
+      return fail(TBG_ERR_OUT_OF_RANGE, "workspace of %zu bytes needed to repack unaligned operands (have %zu)",
+                  a_bytes + b_bytes, workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256 != 0) return fail(TBG_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  }
+  int num_cus = 0;
+  tbg_status st = check_device(&num_cus);
+  if (st != TBG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* Ab = (const uint8_t*)A;
+  const uint8_t* Bb = (const uint8_t*)B;
+  int64_t lda_b = lda, ldb_b = ldb;
+  hipError_t e = hipSuccess;
+  if (pack_a) {
+    uint8_t* dst = (uint8_t*)workspace;
+    e = tbg::launch_pack_bytes(Ab, lda, M, K, dst, k16, s);
+    Ab = dst;
+    lda_b = k16;
+  }
+  if (e == hipSuccess && pack_b) {
+    uint8_t* dst = (uint8_t*)workspace + a_bytes;
+    e = tbg::launch_pack_bytes(Bb, ldb, N, K, dst, k16, s);
+    Bb = dst;
+    ldb_b = k16;
+  }
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "fp8 repack: %s", hipGetErrorString(e));
+  tbg::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = (const uint16_t*)Ab;
+  p.B = (const uint16_t*)Bb;
+  p.C = C;
+  p.lda = lda_b / 2;
+  p.ldb = ldb_b / 2;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)(K > 0 ? k16 / 2 : 0);
+  p.kchunks = K > 0 ? (int)(k16 / 16) : 0;  // K = 0: every copy lane masked, A and B never read
+  p.group_m = 8;
+  p.vec_store = (((uintptr_t)C) % 16 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
+  p.alpha = alpha;
+  p.beta = beta;
+  p.scaled = scaled ? 1 : 0;
+  if (bm == 0) {
+    // the ring's cost model over the fp8 tiles
+    double best = 0;
+    const struct { int bm, bn; double eff; } tiles[] = {{256, 256, 1.0}, {128, 128, 0.82}, {64, 64, 0.52}};
+    const int cus = num_cus > 0 ? num_cus : 256;
+    for (const auto& t : tiles) {
+      const int64_t ntiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+      const double cost = (double)((ntiles + cus - 1) / cus) * t.bm * t.bn / t.eff;
+      if (best == 0 || cost < best * 0.999) {
+        best = cost;
+        bm = t.bm;
+        bn = t.bn;
+      }
+    }
+  }
+  e = tbg::launch_fp8(p, bm, bn, ab_dtype == TBG_F8_E5M2 ? 1 : 0, c_dtype == TBG_BF16, s);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "fp8 gemm launch: %s", hipGetErrorString(e));
+  return TBG_OK;
+}
+
 // C = alpha·A·B + beta·C (scaled) or C = A·B.  With alpha == 0 the product is skipped: K is taken
 // as 0 and A, B and their leading dimensions are not looked at.
 tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                      int64_t ldb, tbg_b_layout bl, float beta, void* C, int64_t ldc, tbg_dtype c_dtype,
                      const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes, void* stream, bool scaled,
-                     tbg_dtype ab_dtype = TBG_BF16) {
+                     tbg_dtype ab_dtype) {
+  if (ab_dtype == TBG_F8_E4M3 || ab_dtype == TBG_F8_E5M2)
+    return gemm_fp8_impl(M, N, K, alpha, A, lda, B, ldb, bl, ab_dtype, beta, C, ldc, c_dtype, cfg, workspace,
+                         workspace_bytes, stream, scaled);
   if (ab_dtype != TBG_BF16 && ab_dtype != TBG_F16)
-    return fail(TBG_ERR_INVALID_VALUE, "A and B must be TBG_BF16 or TBG_F16 (got %d)", (int)ab_dtype);
+    return fail(TBG_ERR_INVALID_VALUE, "A and B must be TBG_BF16, TBG_F16, TBG_F8_E4M3 or TBG_F8_E5M2 (got %d)",
+                (int)ab_dtype);
   const int in = ab_dtype == TBG_F16 ? 1 : 0;
   if (M < 0 || N < 0 || K < 0) return fail(TBG_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                                           (long long)M, (long long)N, (long long)K);

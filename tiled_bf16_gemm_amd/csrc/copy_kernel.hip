@@ -273,6 +273,8 @@ hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, cons
     // canonical quiet NaN of the element type, replicated to 32 bits
     if (d.dtype == 3) fill = 0x7E007E00u;        // f16
     else if (d.dtype == 4) fill = 0x7FC07FC0u;   // bf16
+    else if (d.dtype == 6) fill = 0x7F7F7F7Fu;   // fp8 E4M3
+    else if (d.dtype == 7) fill = 0x7E7E7E7Eu;   // fp8 E5M2
     else fill = 0x7FC00000u;                     // f32
   }
   const size_t lds_bytes = ((size_t)d.image_bytes + 1023u) & ~(size_t)1023u;

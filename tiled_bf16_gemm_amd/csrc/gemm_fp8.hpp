@@ -1,0 +1,176 @@
+// GEMM with 8-bit floating-point inputs (OCP E4M3 or E5M2) on gfx950's 16×16×128 matrix
+// instruction: C = A·Bᵀ, A row-major M×K, B stored N×K (K contiguous), fp32 accumulation.
+//
+// "GEMM: la moltiplicazione di matrici sull'hardware", section "Alcune regole pratiche": the
+// matrix units reach their peak with 16-bit formats and with shorter ones still, like FP8.  A
+// K tile is 128 fp8 values — 128 bytes per row, exactly the rows of the bf16 kernels — so the
+// ring, the copy atoms, the 2-row swizzle and the epilogue are the barrier ring's (gemm_ring.hpp,
+// two stages).  What changes:
+//  * one product per fragment pair per K tile, `v_mfma_f32_16x16x128_f8f6f4`, whose operands are
+//    32 bytes per lane: lane l supplies row l%16 of its fragment and bytes 32(l/16)..+31 of the
+//    tile's row (two ds_read_b128).  The instruction sums over all 128 k of the two operands;
+//    since A and B use the same byte-to-k placement, every k of A meets the same k of B;
+//  * the products run A-fragment outermost: a wave's 8 B fragments stay live for the whole tile,
+//    the next tile's B fragments are read in the first half and each next A fragment right
+//    after the last product that uses the current one, so one tile's fragments plus the next
+//    tile's B fragments fit the register file next to the accumulators;
+//  * one barrier per K tile: it publishes tile kt+1 and frees the stage of tile kt, whose
+//    fragments were all read during the previous tile.  The loop runs pairs of tiles; an odd
+//    tile count adds one tile of zeros (fully masked copies) to the products.
+// The operands are handed over as 16-bit pairs (GemmParams in units of two fp8 values), so the
+// copy helpers are the bf16 kernels' own.
+#pragma once
+#include "gemm_common.hpp"
+#include "gemm_ring.hpp"
+
+namespace tbg {
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+template <class T>
+struct Frags8 {
+  i32x8_t a[T::FM];
+  i32x8_t b[T::FN];
+};
+
+// One 16×16×128 product; FMT 0: E4M3, 1: E5M2 (both operands).  ASM pins the accumulator to
+// AGPRs as in mfma16; DRAIN adds the wait states before the accumulators may be read.
+template <bool ASM, bool DRAIN, int FMT>
+__device__ __forceinline__ void mfma8(f32x4_t& acc, const i32x8_t& a, const i32x8_t& b) {
+  if (!ASM) {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, FMT, FMT, 0, 0, 0, 0);
+  } else if (FMT == 0) {
+    if (DRAIN)
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(acc)
+                   : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  } else {
+    if (DRAIN)
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(acc)
+                   : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(acc) : "v"(a), "v"(b));
+  }
+}
+
+// Per-lane LDS byte offsets of the two 16-byte halves of a fragment row: logical chunks
+// 2(l/16) and 2(l/16)+1 of a 128-byte row at their 2-row-swizzled places.
+struct FragAddr8 {
+  uint32_t a_lane, a_col[2];
+  uint32_t b_lane, b_col[2];
+};
+
+template <class T>
+__device__ __forceinline__ FragAddr8 make_frag_addr8(int wm, int wn, int lane) {
+  FragAddr8 fa;
+  const int arow = wm * T::TM + (lane & 15), brow = wn * T::TN + (lane & 15);
+  const int ax = (arow >> 1) & 7, bx = (brow >> 1) & 7, c = 2 * (lane >> 4);
+  fa.a_lane = (uint32_t)arow * 128u;
+  fa.a_col[0] = (uint32_t)(c ^ ax) * 16u;
+  fa.a_col[1] = (uint32_t)((c + 1) ^ ax) * 16u;
+  fa.b_lane = (uint32_t)brow * 128u;
+  fa.b_col[0] = (uint32_t)(c ^ bx) * 16u;
+  fa.b_col[1] = (uint32_t)((c + 1) ^ bx) * 16u;
+  return fa;
+}
+
+__device__ __forceinline__ i32x8_t read_frag8(const uint8_t* base, uint32_t lane_off, const uint32_t* col) {
+  const u32x4_t lo = *(const u32x4_t*)(base + lane_off + col[0]);
+  const u32x4_t hi = *(const u32x4_t*)(base + lane_off + col[1]);
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// The products of one K tile on `cur`, with the next tile's fragment reads and (later tiles')
+// copy atoms interleaved: B reads over the first half, A fragment fm right after its last
+// product, copy atoms spread evenly.
+template <class T, int FMT>
+__device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], const Frags8<T>& cur, Frags8<T>& nxt,
+                                       const FragAddr8& fa, const uint8_t* nA, const uint8_t* nB, const TileCopy& tc,
+                                       const LaneChunk* la, const LaneChunk* lb) {
+  constexpr int P = T::Products, A = T::Atoms, FN = T::FN, FM = T::FM;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int fm = i / FN, fn = i % FN;
+    // B read j before product (j * P/2) / FN
+#pragma unroll
+    for (int j = (2 * i * FN + P - 1) / P; j < (2 * (i + 1) * FN + P - 1) / P && j < FN; ++j)
+      nxt.b[j] = read_frag8(nB, fa.b_lane + j * 2048, fa.b_col);
+#pragma unroll
+    for (int j = (i * A + P - 1) / P; j < ((i + 1) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
+    if (i == P - 1) mfma8<T::AsmMfma, true, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    else mfma8<T::AsmMfma, false, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    if (fn == FN - 1) nxt.a[fm] = read_frag8(nA, fa.a_lane + fm * 2048, fa.a_col);
+  }
+}
+
+template <int BM, int BN, int FMT, int OUT, int SCALED>
+__global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gemm_fp8_kernel(GemmParams p) {
+  using T = TileCfg<BM, BN>;
+  constexpr int BL = 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::StageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
+  LaneChunk la[T::AtomsA], lb[T::AtomsB];
+#pragma unroll
+  for (int i = 0; i < T::AtomsA; ++i) la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
+#pragma unroll
+  for (int i = 0; i < T::AtomsB; ++i) lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+  const int ktiles = p.K > 0 ? (p.K + kBK - 1) / kBK : 1;  // K counts pairs: a tile is 64 pairs
+  const uint32_t smem_addr = lds_addr_of(smem);
+
+  auto make_copy = [&](int kt, int stage) {
+    const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
+    TileCopy tc;
+    const uint32_t sa = smem_addr + stage * T::StageBytes;
+    tc.ra = o.ra;
+    tc.rb = o.rb;
+    tc.cvalid_a = o.cvalid_a;
+    tc.cvalid_b = o.cvalid_a;
+    tc.lds_a = sa + (BM / 4) * wave * 128;
+    tc.lds_b = sa + T::ABytes + (BN / 4) * wave * 128;
+    return tc;
+  };
+
+  const FragAddr8 fa = make_frag_addr8<T>(wm, wn, lane);
+  f32x4_t acc[T::FN][T::FM];
+  zero_acc<T>(acc);
+  {
+    Frags8<T> f0, f1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const TileCopy tc = make_copy(t, t);
+#pragma unroll
+      for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
+    }
+    stage_barrier<T::Atoms>();  // tile 0 landed
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) f0.a[j] = read_frag8(smem, fa.a_lane + j * 2048, fa.a_col);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) f0.b[j] = read_frag8(smem + T::ABytes, fa.b_lane + j * 2048, fa.b_col);
+    for (int kt = 0; kt < ktiles; kt += 2) {
+      // tile kt (stage 0) with tile kt+1's reads (stage 1) and tile kt+2's copies (stage 0)
+      stage_barrier<0>();
+      {
+        const uint8_t* nA = smem + T::StageBytes;
+        ktile8<T, FMT>(acc, f0, f1, fa, nA, nA + T::ABytes, make_copy(kt + 2, 0), la, lb);
+      }
+      // tile kt+1 (stage 1) with tile kt+2's reads (stage 0) and tile kt+3's copies (stage 1)
+      stage_barrier<0>();
+      ktile8<T, FMT>(acc, f1, f0, fa, smem, smem + T::ABytes, make_copy(kt + 3, 1), la, lb);
+    }
+  }
+  stage_barrier<0>();
+  store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
+}
+
+}  // namespace tbg

@@ -48,6 +48,35 @@ hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_
   return hipGetLastError();
 }
 
+// Byte rows: copy `rows` rows of `cols` bytes into a buffer of pitch ld_dst (a multiple of 16),
+// zero-filling bytes cols..ld_dst-1 (the packing step for 8-bit operands).
+__global__ void __launch_bounds__(256) pack_bytes_kernel(const uint8_t* src, int64_t ld_src, int64_t rows,
+                                                         int64_t cols, uint8_t* dst, int64_t ld_dst) {
+  const int64_t cpr = ld_dst / 16;
+  const int64_t total = rows * cpr;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / cpr;
+    const int64_t c0 = (idx - r * cpr) * 16;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < cols) w[j >> 2] |= (uint32_t)src[r * ld_src + c0 + j] << (8 * (j & 3));
+    *(uint4*)(dst + r * ld_dst + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_pack_bytes(const uint8_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint8_t* dst,
+                             int64_t ld_dst, hipStream_t stream) {
+  const int64_t total = rows * (ld_dst / 16);
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, ld_src, rows, cols, dst,
+                     ld_dst);
+  return hipGetLastError();
+}
+
 namespace {
 
 struct GemmVariant {

@@ -77,5 +77,11 @@ hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, i
                        hipStream_t stream, int in = 0);
 hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ld_dst,
                        hipStream_t stream);
+hipError_t launch_pack_bytes(const uint8_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint8_t* dst,
+                             int64_t ld_dst, hipStream_t stream);
+// fp8 GEMM (gemm_fp8.hpp): p in units of two fp8 values (lda, ldb, K, kchunks as for 16-bit data
+// of half the width); fmt 0 E4M3, 1 E5M2; tiles 256×256, 128×128, 64×64.
+hipError_t launch_fp8(GemmParams p, int bm, int bn, int fmt, int out_bf16, hipStream_t stream);
+bool fp8_tile_built(int bm, int bn);
 
 }  // namespace tbg
