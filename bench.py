@@ -14,8 +14,9 @@ Also reported in the same line:
                 summary when it was taken on the current kernel source, else null.
   cpu_baseline  the CPU oracle on a bounded sample of the same product (the first rows of C),
                 timed on this host's cores.
-  per_config    TFLOP/s and % of peak on all five GEMM workloads and the benchmark convolution
-                layer (timed the same way, fewer steps).
+  per_config    TFLOP/s and % of peak on all five GEMM workloads, the 8192³ product with fp16 and
+                with fp8 E4M3 inputs (against the fp8 peak), and the benchmark convolution layer
+                (timed the same way, fewer steps).
 """
 from __future__ import annotations
 
@@ -30,6 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz ("2.5 PF")
+PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": PEAK_BF16_TFLOPS,
+               "f8e4m3": 5033.2, "f8e5m2": 5033.2}  # dense fp8: 256 CU x 8192 flop/clk x 2.4 GHz ("5.0 PF")
 METRIC = "bf16 GEMM TFLOP/s and % of MI355X MFMA peak at M=N=K=8192, 1 GPU"
 KERNEL_SOURCES = ["tiled_bf16_gemm_amd/csrc/gemm_common.hpp", "tiled_bf16_gemm_amd/csrc/gemm_ring.hpp",
                   "tiled_bf16_gemm_amd/csrc/tile_loader.hpp"]
@@ -56,8 +59,10 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def time_gemm(torch, torch_ops, w, steps, warmup, config=None):
-    """Returns (ms per step over the whole timed region, mean per-launch ms from events)."""
+def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16"):
+    """Returns (ms per step over the whole timed region, mean per-launch ms from events, wall ms
+    per step).  ab: the input type; the workload's bf16 values are converted to it (8-bit inputs
+    take B stored N×K, transposed once here, outside the timed region)."""
     import workloads
     A, B = workloads.gemm_inputs(w)
     lda, ldb, ldc = w.lds()
@@ -65,19 +70,27 @@ def time_gemm(torch, torch_ops, w, steps, warmup, config=None):
     B = B.cuda()
     Av = A[:, :w.K]
     Bv = B[:, :w.N] if w.b_layout == "kn" else B[:, :w.K]
+    b_layout = w.b_layout
+    if ab != "bf16":
+        tdt = {"f16": torch.float16, "f8e4m3": torch.float8_e4m3fn, "f8e5m2": torch.float8_e5m2}[ab]
+        Av = Av.to(tdt)
+        if ab.startswith("f8") and b_layout == "kn":
+            Bv, b_layout = Bv.t().contiguous(), "nk"
+        Bv = Bv.to(tdt)
+        A, B = Av, Bv
     C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
     import tiled_bf16_gemm_amd as tbg
     need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
-        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws, config=config)
+        torch_ops.gemm(Av, Bv, b_layout, w.out_dtype, out=C, workspace=ws, config=config)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
-        torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws, config=config)
+        torch_ops.gemm(Av, Bv, b_layout, w.out_dtype, out=C, workspace=ws, config=config)
         ends[i].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
@@ -235,6 +248,12 @@ SWEEP_CONFIGS = ([("ring", "256x256", 2)] + [("ring", t, st) for t in ("256x128"
                  + [("producer", "128x128", st) for st in (2, 3, 4)]
                  + [("producer", "64x64", st) for st in range(2, 7)])
 
+# The fp16 and 8-bit configurations built (include/tbg.h, tbg_gemm_typed).
+SWEEP_CONFIGS_F16 = ([("ring", t, 2) for t in ("256x256", "256x128", "128x256", "128x128", "64x64")]
+                     + [("producer", t, 2) for t in ("256x128", "128x256")]
+                     + [("producer", t, 3) for t in ("128x128", "64x64")])
+SWEEP_CONFIGS_F8 = [("ring", t, 2) for t in ("256x256", "128x128", "64x64")]
+
 
 def sweep(torch, torch_ops, names, steps, warmup):
     """Time every built configuration on the named workloads; one JSON line per measurement."""
@@ -253,13 +272,20 @@ def sweep(torch, torch_ops, names, steps, warmup):
                 results.append(r)
             torch.cuda.empty_cache()
             continue
-        w = workloads.GEMMS[name]
-        for pipe, tile, st in SWEEP_CONFIGS:
+        wname, _, ab = name.partition("@")
+        ab = ab or "bf16"
+        w = workloads.GEMMS[wname]
+        configs = SWEEP_CONFIGS
+        if ab == "f16":
+            configs = SWEEP_CONFIGS_F16
+        elif ab.startswith("f8"):
+            configs = SWEEP_CONFIGS_F8
+        for pipe, tile, st in configs:
             cfg = tbg.gemm_config(tile, st, pipe)
-            ms, kms, _ = time_gemm(torch, torch_ops, w, steps, warmup, config=cfg)
+            ms, kms, _ = time_gemm(torch, torch_ops, w, steps, warmup, config=cfg, ab=ab)
             tf = w.flops / (ms * 1e-3) / 1e12
             r = {"workload": name, "pipeline": pipe, "tile": tile, "stages": st, "ms": round(ms, 5),
-                 "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+                 "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_TFLOPS[ab], 2)}
             print(json.dumps(r), flush=True)
             results.append(r)
         torch.cuda.empty_cache()
@@ -277,8 +303,9 @@ def main():
                     help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
     ap.add_argument("--sweep", default="",
-                    help="comma-separated workloads (c1..c5, conv_b): time every built pipeline/tile/stages configuration "
-                         "on each and print one JSON line per measurement instead of the bench line")
+                    help="comma-separated workloads (c1..c5, conv_b; a GEMM name may carry an input type, e.g. "
+                         "c4@f16, c4@f8e4m3): time every built pipeline/tile/stages configuration on each and print "
+                         "one JSON line per measurement instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the GEMM shards across GPUs "
@@ -314,6 +341,14 @@ def main():
         per_config["c4"] = {"M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "out": w.out_dtype,
                             "ms": round(ms_step, 5), "tflops": round(tflops, 2),
                             "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
+        for ab in ("f16", "f8e4m3"):
+            s_, _, _ = time_gemm(torch, torch_ops, w, 50, 50, ab=ab)
+            tf = w.flops / (s_ * 1e-3) / 1e12
+            per_config[f"c4_{ab}"] = {"M": w.M, "N": w.N, "K": w.K, "inputs": ab,
+                                      "b_layout": "nk" if ab.startswith("f8") else w.b_layout, "out": w.out_dtype,
+                                      "ms": round(s_, 5), "tflops": round(tf, 2), "peak": PEAK_TFLOPS[ab],
+                                      "pct_peak": round(100 * tf / PEAK_TFLOPS[ab], 2)}
+            torch.cuda.empty_cache()
         cw = workloads.CONVS["conv_b"]
         s_, _ = time_conv(torch, torch_ops, cw, 50, 20)
         tf = cw.flops / (s_ * 1e-3) / 1e12

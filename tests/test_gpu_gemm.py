@@ -478,6 +478,26 @@ def test_fp8_inputs(ops, orc, fmt):
 
 
 @gpu
+def test_fp8_torch_ops(ops, orc):
+    """torch_ops.gemm on float8 tensors: the same bits as tbg_gemm_typed, for dense rows and for
+    rows that the library repacks (K = 200, not a multiple of 16 bytes; a row view with pitch 210)."""
+    for fmt, tdt in (("f8e4m3", torch.float8_e4m3fn), ("f8e5m2", torch.float8_e5m2)):
+        for M, N, K, pitch in ((300, 260, 512, 512), (130, 90, 200, 210)):
+            A8, Av = _f8(M, pitch, 1700, fmt)
+            B8, Bv = _f8(N, pitch, 1701, fmt)
+            _say(f"torch_ops {fmt} M={M} N={N} K={K} pitch {pitch}")
+            want = _run_f8(M, N, K, A8, B8, fmt, "f32", lda=pitch, ldb=pitch)[:, :N]
+            At, Bt = A8.cuda().view(tdt)[:, :K], B8.cuda().view(tdt)[:, :K]
+            got = ops.gemm(At, Bt, "nk", "f32")
+            torch.cuda.synchronize()
+            assert np.array_equal(got.cpu().numpy(), want), (fmt, M, N, K)
+            ref = orc.gemm_f8(A8.numpy(), B8.numpy(), M, N, K, pitch, pitch, "e4m3" if fmt == "f8e4m3" else "e5m2")
+            _check_f8(want, ref, Av[:, :K].numpy(), Bv[:, :K].numpy(), f"{fmt} torch_ops")
+        with pytest.raises(Exception):
+            ops.gemm(At, Bt.t(), "kn", "f32")
+
+
+@gpu
 def test_fp8_large_sampled(ops, orc):
     """The 16384×14336×4096 product (the MLP workload's shape) with E4M3 inputs: sampled rows
     against the oracle, finite everywhere, deterministic."""

@@ -73,6 +73,7 @@ MUTANTS = [
     ("f8 product reads B transposed", "acc += f8_to_f64(A[m * lda + k], fmt) * f8_to_f64(B[n * ldb + k], fmt);",
      "acc += f8_to_f64(A[m * lda + k], fmt) * f8_to_f64(B[k * ldb + n], fmt);"),
     ("convolution drops the last channel", "for (int64_t c = 0; c < C; ++c) acc +=", "for (int64_t c = 0; c + 1 < C; ++c) acc +="),
+    ("e5m2 NaN fill writes infinity", "else if (nan_kind == 5) { fill[0] = 0x7E; }", "else if (nan_kind == 5) { fill[0] = 0x7C; }"),
 ]
 
 

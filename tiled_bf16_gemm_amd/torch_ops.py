@@ -8,6 +8,7 @@ import torch
 
 import tiled_bf16_gemm_amd as tbg
 
+_AB_OF = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float8_e4m3fn: "f8e4m3", torch.float8_e5m2: "f8e5m2"}
 _TORCH_OF = {"u8": torch.uint8, "u16": torch.int16, "u32": torch.int32, "f16": torch.float16,
              "bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -29,15 +30,15 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
          stream: Optional[torch.cuda.Stream] = None, alpha: float = 1.0, beta: float = 0.0,
          config: Optional[tbg.GemmConfig] = None) -> torch.Tensor:
     """C = alpha·A·B + beta·C through tbg_gemm (alpha = 1, beta = 0), tbg_gemm_ex, or
-    tbg_gemm_configured when `config` (tbg.gemm_config(...)) is given; fp16 operands go through
-    tbg_gemm_typed.  A: (M, K) bf16 or fp16 view; B:
-    (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading dimensions.  `out` (M, N)
-    may be a strided view; with beta != 0 it must hold the old C."""
+    tbg_gemm_configured when `config` (tbg.gemm_config(...)) is given; fp16 and 8-bit float
+    operands (float8_e4m3fn, float8_e5m2; B stored "nk" only) go through tbg_gemm_typed.
+    A: (M, K) view; B: (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading
+    dimensions.  `out` (M, N) may be a strided view; with beta != 0 it must hold the old C."""
     _require(A, "A")
     _require(B, "B")
-    if A.dtype not in (torch.bfloat16, torch.float16) or B.dtype != A.dtype:
-        raise ValueError("A and B must both be bfloat16 or both float16")
-    ab = "bf16" if A.dtype == torch.bfloat16 else "f16"
+    ab = _AB_OF.get(A.dtype)
+    if ab is None or B.dtype != A.dtype:
+        raise ValueError("A and B must have the same dtype: bfloat16, float16, float8_e4m3fn or float8_e5m2")
     M, K = A.shape
     if b_layout == "kn":
         Kb, N = B.shape
@@ -50,7 +51,14 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
     _require(out, "out")
     lda, ldb, ldc = A.stride(0), B.stride(0), out.stride(0)
     need = tbg.gemm_workspace_bytes(M, N, K, lda, ldb, b_layout)
-    if (A.data_ptr() % 16) or (B.data_ptr() % 16):
+    if ab.startswith("f8"):
+        # 8-bit rows whose pitch or K is not a multiple of 16 bytes, or that start off a 16-byte
+        # boundary, are repacked with their K rounded up to 16
+        k16 = (max(K, 1) + 15) // 16 * 16
+        pack = lambda ld, t: K > 0 and (ld % 16 or K % 16 or t.data_ptr() % 16)  # noqa: E731
+        need = (((M * k16 + 255) // 256 * 256) if pack(lda, A) else 0) + \
+            (((N * k16 + 255) // 256 * 256) if pack(ldb, B) else 0)
+    elif (A.data_ptr() % 16) or (B.data_ptr() % 16):
         # an operand that starts off a 16-byte boundary is repacked too
         rows_a, rows_b = M, (K if b_layout == "kn" else N)
         kext = (K + 7) // 8 * 8
@@ -60,7 +68,7 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if ab == "f16":
+    if ab != "bf16":
         tbg.gemm_typed(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, ab, beta, out.data_ptr(), ldc,
                        out_dtype, config, ws_ptr, ws_bytes, stream_handle(stream))
     elif config is not None:
