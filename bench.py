@@ -188,7 +188,8 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
     gemm_name = "gemm_ring_kernel"
     top = rows(trace_db, "select name, total_calls, total_duration, average, percentage from top_kernels")
     lines = ["# GEMM kernel trace, 8192^3 workload (bf16 in, fp32 accumulate, bf16 out)", "",
-             "Command (<repo> is the repository root on the GPU box):", "", "```", commands["trace"], "```", "",
+             "Command (<repo> is the repository root, <out> the output folder):", "", "```", commands["trace"], "```", "",
+             "Summary written by `python bench.py --summarize <out>`.", "",
              "rocprofv3 kernel statistics (durations in microseconds):", "",
              "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
     for name, calls, total, avg, pct in top:
@@ -218,8 +219,9 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
     total = fb + wb
     algo = 2 * 8192 * 8192 * 2 + 8192 * 8192 * 2
     lines = ["# HBM traffic of the GEMM kernel, 8192^3 workload", "",
-             "Commands (one counter per run; <repo> is the repository root on the GPU box):", "", "```",
+             "Commands (one counter per run; <repo> is the repository root, <out> the output folder):", "", "```",
              commands["fetch"], commands["write"], "```", "",
+             "Summary written by `python bench.py --summarize <out>`.", "",
              "Calibration: the same runs end with five device copies of 536870912 bytes (`__amd_rocclr_copyBuffer`)",
              "that read and write exactly that many bytes; each counter is scaled by bytes/counter of that copy.", "",
              "| kernel | counter | median KiB per dispatch | dispatches | scale | bytes per dispatch |",
@@ -302,6 +304,12 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
+    ap.add_argument("--summarize", default="", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 runs under DIR (DIR/trace, DIR/fetch, "
+                         "DIR/write, each made with -o run as the summaries' commands show); runs on any host, "
+                         "no GPU needed")
+    ap.add_argument("--bench-kernel-us", type=float, default=None,
+                    help="with --summarize: the bench line's HIP-event kernel average, quoted beside the trace")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workloads (c1..c5, conv_b; a GEMM name may carry an input type, e.g. "
                          "c4@f16, c4@f8e4m3): time every built pipeline/tile/stages configuration on each and print "
@@ -312,6 +320,22 @@ def main():
               "by rows or columns of C with no exchange, which this single-GPU build does not run.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize:
+        d = args.summarize
+        cmds = {
+            "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/trace -o run -- "
+                     "python -u <repo>/bench.py --no-cpu-baseline --no-configs",
+            "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE -d <out>/fetch -o run -- "
+                     "python -u <repo>/bench.py --counters",
+            "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE -d <out>/write -o run -- "
+                     "python -u <repo>/bench.py --counters",
+            "bench_kernel_us": args.bench_kernel_us,
+        }
+        t = summarize_profiles(os.path.join(d, "trace", "run_results.db"), os.path.join(d, "fetch", "run_results.db"),
+                               os.path.join(d, "write", "run_results.db"), os.path.join(ROOT, "profiles"), cmds)
+        print(json.dumps(t))
+        return
 
     import torch
     from tiled_bf16_gemm_amd import torch_ops
