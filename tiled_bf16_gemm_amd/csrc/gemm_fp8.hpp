@@ -10,13 +10,12 @@
 //    32 bytes per lane: lane l supplies row l%16 of its fragment and bytes 32(l/16)..+31 of the
 //    tile's row (two ds_read_b128).  The instruction sums over all 128 k of the two operands;
 //    since A and B use the same byte-to-k placement, every k of A meets the same k of B;
-//  * the products run A-fragment outermost: a wave's 8 B fragments stay live for the whole tile,
-//    the next tile's B fragments are read in the first half and each next A fragment right
-//    after the last product that uses the current one, so one tile's fragments plus the next
-//    tile's B fragments fit the register file next to the accumulators;
-//  * one barrier per K tile: it publishes tile kt+1 and frees the stage of tile kt, whose
-//    fragments were all read during the previous tile.  The loop runs pairs of tiles; an odd
-//    tile count adds one tile of zeros (fully masked copies) to the products.
+//  * the products run A-fragment outermost: a wave's B fragments stay live for the whole tile and
+//    half of its A fragments die in the first half, so one tile's fragments plus the next
+//    tile's B fragments and first A fragments fit the register file next to the accumulators;
+//  * one barrier per K tile, in its middle (ktile8): it publishes tile kt+1 and frees the stage
+//    of tile kt.  The loop runs pairs of tiles; an odd tile count adds one tile of zeros (fully
+//    masked copies) to the products.
 // The operands are handed over as 16-bit pairs (GemmParams in units of two fp8 values), so the
 // copy helpers are the bf16 kernels' own.
 #pragma once
@@ -83,26 +82,43 @@ __device__ __forceinline__ i32x8_t read_frag8(const uint8_t* base, uint32_t lane
   return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// The products of one K tile on `cur`, with the next tile's fragment reads and (later tiles')
-// copy atoms interleaved: B reads over the first half, A fragment fm right after its last
-// product, copy atoms spread evenly.
+// One K tile on `cur` (held in stage sCur), in two halves around the stage barrier:
+//   first half   the products on A fragments 0..H-1 (H = FM/2), with this tile's remaining A
+//                fragments H..FM-1 read from sCur;
+//   barrier      this wave's copies of tile kt+1 have landed (vmcnt 0: nothing newer is in flight
+//                yet) and every wave's reads of sCur have completed, so tile kt+1 is visible and
+//                sCur is free;
+//   second half  the products on A fragments H..FM-1, with tile kt+1's B fragments and its A
+//                fragments 0..H-1 read from sNxt, and tile kt+2's copy atoms into sCur.
+// A copy so has from the middle of the tile it is issued in to the middle of the next one to
+// land, and no fragment is read before its tile is known to be complete.
 template <class T, int FMT>
-__device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], const Frags8<T>& cur, Frags8<T>& nxt,
-                                       const FragAddr8& fa, const uint8_t* nA, const uint8_t* nB, const TileCopy& tc,
-                                       const LaneChunk* la, const LaneChunk* lb) {
-  constexpr int P = T::Products, A = T::Atoms, FN = T::FN, FM = T::FM;
+__device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], Frags8<T>& cur, Frags8<T>& nxt,
+                                       const FragAddr8& fa, const uint8_t* sCurA, const uint8_t* sNxtA,
+                                       const uint8_t* sNxtB, const TileCopy& tc, const LaneChunk* la,
+                                       const LaneChunk* lb) {
+  constexpr int A = T::Atoms, FN = T::FN, FM = T::FM, H = FM / 2;
+  constexpr int P0 = H * FN, P1 = T::Products - P0, NR = FN + H;
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
+  for (int i = 0; i < P0; ++i) {
     const int fm = i / FN, fn = i % FN;
-    // B read j before product (j * P/2) / FN
+    if (fn == 0) cur.a[H + fm] = read_frag8(sCurA, fa.a_lane + (H + fm) * 2048, fa.a_col);
+    mfma8<T::AsmMfma, false, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+  }
+  stage_barrier<0>();
 #pragma unroll
-    for (int j = (2 * i * FN + P - 1) / P; j < (2 * (i + 1) * FN + P - 1) / P && j < FN; ++j)
-      nxt.b[j] = read_frag8(nB, fa.b_lane + j * 2048, fa.b_col);
+  for (int i = 0; i < P1; ++i) {
+    const int fm = H + i / FN, fn = i % FN;
+    // fragment read q (B first, then A 0..H-1) before product (q * P1) / NR; atom j before (j * P1) / A
 #pragma unroll
-    for (int j = (i * A + P - 1) / P; j < ((i + 1) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
-    if (i == P - 1) mfma8<T::AsmMfma, true, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    for (int q = (i * NR + P1 - 1) / P1; q < ((i + 1) * NR + P1 - 1) / P1 && q < NR; ++q) {
+      if (q < FN) nxt.b[q] = read_frag8(sNxtB, fa.b_lane + q * 2048, fa.b_col);
+      else nxt.a[q - FN] = read_frag8(sNxtA, fa.a_lane + (q - FN) * 2048, fa.a_col);
+    }
+#pragma unroll
+    for (int j = (i * A + P1 - 1) / P1; j < ((i + 1) * A + P1 - 1) / P1 && j < A; ++j) copy_atom<T>(tc, la, lb, j);
+    if (i == P1 - 1) mfma8<T::AsmMfma, true, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
     else mfma8<T::AsmMfma, false, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
-    if (fn == FN - 1) nxt.a[fm] = read_frag8(nA, fa.a_lane + fm * 2048, fa.a_col);
   }
 }
 
@@ -152,21 +168,17 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
 #pragma unroll
       for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
     }
-    stage_barrier<T::Atoms>();  // tile 0 landed
+    stage_barrier<T::Atoms>();  // tile 0 landed; tile 1 may be in flight
 #pragma unroll
-    for (int j = 0; j < T::FM; ++j) f0.a[j] = read_frag8(smem, fa.a_lane + j * 2048, fa.a_col);
+    for (int j = 0; j < T::FM / 2; ++j) f0.a[j] = read_frag8(smem, fa.a_lane + j * 2048, fa.a_col);
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) f0.b[j] = read_frag8(smem + T::ABytes, fa.b_lane + j * 2048, fa.b_col);
+    const uint8_t* s1 = smem + T::StageBytes;
     for (int kt = 0; kt < ktiles; kt += 2) {
-      // tile kt (stage 0) with tile kt+1's reads (stage 1) and tile kt+2's copies (stage 0)
-      stage_barrier<0>();
-      {
-        const uint8_t* nA = smem + T::StageBytes;
-        ktile8<T, FMT>(acc, f0, f1, fa, nA, nA + T::ABytes, make_copy(kt + 2, 0), la, lb);
-      }
-      // tile kt+1 (stage 1) with tile kt+2's reads (stage 0) and tile kt+3's copies (stage 1)
-      stage_barrier<0>();
-      ktile8<T, FMT>(acc, f1, f0, fa, smem, smem + T::ABytes, make_copy(kt + 3, 1), la, lb);
+      // tile kt (stage 0); tile kt+1's first fragments from stage 1; tile kt+2's copies into stage 0
+      ktile8<T, FMT>(acc, f0, f1, fa, smem, s1, s1 + T::ABytes, make_copy(kt + 2, 0), la, lb);
+      // tile kt+1 (stage 1); tile kt+2's first fragments from stage 0; tile kt+3's copies into stage 1
+      ktile8<T, FMT>(acc, f1, f0, fa, s1, smem, smem + T::ABytes, make_copy(kt + 3, 1), la, lb);
     }
   }
   stage_barrier<0>();
