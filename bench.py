@@ -164,15 +164,24 @@ def counters_driver(torch, torch_ops, w):
     for _ in range(5):
         torch_ops.gemm(A, B, w.b_layout, w.out_dtype, out=C)
     torch.cuda.synchronize()
+    # the same product with E4M3 inputs (B stored N×K), for the fp8 kernel's counters
+    A8 = A.to(torch.float8_e4m3fn)
+    B8 = B.t().contiguous().to(torch.float8_e4m3fn)
+    for _ in range(5):
+        torch_ops.gemm(A8, B8, "nk", w.out_dtype, out=C)
+    torch.cuda.synchronize()
+    del A8, B8
     src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print("counters driver: 5 gemm launches (8192^3), 5 copies of 536870912 bytes", flush=True)
+    print("counters driver: 5 gemm launches (8192^3 bf16), 5 with E4M3 inputs, 5 copies of 536870912 bytes",
+          flush=True)
 
 
-def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str, commands: dict) -> dict:
+def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str, commands: dict,
+                       sq_db: str = "") -> dict:
     """Write the short text summaries of rocprofv3 runs into profiles/ (and the traffic figure
     bench.py reports).  Reads rocprofv3's SQLite output with the standard library only."""
     import sqlite3
@@ -240,7 +249,60 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
                "algorithmic_bytes": algo, "gemm_trace_avg_us": gemm_avg[0] if gemm_avg else None}
     with open(os.path.join(out_dir, "gemm_8192_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
+    if sq_db and os.path.exists(sq_db):
+        summarize_sq(sq_db, out_dir, commands["sq"])
     return traffic
+
+
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+               "SQ_INSTS_MFMA", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_sq(db: str, out_dir: str, command: str) -> None:
+    """MFMA utilisation and LDS bank conflicts of the GEMM kernels from one rocprofv3 --pmc run.
+
+    SQ_VALU_MFMA_BUSY_CYCLES counts busy cycles of every SIMD's matrix unit, SQ_BUSY_CU_CYCLES
+    busy cycles of every CU (4 SIMDs each): their ratio / 4 is the fraction of the kernel's
+    cycles the matrix units worked, at whatever clock the chip ran.  SQ_LDS_BANK_CONFLICT and
+    SQ_LDS_IDX_ACTIVE are cycles, summed over CUs, so they divide by SQ_BUSY_CU_CYCLES.
+    SQ_WAIT_ANY and SQ_WAVE_CYCLES are per wave (same units), their ratio the waiting share."""
+    import sqlite3
+    import statistics
+    c = sqlite3.connect(db)
+    try:
+        rows = list(c.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"))
+    finally:
+        c.close()
+    per = {}
+    for name, disp, cn, v in rows:
+        if "gemm_" not in name:
+            continue
+        per.setdefault(name, {}).setdefault(disp, {})[cn] = v
+    lines = ["# MFMA utilisation and LDS bank conflicts of the GEMM kernels, 8192^3", "",
+             "Command (<repo> is the repository root, <out> the output folder):", "", "```", command, "```", "",
+             "Summary written by `python bench.py --summarize <out>`.  Medians over the dispatches.", "",
+             "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 × SQ_BUSY_CU_CYCLES): the share of CU-busy cycles the",
+             "  matrix units worked, at the clock the chip actually ran (the % of the 2.4 GHz peak is lower",
+             "  by the clock ratio);",
+             "- bank conflict = SQ_LDS_BANK_CONFLICT / SQ_BUSY_CU_CYCLES; LDS active = SQ_LDS_IDX_ACTIVE / the same;",
+             "- waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (waves at s_waitcnt or s_barrier);",
+             "- MFMA instructions: SQ_INSTS_MFMA per dispatch (2MNK / flops per instruction: 16x16x32 bf16",
+             "  16384, 16x16x128 fp8 65536).", "",
+             "| kernel | dispatches | MFMA busy | bank conflict | LDS active | waiting | MFMA instructions |",
+             "|---|---|---|---|---|---|---|"]
+    for name, disps in per.items():
+        def med(f):
+            vals = [f(d) for d in disps.values() if all(k in d for k in SQ_COUNTERS[:7])]
+            return statistics.median(vals) if vals else float("nan")
+        mf = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * d["SQ_BUSY_CU_CYCLES"]))
+        bc = med(lambda d: d["SQ_LDS_BANK_CONFLICT"] / d["SQ_BUSY_CU_CYCLES"])
+        la = med(lambda d: d["SQ_LDS_IDX_ACTIVE"] / d["SQ_BUSY_CU_CYCLES"])
+        wt = med(lambda d: d["SQ_WAIT_ANY"] / d["SQ_WAVE_CYCLES"])
+        ni = med(lambda d: d["SQ_INSTS_MFMA"])
+        lines.append(f"| `{name}` | {len(disps)} | {100 * mf:.1f} % | {100 * bc:.1f} % | {100 * la:.1f} % | "
+                     f"{100 * wt:.1f} % | {ni:.4g} |")
+    with open(os.path.join(out_dir, "gemm_8192_mfma_lds_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 # Every built (pipeline, tile, stages) configuration, as include/tbg.h lists them.
@@ -306,8 +368,8 @@ def main():
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
     ap.add_argument("--summarize", default="", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 runs under DIR (DIR/trace, DIR/fetch, "
-                         "DIR/write, each made with -o run as the summaries' commands show); runs on any host, "
-                         "no GPU needed")
+                         "DIR/write and optionally DIR/sq, each made with -o run as the summaries' commands show); "
+                         "runs on any host, no GPU needed")
     ap.add_argument("--bench-kernel-us", type=float, default=None,
                     help="with --summarize: the bench line's HIP-event kernel average, quoted beside the trace")
     ap.add_argument("--sweep", default="",
@@ -330,10 +392,13 @@ def main():
                      "python -u <repo>/bench.py --counters",
             "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE -d <out>/write -o run -- "
                      "python -u <repo>/bench.py --counters",
+            "sq": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " -d <out>/sq -o run -- "
+                  "python -u <repo>/bench.py --counters",
             "bench_kernel_us": args.bench_kernel_us,
         }
         t = summarize_profiles(os.path.join(d, "trace", "run_results.db"), os.path.join(d, "fetch", "run_results.db"),
-                               os.path.join(d, "write", "run_results.db"), os.path.join(ROOT, "profiles"), cmds)
+                               os.path.join(d, "write", "run_results.db"), os.path.join(ROOT, "profiles"), cmds,
+                               os.path.join(d, "sq", "run_results.db"))
         print(json.dumps(t))
         return
 

@@ -14,9 +14,13 @@
 //    (BM/2)×(BN/2) block of C whose 16×16 fp32 accumulator fragments stay in registers for the
 //    whole K loop (256 per lane at 256×256);
 //  * a ring stage holds the A box {64 k, BM m} with the 2-row swizzle, then B: stored N×K the
-//    same way, stored K×N as BN/64 boxes {64 n, 64 k} with the 128B swizzle;
+//    same way, stored K×N as BN/64 boxes {64 n, 64 k} in the K×N layout (kSwizzleKnTr);
 //  * fragments come from LDS with ds_read_b128 (k-contiguous rows) or, for B stored K×N, with
-//    ds_read_b64_tr_b16, which transposes 4×16 blocks of 16-bit values across 16 lanes;
+//    ds_read_b64_tr_b16, which transposes 4×16 blocks of 16-bit values across 16 lanes.  Both
+//    layouts are chosen so that every fragment read is free of LDS bank conflicts (measured
+//    with the counters and a read micro-benchmark: the 16-byte reads here are conflict-free
+//    with the 2-row swizzle; the 8-byte transposing read is served 32 lanes at a time from 256
+//    bytes and needs the K×N layout);
 //  * v_mfma_f32_16x16x32_bf16 with the operands swapped (B fragment first), so each lane ends
 //    with four consecutive columns of one row of C; the epilogue regroups them through LDS into
 //    whole-row 16-byte stores, masked at the M and N edges.
@@ -398,7 +402,7 @@ __device__ __forceinline__ FragAddr<T> make_frag_addr(int wm, int wn, int lane) 
       const int f4 = T::TN >= 64 ? q : 2 * wn + q;
       const int r = 8 * tg + 4 * h + te;  // row within a 32-row k step
       const int c = f4 * 2 + (tq >> 1);
-      fa.b_tr[q][h] = (uint32_t)r * 128u + (uint32_t)((c ^ (r & 7)) * 16) + (uint32_t)((tq & 1) * 8);
+      fa.b_tr[q][h] = (uint32_t)r * 128u + (uint32_t)((c ^ row_xor<kSwizzleKnTr>(r)) * 16) + (uint32_t)((tq & 1) * 8);
     }
   fa.wn = wn;
   return fa;

@@ -81,7 +81,7 @@ __device__ __forceinline__ void produce(const GemmParams& p, const uint8_t* smem
       ch[i] = lane_chunk<kSwizzle128B2Row>(8 * (j - BM / 8), lane, pitch_b);
     } else {
       const int jb = j - BM / 8;
-      ch[i] = lane_chunk<3>(8 * (jb & 7), lane, pitch_b);
+      ch[i] = lane_chunk<kSwizzleKnTr>(8 * (jb & 7), lane, pitch_b);
       ch[i].offset += 128u * (uint32_t)(jb >> 3);
     }
   }

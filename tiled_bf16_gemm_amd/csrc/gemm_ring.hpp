@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   // ---- copies: each wave copies AtomsA atoms (1 KiB each) of A and AtomsB of B per K tile ----
   // A: box {64 k, BM m} at (k0, m0), 2-row swizzle; this wave owns box rows (BM/4)*wave .. +BM/4-1.
   // B stored N×K: the same with n.  B stored K×N: BN/64 boxes {64 n, 64 k} at (n0 + 64*b, k0),
-  // 128B swizzle, 8 atoms each; this wave owns atoms AtomsB*wave .. +AtomsB-1 of the boxes in
+  // K×N layout (kSwizzleKnTr), 8 atoms each; this wave owns atoms AtomsB*wave .. +AtomsB-1 of the boxes in
   // order, all inside one box.
   const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
   const int b_box = (wave * T::AtomsB) >> 3;  // K×N box of this wave's B atoms
@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
     if (BL == 1) {
       lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
     } else {
-      lb[i] = lane_chunk<3>(8 * ((wave * T::AtomsB + i) & 7), lane, pitch_b);
+      lb[i] = lane_chunk<kSwizzleKnTr>(8 * ((wave * T::AtomsB + i) & 7), lane, pitch_b);
       lb[i].offset += 128u * b_box;
     }
   }

@@ -34,8 +34,10 @@ __host__ __device__ __forceinline__ uint32_t swizzle_offset(uint32_t a, int mode
 // For images made of 128-byte rows: the XOR applied to the 16-byte chunk index of row r.
 template <int SWZ>
 __device__ __forceinline__ int row_xor(int r) {
-  static_assert(SWZ == 3 || SWZ == 4, "128-byte-row loader takes the 128B or 2-row swizzle");
-  return SWZ == 3 ? (r & 7) : ((r >> 1) & 7);
+  static_assert(SWZ == 3 || SWZ == 4 || SWZ == 5, "128-byte-row loader takes the 128B, 2-row or K×N layout");
+  if (SWZ == 3) return r & 7;
+  if (SWZ == 4) return (r >> 1) & 7;
+  return (((r >> 3) & 1) << 2) | (((r >> 1) & 1) << 1) | ((r >> 2) & 1);
 }
 
 // ---- buffer resources --------------------------------------------------------------------
