@@ -534,18 +534,21 @@ tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const voi
   const uint8_t* Bb = (const uint8_t*)B;
   int64_t lda_b = lda, ldb_b = ldb;
   hipError_t e = hipSuccess;
+  tbg::PackJob jobs[2];
+  int njobs = 0;
   if (pack_a) {
     uint8_t* dst = (uint8_t*)workspace;
-    e = tbg::launch_pack_bytes(Ab, lda, M, K, dst, k16, s);
+    jobs[njobs++] = tbg::PackJob{Ab, lda, M, K, dst, k16};
     Ab = dst;
     lda_b = k16;
   }
-  if (e == hipSuccess && pack_b) {
+  if (pack_b) {
     uint8_t* dst = (uint8_t*)workspace + a_bytes;
-    e = tbg::launch_pack_bytes(Bb, ldb, N, K, dst, k16, s);
+    jobs[njobs++] = tbg::PackJob{Bb, ldb, N, K, dst, k16};
     Bb = dst;
     ldb_b = k16;
   }
+  e = tbg::launch_pack_jobs(jobs, njobs, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "fp8 repack: %s", hipGetErrorString(e));
   tbg::GemmParams p;
   memset(&p, 0, sizeof(p));
@@ -659,21 +662,23 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   const uint16_t* Be = (const uint16_t*)B;
   int64_t lda_e = lda, ldb_e = ldb;
   hipError_t e = hipSuccess;
+  tbg::PackJob jobs[2];
+  int njobs = 0;
   if (pl.pack_a) {
     uint16_t* dst = (uint16_t*)workspace;
-    e = tbg::launch_pack((const uint16_t*)A, lda, M, K, dst, pl.lda_p, s);
-    if (e != hipSuccess) return fail(TBG_ERR_HIP, "pack A: %s", hipGetErrorString(e));
+    jobs[njobs++] = tbg::PackJob{(const uint8_t*)A, lda * 2, M, K * 2, (uint8_t*)dst, pl.lda_p * 2};
     Ae = dst;
     lda_e = pl.lda_p;
   }
   if (pl.pack_b) {
     uint16_t* dst = (uint16_t*)((uint8_t*)workspace + pl.a_bytes);
-    if (bl == TBG_B_NK) e = tbg::launch_pack((const uint16_t*)B, ldb, N, K, dst, pl.ldb_p, s);
-    else e = tbg::launch_pack((const uint16_t*)B, ldb, K, N, dst, pl.ldb_p, s);
-    if (e != hipSuccess) return fail(TBG_ERR_HIP, "pack B: %s", hipGetErrorString(e));
+    const int64_t rows = bl == TBG_B_NK ? N : K, cols = bl == TBG_B_NK ? K : N;
+    jobs[njobs++] = tbg::PackJob{(const uint8_t*)B, ldb * 2, rows, cols * 2, (uint8_t*)dst, pl.ldb_p * 2};
     Be = dst;
     ldb_e = pl.ldb_p;
   }
+  e = tbg::launch_pack_jobs(jobs, njobs, s);
+  if (e != hipSuccess) return fail(TBG_ERR_HIP, "operand repack: %s", hipGetErrorString(e));
   tbg::GemmParams p;
   p.A = Ae;
   p.B = Be;
@@ -848,8 +853,10 @@ tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void
   if (pl.pack) {
     uint16_t* xp = (uint16_t*)workspace;
     uint16_t* wp = (uint16_t*)((uint8_t*)workspace + pl.x_bytes);
-    e = tbg::launch_pack(X, shape->c, shape->n * shape->h * shape->w, shape->c, xp, pl.c8, s);
-    if (e == hipSuccess) e = tbg::launch_pack(W, shape->c, shape->k * shape->r * shape->s, shape->c, wp, pl.c8, s);
+    const tbg::PackJob jobs[2] = {
+        {(const uint8_t*)X, shape->c * 2, shape->n * shape->h * shape->w, shape->c * 2, (uint8_t*)xp, pl.c8 * 2},
+        {(const uint8_t*)W, shape->c * 2, shape->k * shape->r * shape->s, shape->c * 2, (uint8_t*)wp, pl.c8 * 2}};
+    e = tbg::launch_pack_jobs(jobs, 2, s);
     if (e != hipSuccess) return fail(TBG_ERR_HIP, "channel repack: %s", hipGetErrorString(e));
     X = xp;
     W = wp;

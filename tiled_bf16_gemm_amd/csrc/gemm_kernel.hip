@@ -13,67 +13,60 @@
 
 namespace tbg {
 
-// Copy `rows` rows of `cols` bf16 values into a buffer of pitch ld_dst (a multiple of 8),
-// zero-filling columns cols..ld_dst-1: the packing step for operands whose rows are not 16-byte
-// aligned ("GEMM" page: packing a block into a contiguous area before use; 16-byte alignment of
-// the leading dimension, section "In pratica").
-__global__ void __launch_bounds__(256) pack_rows_kernel(const uint16_t* src, int64_t ld_src, int64_t rows,
-                                                        int64_t cols, uint16_t* dst, int64_t ld_dst) {
-  const int64_t cpr = ld_dst / 8;
-  const int64_t total = rows * cpr;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = idx / cpr;
-    const int64_t c0 = (idx - r * cpr) * 8;
-    uint16_t v[8];
+// The packing step for operands whose rows are not 16-byte aligned ("GEMM" page: packing a block
+// into a contiguous area before use; 16-byte alignment of the leading dimension, section "In
+// pratica"): copy `rows` rows of `row_bytes` bytes into a buffer of pitch `ld_dst` bytes (a
+// multiple of 16), zero-filling bytes row_bytes..ld_dst-1.  One thread per 16-byte chunk of the
+// destination: it reads the aligned dwords that hold the chunk's source bytes (the source may sit
+// at any byte alignment) and funnel-shifts them into place; a chunk within 20 bytes of its row's
+// end goes byte by byte, so no read leaves the row.  Blocks of 64 chunks × 4 rows; blockIdx.z
+// picks the repack, so both operands of a product are packed by one launch.
+__device__ __forceinline__ uint4 load16_unaligned(const uint8_t* p) {
+  const uintptr_t a = (uintptr_t)p;
+  const uint32_t* q = (const uint32_t*)(a & ~(uintptr_t)3);
+  const uint32_t sh = (uint32_t)(a & 3);
+  const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+  if (sh == 0) return make_uint4(w0, w1, w2, w3);
+  const uint32_t w4 = q[4];
+  return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
+                    __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
+}
+
+__global__ void __launch_bounds__(256) pack_rows_kernel(PackJob j0, PackJob j1) {
+  const PackJob j = blockIdx.z == 0 ? j0 : j1;
+  const int64_t cpr = j.ld_dst / 16;
+  for (int64_t r = (int64_t)blockIdx.y * 4 + threadIdx.y; r < j.rows; r += (int64_t)gridDim.y * 4) {
+    const uint8_t* srow = j.src + r * j.ld_src;
+    uint8_t* drow = j.dst + r * j.ld_dst;
+    for (int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x; c < cpr; c += (int64_t)gridDim.x * 64) {
+      const int64_t b0 = c * 16;
+      uint4 v;
+      if (b0 + 20 <= j.row_bytes) {
+        v = load16_unaligned(srow + b0);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (c0 + j < cols) ? src[r * ld_src + c0 + j] : (uint16_t)0;
-    uint4 w;
-    w.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-    w.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-    w.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-    w.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-    *(uint4*)(dst + r * ld_dst + c0) = w;
+        for (int k = 0; k < 16; ++k)
+          if (b0 + k < j.row_bytes) w[k >> 2] |= (uint32_t)srow[b0 + k] << (8 * (k & 3));
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      *(uint4*)(drow + b0) = v;
+    }
   }
 }
 
-hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ld_dst,
-                       hipStream_t stream) {
-  const int64_t total = rows * (ld_dst / 8);
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, ld_src, rows, cols, dst,
-                     ld_dst);
-  return hipGetLastError();
-}
-
-// Byte rows: copy `rows` rows of `cols` bytes into a buffer of pitch ld_dst (a multiple of 16),
-// zero-filling bytes cols..ld_dst-1 (the packing step for 8-bit operands).
-__global__ void __launch_bounds__(256) pack_bytes_kernel(const uint8_t* src, int64_t ld_src, int64_t rows,
-                                                         int64_t cols, uint8_t* dst, int64_t ld_dst) {
-  const int64_t cpr = ld_dst / 16;
-  const int64_t total = rows * cpr;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = idx / cpr;
-    const int64_t c0 = (idx - r * cpr) * 16;
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (c0 + j < cols) w[j >> 2] |= (uint32_t)src[r * ld_src + c0 + j] << (8 * (j & 3));
-    *(uint4*)(dst + r * ld_dst + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+hipError_t launch_pack_jobs(const PackJob* jobs, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t gx = 1, gy = 1;
+  for (int i = 0; i < n; ++i) {
+    const int64_t x = (jobs[i].ld_dst / 16 + 63) / 64, y = (jobs[i].rows + 3) / 4;
+    if (x > gx) gx = x;
+    if (y > gy) gy = y;
   }
-}
-
-hipError_t launch_pack_bytes(const uint8_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint8_t* dst,
-                             int64_t ld_dst, hipStream_t stream) {
-  const int64_t total = rows * (ld_dst / 16);
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(pack_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, ld_src, rows, cols, dst,
-                     ld_dst);
+  if (gx > 4096) gx = 4096;
+  if (gy > 65535) gy = 65535;
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)n), dim3(64, 4), 0, stream, jobs[0],
+                     n > 1 ? jobs[1] : jobs[0]);
   return hipGetLastError();
 }
 

@@ -75,10 +75,16 @@ bool choose_gemm(int64_t M, int64_t N, int num_cus, int pipeline, int bm, int bn
 // configuration find_gemm does not know.
 hipError_t launch_gemm(GemmParams p, int pipeline, int bm, int bn, int stages, int b_layout, int out_bf16,
                        hipStream_t stream, int in = 0);
-hipError_t launch_pack(const uint16_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ld_dst,
-                       hipStream_t stream);
-hipError_t launch_pack_bytes(const uint8_t* src, int64_t ld_src, int64_t rows, int64_t cols, uint8_t* dst,
-                             int64_t ld_dst, hipStream_t stream);
+// One repack: `rows` rows of `row_bytes` bytes at pitch ld_src (bytes, any alignment) into
+// pitch ld_dst (bytes, a multiple of 16), zero-filled past row_bytes.
+struct PackJob {
+  const uint8_t* src;
+  int64_t ld_src, rows, row_bytes;
+  uint8_t* dst;
+  int64_t ld_dst;
+};
+// Runs n (1 or 2) repacks in one launch.
+hipError_t launch_pack_jobs(const PackJob* jobs, int n, hipStream_t stream);
 // fp8 GEMM (gemm_fp8.hpp): p in units of two fp8 values (lda, ldb, K, kchunks as for 16-bit data
 // of half the width); fmt 0 E4M3, 1 E5M2; tiles 256×256, 128×128, 64×64.
 hipError_t launch_fp8(GemmParams p, int bm, int bn, int fmt, int out_bf16, hipStream_t stream);
