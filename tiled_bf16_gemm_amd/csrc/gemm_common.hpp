@@ -332,41 +332,72 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], u
 }
 
 
-// Buffer resources of the A box and the B box (or boxes) of K tile `kt` of the workgroup tile at
-// (m0, n0).  A tile past the end of K (`live` false) gets empty ranges and cvalid_a = -1: its
-// copies are fully masked and land zeros in a stage nobody reads.  cvalid_a counts the 16-byte
-// chunks along K that exist from this tile's first column (A, and B stored N×K).
+// Copy descriptors of one workgroup's operand boxes, built once before the K loop: the loop only
+// advances a base address per K tile.  A and B stored N×K use an open range (0x7FFFFFFF bytes):
+// their rows past M (or N) are masked in the per-lane offsets once (mask_row) and their chunks
+// past K by the chunk count, so no lane reads outside the operand.  B stored K×N keeps the exact
+// range to the end of B: the 16-byte chunk that straddles column N is loaded whole, and in B's
+// last row the range check is what keeps it inside the allocation.
+struct CopyPlan {
+  rsrc_t ra0, rb0;   // the boxes at K tile 0
+  int64_t rem_b0;    // B stored K×N: bytes from the box origin to the end of B (range at tile 0)
+  uint32_t step_b;   // bytes per K tile along B: 128 for N×K, 64 rows of ldb for K×N
+  int kchunks;       // 16-byte K chunks in a row of A (and of N×K B)
+};
+
 struct OperandTiles {
   rsrc_t ra, rb;
-  int cvalid_a;
+  int cvalid_a;  // K chunks of tile kt that exist (<= 0 past the end: every lane masked)
   bool live;
 };
 
 template <int BL>
-__device__ __forceinline__ OperandTiles operand_tiles(const GemmParams& p, int m0, int n0, int kt, int ktiles) {
-  OperandTiles o;
-  const int k0 = kt * kBK;
-  const int kext = p.kchunks * 8;
-  o.live = kt < ktiles;
-  o.cvalid_a = o.live ? p.kchunks - (k0 >> 3) : -1;
-  {
-    const uint16_t* origin = p.A + (uint64_t)m0 * p.lda + (o.live ? k0 : 0);
-    const int64_t rem = o.live ? ((int64_t)(p.M - 1 - m0) * p.lda + (kext - k0)) * 2 : 0;
-    o.ra = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
-  }
+__device__ __forceinline__ CopyPlan make_copy_plan(const GemmParams& p, int m0, int n0) {
+  CopyPlan c;
+  c.kchunks = p.kchunks;
+  c.ra0 = make_rsrc(p.A + (uint64_t)m0 * p.lda, 0x7FFFFFFFull);
   if (BL == 1) {
-    const uint16_t* origin = p.B + (uint64_t)n0 * p.ldb + (o.live ? k0 : 0);
-    const int64_t rem = o.live ? ((int64_t)(p.N - 1 - n0) * p.ldb + (kext - k0)) * 2 : 0;
-    o.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+    c.rb0 = make_rsrc(p.B + (uint64_t)n0 * p.ldb, 0x7FFFFFFFull);
+    c.step_b = 128u;
+    c.rem_b0 = 0;
   } else {
-    const uint16_t* origin = p.B + (uint64_t)(o.live ? k0 : 0) * p.ldb + n0;
-    // The range check works on whole dwords: round the last row's end up to one, so a last
-    // element in the low half of a dword is still fetched.  The two bytes past it share that
-    // dword (and its page) and only reach columns past N.
-    const int64_t rem = o.live ? (((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2 + 3) & ~(int64_t)3 : 0;
-    o.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+    c.rb0 = make_rsrc(p.B + n0, 0);
+    c.step_b = (uint32_t)(p.ldb * 2 * kBK);
+    // Round the last row's end up to a whole dword: the range check works on dwords, so a last
+    // element in the low half of one is still fetched.  The two bytes past it share that dword
+    // (and its page) and only reach columns past N.
+    c.rem_b0 = (((int64_t)(p.K - 1) * p.ldb + (p.N - n0)) * 2 + 3) & ~(int64_t)3;
+  }
+  return c;
+}
+
+// A buffer descriptor with its 48-bit base moved on by `bytes`.
+__device__ __forceinline__ rsrc_t rsrc_advance(rsrc_t r, uint64_t bytes) {
+  const uint64_t a = (((uint64_t)(uint32_t)r.y << 32) | (uint32_t)r.x) + bytes;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  return r;
+}
+
+// The boxes of K tile kt (tiles at or past `ktiles` are fully masked).
+template <int BL>
+__device__ __forceinline__ OperandTiles operand_tiles(const CopyPlan& c, int kt, int ktiles) {
+  OperandTiles o;
+  o.live = kt < ktiles;
+  o.cvalid_a = c.kchunks - kt * (kBK / 8);
+  o.ra = rsrc_advance(c.ra0, (uint64_t)kt * 128u);
+  const uint64_t off = (uint64_t)kt * c.step_b;
+  o.rb = rsrc_advance(c.rb0, off);
+  if (BL == 0) {
+    const int64_t rem = o.live ? c.rem_b0 - (int64_t)off : 0;
+    o.rb.z = rem <= 0 ? 0 : (rem > 0x7FFFFFFF ? 0x7FFFFFFF : (int)rem);
   }
   return o;
+}
+
+// Mask a lane's chunk when its box row is past the operand's last row (set once per kernel).
+__device__ __forceinline__ void mask_row(LaneChunk& lc, int row, int rows) {
+  if (row >= rows) lc.offset = kOobOffset;
 }
 
 // 16-byte chunks of columns that exist in the K×N box b (64 columns from n0 + 64 b).  The chunk

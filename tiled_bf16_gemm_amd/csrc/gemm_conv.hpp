@@ -60,10 +60,16 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   const uint32_t pitch_b = (uint32_t)(cp.ldw * 2);
   LaneChunk lb[T::AtomsB];
 #pragma unroll
-  for (int i = 0; i < T::AtomsB; ++i) lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+  for (int i = 0; i < T::AtomsB; ++i) {
+    lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+    mask_row(lb[i], (BN / 4) * wave + 8 * i + (lane >> 3), p.N - n0);
+  }
   const int ktiles = cp.r * cp.s * cp.cblocks;
   const uint32_t smem_addr = lds_addr_of(smem);
   const rsrc_t rx = make_rsrc(cp.X, cp.x_bytes);
+  // The filters' rows n0.. as one open-range buffer (rows past N are masked per lane above,
+  // channels past c8 by the chunk count); each K tile moves its base to the tap's columns.
+  const rsrc_t rw = make_rsrc(cp.W + (uint64_t)n0 * cp.ldw, 0x7FFFFFFFull);
 
   // Copies of K tile kt (tap kt / cblocks, channel block kt % cblocks) into `stage`; la receives
   // this tile's per-lane A sources.  A tile past the end is issued fully masked.
@@ -88,9 +94,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
     tc.ra = rx;
     tc.lds_a = sa + (BM / 4) * wave * 128;
     tc.cvalid_a = live ? (cp.c8 - c0) >> 3 : -1;
-    const uint16_t* origin = cp.W + (uint64_t)n0 * cp.ldw + (live ? tap * cp.c8 + c0 : 0);
-    const int64_t rem = live ? ((int64_t)(p.N - 1 - n0) * cp.ldw + (cp.c8 - c0)) * 2 : 0;
-    tc.rb = make_rsrc(origin, rem > 0 ? (uint64_t)rem : 0);
+    tc.rb = rsrc_advance(rw, (uint64_t)(tap * cp.c8 + c0) * 2u);
     tc.lds_b = sa + T::ABytes + (BN / 4) * wave * 128;
     tc.cvalid_b = tc.cvalid_a;
     return tc;

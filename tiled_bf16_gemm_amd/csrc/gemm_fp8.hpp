@@ -141,14 +141,21 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
   LaneChunk la[T::AtomsA], lb[T::AtomsB];
 #pragma unroll
-  for (int i = 0; i < T::AtomsA; ++i) la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
+  for (int i = 0; i < T::AtomsA; ++i) {
+    la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
+    mask_row(la[i], (BM / 4) * wave + 8 * i + (lane >> 3), p.M - m0);
+  }
 #pragma unroll
-  for (int i = 0; i < T::AtomsB; ++i) lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+  for (int i = 0; i < T::AtomsB; ++i) {
+    lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+    mask_row(lb[i], (BN / 4) * wave + 8 * i + (lane >> 3), p.N - n0);
+  }
   const int ktiles = p.K > 0 ? (p.K + kBK - 1) / kBK : 1;  // K counts pairs: a tile is 64 pairs
   const uint32_t smem_addr = lds_addr_of(smem);
+  const CopyPlan plan = make_copy_plan<BL>(p, m0, n0);
 
   auto make_copy = [&](int kt, int stage) {
-    const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
+    const OperandTiles o = operand_tiles<BL>(plan, kt, ktiles);
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
     tc.ra = o.ra;

@@ -77,19 +77,22 @@ __device__ __forceinline__ void produce(const GemmParams& p, const uint8_t* smem
     const int j = PW * C::PA + i;
     if (j < BM / 8) {
       ch[i] = lane_chunk<kSwizzle128B2Row>(8 * j, lane, pitch_a);
+      mask_row(ch[i], 8 * j + (lane >> 3), p.M - m0);
     } else if (BL == 1) {
       ch[i] = lane_chunk<kSwizzle128B2Row>(8 * (j - BM / 8), lane, pitch_b);
+      mask_row(ch[i], 8 * (j - BM / 8) + (lane >> 3), p.N - n0);
     } else {
       const int jb = j - BM / 8;
       ch[i] = lane_chunk<kSwizzleKnTr>(8 * (jb & 7), lane, pitch_b);
       ch[i].offset += 128u * (uint32_t)(jb >> 3);
     }
   }
+  const CopyPlan plan = make_copy_plan<BL>(p, m0, n0);
   int st = 0, fill = 0;     // stage and fill round of tile kt
   int sig = 0, sig_st = 0;  // next tile to mark full, and its stage
   for (int kt = 0; kt < ktiles; ++kt) {
     if (fill > 0) wait_counter(&empty[st], 4u * (uint32_t)fill);
-    const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
+    const OperandTiles o = operand_tiles<BL>(plan, kt, ktiles);
     const uint32_t base = smem_addr + (uint32_t)(st * T::StageBytes);
 #pragma unroll
     for (int i = 0; i < C::PA; ++i) {

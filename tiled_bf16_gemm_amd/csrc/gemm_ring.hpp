@@ -51,11 +51,15 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   const int b_box = (wave * T::AtomsB) >> 3;  // K×N box of this wave's B atoms
   LaneChunk la[T::AtomsA], lb[T::AtomsB];
 #pragma unroll
-  for (int i = 0; i < T::AtomsA; ++i) la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
+  for (int i = 0; i < T::AtomsA; ++i) {
+    la[i] = lane_chunk<kSwizzle128B2Row>((BM / 4) * wave + 8 * i, lane, pitch_a);
+    mask_row(la[i], (BM / 4) * wave + 8 * i + (lane >> 3), p.M - m0);
+  }
 #pragma unroll
   for (int i = 0; i < T::AtomsB; ++i) {
     if (BL == 1) {
       lb[i] = lane_chunk<kSwizzle128B2Row>((BN / 4) * wave + 8 * i, lane, pitch_b);
+      mask_row(lb[i], (BN / 4) * wave + 8 * i + (lane >> 3), p.N - n0);
     } else {
       lb[i] = lane_chunk<kSwizzleKnTr>(8 * ((wave * T::AtomsB + i) & 7), lane, pitch_b);
       lb[i].offset += 128u * b_box;
@@ -68,9 +72,10 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   // products).
   const int ktiles = p.K > 0 ? (p.K + kBK - 1) / kBK : 1;
   const uint32_t smem_addr = lds_addr_of(smem);
+  const CopyPlan plan = make_copy_plan<BL>(p, m0, n0);
 
   auto make_copy = [&](int kt, int stage) {
-    const OperandTiles o = operand_tiles<BL>(p, m0, n0, kt, ktiles);
+    const OperandTiles o = operand_tiles<BL>(plan, kt, ktiles);
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
     const uint32_t sb = sa + T::ABytes;
