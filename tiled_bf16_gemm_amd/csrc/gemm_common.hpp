@@ -185,16 +185,21 @@ template <class T, int BL, bool COPY>
 __device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<T>& cur, Frags<T>& nxt,
                                       const FragAddr<T>& fa, const uint8_t* nA, const uint8_t* nB, int nkk,
                                       const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb) {
-  // Read r goes before product (r * Products) / Reads, atom j before (j * Products) / Atoms:
-  // before product i come reads [ceil(i*R/P), ceil((i+1)*R/P)) and likewise atoms.
+  // Read r goes before product (r * Products) / Reads; atom j halfway between that slot and the
+  // next, before product (j * Products) / Atoms + Products / (2 * Atoms).  A wave alone on its
+  // SIMD issues one instruction every 4 clocks and a product keeps the matrix unit busy for 16,
+  // so every run of more than 3 other instructions between products idles the unit: staggering
+  // the atoms (5-6 instructions each with their m0 setup and chunk mask) against the reads keeps
+  // the runs short.
   constexpr int P = T::Products, R = T::Reads, A = T::Atoms;
 #pragma unroll
   for (int i = 0; i < P; ++i) {
 #pragma unroll
     for (int r = (i * R + P - 1) / P; r < ((i + 1) * R + P - 1) / P; ++r) read_frag<T, BL>(nxt, fa, nA, nB, nkk, r);
-    if (COPY) {
+    if (COPY && i >= P / (2 * A)) {
+      constexpr int H = P / (2 * A);
 #pragma unroll
-      for (int j = (i * A + P - 1) / P; j < ((i + 1) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
+      for (int j = ((i - H) * A + P - 1) / P; j < ((i + 1 - H) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
     }
     const int fn = i / T::FM, fm = i % T::FM;
     if (COPY && i == T::Products - 1) mfma16<T::AsmMfma, true, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
