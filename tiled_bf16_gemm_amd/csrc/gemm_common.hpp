@@ -28,6 +28,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "launch.hpp"
 #include "tbg_desc.hpp"
 #include "tile_loader.hpp"
@@ -409,6 +412,16 @@ __device__ __forceinline__ void mask_row(LaneChunk& lc, int row, int rows) {
 // that straddles column N is loaded whole: its columns past N only feed outputs that are never
 // written.
 __device__ __forceinline__ int kn_box_cvalid(const GemmParams& p, int n0, int b) { return (p.N - n0 - 64 * b + 7) >> 3; }
+
+// Call f(std::integral_constant<int, s>) for s = 0..N-1 in order (compile-time stage indices).
+template <int... I, class F>
+__device__ __forceinline__ void for_stages_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void for_stages(F&& f) {
+  for_stages_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Per-lane fragment read addresses of compute wave (wm, wn).
 // A (and B stored N×K): lane l reads row (l & 15) of a 16-row fragment, logical chunk

@@ -8,12 +8,12 @@
 // newer tiles in flight); after it, those copies are visible to all waves and every wave's
 // reads of the stage that the next copies overwrite have completed.
 //
-// Iteration kt: k-step 0 of tile kt (its products, with the fragment reads of k-step 1), the
-// stage barrier (tile kt+1 landed everywhere, stage kt%S free), k-step 1 of tile kt (its
-// products, with the reads of tile kt+1's first fragments and the copies of tile kt+S into stage
-// kt%S interleaved).  Every iteration runs the same code — the last ones read fragments nobody
-// uses and issue fully masked copies — so all products sit in one loop body and the
-// accumulators keep one register assignment throughout.
+// Tile kt: k-step 0 (its products, with the fragment reads of k-step 1), the stage barrier
+// (tile kt+1 landed everywhere, stage kt%S free), k-step 1 (its products, with the reads of tile
+// kt+1's first fragments and the copies of tile kt+S into stage kt%S interleaved).  The loop body
+// holds S tiles, one per stage, so stage addresses are constants; the last ones read fragments
+// nobody uses and issue fully masked copies.  The accumulators keep one register assignment
+// throughout.
 #pragma once
 #include "gemm_common.hpp"
 
@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   const uint32_t smem_addr = lds_addr_of(smem);
   const CopyPlan plan = make_copy_plan<BL>(p, m0, n0);
 
-  auto make_copy = [&](int kt, int stage) {
+  auto make_copy = [&](int kt, int stage) __attribute__((always_inline)) {
     const OperandTiles o = operand_tiles<BL>(plan, kt, ktiles);
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
@@ -109,17 +109,25 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
     stage_barrier<T::Atoms*(S - 1)>();  // tile 0 landed; tiles 1..S-1 may be in flight
 #pragma unroll
     for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
-    int cur = 0;  // stage of tile kt
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const int nxt = cur + 1 == S ? 0 : cur + 1;
+    // One K tile on stage CUR (a compile-time constant, so every LDS address below is a fixed
+    // offset from the ring: the loop runs S tiles per iteration, one per stage).
+    auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
+      constexpr int cur = decltype(stage)::value;
+      constexpr int nxt = cur + 1 == S ? 0 : cur + 1;
       const uint8_t* sA = smem + cur * T::StageBytes;
       kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
       stage_barrier<T::Atoms*(S - 2)>();  // tile kt+1 landed; tiles kt+2..kt+S-1 may be in flight
       const uint8_t* nA = smem + nxt * T::StageBytes;
       const TileCopy tc = make_copy(kt + S, cur);
       kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
-      cur = nxt;
-    }
+    };
+    int kt = 0;
+    for (; kt + S <= ktiles; kt += S)
+      for_stages<S>([&](auto st) __attribute__((always_inline)) { tile(kt + decltype(st)::value, st); });
+    // the last ktiles % S tiles, on stages 0.. in order
+    for_stages<S - 1>([&](auto st) __attribute__((always_inline)) {
+      if (kt + decltype(st)::value < ktiles) tile(kt + decltype(st)::value, st);
+    });
   }
 
   // The loop's last product ends with the drain wait states (or, for the builtin, the
