@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
 
   // Copies of K tile kt (tap kt / cblocks, channel block kt % cblocks) into `stage`; la receives
   // this tile's per-lane A sources.  A tile past the end is issued fully masked.
-  auto make_copy = [&](int kt, int stage, LaneChunk* la) {
+  auto make_copy = [&](int kt, int stage, LaneChunk* la) __attribute__((always_inline)) {
     const bool live = kt < ktiles;
     const int tap = live ? kt / cp.cblocks : 0;
     const int cb = live ? kt - tap * cp.cblocks : 0;
@@ -116,15 +116,22 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
     stage_barrier<T::Atoms>();  // tile 0 landed; tile 1 may be in flight
 #pragma unroll
     for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const int cur = kt & 1;
+    // Tile kt on stage CUR = kt & 1, a compile-time constant: two tiles per loop iteration.
+    auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
+      constexpr int cur = decltype(stage)::value;
       const uint8_t* sA = smem + cur * T::StageBytes;
       kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
       stage_barrier<0>();  // tile kt+1 landed everywhere; stage kt&1 free
       const uint8_t* nA = smem + (cur ^ 1) * T::StageBytes;
       const TileCopy tc = make_copy(kt + 2, cur, la);
       kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
+    };
+    int kt = 0;
+    for (; kt + 2 <= ktiles; kt += 2) {
+      tile(kt, std::integral_constant<int, 0>{});
+      tile(kt + 1, std::integral_constant<int, 1>{});
     }
+    if (kt < ktiles) tile(kt, std::integral_constant<int, 0>{});
   }
   stage_barrier<0>();
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);

@@ -161,9 +161,9 @@ struct Candidate {
   double eff;
 };
 const Candidate kCandidates[] = {
-    {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 256, 128, 2, 0.86}, {kPipeProducer, 128, 256, 2, 0.86},
-    {kPipeRing, 128, 128, 2, 0.82},     {kPipeRing, 256, 128, 2, 0.73},     {kPipeRing, 128, 256, 2, 0.72},
-    {kPipeProducer, 128, 128, 3, 0.69}, {kPipeRing, 64, 64, 2, 0.52},       {kPipeProducer, 64, 64, 3, 0.34},
+    {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 128, 256, 2, 0.83}, {kPipeProducer, 256, 128, 2, 0.81},
+    {kPipeRing, 128, 128, 2, 0.81},     {kPipeRing, 256, 128, 2, 0.75},     {kPipeRing, 128, 256, 2, 0.75},
+    {kPipeProducer, 128, 128, 3, 0.69}, {kPipeRing, 64, 64, 2, 0.48},       {kPipeProducer, 64, 64, 3, 0.37},
 };
 }  // namespace
 

@@ -171,9 +171,11 @@ __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>
     wait_counter(&full[0], (uint32_t)C::NP);
 #pragma unroll
     for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
-    int cur = 0, fill_next = 0;  // stage of tile kt; fill round of tile kt+1
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const int nxt = cur + 1 == S ? 0 : cur + 1;
+    int fill_next = 0;  // fill round of tile kt+1
+    // Tile kt on stage CUR = kt % S, a compile-time constant: S tiles per loop iteration.
+    auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
+      constexpr int cur = decltype(stage)::value;
+      constexpr int nxt = cur + 1 == S ? 0 : cur + 1;
       if (nxt == 0) ++fill_next;
       const uint8_t* sA = smem + cur * T::StageBytes;
       kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, nolanes, nolanes);
@@ -181,8 +183,13 @@ __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>
       if (kt + 1 < ktiles) wait_counter(&full[nxt], (uint32_t)(C::NP * (fill_next + 1)));
       const uint8_t* nA = smem + nxt * T::StageBytes;
       kstep<T, BL, false>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, none, nolanes, nolanes);
-      cur = nxt;
-    }
+    };
+    int kt = 0;
+    for (; kt + S <= ktiles; kt += S)
+      for_stages<S>([&](auto st) __attribute__((always_inline)) { tile(kt + decltype(st)::value, st); });
+    for_stages<S - 1>([&](auto st) __attribute__((always_inline)) {
+      if (kt + decltype(st)::value < ktiles) tile(kt + decltype(st)::value, st);
+    });
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();  // every copy landed and every fragment read retired: the ring becomes the park
