@@ -276,6 +276,36 @@ def test_every_configuration(ops, orc, pipeline, tile, stages):
         assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"
 
 
+_remainder_cache = {}
+
+
+@gpu
+@pytest.mark.parametrize("pipeline,tile,stages", [c for c in CONFIGS if c[2] >= 3])
+def test_stage_remainders(ops, orc, pipeline, tile, stages):
+    """The K loop runs S tiles per iteration (one per stage) and the last ktiles mod S tiles
+    through guarded copies of the same bodies: every residue 0..S-1, each with the main loop
+    taken at least once (ktiles = S + r, K ragged), both B layouts, against the oracle and
+    bit-identical to the default configuration."""
+    cfg = _cfg(tile, stages, pipeline)
+    M, N = 150, 130
+    for r in range(stages):
+        K = 64 * (stages + r) - 13
+        bl = "kn" if r % 2 == 0 else "nk"
+        key = (K, bl)
+        if key not in _remainder_cache:
+            A = workloads.matrix(M, K, K, ("normal", 1.0), 1900 + K)
+            B = workloads.matrix(K, N, N, ("normal", 1.0), 2900 + K) if bl == "kn" else \
+                workloads.matrix(N, K, K, ("normal", 1.0), 2900 + K)
+            ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl)
+            base = _to_f32(_run(ops, A, B, M, N, K, bl, "f32"))
+            _remainder_cache[key] = (A, B, ref, base)
+        A, B, ref, base = _remainder_cache[key]
+        _say(f"{pipeline} {tile}/{stages}: K={K} ({stages + r} K tiles, residue {r}) {bl}")
+        got = _to_f32(_run(ops, A, B, M, N, K, bl, "f32", config=cfg))
+        _check(got, ref, f"{pipeline} {tile}/{stages} K={K}")
+        assert np.array_equal(got, base), f"{int((got != base).sum())} entries differ from the default configuration"
+
+
 def _run_ex(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, alpha, beta, C_old, config=None):
     """C_old: (M, ldc) CPU tensor of the output type; returns the GPU result buffer."""
     A = A_cpu.cuda()[:, :K]
