@@ -90,30 +90,21 @@ __device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tile
 // accumulator pinned to AGPRs ("+a"): the 256 accumulators of a wave then stay in the
 // accumulation registers for the whole K loop and the 256 architectural VGPRs hold the fragments
 // and addresses.  Consecutive products there never reuse an accumulator within 63 instructions,
-// so no dependency wait is needed between them.  The last product of a loop iteration (DRAIN)
-// is followed by 24 wait states, more than a matrix result needs before another instruction may
-// read it, so whatever follows the loop can read the accumulators.
-template <bool ASM, bool DRAIN = false, int IN = 0>
+// so no dependency wait is needed between them; after the loop, drain_acc adds the wait states a
+// matrix result needs before another instruction may read it.
+template <bool ASM, int IN = 0>
 __device__ __forceinline__ void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   if (IN == 1) {
     // fp16 operands travel in the same registers as bf16 ones: only the instruction differs.
     if (!ASM)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc,
                                                    0, 0, 0);
-    else if (DRAIN)
-      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(acc)
-                   : "v"(a), "v"(b));
     else
       asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
     return;
   }
   if (!ASM)
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-  else if (DRAIN)
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc)
-                 : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -175,15 +166,23 @@ struct TileCopy {
   int cvalid_a, cvalid_b;
 };
 
+// Atom j of a tile.  A lane's logical chunk depends only on the atom's parity: atoms start
+// 8 rows apart at multiples of 16 rows per wave, and the 2-row and K×N XORs of rows 16 apart are
+// equal (checked for every tile, wave, lane and atom), so the chunk tests of atoms 0 and 1 serve
+// every atom of the tile (two compares per operand instead of one per atom).
 template <class T>
 __device__ __forceinline__ void copy_atom(const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb, int j) {
-  if (j < T::AtomsA) issue_atom(tc.ra, tc.lds_a + j * 1024, la[j], tc.cvalid_a);
-  else issue_atom(tc.rb, tc.lds_b + (j - T::AtomsA) * 1024, lb[j - T::AtomsA], tc.cvalid_b);
+  if (j < T::AtomsA) {
+    issue_atom_if(tc.ra, tc.lds_a + j * 1024, la[j].offset, la[j & 1].chunk < tc.cvalid_a);
+  } else {
+    const int i = j - T::AtomsA;
+    issue_atom_if(tc.rb, tc.lds_b + i * 1024, lb[i].offset, lb[i & 1].chunk < tc.cvalid_b);
+  }
 }
 
 // One k-step: the products on `cur`, with the fragment reads of the next k-step and (if COPY)
-// the copy atoms of a later tile spread evenly between them.  The COPY step closes a loop
-// iteration, so its last product drains.
+// the copy atoms of a later tile spread between them.  The loop's last product is drained after
+// the loop (drain_acc), not here.
 template <class T, int BL, bool COPY>
 __device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<T>& cur, Frags<T>& nxt,
                                       const FragAddr<T>& fa, const uint8_t* nA, const uint8_t* nB, int nkk,
@@ -205,9 +204,23 @@ __device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<
       for (int j = ((i - H) * A + P - 1) / P; j < ((i + 1 - H) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
     }
     const int fn = i / T::FM, fm = i % T::FM;
-    if (COPY && i == T::Products - 1) mfma16<T::AsmMfma, true, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
-    else mfma16<T::AsmMfma, false, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    mfma16<T::AsmMfma, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
   }
+}
+
+// The wait states between the K loop's last product and the first read of an accumulator, for
+// products issued as inline assembly (the compiler cannot see their hazards; for its builtin it
+// inserts the waits itself).  The drain is one assembly statement; each accumulator then passes
+// through an empty statement that claims to rewrite it, so every later read of it depends on a
+// statement that the compiler keeps after the drain.
+template <class T>
+__device__ __forceinline__ void drain_acc(f32x4_t (&acc)[T::FN][T::FM]) {
+  if (!T::AsmMfma) return;
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
+#pragma unroll
+  for (int i = 0; i < T::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
 // LDS chunk swizzle of the epilogue's park: rows of `cpr` 16-byte chunks; XOR the chunk index

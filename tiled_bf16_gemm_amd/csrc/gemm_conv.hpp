@@ -133,6 +133,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
     }
     if (kt < ktiles) tile(kt, std::integral_constant<int, 0>{});
   }
+  drain_acc<T>(acc);
   stage_barrier<0>();
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
 }

@@ -36,26 +36,15 @@ struct Frags8 {
 };
 
 // One 16×16×128 product; FMT 0: E4M3, 1: E5M2 (both operands).  ASM pins the accumulator to
-// AGPRs as in mfma16; DRAIN adds the wait states before the accumulators may be read.
-template <bool ASM, bool DRAIN, int FMT>
+// AGPRs as in mfma16 (drain_acc after the loop).
+template <bool ASM, int FMT>
 __device__ __forceinline__ void mfma8(f32x4_t& acc, const i32x8_t& a, const i32x8_t& b) {
-  if (!ASM) {
+  if (!ASM)
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, FMT, FMT, 0, 0, 0, 0);
-  } else if (FMT == 0) {
-    if (DRAIN)
-      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(acc)
-                   : "v"(a), "v"(b));
-    else
-      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  } else {
-    if (DRAIN)
-      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(acc)
-                   : "v"(a), "v"(b));
-    else
-      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(acc) : "v"(a), "v"(b));
-  }
+  else if (FMT == 0)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Per-lane LDS byte offsets of the two 16-byte halves of a fragment row: logical chunks
@@ -106,7 +95,7 @@ __device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], Frags8<T>& 
   for (int i = 0; i < P0; ++i) {
     const int fm = i / FN, fn = i % FN;
     if (fn == 0) cur.a[H + fm] = read_frag8(sCurA, fa.a_lane + (H + fm) * 2048, fa.a_col);
-    mfma8<T::AsmMfma, false, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    mfma8<T::AsmMfma, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
   }
   stage_barrier<0>();
 #pragma unroll
@@ -120,8 +109,7 @@ __device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], Frags8<T>& 
     }
 #pragma unroll
     for (int j = (i * A + P1 - 1) / P1; j < ((i + 1) * A + P1 - 1) / P1 && j < A; ++j) copy_atom<T>(tc, la, lb, j);
-    if (i == P1 - 1) mfma8<T::AsmMfma, true, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
-    else mfma8<T::AsmMfma, false, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+    mfma8<T::AsmMfma, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
   }
 }
 
@@ -191,6 +179,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
       ktile8<T, FMT>(acc, f1, f0, fa, s1, smem, smem + T::ABytes, make_copy(kt + 3, 1), la, lb);
     }
   }
+  drain_acc<T>(acc);
   stage_barrier<0>();
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
 }

@@ -130,10 +130,10 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
     });
   }
 
-  // The loop's last product ends with the drain wait states (or, for the builtin, the
-  // compiler's own waits): the accumulators are now safe to read.  The ring is drained before it
-  // becomes the park: the last iterations' masked copies still write zeros into stages, and the
-  // other waves may still read their fragments.
+  // Wait states after the last product (drain_acc), then the ring is drained before it becomes
+  // the park: the last iterations' masked copies still write zeros into stages, and the other
+  // waves may still read their fragments.
+  drain_acc<T>(acc);
   stage_barrier<0>();
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
 }

@@ -99,6 +99,15 @@ __device__ __forceinline__ void issue_atom(rsrc_t rs, uint32_t lds_addr, LaneChu
                : "memory");
 }
 
+// issue_atom with the lane's chunk test already made (`valid` false: the lane lands zeros).
+__device__ __forceinline__ void issue_atom_if(rsrc_t rs, uint32_t lds_addr, uint32_t offset, bool valid) {
+  const uint32_t off = valid ? offset : kOobOffset;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"(rs)
+               : "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
