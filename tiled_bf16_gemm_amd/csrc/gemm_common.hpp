@@ -400,6 +400,17 @@ __device__ __forceinline__ rsrc_t rsrc_advance(rsrc_t r, uint64_t bytes) {
   return r;
 }
 
+// Range of B stored K×N from the box origin moved on by `off` bytes: clamp(rem, 0, 2^31-1), or 0
+// for a tile past the end.  Computed on the two 32-bit halves with scalar compares (a 64-bit
+// signed compare would go to the vector unit).
+__device__ __forceinline__ int kn_range(const CopyPlan& c, uint64_t off, bool live) {
+  const uint64_t rem = (uint64_t)(c.rem_b0 - (int64_t)off);
+  int32_t hi = (int32_t)(rem >> 32);
+  uint32_t lo = (uint32_t)rem;
+  asm("" : "+s"(hi), "+s"(lo));  // opaque: the optimizer would fuse the halves into a 64-bit compare
+  return (!live || hi < 0) ? 0 : ((hi != 0 || lo > 0x7FFFFFFFu) ? 0x7FFFFFFF : (int)lo);
+}
+
 // The boxes of K tile kt (tiles at or past `ktiles` are fully masked).
 template <int BL>
 __device__ __forceinline__ OperandTiles operand_tiles(const CopyPlan& c, int kt, int ktiles) {
@@ -409,10 +420,7 @@ __device__ __forceinline__ OperandTiles operand_tiles(const CopyPlan& c, int kt,
   o.ra = rsrc_advance(c.ra0, (uint64_t)kt * 128u);
   const uint64_t off = (uint64_t)kt * c.step_b;
   o.rb = rsrc_advance(c.rb0, off);
-  if (BL == 0) {
-    const int64_t rem = o.live ? c.rem_b0 - (int64_t)off : 0;
-    o.rb.z = rem <= 0 ? 0 : (rem > 0x7FFFFFFF ? 0x7FFFFFFF : (int)rem);
-  }
+  if (BL == 0) o.rb.z = kn_range(c, off, o.live);
   return o;
 }
 

@@ -25,7 +25,8 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   const GemmParams& p = cp.g;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::StageBytes];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform: keeping it scalar keeps every address derived from it scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   int tm, tn;
