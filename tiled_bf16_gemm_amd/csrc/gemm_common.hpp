@@ -173,10 +173,10 @@ struct TileCopy {
 template <class T>
 __device__ __forceinline__ void copy_atom(const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb, int j) {
   if (j < T::AtomsA) {
-    issue_atom_if(tc.ra, tc.lds_a + j * 1024, la[j].offset, la[j & 1].chunk < tc.cvalid_a);
+    issue_atom_if(tc.ra, tc.lds_a, j * 1024, la[j].offset, la[j & 1].chunk < tc.cvalid_a);
   } else {
     const int i = j - T::AtomsA;
-    issue_atom_if(tc.rb, tc.lds_b + i * 1024, lb[i].offset, lb[i & 1].chunk < tc.cvalid_b);
+    issue_atom_if(tc.rb, tc.lds_b, i * 1024, lb[i].offset, lb[i & 1].chunk < tc.cvalid_b);
   }
 }
 

@@ -99,13 +99,15 @@ __device__ __forceinline__ void issue_atom(rsrc_t rs, uint32_t lds_addr, LaneChu
                : "memory");
 }
 
-// issue_atom with the lane's chunk test already made (`valid` false: the lane lands zeros).
-__device__ __forceinline__ void issue_atom_if(rsrc_t rs, uint32_t lds_addr, uint32_t offset, bool valid) {
+// issue_atom with the lane's chunk test already made (`valid` false: the lane lands zeros) and
+// the atom's LDS address as a base plus an offset that is a compile-time constant where this is
+// inlined (the atom index of an unrolled loop): M0 is then set by one scalar add.
+__device__ __forceinline__ void issue_atom_if(rsrc_t rs, uint32_t lds_base, int lds_imm, uint32_t offset, bool valid) {
   const uint32_t off = valid ? offset : kOobOffset;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_add_u32 m0, %0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"(rs)
-               : "memory");
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(off), "s"(rs), "i"(lds_imm)
+               : "scc", "memory");
 }
 
 // LDS byte address of a pointer into a __shared__ array.
