@@ -14,7 +14,8 @@ Also reported in the same line:
                 summary when it was taken on the current kernel source, else null.
   cpu_baseline  the CPU oracle on a bounded sample of the same product (the first rows of C),
                 timed on this host's cores.
-  per_config    TFLOP/s and % of peak on all five GEMM workloads, the 8192³ product with fp16 and
+  per_config    TFLOP/s and % of peak on all five GEMM workloads (for the small c1-c3 also the
+                GPU time per product from HIP-graph replays, `graph_ms`), the 8192³ product with fp16 and
                 with fp8 E4M3 inputs (against the fp8 peak), and the benchmark convolution layer
                 (timed the same way, fewer steps).
 """
@@ -98,6 +99,43 @@ def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16"):
     region = starts[0].elapsed_time(ends[-1])
     del A, B, C, ws
     return region / steps, sum(per) / len(per), wall_ms / steps
+
+
+def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20):
+    """GPU time per product with the host out of the way: `calls` products captured in one HIP
+    graph (torch.cuda.graph), replayed `replays` times; returns ms per product."""
+    import workloads
+    import tiled_bf16_gemm_amd as tbg
+    A, B = workloads.gemm_inputs(w)
+    lda, ldb, ldc = w.lds()
+    A, B = A.cuda(), B.cuda()
+    Av = A[:, :w.K]
+    Bv = B[:, :w.N] if w.b_layout == "kn" else B[:, :w.K]
+    C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
+    need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(calls):
+            torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / (replays * calls)
+    del g, A, B, C, ws
+    return ms
 
 
 def time_conv(torch, torch_ops, w, steps, warmup, config=None):
@@ -426,6 +464,11 @@ def main():
             tf = cw.flops / (s * 1e-3) / 1e12
             per_config[name] = {"M": cw.M, "N": cw.N, "K": cw.K, "b_layout": cw.b_layout, "out": cw.out_dtype,
                                 "ms": round(s, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+            if name in ("c1", "c2", "c3"):
+                # launch-bound shapes: also the GPU time per product from graph replays
+                gms = time_gemm_graph(torch, torch_ops, cw)
+                per_config[name]["graph_ms"] = round(gms, 5)
+                per_config[name]["graph_tflops"] = round(cw.flops / (gms * 1e-3) / 1e12, 2)
             torch.cuda.empty_cache()
         per_config["c4"] = {"M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "out": w.out_dtype,
                             "ms": round(ms_step, 5), "tflops": round(tflops, 2),

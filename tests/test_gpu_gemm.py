@@ -542,3 +542,64 @@ def test_fp8_large_sampled(ops, orc):
     for m0 in (0, 7777, M - 64):
         ref = orc.gemm_f8(A8.numpy(), B8.numpy(), M, N, K, K, K, "e4m3", rows=(m0, m0 + 64))
         _check_f8(got[m0:m0 + 64], ref, Av[m0:m0 + 64].numpy(), Bv.numpy(), f"fp8 rows {m0}..{m0 + 64}")
+
+
+@gpu
+def test_graph_capture(ops, orc):
+    """The GEMM under HIP graph capture (torch.cuda.graph): three products (plain, the repack
+    path of a leading dimension off 16 bytes, and C <- alpha·A·B + beta·C) are captured once and
+    replayed three times, with eager work between the replays; every replay equals the eager
+    result bit for bit."""
+    rng = np.random.default_rng(77)
+    cases = [(512, 384, 256, "kn", 256), (300, 257, 777, "kn", 777), (256, 256, 512, "nk", 512)]
+    ins, outs, eager = [], [], []
+    for M, N, K, bl, lda in cases:
+        A = torch.from_numpy(rng.standard_normal((M, lda)).astype(np.float32)).to(torch.bfloat16).cuda()[:, :K]
+        B = torch.from_numpy(rng.standard_normal((K, N) if bl == "kn" else (N, K)).astype(np.float32)).to(
+            torch.bfloat16).cuda()
+        C0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).cuda()
+        ins.append((A, B, bl, C0))
+    # eager results; the third case as C <- 1.5 AB - 0.5 C0
+    for i, (A, B, bl, C0) in enumerate(ins):
+        C = C0.clone()
+        if i == 2:
+            ops.gemm(A, B, bl, "f32", out=C, alpha=1.5, beta=-0.5)
+        else:
+            ops.gemm(A, B, bl, "f32", out=C)
+        eager.append(C)
+    torch.cuda.synchronize()
+    # the workspace the repack case uses is allocated before capture
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    outs = [C0.clone() for (_, _, _, C0) in ins]
+    starts = [C0.clone() for (_, _, _, C0) in ins]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # warm-up on the capture stream
+        for i, (A, B, bl, _) in enumerate(ins):
+            if i == 2:
+                ops.gemm(A, B, bl, "f32", out=outs[i], workspace=ws, alpha=1.5, beta=-0.5)
+            else:
+                ops.gemm(A, B, bl, "f32", out=outs[i], workspace=ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i, (A, B, bl, _) in enumerate(ins):
+            if i == 2:
+                ops.gemm(A, B, bl, "f32", out=outs[i], workspace=ws, alpha=1.5, beta=-0.5)
+            else:
+                ops.gemm(A, B, bl, "f32", out=outs[i], workspace=ws)
+    for rep in range(3):
+        for i in range(3):
+            outs[i].copy_(starts[i])  # C holds the old C again for the alpha/beta case
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say(f"graph replay {rep}")
+        for i in range(3):
+            assert torch.equal(outs[i], eager[i]), f"replay {rep} case {i} differs from the eager result"
+        # eager work between replays
+        x = torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")
+        torch.cuda.synchronize()
+        del x
+    del g
