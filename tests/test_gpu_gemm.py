@@ -306,6 +306,28 @@ def test_stage_remainders(ops, orc, pipeline, tile, stages):
         assert np.array_equal(got, base), f"{int((got != base).sum())} entries differ from the default configuration"
 
 
+@gpu
+@pytest.mark.parametrize("tile,stages", [(c[1], c[2]) for c in CONFIGS if c[0] == "ring"])
+def test_ring_interior_boundary(ops, orc, tile, stages):
+    """The ring's K loop runs unmasked iterations while every copy they issue is of a tile before
+    the last one, then masked iterations and the guarded remainder.  K tiles 2S .. 3S cover every
+    hand-over between the two, ragged K, M and N (rows, K chunks and the columns past N masked),
+    with B stored K×N at its dense pitch (the last row's straddling chunk at the end of B) and
+    stored N×K."""
+    cfg = _cfg(tile, stages, "ring")
+    M, N = 150, 130
+    for r in range(stages + 1):
+        K = 64 * (2 * stages + r) - 13
+        for bl in ("kn", "nk"):
+            A = workloads.matrix(M, K, K, ("normal", 1.0), 3900 + K)
+            B = workloads.matrix(K, N, N, ("normal", 1.0), 4900 + K) if bl == "kn" else \
+                workloads.matrix(N, K, K, ("normal", 1.0), 4900 + K)
+            ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, K, B.shape[1], bl)
+            _say(f"ring {tile}/{stages}: K={K} ({2 * stages + r} K tiles) {bl}")
+            got = _to_f32(_run(ops, A, B, M, N, K, bl, "f32", config=cfg))
+            _check(got, ref, f"ring {tile}/{stages} K={K} {bl}")
+
+
 def _run_ex(ops, A_cpu, B_cpu, M, N, K, b_layout, out_dtype, alpha, beta, C_old, config=None):
     """C_old: (M, ldc) CPU tensor of the output type; returns the GPU result buffer."""
     A = A_cpu.cuda()[:, :K]

@@ -169,21 +169,23 @@ struct TileCopy {
 // Atom j of a tile.  A lane's logical chunk depends only on the atom's parity: atoms start
 // 8 rows apart at multiples of 16 rows per wave, and the 2-row and K×N XORs of rows 16 apart are
 // equal (checked for every tile, wave, lane and atom), so the chunk tests of atoms 0 and 1 serve
-// every atom of the tile (two compares per operand instead of one per atom).
-template <class T>
+// every atom of the tile (two compares per operand instead of one per atom).  MASK_A / MASK_B
+// false: no chunk test for that operand (a tile that lies wholly inside it, or an operand whose
+// lane offsets and range already mask everything outside it).
+template <class T, bool MASK_A = true, bool MASK_B = true>
 __device__ __forceinline__ void copy_atom(const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb, int j) {
   if (j < T::AtomsA) {
-    issue_atom_if(tc.ra, tc.lds_a, j * 1024, la[j].offset, la[j & 1].chunk < tc.cvalid_a);
+    issue_atom_if(tc.ra, tc.lds_a, j * 1024, la[j].offset, !MASK_A || la[j & 1].chunk < tc.cvalid_a);
   } else {
     const int i = j - T::AtomsA;
-    issue_atom_if(tc.rb, tc.lds_b, i * 1024, lb[i].offset, lb[i & 1].chunk < tc.cvalid_b);
+    issue_atom_if(tc.rb, tc.lds_b, i * 1024, lb[i].offset, !MASK_B || lb[i & 1].chunk < tc.cvalid_b);
   }
 }
 
 // One k-step: the products on `cur`, with the fragment reads of the next k-step and (if COPY)
 // the copy atoms of a later tile spread between them.  The loop's last product is drained after
 // the loop (drain_acc), not here.
-template <class T, int BL, bool COPY>
+template <class T, int BL, bool COPY, bool MASK_A = true, bool MASK_B = true>
 __device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<T>& cur, Frags<T>& nxt,
                                       const FragAddr<T>& fa, const uint8_t* nA, const uint8_t* nB, int nkk,
                                       const TileCopy& tc, const LaneChunk* la, const LaneChunk* lb) {
@@ -201,7 +203,7 @@ __device__ __forceinline__ void kstep(f32x4_t (&acc)[T::FN][T::FM], const Frags<
     if (COPY && i >= P / (2 * A)) {
       constexpr int H = P / (2 * A);
 #pragma unroll
-      for (int j = ((i - H) * A + P - 1) / P; j < ((i + 1 - H) * A + P - 1) / P; ++j) copy_atom<T>(tc, la, lb, j);
+      for (int j = ((i - H) * A + P - 1) / P; j < ((i + 1 - H) * A + P - 1) / P; ++j) copy_atom<T, MASK_A, MASK_B>(tc, la, lb, j);
     }
     const int fn = i / T::FM, fm = i % T::FM;
     mfma16<T::AsmMfma, T::In>(acc[fn][fm], cur.b[fn], cur.a[fm]);
@@ -421,6 +423,20 @@ __device__ __forceinline__ OperandTiles operand_tiles(const CopyPlan& c, int kt,
   const uint64_t off = (uint64_t)kt * c.step_b;
   o.rb = rsrc_advance(c.rb0, off);
   if (BL == 0) o.rb.z = kn_range(c, off, o.live);
+  return o;
+}
+
+// The boxes of K tile kt < ktiles - 1, which lies wholly inside K: open ranges and every chunk
+// valid (rows past M or N stay masked in the lane offsets; B stored K×N has its columns past N
+// masked there too).
+template <int BL>
+__device__ __forceinline__ OperandTiles interior_tiles(const CopyPlan& c, int kt) {
+  OperandTiles o;
+  o.live = true;
+  o.cvalid_a = kBK / 8;
+  o.ra = rsrc_advance(c.ra0, (uint64_t)kt * 128u);
+  o.rb = rsrc_advance(c.rb0, (uint64_t)kt * c.step_b);
+  if (BL == 0) o.rb.z = 0x7FFFFFFF;
   return o;
 }
 

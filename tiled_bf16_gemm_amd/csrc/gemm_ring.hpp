@@ -64,9 +64,10 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
     } else {
       lb[i] = lane_chunk<kSwizzleKnTr>(8 * ((wave * T::AtomsB + i) & 7), lane, pitch_b);
       lb[i].offset += 128u * b_box;
+      // columns past N: masked once here; rows past K by the range of the last tile's copy
+      if (lb[i].chunk >= kn_box_cvalid(p, n0, b_box)) lb[i].offset = kOobOffset;
     }
   }
-  const int b_kn_cvalid = kn_box_cvalid(p, n0, b_box);
   // At least one tile: with K = 0 every copy lane is masked, the products add zeros and the
   // empty sum is stored.  Keeping one straight path from the accumulator initialisation to the
   // epilogue also keeps the accumulators in fixed AGPRs (no register copies next to in-flight
@@ -75,22 +76,19 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   const uint32_t smem_addr = lds_addr_of(smem);
   const CopyPlan plan = make_copy_plan<BL>(p, m0, n0);
 
-  auto make_copy = [&](int kt, int stage) __attribute__((always_inline)) {
-    const OperandTiles o = operand_tiles<BL>(plan, kt, ktiles);
+  // The copies of tile kt into `stage`; INTERIOR (kt < ktiles - 1, the tile lies wholly inside
+  // K) takes open ranges and no chunk tests.
+  auto make_copy = [&](int kt, int stage, auto interior) __attribute__((always_inline)) {
+    const OperandTiles o = decltype(interior)::value ? interior_tiles<BL>(plan, kt) : operand_tiles<BL>(plan, kt, ktiles);
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
     const uint32_t sb = sa + T::ABytes;
     tc.ra = o.ra;
     tc.rb = o.rb;
     tc.cvalid_a = o.cvalid_a;
+    tc.cvalid_b = o.cvalid_a;  // B stored K×N: unused (lane offsets and range mask it)
     tc.lds_a = sa + (BM / 4) * wave * 128;
-    if (BL == 1) {
-      tc.lds_b = sb + (BN / 4) * wave * 128;
-      tc.cvalid_b = o.cvalid_a;
-    } else {
-      tc.lds_b = sb + wave * T::AtomsB * 1024;
-      tc.cvalid_b = o.live ? b_kn_cvalid : -1;
-    }
+    tc.lds_b = BL == 1 ? sb + (BN / 4) * wave * 128 : sb + wave * T::AtomsB * 1024;
     return tc;
   };
 
@@ -103,31 +101,39 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
     const TileCopy none{};
 #pragma unroll
     for (int t = 0; t < S; ++t) {
-      const TileCopy tc = make_copy(t, t);
+      const TileCopy tc = make_copy(t, t, std::false_type{});
 #pragma unroll
-      for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
+      for (int j = 0; j < T::Atoms; ++j) copy_atom<T, true, BL == 1>(tc, la, lb, j);
     }
     stage_barrier<T::Atoms*(S - 1)>();  // tile 0 landed; tiles 1..S-1 may be in flight
 #pragma unroll
     for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
     // One K tile on stage CUR (a compile-time constant, so every LDS address below is a fixed
     // offset from the ring: the loop runs S tiles per iteration, one per stage).
-    auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
+    auto tile = [&](int kt, auto stage, auto interior) __attribute__((always_inline)) {
       constexpr int cur = decltype(stage)::value;
       constexpr int nxt = cur + 1 == S ? 0 : cur + 1;
+      constexpr bool mask = !decltype(interior)::value;
       const uint8_t* sA = smem + cur * T::StageBytes;
       kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
       stage_barrier<T::Atoms*(S - 2)>();  // tile kt+1 landed; tiles kt+2..kt+S-1 may be in flight
       const uint8_t* nA = smem + nxt * T::StageBytes;
-      const TileCopy tc = make_copy(kt + S, cur);
-      kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
+      const TileCopy tc = make_copy(kt + S, cur, interior);
+      kstep<T, BL, true, mask, mask && BL == 1>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
     };
     int kt = 0;
+    // Iterations whose copies (tiles kt+S .. kt+2S-1) all lie before the last tile: no masking.
+    for (; kt + 2 * S < ktiles; kt += S)
+      for_stages<S>([&](auto st) __attribute__((always_inline)) {
+        tile(kt + decltype(st)::value, st, std::true_type{});
+      });
     for (; kt + S <= ktiles; kt += S)
-      for_stages<S>([&](auto st) __attribute__((always_inline)) { tile(kt + decltype(st)::value, st); });
+      for_stages<S>([&](auto st) __attribute__((always_inline)) {
+        tile(kt + decltype(st)::value, st, std::false_type{});
+      });
     // the last ktiles % S tiles, on stages 0.. in order
     for_stages<S - 1>([&](auto st) __attribute__((always_inline)) {
-      if (kt + decltype(st)::value < ktiles) tile(kt + decltype(st)::value, st);
+      if (kt + decltype(st)::value < ktiles) tile(kt + decltype(st)::value, st, std::false_type{});
     });
   }
 
