@@ -16,8 +16,12 @@ Also reported in the same line:
                 timed on this host's cores.
   per_config    TFLOP/s and % of peak on all five GEMM workloads (for the small c1-c3 also the
                 GPU time per product from HIP-graph replays, `graph_ms`), the 8192³ product with fp16 and
-                with fp8 E4M3 inputs (against the fp8 peak), and the benchmark convolution layer
-                (timed the same way, fewer steps).
+                with fp8 E4M3 inputs (against the fp8 peak), the benchmark convolution layer
+                (timed the same way, fewer steps), and the tiled-copy kernel (tbg_tiled_copy_many)
+                on the three copy workloads: the worked 128x64 box at its 10 places, the 432 boxes of
+                the 5-D tensor with NaN fill, and all 8192 boxes of the 8192x8192 operand A, each
+                in achieved GB/s (in-bounds source bytes + image bytes per launch) against the
+                8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz ("2.5 PF")
 PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": PEAK_BF16_TFLOPS,
                "f8e4m3": 5033.2, "f8e5m2": 5033.2}  # dense fp8: 256 CU x 8192 flop/clk x 2.4 GHz ("5.0 PF")
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E: 8 TB/s
 METRIC = "bf16 GEMM TFLOP/s and % of MI355X MFMA peak at M=N=K=8192, 1 GPU"
 KERNEL_SOURCES = ["tiled_bf16_gemm_amd/csrc/gemm_common.hpp", "tiled_bf16_gemm_amd/csrc/gemm_ring.hpp",
                   "tiled_bf16_gemm_amd/csrc/tile_loader.hpp"]
@@ -136,6 +141,47 @@ def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20):
     ms = s.elapsed_time(e) / (replays * calls)
     del g, A, B, C, ws
     return ms
+
+
+def copy_inbounds_bytes(w) -> int:
+    """Source bytes a copy workload's boxes read: elements inside the tensor, per box (the image
+    bytes are box_bytes each, fill included)."""
+    esize = 2
+    total = 0
+    for c in w.coords:
+        n = 1
+        for x, b, e, d in zip(c, w.box, w.estr, w.dims):
+            n *= sum(1 for j in range((b + e - 1) // e) if 0 <= x + j * e < d)
+        total += n * esize
+    return total
+
+
+def time_copy(torch, torch_ops, w, steps, warmup):
+    """tbg_tiled_copy_many over every box of a copy workload, one launch per step; returns (mean
+    per-launch ms from events, algorithmic bytes per launch = in-bounds source bytes + images)."""
+    import workloads
+    import tiled_bf16_gemm_amd as tbg
+    src = workloads.copy_source(w).cuda()
+    d = list(w.dims)
+    strides, acc = [], 2
+    for i in range(len(d) - 1):
+        acc *= d[i]
+        strides.append(acc)
+    desc = torch_ops.encode(src, w.dtype, d, strides, list(w.box), list(w.estr), w.swizzle, w.oob)
+    coords = torch.tensor([list(c) for c in w.coords], dtype=torch.int32, device="cuda").contiguous()
+    out = torch.empty(len(w.coords) * tbg.box_bytes(desc), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        torch_ops.tiled_copy_many(desc, coords, out=out)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record()
+        torch_ops.tiled_copy_many(desc, coords, out=out)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+    return ms, copy_inbounds_bytes(w) + len(w.coords) * tbg.box_bytes(desc)
 
 
 def time_conv(torch, torch_ops, w, steps, warmup, config=None):
@@ -289,7 +335,48 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
         json.dump(traffic, f, indent=1)
     if sq_db and os.path.exists(sq_db):
         summarize_sq(sq_db, out_dir, commands["sq"])
+    copy_db = os.path.join(os.path.dirname(os.path.dirname(trace_db)), "copytrace", "run_results.db")
+    if os.path.exists(copy_db):
+        summarize_copies(copy_db, out_dir, commands["copytrace"])
     return traffic
+
+
+def summarize_copies(db: str, out_dir: str, command: str) -> None:
+    """Kernel-trace summary of the tiled-copy kernel on the three copy workloads (one rocprofv3
+    --kernel-trace run of `bench.py --only-copies`); launches are told apart by their grid size
+    (one workgroup per box)."""
+    import sqlite3
+    import statistics
+    import workloads
+    c = sqlite3.connect(db)
+    try:
+        rows = list(c.execute("select name, grid_x, workgroup_x, duration from kernels"))
+    finally:
+        c.close()
+    by_boxes = {}
+    for name, gx, wx, dur in rows:
+        if "tiled_copy_kernel" in name:
+            by_boxes.setdefault(gx // wx, []).append(dur / 1e3)
+    lines = ["# Tiled-copy kernel trace on the three copy workloads", "",
+             "Command (<repo> is the repository root, <out> the output folder):", "", "```", command, "```", "",
+             "Summary written by `python bench.py --summarize <out>`.  Algorithmic bytes per launch = source",
+             "bytes inside the tensor + image bytes (fill included); GB/s from the trace's average duration,",
+             "against the 8 TB/s HBM peak.", "",
+             "| workload | boxes per launch | launches | average us | median us | algorithmic bytes | GB/s | of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name in ("c1_copy", "c3_copy", "c4_a_boxes"):
+        w = workloads.COPIES[name]
+        d = by_boxes.get(len(w.coords), [])
+        if not d:
+            continue
+        import math
+        nbytes = copy_inbounds_bytes(w) + len(w.coords) * 2 * math.prod((b + e - 1) // e for b, e in zip(w.box, w.estr))
+        avg = statistics.mean(d)
+        gbs = nbytes / (avg * 1e-6) / 1e9
+        lines.append(f"| {name} | {len(w.coords)} | {len(d)} | {avg:.2f} | {statistics.median(d):.2f} | {nbytes} | "
+                     f"{gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} % |")
+    with open(os.path.join(out_dir, "copy_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
@@ -401,6 +488,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--only-copies", action="store_true",
+                    help="time only the tiled-copy kernel on the three copy workloads; one JSON line each")
     ap.add_argument("--counters", action="store_true",
                     help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
@@ -432,6 +521,8 @@ def main():
                      "python -u <repo>/bench.py --counters",
             "sq": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " -d <out>/sq -o run -- "
                   "python -u <repo>/bench.py --counters",
+            "copytrace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/copytrace -o run -- "
+                         "python -u <repo>/bench.py --only-copies",
             "bench_kernel_us": args.bench_kernel_us,
         }
         t = summarize_profiles(os.path.join(d, "trace", "run_results.db"), os.path.join(d, "fetch", "run_results.db"),
@@ -451,6 +542,14 @@ def main():
         return
     if args.sweep:
         sweep(torch, torch_ops, args.sweep.split(","), 20, 5)
+        return
+    if args.only_copies:
+        for name in ("c1_copy", "c3_copy", "c4_a_boxes"):
+            ms_c, nbytes = time_copy(torch, torch_ops, workloads.COPIES[name], 50, 20)
+            gbs = nbytes / (ms_c * 1e-3) / 1e9
+            print(json.dumps({"copy": name, "ms": round(ms_c, 5), "bytes": nbytes, "gb_per_s": round(gbs, 1),
+                              "frac": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+            torch.cuda.empty_cache()
         return
     ms_step, ms_kernel, wall_ms = time_gemm(torch, torch_ops, w, args.steps, args.warmup)
     tflops = w.flops / (ms_step * 1e-3) / 1e12
@@ -480,6 +579,15 @@ def main():
                                       "b_layout": "nk" if ab.startswith("f8") else w.b_layout, "out": w.out_dtype,
                                       "ms": round(s_, 5), "tflops": round(tf, 2), "peak": PEAK_TFLOPS[ab],
                                       "pct_peak": round(100 * tf / PEAK_TFLOPS[ab], 2)}
+            torch.cuda.empty_cache()
+        for name in ("c1_copy", "c3_copy", "c4_a_boxes"):
+            cw = workloads.COPIES[name]
+            ms_c, nbytes = time_copy(torch, torch_ops, cw, 50, 20)
+            gbs = nbytes / (ms_c * 1e-3) / 1e9
+            per_config[name] = {"boxes": len(cw.coords), "box": list(cw.box), "estr": list(cw.estr),
+                                "swizzle": cw.swizzle, "oob": cw.oob, "bytes": nbytes, "ms": round(ms_c, 5),
+                                "gb_per_s": round(gbs, 1), "peak_gb_per_s": PEAK_HBM_GBS,
+                                "frac": round(gbs / PEAK_HBM_GBS, 4)}
             torch.cuda.empty_cache()
         cw = workloads.CONVS["conv_b"]
         s_, _ = time_conv(torch, torch_ops, cw, 50, 20)

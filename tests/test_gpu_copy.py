@@ -109,6 +109,39 @@ def test_c3_copy_5d_nan_fill(ops, orc):
 
 
 @gpu
+def test_c4_a_boxes_full_size(ops, orc):
+    """All 8192 boxes of 64 columns x 128 rows (128B swizzle) of the 8192x8192 GEMM operand A, the
+    launch the bench times.  Sampled boxes against the oracle byte for byte; at full size, undoing
+    the 128-byte swizzle ("2 · Le Tensor Memory Accelerator" §2.4: the 16-byte unit index XORed
+    with the row index within 8 rows of 128 bytes) on every image and putting the boxes back in
+    their places gives A again, bit for bit."""
+    w = workloads.COPIES["c4_a_boxes"]
+    src = workloads.copy_source(w)
+    rows, cols = w.shape_outer_first
+    coords = [list(c) for c in w.coords]
+    assert len(coords) == 8192
+    _say("c4 A boxes: 8192 boxes, one launch")
+    got = _device_copy(ops, src, "bf16", list(w.dims), [cols * 2], list(w.box), list(w.estr), w.swizzle, w.oob,
+                       coords, True)
+    srcb = _src_bytes(src)
+    rng = np.random.default_rng(4)
+    picks = sorted(set([0, 127, 8064, 8191] + rng.integers(0, 8192, 20).tolist()))
+    for i in picks:
+        want = orc.tiled_copy(srcb, "bf16", list(w.dims), [cols * 2], list(w.box), list(w.estr), w.swizzle, False,
+                              coords[i])
+        assert np.array_equal(got[i], want), f"box {i} at {coords[i]} differs from the oracle"
+    _say("c4 A boxes: reassembling A from the unswizzled images")
+    unit = np.arange(1024)                    # 16-byte units of a 16 KiB image
+    logical = unit ^ ((unit >> 3) & 7)        # unit u of the image holds logical unit u ^ row8(u)
+    imgs = got.reshape(8192, 1024, 16)
+    plain = np.empty_like(imgs)
+    plain[:, logical, :] = imgs[:, unit, :]
+    # box (bx, by) -> A[128 by : 128 by + 128, 64 bx : 64 bx + 64]; 128 boxes per box row
+    a = plain.reshape(rows // 128, cols // 64, 128, 128).transpose(0, 2, 1, 3).reshape(rows, cols * 2)
+    assert np.array_equal(a, srcb.reshape(rows, cols * 2)), "images do not reassemble A"
+
+
+@gpu
 def test_dma_path_edges(ops, orc):
     """2-D boxes of 128-byte rows through the direct-to-LDS loader: ragged rows and columns,
     both swizzles, pitches wider than the rows, every chunk-aligned origin class."""

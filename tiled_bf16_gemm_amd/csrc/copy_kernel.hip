@@ -145,7 +145,11 @@ __global__ void __launch_bounds__(256) tiled_copy_kernel(DescImpl d, Coords5 hos
   uint8_t* out = dst + (uint64_t)b * d.image_bytes;
   const uint32_t nbytes = d.image_bytes;
   if ((((uintptr_t)out) % 16u) == 0 && (nbytes % 16u) == 0) {
-    for (uint32_t i = threadIdx.x; i < nbytes / 16u; i += blockDim.x) ((uint4*)out)[i] = ((const uint4*)smem)[i];
+    // Images are written once and not read again here: non-temporal stores keep them from
+    // taking L2 space that the source rows of other boxes are using.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    for (uint32_t i = threadIdx.x; i < nbytes / 16u; i += blockDim.x)
+      __builtin_nontemporal_store(((const u32x4_t*)smem)[i], (u32x4_t*)out + i);
   } else {
     for (uint32_t i = threadIdx.x; i < nbytes; i += blockDim.x) out[i] = smem[i];
   }

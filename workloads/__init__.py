@@ -162,11 +162,21 @@ def _c3_copy_coords():
     return tuple(out)
 
 
+def _a_box_coords(rows: int, cols: int, bx: int, by: int):
+    """Every box of a rows×cols matrix in a grid of bx columns × by rows (innermost first)."""
+    return tuple((x, y) for y in range(0, rows, by) for x in range(0, cols, bx))
+
+
 COPIES = {
     "c1_copy": CopyWorkload("c1_copy", (256, 256), "bf16", (64, 128), (1, 1), "128B", "zero", 1001,
                             ("uniform", 1.0), _c1_copy_coords()),
     "c3_copy": CopyWorkload("c3_copy", (3, 5, 7, 129, 200), "bf16", (64, 16, 4, 2, 2), (1, 2, 1, 1, 1), "none",
                             "nan", 3003, ("normal", 1.0), _c3_copy_coords()),
+    # The 8192x8192 GEMM's A operand cut into all of its 8192 boxes of 64 columns x 128 rows with
+    # the 128-byte swizzle: the worked box's copy at a size where HBM bandwidth, not launch
+    # latency, bounds the kernel (128 MiB read, 128 MiB of images written).
+    "c4_a_boxes": CopyWorkload("c4_a_boxes", (8192, 8192), "bf16", (64, 128), (1, 1), "128B", "zero", 4001,
+                               ("uniform", 1.0), _a_box_coords(8192, 8192, 64, 128)),
 }
 
 
@@ -207,8 +217,8 @@ def gemm_inputs(w: GemmWorkload):
 
 def copy_source(w: CopyWorkload) -> torch.Tensor:
     """The tensor a copy workload reads, as a contiguous CPU tensor (outermost dim first)."""
-    if w.name == "c1_copy":
-        g = GEMMS["c1"]
+    if w.name in ("c1_copy", "c4_a_boxes"):
+        g = GEMMS["c1" if w.name == "c1_copy" else "c4"]
         return matrix(g.M, g.K, g.K, g.dist_a, g.seed_a)
     return _draw(w.shape_outer_first, w.dist, w.seed).contiguous()
 
