@@ -5,7 +5,9 @@ for bit where the inputs are small integers (every partial sum is then exact in 
 summation order gives the same bits).  The workload sizes that the oracle finishes in seconds
 are compared in full; the 8192³ and 16384×14336×4096 workloads — in the launch configuration the
 benchmark times — are compared on sampled whole rows and scattered points, and checked for
-finiteness and run-to-run determinism everywhere."""
+finiteness and run-to-run determinism everywhere; with integer operands whose product the output
+type holds exactly, every entry of those two products is checked through Freivalds' identities
+(C·x and yᵀ·C against A·(B·x) and (yᵀ·A)·B, exact in binary64)."""
 import sys
 
 import numpy as np
@@ -118,6 +120,60 @@ def test_c4_8192_sampled(ops, orc):
 def test_c5_mlp_sampled(ops, orc):
     w = workloads.GEMMS["c5"]
     _sampled(ops, orc, w, rows=[0, 300, 8191, 12345, 16383])
+
+
+def _freivalds_exact(C: np.ndarray, A: np.ndarray, B: np.ndarray, bl: str, seed: int, what: str):
+    """Every entry of C at once: with integer operands every partial sum below is an integer
+    under 2^53, so C·x == A·(B·x) and yᵀ·C == (yᵀ·A)·B hold exactly in binary64 for the true
+    product and fail for almost any wrong entry (x, y: random integers in [1, 2^16], so an error
+    cancels only if weights coincide).  B is K×N for "kn", N×K for "nk"."""
+    rng = np.random.default_rng(seed)
+    M, N = C.shape
+    x = rng.integers(1, 1 << 16, N).astype(np.float64)
+    y = rng.integers(1, 1 << 16, M).astype(np.float64)
+    C64, A64, B64 = C.astype(np.float64), A.astype(np.float64), B.astype(np.float64)
+    Bx = B64 @ x if bl == "kn" else B64.T @ x
+    yA = y @ A64
+    yAB = yA @ B64 if bl == "kn" else B64 @ yA
+    bad_rows = np.nonzero(C64 @ x != A64 @ Bx)[0]
+    bad_cols = np.nonzero(y @ C64 != yAB)[0]
+    assert bad_rows.size == 0 and bad_cols.size == 0, \
+        f"{what}: {bad_rows.size} rows and {bad_cols.size} columns differ from the exact product " \
+        f"(first rows {bad_rows[:8]}, first columns {bad_cols[:8]})"
+
+
+def _int_operands(rng, M, N, K, bl, sparse_a):
+    """Integer operands.  sparse_a: 16 entries of ±1 per row of A (some may coincide) and B in
+    [-16, 16], so |C| <= 256 and every product is an integer that bf16 holds exactly; else A and
+    B dense in [-8, 8] (|C| <= 64·K, exact in binary32 up to K = 2^18)."""
+    shape_b = (K, N) if bl == "kn" else (N, K)
+    if sparse_a:
+        A = np.zeros((M, K), np.float32)
+        cols = rng.integers(0, K, (M, 16))
+        np.add.at(A, (np.repeat(np.arange(M), 16), cols.reshape(-1)), rng.choice([-1.0, 1.0], M * 16))
+        B = rng.integers(-16, 17, shape_b).astype(np.float32)
+    else:
+        A = rng.integers(-8, 9, (M, K)).astype(np.float32)
+        B = rng.integers(-8, 9, shape_b).astype(np.float32)
+    return A, B
+
+
+@gpu
+@pytest.mark.parametrize("name,out,sparse", [("c4", "bf16", True), ("c4", "f32", False), ("c5", "bf16", True),
+                                             ("c5", "f32", False)])
+def test_full_size_exact(ops, name, out, sparse):
+    """The 8192³ and 16384×14336×4096 products in full, in the launch configuration the benchmark
+    times (bf16 out: the benchmark's own kernel instance), with integer operands whose product
+    the output type holds exactly: every entry is then checked by Freivalds' identities."""
+    w = workloads.GEMMS[name]
+    rng = np.random.default_rng({"c4": 40, "c5": 50}[name] + (out == "bf16"))
+    A, B = _int_operands(rng, w.M, w.N, w.K, w.b_layout, sparse)
+    _say(f"full-size exact gemm {name}: M={w.M} N={w.N} K={w.K} {w.b_layout} {out} sparse_a={sparse}")
+    Cbuf = _run(ops, torch.from_numpy(A).to(torch.bfloat16), torch.from_numpy(B).to(torch.bfloat16), w.M, w.N, w.K,
+                w.b_layout, out)
+    C = _to_f32(Cbuf)
+    assert np.isfinite(C).all(), "non-finite output"
+    _freivalds_exact(C, A, B, w.b_layout, 7, f"{name} {out}")
 
 
 @gpu
