@@ -586,6 +586,28 @@ def test_fp8_inputs(ops, orc, fmt):
 
 
 @gpu
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64"])
+def test_fp8_interior_boundary(ops, orc, tile):
+    """K-tile counts 1..9 (128 values each), whole and ragged last tiles: the fp8 loop takes its
+    pairs of tiles without masking while both tiles they copy lie before the last one, masked
+    after; small integers make every result exact, so each case is compared bit for bit."""
+    import tiled_bf16_gemm_amd as tbg
+    cfg = tbg.gemm_config(tile, 2, "ring")
+    rng = np.random.default_rng(77)
+    M, N = 300, 200
+    for t in range(1, 10):
+        for K in (128 * t, 128 * t - 48):
+            Ai = rng.integers(-4, 5, (M, K)).astype(np.float32)
+            Bi = rng.integers(-4, 5, (N, K)).astype(np.float32)
+            A8 = torch.from_numpy(Ai).to(torch.float8_e4m3fn).view(torch.uint8)
+            B8 = torch.from_numpy(Bi).to(torch.float8_e4m3fn).view(torch.uint8)
+            _say(f"fp8 interior boundary: tile {tile} K={K} ({t} K tiles)")
+            got = _run_f8(M, N, K, A8, B8, "f8e4m3", "f32", cfg)
+            want = (Ai.astype(np.float64) @ Bi.T.astype(np.float64)).astype(np.float32)
+            assert np.array_equal(got[:, :N], want), f"K={K}: {int((got[:, :N] != want).sum())} entries differ"
+
+
+@gpu
 def test_fp8_torch_ops(ops, orc):
     """torch_ops.gemm on float8 tensors: the same bits as tbg_gemm_typed, for dense rows and for
     rows that the library repacks (K = 200, not a multiple of 16 bytes; a row view with pitch 210)."""

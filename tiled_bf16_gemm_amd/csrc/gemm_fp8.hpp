@@ -84,7 +84,7 @@ __device__ __forceinline__ i32x8_t read_frag8(const uint8_t* base, uint32_t lane
 //                fragments 0..H-1 read from sNxt, and tile kt+2's copy atoms into sCur.
 // A copy so has from the middle of the tile it is issued in to the middle of the next one to
 // land, and no fragment is read before its tile is known to be complete.
-template <class T, int FMT>
+template <class T, int FMT, bool MASK>
 __device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], Frags8<T>& cur, Frags8<T>& nxt,
                                        const FragAddr8& fa, const uint8_t* sCurA, const uint8_t* sNxtA,
                                        const uint8_t* sNxtB, const TileCopy& tc, const LaneChunk* la,
@@ -108,7 +108,8 @@ __device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], Frags8<T>& 
       else nxt.a[q - FN] = read_frag8(sNxtA, fa.a_lane + (q - FN) * 2048, fa.a_col);
     }
 #pragma unroll
-    for (int j = (i * A + P1 - 1) / P1; j < ((i + 1) * A + P1 - 1) / P1 && j < A; ++j) copy_atom<T>(tc, la, lb, j);
+    for (int j = (i * A + P1 - 1) / P1; j < ((i + 1) * A + P1 - 1) / P1 && j < A; ++j)
+      copy_atom<T, MASK, MASK>(tc, la, lb, j);
     mfma8<T::AsmMfma, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
   }
 }
@@ -143,8 +144,10 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   const uint32_t smem_addr = lds_addr_of(smem);
   const CopyPlan plan = make_copy_plan<BL>(p, m0, n0);
 
-  auto make_copy = [&](int kt, int stage) {
-    const OperandTiles o = operand_tiles<BL>(plan, kt, ktiles);
+  // The copies of tile kt into `stage`; INTERIOR (kt < ktiles - 1: the tile lies wholly inside
+  // K) takes open ranges and no chunk tests (rows past M or N stay masked in the lane offsets).
+  auto make_copy = [&](int kt, int stage, auto interior) __attribute__((always_inline)) {
+    const OperandTiles o = decltype(interior)::value ? interior_tiles<BL>(plan, kt) : operand_tiles<BL>(plan, kt, ktiles);
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
     tc.ra = o.ra;
@@ -163,7 +166,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
     Frags8<T> f0, f1;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const TileCopy tc = make_copy(t, t);
+      const TileCopy tc = make_copy(t, t, std::false_type{});
 #pragma unroll
       for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
     }
@@ -173,12 +176,17 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) f0.b[j] = read_frag8(smem + T::ABytes, fa.b_lane + j * 2048, fa.b_col);
     const uint8_t* s1 = smem + T::StageBytes;
-    for (int kt = 0; kt < ktiles; kt += 2) {
-      // tile kt (stage 0); tile kt+1's first fragments from stage 1; tile kt+2's copies into stage 0
-      ktile8<T, FMT>(acc, f0, f1, fa, smem, s1, s1 + T::ABytes, make_copy(kt + 2, 0), la, lb);
-      // tile kt+1 (stage 1); tile kt+2's first fragments from stage 0; tile kt+3's copies into stage 1
-      ktile8<T, FMT>(acc, f1, f0, fa, s1, smem, smem + T::ABytes, make_copy(kt + 3, 1), la, lb);
-    }
+    // Tile kt (stage 0) with tile kt+1's first fragments from stage 1 and tile kt+2's copies into
+    // stage 0; then tile kt+1 (stage 1) with tile kt+2's first fragments and tile kt+3's copies.
+    auto pair = [&](int kt, auto interior) __attribute__((always_inline)) {
+      constexpr bool mask = !decltype(interior)::value;
+      ktile8<T, FMT, mask>(acc, f0, f1, fa, smem, s1, s1 + T::ABytes, make_copy(kt + 2, 0, interior), la, lb);
+      ktile8<T, FMT, mask>(acc, f1, f0, fa, s1, smem, smem + T::ABytes, make_copy(kt + 3, 1, interior), la, lb);
+    };
+    int kt = 0;
+    // Pairs whose copies (tiles kt+2, kt+3) both lie before the last tile: no masking.
+    for (; kt + 5 <= ktiles; kt += 2) pair(kt, std::true_type{});
+    for (; kt < ktiles; kt += 2) pair(kt, std::false_type{});
   }
   drain_acc<T>(acc);
   stage_barrier<0>();
