@@ -17,56 +17,66 @@ namespace tbg {
 // into a contiguous area before use; 16-byte alignment of the leading dimension, section "In
 // pratica"): copy `rows` rows of `row_bytes` bytes into a buffer of pitch `ld_dst` bytes (a
 // multiple of 16), zero-filling bytes row_bytes..ld_dst-1.  One thread per 16-byte chunk of the
-// destination: it reads the aligned dwords that hold the chunk's source bytes (the source may sit
-// at any byte alignment) and funnel-shifts them into place; a chunk within 20 bytes of its row's
-// end goes byte by byte, so no read leaves the row.  Blocks of 64 chunks × 4 rows; blockIdx.z
-// picks the repack, so both operands of a product are packed by one launch.
-__device__ __forceinline__ uint4 load16_unaligned(const uint8_t* p) {
-  const uintptr_t a = (uintptr_t)p;
+// destination: it reads the five aligned dwords that hold the chunk's source bytes (the source may
+// sit at any byte alignment) and funnel-shifts them into place.  Near the row's end the dword
+// reads stop at the dword that holds the row's last byte and the bytes past the row are zeroed,
+// so every lane runs the same instructions and no read leaves the dwords of the row.  Both
+// operands of a product are packed by one launch.
+__device__ __forceinline__ uint4 pack_chunk(const PackJob& j, int64_t r, int64_t b0) {
+  const int64_t valid = j.row_bytes - b0;  // bytes of this chunk inside the row
+  if (valid <= 0) return make_uint4(0, 0, 0, 0);
+  const uint8_t* srow = j.src + r * j.ld_src;
+  const uintptr_t a = (uintptr_t)(srow + b0);
   const uint32_t* q = (const uint32_t*)(a & ~(uintptr_t)3);
   const uint32_t sh = (uint32_t)(a & 3);
-  const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
-  if (sh == 0) return make_uint4(w0, w1, w2, w3);
-  const uint32_t w4 = q[4];
-  return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
-                    __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
+  const uint32_t* qlast = (const uint32_t*)((uintptr_t)(srow + j.row_bytes - 1) & ~(uintptr_t)3);
+  const int64_t nlast = qlast - q;
+  uint32_t w[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) w[i] = q[i < nlast ? i : nlast];
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+    const int64_t keep = valid - 4 * k;  // bytes of this dword inside the row
+    if (keep < 4) o[k] &= keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-__global__ void __launch_bounds__(256) pack_rows_kernel(PackJob j0, PackJob j1) {
-  const PackJob j = blockIdx.z == 0 ? j0 : j1;
-  const int64_t cpr = j.ld_dst / 16;
-  for (int64_t r = (int64_t)blockIdx.y * 4 + threadIdx.y; r < j.rows; r += (int64_t)gridDim.y * 4) {
-    const uint8_t* srow = j.src + r * j.ld_src;
-    uint8_t* drow = j.dst + r * j.ld_dst;
-    for (int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x; c < cpr; c += (int64_t)gridDim.x * 64) {
-      const int64_t b0 = c * 16;
-      uint4 v;
-      if (b0 + 20 <= j.row_bytes) {
-        v = load16_unaligned(srow + b0);
-      } else {
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (b0 + k < j.row_bytes) w[k >> 2] |= (uint32_t)srow[b0 + k] << (8 * (k & 3));
-        v = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      *(uint4*)(drow + b0) = v;
-    }
+// Blocks of 64 chunks × 4 rows, numbered flat: blocks below `b0` pack j0, the rest j1, so each
+// repack gets exactly its own blocks when the two operands have different shapes.  Workgroups
+// step through the blocks by the grid size.
+struct PackGrid {
+  uint32_t b0, total;  // blocks of the first repack; blocks of both
+  uint32_t gx0, gx1;   // blocks across a row of each repack
+};
+
+__global__ void __launch_bounds__(256) pack_rows_kernel(PackJob j0, PackJob j1, PackGrid g) {
+  for (uint32_t blk = blockIdx.x; blk < g.total; blk += gridDim.x) {
+    const bool second = blk >= g.b0;
+    const PackJob& j = second ? j1 : j0;
+    const uint32_t w = second ? blk - g.b0 : blk;
+    const uint32_t gx = second ? g.gx1 : g.gx0;
+    const int64_t r = (int64_t)(w / gx) * 4 + threadIdx.y;
+    const int64_t c = (int64_t)(w % gx) * 64 + threadIdx.x;
+    if (r >= j.rows || c >= j.ld_dst / 16) continue;
+    *(uint4*)(j.dst + r * j.ld_dst + c * 16) = pack_chunk(j, r, c * 16);
   }
 }
 
 hipError_t launch_pack_jobs(const PackJob* jobs, int n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  int64_t gx = 1, gy = 1;
+  uint64_t gx[2] = {1, 1}, blocks[2] = {0, 0};
   for (int i = 0; i < n; ++i) {
-    const int64_t x = (jobs[i].ld_dst / 16 + 63) / 64, y = (jobs[i].rows + 3) / 4;
-    if (x > gx) gx = x;
-    if (y > gy) gy = y;
+    gx[i] = (uint64_t)(jobs[i].ld_dst / 16 + 63) / 64;
+    blocks[i] = gx[i] * (uint64_t)((jobs[i].rows + 3) / 4);
   }
-  if (gx > 4096) gx = 4096;
-  if (gy > 65535) gy = 65535;
-  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)n), dim3(64, 4), 0, stream, jobs[0],
-                     n > 1 ? jobs[1] : jobs[0]);
+  if (blocks[0] + blocks[1] >= (1ull << 32)) return hipErrorInvalidValue;
+  const PackGrid g{(uint32_t)blocks[0], (uint32_t)(blocks[0] + blocks[1]), (uint32_t)gx[0], (uint32_t)gx[1]};
+  if (g.total == 0) return hipSuccess;
+  const uint32_t grid = g.total < (1u << 20) ? g.total : (1u << 20);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(grid), dim3(64, 4), 0, stream, jobs[0], n > 1 ? jobs[1] : jobs[0], g);
   return hipGetLastError();
 }
 
