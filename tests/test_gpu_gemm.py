@@ -236,6 +236,29 @@ def test_degenerate_sizes(ops):
     assert float(C[0, 0]) == float(A[0, 0].float() * B[0, 0].float())
 
 
+@gpu
+def test_repack_many_rows(ops, orc):
+    """An A of 2^22 + 5 rows with K = 7 (rows of 14 bytes: repacked to 16) is more than 2^20
+    blocks of the repack, which then steps through its blocks by the grid size; B K×N with a pitch
+    of 27 elements is repacked in the same launch.  Integer operands: exact.  Checked on sampled
+    rows (first, last, block and grid-stride boundaries) and through Freivalds' identities."""
+    M, N, K = (1 << 22) + 5, 24, 7
+    rng = np.random.default_rng(23)
+    A = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    Bbuf = np.full((K, 27), np.nan, np.float32)
+    Bbuf[:, :N] = rng.integers(-8, 9, (K, N))
+    _say(f"repack of {M} rows (K={K}), B pitch 27")
+    Ad = torch.from_numpy(A).to(torch.bfloat16).cuda()
+    Bd = torch.from_numpy(Bbuf).to(torch.bfloat16).cuda()
+    C = ops.gemm(Ad, Bd[:, :N], "kn", "f32")
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    want_rows = [0, 1, 3, 4, 5, 4 * (1 << 20) - 1, 4 * (1 << 20), 4 * (1 << 20) + 1, M - 2, M - 1]
+    exact = A[want_rows].astype(np.float64) @ Bbuf[:, :N].astype(np.float64)
+    assert np.array_equal(got[want_rows], exact.astype(np.float32))
+    _freivalds_exact(got, A, Bbuf[:, :N], "kn", 3, "repacked rows")
+
+
 TILES = ["256x256", "256x128", "128x256", "128x128", "64x64"]
 
 
