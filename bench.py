@@ -22,6 +22,9 @@ Also reported in the same line:
                 the 5-D tensor with NaN fill, and all 8192 boxes of the 8192x8192 operand A, each
                 in achieved GB/s (in-bounds source bytes + image bytes per launch) against the
                 8 TB/s HBM peak.
+  roofline.ceiling  the bf16 products alone (no loads, no stores) on random register-resident
+                operands, timed in the same run: what the power limit lets the matrix units
+                sustain; frac_of_ceiling is the GEMM kernel's rate over it.
 """
 from __future__ import annotations
 
@@ -182,6 +185,49 @@ def time_copy(torch, torch_ops, w, steps, warmup):
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
     return ms, copy_inbounds_bytes(w) + len(w.coords) * tbg.box_bytes(desc)
+
+
+def mfma_ceiling(torch, launches: int = 60, warmup: int = 60):
+    """The bf16 matrix products alone (tiled_bf16_gemm_amd/diag/mfma_rate.hip): 16x16x32 products
+    back to back on register-resident random operands, one workgroup of four waves per CU as the
+    256x256 GEMM tile, four rounds of workgroups like the 8192^3 product.  Returns (TFLOP/s, median
+    shader clock in GHz from the kernel's own counters): the ceiling of any GEMM kernel at the clock
+    the power limit allows with such operands."""
+    import ctypes
+    import statistics
+    here = os.path.join(ROOT, "tiled_bf16_gemm_amd", "diag", "libtbg_diag.so")
+    if not os.path.exists(here):
+        raise RuntimeError(f"{here} is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(here)
+    lib.tbg_diag_mfma_rate.restype = ctypes.c_int
+    lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    nwg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 200
+    g = torch.Generator().manual_seed(77)
+    src = (torch.rand(nwg * 16 * 256 * 8, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    out = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2 * nwg, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def go():
+        rc = lib.tbg_diag_mfma_rate(src.data_ptr(), out.data_ptr(), nwg, iters, clk.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"mfma rate launch failed ({rc})")
+    for _ in range(warmup):
+        go()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        go()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    flops = nwg * 4 * iters * 64 * 16384  # 16x16x32 product: 8192 multiply-adds, 16384 flops
+    c = clk.cpu().tolist()
+    ghz = statistics.median(c[2 * i + 1] / (c[2 * i] / 100e6) / 1e9 for i in range(nwg) if c[2 * i] > 0)
+    return flops / (ms * 1e-3) / 1e12, ghz
 
 
 def time_conv(torch, torch_ops, w, steps, warmup, config=None):
@@ -395,14 +441,16 @@ def summarize_sq(db: str, out_dir: str, command: str) -> None:
     import statistics
     c = sqlite3.connect(db)
     try:
-        rows = list(c.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"))
+        rows = list(c.execute("select kernel_name, dispatch_id, counter_name, value, duration from counters_collection"))
     finally:
         c.close()
     per = {}
-    for name, disp, cn, v in rows:
+    for name, disp, cn, v, dur in rows:
         if "gemm_" not in name:
             continue
-        per.setdefault(name, {}).setdefault(disp, {})[cn] = v
+        d = per.setdefault(name, {}).setdefault(disp, {})
+        d[cn] = v
+        d["duration_ns"] = dur
     lines = ["# MFMA utilisation and LDS bank conflicts of the GEMM kernels, 8192^3", "",
              "Command (<repo> is the repository root, <out> the output folder):", "", "```", command, "```", "",
              "Summary written by `python bench.py --summarize <out>`.  Medians over the dispatches.", "",
@@ -412,9 +460,13 @@ def summarize_sq(db: str, out_dir: str, command: str) -> None:
              "- bank conflict = SQ_LDS_BANK_CONFLICT / SQ_BUSY_CU_CYCLES; LDS active = SQ_LDS_IDX_ACTIVE / the same;",
              "- waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (waves at s_waitcnt or s_barrier);",
              "- MFMA instructions: SQ_INSTS_MFMA per dispatch (2MNK / flops per instruction: 16x16x32 bf16",
-             "  16384, 16x16x128 fp8 65536).", "",
-             "| kernel | dispatches | MFMA busy | bank conflict | LDS active | waiting | MFMA instructions |",
-             "|---|---|---|---|---|---|---|"]
+             "  16384, 16x16x128 fp8 65536);",
+             "- clock = GRBM_GUI_ACTIVE / 8 / dispatch duration: the counter sums the active cycles of the 8 XCDs",
+             "  (this division reproduces the clock the kernels measure themselves with s_memtime, and gives",
+             "  ≈2.45 GHz for the memory-bound device copies of the same run); listed per dispatch in order,",
+             "  the dispatches running back to back.", "",
+             "| kernel | dispatches | MFMA busy | bank conflict | LDS active | waiting | MFMA instructions | clock per dispatch (GHz) |",
+             "|---|---|---|---|---|---|---|---|"]
     for name, disps in per.items():
         def med(f):
             vals = [f(d) for d in disps.values() if all(k in d for k in SQ_COUNTERS[:7])]
@@ -424,8 +476,10 @@ def summarize_sq(db: str, out_dir: str, command: str) -> None:
         la = med(lambda d: d["SQ_LDS_IDX_ACTIVE"] / d["SQ_BUSY_CU_CYCLES"])
         wt = med(lambda d: d["SQ_WAIT_ANY"] / d["SQ_WAVE_CYCLES"])
         ni = med(lambda d: d["SQ_INSTS_MFMA"])
+        clocks = ", ".join(f"{d['GRBM_GUI_ACTIVE'] / 8 / d['duration_ns']:.2f}" for _, d in sorted(disps.items())
+                           if "GRBM_GUI_ACTIVE" in d and d.get("duration_ns"))
         lines.append(f"| `{name}` | {len(disps)} | {100 * mf:.1f} % | {100 * bc:.1f} % | {100 * la:.1f} % | "
-                     f"{100 * wt:.1f} % | {ni:.4g} |")
+                     f"{100 * wt:.1f} % | {ni:.4g} | {clocks} |")
     with open(os.path.join(out_dir, "gemm_8192_mfma_lds_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -488,6 +542,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the products-alone ceiling measured next to the GEMM (roofline.ceiling)")
     ap.add_argument("--only-copies", action="store_true",
                     help="time only the tiled-copy kernel on the three copy workloads; one JSON line each")
     ap.add_argument("--counters", action="store_true",
@@ -514,7 +570,7 @@ def main():
         d = args.summarize
         cmds = {
             "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/trace -o run -- "
-                     "python -u <repo>/bench.py --no-cpu-baseline --no-configs",
+                     "python -u <repo>/bench.py --no-cpu-baseline --no-configs --no-ceiling",
             "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE -d <out>/fetch -o run -- "
                      "python -u <repo>/bench.py --counters",
             "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE -d <out>/write -o run -- "
@@ -596,6 +652,12 @@ def main():
                                         f"{cw.M}x{cw.k}x{cw.r * cw.s * cw.c})", "out": cw.out_dtype, "ms": round(s_, 5),
                                 "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
 
+    ceiling = None
+    if not args.no_ceiling:
+        c_tf, c_ghz = mfma_ceiling(torch)
+        ceiling = {"what": "bf16 16x16x32 products alone on register-resident random operands (no loads, no stores), "
+                           "same process, after the GEMM", "tflops": round(c_tf, 1), "clock_ghz": round(c_ghz, 3),
+                   "frac_of_peak": round(c_tf / PEAK_BF16_TFLOPS, 4)}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     line = {
@@ -624,6 +686,8 @@ def main():
             "traffic": load_traffic(),
             "kernel_ms": round(ms_kernel, 5),
             "flops_per_launch": w.flops,
+            "ceiling": ceiling,
+            "frac_of_ceiling": round(achieved / ceiling["tflops"], 4) if ceiling else None,
         },
         "cpu_baseline": cpu,
         "per_config": per_config,

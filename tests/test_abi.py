@@ -440,3 +440,19 @@ def test_gemm_fp8_checks():
     # the 8-bit types as copy element types, NaN fill included
     d = tbg.encode_tiled("f8e4m3", 2, BASE, [256, 64], [256], [128, 8], [1, 1], "128B", "none", "nan")
     assert tbg.box_bytes(d) == 128 * 8
+
+
+def test_benchmark_ceiling_library():
+    """The benchmark's products-alone measurement lives in its own library, outside include/tbg.h;
+    it exports one C function and rejects empty launches without touching a device."""
+    import os
+    path = os.path.join(os.path.dirname(tbg.library_path()), "diag", "libtbg_diag.so")
+    lib = ctypes.CDLL(path)
+    lib.tbg_diag_mfma_rate.restype = ctypes.c_int
+    lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    assert lib.tbg_diag_mfma_rate(None, None, 0, 1, None, None) != 0
+    assert lib.tbg_diag_mfma_rate(BASE, BASE, 4, 0, BASE, None) != 0
+    main = subprocess.run(["nm", "-D", "--defined-only", tbg.library_path()], capture_output=True, text=True,
+                          check=True).stdout
+    assert "tbg_diag_mfma_rate" not in main, "the measurement aid must stay out of the library's ABI"

@@ -16,6 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtbg.so")
+# The benchmark's measurement aid (products alone, the power-limited ceiling): a library of its own,
+# outside the C ABI of include/tbg.h.
+DIAG_SRC = os.path.join(HERE, "diag", "mfma_rate.hip")
+DIAG_LIB = os.path.join(HERE, "diag", "libtbg_diag.so")
 
 
 def hipcc() -> str:
@@ -65,6 +69,14 @@ def build(out: str = LIB, verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    tmp = DIAG_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *flags(), "-shared", DIAG_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {DIAG_SRC}:\n{r.stderr}")
+    os.replace(tmp, DIAG_LIB)
     isa_dir = os.environ.get("TBG_SAVE_ISA")
     if isa_dir:
         save_isa(isa_dir)
