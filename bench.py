@@ -492,7 +492,7 @@ SWEEP_CONFIGS = ([("ring", "256x256", 2)] + [("ring", t, st) for t in ("256x128"
                  + [("producer", "64x64", st) for st in range(2, 7)])
 
 # The fp16 and 8-bit configurations built (include/tbg.h, tbg_gemm_typed).
-SWEEP_CONFIGS_F16 = ([("ring", t, 2) for t in ("256x256", "256x128", "128x256", "128x128", "64x64")]
+SWEEP_CONFIGS_F16 = ([("ring", t, 2) for t in ("256x256", "256x128", "128x256", "128x128", "64x64")] + [("ring", "64x64", 3)]
                      + [("producer", t, 2) for t in ("256x128", "128x256")]
                      + [("producer", t, 3) for t in ("128x128", "64x64")])
 SWEEP_CONFIGS_F8 = [("ring", t, 2) for t in ("256x256", "128x128", "64x64")]

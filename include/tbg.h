@@ -226,8 +226,8 @@ typedef enum { TBG_PIPE_AUTO = 0, TBG_PIPE_RING = 1, TBG_PIPE_PRODUCER = 2 } tbg
 /* Kernel configuration of tbg_gemm_configured.  Zero fields are left to the library.
  *   tile_m, tile_n  workgroup tile of C ([GEMM] "Tiling"): both 0 (chosen from the shape), or
  *                   one of 256x256, 256x128, 128x256, 128x128, 64x64.
- *   stages          LDS stages of the ring: 0 (default: 2; 3 for the producer pipeline's 128x128
- *                   and 64x64 tiles) or >= 2.  Each stage holds one tile_m x 64 block of A and
+ *   stages          LDS stages of the ring: 0 (default: 2; 3 for 64x64 tiles and for the
+ *                   producer pipeline's 128x128 tiles) or >= 2.  Each stage holds one tile_m x 64 block of A and
  *                   one 64 x tile_n block of B in bf16, so the count is bounded by the 160 KiB
  *                   of LDS.
  *   pipeline        a tbg_pipeline value.
@@ -257,9 +257,9 @@ tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, con
  * matrix units reach their peak with 16-bit formats and shorter ones still, like FP8).  A and B
  * are both of type ab_dtype:
  *   TBG_BF16, TBG_F16   as tbg_gemm_configured.  fp16 inputs are built for the configurations
- *                       the automatic choice uses (ring 256x256, 256x128, 128x256, 128x128,
- *                       64x64 with 2 stages; producer 256x128 and 128x256 with 2 stages, 128x128
- *                       and 64x64 with 3); others are UNSUPPORTED.
+ *                       the automatic choice uses (ring 256x256, 256x128, 128x256, 128x128
+ *                       with 2 stages, 64x64 with 2 and 3; producer 256x128 and 128x256 with 2
+ *                       stages, 128x128 and 64x64 with 3); others are UNSUPPORTED.
  *   TBG_F8_E4M3, TBG_F8_E5M2
  *                       8-bit inputs on the 16x16x128 matrix instruction.  B must be stored N×K
  *                       (TBG_B_NK; TBG_B_KN is UNSUPPORTED); lda, ldb in elements (bytes); rows

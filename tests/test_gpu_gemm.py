@@ -461,7 +461,7 @@ def test_gemm_alpha_beta(ops, orc, pipeline, tile):
 
 
 F16_CONFIGS = [("ring", "256x256", 2), ("ring", "256x128", 2), ("ring", "128x256", 2), ("ring", "128x128", 2),
-               ("ring", "64x64", 2), ("producer", "256x128", 2), ("producer", "128x256", 2), ("producer", "128x128", 3),
+               ("ring", "64x64", 2), ("ring", "64x64", 3), ("producer", "256x128", 2), ("producer", "128x256", 2), ("producer", "128x128", 3),
                ("producer", "64x64", 3)]
 
 

@@ -123,6 +123,7 @@ const GemmVariant kVariants[] = {
     {kPipeRing, 128, 256, 2, 1, &launch_ring<128, 256, 2, 1>},
     {kPipeRing, 128, 128, 2, 1, &launch_ring<128, 128, 2, 1>},
     {kPipeRing, 64, 64, 2, 1, &launch_ring<64, 64, 2, 1>},
+    {kPipeRing, 64, 64, 3, 1, &launch_ring<64, 64, 3, 1>},
     {kPipeProducer, 256, 128, 2, 1, &launch_pc<256, 128, 2, 1>},
     {kPipeProducer, 128, 256, 2, 1, &launch_pc<128, 256, 2, 1>},
     {kPipeProducer, 128, 128, 3, 1, &launch_pc<128, 128, 3, 1>},
@@ -173,7 +174,7 @@ struct Candidate {
 const Candidate kCandidates[] = {
     {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 128, 256, 2, 0.83}, {kPipeProducer, 256, 128, 2, 0.81},
     {kPipeRing, 128, 128, 2, 0.81},     {kPipeRing, 256, 128, 2, 0.75},     {kPipeRing, 128, 256, 2, 0.75},
-    {kPipeProducer, 128, 128, 3, 0.69}, {kPipeRing, 64, 64, 2, 0.48},       {kPipeProducer, 64, 64, 3, 0.37},
+    {kPipeProducer, 128, 128, 3, 0.69}, {kPipeRing, 64, 64, 3, 0.48},       {kPipeProducer, 64, 64, 3, 0.37},
 };
 }  // namespace
 

@@ -8,4 +8,5 @@ template hipError_t launch_ring<256, 128, 2, 1>(const GemmParams&, int, int, hip
 template hipError_t launch_ring<128, 256, 2, 1>(const GemmParams&, int, int, hipStream_t);
 template hipError_t launch_ring<128, 128, 2, 1>(const GemmParams&, int, int, hipStream_t);
 template hipError_t launch_ring<64, 64, 2, 1>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_ring<64, 64, 3, 1>(const GemmParams&, int, int, hipStream_t);
 }  // namespace tbg
