@@ -242,9 +242,8 @@ __device__ __forceinline__ int park_xor(int r) {
 // row segments.  Whole-row stores are non-temporal: C is written once and not read again here,
 // so it should not push operand tiles out of the caches.  With SCALED the park keeps the fp32
 // sums and each piece becomes alpha·S + beta·C_old (C_old read only when beta != 0) before it is
-// rounded to C's type ("GEMM" page, tensor-core section: C <- alpha·A·B + beta·C).  A park
-// smaller than the block takes it in bands of fragment rows.
-template <class T, int OUT, int SCALED, int PARK_BYTES = T::RingBytes / 4>
+// rounded to C's type ("GEMM" page, tensor-core section: C <- alpha·A·B + beta·C).
+template <class T, int OUT, int SCALED>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], uint8_t* park, const GemmParams& p,
                                           int row0, int col0, int lane) {
   constexpr int ES = OUT == 1 ? 2 : 4;                     // element size of C
@@ -252,7 +251,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[T::FN][T::FM], u
   constexpr int RowBytes = T::TN * PES;
   constexpr int CPR = RowBytes / 16;
   constexpr int EPC = 16 / PES;  // elements per 16-byte park chunk
-  constexpr int ParkBytes = PARK_BYTES;  // this wave's park
+  constexpr int ParkBytes = T::RingBytes / 4;
   constexpr int Bands = (T::TM * RowBytes + ParkBytes - 1) / ParkBytes;
   constexpr int BandFM = T::FM / Bands;
   constexpr int BandRows = 16 * BandFM;
