@@ -371,7 +371,11 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
              f"| GEMM | WRITE_SIZE | {statistics.median(gemm_w):.1f} | {len(gemm_w)} | {sw:.4f} | {wb:.4g} |", "",
              f"HBM bytes per GEMM launch: {total:.4g} (algorithmic minimum A + B + C once: {algo:.4g}; "
              f"ratio {total / algo:.2f}).",
-             f"Kernel source hash at collection: {kernel_source_hash()}"]
+             (f"Over the kernel trace's average launch ({gemm_avg[0]:.1f} us): {total / (gemm_avg[0] * 1e-6) / 1e9:.0f} "
+              f"GB/s of these bytes, {100 * total / (gemm_avg[0] * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f} % of the 8 TB/s HBM "
+              f"peak; the algorithmic bytes alone: {algo / (gemm_avg[0] * 1e-6) / 1e9:.0f} GB/s." if gemm_avg else ""),
+             f"Kernel source hash of the tree summarized (the counter runs are taken on that same tree): "
+             f"{kernel_source_hash()}"]
     with open(os.path.join(out_dir, "gemm_8192_hbm_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     traffic = {"kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": round(total),
