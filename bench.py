@@ -109,7 +109,7 @@ def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16"):
     return region / steps, sum(per) / len(per), wall_ms / steps
 
 
-def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20):
+def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20, config=None):
     """GPU time per product with the host out of the way: `calls` products captured in one HIP
     graph (torch.cuda.graph), replayed `replays` times; returns ms per product."""
     import workloads
@@ -126,13 +126,13 @@ def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20):
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         for _ in range(3):
-            torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+            torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws, config=config)
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for _ in range(calls):
-            torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws)
+            torch_ops.gemm(Av, Bv, w.b_layout, w.out_dtype, out=C, workspace=ws, config=config)
     g.replay()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -533,10 +533,104 @@ def sweep(torch, torch_ops, names, steps, warmup):
             tf = w.flops / (ms * 1e-3) / 1e12
             r = {"workload": name, "pipeline": pipe, "tile": tile, "stages": st, "ms": round(ms, 5),
                  "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_TFLOPS[ab], 2)}
+            if ab == "bf16" and wname in ("c1", "c2", "c3"):
+                # launch-bound products: the GPU time per product from graph replays as well
+                gms = time_gemm_graph(torch, torch_ops, w, config=cfg)
+                r["graph_ms"] = round(gms, 5)
+                r["graph_tflops"] = round(w.flops / (gms * 1e-3) / 1e12, 2)
             print(json.dumps(r), flush=True)
             results.append(r)
         torch.cuda.empty_cache()
     return results
+
+
+SWEEP_CMD = "python -u bench.py --sweep c1,c2,c3,c4,c5,conv_b,c4@f16,c4@f8e4m3,c5@f8e4m3 > <out>/sweep.jsonl"
+
+
+def write_sweep_profiles(jsonl: str, out_dir: str) -> None:
+    """profiles/gemm_pipeline_sweep.md, gemm_f16_f8_sweep.md and conv_pipeline_sweep.md from the
+    JSON lines of one `--sweep` run: one table per workload, the fastest configuration marked
+    (by GPU time from graph replays where measured), and for the bf16 configurations the throughput
+    on c4 and c5 relative to the 256x256 ring (the efficiencies of the automatic choice)."""
+    import workloads
+    rows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    by = {}
+    for r in rows:
+        by.setdefault(r["workload"], []).append(r)
+    desc = {"c1": "256³ (B K×N, fp32 out)", "c2": "1024³ (B K×N, bf16 out)",
+            "c3": "3001×2049×777 (B K×N, fp32 out, repack path)", "c4": "8192³ (B K×N, bf16 out)",
+            "c5": "16384×14336×4096 (B N×K, bf16 out)", "c4@f16": "8192³, fp16 inputs",
+            "c4@f8e4m3": "8192³, E4M3 inputs (B N×K)", "c5@f8e4m3": "16384×14336×4096, E4M3 inputs"}
+
+    def table(name, rs, peak_note):
+        graph = any("graph_ms" in r for r in rs)
+        key = (lambda r: r["graph_ms"]) if graph else (lambda r: r["ms"])
+        best = min(key(r) for r in rs)
+        lines = [f"## {name}: {desc.get(name, name)}", ""]
+        if graph:
+            lines += ["| pipeline | tile | stages | µs per call | µs GPU (graph) | TFLOP/s (graph) | % peak (graph) |",
+                      "|---|---|---|---|---|---|---|"]
+            for r in rs:
+                b = " **best**" if key(r) == best else ""
+                lines.append(f"| {r['pipeline']} | {r['tile']} | {r['stages']} | {1e3 * r['ms']:.1f} | "
+                             f"{1e3 * r['graph_ms']:.2f} | {r['graph_tflops']}{b} | "
+                             f"{100 * r['graph_tflops'] / peak_note:.2f} |")
+        else:
+            lines += ["| pipeline | tile | stages | µs | TFLOP/s | % peak |", "|---|---|---|---|---|---|"]
+            for r in rs:
+                b = " **best**" if key(r) == best else ""
+                lines.append(f"| {r['pipeline']} | {r['tile']} | {r['stages']} | {1e3 * r['ms']:.1f} | "
+                             f"{r['tflops']}{b} | {r['pct_peak']} |")
+        return lines + [""]
+
+    head = ["Command (repository root on the GPU box; <out> an output folder), then "
+            "`python bench.py --sweep-md <out>/sweep.jsonl`:", "", "```", SWEEP_CMD, "```", "",
+            "Each configuration: 20 timed calls after 5 warm-up calls, HIP events on the launch stream (per-call "
+            "times include the host); for c1-c3 also 20 products captured in a HIP graph and replayed 20 times "
+            "(GPU time per product).  One pass on one MI355X; boxes differ by a few per cent.", ""]
+    # bf16 GEMM
+    lines = ["# GEMM pipeline × tile × stages sweep", "",
+             "Every built configuration of `tbg_gemm_configured` (barrier ring and producer/consumer ring, each "
+             "workgroup tile, each stage count that fits LDS and the vmcnt counter).  % of the 2516.6 TFLOP/s dense "
+             "bf16 peak.", ""] + head
+    rel = {}
+    for name in ("c4", "c5"):
+        rs = by.get(name, [])
+        ref = [r["tflops"] for r in rs if r["pipeline"] == "ring" and r["tile"] == "256x256"]
+        for r in rs:
+            if ref:
+                rel.setdefault((r["pipeline"], r["tile"], r["stages"]), []).append(r["tflops"] / ref[0])
+    if rel:
+        lines += ["Throughput relative to the 256×256 ring on c4 and c5 (the automatic choice's efficiencies are "
+                  "taken from these):", "", "| pipeline | tile | stages | c4 | c5 | mean |", "|---|---|---|---|---|---|"]
+        for (pipe, tile, st), v in rel.items():
+            cells = " | ".join(f"{x:.2f}" for x in v) + (" | " if len(v) == 1 else "")
+            lines.append(f"| {pipe} | {tile} | {st} | {cells} | {sum(v) / len(v):.2f} |")
+        lines.append("")
+    for name in ("c1", "c2", "c3", "c4", "c5"):
+        if name in by:
+            lines += table(name, by[name], PEAK_BF16_TFLOPS)
+    with open(os.path.join(out_dir, "gemm_pipeline_sweep.md"), "w") as f:
+        f.write("\n".join(lines))
+    # fp16 / fp8
+    lines = ["# fp16 and fp8 GEMM configurations: 8192³ and 16384×14336×4096", "",
+             "Inputs: the workload's values converted to the input type; 8-bit inputs take B stored N×K.  Peaks: "
+             "fp16 2516.6 TFLOP/s, fp8 5033.2 TFLOP/s (dense).", ""] + head
+    for name in ("c4@f16", "c4@f8e4m3", "c5@f8e4m3"):
+        if name in by:
+            lines += table(name, by[name], PEAK_TFLOPS[name.partition("@")[2]])
+    with open(os.path.join(out_dir, "gemm_f16_f8_sweep.md"), "w") as f:
+        f.write("\n".join(lines))
+    # convolution
+    cw = workloads.CONVS["conv_b"]
+    lines = ["# Implicit-GEMM convolution: tile sweep on the benchmark layer", "",
+             f"Layer conv_b: batch {cw.n}, {cw.h}×{cw.w}, {cw.c} → {cw.k} channels, {cw.r}×{cw.s} filter, padding 1, "
+             f"bf16 in, fp32 accumulate, bf16 out (NHWC / KRSC / NHWK).  As a GEMM: {cw.M} × {cw.k} × "
+             f"{cw.r * cw.s * cw.c}.  Ring, two stages; tile forced through the configuration.", ""] + head
+    if "conv_b" in by:
+        lines += table("conv_b", by["conv_b"], PEAK_BF16_TFLOPS)
+    with open(os.path.join(out_dir, "conv_pipeline_sweep.md"), "w") as f:
+        f.write("\n".join(lines))
 
 
 def main():
@@ -546,6 +640,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--sweep-md", default="", metavar="JSONL",
+                    help="write the sweep summaries in profiles/ from the JSON lines of a --sweep run (no GPU needed)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the products-alone ceiling measured next to the GEMM (roofline.ceiling)")
     ap.add_argument("--only-copies", action="store_true",
@@ -569,6 +665,10 @@ def main():
               "by rows or columns of C with no exchange, which this single-GPU build does not run.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep_md:
+        write_sweep_profiles(args.sweep_md, os.path.join(ROOT, "profiles"))
+        return
 
     if args.summarize:
         d = args.summarize

@@ -163,18 +163,18 @@ const char* gemm_configs_text(int pipeline, int in) {
 // the 256×256 ring (measured with the configuration sweep of bench.py).  Fragment reads and copies
 // per product grow as the tile shrinks; the 128×128 ring and the 64×64 tiles run two workgroups
 // per compute unit; with dedicated producer waves the 256×128 and 128×256 tiles keep their
-// compute waves free of copy instructions and run 18 % faster than as a ring, while the 128×128
-// and 64×64 tiles lose the second workgroup per compute unit to the extra waves or the deeper
-// ring and run slower.  Deeper rings lose occupancy and never win at the default.
+// compute waves free of copy instructions and run ≈8 % faster than as a two-stage ring, while the
+// 128×128 and 64×64 tiles lose the second workgroup per compute unit to the extra waves and run
+// slower.
 namespace {
 struct Candidate {
   int pipeline, bm, bn, stages;
   double eff;
 };
 const Candidate kCandidates[] = {
-    {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 128, 256, 2, 0.83}, {kPipeProducer, 256, 128, 2, 0.81},
-    {kPipeRing, 128, 128, 2, 0.81},     {kPipeRing, 256, 128, 2, 0.75},     {kPipeRing, 128, 256, 2, 0.75},
-    {kPipeProducer, 128, 128, 3, 0.69}, {kPipeRing, 64, 64, 3, 0.48},       {kPipeProducer, 64, 64, 3, 0.37},
+    {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 128, 256, 2, 0.79}, {kPipeProducer, 256, 128, 2, 0.77},
+    {kPipeRing, 128, 128, 2, 0.79},     {kPipeRing, 256, 128, 2, 0.72},     {kPipeRing, 128, 256, 2, 0.71},
+    {kPipeProducer, 128, 128, 3, 0.65}, {kPipeRing, 64, 64, 3, 0.44},       {kPipeProducer, 64, 64, 3, 0.35},
 };
 }  // namespace
 
