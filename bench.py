@@ -16,7 +16,8 @@ Also reported in the same line:
                 timed on this host's cores.
   per_config    TFLOP/s and % of peak on all five GEMM workloads (for the small c1-c3 also the
                 GPU time per product from HIP-graph replays, `graph_ms`), the 8192³ product with fp16 and
-                with fp8 E4M3 inputs (against the fp8 peak), the benchmark convolution layer
+                with fp8 E4M3 inputs (against the fp8 peak, with the fp8 products-alone ceiling
+                measured the same way as the bf16 one), the benchmark convolution layer
                 (timed the same way, fewer steps), and the tiled-copy kernel (tbg_tiled_copy_many)
                 on the three copy workloads: the worked 128x64 box at its 10 places, the 432 boxes of
                 the 5-D tensor with NaN fill, and all 8192 boxes of the 8192x8192 operand A, each
@@ -187,9 +188,10 @@ def time_copy(torch, torch_ops, w, steps, warmup):
     return ms, copy_inbounds_bytes(w) + len(w.coords) * tbg.box_bytes(desc)
 
 
-def mfma_ceiling(torch, launches: int = 60, warmup: int = 60):
-    """The bf16 matrix products alone (tiled_bf16_gemm_amd/diag/mfma_rate.hip): 16x16x32 products
-    back to back on register-resident random operands, one workgroup of four waves per CU as the
+def mfma_ceiling(torch, kind: int = 0, launches: int = 60, warmup: int = 60):
+    """The matrix products alone (tiled_bf16_gemm_amd/diag/mfma_rate.hip): kind 0 bf16 16x16x32
+    products on uniform[-1,1] bf16 operands, kind 1 fp8 16x16x128 products on the same values as
+    E4M3, back to back on register-resident fragments, one workgroup of four waves per CU as the
     256x256 GEMM tile, four rounds of workgroups like the 8192^3 product.  Returns (TFLOP/s, median
     shader clock in GHz from the kernel's own counters): the ceiling of any GEMM kernel at the clock
     the power limit allows with such operands."""
@@ -200,18 +202,21 @@ def mfma_ceiling(torch, launches: int = 60, warmup: int = 60):
         raise RuntimeError(f"{here} is not built: run __graft_entry__.build()")
     lib = ctypes.CDLL(here)
     lib.tbg_diag_mfma_rate.restype = ctypes.c_int
-    lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                       ctypes.c_void_p]
+    lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     nwg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     iters = 200
     g = torch.Generator().manual_seed(77)
-    src = (torch.rand(nwg * 16 * 256 * 8, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    if kind == 0:
+        src = (torch.rand(nwg * 16 * 256 * 8, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    else:
+        src = (torch.rand(nwg * 16 * 256 * 16, generator=g) * 2 - 1).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
     out = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
     clk = torch.zeros(2 * nwg, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
     def go():
-        rc = lib.tbg_diag_mfma_rate(src.data_ptr(), out.data_ptr(), nwg, iters, clk.data_ptr(), stream)
+        rc = lib.tbg_diag_mfma_rate(kind, src.data_ptr(), out.data_ptr(), nwg, iters, clk.data_ptr(), stream)
         if rc != 0:
             raise RuntimeError(f"mfma rate launch failed ({rc})")
     for _ in range(warmup):
@@ -224,7 +229,8 @@ def mfma_ceiling(torch, launches: int = 60, warmup: int = 60):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / launches
-    flops = nwg * 4 * iters * 64 * 16384  # 16x16x32 product: 8192 multiply-adds, 16384 flops
+    # a 16x16x32 product is 8192 multiply-adds (16384 flops), a 16x16x128 one four times that
+    flops = nwg * 4 * iters * 64 * (16384 if kind == 0 else 65536)
     c = clk.cpu().tolist()
     ghz = statistics.median(c[2 * i + 1] / (c[2 * i] / 100e6) / 1e9 for i in range(nwg) if c[2 * i] > 0)
     return flops / (ms * 1e-3) / 1e12, ghz
@@ -758,10 +764,17 @@ def main():
 
     ceiling = None
     if not args.no_ceiling:
-        c_tf, c_ghz = mfma_ceiling(torch)
+        c_tf, c_ghz = mfma_ceiling(torch, 0)
         ceiling = {"what": "bf16 16x16x32 products alone on register-resident random operands (no loads, no stores), "
                            "same process, after the GEMM", "tflops": round(c_tf, 1), "clock_ghz": round(c_ghz, 3),
                    "frac_of_peak": round(c_tf / PEAK_BF16_TFLOPS, 4)}
+    if ceiling and "c4_f8e4m3" in per_config:
+        f_tf, f_ghz = mfma_ceiling(torch, 1)
+        fc = per_config["c4_f8e4m3"]
+        fc["ceiling"] = {"what": "fp8 16x16x128 products alone on register-resident random E4M3 operands",
+                         "tflops": round(f_tf, 1), "clock_ghz": round(f_ghz, 3),
+                         "frac_of_peak": round(f_tf / PEAK_TFLOPS["f8e4m3"], 4)}
+        fc["frac_of_ceiling"] = round(fc["tflops"] / f_tf, 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     line = {

@@ -449,10 +449,11 @@ def test_benchmark_ceiling_library():
     path = os.path.join(os.path.dirname(tbg.library_path()), "diag", "libtbg_diag.so")
     lib = ctypes.CDLL(path)
     lib.tbg_diag_mfma_rate.restype = ctypes.c_int
-    lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                       ctypes.c_void_p]
-    assert lib.tbg_diag_mfma_rate(None, None, 0, 1, None, None) != 0
-    assert lib.tbg_diag_mfma_rate(BASE, BASE, 4, 0, BASE, None) != 0
+    lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tbg_diag_mfma_rate(0, None, None, 0, 1, None, None) != 0
+    assert lib.tbg_diag_mfma_rate(0, BASE, BASE, 4, 0, BASE, None) != 0
+    assert lib.tbg_diag_mfma_rate(2, BASE, BASE, 4, 1, BASE, None) != 0
     main = subprocess.run(["nm", "-D", "--defined-only", tbg.library_path()], capture_output=True, text=True,
                           check=True).stdout
     assert "tbg_diag_mfma_rate" not in main, "the measurement aid must stay out of the library's ABI"
