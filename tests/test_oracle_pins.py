@@ -109,3 +109,30 @@ def test_broken_oracle_fails_a_pin(tmp_path, desc, old, new):
     line = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED_PINS")][0]
     failures = [x for x in line.split(" ", 1)[1].split(",") if x]
     assert failures, f"no pin catches: {desc}"
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    """Every pin against a build of ``oracle.c`` with AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code only): an out-of-bounds access, a use of freed memory, a signed overflow or a shift
+    out of range anywhere the pins reach aborts the child and fails the test."""
+    libasan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    libubsan = subprocess.run(["gcc", "-print-file-name=libubsan.so"], capture_output=True, text=True).stdout.strip()
+    if not (os.path.isabs(libasan) and os.path.exists(libasan) and os.path.isabs(libubsan)):
+        pytest.skip("gcc's sanitizer runtimes are not installed")
+    out = str(tmp_path / "liboracle_san.so")
+    subprocess.run(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+                    oracle_build.SRC, "-o", out], check=True)
+    child = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import oracle\n"
+        "from tests import oracle_pins\n"
+        "o = oracle.Oracle(%r)\n"
+        "for pin in oracle_pins.ALL_PINS:\n"
+        "    pin(o)\n"
+        "print('ALL_PINS_PASSED', len(oracle_pins.ALL_PINS))\n"
+    ) % (ROOT, out)
+    env = dict(os.environ, LD_PRELOAD=f"{libasan}:{libubsan}", ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-c", child], capture_output=True, text=True, timeout=900, env=env)
+    assert r.returncode == 0 and "ALL_PINS_PASSED" in r.stdout, (r.stdout[-2000:] + r.stderr[-4000:])
