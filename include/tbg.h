@@ -22,6 +22,9 @@
  *   - No exception crosses the ABI.  tbg_last_error() gives a readable detail of the last
  *     failure on the calling thread.
  *   - Every array of per-dimension values is ordered innermost dimension first ([MAP] §8.2).
+ *   - With the environment variable TBG_LOG set to a value other than "" or "0", every GEMM and
+ *     convolution call prints the kernel configuration it launches (pipeline, tile, stages, which
+ *     operands were repacked) as one line on stderr.
  */
 #ifndef TBG_H_
 #define TBG_H_

@@ -8,6 +8,7 @@ benchmark times — are compared on sampled whole rows and scattered points, and
 finiteness and run-to-run determinism everywhere; with integer operands whose product the output
 type holds exactly, every entry of those two products is checked through Freivalds' identities
 (C·x and yᵀ·C against A·(B·x) and (yᵀ·A)·B, exact in binary64)."""
+import os
 import sys
 
 import numpy as np
@@ -257,6 +258,33 @@ def test_repack_many_rows(ops, orc):
     exact = A[want_rows].astype(np.float64) @ Bbuf[:, :N].astype(np.float64)
     assert np.array_equal(got[want_rows], exact.astype(np.float32))
     _freivalds_exact(got, A, Bbuf[:, :N], "kn", 3, "repacked rows")
+
+
+@gpu
+def test_log_reports_the_choice(ops):
+    """TBG_LOG=1 makes each call print the configuration it launches; a child process (the
+    variable is read once per process) runs the 1024³ product and the ragged 3001×2049×777 one."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    child = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import torch\n"
+        "from tiled_bf16_gemm_amd import torch_ops\n"
+        "a = torch.ones(1024, 1024, dtype=torch.bfloat16, device='cuda')\n"
+        "torch_ops.gemm(a, a, 'kn', 'bf16')\n"
+        "b = torch.ones(3001, 777, dtype=torch.bfloat16, device='cuda')\n"
+        "c = torch.ones(777, 2049, dtype=torch.bfloat16, device='cuda')\n"
+        "torch_ops.gemm(b, c, 'kn', 'f32')\n"
+        "torch.cuda.synchronize()\n"
+    ) % root
+    _say("TBG_LOG child process")
+    r = subprocess.run([sys.executable, "-c", child], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, TBG_LOG="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("tbg: gemm")]
+    assert len(lines) == 2, r.stderr[-2000:]
+    assert "M=1024 N=1024 K=1024 B=kn in=bf16 out=bf16: ring 64x64, 3 stages; repack A no, B no" in lines[0]
+    assert "M=3001 N=2049 K=777" in lines[1] and "repack A yes, B yes" in lines[1]
 
 
 TILES = ["256x256", "256x128", "128x256", "128x128", "64x64"]

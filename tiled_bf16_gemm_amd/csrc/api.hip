@@ -107,6 +107,22 @@ int64_t conv_out_dim(int64_t in, int64_t pad_lo, int64_t pad_hi, int64_t stride,
   return span / stride + 1;
 }
 
+// TBG_LOG set to anything but "" or "0": every GEMM and convolution call reports the kernel
+// configuration it launches on stderr (read once per process).
+void log_choice(const char* fmt, ...) {
+  static const bool on = [] {
+    const char* v = getenv("TBG_LOG");
+    return v && *v && strcmp(v, "0") != 0;
+  }();
+  if (!on) return;
+  va_list ap;
+  va_start(ap, fmt);
+  fputs("tbg: ", stderr);
+  vfprintf(stderr, fmt, ap);
+  fputc('\n', stderr);
+  va_end(ap);
+}
+
 int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
@@ -582,6 +598,9 @@ tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const voi
       }
     }
   }
+  log_choice("gemm M=%lld N=%lld K=%lld B=nk in=%s out=%s: ring %dx%d, 2 stages; repack A %s, B %s", (long long)M,
+             (long long)N, (long long)K, ab_dtype == TBG_F8_E5M2 ? "e5m2" : "e4m3", c_dtype == TBG_BF16 ? "bf16" : "f32",
+             bm, bn, pack_a ? "yes" : "no", pack_b ? "yes" : "no");
   e = tbg::launch_fp8(p, bm, bn, ab_dtype == TBG_F8_E5M2 ? 1 : 0, c_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "fp8 gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
@@ -702,6 +721,10 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
+  log_choice("gemm M=%lld N=%lld K=%lld B=%s in=%s out=%s: %s %dx%d, %d stages; repack A %s, B %s", (long long)M,
+             (long long)N, (long long)K, bl == TBG_B_KN ? "kn" : "nk", in ? "f16" : "bf16",
+             c_dtype == TBG_BF16 ? "bf16" : "f32", ch.pipeline == tbg::kPipeProducer ? "producer" : "ring", ch.bm,
+             ch.bn, ch.stages, pl.pack_a ? "yes" : "no", pl.pack_b ? "yes" : "no");
   e = tbg::launch_gemm(p, ch.pipeline, ch.bm, ch.bn, ch.stages, (int)bl, c_dtype == TBG_BF16, s, in);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return TBG_OK;
@@ -918,6 +941,9 @@ tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void
     bm = cfg->tile_m;
     bn = cfg->tile_n;
   }
+  log_choice("conv2d N=%lld H=%lld W=%lld C=%lld K=%lld %dx%d (GEMM %lld x %lld x %lld): ring %dx%d, 2 stages",
+             (long long)shape->n, (long long)shape->h, (long long)shape->w, (long long)shape->c, (long long)shape->k,
+             shape->r, shape->s, (long long)cp.g.M, (long long)cp.g.N, (long long)(shape->r * shape->s * cp.c8), bm, bn);
   e = tbg::launch_conv(cp, bm, bn, y_dtype == TBG_BF16, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "convolution launch: %s", hipGetErrorString(e));
   return TBG_OK;
