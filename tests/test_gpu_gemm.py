@@ -287,6 +287,38 @@ def test_log_reports_the_choice(ops):
     assert "M=3001 N=2049 K=777" in lines[1] and "repack A yes, B yes" in lines[1]
 
 
+@gpu
+def test_concurrent_streams(ops):
+    """Products on two streams at once (the library keeps no device state between calls: every
+    kernel's scratch is its own LDS, the repack goes to each caller's workspace) give the same
+    bits as the same products run one after another."""
+    rng = np.random.default_rng(31)
+    shapes = [(1024, 1024, 1024, "kn"), (3001, 2049, 777, "kn"), (512, 768, 4096, "nk"), (300, 257, 136, "nk")]
+    cases = []
+    for M, N, K, bl in shapes:
+        A = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16).cuda()
+        Bs = (K, N) if bl == "kn" else (N, K)
+        B = torch.from_numpy(rng.standard_normal(Bs).astype(np.float32)).to(torch.bfloat16).cuda()
+        cases.append((A, B, bl))
+    torch.cuda.synchronize()
+    want = [ops.gemm(A, B, bl, "f32") for A, B, bl in cases]
+    torch.cuda.synchronize()
+    _say("two streams, four products each, interleaved")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[None] * len(cases) for _ in streams]
+    for _ in range(4):
+        for si, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                order = list(range(si, len(cases), 2)) + list(range(1 - si, len(cases), 2))
+                for idx in order:
+                    A, B, bl = cases[idx]
+                    outs[si][idx] = ops.gemm(A, B, bl, "f32", stream=st)
+    torch.cuda.synchronize()
+    for si in range(2):
+        for ci in range(len(cases)):
+            assert torch.equal(outs[si][ci].view(torch.int32), want[ci].view(torch.int32)), f"stream {si} case {ci}"
+
+
 TILES = ["256x256", "256x128", "128x256", "128x128", "64x64"]
 
 
