@@ -160,6 +160,43 @@ def copy_inbounds_bytes(w) -> int:
     return total
 
 
+def time_copy_graph(torch, torch_ops, w, calls=20, replays=20):
+    """GPU time per tbg_tiled_copy_many launch from HIP-graph replays (as time_gemm_graph)."""
+    import workloads
+    import tiled_bf16_gemm_amd as tbg
+    src = workloads.copy_source(w).cuda()
+    d = list(w.dims)
+    strides, acc = [], 2
+    for i in range(len(d) - 1):
+        acc *= d[i]
+        strides.append(acc)
+    desc = torch_ops.encode(src, w.dtype, d, strides, list(w.box), list(w.estr), w.swizzle, w.oob)
+    coords = torch.tensor([list(c) for c in w.coords], dtype=torch.int32, device="cuda").contiguous()
+    out = torch.empty(len(w.coords) * tbg.box_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            torch_ops.tiled_copy_many(desc, coords, out=out, stream=stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(calls):
+            torch_ops.tiled_copy_many(desc, coords, out=out, stream=stream)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / (replays * calls)
+    del g
+    return ms
+
+
 def time_copy(torch, torch_ops, w, steps, warmup):
     """tbg_tiled_copy_many over every box of a copy workload, one launch per step; returns (mean
     per-launch ms from events, algorithmic bytes per launch = in-bounds source bytes + images)."""
@@ -754,6 +791,11 @@ def main():
                                 "swizzle": cw.swizzle, "oob": cw.oob, "bytes": nbytes, "ms": round(ms_c, 5),
                                 "gb_per_s": round(gbs, 1), "peak_gb_per_s": PEAK_HBM_GBS,
                                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            if name != "c4_a_boxes":
+                # launch-bound copies: the GPU time per launch from graph replays as well
+                gms = time_copy_graph(torch, torch_ops, cw)
+                per_config[name]["graph_ms"] = round(gms, 5)
+                per_config[name]["graph_gb_per_s"] = round(nbytes / (gms * 1e-3) / 1e9, 1)
             torch.cuda.empty_cache()
         cw = workloads.CONVS["conv_b"]
         s_, _ = time_conv(torch, torch_ops, cw, 50, 20)
