@@ -30,7 +30,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-SWIZZLE_MODES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
+SWIZZLE_MODES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4, "128B_TR": 5}
 # element type -> (element size, NaN kind understood by oracle.c; 0 = integer, no NaN)
 DTYPES = {
     "u8": (1, 0), "u16": (2, 0), "u32": (4, 0),
@@ -326,13 +326,24 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def gemm_check(got: np.ndarray, ref32: np.ndarray, rtol: float = 1e-2, atol: float = 1e-3) -> dict:
-    """O4: a GPU value g passes iff it is finite and |g − r| ≤ max(rtol·|r|, atol), where r is the
-    oracle's binary32 result (before any bf16 rounding).  Returns the statistics and the verdict."""
+def gemm_check(got: np.ndarray, ref32: np.ndarray, rtol: float = 1e-2, atol: float = 1e-3,
+               extra: Optional[np.ndarray] = None) -> dict:
+    """O4: a GPU value g passes iff it is finite and |g − r| ≤ max(rtol·|r|, atol) (+ extra, when
+    given: a per-entry widening of the bound, see gemm_check_f8), where r is the oracle's binary32
+    result (before any bf16 rounding).  The tolerance is the one the GEMM's contract fixes: 1e-2
+    relative, 1e-3 absolute on entries below 0.1 in magnitude, where 1e-2·|r| < 1e-3.  `got` and
+    `ref32` must have the same shape (no broadcasting).  Returns the statistics and the verdict."""
     g = np.asarray(got, dtype=np.float64)
     r = np.asarray(ref32, dtype=np.float64)
+    if g.shape != r.shape:
+        raise ValueError(f"result shape {g.shape} differs from the reference shape {r.shape}")
     err = np.abs(g - r)
     bound = np.maximum(rtol * np.abs(r), atol)
+    if extra is not None:
+        e = np.asarray(extra, dtype=np.float64)
+        if e.shape != r.shape:
+            raise ValueError(f"bound widening shape {e.shape} differs from the reference shape {r.shape}")
+        bound = bound + e
     finite = np.isfinite(g)
     ok = finite & (err <= bound)
     rel = err / np.maximum(np.abs(r), 1e-30)
@@ -344,3 +355,28 @@ def gemm_check(got: np.ndarray, ref32: np.ndarray, rtol: float = 1e-2, atol: flo
         "max_rel_err": float(np.where(np.abs(r) >= atol / rtol, rel, 0.0).max()) if g.size else 0.0,
         "n_abs_branch": int((np.abs(r) < atol / rtol).sum()),
     }
+
+
+# The 8-bit matrix instruction's own error, a hardware characterisation (not from the pages, which
+# fix only fp32 accumulation): gfx950's 16×16×128 fp8 product adds its 128 exact products with
+# about 16 significant bits relative to the sum of their magnitudes.  The GPU test
+# test_fp8_instruction_error measures it on single instructions (K = 128) and requires at most
+# 2^-15 · Σ|a_k·b_k|; fp8 results are checked with four times that.
+F8_DOT_BOUND = 2.0 ** -13
+
+
+def gemm_check_f8(got: np.ndarray, ref32: np.ndarray, a_vals: np.ndarray, b_vals_nk: np.ndarray,
+                  dot_bound: float = F8_DOT_BOUND) -> dict:
+    """O4 for 8-bit float inputs: gemm_check with each entry's bound widened by
+    dot_bound · Σ_k |A[m,k]|·|B[n,k]| (binary64), the matrix instruction's forward error.
+    a_vals (M×K) and b_vals_nk (N×K) are the decoded input values; B is stored N×K."""
+    a = np.abs(np.asarray(a_vals, dtype=np.float64))
+    b = np.abs(np.asarray(b_vals_nk, dtype=np.float64))
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"operands {a.shape} and {b.shape} are not M×K and N×K")
+    absum = a @ b.T
+    r = gemm_check(got, ref32, extra=dot_bound * absum)
+    g = np.asarray(got, dtype=np.float64)
+    err = np.abs(g - np.asarray(ref32, dtype=np.float64))
+    r["max_err_over_abs_dot"] = float((err / np.maximum(absum, 1e-30)).max()) if g.size else 0.0
+    return r
