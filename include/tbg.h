@@ -63,13 +63,23 @@ typedef enum {
  * which serves 16 lanes of a 16-byte read per cycle from 64 four-byte banks (256 bytes):
  *   a' = a ^ ((a & 0x700) >> 4),  i.e. a[6:4] ^= a[10:8],
  * so sixteen consecutive 128-byte rows read at one logical 16-byte column hit 16 distinct
- * 16-byte bank groups.  It permutes 16-byte units inside each aligned 128-byte block. */
+ * 16-byte bank groups.  It permutes 16-byte units inside each aligned 128-byte block.
+ * TBG_SWIZZLE_128B_TR is the library's layout for a 128-byte-row box read back with gfx950's
+ * transposing 8-byte LDS read (ds_read_b64_tr_b16, which the GEMM uses for B stored K×N): the
+ * 16-byte unit index of 128-byte row r is XORed with 4·r[3] + 2·r[1] + r[2], i.e.
+ *   a[4] ^= a[9],  a[5] ^= a[8],  a[6] ^= a[10]
+ * (not of the single-shift form above).  That read takes 32 bytes from each of the rows
+ * {r0 + 8t + e : t < 2, e < 4} per 32 lanes, served from one 256-byte bank window; this XOR puts
+ * the eight 32-byte pieces on eight distinct 32-byte bank groups, which neither 128B nor
+ * 128B_2ROW does.  It permutes 16-byte units inside each aligned 128-byte block and repeats every
+ * 16 rows (2048 bytes). */
 typedef enum {
     TBG_SWIZZLE_NONE = 0,
     TBG_SWIZZLE_32B = 1,
     TBG_SWIZZLE_64B = 2,
     TBG_SWIZZLE_128B = 3,
-    TBG_SWIZZLE_128B_2ROW = 4
+    TBG_SWIZZLE_128B_2ROW = 4,
+    TBG_SWIZZLE_128B_TR = 5
 } tbg_swizzle;
 
 /* Out-of-bounds fill ([MAP] §14; [TMA] §2.5): box elements outside the tensor are written to
@@ -138,8 +148,11 @@ tbg_status tbg_encode_tiled_interleaved(tbg_tensor_desc* out, tbg_dtype dtype, u
                                         const uint32_t* element_strides, tbg_interleave interleave,
                                         tbg_swizzle swizzle, tbg_l2_hint l2, tbg_oob_fill oob);
 
-/* Bytes of one copy's image for an encoded descriptor (tiled or im2col); 0 if `d` is not a valid
- * descriptor. */
+/* Bytes of one copy's image for an encoded descriptor: for a tiled descriptor elsize times the
+ * product over dimensions of n[i] = ceil(box_dim[i] / element_strides[i]), the elements one copy
+ * lands ("H100 · cuTensorMap" §9.1-§9.2: the box is the traversal extent and every
+ * element_strides[i]-th element along it is copied); for an im2col descriptor elsize * channels *
+ * pixels.  0 if `d` is not a valid descriptor. */
 size_t tbg_box_bytes(const tbg_tensor_desc* d);
 
 /* Copy one box ([TMA] §2.2, §2.4): the element at box position j (innermost first) comes from
@@ -183,6 +196,20 @@ tbg_status tbg_tiled_store_many(const tbg_tensor_desc* d, const int32_t* coords_
  * the leading dimension): A when lda % 8 != 0 or K % 8 != 0; B (N×K) likewise with ldb; B (K×N)
  * when ldb % 8 != 0. */
 size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, tbg_b_layout bl);
+
+/* The exact workspace bytes a product of these sizes and operands needs, for every input type
+ * (tbg_gemm, tbg_gemm_ex, tbg_gemm_configured, tbg_gemm_typed; the same repack rules, [GEMM]
+ * "In pratica": 16-byte leading dimensions, and "I tensor core": packing a block into a
+ * contiguous area).  Unlike tbg_gemm_workspace_bytes it looks at the operands' base addresses
+ * (A and B are only compared against 16-byte boundaries, never dereferenced) and at the type:
+ *   TBG_BF16, TBG_F16  A is repacked when lda % 8, K % 8 or A % 16 is non-zero; B (N×K) likewise
+ *                      with ldb; B (K×N) when ldb % 8 or B % 16 is non-zero;
+ *   TBG_F8_E4M3/E5M2   A (B, stored N×K) is repacked when lda (ldb) % 16, K % 16 or its base
+ *                      % 16 is non-zero, with K rounded up to 16.
+ * Each repack takes its rows at the rounded pitch, 256-byte rounded.  Returns 0 when no repack
+ * is needed, for non-positive sizes or leading dimensions, and for any other ab_dtype. */
+size_t tbg_gemm_workspace_query(int64_t M, int64_t N, int64_t K, tbg_dtype ab_dtype, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, tbg_b_layout bl);
 
 /* C = A·B ([GEMM] "Il conto": C_ij = Σ_k A_ik B_kj, 2MNK flops), bf16 inputs, fp32 accumulation
  * in the matrix cores ([GEMM] tensor-core section), fp32 or bf16 (round to nearest even) output.
@@ -343,6 +370,11 @@ tbg_status tbg_conv2d_out_dims(const tbg_conv2d_shape* shape, int64_t* oh, int64
  * aligned, which this function assumes); else room to repack X and W with the channel pitch
  * rounded up to 8 (zero channels added), 256-byte aligned.  0 for an invalid shape. */
 size_t tbg_conv2d_workspace_bytes(const tbg_conv2d_shape* shape);
+
+/* The exact workspace bytes tbg_conv2d_fwd needs for this shape and these operands: as
+ * tbg_conv2d_workspace_bytes, and also when x or w is not 16-byte aligned (only compared against
+ * 16-byte boundaries, never dereferenced); 0 when nothing is repacked or the shape is invalid. */
+size_t tbg_conv2d_workspace_query(const tbg_conv2d_shape* shape, const void* x, const void* w);
 
 /* Y <- alpha * conv2d(X, W) + beta * Y as an implicit GEMM ([TMA] section "im2col": the im2col
  * matrix of X is formed tile by tile by the operand copies and never stored; [GEMM] the product).

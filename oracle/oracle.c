@@ -74,6 +74,8 @@ uint16_t oracle_f32_to_bf16(float f) {
  * reproduces the 32B row).  mode: 0 none, 1 32B, 2 64B, 3 128B.
  * mode 4 is the library's extension of the same XOR form with the row bits taken one place
  * higher, a ^ ((a & 0x700) >> 4), i.e. a[6:4] ^= a[10:8]; it is defined by that mask and shift.
+ * mode 5 is the library's layout for boxes read back with the transposing 8-byte read; it is
+ * not of that form and is defined bit by bit: a[4] ^= a[9], a[5] ^= a[8], a[6] ^= a[10].
  * ---------------------------------------------------------------------------------------- */
 uint64_t oracle_swizzle_general(uint64_t a, uint64_t y_mask, unsigned shift) {
     return a ^ ((a & y_mask) >> shift);
@@ -86,6 +88,7 @@ uint64_t oracle_swizzle(uint64_t a, int mode) {
         case 2: return oracle_swizzle_general(a, 0x180u, 3);
         case 3: return oracle_swizzle_general(a, 0x380u, 3);
         case 4: return oracle_swizzle_general(a, 0x700u, 4);
+        case 5: return a ^ (((a >> 9) & 1u) << 4) ^ (((a >> 8) & 1u) << 5) ^ (((a >> 10) & 1u) << 6);
         default: return (uint64_t)-1;
     }
 }
@@ -96,7 +99,7 @@ void oracle_swizzle_array(const uint64_t* in, uint64_t* out, int64_t n, int mode
 
 /* Size in bytes of the aligned block inside which a mode permutes 16-byte units. */
 static uint64_t swizzle_span(int mode) {
-    return mode == 1 ? 32u : mode == 2 ? 64u : (mode == 3 || mode == 4) ? 128u : 1u;
+    return mode == 1 ? 32u : mode == 2 ? 64u : (mode == 3 || mode == 4 || mode == 5) ? 128u : 1u;
 }
 
 /* ------------------------------------------------------------------------------------------

@@ -26,8 +26,14 @@ def golden():
 # ---------------------------------------------------------------------------------------------
 # Swizzle ("H100 · cuTensorMap" §11.2–§11.4)
 # ---------------------------------------------------------------------------------------------
-# The library's gfx950 extension mode, stated bit by bit: a[6:4] ^= a[10:8].
-EXT_RULES = {"128B_2ROW": [[6, 10], [5, 9], [4, 8]]}
+# The library's gfx950 extension modes, stated bit by bit (pairs [destination bit, source bit]):
+# 128B_2ROW a[6:4] ^= a[10:8]; 128B_TR (the layout read back with the transposing 8-byte read)
+# a[4] ^= a[9], a[5] ^= a[8], a[6] ^= a[10].
+EXT_RULES = {"128B_2ROW": [[6, 10], [5, 9], [4, 8]], "128B_TR": [[4, 9], [5, 8], [6, 10]]}
+# 128B_TR worked by hand from its row/unit statement (unit c of 128-byte row r moves to
+# c ^ (4·r[3] + 2·r[1] + r[2])): e.g. 1973 is row 15, unit 3, byte 5 -> unit 3 ^ 7 = 4 -> 1989.
+EXT_HAND_EXAMPLES = {"128B_TR": [(0, 0), (128, 128), (256, 288), (512, 528), (1024, 1088), (1973, 1989),
+                                 (2304, 2336), (2047, 1935), (3072, 3136)]}
 
 
 def _per_bit(a: np.ndarray, rules) -> np.ndarray:
@@ -49,8 +55,14 @@ def pin_swizzle_bit_rules(o):
         assert np.array_equal(o.swizzle(a, mode), _per_bit(a, g[mode])), mode
     for mode, rules in EXT_RULES.items():
         assert np.array_equal(o.swizzle(a, mode), _per_bit(a, rules)), mode
+    # 128B_TR as the GEMM's K×N layout states it: row r = a >> 7 keeps its place, its 16-byte
+    # unit c = a[6:4] moves to c ^ (4·r[3] + 2·r[1] + r[2])
+    r, c, b = a >> np.uint64(7), (a >> np.uint64(4)) & np.uint64(7), a & np.uint64(15)
+    x = (((r >> np.uint64(3)) & np.uint64(1)) << np.uint64(2)) | (((r >> np.uint64(1)) & np.uint64(1)) << np.uint64(1)) \
+        | ((r >> np.uint64(2)) & np.uint64(1))
+    assert np.array_equal(o.swizzle(a, "128B_TR"), (r << np.uint64(7)) | ((c ^ x) << np.uint64(4)) | b)
     # a[3:0] never changes (§11.3)
-    for mode in ("32B", "64B", "128B", "128B_2ROW"):
+    for mode in ("32B", "64B", "128B", "128B_2ROW", "128B_TR"):
         s = o.swizzle(a, mode)
         assert np.array_equal(s & np.uint64(15), a & np.uint64(15))
 
@@ -60,13 +72,16 @@ def pin_swizzle_hand_examples(o):
     for mode in ("32B", "64B", "128B"):
         for a, want in ex[mode]:
             assert int(o.swizzle([a], mode)[0]) == want, (mode, a, want)
+    for mode, pairs in EXT_HAND_EXAMPLES.items():
+        for a, want in pairs:
+            assert int(o.swizzle([a], mode)[0]) == want, (mode, a, want)
 
 
 def pin_swizzle_structure(o):
     """Involution; bijection inside each atom (rows of 128 B × the rows the mode reads its
     bits from); 16-byte units move whole; the permutation never leaves its span block."""
-    atoms = {"32B": 256, "64B": 512, "128B": 1024, "128B_2ROW": 2048}
-    spans = {"32B": 32, "64B": 64, "128B": 128, "128B_2ROW": 128}
+    atoms = {"32B": 256, "64B": 512, "128B": 1024, "128B_2ROW": 2048, "128B_TR": 2048}
+    spans = {"32B": 32, "64B": 64, "128B": 128, "128B_2ROW": 128, "128B_TR": 128}
     a = np.arange(1 << 15, dtype=np.uint64)
     for mode, atom in atoms.items():
         s = o.swizzle(a, mode)
@@ -101,6 +116,23 @@ def pin_bank_spread(o):
         offs = np.array([r * 128 + col * 16 for r in range(16)], dtype=np.uint64)
         s = o.swizzle(offs, "128B_2ROW")
         assert len({int(x // 16) % 16 for x in s}) == 16, col
+    # 128B_TR: the transposing 8-byte read takes 32 bytes (an aligned pair of 16-byte units, pair p)
+    # from each of the rows {r0 + 8t + 4h + e : t < 2, e < 4} per 32 lanes, which the LDS serves from
+    # one 256-byte window (64 banks of 4 bytes); the eight pieces must fall on eight distinct
+    # 32-byte bank groups.  The 128B and 2-row modes put two of them on one group.
+    for r0 in (0, 16, 32):
+        for h in (0, 1):
+            rows = [r0 + 8 * t + 4 * h + e for t in range(2) for e in range(4)]
+            for p in range(4):
+                offs = np.array([r * 128 + p * 32 for r in rows], dtype=np.uint64)
+                groups = {mode: {int(x // 32) % 8 for x in o.swizzle(offs, mode)} for mode in
+                          ("128B_TR", "128B", "128B_2ROW")}
+                assert len(groups["128B_TR"]) == 8, (r0, h, p)
+                assert len(groups["128B"]) < 8 and len(groups["128B_2ROW"]) < 8, (r0, h, p)
+                # the two 16-byte units of a pair stay an aligned pair
+                both = np.concatenate([offs, offs + np.uint64(16)])
+                s = o.swizzle(both, "128B_TR")
+                assert np.array_equal(s[:len(offs)] // np.uint64(32), s[len(offs):] // np.uint64(32))
 
 
 # ---------------------------------------------------------------------------------------------

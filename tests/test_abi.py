@@ -457,3 +457,136 @@ def test_benchmark_ceiling_library():
     main = subprocess.run(["nm", "-D", "--defined-only", tbg.library_path()], capture_output=True, text=True,
                           check=True).stdout
     assert "tbg_diag_mfma_rate" not in main, "the measurement aid must stay out of the library's ABI"
+
+
+def test_transposing_read_swizzle_encodes():
+    """TBG_SWIZZLE_128B_TR is a 128-byte-row mode: the GEMM's {64 n, 64 k} K×N bf16 box encodes with
+    it; a wider inner extent or an image that is not whole 128-byte rows is refused."""
+    d = tbg.encode_tiled("bf16", 2, BASE, [8192, 8192], [16384], [64, 64], [1, 1], "128B_TR")
+    assert tbg.box_bytes(d) == 8192
+    assert tbg.encode_tiled_status(**_c1_args(swizzle="128B_TR")) == tbg.OK
+    assert tbg.encode_tiled_status(**_c1_args(swizzle="128B_TR", box_dim=[72, 128])) == tbg.ERR_INVALID_VALUE
+    assert tbg.encode_tiled_status(**_c1_args(swizzle="128B_TR", box_dim=[8, 3])) == tbg.ERR_INVALID_VALUE
+    assert tbg.encode_tiled_status(**_c1_args(swizzle=6)) == tbg.ERR_INVALID_VALUE
+
+
+def _gemm_detail(**kw):
+    """Status and the OUT_OF_RANGE detail's byte count of a tbg_gemm_typed call that stops at the
+    workspace check (no device is reached)."""
+    import re
+    try:
+        tbg.gemm_typed(**kw)
+        return tbg.OK, None
+    except tbg.Error as e:
+        m = re.search(r"workspace of (\d+) bytes needed", e.message)
+        return e.status, int(m.group(1)) if m else None
+
+
+@pytest.mark.parametrize("ab", ["bf16", "f16", "f8e4m3", "f8e5m2"])
+def test_workspace_query_matches_the_call(ab):
+    """tbg_gemm_workspace_query gives exactly the bytes the product asks for in its OUT_OF_RANGE
+    detail, for every repack case: misaligned bases, ragged leading dimensions, ragged K, both B
+    layouts (8-bit types: B stored N×K only), and 0 when nothing is repacked."""
+    layouts = ("kn", "nk") if ab in ("bf16", "f16") else ("nk",)
+    cases = []
+    for bl in layouts:
+        for (M, N, K, lda, ldb) in [(300, 257, 136, 136, 264 if bl == "kn" else 136), (300, 257, 136, 137, 259),
+                                    (300, 257, 100, 100, 257 if bl == "kn" else 100), (3001, 2049, 777, 777, 2049),
+                                    (64, 64, 128, 128, 128)]:
+            for a_off, b_off in ((0, 0), (2, 0), (0, 6), (8, 8)):
+                if bl == "kn" and ldb < N:
+                    continue
+                cases.append((bl, M, N, K, lda, ldb, a_off, b_off))
+    for bl, M, N, K, lda, ldb, a_off, b_off in cases:
+        A, B = BASE + 0x100000 + a_off, BASE + 0x200000 + b_off
+        q = tbg.gemm_workspace_query(M, N, K, ab, A, lda, B, ldb, bl)
+        st, need = _gemm_detail(M=M, N=N, K=K, alpha=1.0, A=A, lda=lda, B=B, ldb=ldb, b_layout=bl, ab_dtype=ab,
+                                beta=0.0, C=BASE, ldc=N, c_dtype="f32")
+        what = f"{ab} {bl} M={M} N={N} K={K} lda={lda} ldb={ldb} offsets {a_off},{b_off}"
+        if q == 0:
+            assert st != tbg.ERR_OUT_OF_RANGE, what
+        else:
+            assert st == tbg.ERR_OUT_OF_RANGE and need == q, (what, q, need)
+            # with exactly that much workspace the call gets past the check
+            st2, _ = _gemm_detail(M=M, N=N, K=K, alpha=1.0, A=A, lda=lda, B=B, ldb=ldb, b_layout=bl, ab_dtype=ab,
+                                  beta=0.0, C=BASE, ldc=N, c_dtype="f32", workspace=BASE + 0x4000000,
+                                  workspace_bytes=q)
+            assert st2 != tbg.ERR_OUT_OF_RANGE, what
+    # aligned bf16 operands: the query agrees with the older size-only function
+    assert tbg.gemm_workspace_query(3001, 2049, 777, "bf16", BASE, 777, BASE, 2049, "kn") == \
+        tbg.gemm_workspace_bytes(3001, 2049, 777, 777, 2049, "kn")
+    assert tbg.gemm_workspace_query(0, 64, 64, ab, BASE, 64, BASE, 64, "nk") == 0
+
+
+def test_conv_workspace_query():
+    shp = tbg.conv2d_shape(2, 17, 17, 24, 36, 3, 3, (1, 1, 1, 1))
+    assert tbg.conv2d_workspace_query(shp, BASE, BASE) == tbg.conv2d_workspace_bytes(shp) == 0
+    c8 = 24
+    want = (2 * 17 * 17 * c8 * 2 + 255) // 256 * 256 + (36 * 3 * 3 * c8 * 2 + 255) // 256 * 256
+    assert tbg.conv2d_workspace_query(shp, BASE + 2, BASE) == want
+    assert tbg.conv2d_workspace_query(shp, BASE, BASE + 8) == want
+    shp = tbg.conv2d_shape(2, 15, 13, 20, 40, 3, 3, (1, 1, 1, 1))
+    assert tbg.conv2d_workspace_query(shp, BASE, BASE) == tbg.conv2d_workspace_bytes(shp) > 0
+
+
+class _FakeDeviceTensor:
+    """Stands in for a device tensor in the binding's host-side checks: every check it trips must
+    raise before anything reaches the C ABI (no device is used)."""
+
+    def __init__(self, shape, dtype, device="cuda:0", stride=None, ptr=BASE):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = self.device.type == "cuda"
+        self._stride = stride or tuple(int(np.prod(shape[i + 1:])) for i in range(len(shape)))
+        self._ptr = ptr
+
+    def dim(self):
+        return len(self.shape)
+
+    def stride(self, i=None):
+        return self._stride if i is None else self._stride[i]
+
+    def data_ptr(self):
+        return self._ptr
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def element_size(self):
+        import torch
+        return torch.empty(0, dtype=self.dtype).element_size()
+
+    def is_contiguous(self):
+        return True
+
+
+def test_torch_ops_rejects_mismatched_outputs():
+    """torch_ops.gemm refuses an `out` whose shape, element type or device does not match what the
+    kernel writes (M rows of N elements of out_dtype), operands on different devices and a
+    workspace on another device, before calling the library."""
+    import torch
+    from tiled_bf16_gemm_amd import torch_ops
+    A = _FakeDeviceTensor((64, 32), torch.bfloat16)
+    B = _FakeDeviceTensor((32, 48), torch.bfloat16)
+    good = dict(out_dtype="bf16")
+    for out, why in [(_FakeDeviceTensor((32, 48), torch.bfloat16), "too few rows"),
+                     (_FakeDeviceTensor((64, 40), torch.bfloat16), "too few columns"),
+                     (_FakeDeviceTensor((64, 48), torch.float32), "fp32 out for bf16"),
+                     (_FakeDeviceTensor((64, 48), torch.bfloat16, device="cuda:1"), "another device"),
+                     (_FakeDeviceTensor((64, 48), torch.bfloat16, stride=(48, 2)), "strided columns")]:
+        with pytest.raises(ValueError):
+            torch_ops.gemm(A, B, "kn", out=out, **good)
+        print("refused:", why)
+    with pytest.raises(ValueError):
+        torch_ops.gemm(A, B, "kn", out=_FakeDeviceTensor((64, 48), torch.bfloat16), out_dtype="f32")
+    with pytest.raises(ValueError):
+        torch_ops.gemm(A, B, "kn", out_dtype="u8")
+    with pytest.raises(ValueError):
+        torch_ops.gemm(A, _FakeDeviceTensor((32, 48), torch.bfloat16, device="cuda:1"), "kn")
+    with pytest.raises(ValueError):
+        torch_ops.gemm(A, B, "kn", out=_FakeDeviceTensor((64, 48), torch.bfloat16),
+                       workspace=_FakeDeviceTensor((4096,), torch.uint8, device="cuda:1"))
+    with pytest.raises(ValueError):
+        torch_ops.gemm(A, _FakeDeviceTensor((33, 48), torch.bfloat16), "kn")

@@ -158,6 +158,40 @@ def test_dma_path_edges(ops, orc):
 
 
 @gpu
+def test_transposing_read_layout(ops, orc):
+    """The 128B_TR swizzle (the GEMM's layout of B tiles stored K×N) byte for byte against the
+    oracle: {64, rows} bf16 boxes of K×N operands through the direct-to-LDS atom loader the GEMM
+    uses (ragged rows and columns, negative and overhanging origins, pitches wider than the rows),
+    the register-staged path (NaN fill, element strides, 8-bit and 32-bit elements, rank 3), and
+    the store direction."""
+    rng = np.random.default_rng(55)
+    for (rows, cols, pitch, brows) in [(200, 136, 136, 64), (64, 64, 64, 64), (1000, 520, 528, 64),
+                                       (37, 72, 80, 16), (513, 64, 64, 256)]:
+        src = torch.from_numpy(rng.integers(0, 1 << 16, (rows, pitch), dtype=np.int64).astype(np.int16)
+                               ).view(torch.bfloat16)
+        coords = [[x, y] for x in range(0, cols + 8, 8 * max(1, cols // 64)) for y in (0, 1, rows // 2, rows - 1)]
+        coords += [[-8, 0], [0, -1], [cols, 0], [0, rows], [cols - 8, rows - 8], [64, 64]]
+        _say(f"128B_TR atom path rows={rows} cols={cols} pitch={pitch} box=64x{brows}")
+        _check_case(ops, orc, src, "bf16", [cols, rows], [pitch * 2], [64, brows], [1, 1], "128B_TR", "zero", coords)
+        _check_case(ops, orc, src, "bf16", [cols, rows], [pitch * 2], [64, brows], [1, 1], "128B_TR", "zero",
+                    coords[:4], many=False)
+    src = torch.from_numpy(rng.standard_normal((96, 72)).astype(np.float32)).to(torch.bfloat16)
+    _say("128B_TR register-staged: NaN fill, element strides")
+    _check_case(ops, orc, src, "bf16", [72, 96], [144], [64, 32], [1, 1], "128B_TR", "nan",
+                [[0, 0], [16, 80], [-8, -3], [64, 90]])
+    _check_case(ops, orc, src, "bf16", [72, 96], [144], [64, 48], [1, 3], "128B_TR", "zero", [[0, 0], [8, 50]])
+    raw = rng.integers(0, 256, 40 * 12 * 144, dtype=np.int64).astype(np.uint8)
+    _check_case(ops, orc, torch.from_numpy(raw), "u8", [144, 12, 40], [144, 144 * 12], [128, 4, 8], [1, 2, 1],
+                "128B_TR", "zero", [[0, 0, 0], [16, 5, 33], [-16, -1, 2]])
+    raw32 = rng.integers(0, 1 << 32, 50 * 40, dtype=np.uint64).astype(np.uint32)
+    _check_case(ops, orc, torch.from_numpy(raw32.view(np.int32)), "f32", [40, 50], [160], [32, 40], [1, 1],
+                "128B_TR", "nan", [[0, 0], [12, 20], [-4, 30]])
+    _say("128B_TR store direction")
+    _store_case(ops, orc, "bf16", [72, 96], [144], [64, 32], [1, 1], "128B_TR", [[0, 0], [16, 80], [-8, -3]],
+                False, 77)
+
+
+@gpu
 def test_random_descriptors(ops, orc):
     """Seeded random descriptors: rank 1..5, every element type, element strides, both fills,
     every swizzle the box allows."""

@@ -26,6 +26,15 @@ MUTANTS = [
     ("128B mask drops bit 9", "oracle_swizzle_general(a, 0x380u, 3)", "oracle_swizzle_general(a, 0x180u, 3)"),
     ("64B shift off by one", "oracle_swizzle_general(a, 0x180u, 3)", "oracle_swizzle_general(a, 0x180u, 2)"),
     ("2-row mode uses 128B bits", "oracle_swizzle_general(a, 0x700u, 4)", "oracle_swizzle_general(a, 0x380u, 3)"),
+    ("transposing-read mode uses the 2-row bits",
+     "case 5: return a ^ (((a >> 9) & 1u) << 4) ^ (((a >> 8) & 1u) << 5) ^ (((a >> 10) & 1u) << 6);",
+     "case 5: return oracle_swizzle_general(a, 0x700u, 4);"),
+    ("transposing-read mode swaps its low two bits",
+     "case 5: return a ^ (((a >> 9) & 1u) << 4) ^ (((a >> 8) & 1u) << 5) ^ (((a >> 10) & 1u) << 6);",
+     "case 5: return a ^ (((a >> 8) & 1u) << 4) ^ (((a >> 9) & 1u) << 5) ^ (((a >> 10) & 1u) << 6);"),
+    ("transposing-read mode drops row bit 3",
+     "case 5: return a ^ (((a >> 9) & 1u) << 4) ^ (((a >> 8) & 1u) << 5) ^ (((a >> 10) & 1u) << 6);",
+     "case 5: return a ^ (((a >> 9) & 1u) << 4) ^ (((a >> 8) & 1u) << 5);"),
     ("negative coordinate counted inside", "if (x < 0 || (uint64_t)x >= dim[i]) inside = 0;",
      "if ((uint64_t)x >= dim[i] && x >= 0) inside = 0;"),
     ("upper bound off by one", "(uint64_t)x >= dim[i]", "(uint64_t)x > dim[i]"),

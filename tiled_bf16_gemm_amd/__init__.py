@@ -38,7 +38,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_VALUE, ERR_MISALIGNED, ERR_UNSUPPORTED, ERR_OUT_OF_RANGE, ERR_NO_DEVICE, ERR_HIP = range(7)
 DTYPES = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "f8e4m3": 6, "f8e5m2": 7}
 ELSIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "f8e4m3": 1, "f8e5m2": 1}
-SWIZZLES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4}
+SWIZZLES = {"none": 0, "32B": 1, "64B": 2, "128B": 3, "128B_2ROW": 4, "128B_TR": 5}
 OOB = {"zero": 0, "nan": 1}
 L2 = {"none": 0, "64B": 1, "128B": 2, "256B": 3}
 B_LAYOUTS = {"kn": 0, "nk": 1}
@@ -137,6 +137,10 @@ _lib.tbg_conv2d_out_dims.argtypes = [ctypes.POINTER(Conv2dShape), ctypes.POINTER
                                      ctypes.POINTER(ctypes.c_int64)]
 _lib.tbg_conv2d_workspace_bytes.restype = ctypes.c_size_t
 _lib.tbg_conv2d_workspace_bytes.argtypes = [ctypes.POINTER(Conv2dShape)]
+_lib.tbg_conv2d_workspace_query.restype = ctypes.c_size_t
+_lib.tbg_conv2d_workspace_query.argtypes = [ctypes.POINTER(Conv2dShape), _vp, _vp]
+_lib.tbg_gemm_workspace_query.restype = ctypes.c_size_t
+_lib.tbg_gemm_workspace_query.argtypes = [_i64, _i64, _i64, ctypes.c_int, _vp, _i64, _vp, _i64, ctypes.c_int]
 _lib.tbg_conv2d_fwd.restype = ctypes.c_int
 _lib.tbg_conv2d_fwd.argtypes = [ctypes.POINTER(Conv2dShape), ctypes.c_float, _vp, _vp, ctypes.c_float, _vp, _i64,
                                 ctypes.c_int, ctypes.POINTER(GemmConfig), _vp, ctypes.c_size_t, _vp]
@@ -287,6 +291,10 @@ def conv2d_workspace_bytes(shape: Conv2dShape) -> int:
     return int(_lib.tbg_conv2d_workspace_bytes(ctypes.byref(shape)))
 
 
+def conv2d_workspace_query(shape: Conv2dShape, x: int, w: int) -> int:
+    return int(_lib.tbg_conv2d_workspace_query(ctypes.byref(shape), _vp(int(x)), _vp(int(w))))
+
+
 def conv2d_fwd(shape: Conv2dShape, alpha: float, x: int, w: int, beta: float, y: int, ldy: int, y_dtype,
                config: Optional[GemmConfig] = None, workspace: int = 0, workspace_bytes: int = 0,
                stream: Optional[int] = None) -> None:
@@ -307,6 +315,11 @@ def conv2d_fwd_status(*args, **kwargs) -> int:
 
 def gemm_workspace_bytes(M: int, N: int, K: int, lda: int, ldb: int, b_layout="kn") -> int:
     return int(_lib.tbg_gemm_workspace_bytes(M, N, K, lda, ldb, _enum(B_LAYOUTS, b_layout)))
+
+
+def gemm_workspace_query(M: int, N: int, K: int, ab_dtype, A: int, lda: int, B: int, ldb: int, b_layout="kn") -> int:
+    return int(_lib.tbg_gemm_workspace_query(M, N, K, _enum(DTYPES, ab_dtype), _vp(int(A)), lda, _vp(int(B)), ldb,
+                                             _enum(B_LAYOUTS, b_layout)))
 
 
 def gemm(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C: int, ldc: int, c_dtype,

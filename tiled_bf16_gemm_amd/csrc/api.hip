@@ -46,7 +46,7 @@ uint32_t swizzle_span(int mode) {
   switch (mode) {
     case TBG_SWIZZLE_32B: return 32;
     case TBG_SWIZZLE_64B: return 64;
-    case TBG_SWIZZLE_128B: case TBG_SWIZZLE_128B_2ROW: return 128;
+    case TBG_SWIZZLE_128B: case TBG_SWIZZLE_128B_2ROW: case TBG_SWIZZLE_128B_TR: return 128;
     default: return 0;
   }
 }
@@ -160,7 +160,7 @@ tbg_status tbg_encode_tiled(tbg_tensor_desc* out, tbg_dtype dtype, uint32_t rank
     return fail(TBG_ERR_MISALIGNED, "global_address %p is not a multiple of 16 bytes", global_address);
   if (!global_dim || !box_dim || !element_strides || (rank > 1 && !global_strides))
     return fail(TBG_ERR_INVALID_VALUE, "a per-dimension array is NULL");
-  if ((int)swizzle < TBG_SWIZZLE_NONE || (int)swizzle > TBG_SWIZZLE_128B_2ROW)
+  if ((int)swizzle < TBG_SWIZZLE_NONE || (int)swizzle > TBG_SWIZZLE_128B_TR)
     return fail(TBG_ERR_INVALID_VALUE, "unknown swizzle %d", (int)swizzle);
   if ((int)l2 < TBG_L2_NONE || (int)l2 > TBG_L2_256B) return fail(TBG_ERR_INVALID_VALUE, "unknown l2 hint %d", (int)l2);
   if ((int)oob != TBG_OOB_ZERO && (int)oob != TBG_OOB_NAN)
@@ -337,7 +337,7 @@ tbg_status tbg_encode_im2col(tbg_tensor_desc* out, tbg_dtype dtype, const void* 
     return fail(TBG_ERR_INVALID_VALUE, "a per-dimension array is NULL");
   if (((uintptr_t)global_address) % 16 != 0)
     return fail(TBG_ERR_MISALIGNED, "global_address %p is not a multiple of 16 bytes", global_address);
-  if ((int)swizzle < TBG_SWIZZLE_NONE || (int)swizzle > TBG_SWIZZLE_128B_2ROW)
+  if ((int)swizzle < TBG_SWIZZLE_NONE || (int)swizzle > TBG_SWIZZLE_128B_TR)
     return fail(TBG_ERR_INVALID_VALUE, "unknown swizzle %d", (int)swizzle);
   if ((int)l2 < TBG_L2_NONE || (int)l2 > TBG_L2_256B) return fail(TBG_ERR_INVALID_VALUE, "unknown l2 hint %d", (int)l2);
   if ((int)oob != TBG_OOB_ZERO && (int)oob != TBG_OOB_NAN)
@@ -476,6 +476,26 @@ PackPlan plan_packs(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
   return pl;
 }
 
+// Repacks of 8-bit operands: rows whose pitch or K is not a multiple of 16 bytes, or that start
+// off a 16-byte boundary, are copied with K rounded up to 16 (zero padded).  B is stored N×K.
+struct Fp8PackPlan {
+  bool pack_a = false, pack_b = false;
+  int64_t k16 = 16;
+  size_t a_bytes = 0, b_bytes = 0;
+};
+
+Fp8PackPlan plan_fp8_packs(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bool a_aligned, bool b_aligned) {
+  Fp8PackPlan pl;
+  pl.k16 = round_up(K > 0 ? K : 1, 16);
+  pl.pack_a = K > 0 && ((lda % 16) != 0 || (K % 16) != 0 || !a_aligned);
+  pl.pack_b = K > 0 && ((ldb % 16) != 0 || (K % 16) != 0 || !b_aligned);
+  pl.a_bytes = pl.pack_a ? (size_t)round_up(M * pl.k16, 256) : 0;
+  pl.b_bytes = pl.pack_b ? (size_t)round_up(N * pl.k16, 256) : 0;
+  return pl;
+}
+
+bool is_f8(tbg_dtype t) { return t == TBG_F8_E4M3 || t == TBG_F8_E5M2; }
+
 }  // namespace
 
 extern "C" {
@@ -483,6 +503,19 @@ extern "C" {
 size_t tbg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, tbg_b_layout bl) {
   if (M <= 0 || N <= 0 || K <= 0 || lda <= 0 || ldb <= 0) return 0;
   PackPlan pl = plan_packs(M, N, K, lda, ldb, (int)bl, true, true);
+  return pl.a_bytes + pl.b_bytes;
+}
+
+size_t tbg_gemm_workspace_query(int64_t M, int64_t N, int64_t K, tbg_dtype ab_dtype, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, tbg_b_layout bl) {
+  if (M <= 0 || N <= 0 || K <= 0 || lda <= 0 || ldb <= 0) return 0;
+  const bool a_aligned = ((uintptr_t)A % 16) == 0, b_aligned = ((uintptr_t)B % 16) == 0;
+  if (is_f8(ab_dtype)) {
+    const Fp8PackPlan pl = plan_fp8_packs(M, N, K, lda, ldb, a_aligned, b_aligned);
+    return pl.a_bytes + pl.b_bytes;
+  }
+  if (ab_dtype != TBG_BF16 && ab_dtype != TBG_F16) return 0;
+  const PackPlan pl = plan_packs(M, N, K, lda, ldb, (int)bl, a_aligned, b_aligned);
   return pl.a_bytes + pl.b_bytes;
 }
 
@@ -531,11 +564,10 @@ tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const voi
   if (M == 0 || N == 0) return TBG_OK;
   if (!C) return fail(TBG_ERR_INVALID_VALUE, "C is NULL");
   if (K > 0 && (!A || !B)) return fail(TBG_ERR_INVALID_VALUE, "A or B is NULL");
-  const int64_t k16 = round_up(K > 0 ? K : 1, 16);
-  const bool pack_a = K > 0 && ((lda % 16) != 0 || (K % 16) != 0 || ((uintptr_t)A % 16) != 0);
-  const bool pack_b = K > 0 && ((ldb % 16) != 0 || (K % 16) != 0 || ((uintptr_t)B % 16) != 0);
-  const size_t a_bytes = pack_a ? (size_t)round_up(M * k16, 256) : 0;
-  const size_t b_bytes = pack_b ? (size_t)round_up(N * k16, 256) : 0;
+  const Fp8PackPlan fpl = plan_fp8_packs(M, N, K, lda, ldb, ((uintptr_t)A % 16) == 0, ((uintptr_t)B % 16) == 0);
+  const int64_t k16 = fpl.k16;
+  const bool pack_a = fpl.pack_a, pack_b = fpl.pack_b;
+  const size_t a_bytes = fpl.a_bytes, b_bytes = fpl.b_bytes;
   if (a_bytes + b_bytes > 0) {
     if (!workspace || workspace_bytes < a_bytes + b_bytes)
       return fail(TBG_ERR_OUT_OF_RANGE, "workspace of %zu bytes needed to repack unaligned operands (have %zu)",
@@ -663,9 +695,6 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   if (M == 0 || N == 0) return TBG_OK;
   if (!C) return fail(TBG_ERR_INVALID_VALUE, "C is NULL");
   if (K > 0 && (!A || !B)) return fail(TBG_ERR_INVALID_VALUE, "A or B is NULL");
-  int num_cus = 0;
-  tbg_status st = check_device(&num_cus);
-  if (st != TBG_OK) return st;
 
   const bool a_aligned = ((uintptr_t)A % 16) == 0, b_aligned = ((uintptr_t)B % 16) == 0;
   PackPlan pl = plan_packs(M, N, K, lda, ldb, (int)bl, a_aligned, b_aligned);
@@ -676,6 +705,9 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
                   workspace ? workspace_bytes : (size_t)0);
     if (((uintptr_t)workspace) % 256 != 0) return fail(TBG_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   }
+  int num_cus = 0;
+  tbg_status st = check_device(&num_cus);
+  if (st != TBG_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const uint16_t* Ae = (const uint16_t*)A;
   const uint16_t* Be = (const uint16_t*)B;
@@ -699,6 +731,7 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   e = tbg::launch_pack_jobs(jobs, njobs, s);
   if (e != hipSuccess) return fail(TBG_ERR_HIP, "operand repack: %s", hipGetErrorString(e));
   tbg::GemmParams p;
+  memset(&p, 0, sizeof(p));
   p.A = Ae;
   p.B = Be;
   p.C = C;
@@ -827,6 +860,12 @@ tbg_status tbg_conv2d_out_dims(const tbg_conv2d_shape* shape, int64_t* oh, int64
 size_t tbg_conv2d_workspace_bytes(const tbg_conv2d_shape* shape) {
   ConvPlan pl;
   if (conv_plan(shape, true, true, pl) != TBG_OK) return 0;
+  return pl.x_bytes + pl.w_bytes;
+}
+
+size_t tbg_conv2d_workspace_query(const tbg_conv2d_shape* shape, const void* x, const void* w) {
+  ConvPlan pl;
+  if (conv_plan(shape, ((uintptr_t)x % 16) == 0, ((uintptr_t)w % 16) == 0, pl) != TBG_OK) return 0;
   return pl.x_bytes + pl.w_bytes;
 }
 

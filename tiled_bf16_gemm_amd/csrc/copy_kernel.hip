@@ -4,7 +4,7 @@
 //
 // "2 · Le Tensor Memory Accelerator" §2.2, §2.4, §2.5 and "H100 · cuTensorMap" §8, §9, §11, §14
 // define what a copy produces; this file decides how gfx950 produces it:
-//  * 2-D boxes of 128-byte rows with a 128-byte swizzle and zero fill go through the same
+//  * 2-D boxes of 128-byte rows with a 128-byte-row swizzle and zero fill go through the same
 //    direct-to-LDS atom loader the GEMM uses for its operand tiles (tile_loader.hpp), so the
 //    copy API checks the GEMM's loader bit for bit;
 //  * every other box (rank up to 5, element strides, NaN fill, any swizzle) is staged through
@@ -105,8 +105,9 @@ __device__ void build_box_generic(const DescImpl& d, const int64_t* c, uint8_t* 
   }
 }
 
-// Direct-to-LDS path: rank 2, 128-byte box rows, box rows a multiple of 8, 128B or 2-row
-// swizzle, zero fill, chunk-aligned origin inside the tensor.  Same atoms as the GEMM's loads.
+// Direct-to-LDS path: rank 2, 128-byte box rows, box rows a multiple of 8, 128B, 2-row or
+// transposing-read swizzle, zero fill, chunk-aligned origin inside the tensor.  Same atoms as the
+// GEMM's loads.
 template <int SWZ>
 __device__ void build_box_dma(const DescImpl& d, const int64_t* c, uint8_t* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
@@ -137,7 +138,8 @@ __global__ void __launch_bounds__(256) tiled_copy_kernel(DescImpl d, Coords5 hos
                    ((c[0] * d.elsize) % 16) == 0;
   if (dma) {
     if (d.swizzle == 3) build_box_dma<3>(d, c, smem);
-    else build_box_dma<4>(d, c, smem);
+    else if (d.swizzle == kSwizzle128B2Row) build_box_dma<kSwizzle128B2Row>(d, c, smem);
+    else build_box_dma<kSwizzleKnTr>(d, c, smem);
   } else {
     build_box_generic(d, c, smem, fill);
   }
@@ -269,7 +271,7 @@ hipError_t launch_tiled_copy(const DescImpl& d, const int32_t* host_coords, cons
   if (host_coords)
     for (int i = 0; i < d.rank; ++i) hc.c[i] = host_coords[i];
   const int dma_ok = d.rank == 2 && d.estr[0] == 1 && d.estr[1] == 1 && (uint32_t)d.box[0] * d.elsize == 128u &&
-                     (d.box[1] % 8) == 0 && (d.swizzle == 3 || d.swizzle == kSwizzle128B2Row) && d.oob == 0 &&
+                     (d.box[1] % 8) == 0 && (d.swizzle == 3 || d.swizzle == kSwizzle128B2Row || d.swizzle == kSwizzleKnTr) && d.oob == 0 &&
                      ((d.dim[0] * d.elsize) % 16u) == 0 && d.stride[1] < (1ull << 23) &&
                      d.stride[1] >= d.dim[0] * d.elsize;
   uint32_t fill = 0;

@@ -57,8 +57,8 @@ static_assert(sizeof(DescIm2col) == 128, "im2col descriptor must stay 128 bytes"
 
 // Extension swizzle mode for gfx950's 64-bank LDS (see tbg.h): a[6:4] ^= a[10:8].
 constexpr int kSwizzle128B2Row = 4;
-// GEMM-internal layout of B tiles stored K×N (not a descriptor mode): the 16-byte chunk index of
-// row r is XORed with (r[3] << 2) | (r[1] << 1) | r[2].  The transposing fragment read takes 32
+// Layout of the GEMM's B tiles stored K×N, descriptor mode TBG_SWIZZLE_128B_TR: the 16-byte chunk
+// index of row r is XORed with (r[3] << 2) | (r[1] << 1) | r[2].  The transposing fragment read takes 32
 // bytes from each of 16 rows {r0 + 8a + 2b + c}; LDS serves it 32 lanes (256 bytes) at a time,
 // and this XOR gives the 8 rows of each half (rows 2 and 8 apart) distinct 32-byte bank groups,
 // which neither the 128B nor the 2-row mode does (measured: 1.65x the cycles of a linear read

@@ -20,18 +20,24 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // ---- swizzle ("H100 · cuTensorMap" §11.3) ---------------------------------------------------
 // Byte offset inside an image -> LDS byte offset.  mode 0 none, 1 32B, 2 64B, 3 128B,
-// 4 the 2-row extension a ^ ((a & 0x700) >> 4).
+// 4 the 2-row extension a ^ ((a & 0x700) >> 4), 5 the transposing-read layout (the 16-byte unit
+// of 128-byte row r XORed with row_xor<5>(r)).
 __host__ __device__ __forceinline__ uint32_t swizzle_offset(uint32_t a, int mode) {
   switch (mode) {
     case 1: return a ^ ((a & 0x080u) >> 3);
     case 2: return a ^ ((a & 0x180u) >> 3);
     case 3: return a ^ ((a & 0x380u) >> 3);
     case 4: return a ^ ((a & 0x700u) >> 4);
+    case 5: {
+      const uint32_t r = a >> 7;
+      return a ^ (((((r >> 3) & 1u) << 2) | (((r >> 1) & 1u) << 1) | ((r >> 2) & 1u)) << 4);
+    }
     default: return a;
   }
 }
 
-// For images made of 128-byte rows: the XOR applied to the 16-byte chunk index of row r.
+// For images made of 128-byte rows: the XOR applied to the 16-byte chunk index of row r (modes
+// 3, 4 and 5 of swizzle_offset).
 template <int SWZ>
 __device__ __forceinline__ int row_xor(int r) {
   static_assert(SWZ == 3 || SWZ == 4 || SWZ == 5, "128-byte-row loader takes the 128B, 2-row or K×N layout");
@@ -89,25 +95,27 @@ __device__ __forceinline__ LaneChunk lane_chunk(int row0, int lane, uint32_t row
 // `lds_addr` is the LDS byte address of the atom, the same for the whole wave, 16-byte aligned
 // (1 KiB for swizzled images).  The instruction is emitted as inline assembly so that the
 // compiler does not add its own vmcnt waits before every later LDS read: completion is awaited
-// explicitly with `s_waitcnt vmcnt` before the barrier that publishes a stage.
+// explicitly with `s_waitcnt vmcnt` before the barrier that publishes a stage.  The LDS
+// destination goes in through the "{m0}" operand constraint: the compiler itself writes M0
+// before the statement, so it knows M0's contents and keeps no value of its own there.
 __device__ __forceinline__ void issue_atom(rsrc_t rs, uint32_t lds_addr, LaneChunk lc,
                                            int chunks_valid) {
   const uint32_t off = lc.chunk < chunks_valid ? lc.offset : kOobOffset;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"(rs)
+               : "v"(off), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 
 // issue_atom with the lane's chunk test already made (`valid` false: the lane lands zeros) and
 // the atom's LDS address as a base plus an offset that is a compile-time constant where this is
-// inlined (the atom index of an unrolled loop): M0 is then set by one scalar add.
+// inlined (the atom index of an unrolled loop): the compiler then sets M0 with one scalar add.
 __device__ __forceinline__ void issue_atom_if(rsrc_t rs, uint32_t lds_base, int lds_imm, uint32_t offset, bool valid) {
   const uint32_t off = valid ? offset : kOobOffset;
-  asm volatile("s_add_u32 m0, %0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(off), "s"(rs), "i"(lds_imm)
-               : "scc", "memory");
+               : "v"(off), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base) + (uint32_t)lds_imm)
+               : "memory");
 }
 
 // LDS byte address of a pointer into a __shared__ array.

@@ -18,11 +18,18 @@ def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:
     return int(s.cuda_stream)
 
 
-def _require(t: torch.Tensor, name: str):
+def _require(t: torch.Tensor, name: str, device: Optional[torch.device] = None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError(f"{name} must be a 2-D row-major view (unit inner stride)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, A on {device}: every operand must be on one device")
+
+
+def _require_workspace(ws: Optional[torch.Tensor], device: torch.device):
+    if ws is not None and (not ws.is_cuda or ws.device != device or not ws.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous CUDA tensor on {device}")
 
 
 def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str = "bf16",
@@ -35,7 +42,7 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
     A: (M, K) view; B: (K, N) for "kn" or (N, K) for "nk".  Row strides become the leading
     dimensions.  `out` (M, N) may be a strided view; with beta != 0 it must hold the old C."""
     _require(A, "A")
-    _require(B, "B")
+    _require(B, "B", A.device)
     ab = _AB_OF.get(A.dtype)
     if ab is None or B.dtype != A.dtype:
         raise ValueError("A and B must have the same dtype: bfloat16, float16, float8_e4m3fn or float8_e5m2")
@@ -46,24 +53,17 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
         N, Kb = B.shape
     if Kb != K:
         raise ValueError(f"inner sizes differ: {K} vs {Kb}")
+    if out_dtype not in ("f32", "bf16"):
+        raise ValueError(f"out_dtype must be 'f32' or 'bf16' (got {out_dtype!r})")
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH_OF[out_dtype], device=A.device)
-    _require(out, "out")
+    _require(out, "out", A.device)
+    # the kernel writes M rows of N elements of out_dtype at out's row stride: out must be exactly that
+    if tuple(out.shape) != (M, N) or out.dtype != _TORCH_OF[out_dtype]:
+        raise ValueError(f"out must be a ({M}, {N}) {_TORCH_OF[out_dtype]} view (got {tuple(out.shape)} {out.dtype})")
+    _require_workspace(workspace, A.device)
     lda, ldb, ldc = A.stride(0), B.stride(0), out.stride(0)
-    need = tbg.gemm_workspace_bytes(M, N, K, lda, ldb, b_layout)
-    if ab.startswith("f8"):
-        # 8-bit rows whose pitch or K is not a multiple of 16 bytes, or that start off a 16-byte
-        # boundary, are repacked with their K rounded up to 16
-        k16 = (max(K, 1) + 15) // 16 * 16
-        pack = lambda ld, t: K > 0 and (ld % 16 or K % 16 or t.data_ptr() % 16)  # noqa: E731
-        need = (((M * k16 + 255) // 256 * 256) if pack(lda, A) else 0) + \
-            (((N * k16 + 255) // 256 * 256) if pack(ldb, B) else 0)
-    elif (A.data_ptr() % 16) or (B.data_ptr() % 16):
-        # an operand that starts off a 16-byte boundary is repacked too
-        rows_a, rows_b = M, (K if b_layout == "kn" else N)
-        kext = (K + 7) // 8 * 8
-        nb = (N + 7) // 8 * 8 if b_layout == "kn" else kext
-        need = ((rows_a * kext * 2 + 255) // 256 * 256) + ((rows_b * nb * 2 + 255) // 256 * 256)
+    need = tbg.gemm_workspace_query(M, N, K, ab, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
@@ -150,10 +150,12 @@ def conv2d(x: torch.Tensor, w: torch.Tensor, pad=(0, 0, 0, 0), stride=(1, 1), di
         out = torch.empty((n * oh * ow, k), dtype=_TORCH_OF[out_dtype], device=x.device)
     if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != n * oh * ow or out.shape[1] != k:
         raise ValueError("out must be a (N·OH·OW, K) row-major view")
-    need = tbg.conv2d_workspace_bytes(shp)
-    if (x.data_ptr() % 16) or (w.data_ptr() % 16):
-        c8 = (c + 7) // 8 * 8
-        need = ((n * h * wd * c8 * 2 + 255) // 256 * 256) + ((k * r * s * c8 * 2 + 255) // 256 * 256)
+    if w.device != x.device or out.device != x.device:
+        raise ValueError("x, w and out must be on one device")
+    if out.dtype != _TORCH_OF[out_dtype]:
+        raise ValueError(f"out must hold {_TORCH_OF[out_dtype]} for out_dtype {out_dtype!r} (got {out.dtype})")
+    _require_workspace(workspace, x.device)
+    need = tbg.conv2d_workspace_query(shp, x.data_ptr(), w.data_ptr())
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
