@@ -4,12 +4,16 @@
 
 A step is one tbg_gemm call on the 8192³ workload (bf16 A row-major, B row-major K×N, fp32
 accumulation, bf16 out): host-side descriptor encoding, the tiled copies into LDS, the MFMA
-main loop and the masked epilogue, with operands already resident in HBM.  W untimed steps,
-then K timed steps bracketed by device synchronisation; one JSON line is printed.
+main loop and the masked epilogue, with operands already resident in HBM.  First an untimed
+settle of the same calls (--settle seconds, reported as roofline.settle: after any idle time the
+device's power controller needs ~40 launches of this product before the clock settles), then W
+untimed steps, then K timed steps bracketed by device synchronisation; one JSON line is printed.
 
 Also reported in the same line:
   roofline      the GEMM kernel against the bf16 dense MFMA peak: algorithmic flops per launch
-                (2MNK) over the average launch time from HIP events on the launch stream;
+                (2MNK) over the average launch time from HIP events on the launch stream
+                (launch_ms: min / median / max per launch; gemm_clock_ghz: the shader clock the
+                same kernel reports from inside, per workgroup, right after the timed steps);
                 `traffic` is the HBM bytes per launch from the committed rocprofv3 counter
                 summary when it was taken on the current kernel source, else null.
   cpu_baseline  the CPU oracle on a bounded sample of the same product (the first rows of C),
@@ -69,11 +73,12 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16"):
-    """Returns (ms per step over the whole timed region, mean per-launch ms from events, wall ms
-    per step).  ab: the input type; the workload's bf16 values are converted to it (8-bit inputs
-    take B stored N×K, transposed once here, outside the timed region)."""
+def gemm_operands(torch, w, ab="bf16"):
+    """Device operands of a GEMM workload: (A view, B view, B layout, C, workspace).  ab: the input
+    type; the workload's bf16 values are converted to it (8-bit inputs take B stored N×K,
+    transposed once here, outside any timed region)."""
     import workloads
+    import tiled_bf16_gemm_amd as tbg
     A, B = workloads.gemm_inputs(w)
     lda, ldb, ldc = w.lds()
     A = A.cuda()
@@ -87,27 +92,127 @@ def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16"):
         if ab.startswith("f8") and b_layout == "kn":
             Bv, b_layout = Bv.t().contiguous(), "nk"
         Bv = Bv.to(tdt)
-        A, B = Av, Bv
     C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
-    import tiled_bf16_gemm_amd as tbg
     need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
+    return Av, Bv, b_layout, C, ws
+
+
+def launch_stats(per):
+    """min / median / max of per-launch times (ms)."""
+    import statistics
+    return {"min": round(min(per), 5), "median": round(statistics.median(per), 5), "max": round(max(per), 5)}
+
+
+def time_gemm_detail(torch, torch_ops, w, steps, warmup, config=None, ab="bf16", settle_s=0.0, operands=None):
+    """The timed region of `steps` calls after `warmup` untimed ones, and before those an untimed
+    settle of at least `settle_s` seconds of the same calls (0: none).  Every launch of the settle
+    and of the timed region is bracketed by HIP events on the launch stream.  Returns a dict:
+    ms_step (timed region / steps), ms_kernel (mean per-launch time), per (per-launch ms of the
+    timed region), wall_ms (host wall time per step) and settle (calls, seconds, per-launch ms of
+    its first and last 20 calls)."""
+    Av, Bv, b_layout, C, ws = operands if operands is not None else gemm_operands(torch, w, ab)
+
+    def call():
         torch_ops.gemm(Av, Bv, b_layout, w.out_dtype, out=C, workspace=ws, config=config)
+
+    settle = None
+    if settle_s > 0:
+        ev = []
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            for _ in range(20):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                ev.append((e0, e1))
+                n += 1
+            if len(ev) > 40:  # keep the first and the latest 20 pairs only
+                del ev[20:len(ev) - 20]
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= settle_s:
+                break
+        dt = time.perf_counter() - t0
+        first = [a.elapsed_time(b) for a, b in ev[:20]]
+        last = [a.elapsed_time(b) for a, b in ev[-20:]]
+        settle = {"calls": n, "seconds": round(dt, 3), "first20": launch_stats(first), "last20": launch_stats(last)}
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
-        torch_ops.gemm(Av, Bv, b_layout, w.out_dtype, out=C, workspace=ws, config=config)
+        call()
         ends[i].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     region = starts[0].elapsed_time(ends[-1])
-    del A, B, C, ws
-    return region / steps, sum(per) / len(per), wall_ms / steps
+    return {"ms_step": region / steps, "ms_kernel": sum(per) / len(per), "per": per, "wall_ms": wall_ms / steps,
+            "settle": settle}
+
+
+def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16", settle_s=0.0):
+    """Returns (ms per step over the whole timed region, mean per-launch ms from events, wall ms
+    per step)."""
+    r = time_gemm_detail(torch, torch_ops, w, steps, warmup, config=config, ab=ab, settle_s=settle_s)
+    return r["ms_step"], r["ms_kernel"], r["wall_ms"]
+
+
+_DIAG = None
+
+
+def diag_lib():
+    """The measurement library (products alone, the clock-recording GEMM), loaded once.  Load it
+    before any timed region: loading a code object leaves the device idle for a moment, and
+    after any idle time the first ~40 launches of the 8192^3 product run slow while the power
+    controller settles."""
+    global _DIAG
+    if _DIAG is None:
+        import ctypes
+        path = os.path.join(ROOT, "tiled_bf16_gemm_amd", "diag", "libtbg_diag.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build()")
+        _DIAG = ctypes.CDLL(path)
+    return _DIAG
+
+
+def gemm_clock(torch, Av, Bv, C, launches: int = 40):
+    """The shader clock the GEMM kernel itself runs at: the library's 8192^3 kernel built with
+    clock recording (tiled_bf16_gemm_amd/diag/mfma_rate.hip, tbg_diag_gemm_clock) launched
+    `launches` times back to back on the same operands; each workgroup of the last launch reports
+    its shader-clock and 100 MHz real-time counter advance.  Returns min / median / max over the
+    workgroups in GHz and the mean launch time in ms."""
+    import ctypes
+    import statistics
+    lib = diag_lib()
+    lib.tbg_diag_gemm_clock.restype = ctypes.c_int
+    lib.tbg_diag_gemm_clock.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    M, K = Av.shape
+    N = Bv.shape[1]
+    nwg = ((M + 255) // 256) * ((N + 255) // 256)
+    clk = torch.zeros(2 * nwg, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    n_out = ctypes.c_int(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        rc = lib.tbg_diag_gemm_clock(Av.data_ptr(), Bv.data_ptr(), C.data_ptr(), M, N, K, Av.stride(0), Bv.stride(0),
+                                     C.stride(0), clk.data_ptr(), ctypes.byref(n_out), stream)
+        if rc != 0:
+            raise RuntimeError(f"clock-recording GEMM launch failed ({rc})")
+    e1.record()
+    torch.cuda.synchronize()
+    c = clk.cpu().tolist()
+    ghz = [c[2 * i + 1] / (c[2 * i] / 100e6) / 1e9 for i in range(nwg) if c[2 * i] > 0]
+    return {"min": round(min(ghz), 3), "median": round(statistics.median(ghz), 3), "max": round(max(ghz), 3),
+            "workgroups": len(ghz), "launch_ms": round(e0.elapsed_time(e1) / launches, 5)}
 
 
 def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20, config=None):
@@ -234,10 +339,7 @@ def mfma_ceiling(torch, kind: int = 0, launches: int = 60, warmup: int = 60):
     the power limit allows with such operands."""
     import ctypes
     import statistics
-    here = os.path.join(ROOT, "tiled_bf16_gemm_amd", "diag", "libtbg_diag.so")
-    if not os.path.exists(here):
-        raise RuntimeError(f"{here} is not built: run __graft_entry__.build()")
-    lib = ctypes.CDLL(here)
+    lib = diag_lib()
     lib.tbg_diag_mfma_rate.restype = ctypes.c_int
     lib.tbg_diag_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -683,6 +785,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--settle", type=float, default=0.25, metavar="SECONDS",
+                    help="untimed calls of the headline product right before its warm-up, for at least this long "
+                         "(reported as roofline.settle; 0: none).  After any idle time the device needs about 40 "
+                         "launches of this product (~30 ms) before its power controller settles; the per-workload "
+                         "rows get a settle of a third of this")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the GEMM's own shader clock (a clock-recording build of the same kernel, after the "
+                         "timed steps)")
     ap.add_argument("--sweep-md", default="", metavar="JSONL",
                     help="write the sweep summaries in profiles/ from the JSON lines of a --sweep run (no GPU needed)")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -754,15 +864,25 @@ def main():
                               "frac": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
             torch.cuda.empty_cache()
         return
-    ms_step, ms_kernel, wall_ms = time_gemm(torch, torch_ops, w, args.steps, args.warmup)
+    # The headline: an untimed settle of the same product first (a device that has been idle
+    # starts below its working clock; the settle's first and last launches are reported), then
+    # the driver's warm-up and timed steps.
+    if not args.no_clock or not args.no_ceiling:
+        diag_lib()
+    ops = gemm_operands(torch, w)
+    head = time_gemm_detail(torch, torch_ops, w, args.steps, args.warmup, settle_s=args.settle, operands=ops)
+    ms_step, ms_kernel = head["ms_step"], head["ms_kernel"]
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     achieved = w.flops / (ms_kernel * 1e-3) / 1e12
+    clock = None if args.no_clock else gemm_clock(torch, ops[0], ops[1], ops[3])
+    del ops
+    torch.cuda.empty_cache()
 
     per_config = {}
     if not args.no_configs:
         for name in ("c1", "c2", "c3", "c5"):
             cw = workloads.GEMMS[name]
-            s, k, _ = time_gemm(torch, torch_ops, cw, 50, 50)
+            s, k, _ = time_gemm(torch, torch_ops, cw, 50, 50, settle_s=args.settle / 3)
             tf = cw.flops / (s * 1e-3) / 1e12
             per_config[name] = {"M": cw.M, "N": cw.N, "K": cw.K, "b_layout": cw.b_layout, "out": cw.out_dtype,
                                 "ms": round(s, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
@@ -776,7 +896,7 @@ def main():
                             "ms": round(ms_step, 5), "tflops": round(tflops, 2),
                             "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
         for ab in ("f16", "f8e4m3"):
-            s_, _, _ = time_gemm(torch, torch_ops, w, 50, 50, ab=ab)
+            s_, _, _ = time_gemm(torch, torch_ops, w, 50, 50, ab=ab, settle_s=args.settle / 3)
             tf = w.flops / (s_ * 1e-3) / 1e12
             per_config[f"c4_{ab}"] = {"M": w.M, "N": w.N, "K": w.K, "inputs": ab,
                                       "b_layout": "nk" if ab.startswith("f8") else w.b_layout, "out": w.out_dtype,
@@ -844,7 +964,10 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": load_traffic(),
             "kernel_ms": round(ms_kernel, 5),
+            "launch_ms": launch_stats(head["per"]),
             "flops_per_launch": w.flops,
+            "settle": head["settle"],
+            "gemm_clock_ghz": clock,
             "ceiling": ceiling,
             "frac_of_ceiling": round(achieved / ceiling["tflops"], 4) if ceiling else None,
         },

@@ -30,9 +30,16 @@ struct RingCfg {
   static_assert(T::Atoms * (S - 2) <= 63, "tiles in flight must fit the vmcnt counter");
 };
 
-template <int BM, int BN, int S, int IN, int BL, int OUT, int SCALED>
+// CLK 1: a measurement instance (never launched by the library) that records, per workgroup, the
+// real-time and shader-clock counters' advance from its start to the end of its stores.
+template <int BM, int BN, int S, int IN, int BL, int OUT, int SCALED, int CLK = 0>
 __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gemm_ring_kernel(GemmParams p) {
   using T = TileCfg<BM, BN, IN>;
+  uint64_t clk_r0 = 0, clk_m0 = 0;
+  if (CLK) {
+    clk_r0 = __builtin_amdgcn_s_memrealtime();
+    clk_m0 = __builtin_amdgcn_s_memtime();
+  }
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RingCfg<BM, BN, S>::LdsBytes];
   const int lane = threadIdx.x & 63;
   // The wave index is uniform: keeping it scalar keeps every address derived from it scalar.
@@ -143,6 +150,13 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   drain_acc<T>(acc);
   stage_barrier<0>();
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
+  if (CLK) {
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime(), m1 = __builtin_amdgcn_s_memtime();
+    if (threadIdx.x == 0) {
+      p.clock[2 * (uint64_t)blockIdx.x] = r1 - clk_r0;
+      p.clock[2 * (uint64_t)blockIdx.x + 1] = m1 - clk_m0;
+    }
+  }
 }
 
 template <int BM, int BN, int S, int IN>

@@ -19,6 +19,9 @@ struct GemmParams {
   int vec_store;   // C and its rows are 16-byte aligned: whole 16-byte stores allowed
   float alpha, beta;
   int scaled;      // 0: C = A·B; 1: C = alpha·A·B + beta·C (C read only when beta != 0)
+  // Clock-recording instances only (a measurement build outside the C ABI): per workgroup the
+  // 100 MHz real-time and shader-clock counter deltas from its start to its end.  Null otherwise.
+  uint64_t* clock;
 };
 
 // Arguments of one implicit-GEMM convolution launch (gemm_conv.hpp).  `g` carries what the

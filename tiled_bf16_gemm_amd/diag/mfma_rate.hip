@@ -10,6 +10,9 @@
 // clock the products ran at.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
+
+#include "gemm_ring.hpp"
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
@@ -68,5 +71,41 @@ extern "C" int tbg_diag_mfma_rate(int kind, const void* src, void* out, int nwg,
   else
     hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(nwg), dim3(256), 0, (hipStream_t)stream, (const i32x4_t*)src,
                        (float*)out, iters, (uint64_t*)clk);
+  return (int)hipGetLastError();
+}
+
+// The library's 256x256 two-stage ring on a bf16 product with B stored K×N and bf16 output (the
+// kernel the library runs on the 8192^3 workload), built with clock recording: each workgroup
+// writes {real-time ticks at 100 MHz, shader-clock ticks} from its start to the end of its stores
+// into clk[2 * workgroup].  Operands must need no repack (16-byte aligned, lda, ldb, ldc and K
+// multiples of 8).  Returns the launch's hipError_t as an int; the number of workgroups through
+// nwg_out.
+extern "C" int tbg_diag_gemm_clock(const void* A, const void* B, void* C, int M, int N, int K, long long lda,
+                                   long long ldb, long long ldc, void* clk, int* nwg_out, void* stream) {
+  if (!A || !B || !C || !clk || M <= 0 || N <= 0 || K <= 0 || lda % 8 || ldb % 8 || ldc % 8 || K % 8 || lda < K ||
+      ldb < N || ldc < N || ((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) % 16)
+    return (int)hipErrorInvalidValue;
+  tbg::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.kchunks = K / 8;
+  p.tiles_m = (M + 255) / 256;
+  p.tiles_n = (N + 255) / 256;
+  p.group_m = 4;
+  p.vec_store = 1;
+  p.alpha = 1.f;
+  p.clock = (uint64_t*)clk;
+  const int nwg = p.tiles_m * p.tiles_n;
+  if (nwg_out) *nwg_out = nwg;
+  hipLaunchKernelGGL((tbg::gemm_ring_kernel<256, 256, 2, 0, 0, 1, 0, 1>), dim3(nwg), dim3(tbg::kThreads), 0,
+                     (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
