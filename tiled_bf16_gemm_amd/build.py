@@ -20,6 +20,9 @@ LIB = os.path.join(HERE, "libtbg.so")
 # outside the C ABI of include/tbg.h.
 DIAG_SRC = os.path.join(HERE, "diag", "mfma_rate.hip")
 DIAG_LIB = os.path.join(HERE, "diag", "libtbg_diag.so")
+# The hand-off checking build of the same sources (TBG_HANDOFF_CHECK=1: every stage hand-off
+# drains all copies and LDS reads), with the same C ABI; only the tests load it.
+CHECK_LIB = os.path.join(HERE, "diag", "libtbg_check.so")
 
 
 def hipcc() -> str:
@@ -40,16 +43,35 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out: str = LIB, verbose: bool = False) -> str:
-    """Compile every csrc/*.hip to an object in parallel (one hipcc per file), then link."""
+def build(out: str = LIB, verbose: bool = False, check: bool = True) -> str:
+    """Compile every csrc/*.hip to an object in parallel (one hipcc per file), then link; then the
+    measurement library and (check=True) the hand-off checking build of the same sources."""
+    build_library(out, verbose)
+    tmp = DIAG_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *flags(), "-shared", DIAG_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {DIAG_SRC}:\n{r.stderr}")
+    os.replace(tmp, DIAG_LIB)
+    if check:
+        build_library(CHECK_LIB, verbose, defines=["-DTBG_HANDOFF_CHECK=1"], objdir="_build_check")
+    isa_dir = os.environ.get("TBG_SAVE_ISA")
+    if isa_dir:
+        save_isa(isa_dir)
+    return out
+
+
+def build_library(out: str, verbose: bool = False, defines=(), objdir: str = "_build") -> str:
     import concurrent.futures
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, objdir)
     os.makedirs(objdir, exist_ok=True)
     srcs = sources()
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
-        cmd = [hipcc(), *flags(), "-c", src, "-o", obj]
+        cmd = [hipcc(), *flags(), *defines, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,17 +91,6 @@ def build(out: str = LIB, verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
-    tmp = DIAG_LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), "-shared", DIAG_SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {DIAG_SRC}:\n{r.stderr}")
-    os.replace(tmp, DIAG_LIB)
-    isa_dir = os.environ.get("TBG_SAVE_ISA")
-    if isa_dir:
-        save_isa(isa_dir)
     return out
 
 

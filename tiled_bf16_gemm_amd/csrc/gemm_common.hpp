@@ -109,13 +109,25 @@ __device__ __forceinline__ void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// TBG_HANDOFF_CHECK 1 builds the hand-off checking variant of every kernel (a library of its own,
+// never the product): each stage hand-off waits for all of the wave's copies and LDS reads
+// (vmcnt(0), lgkmcnt(0)) instead of only the awaited tile's, so a schedule that read a stage
+// before its copies landed, or overwrote it while another wave still read it, would show up as
+// a difference from the lean kernels' bits.
+#ifndef TBG_HANDOFF_CHECK
+#define TBG_HANDOFF_CHECK 0
+#endif
+
 // Wait for this wave's outstanding tile copies (down to `N` in flight) and its LDS reads, then
 // meet the other waves: afterwards every wave's copies of the awaited tile are visible in LDS
 // and no wave still reads the stage that the next copies overwrite ("1 · Asynchronisme et
 // mbarrier" §1.5: the full/empty hand-off of a ring stage, done here with one barrier).
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  if (TBG_HANDOFF_CHECK)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <class T>

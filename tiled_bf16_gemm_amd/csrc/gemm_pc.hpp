@@ -104,6 +104,7 @@ __device__ __forceinline__ void produce(const GemmParams& p, const uint8_t* smem
         issue_atom(o.rb, base + 1024u * j, ch[i], cv);
       }
     }
+    if (TBG_HANDOFF_CHECK) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (kt >= S - 2) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::PA * (S - 2)) : "memory");
       arrive(&full[sig_st], lane);
@@ -179,6 +180,7 @@ __global__ void __launch_bounds__((PcCfg<BM, BN, S>::Threads), (PcCfg<BM, BN, S>
       if (nxt == 0) ++fill_next;
       const uint8_t* sA = smem + cur * T::StageBytes;
       kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, nolanes, nolanes);
+      if (TBG_HANDOFF_CHECK) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       arrive(&empty[cur], lane);
       if (kt + 1 < ktiles) wait_counter(&full[nxt], (uint32_t)(C::NP * (fill_next + 1)));
       const uint8_t* nA = smem + nxt * T::StageBytes;
