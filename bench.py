@@ -4,10 +4,12 @@
 
 A step is one tbg_gemm call on the 8192³ workload (bf16 A row-major, B row-major K×N, fp32
 accumulation, bf16 out): host-side descriptor encoding, the tiled copies into LDS, the MFMA
-main loop and the masked epilogue, with operands already resident in HBM.  First an untimed
-settle of the same calls (--settle seconds, reported as roofline.settle: after any idle time the
-device's power controller needs ~40 launches of this product before the clock settles), then W
-untimed steps, then K timed steps bracketed by device synchronisation; one JSON line is printed.
+main loop and the masked epilogue, with operands already resident in HBM.  A region is W
+untimed steps, a synchronisation, then K steps bracketed by HIP events and device
+synchronisation.  The same region first runs untimed, back to back, for --settle seconds
+(reported as roofline.settle: after any idle time the device's power controller needs ~40
+launches of this product before the clock settles); the region timed is the next one.  One
+JSON line is printed.
 
 Also reported in the same line:
   roofline      the GEMM kernel against the bf16 dense MFMA peak: algorithmic flops per launch
@@ -105,54 +107,47 @@ def launch_stats(per):
 
 
 def time_gemm_detail(torch, torch_ops, w, steps, warmup, config=None, ab="bf16", settle_s=0.0, operands=None):
-    """The timed region of `steps` calls after `warmup` untimed ones, and before those an untimed
-    settle of at least `settle_s` seconds of the same calls (0: none).  Every launch of the settle
-    and of the timed region is bracketed by HIP events on the launch stream.  Returns a dict:
-    ms_step (timed region / steps), ms_kernel (mean per-launch time), per (per-launch ms of the
-    timed region), wall_ms (host wall time per step) and settle (calls, seconds, per-launch ms of
-    its first and last 20 calls)."""
+    """One timed region: `warmup` untimed calls, a synchronisation, then `steps` calls each
+    bracketed by HIP events on the launch stream, and a synchronisation.  With settle_s > 0 the
+    same region is first run back to back, untimed, until settle_s seconds have passed, and the
+    region timed is the next one: the same calls in the same pattern as those before it.
+    Returns a dict: ms_step (timed region / steps), ms_kernel (mean per-launch time), per
+    (per-launch ms of the timed region), wall_ms (host wall time per step) and settle (the number
+    of settle regions, their seconds, and the median launch time of the first and of each of the
+    last five)."""
     Av, Bv, b_layout, C, ws = operands if operands is not None else gemm_operands(torch, w, ab)
 
     def call():
         torch_ops.gemm(Av, Bv, b_layout, w.out_dtype, out=C, workspace=ws, config=config)
 
+    def region():
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record()
+            call()
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return [a.elapsed_time(b) for a, b in zip(starts, ends)], starts[0].elapsed_time(ends[-1]), wall
+
+    import statistics
     settle = None
     if settle_s > 0:
-        ev = []
+        meds = []
         t0 = time.perf_counter()
-        n = 0
-        while True:
-            for _ in range(20):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                call()
-                e1.record()
-                ev.append((e0, e1))
-                n += 1
-            if len(ev) > 40:  # keep the first and the latest 20 pairs only
-                del ev[20:len(ev) - 20]
-            torch.cuda.synchronize()
-            if time.perf_counter() - t0 >= settle_s:
-                break
-        dt = time.perf_counter() - t0
-        first = [a.elapsed_time(b) for a, b in ev[:20]]
-        last = [a.elapsed_time(b) for a, b in ev[-20:]]
-        settle = {"calls": n, "seconds": round(dt, 3), "first20": launch_stats(first), "last20": launch_stats(last)}
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
-        call()
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    region = starts[0].elapsed_time(ends[-1])
-    return {"ms_step": region / steps, "ms_kernel": sum(per) / len(per), "per": per, "wall_ms": wall_ms / steps,
+        while time.perf_counter() - t0 < settle_s:
+            per, _, _ = region()
+            meds.append(statistics.median(per))
+        settle = {"regions": len(meds), "seconds": round(time.perf_counter() - t0, 3),
+                  "first_region_median_ms": round(meds[0], 5),
+                  "last_regions_median_ms": [round(x, 5) for x in meds[-5:]]}
+    per, span, wall_ms = region()
+    return {"ms_step": span / steps, "ms_kernel": sum(per) / len(per), "per": per, "wall_ms": wall_ms / steps,
             "settle": settle}
 
 
