@@ -228,6 +228,24 @@ tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                     tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* tbg_gemm for callers that cannot allocate device memory or pass a workspace: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * product, kernels and results as tbg_gemm; operands that need a repack (see
+ * tbg_gemm_workspace_query) are repacked into a scratch array that the library holds in device
+ * memory, one per GPU it runs on, for the life of the process: tbg_gemm_noalloc_scratch_bytes()
+ * bytes (32 MiB).  The call allocates nothing (no hipMalloc, no hipFree).
+ * The scratch array is shared by every call on a GPU and keeps the last call's contents (each
+ * repack writes every byte it reads back, zero padding included): calls that overlap on one GPU
+ * (on different streams, or from different threads) race on it and must be serialised by the
+ * caller; calls on one stream are ordered.
+ * Returns what tbg_gemm returns; OUT_OF_RANGE when the repack needs more than the scratch array
+ * holds (the detail names both sizes), HIP when the array's device address cannot be found. */
+tbg_status tbg_gemm_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                            tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* stream);
+
+/* Size in bytes of the scratch array behind tbg_gemm_noalloc. */
+size_t tbg_gemm_noalloc_scratch_bytes(void);
+
 /* C <- alpha·A·B + beta·C, the general form of the BLAS product that [GEMM]'s tensor-core section
  * gives for the matrix units.  Arguments, layouts, checks and workspace as tbg_gemm, plus:
  *   alpha, beta  binary32 scalars.  The product's fp32 sum S is combined as alpha·S + beta·C_old

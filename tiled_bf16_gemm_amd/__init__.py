@@ -139,6 +139,10 @@ _lib.tbg_conv2d_workspace_bytes.restype = ctypes.c_size_t
 _lib.tbg_conv2d_workspace_bytes.argtypes = [ctypes.POINTER(Conv2dShape)]
 _lib.tbg_conv2d_workspace_query.restype = ctypes.c_size_t
 _lib.tbg_conv2d_workspace_query.argtypes = [ctypes.POINTER(Conv2dShape), _vp, _vp]
+_lib.tbg_gemm_noalloc.restype = ctypes.c_int
+_lib.tbg_gemm_noalloc.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, ctypes.c_int, _vp]
+_lib.tbg_gemm_noalloc_scratch_bytes.restype = ctypes.c_size_t
+_lib.tbg_gemm_noalloc_scratch_bytes.argtypes = []
 _lib.tbg_gemm_workspace_query.restype = ctypes.c_size_t
 _lib.tbg_gemm_workspace_query.argtypes = [_i64, _i64, _i64, ctypes.c_int, _vp, _i64, _vp, _i64, ctypes.c_int]
 _lib.tbg_conv2d_fwd.restype = ctypes.c_int
@@ -327,6 +331,17 @@ def gemm(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C
     """tbg_gemm: C = A·B (bf16 in, fp32 accumulate, fp32 or bf16 out) on `stream`."""
     _check(_lib.tbg_gemm(M, N, K, _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout), _vp(int(C)), ldc,
                          _enum(DTYPES, c_dtype), _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+
+
+def gemm_noalloc(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C: int, ldc: int, c_dtype,
+                 stream: Optional[int] = None) -> None:
+    """tbg_gemm_noalloc: tbg_gemm with any repack in the library's own scratch array (no workspace)."""
+    _check(_lib.tbg_gemm_noalloc(M, N, K, _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout), _vp(int(C)),
+                                 ldc, _enum(DTYPES, c_dtype), _vp(stream or 0)))
+
+
+def gemm_noalloc_scratch_bytes() -> int:
+    return int(_lib.tbg_gemm_noalloc_scratch_bytes())
 
 
 def gemm_ex(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, beta: float, C: int,

@@ -767,7 +767,64 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
 
 }  // namespace
 
+// The allocation-free product's repack area: a file-scope device array, one per GPU the library
+// runs on, held until the process ends.  Host code never passes `scratch` itself to a kernel or
+// a copy (on the host the name stands for a host-side shadow, not the device memory): it uses the
+// device address that hipGetSymbolAddress returns for the current device (scratch_ptr).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device with that device
+// current (each GPU holds its own copy at its own address).
+tbg_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return fail(TBG_ERR_NO_DEVICE, "no current HIP device");
+  }
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(TBG_ERR_HIP, "hipGetSymbolAddress of the scratch array on device %d: %s", dev, hipGetErrorString(e));
+    }
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return TBG_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+tbg_status tbg_gemm_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                            tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* stream) {
+  // Sizes and operands that need no repack go straight to tbg_gemm's path; the argument checks
+  // are tbg_gemm's own.
+  const size_t need = tbg_gemm_workspace_query(M, N, K, TBG_BF16, A, lda, B, ldb, bl);
+  if (need == 0)
+    return gemm_impl(M, N, K, 1.f, A, lda, B, ldb, bl, 0.f, C, ldc, c_dtype, nullptr, nullptr, 0, stream, false);
+  if (need > kNoAllocScratchBytes)
+    return fail(TBG_ERR_OUT_OF_RANGE,
+                "the operands' repack needs %zu bytes; the allocation-free product holds %zu bytes of scratch "
+                "(use tbg_gemm with a workspace)", need, kNoAllocScratchBytes);
+  tbg_status st = check_device();
+  if (st != TBG_OK) return st;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != TBG_OK) return st;
+  return gemm_impl(M, N, K, 1.f, A, lda, B, ldb, bl, 0.f, C, ldc, c_dtype, nullptr, ws, kNoAllocScratchBytes, stream,
+                   false);
+}
+
+size_t tbg_gemm_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 tbg_status tbg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                     tbg_b_layout bl, void* C, int64_t ldc, tbg_dtype c_dtype, void* workspace, size_t workspace_bytes,
