@@ -123,6 +123,14 @@ void log_choice(const char* fmt, ...) {
   va_end(ap);
 }
 
+// Whether the epilogue may store whole 16-byte pieces of C's rows (8-byte pieces in the scaled
+// bf16 path): gfx9's multi-dword memory instructions need only dword-aligned addresses, so C's
+// base and its row pitch in bytes must be multiples of 4 (every fp32 C at a 4-byte aligned base;
+// a bf16 C when ldc is even).  Otherwise the epilogue stores element by element.
+int rows_dword_aligned(const void* C, int64_t ldc, tbg_dtype c_dtype) {
+  return (((uintptr_t)C) % 4 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 4 == 0);
+}
+
 int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
@@ -611,7 +619,7 @@ tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const voi
   p.K = (int)(K > 0 ? k16 / 2 : 0);
   p.kchunks = K > 0 ? (int)(k16 / 16) : 0;  // K = 0: every copy lane masked, A and B never read
   p.group_m = 8;
-  p.vec_store = (((uintptr_t)C) % 16 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
+  p.vec_store = rows_dword_aligned(C, ldc, c_dtype);
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
@@ -752,7 +760,7 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   // 16384×14336×4096; 2, 16 and 32 are slower.
   p.group_m = env_int("TBG_GROUP_M", 4);
   if (p.group_m < 1) p.group_m = 1;
-  p.vec_store = (((uintptr_t)C) % 16 == 0) && ((ldc * (c_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
+  p.vec_store = rows_dword_aligned(C, ldc, c_dtype);
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
@@ -995,7 +1003,7 @@ tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void
   cp.g.K = (int)(ldw);
   cp.g.kchunks = (int)(ldw / 8);
   cp.g.group_m = 8;
-  cp.g.vec_store = (((uintptr_t)y) % 16 == 0) && ((ldy * (y_dtype == TBG_BF16 ? 2 : 4)) % 16 == 0);
+  cp.g.vec_store = rows_dword_aligned(y, ldy, y_dtype);
   cp.g.alpha = alpha;
   cp.g.beta = beta;
   cp.g.scaled = scaled ? 1 : 0;

@@ -17,66 +17,75 @@ namespace tbg {
 // into a contiguous area before use; 16-byte alignment of the leading dimension, section "In
 // pratica"): copy `rows` rows of `row_bytes` bytes into a buffer of pitch `ld_dst` bytes (a
 // multiple of 16), zero-filling bytes row_bytes..ld_dst-1.  One thread per 16-byte chunk of the
-// destination: it reads the five aligned dwords that hold the chunk's source bytes (the source may
-// sit at any byte alignment) and funnel-shifts them into place.  Near the row's end the dword
-// reads stop at the dword that holds the row's last byte and the bytes past the row are zeroed,
-// so every lane runs the same instructions and no read leaves the dwords of the row.  Both
-// operands of a product are packed by one launch.
+// destination, numbered flat over both operands' chunks (no idle threads at ragged row ends).
+// The chunk's 16 source bytes may start at any byte: the thread loads the two aligned 16-byte
+// blocks that hold them (consecutive lanes load consecutive blocks, so every load instruction is
+// one contiguous run) and funnel-shifts them into place.  The second block is clamped to the
+// aligned block that holds the row's last byte, and the bytes past the row are zeroed, so no load
+// leaves the 16-byte blocks the row touches (those never cross a page).
 __device__ __forceinline__ uint4 pack_chunk(const PackJob& j, int64_t r, int64_t b0) {
   const int64_t valid = j.row_bytes - b0;  // bytes of this chunk inside the row
   if (valid <= 0) return make_uint4(0, 0, 0, 0);
   const uint8_t* srow = j.src + r * j.ld_src;
   const uintptr_t a = (uintptr_t)(srow + b0);
-  const uint32_t* q = (const uint32_t*)(a & ~(uintptr_t)3);
-  const uint32_t sh = (uint32_t)(a & 3);
-  const uint32_t* qlast = (const uint32_t*)((uintptr_t)(srow + j.row_bytes - 1) & ~(uintptr_t)3);
-  const int64_t nlast = qlast - q;
-  uint32_t w[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) w[i] = q[i < nlast ? i : nlast];
+  const uintptr_t base = a & ~(uintptr_t)15;
+  const uintptr_t last = (uintptr_t)(srow + j.row_bytes - 1) & ~(uintptr_t)15;
+  const uint4 q0 = *(const uint4*)base;
+  const uint4 q1 = *(const uint4*)(base + 16 <= last ? base + 16 : last);
+  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint32_t d = (uint32_t)(a & 15) >> 2, sh = (uint32_t)(a & 3);
   uint32_t o[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    o[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+    // dwords d + k and d + k + 1 of the 32 loaded bytes, selected without indexing registers
+    uint32_t lo = w[k], hi = w[k + 1];
+#pragma unroll
+    for (int s = 1; s < 4; ++s) {
+      if (d == (uint32_t)s) {
+        lo = w[k + s];
+        hi = w[k + s + 1 < 8 ? k + s + 1 : 7];
+      }
+    }
+    o[k] = __builtin_amdgcn_alignbyte(hi, lo, sh);
     const int64_t keep = valid - 4 * k;  // bytes of this dword inside the row
     if (keep < 4) o[k] &= keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Blocks of 64 chunks × 4 rows, numbered flat: blocks below `b0` pack j0, the rest j1, so each
-// repack gets exactly its own blocks when the two operands have different shapes.  Workgroups
-// step through the blocks by the grid size.
+// Chunks numbered flat: chunks below `n0` belong to j0 (row-major over its rows × cpr0 chunks),
+// the rest to j1.  Workgroups step through the chunks by the grid size.
 struct PackGrid {
-  uint32_t b0, total;  // blocks of the first repack; blocks of both
-  uint32_t gx0, gx1;   // blocks across a row of each repack
+  uint64_t n0, total;  // chunks of the first repack; chunks of both
+  uint32_t cpr0, cpr1;  // destination chunks per row of each repack
 };
 
 __global__ void __launch_bounds__(256) pack_rows_kernel(PackJob j0, PackJob j1, PackGrid g) {
-  for (uint32_t blk = blockIdx.x; blk < g.total; blk += gridDim.x) {
-    const bool second = blk >= g.b0;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < g.total; t += stride) {
+    const bool second = t >= g.n0;
     const PackJob& j = second ? j1 : j0;
-    const uint32_t w = second ? blk - g.b0 : blk;
-    const uint32_t gx = second ? g.gx1 : g.gx0;
-    const int64_t r = (int64_t)(w / gx) * 4 + threadIdx.y;
-    const int64_t c = (int64_t)(w % gx) * 64 + threadIdx.x;
-    if (r >= j.rows || c >= j.ld_dst / 16) continue;
+    const uint64_t i = second ? t - g.n0 : t;
+    const uint32_t cpr = second ? g.cpr1 : g.cpr0;
+    const int64_t r = (int64_t)(i / cpr), c = (int64_t)(i % cpr);
     *(uint4*)(j.dst + r * j.ld_dst + c * 16) = pack_chunk(j, r, c * 16);
   }
 }
 
 hipError_t launch_pack_jobs(const PackJob* jobs, int n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  uint64_t gx[2] = {1, 1}, blocks[2] = {0, 0};
+  uint64_t chunks[2] = {0, 0};
+  uint32_t cpr[2] = {1, 1};
   for (int i = 0; i < n; ++i) {
-    gx[i] = (uint64_t)(jobs[i].ld_dst / 16 + 63) / 64;
-    blocks[i] = gx[i] * (uint64_t)((jobs[i].rows + 3) / 4);
+    if (jobs[i].ld_dst / 16 >= (1ll << 32)) return hipErrorInvalidValue;
+    cpr[i] = (uint32_t)(jobs[i].ld_dst / 16);
+    chunks[i] = (uint64_t)cpr[i] * (uint64_t)jobs[i].rows;
   }
-  if (blocks[0] + blocks[1] >= (1ull << 32)) return hipErrorInvalidValue;
-  const PackGrid g{(uint32_t)blocks[0], (uint32_t)(blocks[0] + blocks[1]), (uint32_t)gx[0], (uint32_t)gx[1]};
+  const PackGrid g{chunks[0], chunks[0] + chunks[1], cpr[0], cpr[1]};
   if (g.total == 0) return hipSuccess;
-  const uint32_t grid = g.total < (1u << 20) ? g.total : (1u << 20);
-  hipLaunchKernelGGL(pack_rows_kernel, dim3(grid), dim3(64, 4), 0, stream, jobs[0], n > 1 ? jobs[1] : jobs[0], g);
+  const uint64_t blocks = (g.total + 255) / 256;
+  const uint32_t grid = blocks < (1u << 20) ? (uint32_t)blocks : (1u << 20);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(grid), dim3(256), 0, stream, jobs[0], n > 1 ? jobs[1] : jobs[0], g);
   return hipGetLastError();
 }
 
@@ -171,9 +180,11 @@ struct Candidate {
   int pipeline, bm, bn, stages;
   double eff;
 };
+// Candidates of equal cost keep the first listed: the 128×128 ring comes before the 128×256 producer
+// ring (on 3008×2056×784, where their costs tie, the ring's kernel took 19.4 µs, the producer's 21.0).
 const Candidate kCandidates[] = {
-    {kPipeRing, 256, 256, 2, 1.00},     {kPipeProducer, 128, 256, 2, 0.79}, {kPipeProducer, 256, 128, 2, 0.77},
-    {kPipeRing, 128, 128, 2, 0.79},     {kPipeRing, 256, 128, 2, 0.72},     {kPipeRing, 128, 256, 2, 0.71},
+    {kPipeRing, 256, 256, 2, 1.00},     {kPipeRing, 128, 128, 2, 0.79},     {kPipeProducer, 128, 256, 2, 0.79},
+    {kPipeProducer, 256, 128, 2, 0.77}, {kPipeRing, 256, 128, 2, 0.72},     {kPipeRing, 128, 256, 2, 0.71},
     {kPipeProducer, 128, 128, 3, 0.65}, {kPipeRing, 64, 64, 3, 0.44},       {kPipeProducer, 64, 64, 3, 0.35},
 };
 }  // namespace

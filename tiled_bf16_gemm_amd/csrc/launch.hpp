@@ -16,7 +16,7 @@ struct GemmParams {
   int M, N, K;
   int kchunks;     // 16-byte chunks along K present in memory (ceil(K/8)); data past K there is zero
   int tiles_m, tiles_n, group_m;
-  int vec_store;   // C and its rows are 16-byte aligned: whole 16-byte stores allowed
+  int vec_store;   // C's base and row pitch are multiples of 4 bytes: whole 16-byte pieces may be stored
   float alpha, beta;
   int scaled;      // 0: C = A·B; 1: C = alpha·A·B + beta·C (C read only when beta != 0)
   // Clock-recording instances only (a measurement build outside the C ABI): per workgroup the
