@@ -536,6 +536,44 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
                      const tbg_gemm_config* cfg, void* workspace, size_t workspace_bytes, void* stream, bool scaled,
                      tbg_dtype ab_dtype = TBG_BF16);
 
+// The operand boxes of a product as this library's descriptors, encoded (and so checked) by
+// tbg_encode_tiled ("2 · Le Tensor Memory Accelerator" §2.3: the descriptor is built once on the
+// host and handed to the kernel): A {K, M} with box {one 128-byte row of K, bm}; B stored N×K
+// {K, N} with box {one 128-byte row of K, bn}, both with the 2-row swizzle; B stored K×N {N, K}
+// with box {64, 64} and the transposing-read swizzle; zero fill.  These are the boxes and layouts
+// the kernels copy into their LDS stages.  K = 0: no operand is read and both stay zero.
+tbg_status encode_operand_boxes(tbg::GemmParams& p, tbg_dtype ab, tbg_b_layout bl, int bm, int bn, int64_t M,
+                                int64_t N, int64_t K, const void* A, int64_t lda_bytes, const void* B,
+                                int64_t ldb_bytes) {
+  memset(&p.da, 0, sizeof(p.da));
+  memset(&p.db, 0, sizeof(p.db));
+  if (K == 0) return TBG_OK;
+  static_assert(sizeof(tbg_tensor_desc) == sizeof(tbg::DescImpl), "descriptor sizes");
+  const uint32_t row = (ab == TBG_F8_E4M3 || ab == TBG_F8_E5M2) ? 128u : 64u;  // elements per 128 bytes
+  const uint32_t one[2] = {1, 1};
+  tbg_tensor_desc d;
+  {
+    const uint64_t dims[2] = {(uint64_t)K, (uint64_t)M};
+    const uint64_t strides[1] = {(uint64_t)lda_bytes};
+    const uint32_t box[2] = {row, (uint32_t)bm};
+    const tbg_status st =
+        tbg_encode_tiled(&d, ab, 2, A, dims, strides, box, one, TBG_SWIZZLE_128B_2ROW, TBG_L2_NONE, TBG_OOB_ZERO);
+    if (st != TBG_OK) return st;
+    memcpy(&p.da, &d, sizeof(d));
+  }
+  {
+    const bool nk = bl == TBG_B_NK;
+    const uint64_t dims[2] = {(uint64_t)(nk ? K : N), (uint64_t)(nk ? N : K)};
+    const uint64_t strides[1] = {(uint64_t)ldb_bytes};
+    const uint32_t box[2] = {nk ? row : 64u, nk ? (uint32_t)bn : 64u};
+    const tbg_status st = tbg_encode_tiled(&d, ab, 2, B, dims, strides, box, one,
+                                           nk ? TBG_SWIZZLE_128B_2ROW : TBG_SWIZZLE_128B_TR, TBG_L2_NONE, TBG_OOB_ZERO);
+    if (st != TBG_OK) return st;
+    memcpy(&p.db, &d, sizeof(d));
+  }
+  return TBG_OK;
+}
+
 // The fp8 product: operands are byte matrices, repacked to 16-byte pitches with zero padding
 // where needed, then handed to the kernel as 16-bit pairs.
 tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
@@ -638,6 +676,8 @@ tbg_status gemm_fp8_impl(int64_t M, int64_t N, int64_t K, float alpha, const voi
       }
     }
   }
+  st = encode_operand_boxes(p, ab_dtype, bl, bm, bn, M, N, K, Ab, lda_b, Bb, ldb_b);
+  if (st != TBG_OK) return st;
   log_choice("gemm M=%lld N=%lld K=%lld B=nk in=%s out=%s: ring %dx%d, 2 stages; repack A %s, B %s", (long long)M,
              (long long)N, (long long)K, ab_dtype == TBG_F8_E5M2 ? "e5m2" : "e4m3", c_dtype == TBG_BF16 ? "bf16" : "f32",
              bm, bn, pack_a ? "yes" : "no", pack_b ? "yes" : "no");
@@ -764,6 +804,8 @@ tbg_status gemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void* A
   p.alpha = alpha;
   p.beta = beta;
   p.scaled = scaled ? 1 : 0;
+  st = encode_operand_boxes(p, ab_dtype, bl, ch.bm, ch.bn, M, N, K, Ae, lda_e * 2, Be, ldb_e * 2);
+  if (st != TBG_OK) return st;
   log_choice("gemm M=%lld N=%lld K=%lld B=%s in=%s out=%s: %s %dx%d, %d stages; repack A %s, B %s", (long long)M,
              (long long)N, (long long)K, bl == TBG_B_KN ? "kn" : "nk", in ? "f16" : "bf16",
              c_dtype == TBG_BF16 ? "bf16" : "f32", ch.pipeline == tbg::kPipeProducer ? "producer" : "ring", ch.bm,

@@ -386,22 +386,31 @@ struct OperandTiles {
   bool live;
 };
 
+// Row pitch in bytes of an operand descriptor (its dimension-1 stride).
+__device__ __forceinline__ uint32_t row_pitch(const DescImpl& d) { return (uint32_t)d.stride[1]; }
+
+// The copy plan from the operand descriptors the host encoded: A's box origin moves m0 rows down,
+// B's n0 rows (stored N×K) or n0 elements along a row (stored K×N); the 16-byte K chunks present
+// in a row are A's inner extent in bytes, rounded up.
 template <int BL>
 __device__ __forceinline__ CopyPlan make_copy_plan(const GemmParams& p, int m0, int n0) {
   CopyPlan c;
-  c.kchunks = p.kchunks;
-  c.ra0 = make_rsrc(p.A + (uint64_t)m0 * p.lda, 0x7FFFFFFFull);
+  const DescImpl& da = p.da;
+  const DescImpl& db = p.db;
+  c.kchunks = (int)((da.dim[0] * da.elsize + 15) / 16);
+  c.ra0 = make_rsrc((const uint8_t*)da.base + (uint64_t)m0 * da.stride[1], 0x7FFFFFFFull);
   if (BL == 1) {
-    c.rb0 = make_rsrc(p.B + (uint64_t)n0 * p.ldb, 0x7FFFFFFFull);
+    c.rb0 = make_rsrc((const uint8_t*)db.base + (uint64_t)n0 * db.stride[1], 0x7FFFFFFFull);
     c.step_b = 128u;
     c.rem_b0 = 0;
   } else {
-    c.rb0 = make_rsrc(p.B + n0, 0);
-    c.step_b = (uint32_t)(p.ldb * 2 * kBK);
+    c.rb0 = make_rsrc((const uint8_t*)db.base + (uint64_t)n0 * db.elsize, 0);
+    c.step_b = (uint32_t)(db.stride[1] * kBK);
     // Round the last row's end up to a whole dword: the range check works on dwords, so a last
     // element in the low half of one is still fetched.  The two bytes past it share that dword
     // (and its page) and only reach columns past N.
-    c.rem_b0 = (((int64_t)(p.K - 1) * p.ldb + (p.N - n0)) * 2 + 3) & ~(int64_t)3;
+    c.rem_b0 = ((int64_t)(db.dim[1] - 1) * (int64_t)db.stride[1] + ((int64_t)db.dim[0] - n0) * db.elsize + 3) &
+               ~(int64_t)3;
   }
   return c;
 }

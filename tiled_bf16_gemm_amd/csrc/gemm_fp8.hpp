@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
+  const uint32_t pitch_a = row_pitch(p.da), pitch_b = row_pitch(p.db);
   LaneChunk la[T::AtomsA], lb[T::AtomsB];
 #pragma unroll
   for (int i = 0; i < T::AtomsA; ++i) {

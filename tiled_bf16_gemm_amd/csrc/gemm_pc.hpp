@@ -69,7 +69,7 @@ __device__ __forceinline__ void produce(const GemmParams& p, const uint8_t* smem
   using C = PcCfg<BM, BN, S>;
   using T = TileCfg<BM, BN>;
   static_assert(PW < C::NP, "producer wave index");
-  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
+  const uint32_t pitch_a = row_pitch(p.da), pitch_b = row_pitch(p.db);
   const uint32_t smem_addr = lds_addr_of(smem);
   LaneChunk ch[C::PA];
 #pragma unroll

@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   // B stored N×K: the same with n.  B stored K×N: BN/64 boxes {64 n, 64 k} at (n0 + 64*b, k0),
   // K×N layout (kSwizzleKnTr), 8 atoms each; this wave owns atoms AtomsB*wave .. +AtomsB-1 of the boxes in
   // order, all inside one box.
-  const uint32_t pitch_a = (uint32_t)(p.lda * 2), pitch_b = (uint32_t)(p.ldb * 2);
+  const uint32_t pitch_a = row_pitch(p.da), pitch_b = row_pitch(p.db);
   const int b_box = (wave * T::AtomsB) >> 3;  // K×N box of this wave's B atoms
   LaneChunk la[T::AtomsA], lb[T::AtomsB];
 #pragma unroll

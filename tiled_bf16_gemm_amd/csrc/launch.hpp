@@ -7,7 +7,11 @@
 
 namespace tbg {
 
-// Arguments of one GEMM launch (see gemm_kernel.hip).
+// Arguments of one GEMM launch (see gemm_kernel.hip).  The barrier ring, the producer ring and
+// the fp8 ring read their operands through `da` and `db`, the descriptors of the operand boxes
+// that the host encodes with tbg_encode_tiled ("2 · Le Tensor Memory Accelerator" §2.3: built
+// once on the host, handed to the kernel): base address, row pitch in bytes and extents (A {K, M};
+// B {K, N} stored N×K, {N, K} stored K×N).  A, B, lda and ldb stay for the convolution kernel.
 struct GemmParams {
   const uint16_t* A;
   const uint16_t* B;
@@ -22,6 +26,7 @@ struct GemmParams {
   // Clock-recording instances only (a measurement build outside the C ABI): per workgroup the
   // 100 MHz real-time and shader-clock counter deltas from its start to its end.  Null otherwise.
   uint64_t* clock;
+  DescImpl da, db;  // operand box descriptors (zero when K = 0: every copy is masked)
 };
 
 // Arguments of one implicit-GEMM convolution launch (gemm_conv.hpp).  `g` carries what the

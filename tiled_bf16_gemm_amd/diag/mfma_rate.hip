@@ -103,6 +103,17 @@ extern "C" int tbg_diag_gemm_clock(const void* A, const void* B, void* C, int M,
   p.vec_store = 1;
   p.alpha = 1.f;
   p.clock = (uint64_t*)clk;
+  // the operand descriptors the library's encoder would produce (the fields the kernel reads):
+  // A {K, M}, B stored K×N {N, K}, bf16, row pitches in bytes
+  p.da.elsize = p.db.elsize = 2;
+  p.da.base = (uint64_t)(uintptr_t)A;
+  p.da.dim[0] = (uint64_t)K;
+  p.da.dim[1] = (uint64_t)M;
+  p.da.stride[1] = (uint64_t)lda * 2;
+  p.db.base = (uint64_t)(uintptr_t)B;
+  p.db.dim[0] = (uint64_t)N;
+  p.db.dim[1] = (uint64_t)K;
+  p.db.stride[1] = (uint64_t)ldb * 2;
   const int nwg = p.tiles_m * p.tiles_n;
   if (nwg_out) *nwg_out = nwg;
   hipLaunchKernelGGL((tbg::gemm_ring_kernel<256, 256, 2, 0, 0, 1, 0, 1>), dim3(nwg), dim3(tbg::kThreads), 0,
