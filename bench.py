@@ -424,8 +424,15 @@ def cpu_baseline(w, target_s: float = 15.0):
     }
 
 
+# The library's kernels for the two large workloads (bf16 in, bf16 out, 256×256 ring, 2 stages):
+# B stored K×N (8192³) and B stored N×K (16384×14336×4096).
+C4_KERNEL = "gemm_ring_kernel<256, 256, 2, 0, 0, 1, 0, 0>"
+C5_KERNEL = "gemm_ring_kernel<256, 256, 2, 0, 1, 1, 0, 0>"
+
+
 def counters_driver(torch, torch_ops, w):
-    """Fixed launches for counter collection: the GEMM, then a copy of known size."""
+    """Fixed launches for counter collection: the 8192³ GEMM, the same with E4M3 inputs, the
+    16384×14336×4096 GEMM, then a copy of known size (the calibration kernel)."""
     import workloads
     A, B = workloads.gemm_inputs(w)
     A = A.cuda()
@@ -440,20 +447,30 @@ def counters_driver(torch, torch_ops, w):
     for _ in range(5):
         torch_ops.gemm(A8, B8, "nk", w.out_dtype, out=C)
     torch.cuda.synchronize()
-    del A8, B8
+    del A8, B8, A, B, C
+    w5 = workloads.GEMMS["c5"]
+    A, B = workloads.gemm_inputs(w5)
+    A, B = A.cuda(), B.cuda()
+    C = torch.empty((w5.M, w5.N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        torch_ops.gemm(A, B, w5.b_layout, w5.out_dtype, out=C)
+    torch.cuda.synchronize()
+    del A, B, C
     src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print("counters driver: 5 gemm launches (8192^3 bf16), 5 with E4M3 inputs, 5 copies of 536870912 bytes",
-          flush=True)
+    print("counters driver: 5 gemm launches (8192^3 bf16), 5 with E4M3 inputs, 5 of 16384x14336x4096, "
+          "5 copies of 536870912 bytes", flush=True)
 
 
 def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str, commands: dict,
                        sq_db: str = "") -> dict:
     """Write the short text summaries of rocprofv3 runs into profiles/ (and the traffic figure
-    bench.py reports).  Reads rocprofv3's SQLite output with the standard library only."""
+    bench.py reports).  Reads rocprofv3's SQLite output with the standard library only.
+    commands["bench_line"] (optional): the JSON line the traced bench run printed; its timed
+    steps are the last `steps` dispatches of the 8192³ kernel in the trace."""
     import sqlite3
     import statistics
 
@@ -464,17 +481,42 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
         finally:
             c.close()
 
-    gemm_name = "gemm_ring_kernel"
+    line = commands.get("bench_line")
     top = rows(trace_db, "select name, total_calls, total_duration, average, percentage from top_kernels")
-    lines = ["# GEMM kernel trace, 8192^3 workload (bf16 in, fp32 accumulate, bf16 out)", "",
-             "Command (<repo> is the repository root, <out> the output folder):", "", "```", commands["trace"], "```", "",
-             "Summary written by `python bench.py --summarize <out>`.", "",
+    lines = ["# GEMM kernel trace, 8192³ workload (bf16 in, fp32 accumulate, bf16 out) and the rest of the bench run",
+             "", "Command (<repo> is the repository root, <out> the output folder):", "", "```", commands["trace"], "```",
+             "", "Summary written by `python bench.py --summarize <out>`.", "",
              "rocprofv3 kernel statistics (durations in microseconds):", "",
              "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
     for name, calls, total, avg, pct in top:
-        lines.append(f"| `{name}` | {calls} | {total:.1f} | {avg:.3f} | {pct:.1f} |")
-    gemm_avg = [avg for name, _, _, avg, _ in top if gemm_name in name]
-    lines += ["", f"bench.py's HIP-event average for the same kernel: {commands.get('bench_kernel_us', 'n/a')} us."]
+        short = name if len(name) <= 110 else name[:107] + "..."
+        lines.append(f"| `{short}` | {calls} | {total:.1f} | {avg:.3f} | {pct:.1f} |")
+    gemm_avg = [avg for name, _, _, avg, _ in top if C4_KERNEL in name]
+    try:
+        disp = [d / 1e3 for n, d in rows(trace_db, "select name, duration from kernels order by start") if C4_KERNEL in n]
+    except sqlite3.Error:
+        disp = []
+    timed_avg = None
+    if line and disp:
+        steps = int(line.get("steps", 20))
+        timed = disp[-steps:]
+        timed_avg = statistics.mean(timed)
+        k_ms = line["roofline"]["kernel_ms"]
+        flops = line["roofline"]["flops_per_launch"]
+        lines += ["", f"The 8192³ kernel's {len(disp)} dispatches are the bench's settle regions, its warm-up and its "
+                      f"{steps} timed steps, in that order; the last {steps} are the timed steps.", "",
+                  "| dispatches | average us | median us | TFLOP/s at the average | frac of 2516.6 |",
+                  "|---|---|---|---|---|",
+                  f"| all {len(disp)} | {statistics.mean(disp):.2f} | {statistics.median(disp):.2f} | "
+                  f"{flops / (statistics.mean(disp) * 1e-6) / 1e12:.1f} | "
+                  f"{flops / (statistics.mean(disp) * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |",
+                  f"| timed {steps} | {timed_avg:.2f} | {statistics.median(timed):.2f} | "
+                  f"{flops / (timed_avg * 1e-6) / 1e12:.1f} | {flops / (timed_avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |",
+                  "", f"The same run's bench line (HIP events on the launch stream): kernel_ms {k_ms} "
+                      f"({k_ms * 1e3:.2f} us), roofline.achieved {line['roofline']['achieved']} TFLOP/s, frac "
+                      f"{line['roofline']['frac']}; value {line['value']} TFLOP/s."]
+    elif commands.get("bench_kernel_us") is not None:
+        lines += ["", f"bench.py's HIP-event average for the same kernel: {commands['bench_kernel_us']} us."]
     with open(os.path.join(out_dir, "gemm_8192_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -489,15 +531,25 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
     copy_bytes = 512 << 20
     calib_f = [v for k, v in fetch.items() if "copyBuffer" in k][0]
     calib_w = [v for k, v in write.items() if "copyBuffer" in k][0]
-    gemm_f = [v for k, v in fetch.items() if gemm_name in k][0]
-    gemm_w = [v for k, v in write.items() if gemm_name in k][0]
     sf = copy_bytes / (statistics.median(calib_f) * 1024)
     sw = copy_bytes / (statistics.median(calib_w) * 1024)
-    fb = statistics.median(gemm_f) * 1024 * sf
-    wb = statistics.median(gemm_w) * 1024 * sw
+    avg_us = timed_avg if timed_avg is not None else (gemm_avg[0] if gemm_avg else None)
+    table, figures = [], {}
+    for label, kname, (M, N, K) in (("8192³", C4_KERNEL, (8192, 8192, 8192)),
+                                    ("16384×14336×4096", C5_KERNEL, (16384, 14336, 4096))):
+        gf = [v for k, v in fetch.items() if kname in k]
+        gw = [v for k, v in write.items() if kname in k]
+        if not gf or not gw:
+            continue
+        fb = statistics.median(gf[0]) * 1024 * sf
+        wb = statistics.median(gw[0]) * 1024 * sw
+        algo = (M * K + K * N + M * N) * 2
+        figures[label] = (fb, wb, algo)
+        table += [f"| {label} | FETCH_SIZE | {statistics.median(gf[0]):.1f} | {len(gf[0])} | {sf:.4f} | {fb:.4g} |",
+                  f"| {label} | WRITE_SIZE | {statistics.median(gw[0]):.1f} | {len(gw[0])} | {sw:.4f} | {wb:.4g} |"]
+    fb, wb, algo = figures["8192³"]
     total = fb + wb
-    algo = 2 * 8192 * 8192 * 2 + 8192 * 8192 * 2
-    lines = ["# HBM traffic of the GEMM kernel, 8192^3 workload", "",
+    lines = ["# HBM traffic of the GEMM kernel, 8192³ and 16384×14336×4096 workloads", "",
              "Commands (one counter per run; <repo> is the repository root, <out> the output folder):", "", "```",
              commands["fetch"], commands["write"], "```", "",
              "Summary written by `python bench.py --summarize <out>`.", "",
@@ -507,20 +559,26 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
              "|---|---|---|---|---|---|",
              f"| calibration copy | FETCH_SIZE | {statistics.median(calib_f):.1f} | {len(calib_f)} | {sf:.4f} | {copy_bytes} |",
              f"| calibration copy | WRITE_SIZE | {statistics.median(calib_w):.1f} | {len(calib_w)} | {sw:.4f} | {copy_bytes} |",
-             f"| GEMM | FETCH_SIZE | {statistics.median(gemm_f):.1f} | {len(gemm_f)} | {sf:.4f} | {fb:.4g} |",
-             f"| GEMM | WRITE_SIZE | {statistics.median(gemm_w):.1f} | {len(gemm_w)} | {sw:.4f} | {wb:.4g} |", "",
-             f"HBM bytes per GEMM launch: {total:.4g} (algorithmic minimum A + B + C once: {algo:.4g}; "
-             f"ratio {total / algo:.2f}).",
-             (f"Over the kernel trace's average launch ({gemm_avg[0]:.1f} us): {total / (gemm_avg[0] * 1e-6) / 1e9:.0f} "
-              f"GB/s of these bytes, {100 * total / (gemm_avg[0] * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f} % of the 8 TB/s HBM "
-              f"peak; the algorithmic bytes alone: {algo / (gemm_avg[0] * 1e-6) / 1e9:.0f} GB/s." if gemm_avg else ""),
-             f"Kernel source hash of the tree summarized (the counter runs are taken on that same tree): "
-             f"{kernel_source_hash()}"]
+             *table, ""]
+    for label, (f_, w_, a_) in figures.items():
+        lines.append(f"HBM bytes per {label} launch: {f_ + w_:.4g} (algorithmic minimum A + B + C once: {a_:.4g}; "
+                     f"ratio {(f_ + w_) / a_:.2f}).")
+    if avg_us:
+        lines.append(f"Over the 8192³ kernel's timed launches ({avg_us:.1f} us on average): "
+                     f"{total / (avg_us * 1e-6) / 1e9:.0f} GB/s of these bytes, "
+                     f"{100 * total / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f} % of the 8 TB/s HBM peak; the "
+                     f"algorithmic bytes alone: {algo / (avg_us * 1e-6) / 1e9:.0f} GB/s.")
+    lines.append(f"Kernel source hash of the tree summarized (the counter runs are taken on that same tree): "
+                 f"{kernel_source_hash()}")
     with open(os.path.join(out_dir, "gemm_8192_hbm_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     traffic = {"kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": round(total),
                "fetch_bytes": round(fb), "write_bytes": round(wb), "fetch_scale": sf, "write_scale": sw,
-               "algorithmic_bytes": algo, "gemm_trace_avg_us": gemm_avg[0] if gemm_avg else None}
+               "algorithmic_bytes": algo, "gemm_trace_avg_us": avg_us}
+    if "16384×14336×4096" in figures:
+        f5, w5, a5 = figures["16384×14336×4096"]
+        traffic["c5"] = {"hbm_bytes_per_launch": round(f5 + w5), "fetch_bytes": round(f5), "write_bytes": round(w5),
+                         "algorithmic_bytes": a5}
     with open(os.path.join(out_dir, "gemm_8192_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
     if sq_db and os.path.exists(sq_db):
@@ -595,7 +653,7 @@ def summarize_sq(db: str, out_dir: str, command: str) -> None:
         d = per.setdefault(name, {}).setdefault(disp, {})
         d[cn] = v
         d["duration_ns"] = dur
-    lines = ["# MFMA utilisation and LDS bank conflicts of the GEMM kernels, 8192^3", "",
+    lines = ["# MFMA utilisation and LDS bank conflicts of the GEMM kernels, 8192³ (bf16 and E4M3) and 16384×14336×4096", "",
              "Command (<repo> is the repository root, <out> the output folder):", "", "```", command, "```", "",
              "Summary written by `python bench.py --summarize <out>`.  Medians over the dispatches.", "",
              "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 × SQ_BUSY_CU_CYCLES): the share of CU-busy cycles the",
@@ -773,6 +831,16 @@ def write_sweep_profiles(jsonl: str, out_dir: str) -> None:
         f.write("\n".join(lines))
 
 
+def _read_bench_line(path: str):
+    """The last JSON line a bench run wrote to `path`, or None."""
+    try:
+        with open(path) as f:
+            lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+        return json.loads(lines[-1]) if lines else None
+    except (OSError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -798,9 +866,10 @@ def main():
                     help="profiling driver: 5 GEMM launches on the 8192^3 workload, then 5 plain device copies "
                          "of 512 MiB (the calibration kernel for HBM byte counters); prints no JSON")
     ap.add_argument("--summarize", default="", metavar="DIR",
-                    help="write the profiles/ summaries from rocprofv3 runs under DIR (DIR/trace, DIR/fetch, "
-                         "DIR/write and optionally DIR/sq, each made with -o run as the summaries' commands show); "
-                         "runs on any host, no GPU needed")
+                    help="write the profiles/ summaries from rocprofv3 runs under DIR (DIR/trace with the traced "
+                         "bench line in DIR/trace/bench_line.json, DIR/fetch, DIR/write and optionally DIR/sq and "
+                         "DIR/copytrace, each made with -o run as the summaries' commands show); the traced bench "
+                         "line is also written to profiles/bench_8192_line.json; runs on any host, no GPU needed")
     ap.add_argument("--bench-kernel-us", type=float, default=None,
                     help="with --summarize: the bench line's HIP-event kernel average, quoted beside the trace")
     ap.add_argument("--sweep", default="",
@@ -822,7 +891,7 @@ def main():
         d = args.summarize
         cmds = {
             "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/trace -o run -- "
-                     "python -u <repo>/bench.py --no-cpu-baseline --no-configs --no-ceiling",
+                     "python3 -u <repo>/bench.py --gpus 1 --steps 20 --warmup 5 > <out>/trace/bench_line.json",
             "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE -d <out>/fetch -o run -- "
                      "python -u <repo>/bench.py --counters",
             "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE -d <out>/write -o run -- "
@@ -832,10 +901,14 @@ def main():
             "copytrace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/copytrace -o run -- "
                          "python -u <repo>/bench.py --only-copies",
             "bench_kernel_us": args.bench_kernel_us,
+            "bench_line": _read_bench_line(os.path.join(d, "trace", "bench_line.json")),
         }
         t = summarize_profiles(os.path.join(d, "trace", "run_results.db"), os.path.join(d, "fetch", "run_results.db"),
                                os.path.join(d, "write", "run_results.db"), os.path.join(ROOT, "profiles"), cmds,
                                os.path.join(d, "sq", "run_results.db"))
+        if cmds["bench_line"]:
+            with open(os.path.join(ROOT, "profiles", "bench_8192_line.json"), "w") as f:
+                f.write(json.dumps(cmds["bench_line"]) + "\n")
         print(json.dumps(t))
         return
 

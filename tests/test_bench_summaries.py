@@ -10,7 +10,8 @@ import sys
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM = "void tbg::gemm_ring_kernel<256, 256, 2, 0, 0, 1, 0>(tbg::GemmParams)"
+GEMM = "void tbg::gemm_ring_kernel<256, 256, 2, 0, 0, 1, 0, 0>(tbg::GemmParams)"
+GEMM5 = "void tbg::gemm_ring_kernel<256, 256, 2, 0, 1, 1, 0, 0>(tbg::GemmParams)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -39,8 +40,9 @@ def _trace_db(path, avg_us):
 def test_traffic_from_counter_databases(tmp_path):
     # the calibration copy moves 512 MiB each way; FETCH_SIZE reads half of it (scale 2), WRITE_SIZE all
     copy_kib = (512 << 20) / 1024
-    fetch = {COPY: [(copy_kib / 2, 1)] * 5, GEMM: [(1000000.0, 700000)] * 4 + [(9e9, 700000)]}
-    write = {COPY: [(copy_kib, 1)] * 5, GEMM: [(131072.0, 700000)] * 5}
+    fetch = {COPY: [(copy_kib / 2, 1)] * 5, GEMM: [(1000000.0, 700000)] * 4 + [(9e9, 700000)],
+             GEMM5: [(2000000.0, 1200000)] * 5}
+    write = {COPY: [(copy_kib, 1)] * 5, GEMM: [(131072.0, 700000)] * 5, GEMM5: [(458752.0, 1200000)] * 5}
     for sub in ("trace", "fetch", "write"):
         os.makedirs(tmp_path / sub)
     _trace_db(str(tmp_path / "trace" / "run_results.db"), 700.0)
@@ -64,6 +66,11 @@ def test_traffic_from_counter_databases(tmp_path):
     assert "700.000" in (out / "gemm_8192_kernel_trace.md").read_text()
     saved = json.loads((out / "gemm_8192_traffic.json").read_text())
     assert saved["hbm_bytes_per_launch"] == t["hbm_bytes_per_launch"]
+    # the 16384x14336x4096 kernel gets its own figures
+    assert saved["c5"]["fetch_bytes"] == round(2000000.0 * 1024 * 2)
+    assert saved["c5"]["write_bytes"] == round(458752.0 * 1024)
+    assert saved["c5"]["algorithmic_bytes"] == (16384 * 4096 + 4096 * 14336 + 16384 * 14336) * 2
+    assert "16384×14336×4096 | FETCH_SIZE" in text
 
 
 def test_more_than_one_gpu_is_refused():
@@ -71,3 +78,37 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path):
+    """The traced bench run's last `steps` dispatches of the 8192^3 kernel are its timed steps: the
+    summary gives their average next to the bench line's own HIP-event figure."""
+    for sub in ("trace", "fetch", "write"):
+        os.makedirs(tmp_path / sub)
+    db = str(tmp_path / "trace" / "run_results.db")
+    _trace_db(db, 700.0)
+    c = sqlite3.connect(db)
+    c.execute("create table kernels (name text, start int, duration int)")
+    durs = [800000] * 30 + [700000] * 20   # ns: settle / warm-up dispatches, then 20 timed ones
+    for i, d in enumerate(durs):
+        c.execute("insert into kernels values (?, ?, ?)", (GEMM, i, d))
+    c.execute("insert into kernels values (?, ?, ?)", ("other", 99, 5))
+    c.commit()
+    c.close()
+    copy_kib = (512 << 20) / 1024
+    _counters_db(str(tmp_path / "fetch" / "run_results.db"), "FETCH_SIZE",
+                 {COPY: [(copy_kib / 2, 1)] * 5, GEMM: [(1000000.0, 700000)] * 5})
+    _counters_db(str(tmp_path / "write" / "run_results.db"), "WRITE_SIZE",
+                 {COPY: [(copy_kib, 1)] * 5, GEMM: [(131072.0, 700000)] * 5})
+    out = tmp_path / "profiles"
+    os.makedirs(out)
+    line = {"steps": 20, "value": 1500.0, "roofline": {"kernel_ms": 0.7, "achieved": 1570.7, "frac": 0.6241,
+                                                        "flops_per_launch": 2 * 8192 ** 3}}
+    cmds = {k: k for k in ("trace", "fetch", "write", "sq", "copytrace")}
+    cmds["bench_line"] = line
+    t = bench.summarize_profiles(db, str(tmp_path / "fetch" / "run_results.db"),
+                                 str(tmp_path / "write" / "run_results.db"), str(out), cmds)
+    text = (out / "gemm_8192_kernel_trace.md").read_text()
+    assert "| timed 20 | 700.00 | 700.00 |" in text
+    assert "| all 50 |" in text and "kernel_ms 0.7" in text
+    assert abs(t["gemm_trace_avg_us"] - 700.0) < 1e-9
