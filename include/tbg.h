@@ -217,8 +217,12 @@ size_t tbg_gemm_workspace_query(int64_t M, int64_t N, int64_t K, tbg_dtype ab_dt
  *   B          bf16, TBG_B_KN: row-major K×N, ldb >= N;  TBG_B_NK: N×K, ldb >= K.
  *   C          TBG_F32 or TBG_BF16, row-major M×N, ldc >= N.  Only C[m][n] with m < M, n < N is
  *              written; C must not overlap A, B or the workspace.
- *   workspace  device memory of at least tbg_gemm_workspace_bytes(...) bytes (plus the pack
- *              size of any operand whose base is not 16-byte aligned); may be NULL when 0.
+ *   workspace  device memory of at least tbg_gemm_workspace_query(...) bytes (the exact need,
+ *              misaligned bases included; tbg_gemm_workspace_bytes gives it for 16-byte aligned
+ *              operands), 256-byte aligned; may be NULL when 0.
+ * The operand boxes the kernels copy are encoded with tbg_encode_tiled (A {K, M}, B {K, N} or
+ * {N, K}, with this library's LDS layouts) and handed to the kernels, which take base, row pitch
+ * and extents from them.
  * M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).  Leading dimensions are
  * limited to 2^22 - 1 elements.
  * Returns INVALID_VALUE (negative sizes, ld below its minimum, null pointers, bad enum),
@@ -312,10 +316,9 @@ tbg_status tbg_gemm_configured(int64_t M, int64_t N, int64_t K, float alpha, con
  *                       8-bit inputs on the 16x16x128 matrix instruction.  B must be stored N×K
  *                       (TBG_B_NK; TBG_B_KN is UNSUPPORTED); lda, ldb in elements (bytes); rows
  *                       whose pitch or K is not a multiple of 16 bytes, or operands off a 16-byte
- *                       boundary, are repacked into the workspace (tbg_gemm_workspace_bytes
- *                       with half the leading dimensions and K rounded up to 16 is an upper
- *                       bound; the OUT_OF_RANGE detail names the size).  Configurations: ring,
- *                       2 stages, tiles 256x256, 128x128, 64x64.
+ *                       boundary, are repacked into the workspace (tbg_gemm_workspace_query
+ *                       gives the exact size; the OUT_OF_RANGE detail names it too).
+ *                       Configurations: ring, 2 stages, tiles 256x256, 128x128, 64x64.
  * Every product of two inputs is exact in fp32; accumulation is fp32, output fp32 or bf16.  cfg
  * may be NULL (the library's choice).  Other arguments, layouts and checks as tbg_gemm_ex; any
  * other ab_dtype is INVALID_VALUE.  tbg_gemm_configured is this call with ab_dtype = TBG_BF16. */
