@@ -75,3 +75,46 @@ def test_noalloc_refuses_what_does_not_fit():
     st = lib.tbg_gemm_noalloc(8191, 8191, 8191, 0x7F0000000000, 8191, 0x7F0000000000, 8191, 0, 0x7F0000000000, 8191,
                               5, None)
     assert st == tbg.ERR_OUT_OF_RANGE and "allocation-free" in tbg.last_error()
+
+
+@gpu
+def test_noalloc_under_graph_capture():
+    """The allocation-free product captured into a HIP graph (torch.cuda.graph) on operands that
+    need the repack, replayed three times with eager work (and an eager call of the same entry
+    point on other operands, which overwrites the scratch array) between the replays: every replay
+    equals the eager result bit for bit."""
+    lib = _lib()
+    M, N, K, lda, ldb = 300, 257, 777, 777, 257
+    _, _, Ad, Bd = _ragged(M, N, K, lda, ldb, "kn", 9300)
+    _, _, Ad2, Bd2 = _ragged(200, 130, 100, 101, 131, "kn", 9400)
+
+    def call(A, B, C, m, n, k, la, lb, stream):
+        st = lib.tbg_gemm_noalloc(m, n, k, A.data_ptr(), la, B.data_ptr(), lb, 0, C.data_ptr(), n, 5, stream)
+        assert st == 0
+
+    eager = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    call(Ad, Bd, eager, M, N, K, lda, ldb, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    other = torch.empty((200, 130), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # warm-up on the capture stream
+        call(Ad, Bd, out, M, N, K, lda, ldb, stream.cuda_stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        call(Ad, Bd, out, M, N, K, lda, ldb, stream.cuda_stream)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"noalloc graph replay {rep}", flush=True)
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager result"
+        call(Ad2, Bd2, other, 200, 130, 100, 101, 131, torch.cuda.current_stream().cuda_stream)
+        x = torch.randn(512, 512, device="cuda") @ torch.randn(512, 512, device="cuda")
+        torch.cuda.synchronize()
+        del x
+    del g
