@@ -725,9 +725,13 @@ def sweep(torch, torch_ops, names, steps, warmup):
             configs = SWEEP_CONFIGS_F16
         elif ab.startswith("f8"):
             configs = SWEEP_CONFIGS_F8
+        # operands once per workload; every configuration gets a short settle of its own region
+        # first (after idle time the device runs the first launches slow, see time_gemm_detail)
+        ops = gemm_operands(torch, w, ab)
         for pipe, tile, st in configs:
             cfg = tbg.gemm_config(tile, st, pipe)
-            ms, kms, _ = time_gemm(torch, torch_ops, w, steps, warmup, config=cfg, ab=ab)
+            ms = time_gemm_detail(torch, torch_ops, w, steps, warmup, config=cfg, ab=ab, settle_s=0.1,
+                                  operands=ops)["ms_step"]
             tf = w.flops / (ms * 1e-3) / 1e12
             r = {"workload": name, "pipeline": pipe, "tile": tile, "stages": st, "ms": round(ms, 5),
                  "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_TFLOPS[ab], 2)}
@@ -738,6 +742,7 @@ def sweep(torch, torch_ops, names, steps, warmup):
                 r["graph_tflops"] = round(w.flops / (gms * 1e-3) / 1e12, 2)
             print(json.dumps(r), flush=True)
             results.append(r)
+        del ops
         torch.cuda.empty_cache()
     return results
 
@@ -783,8 +788,9 @@ def write_sweep_profiles(jsonl: str, out_dir: str) -> None:
 
     head = ["Command (repository root on the GPU box; <out> an output folder), then "
             "`python bench.py --sweep-md <out>/sweep.jsonl`:", "", "```", SWEEP_CMD, "```", "",
-            "Each configuration: 20 timed calls after 5 warm-up calls, HIP events on the launch stream (per-call "
-            "times include the host); for c1-c3 also 20 products captured in a HIP graph and replayed 20 times "
+            "Each configuration: its region (5 warm-up calls, then 20 calls timed with HIP events on the launch "
+            "stream; per-call times include the host) run untimed for 0.1 s, then once timed; operands generated "
+            "once per workload; for c1-c3 also 20 products captured in a HIP graph and replayed 20 times "
             "(GPU time per product).  One pass on one MI355X; boxes differ by a few per cent.", ""]
     # bf16 GEMM
     lines = ["# GEMM pipeline × tile × stages sweep", "",

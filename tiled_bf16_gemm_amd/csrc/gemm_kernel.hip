@@ -183,9 +183,9 @@ struct Candidate {
 // Candidates of equal cost keep the first listed: the 128×128 ring comes before the 128×256 producer
 // ring (on 3008×2056×784, where their costs tie, the ring's kernel took 19.4 µs, the producer's 21.0).
 const Candidate kCandidates[] = {
-    {kPipeRing, 256, 256, 2, 1.00},     {kPipeRing, 128, 128, 2, 0.79},     {kPipeProducer, 128, 256, 2, 0.79},
-    {kPipeProducer, 256, 128, 2, 0.77}, {kPipeRing, 256, 128, 2, 0.72},     {kPipeRing, 128, 256, 2, 0.71},
-    {kPipeProducer, 128, 128, 3, 0.65}, {kPipeRing, 64, 64, 3, 0.44},       {kPipeProducer, 64, 64, 3, 0.35},
+    {kPipeRing, 256, 256, 2, 1.00},     {kPipeRing, 128, 128, 2, 0.76},     {kPipeProducer, 128, 256, 2, 0.75},
+    {kPipeProducer, 256, 128, 2, 0.75}, {kPipeRing, 256, 128, 2, 0.70},     {kPipeRing, 128, 256, 2, 0.69},
+    {kPipeProducer, 128, 128, 3, 0.61}, {kPipeRing, 64, 64, 3, 0.43},       {kPipeProducer, 64, 64, 3, 0.33},
 };
 }  // namespace
 
