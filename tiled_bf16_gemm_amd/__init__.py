@@ -92,7 +92,7 @@ class Error(RuntimeError):
 _u64p = ctypes.POINTER(ctypes.c_uint64)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
 _i32p = ctypes.POINTER(ctypes.c_int32)
-_vp = ctypes.c_void_p
+_vp = ctypes.c_void_p  # device addresses and streams are passed as plain ints (None for null)
 _i64 = ctypes.c_int64
 
 _lib.tbg_encode_tiled.restype = ctypes.c_int
@@ -186,7 +186,7 @@ def encode_tiled(dtype, rank: int, global_address: int, global_dim: Sequence[int
     """tbg_encode_tiled.  Per-dimension arrays innermost first; strides in bytes (rank-1)."""
     d = TensorDesc()
     strides = None if global_strides is None else _arr(ctypes.c_uint64, global_strides)
-    st = _lib.tbg_encode_tiled(ctypes.byref(d), _enum(DTYPES, dtype), int(rank), _vp(int(global_address)),
+    st = _lib.tbg_encode_tiled(ctypes.byref(d), _enum(DTYPES, dtype), int(rank), int(global_address),
                                _arr(ctypes.c_uint64, global_dim), strides, _arr(ctypes.c_uint32, box_dim),
                                _arr(ctypes.c_uint32, element_strides), _enum(SWIZZLES, swizzle), _enum(L2, l2),
                                _enum(OOB, oob))
@@ -199,7 +199,7 @@ def encode_tiled_interleaved(dtype, rank: int, global_address: int, global_dim: 
                              interleave="16B", swizzle="none", l2="none", oob="zero") -> TensorDesc:
     """tbg_encode_tiled_interleaved: an NC/xHWCx tensor, dimension 0 one 16- or 32-byte slice."""
     d = TensorDesc()
-    st = _lib.tbg_encode_tiled_interleaved(ctypes.byref(d), _enum(DTYPES, dtype), int(rank), _vp(int(global_address)),
+    st = _lib.tbg_encode_tiled_interleaved(ctypes.byref(d), _enum(DTYPES, dtype), int(rank), int(global_address),
                                            _arr(ctypes.c_uint64, global_dim), _arr(ctypes.c_uint64, global_strides),
                                            _arr(ctypes.c_uint32, box_dim), _arr(ctypes.c_uint32, element_strides),
                                            _enum(INTERLEAVES, interleave), _enum(SWIZZLES, swizzle), _enum(L2, l2),
@@ -230,23 +230,23 @@ def box_bytes(desc: TensorDesc) -> int:
 
 
 def tiled_copy(desc: TensorDesc, coords: Sequence[int], dst_image: int, stream: Optional[int] = None) -> None:
-    _check(_lib.tbg_tiled_copy(ctypes.byref(desc), _arr(ctypes.c_int32, coords), _vp(int(dst_image)),
-                               _vp(stream or 0)))
+    _check(_lib.tbg_tiled_copy(ctypes.byref(desc), _arr(ctypes.c_int32, coords), int(dst_image),
+                               stream or None))
 
 
 def tiled_copy_many(desc: TensorDesc, coords_dev: int, n: int, dst_images: int, stream: Optional[int] = None) -> None:
-    _check(_lib.tbg_tiled_copy_many(ctypes.byref(desc), _vp(int(coords_dev)), int(n), _vp(int(dst_images)),
-                                    _vp(stream or 0)))
+    _check(_lib.tbg_tiled_copy_many(ctypes.byref(desc), int(coords_dev), int(n), int(dst_images),
+                                    stream or None))
 
 
 def tiled_store(desc: TensorDesc, coords: Sequence[int], src_image: int, stream: Optional[int] = None) -> None:
-    _check(_lib.tbg_tiled_store(ctypes.byref(desc), _arr(ctypes.c_int32, coords), _vp(int(src_image)),
-                                _vp(stream or 0)))
+    _check(_lib.tbg_tiled_store(ctypes.byref(desc), _arr(ctypes.c_int32, coords), int(src_image),
+                                stream or None))
 
 
 def tiled_store_many(desc: TensorDesc, coords_dev: int, n: int, src_images: int, stream: Optional[int] = None) -> None:
-    _check(_lib.tbg_tiled_store_many(ctypes.byref(desc), _vp(int(coords_dev)), int(n), _vp(int(src_images)),
-                                     _vp(stream or 0)))
+    _check(_lib.tbg_tiled_store_many(ctypes.byref(desc), int(coords_dev), int(n), int(src_images),
+                                     stream or None))
 
 
 def encode_im2col(dtype, global_address: int, global_dim: Sequence[int], global_strides: Sequence[int],
@@ -256,7 +256,7 @@ def encode_im2col(dtype, global_address: int, global_dim: Sequence[int], global_
     """tbg_encode_im2col.  dims {C, W, H, N}; strides {W, H, N} in bytes; per-spatial arrays
     {along W, along H}."""
     d = TensorDesc()
-    st = _lib.tbg_encode_im2col(ctypes.byref(d), _enum(DTYPES, dtype), _vp(int(global_address)),
+    st = _lib.tbg_encode_im2col(ctypes.byref(d), _enum(DTYPES, dtype), int(global_address),
                                 _arr(ctypes.c_uint64, global_dim), _arr(ctypes.c_uint64, global_strides),
                                 _arr(ctypes.c_int32, pad_lo), _arr(ctypes.c_int32, pad_hi),
                                 _arr(ctypes.c_int32, conv_stride), _arr(ctypes.c_int32, dilation),
@@ -276,13 +276,13 @@ def encode_im2col_status(*args, **kwargs) -> int:
 
 def im2col_copy(desc: TensorDesc, coords: Sequence[int], dst_image: int, stream: Optional[int] = None) -> None:
     """tbg_im2col_copy: coords = {c0, m0, s, r}."""
-    _check(_lib.tbg_im2col_copy(ctypes.byref(desc), _arr(ctypes.c_int32, coords), _vp(int(dst_image)),
-                                _vp(stream or 0)))
+    _check(_lib.tbg_im2col_copy(ctypes.byref(desc), _arr(ctypes.c_int32, coords), int(dst_image),
+                                stream or None))
 
 
 def im2col_copy_many(desc: TensorDesc, coords_dev: int, n: int, dst_images: int, stream: Optional[int] = None) -> None:
-    _check(_lib.tbg_im2col_copy_many(ctypes.byref(desc), _vp(int(coords_dev)), int(n), _vp(int(dst_images)),
-                                     _vp(stream or 0)))
+    _check(_lib.tbg_im2col_copy_many(ctypes.byref(desc), int(coords_dev), int(n), int(dst_images),
+                                     stream or None))
 
 
 def conv2d_out_dims(shape: Conv2dShape):
@@ -296,7 +296,7 @@ def conv2d_workspace_bytes(shape: Conv2dShape) -> int:
 
 
 def conv2d_workspace_query(shape: Conv2dShape, x: int, w: int) -> int:
-    return int(_lib.tbg_conv2d_workspace_query(ctypes.byref(shape), _vp(int(x)), _vp(int(w))))
+    return int(_lib.tbg_conv2d_workspace_query(ctypes.byref(shape), int(x), int(w)))
 
 
 def conv2d_fwd(shape: Conv2dShape, alpha: float, x: int, w: int, beta: float, y: int, ldy: int, y_dtype,
@@ -304,9 +304,9 @@ def conv2d_fwd(shape: Conv2dShape, alpha: float, x: int, w: int, beta: float, y:
                stream: Optional[int] = None) -> None:
     """tbg_conv2d_fwd: Y <- alpha·conv2d(X, W) + beta·Y (X NHWC, W KRSC, Y (N·OH·OW) × K)."""
     cfg = ctypes.byref(config) if config is not None else None
-    _check(_lib.tbg_conv2d_fwd(ctypes.byref(shape), float(alpha), _vp(int(x)), _vp(int(w)), float(beta), _vp(int(y)),
-                               int(ldy), _enum(DTYPES, y_dtype), cfg, _vp(int(workspace)), int(workspace_bytes),
-                               _vp(stream or 0)))
+    _check(_lib.tbg_conv2d_fwd(ctypes.byref(shape), float(alpha), int(x), int(w), float(beta), int(y),
+                               int(ldy), _enum(DTYPES, y_dtype), cfg, int(workspace), int(workspace_bytes),
+                               stream or None))
 
 
 def conv2d_fwd_status(*args, **kwargs) -> int:
@@ -322,22 +322,22 @@ def gemm_workspace_bytes(M: int, N: int, K: int, lda: int, ldb: int, b_layout="k
 
 
 def gemm_workspace_query(M: int, N: int, K: int, ab_dtype, A: int, lda: int, B: int, ldb: int, b_layout="kn") -> int:
-    return int(_lib.tbg_gemm_workspace_query(M, N, K, _enum(DTYPES, ab_dtype), _vp(int(A)), lda, _vp(int(B)), ldb,
+    return int(_lib.tbg_gemm_workspace_query(M, N, K, _enum(DTYPES, ab_dtype), int(A), lda, int(B), ldb,
                                              _enum(B_LAYOUTS, b_layout)))
 
 
 def gemm(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C: int, ldc: int, c_dtype,
          workspace: int = 0, workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
     """tbg_gemm: C = A·B (bf16 in, fp32 accumulate, fp32 or bf16 out) on `stream`."""
-    _check(_lib.tbg_gemm(M, N, K, _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout), _vp(int(C)), ldc,
-                         _enum(DTYPES, c_dtype), _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+    _check(_lib.tbg_gemm(M, N, K, int(A), lda, int(B), ldb, _enum(B_LAYOUTS, b_layout), int(C), ldc,
+                         _enum(DTYPES, c_dtype), int(workspace), int(workspace_bytes), stream or None))
 
 
 def gemm_noalloc(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, b_layout, C: int, ldc: int, c_dtype,
                  stream: Optional[int] = None) -> None:
     """tbg_gemm_noalloc: tbg_gemm with any repack in the library's own scratch array (no workspace)."""
-    _check(_lib.tbg_gemm_noalloc(M, N, K, _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout), _vp(int(C)),
-                                 ldc, _enum(DTYPES, c_dtype), _vp(stream or 0)))
+    _check(_lib.tbg_gemm_noalloc(M, N, K, int(A), lda, int(B), ldb, _enum(B_LAYOUTS, b_layout), int(C),
+                                 ldc, _enum(DTYPES, c_dtype), stream or None))
 
 
 def gemm_noalloc_scratch_bytes() -> int:
@@ -347,9 +347,9 @@ def gemm_noalloc_scratch_bytes() -> int:
 def gemm_ex(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, beta: float, C: int,
             ldc: int, c_dtype, workspace: int = 0, workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
     """tbg_gemm_ex: C = alpha·A·B + beta·C on `stream`."""
-    _check(_lib.tbg_gemm_ex(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout),
-                            float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype), _vp(int(workspace)),
-                            int(workspace_bytes), _vp(stream or 0)))
+    _check(_lib.tbg_gemm_ex(M, N, K, float(alpha), int(A), lda, int(B), ldb, _enum(B_LAYOUTS, b_layout),
+                            float(beta), int(C), ldc, _enum(DTYPES, c_dtype), int(workspace),
+                            int(workspace_bytes), stream or None))
 
 
 def gemm_configured(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, beta: float,
@@ -357,9 +357,9 @@ def gemm_configured(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: i
                     workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
     """tbg_gemm_configured: C = alpha·A·B + beta·C with an explicit kernel configuration."""
     cfg = ctypes.byref(config) if config is not None else None
-    _check(_lib.tbg_gemm_configured(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb,
-                                    _enum(B_LAYOUTS, b_layout), float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype),
-                                    cfg, _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+    _check(_lib.tbg_gemm_configured(M, N, K, float(alpha), int(A), lda, int(B), ldb,
+                                    _enum(B_LAYOUTS, b_layout), float(beta), int(C), ldc, _enum(DTYPES, c_dtype),
+                                    cfg, int(workspace), int(workspace_bytes), stream or None))
 
 
 def gemm_typed(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, b_layout, ab_dtype,
@@ -367,9 +367,9 @@ def gemm_typed(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, l
                workspace_bytes: int = 0, stream: Optional[int] = None) -> None:
     """tbg_gemm_typed: C = alpha·A·B + beta·C with A, B of type ab_dtype ("bf16" or "f16")."""
     cfg = ctypes.byref(config) if config is not None else None
-    _check(_lib.tbg_gemm_typed(M, N, K, float(alpha), _vp(int(A)), lda, _vp(int(B)), ldb, _enum(B_LAYOUTS, b_layout),
-                               _enum(DTYPES, ab_dtype), float(beta), _vp(int(C)), ldc, _enum(DTYPES, c_dtype), cfg,
-                               _vp(int(workspace)), int(workspace_bytes), _vp(stream or 0)))
+    _check(_lib.tbg_gemm_typed(M, N, K, float(alpha), int(A), lda, int(B), ldb, _enum(B_LAYOUTS, b_layout),
+                               _enum(DTYPES, ab_dtype), float(beta), int(C), ldc, _enum(DTYPES, c_dtype), cfg,
+                               int(workspace), int(workspace_bytes), stream or None))
 
 
 def gemm_typed_status(*args, **kwargs) -> int:

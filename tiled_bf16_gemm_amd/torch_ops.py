@@ -27,6 +27,22 @@ def _require(t: torch.Tensor, name: str, device: Optional[torch.device] = None):
         raise ValueError(f"{name} is on {t.device}, A on {device}: every operand must be on one device")
 
 
+# tbg_gemm_workspace_query's answers.  The query reads the sizes, the operand type and layout, the
+# leading dimensions and only the operands' addresses modulo 16 (their 16-byte alignment), so
+# that is the key; the table is cleared when it grows past a few thousand shapes.
+_WS_NEED: dict = {}
+
+
+def _gemm_workspace_need(M, N, K, ab, a_ptr, lda, b_ptr, ldb, b_layout) -> int:
+    key = (M, N, K, ab, a_ptr & 15, lda, b_ptr & 15, ldb, b_layout)
+    need = _WS_NEED.get(key)
+    if need is None:
+        if len(_WS_NEED) > 4096:
+            _WS_NEED.clear()
+        need = _WS_NEED[key] = tbg.gemm_workspace_query(M, N, K, ab, a_ptr, lda, b_ptr, ldb, b_layout)
+    return need
+
+
 def _require_workspace(ws: Optional[torch.Tensor], device: torch.device):
     if ws is not None and (not ws.is_cuda or ws.device != device or not ws.is_contiguous()):
         raise ValueError(f"workspace must be a contiguous CUDA tensor on {device}")
@@ -63,23 +79,23 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
         raise ValueError(f"out must be a ({M}, {N}) {_TORCH_OF[out_dtype]} view (got {tuple(out.shape)} {out.dtype})")
     _require_workspace(workspace, A.device)
     lda, ldb, ldc = A.stride(0), B.stride(0), out.stride(0)
-    need = tbg.gemm_workspace_query(M, N, K, ab, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    a_ptr, b_ptr, c_ptr = A.data_ptr(), B.data_ptr(), out.data_ptr()
+    need = _gemm_workspace_need(M, N, K, ab, a_ptr, lda, b_ptr, ldb, b_layout)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if need and ws_bytes < need:
+        workspace, ws_bytes = torch.empty(need, dtype=torch.uint8, device=A.device), need
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    s = stream_handle(stream)
     if ab != "bf16":
-        tbg.gemm_typed(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, ab, beta, out.data_ptr(), ldc,
-                       out_dtype, config, ws_ptr, ws_bytes, stream_handle(stream))
+        tbg.gemm_typed(M, N, K, alpha, a_ptr, lda, b_ptr, ldb, b_layout, ab, beta, c_ptr, ldc, out_dtype, config,
+                       ws_ptr, ws_bytes, s)
     elif config is not None:
-        tbg.gemm_configured(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, beta, out.data_ptr(), ldc,
-                            out_dtype, config, ws_ptr, ws_bytes, stream_handle(stream))
+        tbg.gemm_configured(M, N, K, alpha, a_ptr, lda, b_ptr, ldb, b_layout, beta, c_ptr, ldc, out_dtype, config,
+                            ws_ptr, ws_bytes, s)
     elif alpha == 1.0 and beta == 0.0:
-        tbg.gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, out.data_ptr(), ldc, out_dtype,
-                 ws_ptr, ws_bytes, stream_handle(stream))
+        tbg.gemm(M, N, K, a_ptr, lda, b_ptr, ldb, b_layout, c_ptr, ldc, out_dtype, ws_ptr, ws_bytes, s)
     else:
-        tbg.gemm_ex(M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, b_layout, beta, out.data_ptr(), ldc,
-                    out_dtype, ws_ptr, ws_bytes, stream_handle(stream))
+        tbg.gemm_ex(M, N, K, alpha, a_ptr, lda, b_ptr, ldb, b_layout, beta, c_ptr, ldc, out_dtype, ws_ptr, ws_bytes, s)
     return out
 
 
