@@ -80,9 +80,7 @@ def gemm_operands(torch, w, ab="bf16"):
     type; the workload's bf16 values are converted to it (8-bit inputs take B stored N×K,
     transposed once here, outside any timed region)."""
     import workloads
-    import tiled_bf16_gemm_amd as tbg
     A, B = workloads.gemm_inputs(w)
-    lda, ldb, ldc = w.lds()
     A = A.cuda()
     B = B.cuda()
     Av = A[:, :w.K]
@@ -95,9 +93,16 @@ def gemm_operands(torch, w, ab="bf16"):
             Bv, b_layout = Bv.t().contiguous(), "nk"
         Bv = Bv.to(tdt)
     C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
-    need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    return Av, Bv, b_layout, C, ws
+    return Av, Bv, b_layout, C, gemm_workspace(torch, w, ab, Av, Bv, b_layout)
+
+
+def gemm_workspace(torch, w, ab, Av, Bv, b_layout):
+    """The product's workspace: twice the library's exact need, so that successive calls repack
+    into alternate halves (include/tbg.h, tbg_gemm)."""
+    import tiled_bf16_gemm_amd as tbg
+    need = tbg.gemm_workspace_query(w.M, w.N, w.K, ab, Av.data_ptr(), Av.stride(0), Bv.data_ptr(), Bv.stride(0),
+                                    b_layout)
+    return torch.empty(max(2 * need, 256), dtype=torch.uint8, device="cuda")
 
 
 def launch_stats(per):
@@ -214,15 +219,12 @@ def time_gemm_graph(torch, torch_ops, w, calls=20, replays=20, config=None):
     """GPU time per product with the host out of the way: `calls` products captured in one HIP
     graph (torch.cuda.graph), replayed `replays` times; returns ms per product."""
     import workloads
-    import tiled_bf16_gemm_amd as tbg
     A, B = workloads.gemm_inputs(w)
-    lda, ldb, ldc = w.lds()
     A, B = A.cuda(), B.cuda()
     Av = A[:, :w.K]
     Bv = B[:, :w.N] if w.b_layout == "kn" else B[:, :w.K]
     C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16, device="cuda")
-    need = max(tbg.gemm_workspace_bytes(w.M, w.N, w.K, lda, ldb, w.b_layout), 256)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = gemm_workspace(torch, w, "bf16", Av, Bv, w.b_layout)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):

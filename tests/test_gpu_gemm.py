@@ -261,6 +261,45 @@ def test_repack_many_rows(ops, orc):
 
 
 @gpu
+def test_repack_alternates_workspace_halves(ops, orc):
+    """With a workspace of twice the exact need, two successive calls put their repacked operands
+    in different halves (each half then holds A's rows at the 16-byte pitch, zero padded), and
+    the products are the same bits; with less than twice the need every call repacks at offset 0
+    and the rest of the workspace is not written."""
+    import tiled_bf16_gemm_amd as tbg
+    M, N, K = 300, 257, 777  # A rows of 1554 bytes, B (K×N) rows of 514 bytes: both repacked
+    A = workloads.matrix(M, K, K, ("normal", 1.0), 71)
+    B = workloads.matrix(K, N, N, ("normal", 1.0), 72)
+    ref = orc.gemm(workloads.bits(A), workloads.bits(B), M, N, K, K, N, "kn")
+    Ad, Bd = A.cuda(), B.cuda()
+    need = tbg.gemm_workspace_query(M, N, K, "bf16", Ad.data_ptr(), K, Bd.data_ptr(), N, "kn")
+    a_bytes = M * 784 * 2  # lda rounded up to 8 elements, 256-byte rounded below
+    assert need >= a_bytes and need % 256 == 0
+    packed_a = torch.zeros((M, 784), dtype=torch.bfloat16)
+    packed_a[:, :K] = A
+    packed_a = packed_a.view(torch.uint8).reshape(-1)
+    stream = torch.cuda.current_stream().cuda_stream
+    for size, halves in ((2 * need, 2), (2 * need - 256, 1)):
+        ws = torch.full((size,), 0xAB, dtype=torch.uint8, device="cuda")
+        outs = []
+        for call in range(2):
+            C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+            _say(f"workspace {size} bytes (need {need}): call {call}")
+            tbg.gemm(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N, "kn", C.data_ptr(), N, "f32", ws.data_ptr(), size,
+                     stream)
+            torch.cuda.synchronize()
+            outs.append(C.cpu().numpy())
+        _check(outs[0], ref, "first call")
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "the two calls differ"
+        host = ws.cpu()
+        for h in range(halves):
+            got = host[h * need: h * need + a_bytes]
+            assert torch.equal(got, packed_a), f"half {h} does not hold the repacked A"
+        if halves == 1:
+            assert int((host[need:] != 0xAB).sum()) == 0
+
+
+@gpu
 def test_log_reports_the_choice(ops):
     """TBG_LOG=1 makes each call print the configuration it launches; a child process (the
     variable is read once per process) runs the 1024³ product and the ragged 3001×2049×777 one."""

@@ -60,13 +60,17 @@ struct PackGrid {
   uint32_t cpr0, cpr1;  // destination chunks per row of each repack
 };
 
+// Index is the chunk number's type: 32-bit when every chunk number fits (a 32-bit division per
+// thread instead of the 64-bit division routine), 64-bit otherwise.
+template <typename Index>
 __global__ void __launch_bounds__(256) pack_rows_kernel(PackJob j0, PackJob j1, PackGrid g) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < g.total; t += stride) {
-    const bool second = t >= g.n0;
+  const Index stride = (Index)gridDim.x * blockDim.x;
+  const Index n0 = (Index)g.n0, total = (Index)g.total;
+  for (Index t = (Index)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const bool second = t >= n0;
     const PackJob& j = second ? j1 : j0;
-    const uint64_t i = second ? t - g.n0 : t;
-    const uint32_t cpr = second ? g.cpr1 : g.cpr0;
+    const Index i = second ? t - n0 : t;
+    const Index cpr = second ? g.cpr1 : g.cpr0;
     const int64_t r = (int64_t)(i / cpr), c = (int64_t)(i % cpr);
     *(uint4*)(j.dst + r * j.ld_dst + c * 16) = pack_chunk(j, r, c * 16);
   }
@@ -85,7 +89,13 @@ hipError_t launch_pack_jobs(const PackJob* jobs, int n, hipStream_t stream) {
   if (g.total == 0) return hipSuccess;
   const uint64_t blocks = (g.total + 255) / 256;
   const uint32_t grid = blocks < (1u << 20) ? (uint32_t)blocks : (1u << 20);
-  hipLaunchKernelGGL(pack_rows_kernel, dim3(grid), dim3(256), 0, stream, jobs[0], n > 1 ? jobs[1] : jobs[0], g);
+  // the grid-stride loop's last step must not wrap the 32-bit index either
+  if (g.total + (uint64_t)grid * 256 < (1ull << 32))
+    hipLaunchKernelGGL(pack_rows_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream, jobs[0],
+                       n > 1 ? jobs[1] : jobs[0], g);
+  else
+    hipLaunchKernelGGL(pack_rows_kernel<uint64_t>, dim3(grid), dim3(256), 0, stream, jobs[0],
+                       n > 1 ? jobs[1] : jobs[0], g);
   return hipGetLastError();
 }
 

@@ -83,7 +83,9 @@ def gemm(A: torch.Tensor, B: torch.Tensor, b_layout: str = "kn", out_dtype: str 
     need = _gemm_workspace_need(M, N, K, ab, a_ptr, lda, b_ptr, ldb, b_layout)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if need and ws_bytes < need:
-        workspace, ws_bytes = torch.empty(need, dtype=torch.uint8, device=A.device), need
+        # twice the need: successive calls alternate the halves their repacks land in
+        workspace = torch.empty(2 * need, dtype=torch.uint8, device=A.device)
+        ws_bytes = 2 * need
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     s = stream_handle(stream)
     if ab != "bf16":
@@ -173,7 +175,7 @@ def conv2d(x: torch.Tensor, w: torch.Tensor, pad=(0, 0, 0, 0), stride=(1, 1), di
     _require_workspace(workspace, x.device)
     need = tbg.conv2d_workspace_query(shp, x.data_ptr(), w.data_ptr())
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(2 * need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     tbg.conv2d_fwd(shp, alpha, x.data_ptr(), w.data_ptr(), beta, out.data_ptr(), out.stride(0), out_dtype, config,
