@@ -752,6 +752,133 @@ def sweep(torch, torch_ops, names, steps, warmup):
 SWEEP_CMD = "python -u bench.py --sweep c1,c2,c3,c4,c5,conv_b,c4@f16,c4@f8e4m3,c5@f8e4m3 > <out>/sweep.jsonl"
 
 
+# The barrier-ring configurations tbg_diag_gemm_timeline instruments: (name, BM, BN, stages).
+TIMELINE_CFGS = [("ring 128x128/2", 128, 128, 2), ("ring 256x128/3", 256, 128, 3), ("ring 256x256/2", 256, 256, 2),
+                 ("ring 64x64/3", 64, 64, 3)]
+
+
+def timeline_stats(tl, ktiles: int, tile_bytes: int) -> dict:
+    """Summary of one launch's per-workgroup timelines (gemm_ring.hpp, CLK 2: eight values per
+    workgroup: real-time counter at start, first tile landed, K loop done, stores done (100 MHz
+    ticks); shader-clock ticks over the whole; HW_ID; XCC_ID).  Times in µs from the first
+    workgroup's start.  The copy rate is per CU: the tile bytes every workgroup on a CU copied,
+    over the span of those workgroups' K loops, in bytes per shader clock, for the CUs holding the
+    most workgroups."""
+    import statistics
+    med = statistics.median
+    t0 = min(r[0] for r in tl)
+    us = lambda x: x / 100.0  # noqa: E731  (100 MHz ticks)
+    start = [us(r[0] - t0) for r in tl]
+    first = [us(r[1] - r[0]) for r in tl]
+    loop = [us(r[2] - r[1]) for r in tl]
+    epi = [us(r[3] - r[2]) for r in tl]
+    end = [us(r[3] - t0) for r in tl]
+    ghz = med([r[4] / (us(r[3] - r[0]) * 1e3) for r in tl if r[3] > r[0]])
+    # the CU: XCD, shader engine, shader array and CU fields of HW_ID
+    cus = {}
+    for r in tl:
+        cu = (r[6] & 0xF, (r[5] >> 13) & 7, (r[5] >> 12) & 1, (r[5] >> 8) & 0xF)
+        cus.setdefault(cu, []).append(r)
+    most = max(len(v) for v in cus.values())
+    rates = []
+    for v in cus.values():
+        if len(v) == most:
+            t = us(max(r[2] for r in v) - min(r[1] for r in v))
+            if t > 0:
+                rates.append(len(v) * ktiles * tile_bytes / (t * 1e3 * ghz))
+    return {"workgroups": len(tl), "cus": len(cus), "max_wg_per_cu": most,
+            "start_us": {"median": round(med(start), 2), "max": round(max(start), 2)},
+            "first_tile_us": round(med(first), 2), "k_loop_us": round(med(loop), 2),
+            "per_k_tile_us": round(med(loop) / ktiles, 3), "epilogue_us": round(med(epi), 2),
+            "end_us": {"min": round(min(end), 2), "median": round(med(end), 2), "max": round(max(end), 2)},
+            "clock_ghz": round(ghz, 3), "copy_bytes_per_clk_per_cu": round(med(rates), 1) if rates else None}
+
+
+def timeline(torch, names=("c2", "c3")) -> None:
+    """Per-workgroup timelines of the barrier ring on the launch-bound products, one JSON line per
+    (workload, configuration): tbg_diag_gemm_timeline on the operands in the form the product
+    runs on (rows padded with zeros to a multiple of 8 elements, K rounded up to 8: what the
+    library's repack produces), 30 untimed launches, then 20 launches timed with HIP events and
+    the timelines of the last."""
+    import ctypes
+    import statistics
+    import workloads
+    lib = diag_lib()
+    ci, ll, vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_void_p
+    lib.tbg_diag_gemm_timeline.restype = ci
+    lib.tbg_diag_gemm_timeline.argtypes = [ci, vp, vp, vp, ci, ci, ci, ll, ll, ll, ci, vp, ctypes.POINTER(ci), vp]
+    for name in names:
+        w = workloads.GEMMS[name]
+        assert w.b_layout == "kn"
+        A, B = workloads.gemm_inputs(w)
+        r8 = lambda x: (x + 7) // 8 * 8  # noqa: E731
+        K8, N8 = r8(w.K), r8(w.N)
+        Ap = torch.zeros((w.M, K8), dtype=torch.bfloat16)
+        Ap[:, :w.K] = A[:, :w.K]
+        Bp = torch.zeros((K8, N8), dtype=torch.bfloat16)
+        Bp[:w.K, :w.N] = B[:, :w.N]
+        Ap, Bp = Ap.cuda(), Bp.cuda()
+        out_bf16 = 1 if w.out_dtype == "bf16" else 0
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        for cfg, (cname, bm, bn, stages) in enumerate(TIMELINE_CFGS):
+            nwg = ((w.M + bm - 1) // bm) * ((w.N + bn - 1) // bn)
+            tl = torch.zeros(8 * nwg, dtype=torch.int64, device="cuda")
+            got = ci(0)
+
+            def launch():
+                st = lib.tbg_diag_gemm_timeline(cfg, Ap.data_ptr(), Bp.data_ptr(), C.data_ptr(), w.M, w.N, K8, K8, N8,
+                                                w.N, out_bf16, tl.data_ptr(), ctypes.byref(got), stream)
+                if st != 0:
+                    raise RuntimeError(f"tbg_diag_gemm_timeline: hipError {st}")
+            for _ in range(30):
+                launch()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for a, b in ev:
+                a.record()
+                launch()
+                b.record()
+            torch.cuda.synchronize()
+            assert got.value == nwg
+            stats = timeline_stats(tl.view(-1, 8).cpu().tolist(), (K8 + 63) // 64, (bm + bn) * 64 * 2)
+            line = {"timeline": name, "M": w.M, "N": w.N, "K": w.K, "out": w.out_dtype, "config": cname,
+                    "launch_us": round(1e3 * statistics.median(a.elapsed_time(b) for a, b in ev), 2)}
+            line.update(stats)
+            print(json.dumps(line), flush=True)
+
+
+def write_timeline_profile(jsonl: str, out_dir: str) -> None:
+    """profiles/gemm_small_timeline.md from the JSON lines of one `--timeline` run."""
+    rows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    lines = ["# Per-workgroup timelines of the barrier ring on the launch-bound products", "",
+             "Each workgroup of the library's barrier-ring kernel, built with timeline recording "
+             "(`tiled_bf16_gemm_amd/csrc/gemm_ring.hpp`, CLK 2; `tiled_bf16_gemm_amd/diag/mfma_rate.hip`, "
+             "`tbg_diag_gemm_timeline`), records the 100 MHz real-time counter at its start, once its first K "
+             "tile has landed in LDS, after its K loop and once its stores have completed, the shader clock "
+             "over the whole, and the CU it ran on.  Operands in the form the product runs on (the repack's "
+             "zero-padded rows).  Medians over the workgroups of one launch, after 30 untimed launches; "
+             "\"launch\" is the median of 20 launches timed with HIP events on the launch stream (it includes the "
+             "dispatch of the grid).  Copy rate: the K tiles' bytes copied by all workgroups of a CU over the "
+             "span of their K loops, per shader clock, for the CUs holding the most workgroups.", "",
+             "Command (repository root on the GPU box; <out> an output folder), then "
+             "`python bench.py --timeline-md <out>/timeline.jsonl`:", "", "```",
+             "python -u bench.py --timeline > <out>/timeline.jsonl", "```", ""]
+    for name in dict.fromkeys(r["timeline"] for r in rows):
+        rs = [r for r in rows if r["timeline"] == name]
+        r0 = rs[0]
+        lines += [f"## {name}: {r0['M']}×{r0['N']}×{r0['K']} (B K×N, {r0['out']} out)", "",
+                  "| configuration | workgroups | CUs | max per CU | launch µs | last store done µs | first tile µs | "
+                  "K loop µs | per K tile µs | epilogue µs | clock GHz | copy B/clk per CU |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        for r in rs:
+            lines.append(f"| {r['config']} | {r['workgroups']} | {r['cus']} | {r['max_wg_per_cu']} | {r['launch_us']} | "
+                         f"{r['end_us']['max']} | {r['first_tile_us']} | {r['k_loop_us']} | {r['per_k_tile_us']} | "
+                         f"{r['epilogue_us']} | {r['clock_ghz']} | {r['copy_bytes_per_clk_per_cu']} |")
+        lines.append("")
+    with open(os.path.join(out_dir, "gemm_small_timeline.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 def write_sweep_profiles(jsonl: str, out_dir: str) -> None:
     """profiles/gemm_pipeline_sweep.md, gemm_f16_f8_sweep.md and conv_pipeline_sweep.md from the
     JSON lines of one `--sweep` run: one table per workload, the fastest configuration marked
@@ -880,6 +1007,11 @@ def main():
                          "line is also written to profiles/bench_8192_line.json; runs on any host, no GPU needed")
     ap.add_argument("--bench-kernel-us", type=float, default=None,
                     help="with --summarize: the bench line's HIP-event kernel average, quoted beside the trace")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup timelines of the barrier ring on c2 and c3 (tbg_diag_gemm_timeline); one "
+                         "JSON line per configuration instead of the bench line")
+    ap.add_argument("--timeline-md", default="", metavar="JSONL",
+                    help="write profiles/gemm_small_timeline.md from the JSON lines of a --timeline run (no GPU)")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workloads (c1..c5, conv_b; a GEMM name may carry an input type, e.g. "
                          "c4@f16, c4@f8e4m3): time every built pipeline/tile/stages configuration on each and print "
@@ -893,6 +1025,9 @@ def main():
 
     if args.sweep_md:
         write_sweep_profiles(args.sweep_md, os.path.join(ROOT, "profiles"))
+        return
+    if args.timeline_md:
+        write_timeline_profile(args.timeline_md, os.path.join(ROOT, "profiles"))
         return
 
     if args.summarize:
@@ -931,6 +1066,9 @@ def main():
         return
     if args.sweep:
         sweep(torch, torch_ops, args.sweep.split(","), 20, 5)
+        return
+    if args.timeline:
+        timeline(torch)
         return
     if args.only_copies:
         for name in ("c1_copy", "c3_copy", "c4_a_boxes"):

@@ -112,3 +112,35 @@ def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path):
     assert "| timed 20 | 700.00 | 700.00 |" in text
     assert "| all 50 |" in text and "kernel_ms 0.7" in text
     assert abs(t["gemm_trace_avg_us"] - 700.0) < 1e-9
+
+
+def _hw_id(se, sh, cu):
+    return (se << 13) | (sh << 12) | (cu << 8)
+
+
+def test_timeline_stats_and_profile(tmp_path):
+    """timeline_stats on hand-made timelines: three workgroups, two on one CU (XCD 1, SE 2, SA 1,
+    CU 5) and one on another; times in 100 MHz ticks, 2 GHz shader clock."""
+    # start, first tile, loop done, stores done, shader ticks, HW_ID, XCC_ID, 0
+    tl = [[1000, 1100, 1500, 1520, 2 * 520 * 10, _hw_id(2, 1, 5), 1, 0],
+          [1010, 1130, 1530, 1560, 2 * 550 * 10, _hw_id(2, 1, 5), 1, 0],
+          [1005, 1105, 1405, 1425, 2 * 420 * 10, _hw_id(0, 0, 3), 4, 0]]
+    s = bench.timeline_stats(tl, ktiles=4, tile_bytes=1000)
+    assert s["workgroups"] == 3 and s["cus"] == 2 and s["max_wg_per_cu"] == 2
+    assert s["start_us"] == {"median": 0.05, "max": 0.1}
+    assert s["first_tile_us"] == 1.0  # median of 1.0, 1.2, 1.0 µs
+    assert s["k_loop_us"] == 4.0 and s["per_k_tile_us"] == 1.0
+    assert s["epilogue_us"] == 0.2
+    assert s["end_us"] == {"min": 4.25, "median": 5.2, "max": 5.6}
+    assert s["clock_ghz"] == 2.0
+    # the two workgroups on CU 5 copied 2 * 4 * 1000 bytes between 11.0 and 15.3 µs at 2 GHz
+    assert s["copy_bytes_per_clk_per_cu"] == round(8000 / (4.3 * 1e3 * 2.0), 1)
+    line = {"timeline": "c2", "M": 1024, "N": 1024, "K": 1024, "out": "bf16", "config": "ring 64x64/3",
+            "launch_us": 6.1}
+    line.update(s)
+    path = tmp_path / "timeline.jsonl"
+    path.write_text(json.dumps(line) + "\n")
+    bench.write_timeline_profile(str(path), str(tmp_path))
+    md = (tmp_path / "gemm_small_timeline.md").read_text()
+    assert "## c2: 1024×1024×1024 (B K×N, bf16 out)" in md
+    assert "| ring 64x64/3 | 3 | 2 | 2 | 6.1 | 5.6 | 1.0 | 4.0 | 1.0 | 0.2 | 2.0 | 0.9 |" in md

@@ -32,10 +32,14 @@ struct RingCfg {
 
 // CLK 1: a measurement instance (never launched by the library) that records, per workgroup, the
 // real-time and shader-clock counters' advance from its start to the end of its stores.
+// CLK 2: a measurement instance that records a timeline per workgroup (8 values): the 100 MHz
+// real-time counter at its start, once its first tile has landed, after its K loop and once its
+// stores have completed (wave 0's); the shader-clock advance over the whole; the hardware ids of
+// the wave (HW_ID) and of the XCD (XCC_ID) it ran on.
 template <int BM, int BN, int S, int IN, int BL, int OUT, int SCALED, int CLK = 0>
 __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gemm_ring_kernel(GemmParams p) {
   using T = TileCfg<BM, BN, IN>;
-  uint64_t clk_r0 = 0, clk_m0 = 0;
+  uint64_t clk_r0 = 0, clk_m0 = 0, clk_first = 0, clk_loop = 0;
   if (CLK) {
     clk_r0 = __builtin_amdgcn_s_memrealtime();
     clk_m0 = __builtin_amdgcn_s_memtime();
@@ -113,6 +117,7 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
       for (int j = 0; j < T::Atoms; ++j) copy_atom<T, true, BL == 1>(tc, la, lb, j);
     }
     stage_barrier<T::Atoms*(S - 1)>();  // tile 0 landed; tiles 1..S-1 may be in flight
+    if (CLK == 2) clk_first = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
     for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
     // One K tile on stage CUR (a compile-time constant, so every LDS address below is a fixed
@@ -147,14 +152,32 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, S>::MinBlocks)) gem
   // Wait states after the last product (drain_acc), then the ring is drained before it becomes
   // the park: the last iterations' masked copies still write zeros into stages, and the other
   // waves may still read their fragments.
+  if (CLK == 2) clk_loop = __builtin_amdgcn_s_memrealtime();
   drain_acc<T>(acc);
   stage_barrier<0>();
   store_tile<T, OUT, SCALED>(acc, smem + wave * (T::RingBytes / 4), p, m0 + wm * T::TM, n0 + wn * T::TN, lane);
-  if (CLK) {
+  if (CLK == 1) {
     const uint64_t r1 = __builtin_amdgcn_s_memrealtime(), m1 = __builtin_amdgcn_s_memtime();
     if (threadIdx.x == 0) {
       p.clock[2 * (uint64_t)blockIdx.x] = r1 - clk_r0;
       p.clock[2 * (uint64_t)blockIdx.x + 1] = m1 - clk_m0;
+    }
+  } else if (CLK == 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have completed
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime(), m1 = __builtin_amdgcn_s_memtime();
+    uint32_t hw_id, xcc_id;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw_id));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc_id));
+    if (threadIdx.x == 0) {
+      uint64_t* o = p.clock + 8 * (uint64_t)blockIdx.x;
+      o[0] = clk_r0;
+      o[1] = clk_first;
+      o[2] = clk_loop;
+      o[3] = r1;
+      o[4] = m1 - clk_m0;
+      o[5] = hw_id;
+      o[6] = xcc_id;
+      o[7] = 0;
     }
   }
 }

@@ -120,3 +120,66 @@ extern "C" int tbg_diag_gemm_clock(const void* A, const void* B, void* C, int M,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
+
+// Per-workgroup timelines of the library's barrier ring (gemm_ring.hpp, CLK 2) on a bf16 product
+// with B stored K×N, for the configurations the library picks on small and ragged products:
+// cfg 0: 128x128, 2 stages; 1: 256x128, 3 stages; 2: 256x256, 2 stages; 3: 64x64, 3 stages.
+// out_bf16 selects the output type (else fp32).  Each workgroup writes 8 uint64 into
+// tl[8 * workgroup] (see gemm_ring.hpp).  Operands must need no repack (16-byte aligned bases,
+// lda, ldb and K multiples of 8); C's base and row pitch multiples of 4 bytes.  Returns the
+// launch's hipError_t as an int; the number of workgroups through nwg_out.
+template <int BM, int BN, int S>
+static int diag_timeline(const void* A, const void* B, void* C, int M, int N, int K, long long lda, long long ldb,
+                         long long ldc, int out_bf16, void* tl, int* nwg_out, hipStream_t stream) {
+  tbg::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.kchunks = K / 8;
+  p.tiles_m = (M + BM - 1) / BM;
+  p.tiles_n = (N + BN - 1) / BN;
+  p.group_m = 4;
+  p.vec_store = 1;
+  p.alpha = 1.f;
+  p.clock = (uint64_t*)tl;
+  p.da.elsize = p.db.elsize = 2;
+  p.da.base = (uint64_t)(uintptr_t)A;
+  p.da.dim[0] = (uint64_t)K;
+  p.da.dim[1] = (uint64_t)M;
+  p.da.stride[1] = (uint64_t)lda * 2;
+  p.db.base = (uint64_t)(uintptr_t)B;
+  p.db.dim[0] = (uint64_t)N;
+  p.db.dim[1] = (uint64_t)K;
+  p.db.stride[1] = (uint64_t)ldb * 2;
+  const int nwg = p.tiles_m * p.tiles_n;
+  if (nwg_out) *nwg_out = nwg;
+  if (out_bf16)
+    hipLaunchKernelGGL((tbg::gemm_ring_kernel<BM, BN, S, 0, 0, 1, 0, 2>), dim3(nwg), dim3(tbg::kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((tbg::gemm_ring_kernel<BM, BN, S, 0, 0, 0, 0, 2>), dim3(nwg), dim3(tbg::kThreads), 0, stream, p);
+  return (int)hipGetLastError();
+}
+
+extern "C" int tbg_diag_gemm_timeline(int cfg, const void* A, const void* B, void* C, int M, int N, int K,
+                                      long long lda, long long ldb, long long ldc, int out_bf16, void* tl,
+                                      int* nwg_out, void* stream) {
+  const int es = out_bf16 ? 2 : 4;
+  if (!A || !B || !C || !tl || M <= 0 || N <= 0 || K <= 0 || lda % 8 || ldb % 8 || K % 8 || lda < K || ldb < N ||
+      ldc < N || ((uintptr_t)A | (uintptr_t)B) % 16 || ((uintptr_t)C) % 4 || (ldc * es) % 4)
+    return (int)hipErrorInvalidValue;
+  const hipStream_t s = (hipStream_t)stream;
+  switch (cfg) {
+    case 0: return diag_timeline<128, 128, 2>(A, B, C, M, N, K, lda, ldb, ldc, out_bf16, tl, nwg_out, s);
+    case 1: return diag_timeline<256, 128, 3>(A, B, C, M, N, K, lda, ldb, ldc, out_bf16, tl, nwg_out, s);
+    case 2: return diag_timeline<256, 256, 2>(A, B, C, M, N, K, lda, ldb, ldc, out_bf16, tl, nwg_out, s);
+    case 3: return diag_timeline<64, 64, 3>(A, B, C, M, N, K, lda, ldb, ldc, out_bf16, tl, nwg_out, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
