@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <string>
 
+#include "fast_div.hpp"
 #include "launch.hpp"
 
 namespace tbg {
@@ -17,62 +18,72 @@ namespace tbg {
 // into a contiguous area before use; 16-byte alignment of the leading dimension, section "In
 // pratica"): copy `rows` rows of `row_bytes` bytes into a buffer of pitch `ld_dst` bytes (a
 // multiple of 16), zero-filling bytes row_bytes..ld_dst-1.  One thread per 16-byte chunk of the
-// destination, numbered flat over both operands' chunks (no idle threads at ragged row ends).
-// The chunk's 16 source bytes may start at any byte: the thread loads the two aligned 16-byte
-// blocks that hold them (consecutive lanes load consecutive blocks, so every load instruction is
-// one contiguous run) and funnel-shifts them into place.  The second block is clamped to the
-// aligned block that holds the row's last byte, and the bytes past the row are zeroed, so no load
-// leaves the 16-byte blocks the row touches (those never cross a page).
-__device__ __forceinline__ uint4 pack_chunk(const PackJob& j, int64_t r, int64_t b0) {
-  const int64_t valid = j.row_bytes - b0;  // bytes of this chunk inside the row
-  if (valid <= 0) return make_uint4(0, 0, 0, 0);
-  const uint8_t* srow = j.src + r * j.ld_src;
-  const uintptr_t a = (uintptr_t)(srow + b0);
-  const uintptr_t base = a & ~(uintptr_t)15;
-  const uintptr_t last = (uintptr_t)(srow + j.row_bytes - 1) & ~(uintptr_t)15;
-  const uint4 q0 = *(const uint4*)base;
-  const uint4 q1 = *(const uint4*)(base + 16 <= last ? base + 16 : last);
-  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-  const uint32_t d = (uint32_t)(a & 15) >> 2, sh = (uint32_t)(a & 3);
-  uint32_t o[4];
+// destination.  The chunk's 16 source bytes may start at any byte: the thread loads the two
+// aligned 16-byte blocks that hold them (consecutive lanes load consecutive blocks, so every load
+// instruction is one contiguous run) and funnel-shifts them into place.  The second block is
+// clamped to the aligned block that holds the row's last byte, and the bytes past the row are
+// zeroed, so no load leaves the 16-byte blocks the row touches (those never cross a page).
+// Offsets inside a row are 32-bit (a row is below 2^24 bytes; the callers check the pitches).
+__device__ __forceinline__ uint4 pack_chunk(const PackJob& j, uint64_t r, uint32_t b0) {
+  const uint32_t rb = (uint32_t)j.row_bytes;
+  if (b0 >= rb) return make_uint4(0, 0, 0, 0);
+  const uint8_t* srow = j.src + r * (uint64_t)j.ld_src;
+  const uint32_t mis = (uint32_t)((uintptr_t)srow & 15);  // the row's offset from a 16-byte boundary
+  const uint8_t* blocks = srow - mis;                      // the aligned block holding its first byte
+  const uint32_t last = ((mis + rb - 1) >> 4) << 4;        // the block holding its last byte
+  const uint4 q0 = *(const uint4*)(blocks + b0);
+  const uint4 q1 = *(const uint4*)(blocks + (b0 + 16 <= last ? b0 + 16 : last));
+  // the 32 loaded bytes shifted down by `mis`: by 8 bytes, by 4, then alignbyte by the rest
+  // (named registers: an indexed array here is lowered through memory)
+  const bool s8 = mis & 8, s4 = mis & 4;
+  const uint32_t sh = mis & 3;
+  const uint32_t y0 = s8 ? q0.z : q0.x, y1 = s8 ? q0.w : q0.y, y2 = s8 ? q1.x : q0.z, y3 = s8 ? q1.y : q0.w,
+                 y4 = s8 ? q1.z : q1.x, y5 = s8 ? q1.w : q1.y;
+  const uint32_t z0 = s4 ? y1 : y0, z1 = s4 ? y2 : y1, z2 = s4 ? y3 : y2, z3 = s4 ? y4 : y3, z4 = s4 ? y5 : y4;
+  uint32_t o[4] = {__builtin_amdgcn_alignbyte(z1, z0, sh), __builtin_amdgcn_alignbyte(z2, z1, sh),
+                   __builtin_amdgcn_alignbyte(z3, z2, sh), __builtin_amdgcn_alignbyte(z4, z3, sh)};
+  const uint32_t valid = rb - b0;  // bytes of this chunk inside the row
+  if (valid < 16) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // dwords d + k and d + k + 1 of the 32 loaded bytes, selected without indexing registers
-    uint32_t lo = w[k], hi = w[k + 1];
-#pragma unroll
-    for (int s = 1; s < 4; ++s) {
-      if (d == (uint32_t)s) {
-        lo = w[k + s];
-        hi = w[k + s + 1 < 8 ? k + s + 1 : 7];
-      }
-    }
-    o[k] = __builtin_amdgcn_alignbyte(hi, lo, sh);
-    const int64_t keep = valid - 4 * k;  // bytes of this dword inside the row
-    if (keep < 4) o[k] &= keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
+    for (int k = 0; k < 4; ++k)
+      if (valid < 4u * k + 4) o[k] &= valid <= 4u * k ? 0u : ((1u << (8 * (valid - 4 * k))) - 1u);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Chunks numbered flat: chunks below `n0` belong to j0 (row-major over its rows × cpr0 chunks),
-// the rest to j1.  Workgroups step through the chunks by the grid size.
+// Two repacks in one launch.  Workgroups 0..blocks0-1 take j0's chunks, the rest j1's, so the job
+// is uniform over a workgroup (its fields stay in scalar registers); chunks are numbered
+// row-major over a job's rows × chunks-per-row.
 struct PackGrid {
-  uint64_t n0, total;  // chunks of the first repack; chunks of both
-  uint32_t cpr0, cpr1;  // destination chunks per row of each repack
+  uint32_t chunks0, chunks1;  // chunks of each repack
+  uint32_t cpr0, cpr1;        // destination chunks per row of each repack
+  FastDiv div0, div1;         // division by cpr0, cpr1
 };
 
-// Index is the chunk number's type: 32-bit when every chunk number fits (a 32-bit division per
-// thread instead of the 64-bit division routine), 64-bit otherwise.
-template <typename Index>
 __global__ void __launch_bounds__(256) pack_rows_kernel(PackJob j0, PackJob j1, PackGrid g) {
-  const Index stride = (Index)gridDim.x * blockDim.x;
-  const Index n0 = (Index)g.n0, total = (Index)g.total;
-  for (Index t = (Index)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+  const uint32_t blocks0 = (g.chunks0 + 255) / 256;
+  const bool second = blockIdx.x >= blocks0;
+  const PackJob& j = second ? j1 : j0;
+  const uint32_t i = (blockIdx.x - (second ? blocks0 : 0u)) * 256u + threadIdx.x;
+  if (i >= (second ? g.chunks1 : g.chunks0)) return;
+  const uint32_t r = fast_div(i, second ? g.div1 : g.div0);
+  const uint32_t c = i - r * (second ? g.cpr1 : g.cpr0);
+  *(uint4*)(j.dst + (uint64_t)r * (uint64_t)j.ld_dst + c * 16u) = pack_chunk(j, r, c * 16u);
+}
+
+// The same for repacks of 2^32 - 256 chunks (64 GiB) or more: 64-bit chunk numbers, numbered flat
+// over both repacks, the grid stepping through them.
+__global__ void __launch_bounds__(256) pack_rows_wide_kernel(PackJob j0, PackJob j1, uint64_t n0, uint64_t total,
+                                                             uint32_t cpr0, uint32_t cpr1) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
     const bool second = t >= n0;
     const PackJob& j = second ? j1 : j0;
-    const Index i = second ? t - n0 : t;
-    const Index cpr = second ? g.cpr1 : g.cpr0;
-    const int64_t r = (int64_t)(i / cpr), c = (int64_t)(i % cpr);
-    *(uint4*)(j.dst + r * j.ld_dst + c * 16) = pack_chunk(j, r, c * 16);
+    const uint64_t i = second ? t - n0 : t;
+    const uint32_t cpr = second ? cpr1 : cpr0;
+    const uint64_t r = i / cpr;
+    const uint32_t c = (uint32_t)(i % cpr);
+    *(uint4*)(j.dst + r * (uint64_t)j.ld_dst + c * 16u) = pack_chunk(j, r, c * 16u);
   }
 }
 
@@ -81,21 +92,24 @@ hipError_t launch_pack_jobs(const PackJob* jobs, int n, hipStream_t stream) {
   uint64_t chunks[2] = {0, 0};
   uint32_t cpr[2] = {1, 1};
   for (int i = 0; i < n; ++i) {
-    if (jobs[i].ld_dst / 16 >= (1ll << 32)) return hipErrorInvalidValue;
+    if (jobs[i].ld_dst >= (1ll << 31) || jobs[i].row_bytes > jobs[i].ld_dst) return hipErrorInvalidValue;
     cpr[i] = (uint32_t)(jobs[i].ld_dst / 16);
     chunks[i] = (uint64_t)cpr[i] * (uint64_t)jobs[i].rows;
   }
-  const PackGrid g{chunks[0], chunks[0] + chunks[1], cpr[0], cpr[1]};
-  if (g.total == 0) return hipSuccess;
-  const uint64_t blocks = (g.total + 255) / 256;
-  const uint32_t grid = blocks < (1u << 20) ? (uint32_t)blocks : (1u << 20);
-  // the grid-stride loop's last step must not wrap the 32-bit index either
-  if (g.total + (uint64_t)grid * 256 < (1ull << 32))
-    hipLaunchKernelGGL(pack_rows_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream, jobs[0],
-                       n > 1 ? jobs[1] : jobs[0], g);
-  else
-    hipLaunchKernelGGL(pack_rows_kernel<uint64_t>, dim3(grid), dim3(256), 0, stream, jobs[0],
-                       n > 1 ? jobs[1] : jobs[0], g);
+  const PackJob& j1 = n > 1 ? jobs[1] : jobs[0];
+  if (chunks[0] + chunks[1] == 0) return hipSuccess;
+  const uint64_t limit = (1ull << 32) - 256;
+  if (chunks[0] < limit && chunks[1] < limit) {
+    const PackGrid g{(uint32_t)chunks[0], (uint32_t)chunks[1], cpr[0], cpr[1], make_fast_div(cpr[0]),
+                     make_fast_div(cpr[1])};
+    const uint64_t blocks = (chunks[0] + 255) / 256 + (chunks[1] + 255) / 256;
+    hipLaunchKernelGGL(pack_rows_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, jobs[0], j1, g);
+  } else {
+    const uint64_t total = chunks[0] + chunks[1], blocks = (total + 255) / 256;
+    const uint32_t grid = blocks < (1u << 20) ? (uint32_t)blocks : (1u << 20);
+    hipLaunchKernelGGL(pack_rows_wide_kernel, dim3(grid), dim3(256), 0, stream, jobs[0], j1, chunks[0], total, cpr[0],
+                       cpr[1]);
+  }
   return hipGetLastError();
 }
 
