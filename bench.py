@@ -105,6 +105,24 @@ def gemm_workspace(torch, w, ab, Av, Bv, b_layout):
     return torch.empty(max(2 * need, 256), dtype=torch.uint8, device="cuda")
 
 
+def time_gemm_cold(torch, torch_ops, w, operands, calls: int = 20, flush_mib: int = 512) -> float:
+    """Median ms of `calls` products each started on cold caches: before each one, a 512 MiB device
+    buffer is overwritten (more than the 256 MB Infinity Cache and every XCD's L2 together), and
+    the HIP events on the launch stream bracket the product only."""
+    import statistics
+    Av, Bv, b_layout, C, ws = operands
+    flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        flush.fill_(1)
+        a.record()
+        torch_ops.gemm(Av, Bv, b_layout, w.out_dtype, out=C, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    del flush
+    return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+
 def launch_stats(per):
     """min / median / max of per-launch times (ms)."""
     import statistics
@@ -405,7 +423,6 @@ def cpu_baseline(w, target_s: float = 15.0):
     lda, ldb, _ = w.lds()
     threads = orc.max_threads()
     rows = 8
-    t = orc.gemm  # noqa
     t0 = time.perf_counter()
     orc.gemm(Ab, Bb, w.M, w.N, w.K, lda, ldb, w.b_layout, rows=(0, rows), threads=threads)
     dt = time.perf_counter() - t0
@@ -423,7 +440,20 @@ def cpu_baseline(w, target_s: float = 15.0):
         "sample": f"rows 0..{rows2 - 1} of the {w.M}x{w.N}x{w.K} product ({rows2}x{w.N}x{w.K} MACs, "
                   f"binary64 accumulation), {dt:.1f} s on {threads} host threads",
         "seconds": round(dt, 2),
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "" where it cannot be read."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 # The library's kernels for the two large workloads (bf16 in, bf16 out, 256×256 ring, 2 stages):
@@ -1089,6 +1119,7 @@ def main():
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     achieved = w.flops / (ms_kernel * 1e-3) / 1e12
     clock = None if args.no_clock else gemm_clock(torch, ops[0], ops[1], ops[3])
+    cold_ms = None if args.no_configs else time_gemm_cold(torch, torch_ops, w, ops)
     del ops
     torch.cuda.empty_cache()
 
@@ -1108,7 +1139,9 @@ def main():
             torch.cuda.empty_cache()
         per_config["c4"] = {"M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "out": w.out_dtype,
                             "ms": round(ms_step, 5), "tflops": round(tflops, 2),
-                            "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
+                            "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                            # each product after a 512 MiB overwrite: operands from HBM, not the caches
+                            "cold_ms": round(cold_ms, 5), "cold_tflops": round(w.flops / (cold_ms * 1e-3) / 1e12, 2)}
         for ab in ("f16", "f8e4m3"):
             s_, _, _ = time_gemm(torch, torch_ops, w, 50, 50, ab=ab, settle_s=args.settle / 3)
             tf = w.flops / (s_ * 1e-3) / 1e12
