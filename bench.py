@@ -105,7 +105,10 @@ def gemm_workspace(torch, w, ab, Av, Bv, b_layout):
     return torch.empty(max(2 * need, 256), dtype=torch.uint8, device="cuda")
 
 
-def time_gemm_cold(torch, torch_ops, w, operands, calls: int = 20, flush_mib: int = 512) -> float:
+COLD_CALLS = 20
+
+
+def time_gemm_cold(torch, torch_ops, w, operands, calls: int = COLD_CALLS, flush_mib: int = 512) -> float:
     """Median ms of `calls` products each started on cold caches: before each one, a 512 MiB device
     buffer is overwritten (more than the 256 MB Infinity Cache and every XCD's L2 together), and
     the HIP events on the launch stream bracket the product only."""
@@ -531,13 +534,17 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
     timed_avg = None
     if line and disp:
         steps = int(line.get("steps", 20))
-        timed = disp[-steps:]
+        # after the timed steps the same kernel runs the cold-cache calls (per_config c4)
+        cold = int(line.get("per_config", {}).get("c4", {}).get("cold_calls", 0))
+        timed = disp[len(disp) - cold - steps:len(disp) - cold]
         timed_avg = statistics.mean(timed)
         k_ms = line["roofline"]["kernel_ms"]
         flops = line["roofline"]["flops_per_launch"]
-        lines += ["", f"The 8192³ kernel's {len(disp)} dispatches are the bench's settle regions, its warm-up and its "
-                      f"{steps} timed steps, in that order; the last {steps} are the timed steps.", "",
-                  "| dispatches | average us | median us | TFLOP/s at the average | frac of 2516.6 |",
+        order = (f"its {steps} timed steps and {cold} calls on cold caches, in that order; the {steps} before the last "
+                 f"{cold} are the timed steps" if cold else
+                 f"its {steps} timed steps, in that order; the last {steps} are the timed steps")
+        lines += ["", f"The 8192³ kernel's {len(disp)} dispatches are the bench's settle regions, its warm-up, {order}.",
+                  "", "| dispatches | average us | median us | TFLOP/s at the average | frac of 2516.6 |",
                   "|---|---|---|---|---|",
                   f"| all {len(disp)} | {statistics.mean(disp):.2f} | {statistics.median(disp):.2f} | "
                   f"{flops / (statistics.mean(disp) * 1e-6) / 1e12:.1f} | "
@@ -1141,7 +1148,8 @@ def main():
                             "ms": round(ms_step, 5), "tflops": round(tflops, 2),
                             "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
                             # each product after a 512 MiB overwrite: operands from HBM, not the caches
-                            "cold_ms": round(cold_ms, 5), "cold_tflops": round(w.flops / (cold_ms * 1e-3) / 1e12, 2)}
+                            "cold_ms": round(cold_ms, 5), "cold_tflops": round(w.flops / (cold_ms * 1e-3) / 1e12, 2),
+                            "cold_calls": COLD_CALLS}
         for ab in ("f16", "f8e4m3"):
             s_, _, _ = time_gemm(torch, torch_ops, w, 50, 50, ab=ab, settle_s=args.settle / 3)
             tf = w.flops / (s_ * 1e-3) / 1e12

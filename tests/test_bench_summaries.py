@@ -7,6 +7,8 @@ import sqlite3
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -80,16 +82,19 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path):
-    """The traced bench run's last `steps` dispatches of the 8192^3 kernel are its timed steps: the
-    summary gives their average next to the bench line's own HIP-event figure."""
+@pytest.mark.parametrize("cold", [0, 20])
+def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path, cold):
+    """The traced bench run's timed steps are the `steps` dispatches of the 8192^3 kernel before
+    its `cold_calls` cold-cache calls (the last ones when there are none): the summary gives their
+    average next to the bench line's own HIP-event figure."""
     for sub in ("trace", "fetch", "write"):
         os.makedirs(tmp_path / sub)
     db = str(tmp_path / "trace" / "run_results.db")
     _trace_db(db, 700.0)
     c = sqlite3.connect(db)
     c.execute("create table kernels (name text, start int, duration int)")
-    durs = [800000] * 30 + [700000] * 20   # ns: settle / warm-up dispatches, then 20 timed ones
+    # ns: settle / warm-up dispatches, then 20 timed ones, then the cold-cache calls
+    durs = [800000] * 30 + [700000] * 20 + [900000] * cold
     for i, d in enumerate(durs):
         c.execute("insert into kernels values (?, ?, ?)", (GEMM, i, d))
     c.execute("insert into kernels values (?, ?, ?)", ("other", 99, 5))
@@ -104,13 +109,15 @@ def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path):
     os.makedirs(out)
     line = {"steps": 20, "value": 1500.0, "roofline": {"kernel_ms": 0.7, "achieved": 1570.7, "frac": 0.6241,
                                                         "flops_per_launch": 2 * 8192 ** 3}}
+    if cold:
+        line["per_config"] = {"c4": {"cold_ms": 0.9, "cold_calls": cold}}
     cmds = {k: k for k in ("trace", "fetch", "write", "sq", "copytrace")}
     cmds["bench_line"] = line
     t = bench.summarize_profiles(db, str(tmp_path / "fetch" / "run_results.db"),
                                  str(tmp_path / "write" / "run_results.db"), str(out), cmds)
     text = (out / "gemm_8192_kernel_trace.md").read_text()
     assert "| timed 20 | 700.00 | 700.00 |" in text
-    assert "| all 50 |" in text and "kernel_ms 0.7" in text
+    assert f"| all {50 + cold} |" in text and "kernel_ms 0.7" in text
     assert abs(t["gemm_trace_avg_us"] - 700.0) < 1e-9
 
 
