@@ -828,10 +828,38 @@ def timeline_stats(tl, ktiles: int, tile_bytes: int) -> dict:
             "first_tile_us": round(med(first), 2), "k_loop_us": round(med(loop), 2),
             "per_k_tile_us": round(med(loop) / ktiles, 3), "epilogue_us": round(med(epi), 2),
             "end_us": {"min": round(min(end), 2), "median": round(med(end), 2), "max": round(max(end), 2)},
-            "clock_ghz": round(ghz, 3), "copy_bytes_per_clk_per_cu": round(med(rates), 1) if rates else None}
+            "clock_ghz": round(ghz, 3), "copy_bytes_per_clk_per_cu": round(med(rates), 1) if rates else None,
+            "xcds": _timeline_xcds(tl)}
 
 
-def timeline(torch, names=("c2", "c3")) -> None:
+def _timeline_xcds(tl) -> list:
+    """Per XCD (XCC_ID): workgroups, median shader clock (GHz) and median K-loop time (µs) of its
+    workgroups, and the correlation of the two over the XCDs (None with fewer than 3 XCDs)."""
+    import statistics
+    by = {}
+    for r in tl:
+        by.setdefault(r[6] & 0xF, []).append(r)
+    out = []
+    for x in sorted(by):
+        v = by[x]
+        ghz = statistics.median(r[4] / ((r[3] - r[0]) * 10.0) for r in v if r[3] > r[0])
+        out.append({"xcd": x, "workgroups": len(v), "clock_ghz": round(ghz, 3),
+                    "k_loop_us": round(statistics.median((r[2] - r[1]) / 100.0 for r in v), 2)})
+    return out
+
+
+def _correlation(xs, ys):
+    n = len(xs)
+    if n < 3:
+        return None
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxy = sum((a - mx) * (b - my) for a, b in zip(xs, ys))
+    sxx = sum((a - mx) ** 2 for a in xs)
+    syy = sum((b - my) ** 2 for b in ys)
+    return round(sxy / (sxx * syy) ** 0.5, 3) if sxx > 0 and syy > 0 else None
+
+
+def timeline(torch, names=("c2", "c3", "c4")) -> None:
     """Per-workgroup timelines of the barrier ring on the launch-bound products, one JSON line per
     (workload, configuration): tbg_diag_gemm_timeline on the operands in the form the product
     runs on (rows padded with zeros to a multiple of 8 elements, K rounded up to 8: what the
@@ -885,9 +913,9 @@ def timeline(torch, names=("c2", "c3")) -> None:
 
 
 def write_timeline_profile(jsonl: str, out_dir: str) -> None:
-    """profiles/gemm_small_timeline.md from the JSON lines of one `--timeline` run."""
+    """profiles/gemm_ring_timeline.md from the JSON lines of one `--timeline` run."""
     rows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
-    lines = ["# Per-workgroup timelines of the barrier ring on the launch-bound products", "",
+    lines = ["# Per-workgroup timelines of the barrier ring: the launch-bound products and 8192³", "",
              "Each workgroup of the library's barrier-ring kernel, built with timeline recording "
              "(`tiled_bf16_gemm_amd/csrc/gemm_ring.hpp`, CLK 2; `tiled_bf16_gemm_amd/diag/mfma_rate.hip`, "
              "`tbg_diag_gemm_timeline`), records the 100 MHz real-time counter at its start, once its first K "
@@ -912,7 +940,17 @@ def write_timeline_profile(jsonl: str, out_dir: str) -> None:
                          f"{r['end_us']['max']} | {r['first_tile_us']} | {r['k_loop_us']} | {r['per_k_tile_us']} | "
                          f"{r['epilogue_us']} | {r['clock_ghz']} | {r['copy_bytes_per_clk_per_cu']} |")
         lines.append("")
-    with open(os.path.join(out_dir, "gemm_small_timeline.md"), "w") as f:
+        # per XCD, for the configuration the library picks on this workload
+        pick = {"c2": "ring 64x64/3", "c3": "ring 128x128/2", "c4": "ring 256x256/2"}.get(name)
+        rp = [r for r in rs if r["config"] == pick and r.get("xcds")]
+        if rp:
+            xs = rp[0]["xcds"]
+            corr = _correlation([x["clock_ghz"] for x in xs], [x["k_loop_us"] for x in xs])
+            lines += [f"Per XCD, {pick} (correlation of clock and K-loop time over the XCDs: {corr}):", "",
+                      "| XCD | workgroups | clock GHz | K loop µs |", "|---|---|---|---|"]
+            lines += [f"| {x['xcd']} | {x['workgroups']} | {x['clock_ghz']} | {x['k_loop_us']} |" for x in xs]
+            lines.append("")
+    with open(os.path.join(out_dir, "gemm_ring_timeline.md"), "w") as f:
         f.write("\n".join(lines))
 
 
@@ -1045,10 +1083,10 @@ def main():
     ap.add_argument("--bench-kernel-us", type=float, default=None,
                     help="with --summarize: the bench line's HIP-event kernel average, quoted beside the trace")
     ap.add_argument("--timeline", action="store_true",
-                    help="per-workgroup timelines of the barrier ring on c2 and c3 (tbg_diag_gemm_timeline); one "
+                    help="per-workgroup timelines of the barrier ring on c2, c3 and c4 (tbg_diag_gemm_timeline); one "
                          "JSON line per configuration instead of the bench line")
     ap.add_argument("--timeline-md", default="", metavar="JSONL",
-                    help="write profiles/gemm_small_timeline.md from the JSON lines of a --timeline run (no GPU)")
+                    help="write profiles/gemm_ring_timeline.md from the JSON lines of a --timeline run (no GPU)")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workloads (c1..c5, conv_b; a GEMM name may carry an input type, e.g. "
                          "c4@f16, c4@f8e4m3): time every built pipeline/tile/stages configuration on each and print "

@@ -148,6 +148,16 @@ def test_timeline_stats_and_profile(tmp_path):
     path = tmp_path / "timeline.jsonl"
     path.write_text(json.dumps(line) + "\n")
     bench.write_timeline_profile(str(path), str(tmp_path))
-    md = (tmp_path / "gemm_small_timeline.md").read_text()
+    md = (tmp_path / "gemm_ring_timeline.md").read_text()
     assert "## c2: 1024×1024×1024 (B K×N, bf16 out)" in md
     assert "| ring 64x64/3 | 3 | 2 | 2 | 6.1 | 5.6 | 1.0 | 4.0 | 1.0 | 0.2 | 2.0 | 0.9 |" in md
+    # per XCD: XCD 1 holds the two workgroups on CU 5, XCD 4 the third
+    assert s["xcds"] == [{"xcd": 1, "workgroups": 2, "clock_ghz": 2.0, "k_loop_us": 4.0},
+                         {"xcd": 4, "workgroups": 1, "clock_ghz": 2.0, "k_loop_us": 3.0}]
+    assert "| 1 | 2 | 2.0 | 4.0 |" in md and "| 4 | 1 | 2.0 | 3.0 |" in md
+
+
+def test_correlation():
+    assert bench._correlation([1, 2, 3], [2, 4, 6]) == 1.0
+    assert bench._correlation([1, 2, 3], [3, 2, 1]) == -1.0
+    assert bench._correlation([1, 2], [1, 2]) is None
