@@ -5,8 +5,8 @@
 A step is one tbg_gemm call on the 8192³ workload (bf16 A row-major, B row-major K×N, fp32
 accumulation, bf16 out): host-side descriptor encoding, the tiled copies into LDS, the MFMA
 main loop and the masked epilogue, with operands already resident in HBM.  A region is W
-untimed steps, a synchronisation, then K steps bracketed by HIP events and device
-synchronisation.  The same region first runs untimed, back to back, for --settle seconds
+untimed steps, a synchronisation, then K steps between two HIP events on the launch stream and a
+device synchronisation.  The same region first runs untimed, back to back, for --settle seconds
 (reported as roofline.settle: after any idle time the device's power controller needs ~40
 launches of this product before the clock settles); the region timed is the next one.  One
 JSON line is printed.
@@ -14,7 +14,8 @@ JSON line is printed.
 Also reported in the same line:
   roofline      the GEMM kernel against the bf16 dense MFMA peak: algorithmic flops per launch
                 (2MNK) over the average launch time from HIP events on the launch stream
-                (launch_ms: min / median / max per launch; gemm_clock_ghz: the shader clock the
+                (launch_ms: min / median / max per launch, from a further region whose launches
+                each have their own pair of events; gemm_clock_ghz: the shader clock the
                 same kernel reports from inside, per workgroup, right after the timed steps);
                 `traffic` is the HBM bytes per launch from the committed rocprofv3 counter
                 summary when it was taken on the current kernel source, else null.
@@ -133,14 +134,16 @@ def launch_stats(per):
 
 
 def time_gemm_detail(torch, torch_ops, w, steps, warmup, config=None, ab="bf16", settle_s=0.0, operands=None):
-    """One timed region: `warmup` untimed calls, a synchronisation, then `steps` calls each
-    bracketed by HIP events on the launch stream, and a synchronisation.  With settle_s > 0 the
-    same region is first run back to back, untimed, until settle_s seconds have passed, and the
-    region timed is the next one: the same calls in the same pattern as those before it.
-    Returns a dict: ms_step (timed region / steps), ms_kernel (mean per-launch time), per
-    (per-launch ms of the timed region), wall_ms (host wall time per step) and settle (the number
-    of settle regions, their seconds, and the median launch time of the first and of each of the
-    last five)."""
+    """The timed region: `warmup` untimed calls, a synchronisation, then `steps` calls between two
+    HIP events on the launch stream, and a synchronisation (no event between the calls: each event
+    recorded with timing costs the GPU a few microseconds, 7 µs per call measured on a 45 µs
+    product).  With settle_s > 0 the same region is first run back to back, untimed, until
+    settle_s seconds have passed, and the region timed is the next one.  Then one more region, of
+    the same calls each bracketed by its own pair of events, gives the per-launch spread.
+    Returns a dict: ms_step and ms_kernel (timed region / steps: the average launch time, the
+    launches back to back), per (per-launch ms of the spread region), wall_ms (host wall time
+    per step of the timed region) and settle (the number of settle regions, their seconds, and
+    the time per step of the first and of each of the last five)."""
     Av, Bv, b_layout, C, ws = operands if operands is not None else gemm_operands(torch, w, ab)
 
     def call():
@@ -150,36 +153,43 @@ def time_gemm_detail(torch, torch_ops, w, steps, warmup, config=None, ab="bf16",
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for i in range(steps):
-            starts[i].record()
+        e0.record()
+        for _ in range(steps):
             call()
-            ends[i].record()
+        e1.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
-        return [a.elapsed_time(b) for a, b in zip(starts, ends)], starts[0].elapsed_time(ends[-1]), wall
+        return e0.elapsed_time(e1) / steps, wall / steps
 
-    import statistics
+    def spread():
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
     settle = None
     if settle_s > 0:
-        meds = []
+        per_step = []
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < settle_s:
-            per, _, _ = region()
-            meds.append(statistics.median(per))
-        settle = {"regions": len(meds), "seconds": round(time.perf_counter() - t0, 3),
-                  "first_region_median_ms": round(meds[0], 5),
-                  "last_regions_median_ms": [round(x, 5) for x in meds[-5:]]}
-    per, span, wall_ms = region()
-    return {"ms_step": span / steps, "ms_kernel": sum(per) / len(per), "per": per, "wall_ms": wall_ms / steps,
-            "settle": settle}
+            per_step.append(region()[0])
+        settle = {"regions": len(per_step), "seconds": round(time.perf_counter() - t0, 3),
+                  "first_region_ms": round(per_step[0], 5), "last_regions_ms": [round(x, 5) for x in per_step[-5:]]}
+    ms_step, wall_ms = region()
+    return {"ms_step": ms_step, "ms_kernel": ms_step, "per": spread(), "wall_ms": wall_ms, "settle": settle}
 
 
 def time_gemm(torch, torch_ops, w, steps, warmup, config=None, ab="bf16", settle_s=0.0):
-    """Returns (ms per step over the whole timed region, mean per-launch ms from events, wall ms
-    per step)."""
+    """Returns (ms per step over the whole timed region, the same as the average launch time, wall
+    ms per step)."""
     r = time_gemm_detail(torch, torch_ops, w, steps, warmup, config=config, ab=ab, settle_s=settle_s)
     return r["ms_step"], r["ms_kernel"], r["wall_ms"]
 
@@ -321,8 +331,9 @@ def time_copy_graph(torch, torch_ops, w, calls=20, replays=20):
 
 
 def time_copy(torch, torch_ops, w, steps, warmup):
-    """tbg_tiled_copy_many over every box of a copy workload, one launch per step; returns (mean
-    per-launch ms from events, algorithmic bytes per launch = in-bounds source bytes + images)."""
+    """tbg_tiled_copy_many over every box of a copy workload, one launch per step, `steps` launches
+    between two HIP events; returns (ms per launch, algorithmic bytes per launch = in-bounds source
+    bytes + images)."""
     import workloads
     import tiled_bf16_gemm_amd as tbg
     src = workloads.copy_source(w).cuda()
@@ -337,14 +348,13 @@ def time_copy(torch, torch_ops, w, steps, warmup):
     for _ in range(warmup):
         torch_ops.tiled_copy_many(desc, coords, out=out)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
         torch_ops.tiled_copy_many(desc, coords, out=out)
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+    ms = e0.elapsed_time(e1) / steps
     return ms, copy_inbounds_bytes(w) + len(w.coords) * tbg.box_bytes(desc)
 
 
@@ -394,8 +404,8 @@ def mfma_ceiling(torch, kind: int = 0, launches: int = 60, warmup: int = 60):
 
 
 def time_conv(torch, torch_ops, w, steps, warmup, config=None):
-    """tbg_conv2d_fwd on a convolution workload; returns (ms per call over the timed region,
-    mean per-launch ms from events)."""
+    """tbg_conv2d_fwd on a convolution workload: `steps` calls between two HIP events after
+    `warmup` untimed ones; returns (ms per call, the same as the average launch time)."""
     import workloads
     x, f = workloads.conv_inputs(w)
     x, f = x.cuda(), f.cuda()
@@ -403,17 +413,15 @@ def time_conv(torch, torch_ops, w, steps, warmup, config=None):
     for _ in range(warmup):
         torch_ops.conv2d(x, f, w.pad, w.stride, w.dil, w.out_dtype, out=y, config=config)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
         torch_ops.conv2d(x, f, w.pad, w.stride, w.dil, w.out_dtype, out=y, config=config)
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    region = starts[0].elapsed_time(ends[-1])
+    ms = e0.elapsed_time(e1) / steps
     del x, f, y
-    return region / steps, sum(per) / len(per)
+    return ms, ms
 
 
 def cpu_baseline(w, target_s: float = 15.0):
@@ -534,14 +542,17 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, out_dir: str
     timed_avg = None
     if line and disp:
         steps = int(line.get("steps", 20))
-        # after the timed steps the same kernel runs the cold-cache calls (per_config c4)
+        # after the timed steps the same kernel runs the per-launch spread region (its own
+        # warm-up and steps) and the cold-cache calls (per_config c4)
         cold = int(line.get("per_config", {}).get("c4", {}).get("cold_calls", 0))
-        timed = disp[len(disp) - cold - steps:len(disp) - cold]
+        spread = int(line["roofline"].get("spread_calls", 0))
+        after = cold + spread
+        timed = disp[len(disp) - after - steps:len(disp) - after]
         timed_avg = statistics.mean(timed)
         k_ms = line["roofline"]["kernel_ms"]
         flops = line["roofline"]["flops_per_launch"]
-        order = (f"its {steps} timed steps and {cold} calls on cold caches, in that order; the {steps} before the last "
-                 f"{cold} are the timed steps" if cold else
+        order = (f"its {steps} timed steps, {spread} calls of the per-launch spread region and {cold} calls on cold "
+                 f"caches, in that order; the {steps} before the last {after} are the timed steps" if after else
                  f"its {steps} timed steps, in that order; the last {steps} are the timed steps")
         lines += ["", f"The 8192³ kernel's {len(disp)} dispatches are the bench's settle regions, its warm-up, {order}.",
                   "", "| dispatches | average us | median us | TFLOP/s at the average | frac of 2516.6 |",
@@ -992,8 +1003,9 @@ def write_sweep_profiles(jsonl: str, out_dir: str) -> None:
 
     head = ["Command (repository root on the GPU box; <out> an output folder), then "
             "`python bench.py --sweep-md <out>/sweep.jsonl`:", "", "```", SWEEP_CMD, "```", "",
-            "Each configuration: its region (5 warm-up calls, then 20 calls timed with HIP events on the launch "
-            "stream; per-call times include the host) run untimed for 0.1 s, then once timed; operands generated "
+            "Each configuration: its region (5 warm-up calls, then 20 calls between two HIP events on the launch "
+            "stream; per-call times include the host where it is slower than the GPU) run untimed for 0.1 s, then "
+            "once timed; operands generated "
             "once per workload; for c1-c3 also 20 products captured in a HIP graph and replayed 20 times "
             "(GPU time per product).  One pass on one MI355X; boxes differ by a few per cent.", ""]
     # bf16 GEMM
@@ -1258,6 +1270,9 @@ def main():
             "traffic": load_traffic(),
             "kernel_ms": round(ms_kernel, 5),
             "launch_ms": launch_stats(head["per"]),
+            # the per-launch spread: a region after the timed one, its warm-up and its launches
+            # each bracketed by a pair of events
+            "spread_calls": args.warmup + args.steps,
             "flops_per_launch": w.flops,
             "settle": head["settle"],
             "gemm_clock_ghz": clock,

@@ -93,8 +93,10 @@ def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path, col
     _trace_db(db, 700.0)
     c = sqlite3.connect(db)
     c.execute("create table kernels (name text, start int, duration int)")
-    # ns: settle / warm-up dispatches, then 20 timed ones, then the cold-cache calls
-    durs = [800000] * 30 + [700000] * 20 + [900000] * cold
+    # ns: settle / warm-up dispatches, then 20 timed ones, then (with cold calls) the spread
+    # region's 5 + 20 and the cold-cache calls
+    spread = 25 if cold else 0
+    durs = [800000] * 30 + [700000] * 20 + [750000] * spread + [900000] * cold
     for i, d in enumerate(durs):
         c.execute("insert into kernels values (?, ?, ?)", (GEMM, i, d))
     c.execute("insert into kernels values (?, ?, ?)", ("other", 99, 5))
@@ -111,13 +113,14 @@ def test_trace_summary_sets_timed_dispatches_beside_the_bench_line(tmp_path, col
                                                         "flops_per_launch": 2 * 8192 ** 3}}
     if cold:
         line["per_config"] = {"c4": {"cold_ms": 0.9, "cold_calls": cold}}
+        line["roofline"]["spread_calls"] = spread
     cmds = {k: k for k in ("trace", "fetch", "write", "sq", "copytrace")}
     cmds["bench_line"] = line
     t = bench.summarize_profiles(db, str(tmp_path / "fetch" / "run_results.db"),
                                  str(tmp_path / "write" / "run_results.db"), str(out), cmds)
     text = (out / "gemm_8192_kernel_trace.md").read_text()
     assert "| timed 20 | 700.00 | 700.00 |" in text
-    assert f"| all {50 + cold} |" in text and "kernel_ms 0.7" in text
+    assert f"| all {50 + spread + cold} |" in text and "kernel_ms 0.7" in text
     assert abs(t["gemm_trace_avg_us"] - 700.0) < 1e-9
 
 
