@@ -815,3 +815,32 @@ def test_graph_capture(ops, orc):
         torch.cuda.synchronize()
         del x
     del g
+
+
+@gpu
+@pytest.mark.parametrize("pipeline,tile,stages", CONFIGS)
+def test_permutation_products(ops, pipeline, tile, stages):
+    """Closed forms that pin the product's row and column placement without the oracle: for a
+    selection matrix P (each row a single 1, at a random column), P·B is B's rows picked out in
+    P's order and Bᵀ·Pᵀ (Pᵀ given as P stored N×K) the same columns, exactly; and I·B = B.
+    Ragged sizes, both B layouts, fp32 out; random bf16 values, so any entry landing in the wrong
+    place shows."""
+    cfg = _cfg(tile, stages, pipeline)
+    rng = np.random.default_rng(4242)
+    M, K, N = 300, 257, 193
+    for case in ("select", "identity"):
+        perm = rng.integers(0, K, M) if case == "select" else np.arange(K)
+        P = np.zeros((len(perm), K), np.float32)
+        P[np.arange(len(perm)), perm] = 1.0
+        Bkn = torch.randn((K, N), generator=torch.Generator().manual_seed(int(rng.integers(1 << 30)))).to(torch.bfloat16)
+        want = Bkn.float().numpy()[perm]  # (rows of P) × N
+        Pt = torch.from_numpy(P).to(torch.bfloat16)
+        _say(f"{pipeline} {tile}/{stages}: {case} · B (K×N and N×K)")
+        got = ops.gemm(Pt.cuda(), Bkn.cuda(), "kn", "f32", config=cfg)
+        got_nk = ops.gemm(Pt.cuda(), Bkn.t().contiguous().cuda(), "nk", "f32", config=cfg)
+        # B' · Pᵀ with B' = Bᵀ (N×K row-major A operand) and Pᵀ given as P stored N×K
+        got_cols = ops.gemm(Bkn.t().contiguous().cuda(), Pt.cuda(), "nk", "f32", config=cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), want), f"{case}: P·B (K×N) misplaced entries"
+        assert np.array_equal(got_nk.cpu().numpy(), want), f"{case}: P·B (N×K) misplaced entries"
+        assert np.array_equal(got_cols.cpu().numpy(), want.T), f"{case}: Bᵀ·Pᵀ misplaced entries"
