@@ -936,7 +936,7 @@ def write_timeline_profile(jsonl: str, out_dir: str) -> None:
              "\"launch\" is the median of 20 launches timed with HIP events on the launch stream (it includes the "
              "dispatch of the grid).  Copy rate: the K tiles' bytes copied by all workgroups of a CU over the "
              "span of their K loops, per shader clock, for the CUs holding the most workgroups.", "",
-             "Command (repository root on the GPU box; <out> an output folder), then "
+             "Command (run from the repository root on an MI355X; <out> an output folder), then "
              "`python bench.py --timeline-md <out>/timeline.jsonl`:", "", "```",
              "python -u bench.py --timeline > <out>/timeline.jsonl", "```", ""]
     for name in dict.fromkeys(r["timeline"] for r in rows):
@@ -1001,7 +1001,7 @@ def write_sweep_profiles(jsonl: str, out_dir: str) -> None:
                              f"{r['tflops']}{b} | {r['pct_peak']} |")
         return lines + [""]
 
-    head = ["Command (repository root on the GPU box; <out> an output folder), then "
+    head = ["Command (run from the repository root on an MI355X; <out> an output folder), then "
             "`python bench.py --sweep-md <out>/sweep.jsonl`:", "", "```", SWEEP_CMD, "```", "",
             "Each configuration: its region (5 warm-up calls, then 20 calls between two HIP events on the launch "
             "stream; per-call times include the host where it is slower than the GPU) run untimed for 0.1 s, then "
