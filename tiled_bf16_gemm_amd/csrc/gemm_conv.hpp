@@ -58,6 +58,16 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
       pix[j] = 0;
     }
   }
+  // The lane's chunk of each atom is fixed (its row's 2-row swizzle); pixc folds its byte offset
+  // into the pixel's.
+  LaneChunk la[T::AtomsA];
+  int pixc[T::AtomsA];
+#pragma unroll
+  for (int j = 0; j < T::AtomsA; ++j) {
+    const int row = (BM / 4) * wave + 8 * j + (lane >> 3);
+    la[j].chunk = (lane & 7) ^ row_xor<kSwizzle128B2Row>(row);
+    pixc[j] = pix[j] + la[j].chunk * 16;
+  }
   const uint32_t pitch_b = (uint32_t)(cp.ldw * 2);
   LaneChunk lb[T::AtomsB];
 #pragma unroll
@@ -72,23 +82,28 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   // channels past c8 by the chunk count); each K tile moves its base to the tap's columns.
   const rsrc_t rw = make_rsrc(cp.W + (uint64_t)n0 * cp.ldw, 0x7FFFFFFFull);
 
-  // Copies of K tile kt (tap kt / cblocks, channel block kt % cblocks) into `stage`; la receives
-  // this tile's per-lane A sources.  A tile past the end is issued fully masked.
-  auto make_copy = [&](int kt, int stage, LaneChunk* la) __attribute__((always_inline)) {
-    const bool live = kt < ktiles;
-    const int tap = live ? kt / cp.cblocks : 0;
-    const int cb = live ? kt - tap * cp.cblocks : 0;
-    const int rr = tap / cp.s, ss = tap - rr * cp.s;
-    const int c0 = cb * 64;
-    const int dy = rr * cp.dh, dx = ss * cp.dw;
+  // The copies of one K tile into `stage`; la receives the tile's per-lane A sources.  make_copy
+  // is called once per K tile, in order (tiles 0 and 1 before the loop, then tile kt+2 during
+  // tile kt), so it keeps the next tile's position as counters and steps them: channel block cb
+  // of filter tap (rr, ss), K tile (rr·S + ss)·cblocks + cb; no division per tile.  A lane whose
+  // window position (iy, ix) lies outside the image takes an offset with bit 31 set, which the
+  // buffer's range (below 2^31) rejects: bit 31 of iy | (h-1-iy) | ix | (w-1-ix) is set exactly
+  // when iy or ix is outside [0, h) or [0, w), so the test needs no compare or branch.  Tiles
+  // past the end are issued fully masked the same way.
+  int nx_kt = 0, nx_cb = 0, nx_rr = 0, nx_ss = 0;
+  const int h1 = cp.h - 1, w1 = cp.w - 1;
+  auto make_copy = [&](int stage, LaneChunk* la) __attribute__((always_inline)) {
+    const bool live = nx_kt < ktiles;
+    const int c0 = nx_cb * 64;
+    const int dy = nx_rr * cp.dh, dx = nx_ss * cp.dw;
+    const int tap = nx_rr * cp.s + nx_ss;
     const int tap_off = (dy * cp.w + dx) * cpix + c0 * 2;
+    const uint32_t dead = live ? 0u : kOobOffset;
 #pragma unroll
     for (int j = 0; j < T::AtomsA; ++j) {
-      const int row = (BM / 4) * wave + 8 * j + (lane >> 3);
-      const int chunk = (lane & 7) ^ row_xor<kSwizzle128B2Row>(row);
-      const bool ok = live && (unsigned)(ih0[j] + dy) < (unsigned)cp.h && (unsigned)(iw0[j] + dx) < (unsigned)cp.w;
-      la[j].chunk = chunk;
-      la[j].offset = ok ? (uint32_t)(pix[j] + tap_off + chunk * 16) : kOobOffset;
+      const int iy = ih0[j] + dy, ix = iw0[j] + dx;
+      const uint32_t outside = (uint32_t)(iy | (h1 - iy) | ix | (w1 - ix)) & kOobOffset;
+      la[j].offset = (uint32_t)(pixc[j] + tap_off) | outside | dead;
     }
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
@@ -96,8 +111,17 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
     tc.lds_a = sa + (BM / 4) * wave * 128;
     tc.cvalid_a = live ? (cp.c8 - c0) >> 3 : -1;
     tc.rb = rsrc_advance(rw, (uint64_t)(tap * cp.c8 + c0) * 2u);
+    if (!live) tc.rb.z = 0;  // a tile past the end reads no filter column
     tc.lds_b = sa + T::ABytes + (BN / 4) * wave * 128;
     tc.cvalid_b = tc.cvalid_a;
+    ++nx_kt;
+    if (++nx_cb == cp.cblocks) {
+      nx_cb = 0;
+      if (++nx_ss == cp.s) {
+        nx_ss = 0;
+        ++nx_rr;
+      }
+    }
     return tc;
   };
 
@@ -107,10 +131,9 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
   {
     Frags<T> f0, f1;
     const TileCopy none{};
-    LaneChunk la[T::AtomsA];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const TileCopy tc = make_copy(t, t, la);
+      const TileCopy tc = make_copy(t, la);
 #pragma unroll
       for (int j = 0; j < T::Atoms; ++j) copy_atom<T>(tc, la, lb, j);
     }
@@ -118,21 +141,33 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
 #pragma unroll
     for (int idx = 0; idx < T::Reads; ++idx) read_frag<T, BL>(f0, fa, smem, smem + T::ABytes, 0, idx);
     // Tile kt on stage CUR = kt & 1, a compile-time constant: two tiles per loop iteration.
-    auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
-      constexpr int cur = decltype(stage)::value;
-      const uint8_t* sA = smem + cur * T::StageBytes;
-      kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
-      stage_barrier<0>();  // tile kt+1 landed everywhere; stage kt&1 free
-      const uint8_t* nA = smem + (cur ^ 1) * T::StageBytes;
-      const TileCopy tc = make_copy(kt + 2, cur, la);
-      kstep<T, BL, true>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
+    // MASK false (channels a multiple of 64: every channel block whole) leaves out the chunk
+    // tests of the copies; the offsets and ranges of make_copy still mask the window, the rows
+    // past N and the tiles past the end.
+    auto kloop = [&](auto maskc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(maskc)::value;
+      auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
+        constexpr int cur = decltype(stage)::value;
+        const uint8_t* sA = smem + cur * T::StageBytes;
+        kstep<T, BL, false>(acc, f0, f1, fa, sA, sA + T::ABytes, 1, none, la, lb);
+        stage_barrier<0>();  // tile kt+1 landed everywhere; stage kt&1 free
+        const uint8_t* nA = smem + (cur ^ 1) * T::StageBytes;
+        const TileCopy tc = make_copy(cur, la);  // tile kt+2
+        kstep<T, BL, true, MASK, MASK>(acc, f1, f0, fa, nA, nA + T::ABytes, 0, tc, la, lb);
+      };
+      int kt = 0;
+      for (; kt + 2 <= ktiles; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        tile(kt + 1, std::integral_constant<int, 1>{});
+      }
+      if (kt < ktiles) tile(kt, std::integral_constant<int, 0>{});
     };
-    int kt = 0;
-    for (; kt + 2 <= ktiles; kt += 2) {
-      tile(kt, std::integral_constant<int, 0>{});
-      tile(kt + 1, std::integral_constant<int, 1>{});
-    }
-    if (kt < ktiles) tile(kt, std::integral_constant<int, 0>{});
+    // (the second copy of the loop only where registers allow it: two loops of the 256-row
+    // tiles would spill)
+    if (BM * BN <= 128 * 128 && cp.c8 % 64 == 0)
+      kloop(std::integral_constant<bool, !(BM * BN <= 128 * 128)>{});
+    else
+      kloop(std::true_type{});
   }
   drain_acc<T>(acc);
   stage_barrier<0>();
