@@ -97,13 +97,14 @@ __global__ void __launch_bounds__(kThreads, (RingCfg<BM, BN, 2>::MinBlocks)) gem
     const int c0 = nx_cb * 64;
     const int dy = nx_rr * cp.dh, dx = nx_ss * cp.dw;
     const int tap = nx_rr * cp.s + nx_ss;
-    const int tap_off = (dy * cp.w + dx) * cpix + c0 * 2;
+    // modulo 2^32: exact wherever the window lies in the image, the only places it is used
+    const uint32_t tap_off = ((uint32_t)dy * (uint32_t)cp.w + (uint32_t)dx) * (uint32_t)cpix + (uint32_t)c0 * 2u;
     const uint32_t dead = live ? 0u : kOobOffset;
 #pragma unroll
     for (int j = 0; j < T::AtomsA; ++j) {
       const int iy = ih0[j] + dy, ix = iw0[j] + dx;
       const uint32_t outside = (uint32_t)(iy | (h1 - iy) | ix | (w1 - ix)) & kOobOffset;
-      la[j].offset = (uint32_t)(pixc[j] + tap_off) | outside | dead;
+      la[j].offset = ((uint32_t)pixc[j] + tap_off) | outside | dead;
     }
     TileCopy tc;
     const uint32_t sa = smem_addr + stage * T::StageBytes;
