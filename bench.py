@@ -433,7 +433,7 @@ def cpu_baseline(w, target_s: float = 15.0):
     Ab, Bb = workloads.bits(A), workloads.bits(B)
     lda, ldb, _ = w.lds()
     threads = orc.max_threads()
-    rows = 8
+    rows = max(8, threads)  # one row per thread at least, so the trial keeps every thread busy
     t0 = time.perf_counter()
     orc.gemm(Ab, Bb, w.M, w.N, w.K, lda, ldb, w.b_layout, rows=(0, rows), threads=threads)
     dt = time.perf_counter() - t0
