@@ -131,6 +131,66 @@ def test_conv_workloads(ops, orc, name):
             assert np.array_equal(got[:, :w.k], base[:, :w.k]), "tiles disagree"
 
 
+HALO = ["conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_dil2"]
+
+
+@gpu
+@pytest.mark.parametrize("name", HALO)
+def test_conv_halo_kernel(ops, orc, name):
+    """The halo kernel (tile 448x128: stride 1, the input window copied once per 32-channel
+    block) in full against the oracle for both output types, bit for bit on small integers, with
+    the output rows padded and left untouched past K.  These layers cover partial last tiles of
+    an image, output channels past a multiple of 128, dilation, asymmetric padding and one to
+    four window atoms per wave and tap.  (Its sums run in another order than the im2col tiles',
+    so only the oracle decides.)"""
+    import tiled_bf16_gemm_amd as tbg
+    w = workloads.CONVS[name]
+    x, f = workloads.conv_inputs(w)
+    ref = _ref(orc, w, x, f)
+    cfg = tbg.gemm_config("448x128", 0, "ring")
+    for out in ("f32", "bf16"):
+        _say(f"halo conv {name} (M={w.M} K={w.k} RSC={w.r * w.s * w.c}) out {out}")
+        got = _conv(ops, w, x, f, out, config=cfg)
+        r = oracle.gemm_check(got[:, :w.k], ref)
+        _say(f"  max_abs={r['max_abs_err']:.3g} max_rel={r['max_rel_err']:.3g} fail={r['n_fail']}")
+        assert r["pass"], r
+        assert np.all(np.isnan(got[:, w.k:])), "columns past K were written"
+    rng = np.random.default_rng(17)
+    xi = torch.from_numpy(rng.integers(-4, 5, (w.n, w.h, w.w, w.c)).astype(np.float32)).to(torch.bfloat16)
+    fi = torch.from_numpy(rng.integers(-4, 5, (w.k, w.r, w.s, w.c)).astype(np.float32)).to(torch.bfloat16)
+    _say(f"halo conv {name}: integers")
+    got = _conv(ops, w, xi, fi, "f32", config=cfg)
+    want = _ref(orc, w, xi, fi)
+    assert np.array_equal(got[:, :w.k], want), f"{int((got[:, :w.k] != want).sum())} entries differ"
+
+
+@gpu
+def test_conv_halo_alpha_beta_and_refusals(ops, orc):
+    """Y <- alpha·conv + beta·Y through the halo kernel (both output types); tile 448x128 is
+    refused where the halo kernel does not apply (stride 2, channels not a multiple of 32)."""
+    import tiled_bf16_gemm_amd as tbg
+    w = workloads.CONVS["conv_halo_rows"]
+    x, f = workloads.conv_inputs(w)
+    _, s64 = orc.conv2d(workloads.bits(x), workloads.bits(f), w.n, w.h, w.w, w.c, w.k, w.r, w.s, w.pad, w.stride,
+                        w.dil, want64=True)
+    y_old = torch.from_numpy(np.random.default_rng(5).standard_normal((w.M, w.k + 3)).astype(np.float32))
+    cfg = tbg.gemm_config("448x128", 0, "ring")
+    for out in ("f32", "bf16"):
+        _say(f"halo conv alpha=1.5 beta=-0.5 out {out}")
+        old = y_old.to(torch.bfloat16).float() if out == "bf16" else y_old
+        got = _conv(ops, w, x, f, out, alpha=1.5, beta=-0.5, y_old=old, config=cfg)
+        ref = (1.5 * s64 + (-0.5) * old[:, :w.k].double().numpy()).astype(np.float32)
+        r = oracle.gemm_check(got[:, :w.k], ref)
+        assert r["pass"], r
+        assert np.array_equal(got[:, w.k:], old[:, w.k:].numpy())
+    for name in ("conv_stride2", "conv_3x3"):
+        wr = workloads.CONVS[name]
+        xr, fr = workloads.conv_inputs(wr)
+        _say(f"halo conv refused on {name}")
+        with pytest.raises(tbg.Error, match="halo"):
+            _conv(ops, wr, xr, fr, "f32", config=cfg)
+
+
 @gpu
 def test_conv_integer_bit_exact(ops, orc):
     """Small-integer inputs: every partial sum is exact in binary32, so the bits must match."""
@@ -176,15 +236,23 @@ def test_conv_benchmark_layer_sampled(ops, orc):
     x, f = workloads.conv_inputs(w)
     xd, fd = x.cuda(), f.cuda()
     _say(f"conv_b M={w.M} K={w.k}")
+    import tiled_bf16_gemm_amd as tbg
     y = ops.conv2d(xd, fd, w.pad, w.stride, w.dil, "bf16")
     y2 = ops.conv2d(xd, fd, w.pad, w.stride, w.dil, "bf16")
+    # the library's choice here is the halo kernel (same bits as forcing it); the im2col kernel
+    # is checked on the same rows
+    yh = ops.conv2d(xd, fd, w.pad, w.stride, w.dil, "bf16", config=tbg.gemm_config("448x128", 0, "ring"))
+    yi = ops.conv2d(xd, fd, w.pad, w.stride, w.dil, "bf16", config=tbg.gemm_config("128x128", 0, "ring"))
     torch.cuda.synchronize()
     assert torch.isfinite(y.float()).all()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    assert torch.equal(y.view(torch.int16), yh.view(torch.int16)), "the library's choice is not the halo kernel"
     yc = y.float().cpu().numpy()
+    yic = yi.float().cpu().numpy()
     per_img = w.M // w.n
     for m0, m1 in ((0, 200), (per_img * 15 + 3000, per_img * 15 + 3200), (w.M - 200, w.M)):
         ref = _ref(orc, w, x, f, rows=(m0, m1))
-        r = oracle.gemm_check(yc[m0:m1], ref)
-        _say(f"  rows {m0}..{m1}: max_abs={r['max_abs_err']:.3g} fail={r['n_fail']}")
-        assert r["pass"], r
+        for what, yy in (("halo", yc), ("128x128", yic)):
+            r = oracle.gemm_check(yy[m0:m1], ref)
+            _say(f"  {what} rows {m0}..{m1}: max_abs={r['max_abs_err']:.3g} fail={r['n_fail']}")
+            assert r["pass"], r

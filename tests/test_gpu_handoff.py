@@ -8,8 +8,8 @@ library is also built with TBG_HANDOFF_CHECK=1 (tiled_bf16_gemm_amd/diag/libtbg_
 same C ABI), where every hand-off drains all of the wave's copies and LDS reads first.  A
 schedule that let a wave read a stage before its data landed, or overwrite a stage another wave
 still read, gives different bits from the drained build; these tests require identical bits on
-every configuration of the barrier ring, the producer/consumer ring, the fp8 ring and the
-convolution ring."""
+every configuration of the barrier ring, the producer/consumer ring, the fp8 ring, the
+convolution ring and the halo convolution."""
 import ctypes
 import os
 
@@ -115,3 +115,19 @@ def test_fp8_and_convolution_handoffs(libs):
         assert st == 0, check.tbg_last_error().decode()
         torch.cuda.synchronize()
         _same(got[0], got[1], f"conv {tile}")
+    # the halo kernel: its filter ring and its two window images (atoms per wave and tap 1..4)
+    for name in ("conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3"):
+        w = workloads.CONVS[name]
+        x, f = workloads.conv_inputs(w)
+        x, f = x.cuda(), f.cuda()
+        shp = tbg.conv2d_shape(w.n, w.h, w.w, w.c, w.k, w.r, w.s, w.pad, w.stride, w.dil)
+        cfg = tbg.gemm_config("448x128", 0, "ring")
+        got = [torch.full((w.M, w.k), float("nan"), dtype=torch.float32, device="cuda") for _ in range(2)]
+        _say(f"halo conv {name}: lean and drained")
+        tbg.conv2d_fwd(shp, 1.0, x.data_ptr(), f.data_ptr(), 0.0, got[0].data_ptr(), w.k, "f32", cfg, ws.data_ptr(),
+                       ws.numel(), stream)
+        st = check.tbg_conv2d_fwd(ctypes.byref(shp), 1.0, x.data_ptr(), f.data_ptr(), 0.0, got[1].data_ptr(), w.k,
+                                  tbg.DTYPES["f32"], ctypes.byref(cfg), ws.data_ptr(), ws.numel(), stream)
+        assert st == 0, check.tbg_last_error().decode()
+        torch.cuda.synchronize()
+        _same(got[0], got[1], f"halo conv {name}")

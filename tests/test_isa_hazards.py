@@ -1,0 +1,129 @@
+"""Static check of the kernels' AMD assembly (CPU only): every direct-to-LDS buffer load written as
+inline assembly has its scalar operands settled.
+
+gfx9 needs 5 wait states between a vector instruction that writes a scalar register (for example
+v_readfirstlane_b32) and a vector-memory instruction that reads that register (the buffer
+descriptor, M0).  The compiler inserts them in front of its own memory instructions but cannot see
+inside inline assembly, so a descriptor built with v_readfirstlane right before an asm buffer load
+is read stale, and a stale descriptor can address memory outside the operand.  This test compiles
+every kernel source (product build and hand-off checking build) to assembly and requires that no
+such load has a vector write of one of its scalar operands within the 5 preceding wait states
+(each instruction counts 1, s_nop N counts N + 1)."""
+import concurrent.futures
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "tiled_bf16_gemm_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def _hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def _sregs(tok):
+    tok = tok.strip()
+    m = re.match(r"s\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {f"s{i}" for i in range(int(m.group(1)), int(m.group(2)) + 1)}
+    if re.match(r"s\d+$", tok) or tok in ("m0", "vcc"):
+        return {tok}
+    return set()
+
+
+def _vector_sgpr_writes(ins):
+    """Scalar registers a vector instruction writes (empty for any other instruction)."""
+    op, _, rest = ins.partition(" ")
+    if not op.startswith("v_"):
+        return set()
+    ops = [o.strip() for o in rest.split(",")]
+    out = set()
+    if op.startswith(("v_readfirstlane", "v_readlane")) or (op.startswith("v_cmp") and op.endswith("_e64")):
+        out |= _sregs(ops[0])
+    if op.startswith(("v_add_co", "v_sub_co", "v_subrev_co", "v_addc_co", "v_subb_co", "v_mad_u64", "v_mad_i64",
+                      "v_div_scale")) and len(ops) > 1:
+        out |= _sregs(ops[1])
+    return out
+
+
+def scan(text):
+    """Hazards in one assembly listing: (load, offending instruction, wait states between)."""
+    ins = []
+    for line in text.splitlines():
+        t = line.strip()
+        if not t or t.startswith((".", ";", "//")) or t.endswith(":"):
+            continue
+        ins.append(t.split(";")[0].strip())
+    found = []
+    for i, t in enumerate(ins):
+        if not (t.startswith("buffer_load") and t.endswith(" lds")):
+            continue
+        ops = [o.strip() for o in t.partition(" ")[2].split(",")]
+        if ops[1].startswith("v"):
+            found.append((t, "descriptor in vector registers", 0))
+            continue
+        need = _sregs(ops[1]) | {"m0"}
+        ws = 0
+        for prev in reversed(ins[max(0, i - 8):i]):
+            if _vector_sgpr_writes(prev) & need:
+                found.append((t, prev, ws))
+                break
+            m = re.match(r"s_nop\s+(\d+)", prev)
+            ws += int(m.group(1)) + 1 if m else 1
+            if ws >= 5:
+                break
+    return found
+
+
+def test_scan_flags_a_planted_hazard_and_passes_settled_code():
+    """The scanner itself: a readfirstlane straight into a descriptor register is flagged; the same
+    with s_nop 4 in between, or with the descriptor written by scalar instructions, is not."""
+    bad = "v_readfirstlane_b32 s43, v70\n s_mov_b32 m0, s2\n buffer_load_dwordx4 v1, s[40:43], 0 offen lds\n"
+    assert len(scan(bad)) == 1
+    ok = "v_readfirstlane_b32 s43, v70\n s_nop 4\n buffer_load_dwordx4 v1, s[40:43], 0 offen lds\n"
+    assert scan(ok) == []
+    ok2 = "s_mov_b32 s43, 0x20000\n buffer_load_dwordx4 v1, s[40:43], 0 offen lds\n"
+    assert scan(ok2) == []
+    far = "v_readfirstlane_b32 s43, v70\n" + "s_add_i32 s1, s1, 1\n" * 5 + "buffer_load_dwordx4 v1, s[40:43], 0 offen lds\n"
+    assert scan(far) == []
+    m0 = "v_readfirstlane_b32 m0, v3\n buffer_load_dwordx4 v1, s[40:43], 0 offen lds\n"
+    assert len(scan(m0)) == 1
+
+
+def _compile(src, check):
+    out = tempfile.NamedTemporaryFile(suffix=".s", delete=False).name
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wno-unused-command-line-argument",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC,
+           f"-DTBG_HANDOFF_CHECK={check}", "--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    try:
+        if r.returncode != 0:
+            return src, check, None, r.stderr[-2000:]
+        with open(out) as f:
+            return src, check, scan(f.read()), ""
+    finally:
+        os.unlink(out)
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
+def test_inline_buffer_loads_have_settled_scalar_operands():
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    jobs = [(s, c) for s in srcs for c in (0, 1)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(lambda j: _compile(*j), jobs))
+    problems = []
+    for src, check, found, err in results:
+        name = f"{os.path.basename(src)} (hand-off check {check})"
+        if found is None:
+            problems.append(f"{name}: hipcc failed: {err}")
+        for load, prev, ws in found or []:
+            problems.append(f"{name}: {load!r} after {prev!r} ({ws} wait states)")
+    assert not problems, "\n".join(problems[:20])

@@ -999,15 +999,19 @@ tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void
   ConvPlan pl;
   tbg_status st = conv_plan(shape, x_aligned, w_aligned, pl);
   if (st != TBG_OK) return st;
+  // tile 448x128 names the halo kernel (stride 1: the input window copied once per channel block)
+  const bool want_halo = cfg && cfg->tile_m == 448 && cfg->tile_n == 128;
   if (cfg) {
     if (cfg->pipeline != TBG_PIPE_AUTO && cfg->pipeline != TBG_PIPE_RING)
       return fail(TBG_ERR_UNSUPPORTED, "the convolution runs on the barrier ring only");
-    if (cfg->stages != 0 && cfg->stages != 2)
-      return fail(TBG_ERR_UNSUPPORTED, "the convolution ring has 2 stages");
+    if (want_halo ? (cfg->stages != 0 && cfg->stages != 4) : (cfg->stages != 0 && cfg->stages != 2))
+      return fail(TBG_ERR_UNSUPPORTED, want_halo ? "the halo convolution has 4 filter stages"
+                                                 : "the convolution ring has 2 stages");
     if ((cfg->tile_m == 0) != (cfg->tile_n == 0))
       return fail(TBG_ERR_INVALID_VALUE, "tile_m and tile_n must both be 0 or both be set");
-    if (cfg->tile_m != 0 && !tbg::conv_tile_built(cfg->tile_m, cfg->tile_n))
-      return fail(TBG_ERR_UNSUPPORTED, "no convolution kernel with tile %dx%d (built: 256x256, 256x128, 128x128, 64x64)",
+    if (cfg->tile_m != 0 && !want_halo && !tbg::conv_tile_built(cfg->tile_m, cfg->tile_n))
+      return fail(TBG_ERR_UNSUPPORTED,
+                  "no convolution kernel with tile %dx%d (built: 256x256, 256x128, 128x128, 64x64; 448x128 halo)",
                   cfg->tile_m, cfg->tile_n);
   }
   if (y_dtype != TBG_F32 && y_dtype != TBG_BF16) return fail(TBG_ERR_INVALID_VALUE, "y must be TBG_F32 or TBG_BF16");
@@ -1085,6 +1089,29 @@ tbg_status tbg_conv2d_fwd(const tbg_conv2d_shape* shape, float alpha, const void
   cp.dh = shape->dil_h;
   cp.dw = shape->dil_w;
   cp.cblocks = (int)((pl.c8 + 63) / 64);
+  // The halo kernel, where the shape allows it (stride 1, channels a multiple of 32 with nothing
+  // repacked, a window that fits LDS): forced by tile 448x128, chosen by the library when its
+  // tiles use at least 3/4 of their rows and fill at least half of the compute units.
+  tbg::HaloParams hp;
+  memset(&hp, 0, sizeof(hp));
+  int hs = 0;
+  const char* why = "channels a multiple of 32 and 16-byte aligned x and w";
+  hp.c = cp;
+  const bool halo_ok = !pl.pack && shape->c % 32 == 0 && tbg::plan_conv_halo(hp, &hs, &why);
+  if (want_halo && !halo_ok) return fail(TBG_ERR_UNSUPPORTED, "the 448x128 halo convolution needs %s", why);
+  const int cus_h = num_cus > 0 ? num_cus : 256;
+  const bool auto_halo = halo_ok && (!cfg || cfg->tile_m == 0) &&
+                         4 * pl.oh * pl.ow >= 3 * (int64_t)hp.tpi * 448 &&
+                         2 * (int64_t)hp.c.g.tiles_m * hp.c.g.tiles_n >= cus_h;
+  if (want_halo || auto_halo) {
+    log_choice("conv2d N=%lld H=%lld W=%lld C=%lld K=%lld %dx%d: halo 448x128, %d output rows per tile, "
+               "window %dx%d, %d atoms per wave and tap",
+               (long long)shape->n, (long long)shape->h, (long long)shape->w, (long long)shape->c,
+               (long long)shape->k, shape->r, shape->s, hp.tr, hp.hh, hp.hw, hs);
+    e = tbg::launch_conv_halo(hp, hs, y_dtype == TBG_BF16, s);
+    if (e != hipSuccess) return fail(TBG_ERR_HIP, "convolution launch: %s", hipGetErrorString(e));
+    return TBG_OK;
+  }
   // Workgroup tile: the GEMM ring's cost model (tiles per busiest CU × tile work / measured
   // efficiency relative to 256×256) over the tiles built for convolution.
   int bm = 256, bn = 256;

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fast_div.hpp"
 #include "tbg_desc.hpp"
 
 namespace tbg {
@@ -44,11 +45,28 @@ struct ConvParams {
   int cblocks;         // ceil(c8 / 64): 64-channel blocks per tap
 };
 
+// Arguments of the halo convolution (gemm_conv_halo.hpp): stride 1, channels a multiple of 32.
+// A workgroup computes `tr` whole output rows of one image (tr·ow <= 448 pixels) for 128 output
+// channels; the input window those rows need (hh × hw pixels, zero outside the image) is copied
+// into LDS once per 32-channel block and every filter tap reads it there.
+struct HaloParams {
+  ConvParams c;        // c.g.tiles_m = images × tiles per image, c.g.tiles_n = ceil(k / 128)
+  int tr, tpi;         // output rows per tile, tiles per image
+  int hh, hw, ns;      // window rows, columns, pixels (hh·hw)
+  int hat, hb;         // 1 KiB copy atoms per window image, its LDS bytes (hat·1024)
+  int cb32, rs;        // 32-channel blocks, filter taps
+  FastDiv div5, div_hw, div_ow;
+};
+
 hipError_t launch_im2col_copy(const DescIm2col& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
                               void* dst, hipStream_t stream);
 // Convolution with workgroup tile bm × bn (256×256, 256×128, 128×128 or 64×64); fills the grid.
 hipError_t launch_conv(ConvParams cp, int bm, int bn, int out_bf16, hipStream_t stream);
 bool conv_tile_built(int bm, int bn);
+// Fills the halo fields of `hp` from hp.c (shape fields set); false with `why` set when the shape
+// does not fit the halo kernel.  hs_out: window atoms each wave copies per filter tap (1..4).
+bool plan_conv_halo(HaloParams& hp, int* hs_out, const char** why);
+hipError_t launch_conv_halo(const HaloParams& hp, int hs, int out_bf16, hipStream_t stream);
 
 hipError_t launch_tiled_store(const DescImpl& d, const int32_t* host_coords, const int32_t* coords_dev, uint32_t n,
                               const void* src, hipStream_t stream);
