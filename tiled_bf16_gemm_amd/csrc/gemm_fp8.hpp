@@ -93,14 +93,15 @@ __device__ __forceinline__ void ktile8(f32x4_t (&acc)[T::FN][T::FM], Frags8<T>& 
   constexpr int P0 = H * FN, P1 = T::Products - P0, NR = FN + H;
 #pragma unroll
   for (int i = 0; i < P0; ++i) {
-    const int fm = i / FN, fn = i % FN;
-    if (fn == 0) cur.a[H + fm] = read_frag8(sCurA, fa.a_lane + (H + fm) * 2048, fa.a_col);
+    // serpentine over fn (as kstep in gemm_common.hpp): consecutive products share an operand
+    const int fm = i / FN, fn = (fm & 1) ? FN - 1 - i % FN : i % FN;
+    if (i % FN == 0) cur.a[H + fm] = read_frag8(sCurA, fa.a_lane + (H + fm) * 2048, fa.a_col);
     mfma8<T::AsmMfma, FMT>(acc[fn][fm], cur.b[fn], cur.a[fm]);
   }
   stage_barrier<0>();
 #pragma unroll
   for (int i = 0; i < P1; ++i) {
-    const int fm = H + i / FN, fn = i % FN;
+    const int fm = H + i / FN, fn = (fm & 1) ? FN - 1 - i % FN : i % FN;
     // fragment read q (B first, then A 0..H-1) before product (q * P1) / NR; atom j before (j * P1) / A
 #pragma unroll
     for (int q = (i * NR + P1 - 1) / P1; q < ((i + 1) * NR + P1 - 1) / P1 && q < NR; ++q) {
