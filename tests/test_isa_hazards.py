@@ -8,7 +8,14 @@ inside inline assembly, so a descriptor built with v_readfirstlane right before 
 is read stale, and a stale descriptor can address memory outside the operand.  This test compiles
 every kernel source (product build and hand-off checking build) to assembly and requires that no
 such load has a vector write of one of its scalar operands within the 5 preceding wait states
-(each instruction counts 1, s_nop N counts N + 1)."""
+(each instruction counts 1, s_nop N counts N + 1).
+
+The same listings also fix the ring's stage hand-off: the wait before each barrier of a barrier-ring
+kernel is an immediate built by hand (vmcnt split over bits 3:0 and 15:14), and a wrong field
+would let a barrier pass before its tile landed.  Every barrier of each ring instance must wait
+for vmcnt T·(S−1) (the prologue: tile 0 landed), T·(S−2) (the loop: tile kt+1 landed) or 0, with T
+the instance's copy atoms per wave and K tile and S its stages, and the hand-off checking build
+for 0 everywhere."""
 import concurrent.futures
 import os
 import re
@@ -98,6 +105,73 @@ def test_scan_flags_a_planted_hazard_and_passes_settled_code():
     assert len(scan(m0)) == 1
 
 
+RING = re.compile(r"^(_ZN3tbg16gemm_ring_kernelI((?:Li\d+E)+)EEvNS_10GemmParamsE):", re.M)
+
+
+def _vmcnt(ins):
+    """The vmcnt of an s_waitcnt instruction (None when it does not wait on vmcnt)."""
+    m = re.match(r"s_waitcnt\b.*\bvmcnt\((\d+)\)", ins)
+    return int(m.group(1)) if m else None
+
+
+def barrier_waits(text):
+    """Per barrier-ring kernel instance: (BM, BN, S, CLK) and the vmcnt of the nearest s_waitcnt
+    before each of its s_barrier instructions (None when none precedes it since the last barrier)."""
+    out = {}
+    heads = list(RING.finditer(text))
+    for i, h in enumerate(heads):
+        args = [int(a) for a in re.findall(r"Li(\d+)E", h.group(2))]
+        body = text[h.end():heads[i + 1].start() if i + 1 < len(heads) else len(text)]
+        end = body.find(".Lfunc_end")
+        ins = [t.strip().split(";")[0].strip() for t in body[:end if end >= 0 else len(body)].splitlines()]
+        ins = [t for t in ins if t and not t.startswith((".", "//")) and not t.endswith(":")]
+        waits = []
+        for j, t in enumerate(ins):
+            if t != "s_barrier":
+                continue
+            v = None
+            for prev in reversed(ins[max(0, j - 12):j]):
+                if prev == "s_barrier":
+                    break
+                if _vmcnt(prev) is not None:
+                    v = _vmcnt(prev)
+                    break
+            waits.append(v)
+        out[h.group(1)] = (args, waits)
+    return out
+
+
+def ring_wait_problems(text, check):
+    """Barriers of ring instances whose wait is not the intended count (see the module text)."""
+    problems = []
+    for name, (args, waits) in barrier_waits(text).items():
+        bm, bn, s = args[0], args[1], args[2]
+        atoms = bm // 32 + bn // 32
+        allowed = {0} if check else {0, atoms * (s - 2), atoms * (s - 1)}
+        bad = [w for w in waits if w not in allowed]
+        if bad:
+            problems.append(f"{name}: barrier waits {sorted(set(map(str, bad)))} outside {sorted(allowed)}")
+        if not check and not ({atoms * (s - 1), atoms * (s - 2)} <= set(waits)):
+            problems.append(f"{name}: no prologue or loop hand-off found among waits {sorted(set(map(str, waits)))}")
+    return problems
+
+
+def test_ring_wait_check_flags_wrong_counts():
+    """The checker itself on a small listing: the intended counts pass, a wait with a wrong count
+    or none at all is flagged, and the hand-off checking build accepts only 0."""
+    head = "_ZN3tbg16gemm_ring_kernelILi128ELi128ELi3ELi0ELi0ELi1ELi0ELi0EEEvNS_10GemmParamsE:\n"
+    good = head + ("s_waitcnt vmcnt(16) lgkmcnt(0)\ns_barrier\nv_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]\n"
+                   "s_waitcnt vmcnt(8) lgkmcnt(0)\nv_add_u32 v1, v1, v2\ns_barrier\n"
+                   "s_waitcnt vmcnt(0) lgkmcnt(0)\ns_barrier\n.Lfunc_end3:\n")
+    assert [a for a, _ in barrier_waits(good).values()] == [[128, 128, 3, 0, 0, 1, 0, 0]]
+    assert ring_wait_problems(good, 0) == []
+    assert ring_wait_problems(good, 1) != []
+    assert ring_wait_problems(good.replace("vmcnt(8)", "vmcnt(12)"), 0) != []
+    assert ring_wait_problems(good.replace("s_waitcnt vmcnt(8) lgkmcnt(0)\n", ""), 0) != []
+    drained = re.sub(r"vmcnt\(\d+\)", "vmcnt(0)", good)
+    assert ring_wait_problems(drained, 1) == []
+
+
 def _compile(src, check):
     out = tempfile.NamedTemporaryFile(suffix=".s", delete=False).name
     cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wno-unused-command-line-argument",
@@ -106,24 +180,30 @@ def _compile(src, check):
     r = subprocess.run(cmd, capture_output=True, text=True)
     try:
         if r.returncode != 0:
-            return src, check, None, r.stderr[-2000:]
+            return src, check, None, r.stderr[-2000:], []
         with open(out) as f:
-            return src, check, scan(f.read()), ""
+            text = f.read()
+        return src, check, scan(text), "", ring_wait_problems(text, check)
     finally:
         os.unlink(out)
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
-def test_inline_buffer_loads_have_settled_scalar_operands():
+def test_inline_buffer_loads_have_settled_scalar_operands_and_ring_waits():
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     jobs = [(s, c) for s in srcs for c in (0, 1)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         results = list(ex.map(lambda j: _compile(*j), jobs))
     problems = []
-    for src, check, found, err in results:
+    rings = 0
+    for src, check, found, err, waits in results:
+        problems += [f"{os.path.basename(src)} (hand-off check {check}): {w}" for w in waits]
+        if os.path.basename(src).startswith("gemm_ring_") and found is not None:
+            rings += 1
         name = f"{os.path.basename(src)} (hand-off check {check})"
         if found is None:
             problems.append(f"{name}: hipcc failed: {err}")
         for load, prev, ws in found or []:
             problems.append(f"{name}: {load!r} after {prev!r} ({ws} wait states)")
+    assert rings == 8, "every ring source compiled in both builds"
     assert not problems, "\n".join(problems[:20])
