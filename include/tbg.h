@@ -411,9 +411,22 @@ size_t tbg_conv2d_workspace_query(const tbg_conv2d_shape* shape, const void* x, 
  *              workspace's halves, as for tbg_gemm).
  *   y          fp32 or bf16 device memory, (N*OH*OW) rows of ldy >= k elements; only the first k
  *              of each row are written.
- *   cfg        NULL (the library's choice) or a tbg_gemm_config with pipeline AUTO or RING, stages
- *              0 or 2 and tile 0x0, 256x256, 256x128, 128x128 or 64x64 (else UNSUPPORTED);
- *              every tile gives bit-identical results.
+ *   cfg        NULL (the library's choice) or a tbg_gemm_config with pipeline AUTO or RING and
+ *              one of:
+ *                tile 0x0, 256x256, 256x128, 128x128 or 64x64, stages 0 or 2: the im2col
+ *                kernels, whose sums run tap by tap with 64 channels inside; these tiles give
+ *                bit-identical results;
+ *                tile 448x128, stages 0 or 4: the halo kernel (stride 1 and r*s >= 2 only; c a
+ *                multiple of 32 and x, w 16-byte aligned, so nothing is repacked; OW <= 448; an
+ *                input window of at most 806 pixels that four 1 KiB copies per wave and tap
+ *                bring in time), which copies each input window into LDS once per
+ *                32-channel block for all taps.  Its sums run block by block, tap by tap inside
+ *                a block, so its results may differ from the im2col tiles' in rounding (both are
+ *                fp32 sums of the same exact products; small-integer inputs give equal bits);
+ *              anything else is UNSUPPORTED.  With cfg NULL or tile 0x0 the library takes the
+ *              halo kernel where it applies, its tiles use at least 3/4 of their 448 rows and
+ *              there are at least half as many tiles as compute units; else an im2col tile by
+ *              the GEMM's cost model.
  * Limits: h, w below 2^16; N*OH*OW and k below 2^31; X (with its channel pitch rounded up to 8)
  * below 2 GiB; r*s*c below 2^22; filter, stride, dilation up to 256; padding up to 65535.
  * Returns INVALID_VALUE (bad shape, ldy < k, null pointers, y type), UNSUPPORTED (limits),
