@@ -131,7 +131,7 @@ def test_conv_workloads(ops, orc, name):
             assert np.array_equal(got[:, :w.k], base[:, :w.k]), "tiles disagree"
 
 
-HALO = ["conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_dil2"]
+HALO = ["conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_dil2", "conv_halo_c96"]
 
 
 @gpu
@@ -140,8 +140,9 @@ def test_conv_halo_kernel(ops, orc, name):
     """The halo kernel (tile 448x128: stride 1, the input window copied once per 32-channel
     block) in full against the oracle for both output types, bit for bit on small integers, with
     the output rows padded and left untouched past K.  These layers cover partial last tiles of
-    an image, output channels past a multiple of 128, dilation, asymmetric padding and one to
-    four window atoms per wave and tap.  (Its sums run in another order than the im2col tiles',
+    an image, output channels past a multiple of 128, dilation, asymmetric padding, one to
+    four window atoms per wave and tap, and (3×3 filters, the unrolled nine-tap loop) one, two
+    and three 32-channel blocks.  (Its sums run in another order than the im2col tiles',
     so only the oracle decides.)"""
     import tiled_bf16_gemm_amd as tbg
     w = workloads.CONVS[name]

@@ -5,7 +5,8 @@ gfx9 needs 5 wait states between a vector instruction that writes a scalar regis
 v_readfirstlane_b32) and a vector-memory instruction that reads that register (the buffer
 descriptor, M0).  The compiler inserts them in front of its own memory instructions but cannot see
 inside inline assembly, so a descriptor built with v_readfirstlane right before an asm buffer load
-is read stale, and a stale descriptor can address memory outside the operand.  This test compiles
+is read stale, and a stale descriptor can address memory outside the operand.  The load's
+scalar offset register, where it has one, counts as one of its scalar operands.  This test compiles
 every kernel source (product build and hand-off checking build) to assembly and requires that no
 such load has a vector write of one of its scalar operands within the 5 preceding wait states
 (each instruction counts 1, s_nop N counts N + 1).
@@ -77,7 +78,7 @@ def scan(text):
         if ops[1].startswith("v"):
             found.append((t, "descriptor in vector registers", 0))
             continue
-        need = _sregs(ops[1]) | {"m0"}
+        need = _sregs(ops[1]) | {"m0"} | (_sregs(ops[2].split()[0]) if len(ops) > 2 else set())
         ws = 0
         for prev in reversed(ins[max(0, i - 8):i]):
             if _vector_sgpr_writes(prev) & need:
@@ -103,6 +104,10 @@ def test_scan_flags_a_planted_hazard_and_passes_settled_code():
     assert scan(far) == []
     m0 = "v_readfirstlane_b32 m0, v3\n buffer_load_dwordx4 v1, s[40:43], 0 offen lds\n"
     assert len(scan(m0)) == 1
+    so = "v_readlane_b32 s7, v9, 3\n buffer_load_dwordx4 v1, s[40:43], s7 offen lds\n"
+    assert len(scan(so)) == 1
+    so_ok = "v_readlane_b32 s7, v9, 3\n buffer_load_dwordx4 v1, s[40:43], s8 offen lds\n"
+    assert scan(so_ok) == []
 
 
 RING = re.compile(r"^(_ZN3tbg16gemm_ring_kernelI((?:Li\d+E)+)EEvNS_10GemmParamsE):", re.M)

@@ -61,23 +61,38 @@ bool plan_conv_halo(HaloParams& hp, int* hs_out, const char** why) {
   hp.div5 = make_fast_div(5);
   hp.div_hw = make_fast_div((uint32_t)hw);
   hp.div_ow = make_fast_div((uint32_t)c.ow);
+  for (int v = 0; v < 9; ++v)
+    hp.tap_off[v] = v < rs ? (int)(((int64_t)(v / c.s) * c.dh * hw + (int64_t)(v % c.s) * c.dw) * kHaloPitch) : 0;
   hp.c.g.tiles_m = (int)tiles_m;
   hp.c.g.tiles_n = (int)tiles_n;
   *hs_out = (int)hs;
   return true;
 }
 
-template <int HS>
-static hipError_t launch_halo_hs(const HaloParams& hp, int out_bf16, hipStream_t stream) {
+template <int HS, int TAPS>
+static hipError_t launch_halo_taps(const HaloParams& hp, int out_bf16, hipStream_t stream) {
   const unsigned grid = (unsigned)hp.c.g.tiles_m * (unsigned)hp.c.g.tiles_n;
   if (hp.c.g.scaled) {
-    if (out_bf16) hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 1, 1>), dim3(grid), dim3(kThreads), 0, stream, hp);
-    else hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 0, 1>), dim3(grid), dim3(kThreads), 0, stream, hp);
+    if (out_bf16)
+      hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 1, 1, TAPS>), dim3(grid), dim3(kThreads), 0, stream, hp);
+    else
+      hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 0, 1, TAPS>), dim3(grid), dim3(kThreads), 0, stream, hp);
   } else {
-    if (out_bf16) hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 1, 0>), dim3(grid), dim3(kThreads), 0, stream, hp);
-    else hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 0, 0>), dim3(grid), dim3(kThreads), 0, stream, hp);
+    if (out_bf16)
+      hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 1, 0, TAPS>), dim3(grid), dim3(kThreads), 0, stream, hp);
+    else
+      hipLaunchKernelGGL((gemm_conv_halo_kernel<HS, 0, 0, TAPS>), dim3(grid), dim3(kThreads), 0, stream, hp);
   }
   return hipGetLastError();
+}
+
+// Filters of nine taps (3×3 and the like) run the kernel whose block of taps is unrolled.  With
+// nine taps a window of at most 63 atoms needs at most two atoms per wave and tap.
+template <int HS>
+static hipError_t launch_halo_hs(const HaloParams& hp, int out_bf16, hipStream_t stream) {
+  if constexpr (HS <= 2)
+    if (hp.rs == 9) return launch_halo_taps<HS, 9>(hp, out_bf16, stream);
+  return launch_halo_taps<HS, 0>(hp, out_bf16, stream);
 }
 
 hipError_t launch_conv_halo(const HaloParams& hp, int hs, int out_bf16, hipStream_t stream) {

@@ -66,12 +66,26 @@ __device__ __forceinline__ void issue_atom_settled(rsrc_t rs, uint32_t lds_base,
                : "memory");
 }
 
+// A direct-to-LDS atom whose source is voff + soff bytes into the buffer: soff (uniform) carries
+// what is the same for every lane, here a channel block's or a filter column's offset.
+// Offsets with bit 31 set stay out of the buffer's range with the scalar offset added (it is
+// below 2^31), so those lanes still land zeros.
+__device__ __forceinline__ void issue_atom_so(rsrc_t rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
 struct HaloFrags {
   bf16x8_t a[kHaloFM];
   bf16x8_t b[kHaloFN];
 };
 
-template <int HS, int OUT, int SCALED>
+// TAPS 0: any filter, the step's tap and channel block kept in counters.  TAPS 9: filters of nine
+// taps (r·s == 9), one block of taps unrolled: every tap offset, copy position and wait count is
+// a compile-time choice, and each window atom reuses per-lane offsets computed once.
+template <int HS, int OUT, int SCALED, int TAPS = 0>
 __global__ void __launch_bounds__(kThreads, 1) gemm_conv_halo_kernel(HaloParams hp) {
   using T = HaloTile<OUT, SCALED>;
   const ConvParams& cp = hp.c;
@@ -269,16 +283,116 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_conv_halo_kernel(HaloParams 
     step_rd();
   };
 
-  int t = 0;
-  for (; t + 4 <= steps; t += 4) {
-    step(std::integral_constant<int, 0>{}, f0, f1);
-    step(std::integral_constant<int, 1>{}, f1, f0);
-    step(std::integral_constant<int, 2>{}, f0, f1);
-    step(std::integral_constant<int, 3>{}, f1, f0);
+  if constexpr (TAPS == 0) {
+    int t = 0;
+    for (; t + 4 <= steps; t += 4) {
+      step(std::integral_constant<int, 0>{}, f0, f1);
+      step(std::integral_constant<int, 1>{}, f1, f0);
+      step(std::integral_constant<int, 2>{}, f0, f1);
+      step(std::integral_constant<int, 3>{}, f1, f0);
+    }
+    if (t < steps) step(std::integral_constant<int, 0>{}, f0, f1);
+    if (t + 1 < steps) step(std::integral_constant<int, 1>{}, f1, f0);
+    if (t + 2 < steps) step(std::integral_constant<int, 2>{}, f0, f1);
+  } else {
+    // The same steps, copies and waits as above, with the taps of a block unrolled.  Window
+    // offsets of this wave's atoms at every copy position of a block, for channel block 0 (a
+    // block's 64-byte channel offset goes in as the atom's scalar offset): a position's atoms
+    // cover the same pixels in every block.  Units outside the image or the window get exactly
+    // 2^31.
+    static_assert(TAPS >= 4, "a filter tile four steps ahead lies at most one block ahead");
+    uint32_t woff[TAPS - 1][HS];
+#pragma unroll
+    for (int u = 0; u < TAPS - 1; ++u)
+#pragma unroll
+      for (int j = 0; j < HS; ++j) {
+        const uint32_t o = halo_src((u * 4 + wave) * HS + j, 0);
+        woff[u][j] = (o & kOobOffset) ? kOobOffset : o;
+      }
+    const uint32_t junk = smem_addr + (uint32_t)kHaloJunk;
+    const uint32_t c8x2 = (uint32_t)cp.c8 * 2u;
+    // Step t = cb·TAPS + K (K a compile-time tap index): the products on `cur`, the fragments of
+    // step t+1 into `nxt`, filter tile t+4 into stage t % 4, and the window atoms of copy
+    // position K+1 of block cb+1 (K <= TAPS-3), none (K = TAPS-2: atoms of zeros into the spare
+    // one) or position 0 of block cb+2 (K = TAPS-1), as the counters of the general loop give.
+    auto step_t = [&](auto kc, const HaloFrags& cur, HaloFrags& nxt, int cb, int t) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value;
+      if constexpr (K == TAPS - 1)
+        stage_barrier<2 + HS>();  // step t+1 opens block cb+1: its whole window has landed
+      else
+        stage_barrier<4 + 3 * HS>();
+      const int nblk = K == TAPS - 1 ? cb + 1 : cb;
+      const uint32_t hA = (uint32_t)kHaloOff0 + (uint32_t)(nblk & 1) * (uint32_t)hp.hb +
+                          (uint32_t)hp.tap_off[K == TAPS - 1 ? 0 : K + 1];
+      const uint32_t vB = b0 + (uint32_t)((t + 1) & 3) * (uint32_t)kHaloBStage;
+      constexpr int FB = (K + 4) / TAPS, FT = (K + 4) % TAPS;  // filter tile t+4: block cb+FB, tap FT
+      // (a tile past the last block re-reads block 0's first tile into a stage nobody reads again)
+      const uint32_t fcol = cb + FB < cb32 ? (uint32_t)FT * c8x2 + (uint32_t)(cb + FB) * 64u : 0u;
+      const uint32_t fst = smem_addr + (uint32_t)(t & 3) * (uint32_t)kHaloBStage;
+      constexpr int WP = K <= TAPS - 3 ? K + 1 : (K == TAPS - 1 ? 0 : -1);
+      const int wblk = K == TAPS - 1 ? cb + 2 : cb + 1;
+      const int lim = WP >= 0 && wblk < cb32 ? hp.hat : 0;  // atoms below lim are real
+      // (a block past the last copies block 0's channels, into the spare atom)
+      const uint32_t wsoff = lim ? (uint32_t)wblk * 64u : 0u;
+      const uint32_t wbase = smem_addr + (uint32_t)kHaloOff0 + (uint32_t)(wblk & 1) * (uint32_t)hp.hb;
+      constexpr int P = kHaloFM * kHaloFN, RD = kHaloFM + kHaloFN, CP = 2 + HS, H = P / (2 * CP);
+      for_stages<P>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int r = (i * RD + P - 1) / P;
+        if constexpr (r < ((i + 1) * RD + P - 1) / P) {
+          if constexpr (r < kHaloFM)
+            nxt.a[r] = *(const bf16x8_t*)(smem + hA + a0[r]);
+          else
+            nxt.b[r - kHaloFM] = *(const bf16x8_t*)(smem + vB + (r - kHaloFM) * 1024);
+        }
+        if constexpr (i >= H) {
+          constexpr int j = ((i - H) * CP + P - 1) / P;
+          if constexpr (j < ((i + 1 - H) * CP + P - 1) / P) {
+            if constexpr (j == 0) {
+              issue_atom_so(rw, fst + (uint32_t)(2 * wave) * 1024u, ob[0], fcol);
+              issue_atom_so(rw, fst + (uint32_t)(2 * wave + 1) * 1024u, ob[1], fcol);
+            }
+            if constexpr (j >= 2) {
+              if constexpr (WP < 0) {
+                issue_atom_so(rx, junk, kOobOffset, 0u);
+              } else {
+                const int a = (WP * 4 + wave) * HS + (j - 2);
+                const uint32_t place = wbase + (uint32_t)a * 1024u;
+                uint32_t lds;
+                // (a scalar select written out: the compiler would branch on the uniform test)
+                asm("s_cmp_lt_i32 %1, %2\n\ts_cselect_b32 %0, %3, %4"
+                    : "=s"(lds)
+                    : "s"(a), "s"(lim), "s"(place), "s"(junk)
+                    : "scc");
+                issue_atom_so(rx, lds, woff[WP][j - 2], wsoff);
+              }
+            }
+          }
+        }
+        // serpentine over the fragment grid (as the GEMM's k-step): consecutive products share
+        // an operand
+        constexpr int fn = i / kHaloFM, fm = (fn & 1) ? kHaloFM - 1 - i % kHaloFM : i % kHaloFM;
+        mfma16<true, 0>(acc[fn][fm], cur.b[fn], cur.a[fm]);
+      });
+    };
+    // Two blocks per iteration keep each step's fragment sets (f0 at even steps) compile-time.
+    auto block = [&](auto odd, int cb) __attribute__((always_inline)) {
+      const int t0 = cb * TAPS;
+      for_stages<TAPS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int K = decltype(kc)::value;
+        if constexpr ((decltype(odd)::value * TAPS + K) % 2 == 0)
+          step_t(kc, f0, f1, cb, t0 + K);
+        else
+          step_t(kc, f1, f0, cb, t0 + K);
+      });
+    };
+    int cb = 0;
+    for (; cb + 2 <= cb32; cb += 2) {
+      block(std::false_type{}, cb);
+      block(std::true_type{}, cb + 1);
+    }
+    if (cb < cb32) block(std::false_type{}, cb);
   }
-  if (t < steps) step(std::integral_constant<int, 0>{}, f0, f1);
-  if (t + 1 < steps) step(std::integral_constant<int, 1>{}, f1, f0);
-  if (t + 2 < steps) step(std::integral_constant<int, 2>{}, f0, f1);
 
   drain_acc<T>(acc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -137,13 +137,16 @@ CONVS = {
     "conv_stem": ConvWorkload("conv_stem", 2, 32, 32, 3, 64, 7, 7, (3, 3, 3, 3), (2, 2), seed=6010),
     "conv_b": ConvWorkload("conv_b", 32, 56, 56, 128, 128, 3, 3, (1, 1, 1, 1), seed=6012),
     # stride-1 layers for the halo kernel: tiles of whole output rows, the last one of an image
-    # partial, output channels past a multiple of 128, 1..4 window atoms per wave and tap
+    # partial, output channels past a multiple of 128, 1..4 window atoms per wave and tap; 3×3
+    # filters (the unrolled nine-tap loop) over one, two and three 32-channel blocks
     "conv_halo_rows": ConvWorkload("conv_halo_rows", 2, 30, 30, 64, 160, 3, 3, (1, 1, 1, 1), out_dtype="f32",
                                    seed=6014),
     "conv_halo_wide": ConvWorkload("conv_halo_wide", 3, 9, 100, 96, 64, 3, 2, (1, 0, 1, 1), seed=6016),
     "conv_halo_small": ConvWorkload("conv_halo_small", 4, 8, 8, 32, 48, 3, 3, (1, 1, 1, 1), out_dtype="f32",
                                     seed=6018),
     "conv_halo_1x3": ConvWorkload("conv_halo_1x3", 2, 12, 24, 32, 40, 1, 3, (0, 1, 0, 1), seed=6020),
+    "conv_halo_c96": ConvWorkload("conv_halo_c96", 2, 20, 20, 96, 72, 3, 3, (1, 1, 1, 1), out_dtype="f32",
+                                  seed=6022),
 }
 
 
