@@ -29,13 +29,17 @@ __global__ void __launch_bounds__(256, 1) mfma_rate_kernel(const i32x4_t* src, f
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime(), m0 = __builtin_amdgcn_s_memtime();
+  // The fragment grid is walked in serpentine order, as the GEMM's k-step walks it: consecutive
+  // products share one operand register (the order of least operand toggling, so of least energy).
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       if (KIND == 0) {
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i]) : "v"(v[i & 7]), "v"(v[8 + (i >> 3)]));
+        const int x = ((i >> 3) & 1) ? 7 - (i & 7) : (i & 7);
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i]) : "v"(v[x]), "v"(v[8 + (i >> 3)]));
       } else {
-        const i32x8_t a = __builtin_shufflevector(v[2 * (i & 3)], v[2 * (i & 3) + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const int x = ((i >> 2) & 1) ? 3 - (i & 3) : (i & 3);
+        const i32x8_t a = __builtin_shufflevector(v[2 * x], v[2 * x + 1], 0, 1, 2, 3, 4, 5, 6, 7);
         const i32x8_t b = __builtin_shufflevector(v[8 + 2 * ((i >> 2) & 3)], v[9 + 2 * ((i >> 2) & 3)], 0, 1, 2, 3, 4,
                                                   5, 6, 7);
         asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc[i]) : "v"(a), "v"(b));
