@@ -16,7 +16,12 @@ kernel is an immediate built by hand (vmcnt split over bits 3:0 and 15:14), and 
 would let a barrier pass before its tile landed.  Every barrier of each ring instance must wait
 for vmcnt T·(S−1) (the prologue: tile 0 landed), T·(S−2) (the loop: tile kt+1 landed) or 0, with T
 the instance's copy atoms per wave and K tile and S its stages, and the hand-off checking build
-for 0 everywhere."""
+for 0 everywhere.  Those counts hold only if the copy atoms are the only vector-memory instructions
+a wave has in flight before its drain: in every ring and halo-convolution instance, no other
+vector-memory instruction (a load or store of the compiler's, a register spill) may be reachable
+from the kernel's entry without passing a full drain (`vmcnt(0)` and a barrier), walked over the
+listing's basic blocks and branches, since the blocks' order in the listing is not the order they
+run in."""
 import concurrent.futures
 import os
 import re
@@ -177,6 +182,120 @@ def test_ring_wait_check_flags_wrong_counts():
     assert ring_wait_problems(drained, 1) == []
 
 
+KERNEL = re.compile(r"^(_ZN3tbg(?:16gemm_ring_kernel|21gemm_conv_halo_kernel)I\w+):", re.M)
+
+
+def _blocks(lines):
+    """Basic blocks of one kernel's listing: [label or None, [instructions]] in listing order."""
+    blocks, cur = [], [None, []]
+    for raw in lines:
+        t = raw.split(";")[0].strip()
+        if not t or t.startswith("//"):
+            continue
+        m = re.match(r"^(\.LBB\d+_\d+):", t)
+        if m:
+            blocks.append(cur)
+            cur = [m.group(1), []]
+            continue
+        if t.startswith("."):
+            continue
+        cur[1].append(t)
+        if re.match(r"s_(c?branch|endpgm)", t):
+            blocks.append(cur)
+            cur = [None, []]
+    blocks.append(cur)
+    return [b for b in blocks if b[0] is not None or b[1]]
+
+
+def early_vmem(lines):
+    """Walk the blocks reachable from the entry without passing a full drain (an s_waitcnt with
+    vmcnt(0) followed by s_barrier).  Returns the vector-memory instructions met there that are not
+    direct-to-LDS copy atoms, the number of copy atoms met and the number of barriers met whose
+    wait leaves copies in flight."""
+    bl = _blocks(lines)
+    at = {b[0]: i for i, b in enumerate(bl) if b[0]}
+
+    def succ(i):
+        last = bl[i][1][-1] if bl[i][1] else ""
+        m = re.match(r"s_branch (\.LBB\d+_\d+)", last)
+        if m:
+            return [at[m.group(1)]]
+        if last.startswith("s_endpgm"):
+            return []
+        out = []
+        m = re.match(r"s_cbranch_\w+ (\.LBB\d+_\d+)", last)
+        if m:
+            out.append(at[m.group(1)])
+        return out + ([i + 1] if i + 1 < len(bl) else [])
+
+    seen, todo, bad, copies, open_barriers = set(), [0], [], 0, 0
+    while todo:
+        i = todo.pop()
+        if i in seen:
+            continue
+        seen.add(i)
+        ins, stop = bl[i][1], False
+        for j, t in enumerate(ins):
+            if t == "s_barrier":
+                open_barriers += 1
+            v = _vmcnt(t)
+            if v == 0 and "s_barrier" in ins[j + 1:j + 4]:
+                stop = True
+                break
+            if re.match(r"(buffer|global|flat|scratch)_", t):
+                if t.startswith("buffer_load_dwordx4") and t.endswith(" lds"):
+                    copies += 1
+                else:
+                    bad.append(t)
+        if not stop:
+            todo += succ(i)
+    return bad, copies, open_barriers
+
+
+def early_vmem_problems(text, check):
+    problems = []
+    heads = list(KERNEL.finditer(text))
+    for i, h in enumerate(heads):
+        body = text[h.end():heads[i + 1].start() if i + 1 < len(heads) else len(text)]
+        end = body.find(".Lfunc_end")
+        bad, copies, barriers = early_vmem(body[:end if end >= 0 else len(body)].splitlines())
+        if bad:
+            problems.append(f"{h.group(1)}: {bad[:3]} before the drain")
+        # (in the hand-off checking build every barrier drains: there the walk ends at the first)
+        if copies == 0 or (barriers == 0 and not check):
+            problems.append(f"{h.group(1)}: the walk met {copies} copy atoms and {barriers} barriers before the drain")
+    return problems
+
+
+def test_early_vmem_walk_flags_loads_among_the_copies():
+    """The walk on small listings: a compiler load inside the K loop (before a barrier that leaves
+    copies in flight) is flagged, and so is a register spill; the same load after the drain is not,
+    nor an epilogue block laid out in the listing ahead of the loop's remainder block but reached
+    only after the drain, while a branch that falls through into the epilogue before the drain
+    is."""
+    copy = "buffer_load_dwordx4 v1, s[8:11], 0 offen lds"
+    loop = [".LBB0_1:", copy, "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]",
+            "s_waitcnt vmcnt(8) lgkmcnt(0)", "s_barrier", "s_cbranch_scc1 .LBB0_1"]
+    drain = ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_barrier"]
+    store = "global_store_dwordx4 v[2:3], v[4:7], off nt"
+    load = "global_load_dword v9, v[2:3], off"
+    ok = [copy] + loop + drain + [store, "s_endpgm"]
+    assert early_vmem(ok) == ([], 2, 1)
+    planted = [copy] + loop[:2] + [load] + loop[2:] + drain + [store, "s_endpgm"]
+    assert early_vmem(planted)[0] == [load]
+    spill = [copy, "scratch_store_dword off, v5, s0 offset:16"] + loop + drain + ["s_endpgm"]
+    assert early_vmem(spill)[0] == ["scratch_store_dword off, v5, s0 offset:16"]
+    # listing order: loop, then an epilogue block, then the remainder block that jumps back to it
+    laid_out = [copy] + loop + ["s_branch .LBB0_3", ".LBB0_2:", store, "s_endpgm", ".LBB0_3:", copy,
+                                "s_waitcnt vmcnt(4) lgkmcnt(0)", "s_barrier"] + drain + ["s_branch .LBB0_2"]
+    assert early_vmem(laid_out)[0] == []
+    falls = [copy] + loop + ["s_cbranch_scc0 .LBB0_3", ".LBB0_2:", store, "s_endpgm", ".LBB0_3:"] + drain + \
+        ["s_branch .LBB0_2"]
+    assert early_vmem(falls)[0] == [store]
+    leaked = laid_out[:laid_out.index(".LBB0_3:") + 1] + [load] + laid_out[laid_out.index(".LBB0_3:") + 1:]
+    assert early_vmem(leaked)[0] == [load]
+
+
 def _compile(src, check):
     out = tempfile.NamedTemporaryFile(suffix=".s", delete=False).name
     cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wno-unused-command-line-argument",
@@ -188,7 +307,7 @@ def _compile(src, check):
             return src, check, None, r.stderr[-2000:], []
         with open(out) as f:
             text = f.read()
-        return src, check, scan(text), "", ring_wait_problems(text, check)
+        return src, check, scan(text), "", ring_wait_problems(text, check) + early_vmem_problems(text, check)
     finally:
         os.unlink(out)
 
