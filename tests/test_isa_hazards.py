@@ -17,7 +17,8 @@ would let a barrier pass before its tile landed.  Every barrier of each ring ins
 for vmcnt T·(S−1) (the prologue: tile 0 landed), T·(S−2) (the loop: tile kt+1 landed) or 0, with T
 the instance's copy atoms per wave and K tile and S its stages, and the hand-off checking build
 for 0 everywhere.  Those counts hold only if the copy atoms are the only vector-memory instructions
-a wave has in flight before its drain: in every ring and halo-convolution instance, no other
+a wave has in flight before its drain: in every barrier-ring, fp8, im2col- and halo-convolution
+instance (the kernels whose waves all copy and compute), no other
 vector-memory instruction (a load or store of the compiler's, a register spill) may be reachable
 from the kernel's entry without passing a full drain (`vmcnt(0)` and a barrier), walked over the
 listing's basic blocks and branches, since the blocks' order in the listing is not the order they
@@ -182,7 +183,8 @@ def test_ring_wait_check_flags_wrong_counts():
     assert ring_wait_problems(drained, 1) == []
 
 
-KERNEL = re.compile(r"^(_ZN3tbg(?:16gemm_ring_kernel|21gemm_conv_halo_kernel)I\w+):", re.M)
+KERNEL = re.compile(r"^(_ZN3tbg(?:16gemm_ring_kernel|21gemm_conv_halo_kernel|15gemm_fp8_kernel|16gemm_conv_kernel)I\w+):",
+                    re.M)
 
 
 def _blocks(lines):
