@@ -22,7 +22,9 @@ instance (the kernels whose waves all copy and compute), no other
 vector-memory instruction (a load or store of the compiler's, a register spill) may be reachable
 from the kernel's entry without passing a full drain (`vmcnt(0)` and a barrier), walked over the
 listing's basic blocks and branches, since the blocks' order in the listing is not the order they
-run in."""
+run in.  The same walk requires every vmcnt wait met there to be a barrier's (or a vmcnt(0) that
+settles the copies right before the drain): a wait the compiler places for loads of its own counts
+the copies too and would hold them back without any sign but time."""
 import concurrent.futures
 import os
 import re
@@ -209,11 +211,37 @@ def _blocks(lines):
     return [b for b in blocks if b[0] is not None or b[1]]
 
 
+def _guarded_barrier(ins, j):
+    """Whether the s_waitcnt at ins[j] is the wait of a barrier: an s_barrier follows within 12
+    instructions with no other vmcnt wait in between."""
+    for t in ins[j + 1:j + 13]:
+        if t == "s_barrier":
+            return True
+        if _vmcnt(t) is not None:
+            return False
+    return False
+
+
+def _settles_drain(ins, j):
+    """Whether the wait at ins[j] only settles the copies right before the drain: the next vmcnt
+    wait, within 12 instructions and with no memory instruction or product in between, is a
+    barrier's vmcnt(0)."""
+    for k in range(j + 1, min(j + 13, len(ins))):
+        t = ins[k]
+        if _vmcnt(t) is not None:
+            return _vmcnt(t) == 0 and _guarded_barrier(ins, k)
+        if re.match(r"(buffer|global|flat|scratch|ds)_|v_mfma", t):
+            return False
+    return False
+
+
 def early_vmem(lines):
     """Walk the blocks reachable from the entry without passing a full drain (an s_waitcnt with
-    vmcnt(0) followed by s_barrier).  Returns the vector-memory instructions met there that are not
-    direct-to-LDS copy atoms, the number of copy atoms met and the number of barriers met whose
-    wait leaves copies in flight."""
+    vmcnt(0) that is a barrier's wait).  Returns the vector-memory instructions met there that are
+    not direct-to-LDS copy atoms, the number of copy atoms met, the number of barriers met (each
+    leaving copies in flight) and the vmcnt waits met that are no barrier's wait (a wait the
+    compiler placed for loads it cannot tell apart from the copies would hold them back), except a
+    vmcnt(0) right before the drain."""
     bl = _blocks(lines)
     at = {b[0]: i for i, b in enumerate(bl) if b[0]}
 
@@ -230,7 +258,7 @@ def early_vmem(lines):
             out.append(at[m.group(1)])
         return out + ([i + 1] if i + 1 < len(bl) else [])
 
-    seen, todo, bad, copies, open_barriers = set(), [0], [], 0, 0
+    seen, todo, bad, copies, barriers, stray = set(), [0], [], 0, 0, []
     while todo:
         i = todo.pop()
         if i in seen:
@@ -239,11 +267,15 @@ def early_vmem(lines):
         ins, stop = bl[i][1], False
         for j, t in enumerate(ins):
             if t == "s_barrier":
-                open_barriers += 1
+                barriers += 1
             v = _vmcnt(t)
-            if v == 0 and "s_barrier" in ins[j + 1:j + 4]:
-                stop = True
-                break
+            if v is not None:
+                if _guarded_barrier(ins, j):
+                    if v == 0:
+                        stop = True
+                        break
+                elif not (v == 0 and _settles_drain(ins, j)):
+                    stray.append(t)
             if re.match(r"(buffer|global|flat|scratch)_", t):
                 if t.startswith("buffer_load_dwordx4") and t.endswith(" lds"):
                     copies += 1
@@ -251,7 +283,7 @@ def early_vmem(lines):
                     bad.append(t)
         if not stop:
             todo += succ(i)
-    return bad, copies, open_barriers
+    return bad, copies, barriers, stray
 
 
 def early_vmem_problems(text, check):
@@ -260,9 +292,11 @@ def early_vmem_problems(text, check):
     for i, h in enumerate(heads):
         body = text[h.end():heads[i + 1].start() if i + 1 < len(heads) else len(text)]
         end = body.find(".Lfunc_end")
-        bad, copies, barriers = early_vmem(body[:end if end >= 0 else len(body)].splitlines())
+        bad, copies, barriers, stray = early_vmem(body[:end if end >= 0 else len(body)].splitlines())
         if bad:
             problems.append(f"{h.group(1)}: {bad[:3]} before the drain")
+        if stray:
+            problems.append(f"{h.group(1)}: vmcnt waits {stray[:3]} that no barrier follows, before the drain")
         # (in the hand-off checking build every barrier drains: there the walk ends at the first)
         if copies == 0 or (barriers == 0 and not check):
             problems.append(f"{h.group(1)}: the walk met {copies} copy atoms and {barriers} barriers before the drain")
@@ -274,7 +308,7 @@ def test_early_vmem_walk_flags_loads_among_the_copies():
     copies in flight) is flagged, and so is a register spill; the same load after the drain is not,
     nor an epilogue block laid out in the listing ahead of the loop's remainder block but reached
     only after the drain, while a branch that falls through into the epilogue before the drain
-    is."""
+    is; a vmcnt wait that guards no barrier is reported."""
     copy = "buffer_load_dwordx4 v1, s[8:11], 0 offen lds"
     loop = [".LBB0_1:", copy, "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]",
             "s_waitcnt vmcnt(8) lgkmcnt(0)", "s_barrier", "s_cbranch_scc1 .LBB0_1"]
@@ -282,7 +316,7 @@ def test_early_vmem_walk_flags_loads_among_the_copies():
     store = "global_store_dwordx4 v[2:3], v[4:7], off nt"
     load = "global_load_dword v9, v[2:3], off"
     ok = [copy] + loop + drain + [store, "s_endpgm"]
-    assert early_vmem(ok) == ([], 2, 1)
+    assert early_vmem(ok) == ([], 2, 1, [])
     planted = [copy] + loop[:2] + [load] + loop[2:] + drain + [store, "s_endpgm"]
     assert early_vmem(planted)[0] == [load]
     spill = [copy, "scratch_store_dword off, v5, s0 offset:16"] + loop + drain + ["s_endpgm"]
@@ -294,6 +328,14 @@ def test_early_vmem_walk_flags_loads_among_the_copies():
     falls = [copy] + loop + ["s_cbranch_scc0 .LBB0_3", ".LBB0_2:", store, "s_endpgm", ".LBB0_3:"] + drain + \
         ["s_branch .LBB0_2"]
     assert early_vmem(falls)[0] == [store]
+    # a wait of the compiler's at the loop head (no barrier follows it) is flagged; the kernel's own
+    # vmcnt(0) right before the drain is not
+    throttled = [copy, loop[0], "s_waitcnt vmcnt(1)"] + loop[1:] + drain + [store, "s_endpgm"]
+    assert early_vmem(throttled)[3] == ["s_waitcnt vmcnt(1)"]
+    settle = [copy] + loop + ["s_waitcnt vmcnt(0)", "v_cvt_pk_bf16_f32 v21, v21, v30"] + drain + [store, "s_endpgm"]
+    assert early_vmem(settle)[3] == []
+    early = [copy] + loop[:2] + ["s_waitcnt vmcnt(0)"] + loop[2:] + drain + [store, "s_endpgm"]
+    assert early_vmem(early)[3] == ["s_waitcnt vmcnt(0)"]
     leaked = laid_out[:laid_out.index(".LBB0_3:") + 1] + [load] + laid_out[laid_out.index(".LBB0_3:") + 1:]
     assert early_vmem(leaked)[0] == [load]
 
