@@ -418,7 +418,7 @@ size_t tbg_conv2d_workspace_query(const tbg_conv2d_shape* shape, const void* x, 
  *                bit-identical results;
  *                tile 448x128, stages 0 or 4: the halo kernel (stride 1 and r*s >= 2 only; c a
  *                multiple of 32 and x, w 16-byte aligned, so nothing is repacked; OW <= 448; an
- *                input window of at most 806 pixels that four 1 KiB copies per wave and tap
+ *                input window of at most 1008 pixels that four 1 KiB copies per wave and tap
  *                bring in time), which copies each input window into LDS once per
  *                32-channel block for all taps.  Its sums run block by block, tap by tap inside
  *                a block, so its results may differ from the im2col tiles' in rounding (both are

@@ -131,7 +131,8 @@ def test_conv_workloads(ops, orc, name):
             assert np.array_equal(got[:, :w.k], base[:, :w.k]), "tiles disagree"
 
 
-HALO = ["conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_dil2", "conv_halo_c96"]
+HALO = ["conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_dil2", "conv_halo_c96",
+        "conv_halo_808"]
 
 
 @gpu
@@ -141,8 +142,8 @@ def test_conv_halo_kernel(ops, orc, name):
     block) in full against the oracle for both output types, bit for bit on small integers, with
     the output rows padded and left untouched past K.  These layers cover partial last tiles of
     an image, output channels past a multiple of 128, dilation, asymmetric padding, one to
-    four window atoms per wave and tap, and (3×3 filters, the unrolled nine-tap loop) one, two
-    and three 32-channel blocks.  (Its sums run in another order than the im2col tiles',
+    four window atoms per wave and tap, (3×3 filters, the unrolled nine-tap loop) one, two
+    and three 32-channel blocks, and a window of 808 pixels.  (Its sums run in another order than the im2col tiles',
     so only the oracle decides.)"""
     import tiled_bf16_gemm_amd as tbg
     w = workloads.CONVS[name]

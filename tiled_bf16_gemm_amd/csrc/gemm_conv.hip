@@ -43,7 +43,7 @@ bool plan_conv_halo(HaloParams& hp, int* hs_out, const char** why) {
   const int tr = min(kHaloBM / c.ow, c.oh);
   const int64_t hh = tr + (int64_t)(c.r - 1) * c.dh, hw = c.ow + (int64_t)(c.s - 1) * c.dw;
   const int64_t hat = (hh * hw * kHaloPitch + 1023) / 1024;
-  if (hat > kHaloMaxAtoms) return (*why = "an input window of at most 806 pixels"), false;
+  if (hat > kHaloMaxAtoms) return (*why = "an input window of at most 1008 pixels"), false;
   const int64_t hs = (hat + 4 * (rs - 1) - 1) / (4 * (rs - 1));
   if (hs > 4) return (*why = "an input window that four atoms per wave and tap copy in time"), false;
   const int tpi = (c.oh + tr - 1) / tr;
@@ -58,7 +58,6 @@ bool plan_conv_halo(HaloParams& hp, int* hs_out, const char** why) {
   hp.hb = (int)hat * 1024;
   hp.cb32 = c.c8 / 32;
   hp.rs = rs;
-  hp.div5 = make_fast_div(5);
   hp.div_hw = make_fast_div((uint32_t)hw);
   hp.div_ow = make_fast_div((uint32_t)c.ow);
   for (int v = 0; v < 9; ++v)

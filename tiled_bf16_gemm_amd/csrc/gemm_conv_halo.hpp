@@ -20,9 +20,10 @@
 // LDS: four filter tiles (128 channels-out × 32 channels-in, 8 KiB each) in a ring, two window
 // images (one per channel block, alternating: the next block's window is copied while the
 // current one is read), one spare 1 KiB atom for copies that carry nothing.  A window pixel takes
-// 80 bytes (its 64 channel bytes and 16 unused), so the 16 lanes of a fragment read, 16
-// consecutive pixels, fall on 16 distinct 16-byte bank groups at any tap offset (5 is odd); the
-// filter tiles use 64-byte rows with the chunk XOR (row >> 2) & 3 for the same property.
+// its 64 channel bytes, unpadded: a 16-byte read of 16 consecutive pixels at two chunks then meets
+// each bank group twice (a pitch of 80 or 96 bytes halves that, but each window atom would carry a
+// fifth or a third of unused bytes, and the kernel is bound by its copies, not by LDS reads); the
+// filter tiles use 64-byte rows with the chunk XOR (row >> 2) & 3.
 //
 // Copies per product step and wave: 2 filter atoms of the tile four steps ahead, then HS window
 // atoms of the next block's window (spread over the first R·S − 1 taps of the current block; a
@@ -38,7 +39,7 @@ constexpr int kHaloBM = 448, kHaloBN = 128;
 constexpr int kHaloFM = 7, kHaloFN = 8;  // fragments per wave: 112 pixels × 128 channels
 constexpr int kHaloStages = 4;           // filter tiles in the ring
 constexpr int kHaloBStage = kHaloBN * 64;
-constexpr int kHaloPitch = 80;           // LDS bytes per window pixel
+constexpr int kHaloPitch = 64;           // LDS bytes per window pixel
 constexpr int kHaloMaxAtoms = 63;        // 1 KiB atoms per window image
 constexpr int kHaloOff0 = kHaloStages * kHaloBStage;
 constexpr int kHaloJunk = kHaloOff0 + 2 * kHaloMaxAtoms * 1024;
@@ -134,26 +135,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_conv_halo_kernel(HaloParams 
   const uint32_t smem_addr = lds_addr_of(smem);
 
   // Window copies: atom a covers 16-byte units 64a .. 64a + 63 of the window image, unit U being
-  // chunk U % 5 of window pixel U / 5 (chunk 4 is the unused fifth); pixel s is window row
-  // s / hw, column s % hw, i.e. input row oh0 − ph + s / hw, column s % hw − pw.  Units outside
-  // the image, past the window or in the unused chunk take an offset with bit 31 set, which
-  // the buffer's range rejects (they land zeros).
+  // chunk U % 4 of window pixel U / 4; pixel s is window row s / hw, column s % hw, i.e. input
+  // row oh0 − ph + s / hw, column s % hw − pw.  Units outside the image or past the window take
+  // an offset with bit 31 set, which the buffer's range rejects (they land zeros).
   const int ih_base = oh0 - cp.ph;
   const uint32_t img_base = (uint32_t)img * (uint32_t)cp.h * (uint32_t)cp.w * (uint32_t)cp.c8 * 2u;
   const uint32_t pix_bytes = (uint32_t)cp.c8 * 2u;
   const int h1 = cp.h - 1, w1 = cp.w - 1;
   auto halo_src = [&](int a, int cb) __attribute__((always_inline)) {
     const uint32_t u = (uint32_t)a * 64u + (uint32_t)lane;
-    const uint32_t s = fast_div(u, hp.div5);
-    const int ch = (int)(u - s * 5u);
+    const uint32_t s = u >> 2;
+    const uint32_t ch = u & 3u;
     const uint32_t hr = fast_div(s, hp.div_hw);
     const int ix = (int)(s - hr * (uint32_t)hp.hw) - cp.pw;
     const int iy = ih_base + (int)hr;
     const uint32_t bad =
-        (uint32_t)(iy | (h1 - iy) | ix | (w1 - ix) | (3 - ch) | (hp.ns - 1 - (int)s)) & kOobOffset;
+        (uint32_t)(iy | (h1 - iy) | ix | (w1 - ix) | (hp.ns - 1 - (int)s)) & kOobOffset;
     // modulo 2^32: exact for pixels inside the image, the only ones not rejected
     const uint32_t pix = (uint32_t)iy * (uint32_t)cp.w + (uint32_t)ix;
-    return (img_base + pix * pix_bytes + (uint32_t)cb * 64u + (uint32_t)ch * 16u) | bad;
+    return (img_base + pix * pix_bytes + (uint32_t)cb * 64u + ch * 16u) | bad;
   };
   auto halo_lds = [&](int buf) __attribute__((always_inline)) {
     return smem_addr + (uint32_t)kHaloOff0 + (uint32_t)(buf * hp.hb);

@@ -55,7 +55,7 @@ struct HaloParams {
   int hh, hw, ns;      // window rows, columns, pixels (hh·hw)
   int hat, hb;         // 1 KiB copy atoms per window image, its LDS bytes (hat·1024)
   int cb32, rs;        // 32-channel blocks, filter taps
-  FastDiv div5, div_hw, div_ow;
+  FastDiv div_hw, div_ow;
   int tap_off[9];      // LDS byte offset of tap v = r·S + s from tap 0 in a window image (v < rs, rs <= 9)
 };
 

@@ -147,6 +147,8 @@ CONVS = {
     "conv_halo_1x3": ConvWorkload("conv_halo_1x3", 2, 12, 24, 32, 40, 1, 3, (0, 1, 0, 1), seed=6020),
     "conv_halo_c96": ConvWorkload("conv_halo_c96", 2, 20, 20, 96, 72, 3, 3, (1, 1, 1, 1), out_dtype="f32",
                                   seed=6022),
+    # a window of 4 × 202 = 808 pixels (51 atoms), in the range the unpadded 64-byte pixels opened
+    "conv_halo_808": ConvWorkload("conv_halo_808", 1, 6, 200, 32, 40, 3, 3, (1, 1, 1, 1), seed=6024),
 }
 
 
