@@ -132,7 +132,7 @@ def test_conv_workloads(ops, orc, name):
 
 
 HALO = ["conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_dil2", "conv_halo_c96",
-        "conv_halo_808"]
+        "conv_halo_808", "conv_halo_max"]
 
 
 @gpu
@@ -143,7 +143,7 @@ def test_conv_halo_kernel(ops, orc, name):
     the output rows padded and left untouched past K.  These layers cover partial last tiles of
     an image, output channels past a multiple of 128, dilation, asymmetric padding, one to
     four window atoms per wave and tap, (3×3 filters, the unrolled nine-tap loop) one, two
-    and three 32-channel blocks, and a window of 808 pixels.  (Its sums run in another order than the im2col tiles',
+    and three 32-channel blocks, and windows of 808 and 1008 pixels (the largest it takes).  (Its sums run in another order than the im2col tiles',
     so only the oracle decides.)"""
     import tiled_bf16_gemm_amd as tbg
     w = workloads.CONVS[name]
@@ -169,7 +169,8 @@ def test_conv_halo_kernel(ops, orc, name):
 @gpu
 def test_conv_halo_alpha_beta_and_refusals(ops, orc):
     """Y <- alpha·conv + beta·Y through the halo kernel (both output types); tile 448x128 is
-    refused where the halo kernel does not apply (stride 2, channels not a multiple of 32)."""
+    refused where the halo kernel does not apply (stride 2, channels not a multiple of 32, a
+    window of 1011 pixels)."""
     import tiled_bf16_gemm_amd as tbg
     w = workloads.CONVS["conv_halo_rows"]
     x, f = workloads.conv_inputs(w)
@@ -185,11 +186,11 @@ def test_conv_halo_alpha_beta_and_refusals(ops, orc):
         r = oracle.gemm_check(got[:, :w.k], ref)
         assert r["pass"], r
         assert np.array_equal(got[:, w.k:], old[:, w.k:].numpy())
-    for name in ("conv_stride2", "conv_3x3"):
+    for name, why in (("conv_stride2", "halo"), ("conv_3x3", "halo"), ("conv_halo_over", "1008 pixels")):
         wr = workloads.CONVS[name]
         xr, fr = workloads.conv_inputs(wr)
         _say(f"halo conv refused on {name}")
-        with pytest.raises(tbg.Error, match="halo"):
+        with pytest.raises(tbg.Error, match=why):
             _conv(ops, wr, xr, fr, "f32", config=cfg)
 
 

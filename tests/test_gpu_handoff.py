@@ -117,7 +117,7 @@ def test_fp8_and_convolution_handoffs(libs):
         _same(got[0], got[1], f"conv {tile}")
     # the halo kernel: its filter ring and its two window images (atoms per wave and tap 1..4)
     for name in ("conv_halo_rows", "conv_halo_wide", "conv_halo_small", "conv_halo_1x3", "conv_halo_c96",
-                 "conv_halo_808"):
+                 "conv_halo_808", "conv_halo_max"):
         w = workloads.CONVS[name]
         x, f = workloads.conv_inputs(w)
         x, f = x.cuda(), f.cuda()

@@ -149,6 +149,11 @@ CONVS = {
                                   seed=6022),
     # a window of 4 × 202 = 808 pixels (51 atoms), in the range the unpadded 64-byte pixels opened
     "conv_halo_808": ConvWorkload("conv_halo_808", 1, 6, 200, 32, 40, 3, 3, (1, 1, 1, 1), seed=6024),
+    # the largest window the halo kernel takes, 3 × 336 = 1008 pixels (63 atoms), and one past it
+    # (3 × 337 = 1011: refused)
+    "conv_halo_max": ConvWorkload("conv_halo_max", 1, 2, 334, 32, 16, 3, 3, (1, 1, 1, 1), out_dtype="f32",
+                                  seed=6026),
+    "conv_halo_over": ConvWorkload("conv_halo_over", 1, 2, 335, 32, 16, 3, 3, (1, 1, 1, 1), seed=6028),
 }
 
 
